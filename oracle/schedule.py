@@ -1,0 +1,183 @@
+"""CPU enumeration of the tile mapping, the worker assignment and the Stream-K splits.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Written from the pages' prose, as
+orderings produced by walking the tile grid, not as the closed-form index arithmetic that the
+HIP library uses, so that the two are independent descriptions of the same schedule.
+
+Sources
+  * "DeepGEMM on SM90" page, CTA <-> output tile section and its mapping-family table:
+    the mapping F(i) -> (m, n) assigns the i-th linear task an output tile; Linear N-fast visits
+    C00, C01, ... then C10; Linear M-fast visits C00, C10, ... then C01; Grouped-M cuts M into
+    strips of G tile-rows and runs M-fast inside a strip; Grouped-N cuts N into strips of G
+    tile-columns and runs N-fast inside.  Static assignment gives CTA i the tile F(i);
+    persistent workers take i = p, p + P, p + 2P, ...
+  * Same page, Kernel Configuration Heuristic: CTA count = ceil(M/BM) * ceil(N/BN),
+    waves = ceil(CTAs / num_sms), wave efficiency = CTAs / (waves * num_sms).
+  * "H100 Kernel Design" lesson, section 10.3, and "H100 Stream-K" lesson, sections 2-6:
+    Stream-K treats the whole product as one band of MMA iterations split equally across the
+    workers; only the tail wave is split when it is at most half full (otherwise plain data
+    parallel); a split is one worker's share of one output tile, tracked by
+    (K_idx, k_tile_count, is_final = K_idx + k_tile_count == k-tiles per tile); the worker walks
+    its tiles backwards; the lock counts the cumulative k-tiles reduced so far.
+
+Reading where the pages are open (each is listed in the design doc):
+  * a short last strip in the grouped mappings holds the remaining tile rows (columns);
+  * the Stream-K unit u owns iterations [floor(u T / P), floor((u+1) T / P));
+  * roles: K_idx == 0 and final -> whole tile; K_idx == 0 only -> first; final only -> last;
+    neither -> middle;
+  * the data-parallel tiles run first, then the Stream-K tail.
+
+The XCD remap is this build's own MI355X design, not the pages': with X L2 domains (XCDs) and
+workgroups dealt to them round-robin, the worker id that workgroup b runs under is chosen so that
+every XCD owns a contiguous run of worker ids.  It is enumerated here from that statement.
+"""
+from dataclasses import dataclass
+
+LINEAR_N, LINEAR_M, GROUPED_M, GROUPED_N = 0, 1, 2, 3
+STATIC, PERSISTENT, STREAMK = 0, 1, 2
+ROLE_WHOLE, ROLE_FIRST, ROLE_MIDDLE, ROLE_LAST = 0, 1, 2, 3
+
+
+def tile_counts(M, N, K, BM, BN, BK):
+    """Tiles along M, along N, and k-tiles along K (ceilings)."""
+    cdiv = lambda a, b: -(-a // b)
+    return cdiv(M, BM), cdiv(N, BN), cdiv(K, BK)
+
+
+def tile_order(mode, Mt, Nt, G=1):
+    """The list F(0), F(1), ... of (m, n) tile coordinates, built by walking the grid."""
+    order = []
+    if mode == LINEAR_N:
+        for m in range(Mt):
+            for n in range(Nt):
+                order.append((m, n))
+    elif mode == LINEAR_M:
+        for n in range(Nt):
+            for m in range(Mt):
+                order.append((m, n))
+    elif mode == GROUPED_M:
+        if G < 1:
+            raise ValueError("G must be >= 1")
+        for strip_start in range(0, Mt, G):
+            rows = range(strip_start, min(strip_start + G, Mt))
+            for n in range(Nt):           # the strip advances along N ...
+                for m in rows:            # ... and runs M-fast inside
+                    order.append((m, n))
+    elif mode == GROUPED_N:
+        if G < 1:
+            raise ValueError("G must be >= 1")
+        for strip_start in range(0, Nt, G):
+            cols = range(strip_start, min(strip_start + G, Nt))
+            for m in range(Mt):
+                for n in cols:
+                    order.append((m, n))
+    else:
+        raise ValueError(f"unknown mapping {mode}")
+    return order
+
+
+def xcd_worker_ids(P, X=8):
+    """worker id of each workgroup b < P when workgroups are dealt to X XCDs round-robin.
+
+    XCD x receives workgroups x, x + X, x + 2X, ... in that order; it is given the worker ids
+    x * P/X, x * P/X + 1, ... in the same order.  Only defined when X divides P; otherwise every
+    workgroup keeps its own index.
+    """
+    if P % X != 0:
+        return list(range(P))
+    per = P // X
+    ids = [None] * P
+    for x in range(X):
+        dealt = [b for b in range(P) if b % X == x]
+        for rank, b in enumerate(dealt):
+            ids[b] = x * per + rank
+    return ids
+
+
+def wave_efficiency(ctas, num_sms):
+    waves = -(-ctas // num_sms)
+    return ctas / (waves * num_sms)
+
+
+@dataclass(frozen=True)
+class WorkItem:
+    worker: int      # workgroup index b
+    seq: int         # position in that workgroup's processing order
+    tile: int        # linear task index i (F(i) gives m, n)
+    m: int
+    n: int
+    k_begin: int     # first k-tile (K_idx)
+    k_end: int       # one past the last k-tile (K_idx + k_tile_count)
+    role: int
+
+
+def streamk_split_plan(tiles, P):
+    """(data-parallel tile count, Stream-K tile count) under the hybrid rule."""
+    full, tail = divmod(tiles, P)
+    if tail == 0 or tail * 2 > P:
+        return tiles, 0
+    return full * P, tail
+
+
+def streamk_units(sk_tiles, Kt, P, first_tile=0):
+    """For each unit u, its splits [(tile, K_idx, count, final)] in forward k order."""
+    T = sk_tiles * Kt
+    units = []
+    for u in range(P):
+        lo, hi = (u * T) // P, ((u + 1) * T) // P
+        splits = []
+        it = lo
+        while it < hi:
+            t = it // Kt
+            tile_first_iter = t * Kt
+            end = min(hi, tile_first_iter + Kt)
+            k_idx = it - tile_first_iter
+            count = end - it
+            splits.append((first_tile + t, k_idx, count, k_idx + count == Kt))
+            it = end
+        units.append(splits)
+    return units
+
+
+def role_of(k_idx, final):
+    if k_idx == 0:
+        return ROLE_WHOLE if final else ROLE_FIRST
+    return ROLE_LAST if final else ROLE_MIDDLE
+
+
+def enumerate_schedule(M, N, K, BM, BN, BK, mapping, G, sched, P=None, X=8, xcd_remap=True):
+    """Every work item of the launch, grouped by workgroup, in each workgroup's order."""
+    Mt, Nt, Kt = tile_counts(M, N, K, BM, BN, BK)
+    order = tile_order(mapping, Mt, Nt, G)
+    tiles = Mt * Nt
+    items = []
+    if sched == STATIC:
+        ids = xcd_worker_ids(tiles, X) if xcd_remap else list(range(tiles))
+        for b in range(tiles):
+            i = ids[b]
+            m, n = order[i]
+            items.append(WorkItem(b, 0, i, m, n, 0, Kt, ROLE_WHOLE))
+        return items
+    if P is None or P < 1:
+        raise ValueError("persistent and Stream-K schedules need P >= 1 workers")
+    if sched == PERSISTENT:
+        dp_tiles, sk_tiles = tiles, 0
+    elif sched == STREAMK:
+        dp_tiles, sk_tiles = streamk_split_plan(tiles, P)
+    else:
+        raise ValueError(f"unknown scheduler {sched}")
+    ids = xcd_worker_ids(P, X) if xcd_remap else list(range(P))
+    units = streamk_units(sk_tiles, Kt, P, first_tile=dp_tiles) if sk_tiles else None
+    for b in range(P):
+        seq = 0
+        for i in range(ids[b], dp_tiles, P):
+            m, n = order[i]
+            items.append(WorkItem(b, seq, i, m, n, 0, Kt, ROLE_WHOLE))
+            seq += 1
+        if units:
+            for (i, k_idx, count, final) in reversed(units[b]):
+                m, n = order[i]
+                items.append(WorkItem(b, seq, i, m, n, k_idx, k_idx + count,
+                                      role_of(k_idx, final)))
+                seq += 1
+    return items

@@ -1,0 +1,157 @@
+"""Pins the oracle's CPU enumeration of the tile mapping, assignment and Stream-K splits to the
+pages' worked examples and to invariants that hold for any correct schedule."""
+from collections import Counter
+
+import pytest
+
+from oracle import schedule as S
+from golden_util import load, ints
+
+
+def test_streamk_worked_example():
+    g = load("streamk_worked_example.txt")
+    tiles, kt, units = int(g["tiles"][0]), int(g["k_tiles_per_tile"][0]), int(g["units"][0])
+    plan = S.streamk_units(tiles, kt, units)
+    for s in g["split"]:
+        u, t, k_idx, count, final = ints(s)
+        assert (t, k_idx, count, bool(final)) in plan[u]
+    u, nsplits = ints(g["unit_split_count"][0])
+    assert len(plan[u]) == nsplits
+
+
+def test_wave_quantization_example():
+    g = load("wave_quantization.txt")
+    ctas, sms = int(g["ctas"][0]), int(g["num_sms"][0])
+    assert -(-ctas // sms) == int(g["waves"][0])
+    assert round(100 * S.wave_efficiency(ctas, sms), 1) == float(g["efficiency_percent"][0])
+
+
+def test_mapping_working_set_example():
+    g = load("mapping_working_set.txt")
+    mt, nt = ints(g["grid"][0])
+    BM, BN, K = int(g["BM"][0]), int(g["BN"][0]), int(g["K"][0])
+    esz, conc, G = int(g["bytes_per_element"][0]), int(g["concurrent"][0]), int(g["group"][0])
+    first = S.tile_order(S.GROUPED_M, mt, nt, G)[:conc]
+    a_bands = {m for m, _ in first}
+    b_bands = {n for _, n in first}
+    assert len(a_bands) == int(g["unique_a_bands"][0])
+    assert len(b_bands) == int(g["unique_b_bands"][0])
+    mib = 1 << 20
+    a_bytes = len(a_bands) * BM * K * esz
+    b_bytes = len(b_bands) * BN * K * esz
+    assert a_bytes == int(g["a_mib"][0]) * mib and b_bytes == int(g["b_mib"][0]) * mib
+    assert a_bytes + b_bytes == int(g["working_set_mib"][0]) * mib
+    # linear N-fast over the same grid touches 1 A band and 8 B bands instead
+    lin = S.tile_order(S.LINEAR_N, mt, nt)[:conc]
+    assert len({m for m, _ in lin}) == 1 and len({n for _, n in lin}) == 8
+
+
+@pytest.mark.parametrize("mode", [S.LINEAR_N, S.LINEAR_M, S.GROUPED_M, S.GROUPED_N])
+@pytest.mark.parametrize("Mt,Nt,G", [(1, 1, 1), (7, 5, 3), (32, 32, 8), (4, 112, 8), (9, 2, 4)])
+def test_mapping_is_a_bijection(mode, Mt, Nt, G):
+    order = S.tile_order(mode, Mt, Nt, G)
+    assert len(order) == Mt * Nt
+    assert set(order) == {(m, n) for m in range(Mt) for n in range(Nt)}
+
+
+def test_mapping_equivalences_from_table():
+    # Grouped-M with G = 1 is Linear N-fast; a strip covering all rows is Linear M-fast
+    for Mt, Nt in [(5, 7), (8, 8), (1, 9)]:
+        assert S.tile_order(S.GROUPED_M, Mt, Nt, 1) == S.tile_order(S.LINEAR_N, Mt, Nt)
+        assert S.tile_order(S.GROUPED_M, Mt, Nt, Mt) == S.tile_order(S.LINEAR_M, Mt, Nt)
+        assert S.tile_order(S.GROUPED_N, Mt, Nt, 1) == S.tile_order(S.LINEAR_M, Mt, Nt)
+        assert S.tile_order(S.GROUPED_N, Mt, Nt, Nt) == S.tile_order(S.LINEAR_N, Mt, Nt)
+        # Grouped-N is Grouped-M of the transposed grid
+        for G in (2, 3):
+            gn = S.tile_order(S.GROUPED_N, Mt, Nt, G)
+            gm_t = [(m, n) for (n, m) in S.tile_order(S.GROUPED_M, Nt, Mt, G)]
+            assert gn == gm_t
+
+
+def test_grouped_m_inside_a_strip_is_m_fast():
+    order = S.tile_order(S.GROUPED_M, 10, 3, 4)
+    assert order[:5] == [(0, 0), (1, 0), (2, 0), (3, 0), (0, 1)]
+    # the short last strip (rows 8, 9) still runs M-fast
+    assert order[-4:] == [(8, 1), (9, 1), (8, 2), (9, 2)]
+
+
+def test_persistent_stride():
+    items = S.enumerate_schedule(1024, 1024, 256, 128, 128, 64, S.LINEAR_N, 1, S.PERSISTENT,
+                                 P=24, xcd_remap=False)
+    by_worker = {}
+    for it in items:
+        by_worker.setdefault(it.worker, []).append(it.tile)
+    for p, tiles in by_worker.items():
+        assert tiles == list(range(p, 64, 24))
+    assert sorted(t for ts in by_worker.values() for t in ts) == list(range(64))
+
+
+def test_xcd_remap_contiguous_per_xcd():
+    ids = S.xcd_worker_ids(256, 8)
+    assert sorted(ids) == list(range(256))
+    for x in range(8):
+        got = sorted(ids[b] for b in range(256) if b % 8 == x)
+        assert got == list(range(32 * x, 32 * x + 32))
+    assert S.xcd_worker_ids(100, 8) == list(range(100))
+
+
+def _coverage(items, Kt):
+    cnt = Counter()
+    for it in items:
+        for k in range(it.k_begin, it.k_end):
+            cnt[(it.tile, k)] += 1
+    return cnt
+
+
+@pytest.mark.parametrize("M,N,K,P", [(512, 512, 65536, 256), (512, 384, 4096, 8),
+                                     (1024, 1024, 1024, 40), (384, 256, 7 * 64, 5)])
+def test_streamk_covers_every_k_tile_once(M, N, K, P):
+    BM = BN = 128
+    BK = 64
+    Mt, Nt, Kt = S.tile_counts(M, N, K, BM, BN, BK)
+    items = S.enumerate_schedule(M, N, K, BM, BN, BK, S.LINEAR_N, 1, S.STREAMK, P=P)
+    cnt = _coverage(items, Kt)
+    assert set(cnt) == {(t, k) for t in range(Mt * Nt) for k in range(Kt)}
+    assert set(cnt.values()) == {1}
+    # exactly one split per tile ends the tile, and it is the final (or whole-tile) role
+    for t in range(Mt * Nt):
+        ends = [it for it in items if it.tile == t and it.k_end == Kt]
+        assert len(ends) == 1 and ends[0].role in (S.ROLE_WHOLE, S.ROLE_LAST)
+        starts = [it for it in items if it.tile == t and it.k_begin == 0]
+        assert len(starts) == 1 and starts[0].role in (S.ROLE_WHOLE, S.ROLE_FIRST)
+
+
+def test_streamk_config_band_shape():
+    """512 x 512 x 65536 with 128 x 128 x 64 tiles on 256 workers: 16 tiles, 16 splits each."""
+    items = S.enumerate_schedule(512, 512, 65536, 128, 128, 64, S.LINEAR_N, 1, S.STREAMK, P=256)
+    assert len(items) == 256
+    per_tile = Counter(it.tile for it in items)
+    assert set(per_tile.values()) == {16}
+    roles = Counter(it.role for it in items)
+    assert roles == {S.ROLE_FIRST: 16, S.ROLE_MIDDLE: 224, S.ROLE_LAST: 16}
+    assert all(it.k_end - it.k_begin == 64 for it in items)
+
+
+def test_streamk_fifty_percent_rule():
+    assert S.streamk_split_plan(16, 256) == (0, 16)       # tail far below half: Stream-K
+    assert S.streamk_split_plan(256 + 100, 256) == (256, 100)
+    assert S.streamk_split_plan(256 + 128, 256) == (256, 128)   # exactly half: still Stream-K
+    assert S.streamk_split_plan(256 + 129, 256) == (385, 0)     # more than half full: DP
+    assert S.streamk_split_plan(512, 256) == (512, 0)           # no tail
+
+
+def test_streamk_backward_tile_order_and_roles():
+    items = S.enumerate_schedule(384, 256, 7 * 64, 128, 128, 64, S.LINEAR_N, 1, S.STREAMK, P=5)
+    by_worker = {}
+    for it in items:
+        by_worker.setdefault(it.worker, []).append(it)
+    for its in by_worker.values():
+        sk = [it for it in its if it.role != S.ROLE_WHOLE or it.k_end - it.k_begin != 7]
+        tiles = [it.tile for it in sk]
+        assert tiles == sorted(tiles, reverse=True)
+    for it in items:
+        first = it.k_begin == 0
+        final = it.k_end == 7
+        want = {(True, True): S.ROLE_WHOLE, (True, False): S.ROLE_FIRST,
+                (False, False): S.ROLE_MIDDLE, (False, True): S.ROLE_LAST}[(first, final)]
+        assert it.role == want
