@@ -1,0 +1,228 @@
+"""Benchmark of the MI355X dense GEMM: one step = one C = alpha * A x B through the C ABI.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only NAME]
+
+Headline: BF16 M = N = K = 4096, uniform[-1, 1] operands resident in HBM, FP32 accumulate, bf16
+output, grouped-M (G = 8) tile mapping, persistent scheduler.  The JSON line's "secondary" block
+carries the other workloads (FP8 e4m3 8192^3 with per-tensor scales, the 4096 x 14336 x 4096 MLP
+shape, the 512 x 512 x 65536 Stream-K case, 256^3) timed the same way.  Progress goes to stderr;
+stdout holds exactly one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0}   # MI355X dense MFMA, published
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_design_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json.txt")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            data = json.loads(f.read().strip().splitlines()[-1])
+    except Exception:
+        return None
+    entry = data.get(workload)
+    if not entry or entry.get("source_hash") != source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+# name, workload key, mapping, group, sched, tile, out, workers
+RUNS = {
+    "bf16_4096": ("bf16_4096", "grouped_m", 8, "persistent", 0, "bf16", 0),
+    "bf16_4096_linear": ("bf16_4096", "linear_n", 1, "persistent", 0, "bf16", 0),
+    "bf16_4096_t128": ("bf16_4096", "grouped_m", 8, "persistent", 128, "bf16", 0),
+    "fp8_8192": ("fp8_8192", "grouped_m", 16, "persistent", 0, "bf16", 0),
+    "bf16_mlp_up": ("bf16_mlp_up", "grouped_m", 8, "persistent", 0, "bf16", 0),
+    "bf16_streamk": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256),
+    "bf16_256": ("bf16_256", "linear_n", 1, "static", 128, "f32", 0),
+}
+
+
+def time_run(name, steps, warmup, torch, dg, gi, cache):
+    wl_name, mapping, group, sched, tile, out, workers = RUNS[name]
+    wl = gi.WORKLOADS[wl_name]
+    if wl_name not in cache:
+        t0 = time.time()
+        op = gi.make_workload(wl_name)
+        dev = torch.device("cuda:0")
+        if op.dtype == "bf16":
+            import numpy as np
+            A = torch.from_numpy(op.A.view(np.int16)).to(dev)
+            B = torch.from_numpy(op.B.view(np.int16)).to(dev)
+        else:
+            A = torch.from_numpy(op.A).to(dev)
+            B = torch.from_numpy(op.B).to(dev)
+        sa = torch.tensor([op.scale_a], dtype=torch.float32, device=dev)
+        sb = torch.tensor([op.scale_b], dtype=torch.float32, device=dev)
+        cache[wl_name] = (op, A, B, sa, sb)
+        log(f"{wl_name}: inputs generated and resident in HBM ({time.time() - t0:.1f} s)")
+    op, A, B, sa, sb = cache[wl_name]
+    desc = dg.make_desc(op.M, op.N, op.K,
+                        dg.GEMM_BF16 if op.dtype == "bf16" else dg.GEMM_FP8_E4M3,
+                        dg.GEMM_BF16 if out == "bf16" else dg.GEMM_F32, dg.MAPPINGS[mapping],
+                        group, dg.SCHEDS[sched], workers, tile, tile, 0, 0)
+    plan = dg.Plan(desc)
+    C = torch.empty((op.M, op.N), device=A.device,
+                    dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+    ws = None
+    if plan.workspace_bytes:
+        ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=A.device)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        plan.run(A, B, C, sa, sb, ws, stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        plan.run(A, B, C, sa, sb, ws, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dev_ms = e0.elapsed_time(e1) / steps
+    flops = 2.0 * op.M * op.N * op.K
+    info = plan.info
+    res = {
+        "workload": wl_name, "M": op.M, "N": op.N, "K": op.K, "dtype": op.dtype, "out": out,
+        "tile": [info.bm, info.bn, info.bk], "stages": info.stages, "mapping": mapping,
+        "group": group, "sched": sched, "grid": info.grid,
+        "dp_tiles": info.dp_tiles, "sk_tiles": info.sk_tiles,
+        "ms_per_step": wall * 1e3 / steps, "kernel_us": dev_ms * 1e3,
+        "tflops": flops / (wall / steps) / 1e12, "kernel_tflops": flops / (dev_ms * 1e-3) / 1e12,
+    }
+    res["frac_of_peak"] = res["kernel_tflops"] / PEAK_TFLOPS[op.dtype]
+    alg_bytes = op.A.nbytes + op.B.nbytes + op.M * op.N * (2 if out == "bf16" else 4)
+    res["alg_bytes"] = alg_bytes
+    res["hbm_gbs_alg"] = alg_bytes / (dev_ms * 1e-3) / 1e9
+    log(f"{name}: {res['kernel_us']:.1f} us/launch, {res['kernel_tflops']:.1f} TFLOP/s "
+        f"({100 * res['frac_of_peak']:.1f}% of {PEAK_TFLOPS[op.dtype]:.0f}), grid {info.grid}, "
+        f"tile {info.bm}x{info.bn}x{info.bk}")
+    return res
+
+
+def cpu_baseline(gi, budget_s=12.0):
+    """The oracle as it stands, timed on the host's cores on a row block of the 4096^3 workload."""
+    import numpy as np
+    import oracle
+    op = gi.make_workload("bf16_4096")
+    threads = oracle.default_threads()
+    A = np.ascontiguousarray(op.A).reshape(-1)
+    rows = 64
+    t0 = time.perf_counter()
+    oracle.gemm_ref(rows, op.N, op.K, oracle.BF16, A[: rows * op.K], op.B, threads=threads)
+    t_probe = time.perf_counter() - t0
+    rows = int(min(op.M, max(64, rows * budget_s / max(t_probe, 1e-3))))
+    rows -= rows % 64 or 0
+    rows = max(rows, 64)
+    t0 = time.perf_counter()
+    oracle.gemm_ref(rows, op.N, op.K, oracle.BF16, A[: rows * op.K], op.B, threads=threads)
+    dt = time.perf_counter() - t0
+    tflops = 2.0 * rows * op.N * op.K / dt / 1e12
+    log(f"cpu baseline: oracle on {rows} x {op.N} x {op.K} rows in {dt:.1f} s with {threads} "
+        f"threads -> {tflops * 1e3:.2f} GFLOP/s")
+    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the bf16 4096^3 product (all 4096 columns, full K), "
+                      f"fp64 sequential dot products, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--only", default=None, help="time just this run (see RUNS)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the multi-GPU "
+              "sharding is a design note, not an implemented path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import dense_gemm_design_amd as dg
+    import gemm_inputs as gi
+    dg.load()  # fails loudly if the HIP library is not built
+
+    cache = {}
+    if args.only:
+        res = time_run(args.only, args.steps, args.warmup, torch, dg, gi, cache)
+        print(json.dumps(res), flush=True)
+        return
+
+    head = time_run("bf16_4096", args.steps, args.warmup, torch, dg, gi, cache)
+    secondary = {}
+    if not args.no_secondary:
+        for name in ("bf16_4096_linear", "bf16_4096_t128", "fp8_8192", "bf16_mlp_up",
+                     "bf16_streamk", "bf16_256"):
+            steps = max(10, args.steps // (4 if name == "fp8_8192" else 1))
+            r = time_run(name, steps, max(2, args.warmup // 2), torch, dg, gi, cache)
+            secondary[name] = {k: r[k] for k in ("kernel_us", "kernel_tflops", "frac_of_peak",
+                                                 "hbm_gbs_alg", "tile", "grid", "mapping",
+                                                 "sched")}
+            if name in cache:
+                del cache[name]
+    cache.clear()
+    torch.cuda.empty_cache()
+
+    flops = 2.0 * head["M"] * head["N"] * head["K"]
+    achieved = flops / (head["kernel_us"] * 1e-6) / 1e12
+    line = {
+        "metric": "GEMM TFLOPS and % of MI355X MFMA peak, bf16 4096^3 and fp8 8192^3",
+        "value": round(head["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bf16 gemm M=N=K=4096, uniform[-1,1], fp32 accumulate, bf16 out",
+                   "M": 4096, "N": 4096, "K": 4096, "tile": head["tile"],
+                   "mapping": "grouped_m", "group": 8, "sched": "persistent",
+                   "grid": head["grid"]},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": measured_traffic("bf16_4096")},
+        "secondary": secondary,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(gi)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,334 @@
+// C ABI of the MI355X dense GEMM: planner, launcher and CPU schedule replay (include/gemm.h).
+//
+// The planner turns a gemm_desc into a plan: the tile shape and its kernel, the tile grid
+// (CTA count = ceil(M/BM) * ceil(N/BN), "DeepGEMM on SM90" page, Kernel Configuration Heuristic),
+// the scheduler's parameters (sched.h) and the workspace size for the Stream-K fixup ("H100
+// Stream-K" lesson, section 6: one FP32 partial tile per split output tile, followed by one int
+// lock per tile in the same allocation, all locks zero at launch).
+#include <hip/hip_runtime.h>
+
+#include <new>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/gemm.h"
+#include "gemm_kernel.h"
+#include "sched.h"
+
+namespace {
+
+using namespace dg;
+
+// Tile configurations.  SWZ = 1 spreads the 16 rows that one 16-lane LDS read phase touches over
+// 16 distinct 16-byte bank groups for 128-byte rows.
+using CfgBf16_256 = TileCfg<DT_BF16, 256, 256, 64, 2, 2, 2, 1>;
+using CfgBf16_128 = TileCfg<DT_BF16, 128, 128, 64, 2, 2, 2, 1>;
+using CfgFp8_256 = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1>;
+using CfgFp8_128 = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 2, 1>;
+
+typedef hipError_t (*launch_fn)(const KernelArgs &, int grid, hipStream_t);
+typedef const void *(*kernel_fn)();
+
+template <class CFG>
+hipError_t launch_cfg(const KernelArgs &a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL(gemm_kernel<CFG>, dim3(grid), dim3(CFG::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+template <class CFG>
+const void *kernel_of() {
+  return (const void *)&gemm_kernel<CFG>;
+}
+
+struct KernelEntry {
+  int dt, bm, bn, bk, threads, stages, lds;
+  launch_fn launch;
+  kernel_fn kernel;
+};
+
+template <class CFG>
+constexpr KernelEntry entry() {
+  return KernelEntry{CFG::DT, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::STAGES,
+                     CFG::LDS_BYTES, &launch_cfg<CFG>, &kernel_of<CFG>};
+}
+
+const KernelEntry kKernels[] = {
+    entry<CfgBf16_256>(),
+    entry<CfgBf16_128>(),
+    entry<CfgFp8_256>(),
+    entry<CfgFp8_128>(),
+};
+
+constexpr int kXcds = 8;           // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kDefaultSpin = 1 << 24;
+constexpr int kTestSpin = 4096;
+constexpr int kTraceCap = 64;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t align_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+}  // namespace
+
+struct gemm_plan {
+  gemm_desc d;
+  const KernelEntry *k;
+  KernelArgs proto;     // everything but the pointers
+  gemm_plan_info info;
+  int64_t partial_off, lock_off, error_off, trace_off, ws_bytes;
+};
+
+extern "C" {
+
+const char *gemm_status_string(int status) {
+  switch (status) {
+    case GEMM_OK: return "ok";
+    case GEMM_ERR_INVALID_ARG: return "invalid argument";
+    case GEMM_ERR_UNSUPPORTED: return "unsupported problem or configuration";
+    case GEMM_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
+    case GEMM_ERR_WORKSPACE: return "workspace missing or too small";
+    case GEMM_ERR_HIP: return "HIP runtime error";
+    case GEMM_ERR_CAPACITY: return "output buffer too small";
+    default: return "unknown status";
+  }
+}
+
+int gemm_create(const gemm_desc *desc, gemm_handle *out) {
+  if (!desc || !out) return GEMM_ERR_INVALID_ARG;
+  *out = nullptr;
+  const gemm_desc d = *desc;
+  if (d.M < 0 || d.N < 0 || d.K < 0) return GEMM_ERR_INVALID_ARG;
+  if (d.dtype_ab != GEMM_BF16 && d.dtype_ab != GEMM_FP8_E4M3) return GEMM_ERR_INVALID_ARG;
+  if (d.dtype_c != GEMM_F32 && d.dtype_c != GEMM_BF16) return GEMM_ERR_INVALID_ARG;
+  if ((d.layout_a != GEMM_ROW_MAJOR && d.layout_a != GEMM_COL_MAJOR) ||
+      (d.layout_b != GEMM_ROW_MAJOR && d.layout_b != GEMM_COL_MAJOR))
+    return GEMM_ERR_INVALID_ARG;
+  if (d.mapping < GEMM_MAP_LINEAR_N || d.mapping > GEMM_MAP_GROUPED_N) return GEMM_ERR_INVALID_ARG;
+  const bool grouped = d.mapping == GEMM_MAP_GROUPED_M || d.mapping == GEMM_MAP_GROUPED_N;
+  if (grouped && d.group < 1) return GEMM_ERR_INVALID_ARG;
+  if (d.sched < GEMM_SCHED_STATIC || d.sched > GEMM_SCHED_AUTO) return GEMM_ERR_INVALID_ARG;
+  if (d.num_workers < 0 || d.bm < 0 || d.bn < 0 || d.bk < 0) return GEMM_ERR_INVALID_ARG;
+  if (d.flags & ~(GEMM_FLAG_TRACE | GEMM_FLAG_NO_XCD_REMAP | GEMM_FLAG_TEST_SKIP_PUBLISH))
+    return GEMM_ERR_INVALID_ARG;
+
+  // Well-formed; now what the kernels implement.
+  if (d.layout_a != GEMM_ROW_MAJOR || d.layout_b != GEMM_COL_MAJOR) return GEMM_ERR_UNSUPPORTED;
+  const int eb = d.dtype_ab == GEMM_BF16 ? 2 : 1;
+  if ((d.K * eb) % 16 != 0) return GEMM_ERR_UNSUPPORTED;   // 16-byte rows for the LDS loads
+  if (d.N % 8 != 0) return GEMM_ERR_UNSUPPORTED;           // 16-byte output rows
+  if (d.K * eb > (int64_t)1 << 30) return GEMM_ERR_UNSUPPORTED;
+
+  // Tile shape: 256 x 256 unless asked otherwise or the problem has too few big tiles.
+  int bm = d.bm, bn = d.bn;
+  if (bm == 0 && bn == 0) {
+    const int64_t big = cdiv(d.M, 256) * cdiv(d.N, 256);  // 0 for an empty output
+    const bool streamk = d.sched == GEMM_SCHED_STREAMK;
+    bm = bn = (big >= 128 && !streamk) ? 256 : 128;
+  } else if (bm == 0 || bn == 0) {
+    bm = bn = (bm ? bm : bn);
+  }
+  const int want_dt = d.dtype_ab == GEMM_BF16 ? DT_BF16 : DT_FP8;
+  const KernelEntry *k = nullptr;
+  for (const KernelEntry &e : kKernels)
+    if (e.dt == want_dt && e.bm == bm && e.bn == bn && (d.bk == 0 || d.bk == e.bk)) k = &e;
+  if (!k) return GEMM_ERR_UNSUPPORTED;
+  // rows of one tile must stay addressable by 32-bit buffer offsets
+  if ((int64_t)bm * d.K * eb >= 0x7FFFFFF0ll || (int64_t)bn * d.K * eb >= 0x7FFFFFF0ll)
+    return GEMM_ERR_UNSUPPORTED;
+
+  const int64_t Mt = cdiv(d.M, bm), Nt = cdiv(d.N, bn), Kt = cdiv(d.K, k->bk);
+  const int64_t tiles = Mt * Nt;
+  if (Mt > INT32_MAX || Nt > INT32_MAX || Kt > INT32_MAX || tiles > INT32_MAX)
+    return GEMM_ERR_UNSUPPORTED;
+
+  int sched = d.sched;
+  int workers = d.num_workers;
+  if (sched != GEMM_SCHED_STATIC && workers == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return GEMM_ERR_HIP;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k->kernel(), k->threads, 0) !=
+        hipSuccess)
+      return GEMM_ERR_HIP;
+    if (per_cu < 1) per_cu = 1;
+    workers = cus * per_cu;
+  }
+  if (sched == GEMM_SCHED_AUTO) {
+    int32_t dp, sk;
+    streamk_plan(tiles, workers, dp, sk);
+    sched = sk > 0 ? GEMM_SCHED_STREAMK : GEMM_SCHED_PERSISTENT;
+  }
+
+  SchedParams sp;
+  memset(&sp, 0, sizeof sp);
+  sp.Mt = (int32_t)Mt;
+  sp.Nt = (int32_t)Nt;
+  sp.Kt = (int32_t)Kt;
+  sp.mapping = d.mapping;
+  sp.G = grouped ? d.group : 1;
+  if (sched == GEMM_SCHED_STATIC) {
+    sp.P = (int32_t)tiles;
+    sp.dp_tiles = (int32_t)tiles;
+    sp.sk_tiles = 0;
+  } else if (sched == GEMM_SCHED_PERSISTENT || tiles == 0) {
+    sched = sched == GEMM_SCHED_STREAMK ? sched : GEMM_SCHED_PERSISTENT;
+    sp.P = (int32_t)(workers < tiles ? workers : tiles);
+    sp.dp_tiles = (int32_t)tiles;
+    sp.sk_tiles = 0;
+  } else {
+    sp.P = workers;
+    streamk_plan(tiles, workers, sp.dp_tiles, sp.sk_tiles);
+    if (Kt == 0) {  // nothing to split: every tile is written (with zeros) data-parallel
+      sp.dp_tiles = (int32_t)tiles;
+      sp.sk_tiles = 0;
+    }
+    if ((int64_t)sp.sk_tiles * Kt > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
+  }
+  sp.X = (d.flags & GEMM_FLAG_NO_XCD_REMAP) ? 1 : kXcds;
+
+  gemm_plan *p = new (std::nothrow) gemm_plan;
+  if (!p) return GEMM_ERR_INVALID_ARG;
+  memset(p, 0, sizeof *p);
+  p->d = d;
+  p->k = k;
+
+  // Workspace: [partials: sk_tiles * BM * BN fp32][locks: sk_tiles int][error word][trace]
+  int64_t off = 0;
+  p->partial_off = p->lock_off = p->error_off = p->trace_off = -1;
+  if (sp.sk_tiles > 0 || (d.flags & GEMM_FLAG_TRACE)) {
+    p->partial_off = 0;
+    off = sp.sk_tiles * (int64_t)bm * bn * 4;
+    p->lock_off = off;
+    off = align_up(off + sp.sk_tiles * 4, 256);
+    p->error_off = off;
+    off += 256;
+    if (d.flags & GEMM_FLAG_TRACE) {
+      p->trace_off = off;
+      off += (int64_t)sp.P * kTraceCap * 8 * 4;
+    }
+  }
+  p->ws_bytes = off;
+
+  KernelArgs &a = p->proto;
+  memset(&a, 0, sizeof a);
+  a.M = d.M;
+  a.N = d.N;
+  a.K = d.K;
+  a.lda_bytes = d.K * eb;
+  a.ldb_bytes = d.K * eb;
+  a.ldc = d.N;
+  a.sp = sp;
+  a.out_bf16 = d.dtype_c == GEMM_BF16;
+  a.flags = d.flags;
+  a.trace_cap = kTraceCap;
+  a.max_spin = (d.flags & GEMM_FLAG_TEST_SKIP_PUBLISH) ? kTestSpin : kDefaultSpin;
+
+  gemm_plan_info &in = p->info;
+  in.bm = k->bm;
+  in.bn = k->bn;
+  in.bk = k->bk;
+  in.stages = k->stages;
+  in.threads = k->threads;
+  in.grid = sp.P;
+  in.mt = sp.Mt;
+  in.nt = sp.Nt;
+  in.kt = sp.Kt;
+  in.sched = sched;
+  in.xcds = sp.X;
+  in.lds_bytes = k->lds;
+  in.dp_tiles = sp.dp_tiles;
+  in.sk_tiles = sp.sk_tiles;
+  in.workspace_bytes = p->ws_bytes;
+  in.trace_offset = p->trace_off;
+  in.trace_capacity = (d.flags & GEMM_FLAG_TRACE) ? kTraceCap : 0;
+  in.error_offset = (int32_t)p->error_off;
+  *out = p;
+  return GEMM_OK;
+}
+
+int gemm_workspace_bytes(gemm_handle h, size_t *bytes) {
+  if (!h || !bytes) return GEMM_ERR_INVALID_ARG;
+  *bytes = (size_t)h->ws_bytes;
+  return GEMM_OK;
+}
+
+int gemm_plan_get(gemm_handle h, gemm_plan_info *info) {
+  if (!h || !info) return GEMM_ERR_INVALID_ARG;
+  *info = h->info;
+  return GEMM_OK;
+}
+
+int gemm_run(gemm_handle h, const void *A, const void *B, void *C, const float *scale_a,
+             const float *scale_b, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!h) return GEMM_ERR_INVALID_ARG;
+  if (h->info.grid == 0) return GEMM_OK;  // empty output: nothing to compute
+  if (!A || !B || !C) return GEMM_ERR_INVALID_ARG;
+  const bool fp8 = h->d.dtype_ab == GEMM_FP8_E4M3;
+  if (fp8 && (!scale_a || !scale_b)) return GEMM_ERR_INVALID_ARG;
+  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 15) return GEMM_ERR_ALIGNMENT;
+  if (fp8 && (((uintptr_t)scale_a | (uintptr_t)scale_b) & 3)) return GEMM_ERR_ALIGNMENT;
+  if (h->ws_bytes > 0) {
+    if (!workspace || workspace_bytes < (size_t)h->ws_bytes) return GEMM_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 15) return GEMM_ERR_ALIGNMENT;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  KernelArgs a = h->proto;
+  a.A = (const char *)A;
+  a.B = (const char *)B;
+  a.C = (char *)C;
+  a.scale_a = scale_a;
+  a.scale_b = scale_b;
+  if (h->ws_bytes > 0) {
+    char *ws = (char *)workspace;
+    a.partials = (float *)(ws + h->partial_off);
+    a.locks = (int *)(ws + h->lock_off);
+    a.error_word = (int *)(ws + h->error_off);
+    a.trace = h->trace_off >= 0 ? (int *)(ws + h->trace_off) : nullptr;
+    // zero the locks (and the error word and trace, which follow them)
+    const int64_t first = h->lock_off;
+    const int64_t n_ints = (h->ws_bytes - first) / 4;
+    const int threads = 256;
+    const int blocks = (int)cdiv(n_ints, threads);
+    hipLaunchKernelGGL(clear_ints_kernel, dim3(blocks), dim3(threads), 0, s,
+                       (int *)(ws + first), (int)n_ints);
+    if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+  }
+  if (h->k->launch(a, h->info.grid, s) != hipSuccess) return GEMM_ERR_HIP;
+  return GEMM_OK;
+}
+
+int gemm_destroy(gemm_handle h) {
+  if (!h) return GEMM_ERR_INVALID_ARG;
+  delete h;
+  return GEMM_OK;
+}
+
+int gemm_schedule_enumerate(gemm_handle h, gemm_work_item *items, size_t cap, size_t *n_out) {
+  if (!h || !n_out || (cap > 0 && !items)) return GEMM_ERR_INVALID_ARG;
+  const SchedParams &sp = h->proto.sp;
+  size_t n = 0;
+  for (int32_t b = 0; b < sp.P; ++b) {
+    Cursor c;
+    cursor_init(sp, b, c);
+    WorkItem w;
+    int32_t seq = 0;
+    while (cursor_next(sp, c, w)) {
+      if (n < cap) {
+        gemm_work_item &it = items[n];
+        it.worker = b;
+        it.seq = seq;
+        it.tile = (int32_t)w.tile;
+        it.tile_m = w.m;
+        it.tile_n = w.n;
+        it.k_begin = w.kb;
+        it.k_end = w.ke;
+        it.role = w.role;
+      }
+      ++n;
+      ++seq;
+    }
+  }
+  *n_out = n;
+  return n > cap ? GEMM_ERR_CAPACITY : GEMM_OK;
+}
+
+}  // extern "C"

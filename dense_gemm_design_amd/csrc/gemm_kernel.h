@@ -1,0 +1,423 @@
+// Persistent tiled GEMM kernel for gfx950 (MI355X): C = alpha * A x B with MFMA, FP32 accumulate.
+//
+// One workgroup of WGM x WGN waves owns a BM x BN output tile at a time; each wave owns a
+// (BM/WGM) x (BN/WGN) sub-tile of 32 x 32 MFMA blocks held in accumulator registers.  The work
+// list of a workgroup (data-parallel tiles, then Stream-K splits) comes from sched.h.
+//
+// K-loop: an S-stage ring of LDS buffers ("H100 Kernel Design" lesson, sections 4-6).  Stage
+// s = c mod S holds the A and B k-tiles of the workgroup's c-th k-step; the ring runs across
+// work items, so the next tile's first k-tiles are in flight while the current tile finishes.
+//  * Producer phase: every wave issues its share of the stage's 1 KiB buffer loads that write
+//    LDS directly (buffer_load_dwordx4 ... lds), S-1 k-steps ahead of the MFMA.  These play the
+//    part of the pages' TMA copies; lanes whose element lies outside A or B are pointed past the
+//    buffer's end and fill zeros, which handles ragged M, N and K edges.
+//  * FULL(c): each wave waits until its own loads of step c have landed (s_waitcnt vmcnt(n),
+//    n = loads it issued after step c), then all waves meet at s_barrier.  After the barrier every
+//    wave's bytes of step c are in LDS.
+//  * EMPTY(c-1): the same barrier is also the release of stage (c-1) mod S: each wave reached it
+//    only after its MFMAs of step c-1 consumed their ds_read results, so the producer may refill
+//    that stage with step c+S-1 right after the barrier.  The ring position (stage, phase =
+//    floor(c / S) & 1, count = c) lives in scalar registers; the phase is implicit in c.
+//  * Consumer phase: ds_read_b128 of the A and B fragments of the wave's sub-tile, MFMA chain.
+// LDS rows are XOR-swizzled in 16-byte chunks (chunk' = chunk ^ f(row)), the gfx950 counterpart
+// of the pages' 128-byte swizzle ("H100 cuTensorMap" lesson, section 11; "H100 WGMMA part 1",
+// section 11), so that the 32 rows one MFMA operand read touches spread over all LDS banks.
+//
+// Epilogue ("H100 Kernel Design" lesson, section 12): Z = alpha * Acc, cast to the output type,
+// store -- or, for a Stream-K split, the fixup of "H100 Stream-K" lesson section 6: partial sums
+// go through a per-tile FP32 workspace slot guarded by a lock counting the k-tiles already
+// reduced; each split waits until the lock equals its K_idx (deterministic left-to-right order),
+// the final split adds the slot to its accumulators and runs the epilogue.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sched.h"
+
+namespace dg {
+
+typedef __attribute__((address_space(3))) char lds_t;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+enum { DT_BF16 = 0, DT_FP8 = 1 };
+
+// Flags shared with the C ABI (gemm.h).
+enum : uint32_t { KF_TRACE = 0x1u, KF_TEST_SKIP_PUBLISH = 0x100u };
+
+struct KernelArgs {
+  const char *A;           // M x K, row pitch lda_bytes
+  const char *B;           // N x K (K x N column-major), row pitch ldb_bytes
+  char *C;                 // M x N row-major, ldc elements per row
+  const float *scale_a;    // FP8 only
+  const float *scale_b;
+  float *partials;         // Stream-K slots, BM*BN floats each
+  int *locks;              // one per Stream-K slot
+  int *error_word;
+  int *trace;              // 8 ints per record, trace_cap records per workgroup
+  int64_t M, N, K;
+  int64_t lda_bytes, ldb_bytes, ldc;
+  SchedParams sp;
+  int32_t out_bf16;
+  uint32_t flags;
+  int32_t trace_cap;
+  int32_t max_spin;
+};
+
+template <int DT_, int BM_, int BN_, int BK_, int WGM_, int WGN_, int STAGES_, int SWZ_>
+struct TileCfg {
+  static constexpr int DT = DT_, BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
+  static constexpr int STAGES = STAGES_, SWZ = SWZ_;
+  static constexpr int WAVES = WGM * WGN, THREADS = WAVES * 64;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;     // wave sub-tile
+  static constexpr int FM = WM / 32, FN = WN / 32;       // 32 x 32 MFMA blocks per wave
+  static constexpr int EB = DT == DT_BF16 ? 2 : 1;       // bytes per element
+  static constexpr int ROWB = BK * EB;                   // bytes of one tile row in LDS
+  static constexpr int CH = ROWB / 16;                   // 16-byte chunks per row
+  static constexpr int RPL = 1024 / ROWB;                // rows per wave-wide 1 KiB load
+  static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int LA = A_BYTES / 1024 / WAVES;      // loads per wave per stage (A)
+  static constexpr int LB = B_BYTES / 1024 / WAVES;
+  static constexpr int KMFMA = DT == DT_BF16 ? 16 : 64;  // reduction depth of one MFMA
+  static constexpr int KSUB = BK / KMFMA;                // MFMAs along K per k-tile
+  static constexpr int CPL = KMFMA * EB / 32;            // 16-byte chunks per lane per operand
+  static_assert(ROWB == 64 || ROWB == 128, "tile rows must be 64 or 128 bytes");
+  static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "load split");
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert(LA + LB <= 63, "vmcnt range");
+  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS per workgroup");
+  static_assert((32 >> SWZ) % CH == 0, "swizzle must not depend on the 32-row block");
+};
+
+// ---- small device helpers ------------------------------------------------------------------
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait until at most n of this wave's vector-memory operations are outstanding (n <= 3 * L)
+template <int L>
+__device__ __forceinline__ void wait_loads_after(int steps_after) {
+  if (steps_after <= 0) wait_vmcnt<0>();
+  else if (steps_after == 1) wait_vmcnt<L>();
+  else if (steps_after == 2) wait_vmcnt<(2 * L > 63 ? 63 : 2 * L)>();
+  else wait_vmcnt<(3 * L > 63 ? 63 : 3 * L)>();
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *base, int64_t bytes) {
+  const int32_t n = bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0 : (int32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, n, 0x00020000);
+}
+
+constexpr uint32_t kOOB = 0x80000000u;  // any offset >= num_records reads as zero
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+template <class CFG>
+__device__ __forceinline__ f32x16 mfma(const i32x4 *b, const i32x4 *a, const f32x16 &c) {
+  if constexpr (CFG::DT == DT_BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b[0]),
+                                                   __builtin_bit_cast(bf16x8, a[0]), c, 0, 0, 0);
+  } else {
+    i32x8 bb = {b[0][0], b[0][1], b[0][2], b[0][3], b[1][0], b[1][1], b[1][2], b[1][3]};
+    i32x8 aa = {a[0][0], a[0][1], a[0][2], a[0][3], a[1][0], a[1][1], a[1][2], a[1][3]};
+    // operand formats 0 = e4m3 for both; zero scale operands select the unscaled instruction
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bb, aa, c, 0, 0, 0, 0, 0, 0);
+  }
+}
+
+// ---- the kernel ------------------------------------------------------------------------------
+
+// Producer side of the ring: the cursor of the next k-tile to load (uniform) and the lane's byte
+// offsets inside a tile (one register per 1 KiB load, fixed for the whole kernel).
+template <class CFG>
+struct Producer {
+  Cursor cur;
+  int32_t valid, k, ke, rows_a, rows_b;
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t va[CFG::LA], vb[CFG::LB];
+
+  // row of tile and 16-byte chunk along K that `lane` fills in load j of `wave`
+  static __device__ __forceinline__ int load_row(int j, int wave, int lane) {
+    return (j * CFG::WAVES + wave) * CFG::RPL + lane / CFG::CH;
+  }
+  static __device__ __forceinline__ int load_chunk(int row, int lane) {
+    return (lane % CFG::CH) ^ ((row >> CFG::SWZ) & (CFG::CH - 1));
+  }
+
+  __device__ __forceinline__ void init(const KernelArgs &args, int32_t b, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < CFG::LA; ++j) {
+      const int row = load_row(j, wave, lane);
+      va[j] = (uint32_t)(row * (uint32_t)args.lda_bytes + load_chunk(row, lane) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < CFG::LB; ++j) {
+      const int row = load_row(j, wave, lane);
+      vb[j] = (uint32_t)(row * (uint32_t)args.ldb_bytes + load_chunk(row, lane) * 16);
+    }
+    cursor_init(args.sp, b, cur);
+    next_item(args);
+  }
+
+  __device__ __forceinline__ void next_item(const KernelArgs &args) {
+    WorkItem w;
+    // items without k-tiles (K == 0) load nothing
+    while ((valid = cursor_next(args.sp, cur, w)) && w.kb == w.ke) {
+    }
+    if (valid) {
+      k = w.kb;
+      ke = w.ke;
+      const int64_t m0 = (int64_t)w.m * CFG::BM, n0 = (int64_t)w.n * CFG::BN;
+      rows_a = (int32_t)(args.M - m0 < CFG::BM ? args.M - m0 : CFG::BM);
+      rows_b = (int32_t)(args.N - n0 < CFG::BN ? args.N - n0 : CFG::BN);
+      ra = make_rsrc(args.A + m0 * args.lda_bytes, (int64_t)rows_a * args.lda_bytes);
+      rb = make_rsrc(args.B + n0 * args.ldb_bytes, (int64_t)rows_b * args.ldb_bytes);
+    }
+  }
+
+  // Issue the loads of k-tile k into `stage`, then advance (possibly to the next work item).
+  __device__ __forceinline__ void issue(const KernelArgs &args, lds_t *smem, int stage, int wave,
+                                        int lane) {
+    const uint32_t kbytes = (uint32_t)k * CFG::ROWB;
+    lds_t *sa = smem + stage * CFG::STAGE_BYTES;
+    lds_t *sb = sa + CFG::A_BYTES;
+    const bool edge = rows_a < CFG::BM || rows_b < CFG::BN ||
+                      (int64_t)(k + 1) * CFG::ROWB > args.K * CFG::EB;
+    if (!edge) {
+#pragma unroll
+      for (int j = 0; j < CFG::LA; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, sa + (j * CFG::WAVES + wave) * 1024, 16,
+                                                 va[j] + kbytes, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < CFG::LB; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, sb + (j * CFG::WAVES + wave) * 1024, 16,
+                                                 vb[j] + kbytes, 0, 0, 0);
+    } else {
+      // ragged tile: rows past M (N) and chunks past K read as zero
+      const uint32_t klimit = (uint32_t)(args.K * CFG::EB) - kbytes;
+#pragma unroll
+      for (int j = 0; j < CFG::LA; ++j) {
+        const int row = load_row(j, wave, lane);
+        const bool ok = row < rows_a && (uint32_t)(load_chunk(row, lane) * 16) < klimit;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, sa + (j * CFG::WAVES + wave) * 1024, 16,
+                                                 ok ? va[j] + kbytes : kOOB, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < CFG::LB; ++j) {
+        const int row = load_row(j, wave, lane);
+        const bool ok = row < rows_b && (uint32_t)(load_chunk(row, lane) * 16) < klimit;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, sb + (j * CFG::WAVES + wave) * 1024, 16,
+                                                 ok ? vb[j] + kbytes : kOOB, 0, 0, 0);
+      }
+    }
+    if (++k == ke) next_item(args);
+  }
+};
+
+template <class CFG>
+__device__ __forceinline__ void compute_stage(const lds_t *smem, int stage,
+                                              const uint32_t (&aoff)[CFG::KSUB][CFG::CPL],
+                                              const uint32_t (&boff)[CFG::KSUB][CFG::CPL],
+                                              f32x16 (&acc)[CFG::FM][CFG::FN]) {
+  const lds_t *base = smem + stage * CFG::STAGE_BYTES;
+#pragma unroll
+  for (int s = 0; s < CFG::KSUB; ++s) {
+    i32x4 a[CFG::FM][CFG::CPL], b[CFG::FN][CFG::CPL];
+#pragma unroll
+    for (int f = 0; f < CFG::FM; ++f)
+#pragma unroll
+      for (int h = 0; h < CFG::CPL; ++h)
+        a[f][h] = *(const i32x4 __attribute__((address_space(3))) *)(base + aoff[s][h] +
+                                                                      f * 32 * CFG::ROWB);
+#pragma unroll
+    for (int g = 0; g < CFG::FN; ++g)
+#pragma unroll
+      for (int h = 0; h < CFG::CPL; ++h)
+        b[g][h] = *(const i32x4 __attribute__((address_space(3))) *)(base + boff[s][h] +
+                                                                      g * 32 * CFG::ROWB);
+#pragma unroll
+    for (int f = 0; f < CFG::FM; ++f)
+#pragma unroll
+      for (int g = 0; g < CFG::FN; ++g) acc[f][g] = mfma<CFG>(b[g], a[f], acc[f][g]);
+  }
+}
+
+// Spin (one lane) until *lock == want, at most max_spin polls; returns false on expiry.
+__device__ __forceinline__ bool wait_lock(int *lock, int want, int max_spin) {
+  for (int i = 0; i < max_spin; ++i) {
+    if (__hip_atomic_load(lock, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want) return true;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return false;
+}
+
+// Epilogue of one work item, one accumulator quad (4 consecutive n of one row m) at a time:
+//   whole tile / final split: C = alpha * (slot + acc) cast to the output type (slot only when
+//   the tile was split); first / middle split: slot = (slot +) acc.
+// The accumulators are only read here, never rewritten.
+template <class CFG>
+__device__ __forceinline__ void epilogue(const KernelArgs &args, const WorkItem &w,
+                                         const f32x16 (&acc)[CFG::FM][CFG::FN], float alpha,
+                                         int wm, int wn, int tid) {
+  const int lane = tid & 63;
+  const bool add_slot = w.role == ROLE_MIDDLE || w.role == ROLE_LAST;
+  const bool to_slot = w.role == ROLE_FIRST || w.role == ROLE_MIDDLE;
+  f32x4 *slot = (f32x4 *)(args.partials + (int64_t)(w.sk_slot < 0 ? 0 : w.sk_slot) * CFG::BM *
+                                              CFG::BN) + tid;
+  const int64_t mbase = (int64_t)w.m * CFG::BM + wm * CFG::WM + (lane & 31);
+  const int64_t nbase = (int64_t)w.n * CFG::BN + wn * CFG::WN + (lane >> 5) * 4;
+#pragma unroll
+  for (int f = 0; f < CFG::FM; ++f) {
+    const int64_t m = mbase + f * 32;
+#pragma unroll
+    for (int g = 0; g < CFG::FN; ++g) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int qi = (f * CFG::FN + g) * 4 + q;  // slot layout: quad-major, lane-minor
+        f32x4 v = {acc[f][g][4 * q + 0], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2],
+                   acc[f][g][4 * q + 3]};
+        if (add_slot) {
+          const f32x4 p = slot[qi * CFG::THREADS];
+          v = p + v;
+        }
+        if (to_slot) {
+          slot[qi * CFG::THREADS] = v;
+          continue;
+        }
+        const int64_t n = nbase + g * 32 + q * 8;
+        if (m >= args.M || n >= args.N) continue;
+        v = v * alpha;
+        if (args.out_bf16) {
+          u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *(u32x2 *)(args.C + (m * args.ldc + n) * 2) = pk;
+        } else {
+          *(f32x4 *)(args.C + (m * args.ldc + n) * 4) = v;
+        }
+      }
+    }
+  }
+}
+
+template <class CFG>
+__global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::THREADS),
+                               amdgpu_waves_per_eu(1, 1)))
+gemm_kernel(KernelArgs args) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[CFG::LDS_BYTES];
+  lds_t *smem = (lds_t *)(size_t)(uint32_t)(size_t)(lds_t *)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / CFG::WGN, wn = wave % CFG::WGN;
+  const int32_t b = blockIdx.x;
+
+  float alpha = 1.0f;
+  if constexpr (CFG::DT == DT_FP8) alpha = (*args.scale_a) * (*args.scale_b);
+
+  // Per-lane LDS read offsets of the MFMA operands (bytes within a stage).
+  uint32_t aoff[CFG::KSUB][CFG::CPL], boff[CFG::KSUB][CFG::CPL];
+  {
+    const int r = lane & 31;
+    const int swz = (r >> CFG::SWZ) & (CFG::CH - 1);
+#pragma unroll
+    for (int s = 0; s < CFG::KSUB; ++s)
+#pragma unroll
+      for (int h = 0; h < CFG::CPL; ++h) {
+        const int chunk = (s * 2 + (lane >> 5)) * CFG::CPL + h;
+        const uint32_t in_row = (uint32_t)((chunk ^ swz) * 16);
+        aoff[s][h] = (uint32_t)((wm * CFG::WM + r) * CFG::ROWB) + in_row;
+        boff[s][h] = (uint32_t)(CFG::A_BYTES + (wn * CFG::WN + r) * CFG::ROWB) + in_row;
+      }
+  }
+
+  Producer<CFG> prod;
+  prod.init(args, b, wave, lane);
+
+  Cursor ccur;
+  cursor_init(args.sp, b, ccur);
+  WorkItem cw;
+  bool cvalid = cursor_next(args.sp, ccur, cw);
+
+  // Prologue: fill S-1 stages.
+  int issued = 0;
+#pragma unroll
+  for (int s = 0; s < CFG::STAGES - 1; ++s)
+    if (prod.valid) {
+      prod.issue(args, smem, s, wave, lane);
+      ++issued;
+    }
+
+  int c = 0;  // k-steps consumed by this workgroup (ring count; stage = c % S)
+  int seq = 0;
+  while (cvalid) {
+    if ((args.flags & KF_TRACE) && tid == 0 && seq < args.trace_cap) {
+      int *t = args.trace + ((int64_t)b * args.trace_cap + seq) * 8;
+      t[0] = b; t[1] = seq; t[2] = cw.tile; t[3] = cw.m;
+      t[4] = cw.n; t[5] = cw.kb; t[6] = cw.ke; t[7] = cw.role;
+    }
+    f32x16 acc[CFG::FM][CFG::FN];
+#pragma unroll
+    for (int f = 0; f < CFG::FM; ++f)
+#pragma unroll
+      for (int g = 0; g < CFG::FN; ++g)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.0f;
+
+    for (int k = cw.kb; k < cw.ke; ++k, ++c) {
+      // FULL(c): own loads of step c landed, then everyone's; also EMPTY(c-1).
+      wait_loads_after<CFG::LA + CFG::LB>(issued - c - 1);
+      lds_barrier();
+      if (prod.valid) {
+        prod.issue(args, smem, (c + CFG::STAGES - 1) % CFG::STAGES, wave, lane);
+        ++issued;
+      }
+      compute_stage<CFG>(smem, c % CFG::STAGES, aoff, boff, acc);
+    }
+
+    // ---- Stream-K fixup handshake around the epilogue ----
+    if (cw.role == ROLE_MIDDLE || cw.role == ROLE_LAST) {
+      // wait until the k-tiles before K_idx have been reduced into the slot
+      if (tid == 0 && !wait_lock(args.locks + cw.sk_slot, cw.kb, args.max_spin))
+        __hip_atomic_store(args.error_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lds_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid);
+    if (cw.role == ROLE_FIRST || cw.role == ROLE_MIDDLE) {
+      // publish: the slot now holds k-tiles [0, K_idx + count)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      lds_barrier();
+      const bool skip =
+          (args.flags & KF_TEST_SKIP_PUBLISH) && cw.sk_slot == 0 && cw.role == ROLE_FIRST;
+      if (tid == 0 && !skip)
+        __hip_atomic_store(args.locks + cw.sk_slot, cw.ke, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    ++seq;
+    cvalid = cursor_next(args.sp, ccur, cw);
+  }
+  wait_vmcnt<0>();
+}
+
+// Clears the Stream-K locks and the error word before a run.
+__global__ void clear_ints_kernel(int *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+}  // namespace dg

@@ -1,0 +1,151 @@
+// Tile scheduler of the dense GEMM: the mapping F(i) -> (m, n), the assignment of linear tasks to
+// workgroups (static, persistent, Stream-K hybrid) and the MI355X XCD remap.  Compiled for host
+// and device: the kernel walks its work with it, and gemm_schedule_enumerate() replays the same
+// code on the CPU.
+//
+// Sources:
+//  * "DeepGEMM on SM90" page, CTA <-> output tile section and its mapping-family table: F(i) names
+//    the output tile of the i-th linear task; Linear N-fast, Linear M-fast, Grouped-M strip
+//    (M cut into strips of G tile-rows, M-fast inside), Grouped-N strip (the transpose).
+//    Persistence is not a mapping: a persistent worker p takes i = p, p + P, p + 2P, ...
+//  * "H100 Kernel Design" lesson, sections 9-10 (persistent grid-stride loop, Stream-K hybrid:
+//    data-parallel full waves, Stream-K only for a tail wave at most half full, backward tile
+//    iteration) and "H100 Stream-K" lesson, sections 2-6 (a unit's share of one tile is a split
+//    tracked by K_idx, k_tile_count and is_final = K_idx + k_tile_count == k-tiles per tile).
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__) || defined(__HIP__)
+#define DG_HD __host__ __device__ __forceinline__
+#else
+#define DG_HD inline
+#endif
+
+namespace dg {
+
+enum Mapping { MAP_LINEAR_N = 0, MAP_LINEAR_M = 1, MAP_GROUPED_M = 2, MAP_GROUPED_N = 3 };
+enum Role { ROLE_WHOLE = 0, ROLE_FIRST = 1, ROLE_MIDDLE = 2, ROLE_LAST = 3 };
+
+struct SchedParams {
+  int32_t Mt, Nt, Kt;      // tiles along M and N, k-tiles along K
+  int32_t mapping, G;      // F(i) family and strip width
+  int32_t P;               // workgroups in the launch (workers)
+  int32_t X;               // XCDs the workgroups are dealt to round-robin (1 = no remap)
+  int32_t pad_;
+  int32_t dp_tiles;        // tasks i < dp_tiles run whole (data parallel)
+  int32_t sk_tiles;        // the next sk_tiles tasks are split along K (Stream-K band)
+};
+
+struct WorkItem {
+  int32_t tile;            // linear task i
+  int32_t m, n;            // F(i)
+  int32_t kb, ke;          // k-tiles [kb, ke) of the tile
+  int32_t role;
+  int32_t sk_slot;         // i - dp_tiles for a split tile (workspace slot), else -1
+};
+
+struct TileMN {
+  int32_t m, n;
+};
+
+// F(i) -> (m, n).  Grouped-M: a strip holds G tile-rows (fewer in a short last strip) and is
+// walked column by column, M-fast inside: i = strip * (G * Nt) + n * g + (m - strip * G).
+// Task indices fit in 32 bits (the planner rejects larger grids).
+DG_HD TileMN map_tile(int32_t mapping, int32_t G, int32_t Mt, int32_t Nt, int32_t i) {
+  TileMN t;
+  if (mapping == MAP_LINEAR_N) {
+    t.m = i / Nt;
+    t.n = i - t.m * Nt;
+  } else if (mapping == MAP_LINEAR_M) {
+    t.n = i / Mt;
+    t.m = i - t.n * Mt;
+  } else if (mapping == MAP_GROUPED_M) {
+    const int32_t per_strip = G * Nt;
+    const int32_t strip = i / per_strip;
+    const int32_t j = i - strip * per_strip;
+    const int32_t rows_left = Mt - strip * G;
+    const int32_t g = rows_left < G ? rows_left : G;
+    t.n = j / g;
+    t.m = strip * G + (j - t.n * g);
+  } else {  // MAP_GROUPED_N
+    const int32_t per_strip = G * Mt;
+    const int32_t strip = i / per_strip;
+    const int32_t j = i - strip * per_strip;
+    const int32_t cols_left = Nt - strip * G;
+    const int32_t g = cols_left < G ? cols_left : G;
+    t.m = j / g;
+    t.n = strip * G + (j - t.m * g);
+  }
+  return t;
+}
+
+// Worker id of workgroup b.  Workgroups are dealt to the X XCDs round-robin (b mod X), each XCD
+// with its own L2; giving XCD x the worker ids x*P/X ... x*P/X + P/X - 1 keeps the tiles that
+// consecutive ids take -- which share A and B bands under a grouped mapping -- on one L2.
+DG_HD int32_t xcd_worker(int32_t b, int32_t P, int32_t X) {
+  if (X <= 1 || P % X != 0) return b;
+  return (b % X) * (P / X) + b / X;
+}
+
+// Cursor over one workgroup's work: its data-parallel tiles first, then its Stream-K splits from
+// the last tile it touches back to the first.
+struct Cursor {
+  int32_t next_dp;         // next data-parallel task
+  int32_t sk_lo, sk_hi;    // remaining Stream-K iterations [sk_lo, sk_hi), consumed from the top
+};
+
+DG_HD void cursor_init(const SchedParams &sp, int32_t b, Cursor &c) {
+  c.next_dp = xcd_worker(b, sp.P, sp.X);
+  if (sp.sk_tiles > 0) {
+    // unit b owns iterations [floor(b T / P), floor((b+1) T / P)) of the band of T iterations
+    const int64_t T = sp.sk_tiles * (int64_t)sp.Kt;
+    c.sk_lo = (int32_t)((int64_t)b * T / sp.P);
+    c.sk_hi = (int32_t)((int64_t)(b + 1) * T / sp.P);
+  } else {
+    c.sk_lo = c.sk_hi = 0;
+  }
+}
+
+DG_HD bool cursor_next(const SchedParams &sp, Cursor &c, WorkItem &w) {
+  if (c.next_dp < sp.dp_tiles) {
+    w.tile = c.next_dp;
+    c.next_dp += sp.P;
+    w.kb = 0;
+    w.ke = sp.Kt;
+    w.role = ROLE_WHOLE;
+    w.sk_slot = -1;
+  } else if (c.sk_hi > c.sk_lo) {
+    const int32_t last = c.sk_hi - 1;
+    const int32_t t = last / sp.Kt;                 // band-local tile of the top iteration
+    const int32_t t_first = t * sp.Kt;
+    const int32_t start = c.sk_lo > t_first ? c.sk_lo : t_first;
+    w.tile = sp.dp_tiles + t;
+    w.kb = start - t_first;
+    w.ke = c.sk_hi - t_first;
+    c.sk_hi = start;
+    const bool first = w.kb == 0, final = w.ke == sp.Kt;
+    w.role = first ? (final ? ROLE_WHOLE : ROLE_FIRST) : (final ? ROLE_LAST : ROLE_MIDDLE);
+    w.sk_slot = t;
+  } else {
+    return false;
+  }
+  const TileMN mn = map_tile(sp.mapping, sp.G, sp.Mt, sp.Nt, w.tile);
+  w.m = mn.m;
+  w.n = mn.n;
+  return true;
+}
+
+// Hybrid rule: with P workers and `tiles` tasks, the full waves stay data parallel; the tail
+// wave goes to Stream-K only when it is at most half full, otherwise everything is data parallel.
+DG_HD void streamk_plan(int64_t tiles, int32_t P, int32_t &dp_tiles, int32_t &sk_tiles) {
+  const int64_t full = tiles / P, tail = tiles % P;
+  if (tail == 0 || tail * 2 > P) {
+    dp_tiles = (int32_t)tiles;
+    sk_tiles = 0;
+  } else {
+    dp_tiles = (int32_t)(full * P);
+    sk_tiles = (int32_t)tail;
+  }
+}
+
+}  // namespace dg

@@ -1,0 +1,152 @@
+/*
+ * dense_gemm_design_amd -- C ABI of the tiled dense GEMM for MI355X (gfx950).
+ *
+ *   C = alpha * (A x B),  alpha = scale_a * scale_b for FP8 operands, 1 for BF16.
+ *
+ * The operation is the plain matrix product ("DeepGEMM on SM90" page, CTA <-> output tile
+ * section: C[m, n] is the sum over k of A[m, k] B[k, n]) in BF16, or in FP8 e4m3 with one FP32
+ * scale per tensor ("WGMMA part 2" lesson, section 11, tensor-wise scaling), accumulated in FP32
+ * ("WGMMA part 2" lesson, section 14).  The fused epilogue applies alpha and casts to the output
+ * type ("H100 Kernel Design" lesson, section 12: Z = alpha * Acc, then cast and store).  The work
+ * is cut into BM x BN output tiles and BK-deep k-tiles, ordered by a tile mapping F(i) -> (m, n)
+ * and handed to workgroups by a static, persistent or Stream-K scheduler ("DeepGEMM on SM90" page,
+ * mapping table; "H100 Kernel Design" lesson, sections 9-10; "H100 Stream-K" lesson).
+ *
+ * Conventions
+ *  - Every function returns a gemm_status (0 = success) and never prints or aborts.
+ *  - Argument and plan errors are reported synchronously, before anything is enqueued.
+ *  - Pointers passed to gemm_run are DEVICE pointers owned by the caller (A, B, C, the scales and
+ *    the workspace); the library never allocates device memory.  The handle owns only host state.
+ *  - gemm_run is asynchronous: it enqueues work on `stream` (a hipStream_t, NULL = the default
+ *    stream) and returns; device faults surface at the caller's next synchronisation.
+ *  - A handle is immutable after gemm_create; concurrent gemm_run calls on one handle are allowed
+ *    if each uses its own workspace.
+ */
+#ifndef DENSE_GEMM_DESIGN_AMD_GEMM_H
+#define DENSE_GEMM_DESIGN_AMD_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GEMM_OK = 0,
+  GEMM_ERR_INVALID_ARG = -1,  /* bad enum, non-positive size, NULL handle/pointer ...        */
+  GEMM_ERR_UNSUPPORTED = -2,  /* well-formed but outside what the kernels implement          */
+  GEMM_ERR_ALIGNMENT = -3,    /* a device pointer is not 16-byte aligned                      */
+  GEMM_ERR_WORKSPACE = -4,    /* workspace missing or smaller than gemm_workspace_bytes()     */
+  GEMM_ERR_HIP = -5,          /* a HIP runtime call failed (no device, launch failure ...)    */
+  GEMM_ERR_CAPACITY = -6      /* a buffer passed to the library is too small for the result   */
+} gemm_status;
+
+typedef enum { GEMM_BF16 = 0, GEMM_FP8_E4M3 = 1, GEMM_F32 = 2 } gemm_dtype;
+typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout;
+
+/* Tile mapping F(i) -> (m, n) ("DeepGEMM on SM90" page, mapping-family table). */
+typedef enum {
+  GEMM_MAP_LINEAR_N = 0,   /* C00, C01, ..., C10, ...  (m = i / Nt, n = i % Nt)               */
+  GEMM_MAP_LINEAR_M = 1,   /* C00, C10, ..., C01, ...  (m = i % Mt, n = i / Mt)               */
+  GEMM_MAP_GROUPED_M = 2,  /* strips of G tile-rows, M-fast inside a strip                    */
+  GEMM_MAP_GROUPED_N = 3   /* strips of G tile-columns, N-fast inside a strip                 */
+} gemm_mapping;
+
+/* Assignment of tasks to workgroups ("H100 Kernel Design" lesson, sections 9.2-10.3). */
+typedef enum {
+  GEMM_SCHED_STATIC = 0,      /* one workgroup per output tile, grid = tile count              */
+  GEMM_SCHED_PERSISTENT = 1,  /* P resident workgroups, worker p takes tiles p, p + P, ...     */
+  GEMM_SCHED_STREAMK = 2,     /* persistent data-parallel waves + Stream-K tail (<= half wave) */
+  GEMM_SCHED_AUTO = 3         /* the planner picks one of the above                           */
+} gemm_sched;
+
+/* flags */
+#define GEMM_FLAG_TRACE 0x1u         /* kernel records every work item it runs in the workspace  */
+#define GEMM_FLAG_NO_XCD_REMAP 0x2u  /* keep worker id = workgroup id (no XCD-contiguous remap)  */
+#define GEMM_FLAG_TEST_SKIP_PUBLISH 0x100u /* test only: the first Stream-K split of slot 0 does
+                                              not publish its lock, so its successor's bounded
+                                              wait expires and reports GEMM_DEVICE_ERR_SPIN      */
+
+/* Problem description.  0 in an "auto" field lets the planner choose. */
+typedef struct gemm_desc {
+  int64_t M, N, K;           /* C is M x N, the reduction is over K (all >= 0; M or N == 0 is an
+                                empty product and gemm_run does nothing; K == 0 writes C = 0)   */
+  int32_t dtype_ab;          /* GEMM_BF16 or GEMM_FP8_E4M3                                      */
+  int32_t dtype_c;           /* GEMM_F32 or GEMM_BF16                                           */
+  int32_t layout_a;          /* must be GEMM_ROW_MAJOR: a(m,k) at A[m*K + k]                    */
+  int32_t layout_b;          /* must be GEMM_COL_MAJOR: b(k,n) at B[n*K + k]                    */
+  int32_t mapping;           /* gemm_mapping                                                     */
+  int32_t group;             /* G for the grouped mappings (>= 1); ignored by the linear ones   */
+  int32_t sched;             /* gemm_sched                                                       */
+  int32_t num_workers;       /* P for persistent / Stream-K; 0 = CUs x resident workgroups/CU    */
+  int32_t bm, bn, bk;        /* tile shape; 0 = auto.  Supported: see gemm_create              */
+  uint32_t flags;            /* GEMM_FLAG_*                                                      */
+} gemm_desc;
+
+/* One unit of work as the scheduler hands it out (gemm_schedule_enumerate, device trace). */
+typedef struct gemm_work_item {
+  int32_t worker;            /* workgroup index in the launch                                   */
+  int32_t seq;               /* position in that workgroup's processing order                   */
+  int32_t tile;              /* linear task i                                                    */
+  int32_t tile_m, tile_n;    /* F(i)                                                             */
+  int32_t k_begin, k_end;    /* k-tiles [k_begin, k_end) of the tile (K_idx, K_idx + count)     */
+  int32_t role;              /* 0 whole tile, 1 first split, 2 middle split, 3 final split      */
+} gemm_work_item;
+
+/* What the planner chose (read-only view of a handle). */
+typedef struct gemm_plan_info {
+  int32_t bm, bn, bk, stages;
+  int32_t threads, grid;     /* workgroup size and launch grid                                  */
+  int32_t mt, nt, kt;        /* tile counts                                                      */
+  int32_t sched;             /* resolved scheduler (never AUTO)                                  */
+  int32_t xcds;              /* XCD count used by the remap (1 = no remap)                      */
+  int32_t lds_bytes;         /* LDS per workgroup                                                */
+  int64_t dp_tiles, sk_tiles;
+  int64_t workspace_bytes;
+  int64_t trace_offset;      /* byte offset of the trace records in the workspace (-1: none)    */
+  int32_t trace_capacity;    /* records per workgroup                                            */
+  int32_t error_offset;      /* byte offset of the device error word in the workspace (-1: none)*/
+} gemm_plan_info;
+
+/* device error word values (read back from the workspace after a run) */
+#define GEMM_DEVICE_OK 0
+#define GEMM_DEVICE_ERR_SPIN 1       /* a Stream-K lock wait hit its spin limit                 */
+
+typedef struct gemm_plan *gemm_handle;
+
+/* Validates the description and builds a plan.  Supported in this version:
+ *   dtype_ab BF16 with tiles (bm, bn, bk) in {(256,256,64), (128,128,64)},
+ *   dtype_ab FP8_E4M3 with tiles in {(256,256,128), (128,128,128)};
+ *   layout_a ROW and layout_b COL (both operands K-contiguous);
+ *   K * sizeof(element) a multiple of 16 bytes; N a multiple of 8;
+ *   M, N arbitrary otherwise (ragged tiles are masked), K ragged in the last k-tile.
+ * Needs a visible GPU only when num_workers == 0 (it then queries the CU count). */
+int gemm_create(const gemm_desc *desc, gemm_handle *out);
+
+/* Device bytes the caller must pass to gemm_run as workspace (0 when none is needed). */
+int gemm_workspace_bytes(gemm_handle h, size_t *bytes);
+
+int gemm_plan_get(gemm_handle h, gemm_plan_info *info);
+
+/* Enqueues C = alpha * A x B on `stream`.  A: M x K row-major, B: K x N column-major, C: M x N
+ * row-major of dtype_c.  scale_a / scale_b: device pointers to one float each for FP8 (required),
+ * ignored for BF16 (may be NULL).  workspace: device memory of at least gemm_workspace_bytes(),
+ * 16-byte aligned; the library clears the parts it needs at the start of every run. */
+int gemm_run(gemm_handle h, const void *A, const void *B, void *C, const float *scale_a,
+             const float *scale_b, void *workspace, size_t workspace_bytes, void *stream);
+
+int gemm_destroy(gemm_handle h);
+
+/* CPU replay of the plan's schedule: writes up to `cap` items (grouped by worker, each worker's
+ * items in processing order) and the total count to *n_out.  Returns GEMM_ERR_CAPACITY (with
+ * *n_out set) when cap is too small. */
+int gemm_schedule_enumerate(gemm_handle h, gemm_work_item *items, size_t cap, size_t *n_out);
+
+/* Static string for a gemm_status value. */
+const char *gemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -164,6 +164,8 @@ def enumerate_schedule(M, N, K, BM, BN, BK, mapping, G, sched, P=None, X=8, xcd_
         dp_tiles, sk_tiles = tiles, 0
     elif sched == STREAMK:
         dp_tiles, sk_tiles = streamk_split_plan(tiles, P)
+        if Kt == 0:                       # an empty reduction has nothing to split
+            dp_tiles, sk_tiles = tiles, 0
     else:
         raise ValueError(f"unknown scheduler {sched}")
     ids = xcd_worker_ids(P, X) if xcd_remap else list(range(P))

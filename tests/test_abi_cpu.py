@@ -1,0 +1,163 @@
+"""The C-ABI library loads, exports what include/gemm.h declares, and rejects bad input before
+enqueueing anything.  No compute call is made here: these run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_design_amd as dg
+from dense_gemm_design_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "gemm.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s*(gemm_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = L.load()
+    names = header_functions()
+    assert names, "no declarations found"
+    assert set(names) == set(L.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_struct_layouts_match_c_compiler(tmp_path):
+    """sizeof and every field offset of the ctypes mirrors equal what a C compiler sees."""
+    import subprocess
+    structs = {"gemm_desc": L.GemmDesc, "gemm_work_item": L.GemmWorkItem,
+               "gemm_plan_info": L.GemmPlanInfo}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "gemm.h"', 'int main(void){']
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'printf("{cname}.{fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)],
+                   check=True)
+    out = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True,
+                                                        text=True, check=True).stdout.splitlines())
+    for cname, py in structs.items():
+        assert int(out[cname]) == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert int(out[f"{cname}.{fname}"]) == getattr(py, fname).offset, (cname, fname)
+
+
+def test_status_strings():
+    lib = L.load()
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.gemm_status_string(st).decode() not in ("", "unknown status")
+    assert lib.gemm_status_string(12345).decode() == "unknown status"
+
+
+def create(**kw):
+    base = dict(M=512, N=512, K=512, sched=L.GEMM_SCHED_PERSISTENT, num_workers=8)
+    base.update(kw)
+    lib = L.load()
+    h = ctypes.c_void_p()
+    st = lib.gemm_create(ctypes.byref(L.make_desc(**base)), ctypes.byref(h))
+    if st == 0:
+        lib.gemm_destroy(h)
+    return st
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(M=-1), L.GEMM_ERR_INVALID_ARG),
+    (dict(N=-8), L.GEMM_ERR_INVALID_ARG),
+    (dict(K=-16), L.GEMM_ERR_INVALID_ARG),
+    (dict(M=0), L.GEMM_OK),
+    (dict(N=0), L.GEMM_OK),
+    (dict(K=0), L.GEMM_OK),
+    (dict(dtype_ab=7), L.GEMM_ERR_INVALID_ARG),
+    (dict(dtype_ab=L.GEMM_F32), L.GEMM_ERR_INVALID_ARG),
+    (dict(dtype_c=9), L.GEMM_ERR_INVALID_ARG),
+    (dict(mapping=4), L.GEMM_ERR_INVALID_ARG),
+    (dict(mapping=L.GEMM_MAP_GROUPED_M, group=0), L.GEMM_ERR_INVALID_ARG),
+    (dict(sched=9), L.GEMM_ERR_INVALID_ARG),
+    (dict(num_workers=-1), L.GEMM_ERR_INVALID_ARG),
+    (dict(flags=0x40), L.GEMM_ERR_INVALID_ARG),
+    (dict(layout_a=3), L.GEMM_ERR_INVALID_ARG),
+    (dict(layout_a=L.GEMM_COL_MAJOR), L.GEMM_ERR_UNSUPPORTED),
+    (dict(layout_b=L.GEMM_ROW_MAJOR), L.GEMM_ERR_UNSUPPORTED),
+    (dict(K=100), L.GEMM_ERR_UNSUPPORTED),            # 200-byte rows: not a multiple of 16
+    (dict(N=100), L.GEMM_ERR_UNSUPPORTED),            # output rows must be 8-element multiples
+    (dict(bm=64, bn=64), L.GEMM_ERR_UNSUPPORTED),     # no such tile kernel
+    (dict(bm=256, bn=256, bk=32), L.GEMM_ERR_UNSUPPORTED),
+    (dict(dtype_ab=L.GEMM_FP8_E4M3, K=8), L.GEMM_ERR_UNSUPPORTED),
+    (dict(), L.GEMM_OK),
+    (dict(K=104), L.GEMM_OK),                         # ragged K (multiple of 8 bf16 elements)
+    (dict(M=300, N=264), L.GEMM_OK),                  # ragged M and N
+    (dict(dtype_ab=L.GEMM_FP8_E4M3, K=272, bm=128, bn=128), L.GEMM_OK),
+])
+def test_create_validation(kw, want):
+    assert create(**kw) == want
+
+
+def test_null_arguments():
+    lib = L.load()
+    h = ctypes.c_void_p()
+    assert lib.gemm_create(None, ctypes.byref(h)) == L.GEMM_ERR_INVALID_ARG
+    assert lib.gemm_create(ctypes.byref(L.make_desc(64, 64, 64, num_workers=1)), None) \
+        == L.GEMM_ERR_INVALID_ARG
+    assert lib.gemm_destroy(None) == L.GEMM_ERR_INVALID_ARG
+    n = ctypes.c_size_t()
+    assert lib.gemm_workspace_bytes(None, ctypes.byref(n)) == L.GEMM_ERR_INVALID_ARG
+    assert lib.gemm_schedule_enumerate(None, None, 0, ctypes.byref(n)) == L.GEMM_ERR_INVALID_ARG
+
+
+def test_plan_info_and_workspace():
+    p = L.Plan(L.make_desc(512, 512, 65536, sched=L.GEMM_SCHED_STREAMK, num_workers=256,
+                           bm=128, bn=128))
+    i = p.info
+    assert (i.bm, i.bn, i.bk, i.mt, i.nt, i.kt) == (128, 128, 64, 4, 4, 1024)
+    assert (i.dp_tiles, i.sk_tiles, i.grid, i.sched) == (0, 16, 256, L.GEMM_SCHED_STREAMK)
+    # 16 partial tiles of 128 x 128 fp32, then 16 locks, then the error word
+    assert p.workspace_bytes >= 16 * 128 * 128 * 4 + 16 * 4 + 4
+    assert i.error_offset >= 16 * 128 * 128 * 4 + 16 * 4
+    q = L.Plan(L.make_desc(4096, 4096, 4096, sched=L.GEMM_SCHED_PERSISTENT, num_workers=256,
+                           mapping=L.GEMM_MAP_GROUPED_M, group=8))
+    assert q.workspace_bytes == 0 and q.info.bm == 256 and q.info.grid == 256
+    s = L.Plan(L.make_desc(256, 256, 256, sched=L.GEMM_SCHED_STATIC, bm=128, bn=128))
+    assert s.info.grid == 4 and s.info.sched == L.GEMM_SCHED_STATIC
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                    reason="validation-only test; on a GPU machine the parity suite covers runs")
+def test_run_validation_before_enqueue():
+    p = L.Plan(L.make_desc(512, 512, 65536, sched=L.GEMM_SCHED_STREAMK, num_workers=256,
+                           bm=128, bn=128))
+    ok = 1 << 20  # an aligned address; never dereferenced because every call below fails first
+    assert p.run_raw(0, ok, ok) == L.GEMM_ERR_INVALID_ARG
+    assert p.run_raw(ok + 8, ok, ok, 0, 0, ok, p.workspace_bytes) == L.GEMM_ERR_ALIGNMENT
+    assert p.run_raw(ok, ok, ok) == L.GEMM_ERR_WORKSPACE
+    assert p.run_raw(ok, ok, ok, 0, 0, ok, p.workspace_bytes - 1) == L.GEMM_ERR_WORKSPACE
+    assert p.run_raw(ok, ok, ok, 0, 0, ok + 4, p.workspace_bytes) == L.GEMM_ERR_ALIGNMENT
+    f = L.Plan(L.make_desc(512, 512, 512, dtype_ab=L.GEMM_FP8_E4M3, num_workers=4))
+    assert f.run_raw(ok, ok, ok) == L.GEMM_ERR_INVALID_ARG          # FP8 needs both scales
+    assert f.run_raw(ok, ok, ok, ok, 0) == L.GEMM_ERR_INVALID_ARG
+    assert f.run_raw(ok, ok, ok, ok + 2, ok) == L.GEMM_ERR_ALIGNMENT
+    # everything valid but no device in this container: the launch itself reports the failure
+    b = L.Plan(L.make_desc(256, 256, 256, num_workers=4))
+    assert b.run_raw(ok, ok, ok) == L.GEMM_ERR_HIP
+    # an empty output is a no-op that needs no pointers at all
+    e = L.Plan(L.make_desc(0, 256, 256, num_workers=4))
+    assert e.info.grid == 0 and e.run_raw(0, 0, 0) == L.GEMM_OK
+
+
+def test_package_has_no_cpu_fallback():
+    """The product path neither imports the oracle nor computes a product any other way."""
+    pkg = os.path.join(ROOT, "dense_gemm_design_amd")
+    for name in os.listdir(pkg):
+        if not name.endswith(".py"):
+            continue
+        src = open(os.path.join(pkg, name)).read()
+        assert not re.search(r"^\s*(import|from)\s+oracle", src, re.M), name
+        for pat in ("matmul", "torch.mm(", "einsum", "bmm(", "np.dot", " @ "):
+            assert pat not in src, (name, pat)

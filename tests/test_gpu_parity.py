@@ -1,0 +1,179 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI, on an MI355X.
+
+Tolerance per element: |C - C_ref| <= 4e-3 |C_ref| + 1e-3 sqrt(K) max|a| max|b|.  Integer and
+schedule results are compared exactly: the closed-form row sums and small-integer products are
+exact in FP32 whatever the summation order, and the device trace of work items must equal the CPU
+enumeration.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import gemm_inputs as gi
+import oracle
+from oracle import schedule as S
+from dense_gemm_design_amd import _lib as L
+from gpu_util import assert_within_tolerance, reference, run_gpu, to_device
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load()
+    return torch.device("cuda:0")
+
+
+def test_bf16_256_static_linear_full(dev):
+    """256^3 bf16, A row / B column major, uniform[-1,1], fp32 out, linear N-fast, static."""
+    op = gi.make_workload("bf16_256")
+    C, plan, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STATIC,
+                         tile=128)
+    assert plan.info.grid == 4 and plan.info.bm == 128
+    assert_within_tolerance(C, reference(op), op, "bf16_256")
+
+
+SMALL = [
+    # id, M, N, K, dtype, out, tile, mapping, G, sched, workers
+    ("bf16_t256_grouped_persist", 512, 768, 1024, "bf16", "bf16", 256, L.GEMM_MAP_GROUPED_M, 2,
+     L.GEMM_SCHED_PERSISTENT, 3),
+    ("bf16_t128_linear_m", 640, 512, 384, "bf16", "f32", 128, L.GEMM_MAP_LINEAR_M, 1,
+     L.GEMM_SCHED_PERSISTENT, 5),
+    ("bf16_ragged_t128", 300, 264, 104, "bf16", "f32", 128, L.GEMM_MAP_GROUPED_N, 2,
+     L.GEMM_SCHED_STATIC, 0),
+    ("bf16_ragged_t256", 300, 264, 104, "bf16", "bf16", 256, L.GEMM_MAP_LINEAR_N, 1,
+     L.GEMM_SCHED_PERSISTENT, 2),
+    ("bf16_tiny", 1, 8, 8, "bf16", "f32", 128, L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STATIC, 0),
+    ("fp8_t256", 512, 512, 1024, "e4m3", "bf16", 256, L.GEMM_MAP_GROUPED_M, 16,
+     L.GEMM_SCHED_PERSISTENT, 2),
+    ("fp8_ragged_t128", 384, 264, 272, "e4m3", "f32", 128, L.GEMM_MAP_LINEAR_N, 1,
+     L.GEMM_SCHED_PERSISTENT, 4),
+    ("bf16_streamk", 256, 256, 8192, "bf16", "f32", 128, L.GEMM_MAP_LINEAR_N, 1,
+     L.GEMM_SCHED_STREAMK, 8),
+    ("bf16_streamk_hybrid", 640, 640, 2048, "bf16", "f32", 128, L.GEMM_MAP_GROUPED_M, 2,
+     L.GEMM_SCHED_STREAMK, 20),
+    ("fp8_streamk", 256, 256, 4096, "e4m3", "bf16", 128, L.GEMM_MAP_LINEAR_N, 1,
+     L.GEMM_SCHED_STREAMK, 6),
+    ("bf16_streamk_ragged", 200, 136, 1000, "bf16", "f32", 128, L.GEMM_MAP_LINEAR_N, 1,
+     L.GEMM_SCHED_STREAMK, 9),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_parity(dev, case):
+    name, M, N, K, dt, out, tile, mapping, G, sched, workers = case
+    dist = ("normal", 1.0) if dt == "e4m3" else ("uniform",)
+    op = gi.make_operands(M, N, K, dt, dist, dist, seed=zlib.crc32(name.encode()) % 10000)
+    C, plan, _ = run_gpu(op, torch, dev, out, mapping, G, sched, workers, tile)
+    if sched == L.GEMM_SCHED_STREAMK and name != "bf16_streamk_hybrid":
+        assert plan.info.sk_tiles > 0
+    if name == "bf16_streamk_hybrid":
+        assert plan.info.dp_tiles == 20 and plan.info.sk_tiles == 5
+    assert_within_tolerance(C, reference(op), op, name)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "e4m3"])
+@pytest.mark.parametrize("tile,sched,workers", [(128, L.GEMM_SCHED_STATIC, 0),
+                                                 (256, L.GEMM_SCHED_PERSISTENT, 3),
+                                                 (128, L.GEMM_SCHED_STREAMK, 9)])
+def test_closed_form_row_sums_exact(dev, dt, tile, sched, workers):
+    """A[m,k] = ((m+k) mod 8)/8, B = 1: every output is exactly 7K/16 in FP32."""
+    M, N, K = 384, 264, 2048
+    op = gi.rowsum_pattern(M, N, K, dt)
+    C, plan, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_GROUPED_M, 2, sched, workers, tile)
+    assert np.all(C == 7 * K / 16)
+
+
+def test_streamk_small_integers_bit_exact(dev):
+    """|a|, |b| <= 2 integers: every partial sum is exact in FP32, so the Stream-K fixup must
+    reproduce the oracle bit for bit (a lost or doubled k-tile would show)."""
+    M, N, K = 256, 128, 16384
+    op = gi.make_operands(M, N, K, "bf16", ("smallint", -2, 2), ("smallint", -2, 2), seed=77)
+    C, plan, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK,
+                         24, 128)
+    assert plan.info.sk_tiles == 2
+    assert np.array_equal(C, reference(op))
+
+
+def test_streamk_deterministic(dev):
+    op = gi.make_operands(256, 256, 8192, "bf16", seed=5)
+    C1, plan, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK,
+                          16, 128)
+    C2, _, _ = run_gpu(op, torch, dev, "f32", plan=plan)
+    assert np.array_equal(C1, C2)
+
+
+@pytest.mark.parametrize("sched,workers,tile,mapping,G", [
+    (L.GEMM_SCHED_STREAMK, 20, 128, L.GEMM_MAP_GROUPED_M, 2),
+    (L.GEMM_SCHED_PERSISTENT, 8, 256, L.GEMM_MAP_GROUPED_N, 3),
+    (L.GEMM_SCHED_STATIC, 0, 128, L.GEMM_MAP_LINEAR_M, 1),
+])
+def test_device_trace_matches_enumeration(dev, sched, workers, tile, mapping, G):
+    """Work items recorded by the kernel equal the CPU replay and the oracle's enumeration."""
+    M, N, K = 640, 640, 2048
+    op = gi.make_operands(M, N, K, "bf16", seed=3)
+    C, plan, ws = run_gpu(op, torch, dev, "f32", mapping, G, sched, workers, tile,
+                          flags=L.GEMM_FLAG_TRACE)
+    info = plan.info
+    raw = ws.cpu().numpy()[info.trace_offset:].view(np.int32)[: info.grid * info.trace_capacity * 8]
+    rec = raw.reshape(info.grid, info.trace_capacity, 8)
+    got = []
+    for w in range(info.grid):
+        for r in rec[w]:
+            if r[0] == w and (r[6] > 0):
+                got.append(tuple(int(x) for x in r))
+    want = plan.schedule()
+    assert got == want
+    MAP = {0: S.LINEAR_N, 1: S.LINEAR_M, 2: S.GROUPED_M, 3: S.GROUPED_N}
+    SCH = {0: S.STATIC, 1: S.PERSISTENT, 2: S.STREAMK}
+    ora = S.enumerate_schedule(M, N, K, tile, tile, info.bk, MAP[mapping], G, SCH[sched],
+                               P=None if sched == L.GEMM_SCHED_STATIC else info.grid)
+    assert got == [(w.worker, w.seq, w.tile, w.m, w.n, w.k_begin, w.k_end, w.role) for w in ora]
+    assert_within_tolerance(C, reference(op), op, "trace run")
+
+
+def test_spin_watchdog_reports_instead_of_hanging(dev):
+    """The first split of slot 0 withholds its lock (test flag); its successor's bounded wait
+    expires, the kernel still finishes, and the device error word says so."""
+    op = gi.make_operands(256, 256, 4096, "bf16", seed=9)
+    C, plan, ws = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK, 8,
+                          128, flags=L.GEMM_FLAG_TEST_SKIP_PUBLISH)
+    err = int(ws.cpu().numpy()[plan.info.error_offset:plan.info.error_offset + 4].view(np.int32)[0])
+    assert err == L.GEMM_DEVICE_ERR_SPIN
+    # and a normal run of the same plan shape reports no error
+    C, plan, ws = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK, 8,
+                          128)
+    err = int(ws.cpu().numpy()[plan.info.error_offset:plan.info.error_offset + 4].view(np.int32)[0])
+    assert err == L.GEMM_DEVICE_OK
+
+
+def test_linear_and_grouped_give_identical_bits(dev):
+    """The mapping only reorders whole tiles; each tile's arithmetic is unchanged."""
+    op = gi.make_operands(1024, 1024, 512, "bf16", seed=12)
+    C1, _, _ = run_gpu(op, torch, dev, "bf16", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_PERSISTENT,
+                       7, 128)
+    C2, _, _ = run_gpu(op, torch, dev, "bf16", L.GEMM_MAP_GROUPED_M, 8, L.GEMM_SCHED_PERSISTENT,
+                       7, 128)
+    assert np.array_equal(C1, C2)
+
+
+@pytest.mark.parametrize("M,N,K", [(0, 64, 64), (64, 0, 64), (64, 64, 0), (130, 136, 0)])
+def test_empty_and_zero_depth(dev, M, N, K):
+    """M or N = 0: nothing is written.  K = 0: C is the empty sum, all zeros."""
+    op = gi.make_operands(M, N, K, "bf16", seed=1)
+    if M == 0 or N == 0:
+        A, B, sa, sb = to_device(op, torch, dev)
+        plan = L.Plan(L.make_desc(M, N, K, num_workers=4))
+        C = torch.empty((M, N), device=dev)
+        plan.run(A, B, C)
+        torch.cuda.synchronize()
+        assert C.numel() == 0
+        return
+    for sched, workers in ((L.GEMM_SCHED_PERSISTENT, 3), (L.GEMM_SCHED_STREAMK, 8),
+                           (L.GEMM_SCHED_STATIC, 0)):
+        C, plan, _ = run_gpu(op, torch, dev, "f32", sched=sched, workers=workers, tile=128)
+        assert np.array_equal(C, np.zeros((M, N)))

@@ -1,0 +1,62 @@
+"""The library's schedule (gemm_schedule_enumerate, the same code the kernel runs) matches the
+oracle's independent CPU enumeration bit for bit."""
+import pytest
+
+from dense_gemm_design_amd import _lib as L
+from oracle import schedule as S
+
+MAP = {L.GEMM_MAP_LINEAR_N: S.LINEAR_N, L.GEMM_MAP_LINEAR_M: S.LINEAR_M,
+       L.GEMM_MAP_GROUPED_M: S.GROUPED_M, L.GEMM_MAP_GROUPED_N: S.GROUPED_N}
+SCHED = {L.GEMM_SCHED_STATIC: S.STATIC, L.GEMM_SCHED_PERSISTENT: S.PERSISTENT,
+         L.GEMM_SCHED_STREAMK: S.STREAMK}
+
+CASES = [
+    # M, N, K, dtype, tile, mapping, G, sched, P, remap
+    (256, 256, 256, L.GEMM_BF16, 128, L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STATIC, 0, True),
+    (4096, 4096, 4096, L.GEMM_BF16, 128, L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_PERSISTENT, 256, True),
+    (4096, 4096, 4096, L.GEMM_BF16, 128, L.GEMM_MAP_GROUPED_M, 8, L.GEMM_SCHED_PERSISTENT, 256, True),
+    (4096, 4096, 4096, L.GEMM_BF16, 256, L.GEMM_MAP_GROUPED_M, 8, L.GEMM_SCHED_PERSISTENT, 256, True),
+    (4096, 14336, 4096, L.GEMM_BF16, 256, L.GEMM_MAP_GROUPED_M, 8, L.GEMM_SCHED_PERSISTENT, 256, True),
+    (8192, 8192, 8192, L.GEMM_FP8_E4M3, 256, L.GEMM_MAP_GROUPED_M, 16, L.GEMM_SCHED_PERSISTENT, 256, True),
+    (512, 512, 65536, L.GEMM_BF16, 128, L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK, 256, True),
+    (1000, 1000, 512, L.GEMM_BF16, 128, L.GEMM_MAP_GROUPED_N, 3, L.GEMM_SCHED_PERSISTENT, 24, True),
+    (1000, 1000, 512, L.GEMM_BF16, 128, L.GEMM_MAP_LINEAR_M, 1, L.GEMM_SCHED_STATIC, 0, False),
+    (1280, 640, 1024, L.GEMM_BF16, 128, L.GEMM_MAP_GROUPED_M, 4, L.GEMM_SCHED_STREAMK, 40, True),
+    (1280, 640, 1024, L.GEMM_BF16, 128, L.GEMM_MAP_GROUPED_M, 4, L.GEMM_SCHED_STREAMK, 40, False),
+    (384, 256, 448, L.GEMM_BF16, 128, L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK, 5, True),
+    (300, 264, 104, L.GEMM_BF16, 128, L.GEMM_MAP_GROUPED_M, 2, L.GEMM_SCHED_STREAMK, 3, True),
+    (2048, 2048, 2048, L.GEMM_FP8_E4M3, 128, L.GEMM_MAP_GROUPED_N, 8, L.GEMM_SCHED_STREAMK, 300, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_enumeration_matches_oracle(case):
+    M, N, K, dt, tile, mapping, G, sched, P, remap = case
+    flags = 0 if remap else L.GEMM_FLAG_NO_XCD_REMAP
+    plan = L.Plan(L.make_desc(M, N, K, dtype_ab=dt, mapping=mapping, group=G, sched=sched,
+                              num_workers=P, bm=tile, bn=tile, flags=flags))
+    got = plan.schedule()
+    bk = plan.info.bk
+    Pw = plan.info.grid if sched != L.GEMM_SCHED_STATIC else None
+    want = S.enumerate_schedule(M, N, K, tile, tile, bk, MAP[mapping], G, SCHED[sched],
+                                P=P if sched != L.GEMM_SCHED_STATIC else None,
+                                xcd_remap=remap)
+    want = [(w.worker, w.seq, w.tile, w.m, w.n, w.k_begin, w.k_end, w.role) for w in want]
+    if sched == L.GEMM_SCHED_PERSISTENT:
+        # the planner caps P at the tile count; the oracle is asked with the same P
+        want = [(w.worker, w.seq, w.tile, w.m, w.n, w.k_begin, w.k_end, w.role) for w in
+                S.enumerate_schedule(M, N, K, tile, tile, bk, MAP[mapping], G, SCHED[sched],
+                                     P=Pw, xcd_remap=remap)]
+    assert got == want
+
+
+def test_enumerate_capacity_reporting():
+    plan = L.Plan(L.make_desc(1024, 1024, 1024, sched=L.GEMM_SCHED_PERSISTENT, num_workers=7,
+                              bm=128, bn=128))
+    import ctypes
+    lib = L.load()
+    n = ctypes.c_size_t()
+    arr = (L.GemmWorkItem * 3)()
+    assert lib.gemm_schedule_enumerate(plan.handle, arr, 3, ctypes.byref(n)) == L.GEMM_ERR_CAPACITY
+    assert n.value == 64
+    assert (arr[0].worker, arr[0].seq) == (0, 0)
