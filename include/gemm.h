@@ -130,7 +130,7 @@ int gemm_workspace_bytes(gemm_handle h, size_t *bytes);
 int gemm_plan_get(gemm_handle h, gemm_plan_info *info);
 
 /* Enqueues C = alpha * A x B on `stream`.  A: M x K row-major, B: K x N column-major, C: M x N
- * row-major of dtype_c.  scale_a / scale_b: device pointers to one float each for FP8 (required),
+ * row-major of dtype_c (A and B may be NULL when K == 0; nothing is needed when M or N is 0).  scale_a / scale_b: device pointers to one float each for FP8 (required),
  * ignored for BF16 (may be NULL).  workspace: device memory of at least gemm_workspace_bytes(),
  * 16-byte aligned; the library clears the parts it needs at the start of every run. */
 int gemm_run(gemm_handle h, const void *A, const void *B, void *C, const float *scale_a,

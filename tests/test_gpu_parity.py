@@ -57,7 +57,7 @@ SMALL = [
     ("bf16_streamk_hybrid", 640, 640, 2048, "bf16", "f32", 128, L.GEMM_MAP_GROUPED_M, 2,
      L.GEMM_SCHED_STREAMK, 20),
     ("fp8_streamk", 256, 256, 4096, "e4m3", "bf16", 128, L.GEMM_MAP_LINEAR_N, 1,
-     L.GEMM_SCHED_STREAMK, 6),
+     L.GEMM_SCHED_STREAMK, 11),
     ("bf16_streamk_ragged", 200, 136, 1000, "bf16", "f32", 128, L.GEMM_MAP_LINEAR_N, 1,
      L.GEMM_SCHED_STREAMK, 9),
 ]
