@@ -21,22 +21,28 @@ using namespace dg;
 
 // Tile configurations.  SWZ = 1 spreads the 16 rows that one 16-lane LDS read phase touches over
 // 16 distinct 16-byte bank groups for 128-byte rows.
-using CfgBf16_256 = TileCfg<DT_BF16, 256, 256, 64, 2, 2, 2, 1>;
+using CfgBf16_256 = TileCfg<DT_BF16, 256, 256, 64, 2, 4, 2, 1>;
+using CfgBf16_256k32 = TileCfg<DT_BF16, 256, 256, 32, 2, 4, 4, 2>;
+using CfgBf16_256w4 = TileCfg<DT_BF16, 256, 256, 64, 2, 2, 2, 1>;
 using CfgBf16_128 = TileCfg<DT_BF16, 128, 128, 64, 2, 2, 2, 1>;
-using CfgFp8_256 = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1>;
+using CfgFp8_256 = TileCfg<DT_FP8, 256, 256, 128, 2, 4, 2, 1>;
+using CfgFp8_256w4 = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1>;
 using CfgFp8_128 = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 2, 1>;
 
-typedef hipError_t (*launch_fn)(const KernelArgs &, int grid, hipStream_t);
+typedef hipError_t (*launch_fn)(const KernelArgs &, int grid, bool ragged_k, hipStream_t);
 typedef const void *(*kernel_fn)();
 
 template <class CFG>
-hipError_t launch_cfg(const KernelArgs &a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL(gemm_kernel<CFG>, dim3(grid), dim3(CFG::THREADS), 0, s, a);
+hipError_t launch_cfg(const KernelArgs &a, int grid, bool ragged_k, hipStream_t s) {
+  if (ragged_k)
+    hipLaunchKernelGGL((gemm_kernel<CFG, true>), dim3(grid), dim3(CFG::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<CFG, false>), dim3(grid), dim3(CFG::THREADS), 0, s, a);
   return hipGetLastError();
 }
 template <class CFG>
 const void *kernel_of() {
-  return (const void *)&gemm_kernel<CFG>;
+  return (const void *)&gemm_kernel<CFG, false>;
 }
 
 struct KernelEntry {
@@ -51,10 +57,14 @@ constexpr KernelEntry entry() {
                      CFG::LDS_BYTES, &launch_cfg<CFG>, &kernel_of<CFG>};
 }
 
+// The first entry that matches (dtype, bm, bn[, bk]) is the default for that tile shape.
 const KernelEntry kKernels[] = {
     entry<CfgBf16_256>(),
+    entry<CfgBf16_256k32>(),
+    entry<CfgBf16_256w4>(),
     entry<CfgBf16_128>(),
     entry<CfgFp8_256>(),
+    entry<CfgFp8_256w4>(),
     entry<CfgFp8_128>(),
 };
 
@@ -128,7 +138,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   const int want_dt = d.dtype_ab == GEMM_BF16 ? DT_BF16 : DT_FP8;
   const KernelEntry *k = nullptr;
   for (const KernelEntry &e : kKernels)
-    if (e.dt == want_dt && e.bm == bm && e.bn == bn && (d.bk == 0 || d.bk == e.bk)) k = &e;
+    if (!k && e.dt == want_dt && e.bm == bm && e.bn == bn && (d.bk == 0 || d.bk == e.bk)) k = &e;
   if (!k) return GEMM_ERR_UNSUPPORTED;
   // rows of one tile must stay addressable by 32-bit buffer offsets
   if ((int64_t)bm * d.K * eb >= 0x7FFFFFF0ll || (int64_t)bn * d.K * eb >= 0x7FFFFFF0ll)
@@ -184,6 +194,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     if ((int64_t)sp.sk_tiles * Kt > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
   }
   sp.X = (d.flags & GEMM_FLAG_NO_XCD_REMAP) ? 1 : kXcds;
+  sched_prepare(sp);
 
   gemm_plan *p = new (std::nothrow) gemm_plan;
   if (!p) return GEMM_ERR_INVALID_ARG;
@@ -293,7 +304,8 @@ int gemm_run(gemm_handle h, const void *A, const void *B, void *C, const float *
                        (int *)(ws + first), (int)n_ints);
     if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
   }
-  if (h->k->launch(a, h->info.grid, s) != hipSuccess) return GEMM_ERR_HIP;
+  const bool ragged_k = h->d.K % h->k->bk != 0;
+  if (h->k->launch(a, h->info.grid, ragged_k, s) != hipSuccess) return GEMM_ERR_HIP;
   return GEMM_OK;
 }
 

@@ -19,6 +19,11 @@
 //    that stage with step c+S-1 right after the barrier.  The ring position (stage, phase =
 //    floor(c / S) & 1, count = c) lives in scalar registers; the phase is implicit in c.
 //  * Consumer phase: ds_read_b128 of the A and B fragments of the wave's sub-tile, MFMA chain.
+// With one wave per SIMD a burst of memory instructions stalls the only instruction stream that
+// feeds the MFMA pipe, so each k-step is software-pipelined at the instruction level: the MFMAs of
+// a sub-step are issued one by one and the LDS reads of the next sub-step's fragments and the
+// producer's loads are placed between them (a fixed per-slot plan, below); the handshake sits a
+// quarter of the way into the last sub-step, so the MFMA pipe still has queued work across it.
 // LDS rows are XOR-swizzled in 16-byte chunks (chunk' = chunk ^ f(row)), the gfx950 counterpart
 // of the pages' 128-byte swizzle ("H100 cuTensorMap" lesson, section 11; "H100 WGMMA part 1",
 // section 11), so that the 32 rows one MFMA operand read touches spread over all LDS banks.
@@ -31,6 +36,9 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
+#include <utility>
 
 #include "sched.h"
 
@@ -73,6 +81,9 @@ struct TileCfg {
   static constexpr int DT = DT_, BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
   static constexpr int STAGES = STAGES_, SWZ = SWZ_;
   static constexpr int WAVES = WGM * WGN, THREADS = WAVES * 64;
+  // waves of this workgroup per SIMD (4 SIMDs per CU); with two, each wave gets half the
+  // register file and the other wave of the SIMD issues MFMAs while this one waits on LDS
+  static constexpr int WAVES_PER_SIMD = (WAVES + 3) / 4;
   static constexpr int WM = BM / WGM, WN = BN / WGN;     // wave sub-tile
   static constexpr int FM = WM / 32, FN = WN / 32;       // 32 x 32 MFMA blocks per wave
   static constexpr int EB = DT == DT_BF16 ? 2 : 1;       // bytes per element
@@ -93,6 +104,9 @@ struct TileCfg {
   static_assert(LA + LB <= 63, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS per workgroup");
   static_assert((32 >> SWZ) % CH == 0, "swizzle must not depend on the 32-row block");
+  // An even number of MFMA sub-steps per k-tile keeps the two fragment buffers in fixed roles,
+  // so a fragment load never targets registers an in-flight MFMA is still reading.
+  static_assert(KSUB % 2 == 0, "k-tile must hold an even number of MFMA sub-steps");
 };
 
 // ---- small device helpers ------------------------------------------------------------------
@@ -105,13 +119,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// wait until at most n of this wave's vector-memory operations are outstanding (n <= 3 * L)
+// Wait until this wave's loads of a k-step have landed, given that `steps_after` later k-steps
+// (L loads each) were issued after it: s_waitcnt vmcnt(min(63, steps_after * L)).  Vector memory
+// operations of one wave complete in issue order, so at most that many can still be pending.
 template <int L>
 __device__ __forceinline__ void wait_loads_after(int steps_after) {
   if (steps_after <= 0) wait_vmcnt<0>();
   else if (steps_after == 1) wait_vmcnt<L>();
   else if (steps_after == 2) wait_vmcnt<(2 * L > 63 ? 63 : 2 * L)>();
-  else wait_vmcnt<(3 * L > 63 ? 63 : 3 * L)>();
+  else if (steps_after == 3) wait_vmcnt<(3 * L > 63 ? 63 : 3 * L)>();
+  else wait_vmcnt<(4 * L > 63 ? 63 : 4 * L)>();
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *base, int64_t bytes) {
@@ -126,16 +143,37 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-template <class CFG>
-__device__ __forceinline__ f32x16 mfma(const i32x4 *b, const i32x4 *a, const f32x16 &c) {
-  if constexpr (CFG::DT == DT_BF16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b[0]),
-                                                   __builtin_bit_cast(bf16x8, a[0]), c, 0, 0, 0);
+// One MFMA operand fragment of a lane: 8 bf16 (one 16-byte chunk) or 32 e4m3 (two chunks).
+template <int DT>
+struct FragT;
+template <>
+struct FragT<DT_BF16> {
+  typedef bf16x8 type;
+};
+template <>
+struct FragT<DT_FP8> {
+  typedef i32x8 type;
+};
+
+template <int DT>
+__device__ __forceinline__ typename FragT<DT>::type lds_frag(const lds_t *p0, const lds_t *p1) {
+  typedef const i32x4 __attribute__((address_space(3))) *ptr;
+  if constexpr (DT == DT_BF16) {
+    return __builtin_bit_cast(bf16x8, *(ptr)p0);
   } else {
-    i32x8 bb = {b[0][0], b[0][1], b[0][2], b[0][3], b[1][0], b[1][1], b[1][2], b[1][3]};
-    i32x8 aa = {a[0][0], a[0][1], a[0][2], a[0][3], a[1][0], a[1][1], a[1][2], a[1][3]};
+    const i32x4 lo = *(ptr)p0, hi = *(ptr)p1;
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma(const typename FragT<DT>::type &b,
+                                       const typename FragT<DT>::type &a, const f32x16 &c) {
+  if constexpr (DT == DT_BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
+  } else {
     // operand formats 0 = e4m3 for both; zero scale operands select the unscaled instruction
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bb, aa, c, 0, 0, 0, 0, 0, 0);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 0, 0, 0);
   }
 }
 
@@ -143,12 +181,13 @@ __device__ __forceinline__ f32x16 mfma(const i32x4 *b, const i32x4 *a, const f32
 
 // Producer side of the ring: the cursor of the next k-tile to load (uniform) and the lane's byte
 // offsets inside a tile (one register per 1 KiB load, fixed for the whole kernel).
-template <class CFG>
+template <class CFG, bool RAGGED_K>
 struct Producer {
   Cursor cur;
   int32_t valid, k, ke, rows_a, rows_b;
   __amdgpu_buffer_rsrc_t ra, rb;
-  uint32_t va[CFG::LA], vb[CFG::LB];
+  uint32_t va0[CFG::LA], vb0[CFG::LB];  // lane offsets within a full tile (fixed)
+  uint32_t va[CFG::LA], vb[CFG::LB];    // the same with rows past M (N) of this tile -> kOOB
 
   // row of tile and 16-byte chunk along K that `lane` fills in load j of `wave`
   static __device__ __forceinline__ int load_row(int j, int wave, int lane) {
@@ -162,18 +201,18 @@ struct Producer {
 #pragma unroll
     for (int j = 0; j < CFG::LA; ++j) {
       const int row = load_row(j, wave, lane);
-      va[j] = (uint32_t)(row * (uint32_t)args.lda_bytes + load_chunk(row, lane) * 16);
+      va0[j] = (uint32_t)(row * (uint32_t)args.lda_bytes + load_chunk(row, lane) * 16);
     }
 #pragma unroll
     for (int j = 0; j < CFG::LB; ++j) {
       const int row = load_row(j, wave, lane);
-      vb[j] = (uint32_t)(row * (uint32_t)args.ldb_bytes + load_chunk(row, lane) * 16);
+      vb0[j] = (uint32_t)(row * (uint32_t)args.ldb_bytes + load_chunk(row, lane) * 16);
     }
     cursor_init(args.sp, b, cur);
-    next_item(args);
+    next_item(args, wave, lane);
   }
 
-  __device__ __forceinline__ void next_item(const KernelArgs &args) {
+  __device__ __forceinline__ void next_item(const KernelArgs &args, int wave, int lane) {
     WorkItem w;
     // items without k-tiles (K == 0) load nothing
     while ((valid = cursor_next(args.sp, cur, w)) && w.kb == w.ke) {
@@ -186,74 +225,78 @@ struct Producer {
       rows_b = (int32_t)(args.N - n0 < CFG::BN ? args.N - n0 : CFG::BN);
       ra = make_rsrc(args.A + m0 * args.lda_bytes, (int64_t)rows_a * args.lda_bytes);
       rb = make_rsrc(args.B + n0 * args.ldb_bytes, (int64_t)rows_b * args.ldb_bytes);
+#pragma unroll
+      for (int j = 0; j < CFG::LA; ++j)
+        va[j] = rows_a == CFG::BM || load_row(j, wave, lane) < rows_a ? va0[j] : kOOB;
+#pragma unroll
+      for (int j = 0; j < CFG::LB; ++j)
+        vb[j] = rows_b == CFG::BN || load_row(j, wave, lane) < rows_b ? vb0[j] : kOOB;
     }
   }
 
-  // Issue the loads of k-tile k into `stage`, then advance (possibly to the next work item).
-  __device__ __forceinline__ void issue(const KernelArgs &args, lds_t *smem, int stage, int wave,
-                                        int lane) {
-    const uint32_t kbytes = (uint32_t)k * CFG::ROWB;
-    lds_t *sa = smem + stage * CFG::STAGE_BYTES;
-    lds_t *sb = sa + CFG::A_BYTES;
-    const bool edge = rows_a < CFG::BM || rows_b < CFG::BN ||
-                      (int64_t)(k + 1) * CFG::ROWB > args.K * CFG::EB;
-    if (!edge) {
-#pragma unroll
-      for (int j = 0; j < CFG::LA; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, sa + (j * CFG::WAVES + wave) * 1024, 16,
-                                                 va[j] + kbytes, 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < CFG::LB; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, sb + (j * CFG::WAVES + wave) * 1024, 16,
-                                                 vb[j] + kbytes, 0, 0, 0);
-    } else {
-      // ragged tile: rows past M (N) and chunks past K read as zero
-      const uint32_t klimit = (uint32_t)(args.K * CFG::EB) - kbytes;
-#pragma unroll
-      for (int j = 0; j < CFG::LA; ++j) {
-        const int row = load_row(j, wave, lane);
-        const bool ok = row < rows_a && (uint32_t)(load_chunk(row, lane) * 16) < klimit;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, sa + (j * CFG::WAVES + wave) * 1024, 16,
-                                                 ok ? va[j] + kbytes : kOOB, 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < CFG::LB; ++j) {
-        const int row = load_row(j, wave, lane);
-        const bool ok = row < rows_b && (uint32_t)(load_chunk(row, lane) * 16) < klimit;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, sb + (j * CFG::WAVES + wave) * 1024, 16,
-                                                 ok ? vb[j] + kbytes : kOOB, 0, 0, 0);
-      }
+  // Loads of one k-step are issued one instruction at a time: begin(stage) fixes the stage and
+  // the k offset, load(j) issues 1 KiB load j (A loads first, then B), end() advances the cursor.
+  uint32_t kbytes, klimit;
+  int32_t kedge;
+  lds_t *sa;
+
+  __device__ __forceinline__ void begin(const KernelArgs &args, lds_t *smem, int stage) {
+    kbytes = (uint32_t)k * CFG::ROWB;
+    sa = smem + stage * CFG::STAGE_BYTES;
+    kedge = (int64_t)(k + 1) * CFG::ROWB > args.K * CFG::EB;  // the k-tile runs past K
+    klimit = (uint32_t)(args.K * CFG::EB) - kbytes;
+  }
+
+  template <int J>
+  __device__ __forceinline__ void load(int wave, int lane) {
+    constexpr bool IS_A = J < CFG::LA;
+    constexpr int j = IS_A ? J : J - CFG::LA;
+    lds_t *dst = sa + (IS_A ? 0 : CFG::A_BYTES) + (j * CFG::WAVES + wave) * 1024;
+    uint32_t off = (IS_A ? va[j] : vb[j]) + kbytes;  // rows past M (N) stay past the end
+    if (RAGGED_K && kedge) {  // chunks past K read as zero
+      const int row = load_row(j, wave, lane);
+      if ((uint32_t)(load_chunk(row, lane) * 16) >= klimit) off = kOOB;
     }
-    if (++k == ke) next_item(args);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(IS_A ? ra : rb, dst, 16, off, 0, 0, 0);
+  }
+
+  __device__ __forceinline__ void end(const KernelArgs &args, int wave, int lane) {
+    if (++k == ke) next_item(args, wave, lane);
   }
 };
 
+// MFMA operand fragments of one 16-deep (bf16) / 64-deep (fp8) sub-step of a k-tile.
 template <class CFG>
-__device__ __forceinline__ void compute_stage(const lds_t *smem, int stage,
-                                              const uint32_t (&aoff)[CFG::KSUB][CFG::CPL],
-                                              const uint32_t (&boff)[CFG::KSUB][CFG::CPL],
-                                              f32x16 (&acc)[CFG::FM][CFG::FN]) {
+struct Frags {
+  typename FragT<CFG::DT>::type a[CFG::FM], b[CFG::FN];
+};
+
+// Fragment e of a sub-step: A fragments first (FM of them), then B (FN).
+template <class CFG, int E>
+__device__ __forceinline__ void load_frag(const lds_t *smem, int stage, int s,
+                                          const uint32_t (&aoff)[CFG::KSUB][CFG::CPL],
+                                          const uint32_t (&boff)[CFG::KSUB][CFG::CPL],
+                                          Frags<CFG> &fr) {
   const lds_t *base = smem + stage * CFG::STAGE_BYTES;
-#pragma unroll
-  for (int s = 0; s < CFG::KSUB; ++s) {
-    i32x4 a[CFG::FM][CFG::CPL], b[CFG::FN][CFG::CPL];
-#pragma unroll
-    for (int f = 0; f < CFG::FM; ++f)
-#pragma unroll
-      for (int h = 0; h < CFG::CPL; ++h)
-        a[f][h] = *(const i32x4 __attribute__((address_space(3))) *)(base + aoff[s][h] +
-                                                                      f * 32 * CFG::ROWB);
-#pragma unroll
-    for (int g = 0; g < CFG::FN; ++g)
-#pragma unroll
-      for (int h = 0; h < CFG::CPL; ++h)
-        b[g][h] = *(const i32x4 __attribute__((address_space(3))) *)(base + boff[s][h] +
-                                                                      g * 32 * CFG::ROWB);
-#pragma unroll
-    for (int f = 0; f < CFG::FM; ++f)
-#pragma unroll
-      for (int g = 0; g < CFG::FN; ++g) acc[f][g] = mfma<CFG>(b[g], a[f], acc[f][g]);
+  constexpr int H = CFG::CPL - 1;
+  if constexpr (E < CFG::FM) {
+    fr.a[E] = lds_frag<CFG::DT>(base + aoff[s][0] + E * 32 * CFG::ROWB,
+                                base + aoff[s][H] + E * 32 * CFG::ROWB);
+  } else {
+    constexpr int G = E - CFG::FM;
+    fr.b[G] = lds_frag<CFG::DT>(base + boff[s][0] + G * 32 * CFG::ROWB,
+                                base + boff[s][H] + G * 32 * CFG::ROWB);
   }
+}
+
+// Slot plan: n memory operations spread over MFMA slots [a, b); operation j follows MFMA
+// a + floor(j (b - a) / n).  ops_before(i, ...) counts the operations placed after MFMAs 0..i-1,
+// so the operations that follow MFMA i are [ops_before(i), ops_before(i + 1)).
+__host__ __device__ constexpr int ops_before(int i, int n, int a, int b) {
+  int cnt = 0;
+  for (int j = 0; j < n; ++j)
+    if (a + (j * (b - a)) / n < i) ++cnt;
+  return cnt;
 }
 
 // Spin (one lane) until *lock == want, at most max_spin polls; returns false on expiry.
@@ -266,9 +309,8 @@ __device__ __forceinline__ bool wait_lock(int *lock, int want, int max_spin) {
 }
 
 // Epilogue of one work item, one accumulator quad (4 consecutive n of one row m) at a time:
-//   whole tile / final split: C = alpha * (slot + acc) cast to the output type (slot only when
-//   the tile was split); first / middle split: slot = (slot +) acc.
-// The accumulators are only read here, never rewritten.
+//   whole tile: C = cast(alpha * acc);  first split: slot = acc;  middle split: slot = slot + acc;
+//   final split: C = cast(alpha * (slot + acc)).  The accumulators are only read here.
 template <class CFG>
 __device__ __forceinline__ void epilogue(const KernelArgs &args, const WorkItem &w,
                                          const f32x16 (&acc)[CFG::FM][CFG::FN], float alpha,
@@ -312,9 +354,10 @@ __device__ __forceinline__ void epilogue(const KernelArgs &args, const WorkItem 
   }
 }
 
-template <class CFG>
+// RAGGED_K: K is not a multiple of BK, so the last k-tile of every tile masks its tail.
+template <class CFG, bool RAGGED_K>
 __global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::THREADS),
-                               amdgpu_waves_per_eu(1, 1)))
+                               amdgpu_waves_per_eu(CFG::WAVES_PER_SIMD, CFG::WAVES_PER_SIMD)))
 gemm_kernel(KernelArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[CFG::LDS_BYTES];
   lds_t *smem = (lds_t *)(size_t)(uint32_t)(size_t)(lds_t *)smem_raw;
@@ -344,7 +387,7 @@ gemm_kernel(KernelArgs args) {
       }
   }
 
-  Producer<CFG> prod;
+  Producer<CFG, RAGGED_K> prod;
   prod.init(args, b, wave, lane);
 
   Cursor ccur;
@@ -352,16 +395,103 @@ gemm_kernel(KernelArgs args) {
   WorkItem cw;
   bool cvalid = cursor_next(args.sp, ccur, cw);
 
-  // Prologue: fill S-1 stages.
+  // Ring bookkeeping: `issued` k-steps have been handed to the producer phase so far; the
+  // consumer is at k-step c.  Handshake H(c), executed once per k-step, is FULL(c) -- every wave's
+  // loads of step c have landed -- and EMPTY(c-1) -- every wave has finished its LDS reads of
+  // step c-1 -- after which step c+S-1 may be loaded into stage (c-1) mod S.  Those loads are
+  // issued during the first sub-step of step c (`pending`).
+  constexpr int L = CFG::LA + CFG::LB;
+  constexpr int NM = CFG::FM * CFG::FN;       // MFMAs per sub-step
+  constexpr int NF = CFG::FM + CFG::FN;       // fragments per sub-step
   int issued = 0;
 #pragma unroll
   for (int s = 0; s < CFG::STAGES - 1; ++s)
     if (prod.valid) {
-      prod.issue(args, smem, s, wave, lane);
+      prod.begin(args, smem, s);
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        (prod.template load<J>(wave, lane), ...);
+      }(std::make_integer_sequence<int, L>());
+      prod.end(args, wave, lane);
       ++issued;
     }
 
-  int c = 0;  // k-steps consumed by this workgroup (ring count; stage = c % S)
+  Frags<CFG> fr[2];
+  int c = 0;
+  bool pending = false;  // loads of step `issued` are begun but not yet issued
+  auto handshake = [&](int step) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own reads of step-1 are complete
+    wait_loads_after<L>(issued - step - 1);
+    lds_barrier();
+    if (prod.valid) {
+      prod.begin(args, smem, (step + CFG::STAGES - 1) % CFG::STAGES);
+      pending = true;
+    }
+  };
+  if (issued > 0) {
+    handshake(0);
+    [&]<int... E>(std::integer_sequence<int, E...>) {
+      (load_frag<CFG, E>(smem, 0, 0, aoff, boff, fr[0]), ...);
+    }(std::make_integer_sequence<int, NF>());
+  }
+
+  // One sub-step: NM MFMAs on fr[CUR]; between them, per the slot plan, the producer's loads (first
+  // sub-step only), the fragments of the next sub-step of this k-step, or -- in the last
+  // sub-step -- the handshake of the next k-step followed by its first fragments.
+  auto substep = [&](auto s_c, auto acc_ref) {
+    constexpr int S = decltype(s_c)::value;
+    constexpr int CUR = S & 1, NXT = (S + 1) & 1;
+    constexpr bool FIRST = S == 0, LAST = S == CFG::KSUB - 1;
+    constexpr int HS = LAST ? (CFG::KSUB == 1 ? NM / 2 : NM / 4) : NM;  // handshake slot
+    constexpr int LOAD_END = LAST ? HS : NM;
+    auto &acc = *acc_ref;
+    const int stage = c % CFG::STAGES;
+    const bool have_next = c + 1 < issued;
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (
+          [&] {
+            constexpr int i = I;
+            constexpr int f = i / CFG::FN, g = i % CFG::FN;
+            acc[f][g] = mfma<CFG::DT>(fr[CUR].b[g], fr[CUR].a[f], acc[f][g]);
+            // producer loads of the pending step
+            if constexpr (FIRST) {
+              constexpr int lo = ops_before(i, L, 0, LOAD_END);
+              constexpr int hi = ops_before(i + 1, L, 0, LOAD_END);
+              if (pending) {
+                [&]<int... J>(std::integer_sequence<int, J...>) {
+                  (prod.template load<lo + J>(wave, lane), ...);
+                }(std::make_integer_sequence<int, hi - lo>());
+                if constexpr (hi == L) {
+                  prod.end(args, wave, lane);
+                  ++issued;
+                  pending = false;
+                }
+              }
+            }
+            if constexpr (!LAST) {
+              constexpr int lo = ops_before(i, NF, 0, NM);
+              constexpr int hi = ops_before(i + 1, NF, 0, NM);
+              [&]<int... E>(std::integer_sequence<int, E...>) {
+                (load_frag<CFG, lo + E>(smem, stage, S + 1, aoff, boff, fr[NXT]), ...);
+              }(std::make_integer_sequence<int, hi - lo>());
+            } else {
+              if constexpr (i + 1 == HS) {
+                if (have_next) handshake(c + 1);
+              }
+              constexpr int lo = ops_before(i, NF, HS, NM);
+              constexpr int hi = ops_before(i + 1, NF, HS, NM);
+              if (have_next) {
+                [&]<int... E>(std::integer_sequence<int, E...>) {
+                  (load_frag<CFG, lo + E>(smem, (c + 1) % CFG::STAGES, 0, aoff, boff, fr[NXT]),
+                   ...);
+                }(std::make_integer_sequence<int, hi - lo>());
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }(),
+          ...);
+    }(std::make_integer_sequence<int, NM>());
+  };
+
   int seq = 0;
   while (cvalid) {
     if ((args.flags & KF_TRACE) && tid == 0 && seq < args.trace_cap) {
@@ -378,14 +508,9 @@ gemm_kernel(KernelArgs args) {
         for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.0f;
 
     for (int k = cw.kb; k < cw.ke; ++k, ++c) {
-      // FULL(c): own loads of step c landed, then everyone's; also EMPTY(c-1).
-      wait_loads_after<CFG::LA + CFG::LB>(issued - c - 1);
-      lds_barrier();
-      if (prod.valid) {
-        prod.issue(args, smem, (c + CFG::STAGES - 1) % CFG::STAGES, wave, lane);
-        ++issued;
-      }
-      compute_stage<CFG>(smem, c % CFG::STAGES, aoff, boff, acc);
+      [&]<int... S>(std::integer_sequence<int, S...>) {
+        (substep(std::integral_constant<int, S>(), &acc), ...);
+      }(std::make_integer_sequence<int, CFG::KSUB>());
     }
 
     // ---- Stream-K fixup handshake around the epilogue ----

@@ -26,6 +26,30 @@ namespace dg {
 enum Mapping { MAP_LINEAR_N = 0, MAP_LINEAR_M = 1, MAP_GROUPED_M = 2, MAP_GROUPED_N = 3 };
 enum Role { ROLE_WHOLE = 0, ROLE_FIRST = 1, ROLE_MIDDLE = 2, ROLE_LAST = 3 };
 
+// Division of a non-negative 31-bit value by a fixed positive divisor as a multiply-high, add
+// and shift (Granlund and Montgomery, "Division by invariant integers using multiplication",
+// PLDI 1994): with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, n / d equals
+// (mulhi(m, n) + n) >> l for 0 <= n < 2^31.  Uniform operands stay on the scalar unit.
+struct FastDiv {
+  uint32_t d, m, l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t l = 0;
+  while (l < 32 && ((uint64_t)1 << l) < d) ++l;
+  f.l = l;
+  f.m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1);
+  return f;
+}
+
+DG_HD uint32_t umulhi32(uint32_t a, uint32_t b) { return (uint32_t)(((uint64_t)a * b) >> 32); }
+
+DG_HD int32_t fdiv(int32_t n, const FastDiv &f) {
+  return (int32_t)((umulhi32(f.m, (uint32_t)n) + (uint32_t)n) >> f.l);
+}
+
 struct SchedParams {
   int32_t Mt, Nt, Kt;      // tiles along M and N, k-tiles along K
   int32_t mapping, G;      // F(i) family and strip width
@@ -34,7 +58,31 @@ struct SchedParams {
   int32_t pad_;
   int32_t dp_tiles;        // tasks i < dp_tiles run whole (data parallel)
   int32_t sk_tiles;        // the next sk_tiles tasks are split along K (Stream-K band)
+  // divisors of the mapping and of the Stream-K band (filled by sched_prepare)
+  FastDiv div_major;       // Nt (linear N), Mt (linear M), G*Nt (grouped M), G*Mt (grouped N)
+  FastDiv div_g;           // G (grouped), unused otherwise
+  FastDiv div_g_last;      // width of the short last strip (grouped), else = div_g
+  FastDiv div_kt;          // Kt (Stream-K band), 1 when Kt == 0
+  int32_t full_strips;     // strips of exactly G
+  int32_t pad2_;
 };
+
+// Fills the divisor fields from Mt, Nt, Kt, mapping and G.
+inline void sched_prepare(SchedParams &sp) {
+  const int32_t G = sp.G < 1 ? 1 : sp.G;
+  switch (sp.mapping) {
+    case MAP_LINEAR_N: sp.div_major = make_fastdiv(sp.Nt > 0 ? sp.Nt : 1); break;
+    case MAP_LINEAR_M: sp.div_major = make_fastdiv(sp.Mt > 0 ? sp.Mt : 1); break;
+    case MAP_GROUPED_M: sp.div_major = make_fastdiv((uint32_t)(G * (sp.Nt > 0 ? sp.Nt : 1))); break;
+    default: sp.div_major = make_fastdiv((uint32_t)(G * (sp.Mt > 0 ? sp.Mt : 1))); break;
+  }
+  const int32_t rows = sp.mapping == MAP_GROUPED_N ? sp.Nt : sp.Mt;
+  sp.full_strips = rows / G;
+  const int32_t last = rows - sp.full_strips * G;
+  sp.div_g = make_fastdiv((uint32_t)G);
+  sp.div_g_last = make_fastdiv((uint32_t)(last > 0 ? last : G));
+  sp.div_kt = make_fastdiv((uint32_t)(sp.Kt > 0 ? sp.Kt : 1));
+}
 
 struct WorkItem {
   int32_t tile;            // linear task i
@@ -51,30 +99,30 @@ struct TileMN {
 // F(i) -> (m, n).  Grouped-M: a strip holds G tile-rows (fewer in a short last strip) and is
 // walked column by column, M-fast inside: i = strip * (G * Nt) + n * g + (m - strip * G).
 // Task indices fit in 32 bits (the planner rejects larger grids).
-DG_HD TileMN map_tile(int32_t mapping, int32_t G, int32_t Mt, int32_t Nt, int32_t i) {
+DG_HD TileMN map_tile(const SchedParams &sp, int32_t i) {
   TileMN t;
-  if (mapping == MAP_LINEAR_N) {
-    t.m = i / Nt;
-    t.n = i - t.m * Nt;
-  } else if (mapping == MAP_LINEAR_M) {
-    t.n = i / Mt;
-    t.m = i - t.n * Mt;
-  } else if (mapping == MAP_GROUPED_M) {
-    const int32_t per_strip = G * Nt;
-    const int32_t strip = i / per_strip;
-    const int32_t j = i - strip * per_strip;
-    const int32_t rows_left = Mt - strip * G;
-    const int32_t g = rows_left < G ? rows_left : G;
-    t.n = j / g;
-    t.m = strip * G + (j - t.n * g);
-  } else {  // MAP_GROUPED_N
-    const int32_t per_strip = G * Mt;
-    const int32_t strip = i / per_strip;
-    const int32_t j = i - strip * per_strip;
-    const int32_t cols_left = Nt - strip * G;
-    const int32_t g = cols_left < G ? cols_left : G;
-    t.m = j / g;
-    t.n = strip * G + (j - t.m * g);
+  const int32_t q = fdiv(i, sp.div_major);
+  const int32_t r = i - q * (int32_t)sp.div_major.d;
+  if (sp.mapping == MAP_LINEAR_N) {
+    t.m = q;
+    t.n = r;
+  } else if (sp.mapping == MAP_LINEAR_M) {
+    t.n = q;
+    t.m = r;
+  } else {
+    // strip q, position r inside it; the strip is g wide (G, or less for the last one)
+    const bool last = q >= sp.full_strips;
+    const FastDiv &dg = last ? sp.div_g_last : sp.div_g;
+    const int32_t along = fdiv(r, dg);            // tile index along the strip's length
+    const int32_t across = r - along * (int32_t)dg.d;
+    const int32_t first = q * sp.G + across;      // tile index across the strip
+    if (sp.mapping == MAP_GROUPED_M) {
+      t.m = first;
+      t.n = along;
+    } else {
+      t.n = first;
+      t.m = along;
+    }
   }
   return t;
 }
@@ -116,7 +164,7 @@ DG_HD bool cursor_next(const SchedParams &sp, Cursor &c, WorkItem &w) {
     w.sk_slot = -1;
   } else if (c.sk_hi > c.sk_lo) {
     const int32_t last = c.sk_hi - 1;
-    const int32_t t = last / sp.Kt;                 // band-local tile of the top iteration
+    const int32_t t = fdiv(last, sp.div_kt);        // band-local tile of the top iteration
     const int32_t t_first = t * sp.Kt;
     const int32_t start = c.sk_lo > t_first ? c.sk_lo : t_first;
     w.tile = sp.dp_tiles + t;
@@ -129,7 +177,7 @@ DG_HD bool cursor_next(const SchedParams &sp, Cursor &c, WorkItem &w) {
   } else {
     return false;
   }
-  const TileMN mn = map_tile(sp.mapping, sp.G, sp.Mt, sp.Nt, w.tile);
+  const TileMN mn = map_tile(sp, w.tile);
   w.m = mn.m;
   w.n = mn.n;
   return true;

@@ -38,10 +38,13 @@ def operands(name):
 
 @pytest.mark.parametrize("run", list(bench.RUNS))
 def test_fullsize_sampled(dev, run):
-    wl, mapping, group, sched, tile, out, workers = bench.RUNS[run]
+    wl, mapping, group, sched, tile, out, workers = bench.RUNS[run][:7]
+    bk = bench.RUNS[run][7] if len(bench.RUNS[run]) > 7 else 0
     op = operands(wl)
     C, plan, _ = run_gpu(op, torch, dev, out, dg.MAPPINGS[mapping], group, dg.SCHEDS[sched],
-                         workers, tile)
+                         workers, tile, bk=bk)
+    if bk:
+        assert plan.info.bk == bk
     assert np.isfinite(C).all()
     rows, cols = gi.sample_positions(op.M, op.N, SAMPLES, seed=len(run), BM=plan.info.bm,
                                      BN=plan.info.bn)
@@ -60,7 +63,7 @@ def test_streamk_workload_bit_exact_small_integers(dev):
     the full output must equal the oracle bit for bit."""
     op = gi.make_operands(512, 512, 65536, "bf16", ("smallint", -2, 2), ("smallint", -2, 2),
                           seed=55)
-    wl, mapping, group, sched, tile, out, workers = bench.RUNS["bf16_streamk"]
+    wl, mapping, group, sched, tile, out, workers = bench.RUNS["bf16_streamk"][:7]
     C, plan, _ = run_gpu(op, torch, dev, out, dg.MAPPINGS[mapping], group, dg.SCHEDS[sched],
                          workers, tile)
     assert plan.info.sk_tiles == 16 and plan.info.dp_tiles == 0
