@@ -55,13 +55,15 @@ def measured_traffic(workload):
 # name, workload key, mapping, group, sched, tile, out, workers[, bk]
 RUNS = {
     "bf16_4096": ("bf16_4096", "grouped_m", 8, "persistent", 0, "bf16", 0),
-    "bf16_4096_k64": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 64),
-    "bf16_4096_k32": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 32),
+    "bf16_4096_pp": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 32),
     "bf16_4096_linear": ("bf16_4096", "linear_n", 1, "persistent", 0, "bf16", 0),
     "bf16_4096_t128": ("bf16_4096", "grouped_m", 8, "persistent", 128, "bf16", 0),
     "fp8_8192": ("fp8_8192", "grouped_m", 16, "persistent", 0, "bf16", 0),
+    "fp8_8192_pp": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 64),
     "bf16_mlp_up": ("bf16_mlp_up", "grouped_m", 8, "persistent", 0, "bf16", 0),
     "bf16_streamk": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256),
+    "bf16_streamk_chain": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256, 0,
+                           "chain"),
     "bf16_256": ("bf16_256", "linear_n", 1, "static", 128, "f32", 0),
 }
 
@@ -69,6 +71,7 @@ RUNS = {
 def time_run(name, steps, warmup, torch, dg, gi, cache):
     wl_name, mapping, group, sched, tile, out, workers = RUNS[name][:7]
     bk = RUNS[name][7] if len(RUNS[name]) > 7 else 0
+    flags = dg.GEMM_FLAG_STREAMK_CHAIN if len(RUNS[name]) > 8 and RUNS[name][8] == "chain" else 0
     wl = gi.WORKLOADS[wl_name]
     if wl_name not in cache:
         t0 = time.time()
@@ -89,7 +92,7 @@ def time_run(name, steps, warmup, torch, dg, gi, cache):
     desc = dg.make_desc(op.M, op.N, op.K,
                         dg.GEMM_BF16 if op.dtype == "bf16" else dg.GEMM_FP8_E4M3,
                         dg.GEMM_BF16 if out == "bf16" else dg.GEMM_F32, dg.MAPPINGS[mapping],
-                        group, dg.SCHEDS[sched], workers, tile, tile, bk, 0)
+                        group, dg.SCHEDS[sched], workers, tile, tile, bk, flags)
     plan = dg.Plan(desc)
     C = torch.empty((op.M, op.N), device=A.device,
                     dtype=torch.bfloat16 if out == "bf16" else torch.float32)

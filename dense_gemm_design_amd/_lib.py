@@ -20,6 +20,7 @@ GEMM_MAP_LINEAR_N, GEMM_MAP_LINEAR_M, GEMM_MAP_GROUPED_M, GEMM_MAP_GROUPED_N = 0
 GEMM_SCHED_STATIC, GEMM_SCHED_PERSISTENT, GEMM_SCHED_STREAMK, GEMM_SCHED_AUTO = 0, 1, 2, 3
 GEMM_FLAG_TRACE = 0x1
 GEMM_FLAG_NO_XCD_REMAP = 0x2
+GEMM_FLAG_STREAMK_CHAIN = 0x4
 GEMM_FLAG_TEST_SKIP_PUBLISH = 0x100
 GEMM_DEVICE_OK, GEMM_DEVICE_ERR_SPIN = 0, 1
 
@@ -49,7 +50,8 @@ class GemmPlanInfo(ctypes.Structure):
                 ("sched", ctypes.c_int32), ("xcds", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
                 ("dp_tiles", ctypes.c_int64), ("sk_tiles", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("trace_offset", ctypes.c_int64),
-                ("trace_capacity", ctypes.c_int32), ("error_offset", ctypes.c_int32)]
+                ("trace_capacity", ctypes.c_int32), ("error_offset", ctypes.c_int32),
+                ("streamk_mode", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _lib = None

@@ -19,14 +19,16 @@ namespace {
 
 using namespace dg;
 
-// Tile configurations.  SWZ = 1 spreads the 16 rows that one 16-lane LDS read phase touches over
-// 16 distinct 16-byte bank groups for 128-byte rows.
+// Tile configurations: TileCfg<dtype, BM, BN, BK, wave rows, wave columns, stages, swizzle>.
+// SWZ spreads the 16 rows one 16-lane LDS read phase touches over 16 distinct 16-byte bank groups
+// (1 for 128-byte rows, 2 for 64-byte rows).  Defaults (first match per tile shape): 8 waves of
+// 128 x 64 sub-tiles with 2 stages of 64 KiB -- two waves per SIMD hide each other's LDS waits.
+// The ping-pong variants (bk 32 for bf16, 64 for e4m3) stay selectable through bk.
+using CfgBf16_256pp = TileCfg<DT_BF16, 256, 256, 32, 2, 4, 4, 2>;
 using CfgBf16_256 = TileCfg<DT_BF16, 256, 256, 64, 2, 4, 2, 1>;
-using CfgBf16_256k32 = TileCfg<DT_BF16, 256, 256, 32, 2, 4, 4, 2>;
-using CfgBf16_256w4 = TileCfg<DT_BF16, 256, 256, 64, 2, 2, 2, 1>;
 using CfgBf16_128 = TileCfg<DT_BF16, 128, 128, 64, 2, 2, 2, 1>;
+using CfgFp8_256pp = TileCfg<DT_FP8, 256, 256, 64, 2, 4, 4, 2>;
 using CfgFp8_256 = TileCfg<DT_FP8, 256, 256, 128, 2, 4, 2, 1>;
-using CfgFp8_256w4 = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1>;
 using CfgFp8_128 = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 2, 1>;
 
 typedef hipError_t (*launch_fn)(const KernelArgs &, int grid, bool ragged_k, hipStream_t);
@@ -44,9 +46,22 @@ template <class CFG>
 const void *kernel_of() {
   return (const void *)&gemm_kernel<CFG, false>;
 }
+template <class CFG>
+hipError_t launch_pp(const KernelArgs &a, int grid, bool ragged_k, hipStream_t s) {
+  if (ragged_k)
+    hipLaunchKernelGGL((gemm_kernel_pp<CFG, true>), dim3(grid), dim3(CFG::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel_pp<CFG, false>), dim3(grid), dim3(CFG::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+template <class CFG>
+const void *kernel_of_pp() {
+  return (const void *)&gemm_kernel_pp<CFG, false>;
+}
 
+// pingpong: runs data-parallel work only (no Stream-K splits, K > 0)
 struct KernelEntry {
-  int dt, bm, bn, bk, threads, stages, lds;
+  int dt, bm, bn, bk, threads, stages, lds, pingpong;
   launch_fn launch;
   kernel_fn kernel;
 };
@@ -54,17 +69,21 @@ struct KernelEntry {
 template <class CFG>
 constexpr KernelEntry entry() {
   return KernelEntry{CFG::DT, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::STAGES,
-                     CFG::LDS_BYTES, &launch_cfg<CFG>, &kernel_of<CFG>};
+                     CFG::LDS_BYTES, 0, &launch_cfg<CFG>, &kernel_of<CFG>};
+}
+template <class CFG>
+constexpr KernelEntry entry_pp() {
+  return KernelEntry{CFG::DT, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::STAGES,
+                     CFG::LDS_BYTES, 1, &launch_pp<CFG>, &kernel_of_pp<CFG>};
 }
 
 // The first entry that matches (dtype, bm, bn[, bk]) is the default for that tile shape.
 const KernelEntry kKernels[] = {
     entry<CfgBf16_256>(),
-    entry<CfgBf16_256k32>(),
-    entry<CfgBf16_256w4>(),
+    entry_pp<CfgBf16_256pp>(),
     entry<CfgBf16_128>(),
     entry<CfgFp8_256>(),
-    entry<CfgFp8_256w4>(),
+    entry_pp<CfgFp8_256pp>(),
     entry<CfgFp8_128>(),
 };
 
@@ -116,7 +135,8 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (grouped && d.group < 1) return GEMM_ERR_INVALID_ARG;
   if (d.sched < GEMM_SCHED_STATIC || d.sched > GEMM_SCHED_AUTO) return GEMM_ERR_INVALID_ARG;
   if (d.num_workers < 0 || d.bm < 0 || d.bn < 0 || d.bk < 0) return GEMM_ERR_INVALID_ARG;
-  if (d.flags & ~(GEMM_FLAG_TRACE | GEMM_FLAG_NO_XCD_REMAP | GEMM_FLAG_TEST_SKIP_PUBLISH))
+  if (d.flags & ~(GEMM_FLAG_TRACE | GEMM_FLAG_NO_XCD_REMAP | GEMM_FLAG_STREAMK_CHAIN |
+                  GEMM_FLAG_TEST_SKIP_PUBLISH))
     return GEMM_ERR_INVALID_ARG;
 
   // Well-formed; now what the kernels implement.
@@ -136,9 +156,13 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     bm = bn = (bm ? bm : bn);
   }
   const int want_dt = d.dtype_ab == GEMM_BF16 ? DT_BF16 : DT_FP8;
+  // the ping-pong kernels run data-parallel work only
+  const bool may_pp = d.K > 0 && d.sched != GEMM_SCHED_STREAMK && d.sched != GEMM_SCHED_AUTO;
   const KernelEntry *k = nullptr;
   for (const KernelEntry &e : kKernels)
-    if (!k && e.dt == want_dt && e.bm == bm && e.bn == bn && (d.bk == 0 || d.bk == e.bk)) k = &e;
+    if (!k && e.dt == want_dt && e.bm == bm && e.bn == bn && (d.bk == 0 || d.bk == e.bk) &&
+        (may_pp || !e.pingpong))
+      k = &e;
   if (!k) return GEMM_ERR_UNSUPPORTED;
   // rows of one tile must stay addressable by 32-bit buffer offsets
   if ((int64_t)bm * d.K * eb >= 0x7FFFFFF0ll || (int64_t)bn * d.K * eb >= 0x7FFFFFF0ll)
@@ -202,12 +226,25 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   p->d = d;
   p->k = k;
 
-  // Workspace: [partials: sk_tiles * BM * BN fp32][locks: sk_tiles int][error word][trace]
+  // Stream-K fixup mode: the separate reduction needs every unit to own at least one iteration
+  // (band of T >= P iterations); otherwise, or when asked, the lock chain.
+  const bool chain = (d.flags & GEMM_FLAG_STREAMK_CHAIN) || (int64_t)sp.sk_tiles * Kt < sp.P;
+  const int sk_mode = chain ? SK_CHAIN : SK_SEPARATE;
+  // partial tiles: one per split tile (chain), or one per (unit, tile) pair, indexed unit + tile,
+  // at most P + sk_tiles of them (separate)
+  const int64_t partial_slots = sp.sk_tiles == 0 ? 0 : (chain ? sp.sk_tiles : sp.P + sp.sk_tiles);
+  // the kernels address the partial area with 32-bit buffer offsets
+  if (partial_slots * (int64_t)bm * bn * 4 > 0x7FFFFFF0ll) {
+    delete p;
+    return GEMM_ERR_UNSUPPORTED;
+  }
+
+  // Workspace: [partials][locks or counters: sk_tiles int][error word][trace]
   int64_t off = 0;
   p->partial_off = p->lock_off = p->error_off = p->trace_off = -1;
   if (sp.sk_tiles > 0 || (d.flags & GEMM_FLAG_TRACE)) {
     p->partial_off = 0;
-    off = sp.sk_tiles * (int64_t)bm * bn * 4;
+    off = partial_slots * (int64_t)bm * bn * 4;
     p->lock_off = off;
     off = align_up(off + sp.sk_tiles * 4, 256);
     p->error_off = off;
@@ -232,6 +269,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   a.flags = d.flags;
   a.trace_cap = kTraceCap;
   a.max_spin = (d.flags & GEMM_FLAG_TEST_SKIP_PUBLISH) ? kTestSpin : kDefaultSpin;
+  a.sk_mode = sk_mode;
 
   gemm_plan_info &in = p->info;
   in.bm = k->bm;
@@ -252,6 +290,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   in.trace_offset = p->trace_off;
   in.trace_capacity = (d.flags & GEMM_FLAG_TRACE) ? kTraceCap : 0;
   in.error_offset = (int32_t)p->error_off;
+  in.streamk_mode = sk_mode;
   *out = p;
   return GEMM_OK;
 }

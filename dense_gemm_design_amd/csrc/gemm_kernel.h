@@ -57,14 +57,17 @@ enum { DT_BF16 = 0, DT_FP8 = 1 };
 // Flags shared with the C ABI (gemm.h).
 enum : uint32_t { KF_TRACE = 0x1u, KF_TEST_SKIP_PUBLISH = 0x100u };
 
+// Stream-K fixup modes.
+enum { SK_CHAIN = 0, SK_SEPARATE = 1 };
+
 struct KernelArgs {
   const char *A;           // M x K, row pitch lda_bytes
   const char *B;           // N x K (K x N column-major), row pitch ldb_bytes
   char *C;                 // M x N row-major, ldc elements per row
   const float *scale_a;    // FP8 only
   const float *scale_b;
-  float *partials;         // Stream-K slots, BM*BN floats each
-  int *locks;              // one per Stream-K slot
+  float *partials;         // Stream-K partial tiles, BM*BN floats each
+  int *locks;              // per split tile: lock (chain mode) or arrival counter (separate)
   int *error_word;
   int *trace;              // 8 ints per record, trace_cap records per workgroup
   int64_t M, N, K;
@@ -74,6 +77,8 @@ struct KernelArgs {
   uint32_t flags;
   int32_t trace_cap;
   int32_t max_spin;
+  int32_t sk_mode;         // SK_CHAIN or SK_SEPARATE
+  int32_t pad_;
 };
 
 template <int DT_, int BM_, int BN_, int BK_, int WGM_, int WGN_, int STAGES_, int SWZ_>
@@ -104,9 +109,6 @@ struct TileCfg {
   static_assert(LA + LB <= 63, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS per workgroup");
   static_assert((32 >> SWZ) % CH == 0, "swizzle must not depend on the 32-row block");
-  // An even number of MFMA sub-steps per k-tile keeps the two fragment buffers in fixed roles,
-  // so a fragment load never targets registers an in-flight MFMA is still reading.
-  static_assert(KSUB % 2 == 0, "k-tile must hold an even number of MFMA sub-steps");
 };
 
 // ---- small device helpers ------------------------------------------------------------------
@@ -137,6 +139,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *base, in
 }
 
 constexpr uint32_t kOOB = 0x80000000u;  // any offset >= num_records reads as zero
+
+// Stream-K partial sums move between workgroups on different XCDs, each with its own L2.  They
+// are written and read with device-coherent buffer accesses (cache-policy bit sc1: the line is
+// not served from or left dirty in a non-coherent L2), and ordered by s_waitcnt vmcnt(0) plus the
+// workgroup barrier before the flag store -- instead of agent-scope fences, which write back and
+// invalidate the whole L2 of the XCD.  The accesses are compiler builtins, so the compiler itself
+// places the waits before each use of a loaded value.  Offsets are bytes from the start of the
+// partial-tile area, which the planner keeps below 2 GiB.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCachePolicySC1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const float *partials) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)partials, (short)0, 0x7FFFFFF0, 0x00020000);
+}
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCachePolicySC1);
+}
+__device__ __forceinline__ f32x4 load_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicySC1));
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
@@ -308,57 +329,199 @@ __device__ __forceinline__ bool wait_lock(int *lock, int want, int max_spin) {
   return false;
 }
 
-// Epilogue of one work item, one accumulator quad (4 consecutive n of one row m) at a time:
-//   whole tile: C = cast(alpha * acc);  first split: slot = acc;  middle split: slot = slot + acc;
-//   final split: C = cast(alpha * (slot + acc)).  The accumulators are only read here.
+// Output store of one accumulator quad: 4 consecutive n of row m, times alpha, cast.
+template <class CFG>
+__device__ __forceinline__ void store_quad(const KernelArgs &args, int64_t m, int64_t n, f32x4 v,
+                                           float alpha) {
+  if (m >= args.M || n >= args.N) return;
+  v = v * alpha;
+  if (args.out_bf16) {
+    u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *(u32x2 *)(args.C + (m * args.ldc + n) * 2) = pk;
+  } else {
+    *(f32x4 *)(args.C + (m * args.ldc + n) * 4) = v;
+  }
+}
+
+template <class CFG, int F, int G, int Q>
+__device__ __forceinline__ f32x4 acc_quad(const f32x16 (&acc)[CFG::FM][CFG::FN]) {
+  return f32x4{acc[F][G][4 * Q + 0], acc[F][G][4 * Q + 1], acc[F][G][4 * Q + 2],
+               acc[F][G][4 * Q + 3]};
+}
+
+// Whole tile: C = cast(alpha * acc), one accumulator quad at a time.  The lane holds, for its
+// MFMA block (f, g), rows m = f*32 + lane%32 and columns n = g*32 + 8q + 4*(lane/32) + 0..3.
 template <class CFG>
 __device__ __forceinline__ void epilogue(const KernelArgs &args, const WorkItem &w,
                                          const f32x16 (&acc)[CFG::FM][CFG::FN], float alpha,
                                          int wm, int wn, int tid) {
   const int lane = tid & 63;
-  const bool add_slot = w.role == ROLE_MIDDLE || w.role == ROLE_LAST;
-  const bool to_slot = w.role == ROLE_FIRST || w.role == ROLE_MIDDLE;
-  f32x4 *slot = (f32x4 *)(args.partials + (int64_t)(w.sk_slot < 0 ? 0 : w.sk_slot) * CFG::BM *
-                                              CFG::BN) + tid;
   const int64_t mbase = (int64_t)w.m * CFG::BM + wm * CFG::WM + (lane & 31);
   const int64_t nbase = (int64_t)w.n * CFG::BN + wn * CFG::WN + (lane >> 5) * 4;
 #pragma unroll
-  for (int f = 0; f < CFG::FM; ++f) {
-    const int64_t m = mbase + f * 32;
+  for (int f = 0; f < CFG::FM; ++f)
 #pragma unroll
-    for (int g = 0; g < CFG::FN; ++g) {
+    for (int g = 0; g < CFG::FN; ++g)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int qi = (f * CFG::FN + g) * 4 + q;  // slot layout: quad-major, lane-minor
-        f32x4 v = {acc[f][g][4 * q + 0], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2],
-                   acc[f][g][4 * q + 3]};
-        if (add_slot) {
-          const f32x4 p = slot[qi * CFG::THREADS];
-          v = p + v;
-        }
-        if (to_slot) {
-          slot[qi * CFG::THREADS] = v;
-          continue;
-        }
-        const int64_t n = nbase + g * 32 + q * 8;
-        if (m >= args.M || n >= args.N) continue;
-        v = v * alpha;
-        if (args.out_bf16) {
-          u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          *(u32x2 *)(args.C + (m * args.ldc + n) * 2) = pk;
-        } else {
-          *(f32x4 *)(args.C + (m * args.ldc + n) * 4) = v;
-        }
+        const f32x4 v = {acc[f][g][4 * q + 0], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2],
+                         acc[f][g][4 * q + 3]};
+        store_quad<CFG>(args, mbase + f * 32, nbase + g * 32 + q * 8, v, alpha);
       }
-    }
+}
+
+// Partial-tile slot layout: quad qi = (f * FN + g) * 4 + q of thread tid sits at
+// quad index qi * THREADS + tid of the slot -- each access is a contiguous 1 KiB run per wave.
+template <class CFG>
+__device__ __forceinline__ uint32_t slot_byte(int64_t slot) {
+  return (uint32_t)(slot * (CFG::BM * CFG::BN * 4));
+}
+
+// Chain fixup ("H100 Stream-K" lesson, section 6, deterministic mode): the first split stores its
+// partial; every later split waits until the lock equals its K_idx, adds the slot to its own sum
+// and either stores it back (middle) or finishes the tile (final).  The lock then becomes
+// K_idx + k_tile_count.  Sums are formed left to right in K.
+template <class CFG>
+__device__ __forceinline__ void fixup_chain(const KernelArgs &args, const WorkItem &w,
+                                            const f32x16 (&acc)[CFG::FM][CFG::FN], float alpha,
+                                            int wm, int wn, int tid) {
+  const int lane = tid & 63;
+  const bool add_slot = w.role == ROLE_MIDDLE || w.role == ROLE_LAST;
+  const bool to_slot = w.role == ROLE_FIRST || w.role == ROLE_MIDDLE;
+  int *lock = args.locks + w.sk_slot;
+  const __amdgpu_buffer_rsrc_t pr = partial_rsrc(args.partials);
+  const uint32_t slot = slot_byte<CFG>(w.sk_slot) + tid * 16;
+  if (add_slot) {
+    if (tid == 0 && !wait_lock(lock, w.kb, args.max_spin))
+      __hip_atomic_store(args.error_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lds_barrier();
+  }
+  const int64_t mbase = (int64_t)w.m * CFG::BM + wm * CFG::WM + (lane & 31);
+  const int64_t nbase = (int64_t)w.n * CFG::BN + wn * CFG::WN + (lane >> 5) * 4;
+  constexpr int NQ = CFG::FM * CFG::FN * 4;
+  constexpr int BATCH = NQ < 4 ? NQ : 4;
+  [&]<int... BI>(std::integer_sequence<int, BI...>) {
+    (
+        [&] {
+          constexpr int q0 = BI * BATCH;
+          f32x4 p[BATCH];
+          if (add_slot) {
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i)
+              p[i] = load_coherent(pr, slot + (q0 + i) * CFG::THREADS * 16);
+          }
+#pragma unroll
+          for (int i = 0; i < BATCH; ++i) {
+            const int qi = q0 + i, fg = qi / 4, q = qi % 4, f = fg / CFG::FN, g = fg % CFG::FN;
+            f32x4 v = {acc[f][g][4 * q + 0], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2],
+                       acc[f][g][4 * q + 3]};
+            if (add_slot) v = p[i] + v;
+            if (to_slot)
+              store_coherent(pr, slot + qi * CFG::THREADS * 16, v);
+            else
+              store_quad<CFG>(args, mbase + f * 32, nbase + g * 32 + q * 8, v, alpha);
+          }
+          // one batch of four loads in flight at a time: the accumulators fill most registers
+          __builtin_amdgcn_sched_barrier(0);
+        }(),
+        ...);
+  }(std::make_integer_sequence<int, NQ / BATCH>());
+  if (to_slot) {
+    wait_vmcnt<0>();  // this wave's slot stores are complete ...
+    lds_barrier();    // ... and so are everyone's: publish
+    const bool skip = (args.flags & KF_TEST_SKIP_PUBLISH) && w.sk_slot == 0 && w.role == ROLE_FIRST;
+    if (tid == 0 && !skip)
+      __hip_atomic_store(lock, w.ke, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// RAGGED_K: K is not a multiple of BK, so the last k-tile of every tile masks its tail.
+// Separate-reduction fixup, part 1: split (unit b on band tile t) stores its partial into its own
+// slot b + t and arrives on the tile's counter.
+template <class CFG>
+__device__ __forceinline__ void fixup_separate_store(const KernelArgs &args, const WorkItem &w,
+                                                     const f32x16 (&acc)[CFG::FM][CFG::FN],
+                                                     int32_t b, int tid) {
+  const __amdgpu_buffer_rsrc_t pr = partial_rsrc(args.partials);
+  const uint32_t slot = slot_byte<CFG>((int64_t)b + w.sk_slot) + tid * 16;
+#pragma unroll
+  for (int f = 0; f < CFG::FM; ++f)
+#pragma unroll
+    for (int g = 0; g < CFG::FN; ++g)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {acc[f][g][4 * q + 0], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2],
+                         acc[f][g][4 * q + 3]};
+        store_coherent(pr, slot + ((f * CFG::FN + g) * 4 + q) * CFG::THREADS * 16, v);
+      }
+  wait_vmcnt<0>();
+  lds_barrier();
+  const bool skip = (args.flags & KF_TEST_SKIP_PUBLISH) && w.sk_slot == 0 && w.role == ROLE_FIRST;
+  if (tid == 0 && !skip)
+    __hip_atomic_fetch_add(args.locks + w.sk_slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Separate-reduction fixup, part 2 (after every unit has stored its partials, so no unit ever
+// waits on another unit's reduction): unit b, the j-th of the n units u0..u1 of tile t, waits for
+// all n arrivals, then sums the n partials of its 1/n share of the tile in K order (u0 first --
+// the same association as the chain) and writes that share of C.
+template <class CFG>
+__device__ __forceinline__ void fixup_separate_reduce(const KernelArgs &args, const WorkItem &w,
+                                                      float alpha, int32_t b, int tid) {
+  int32_t u0, u1;
+  sk_tile_units(args.sp, w.sk_slot, u0, u1);
+  const int n = u1 - u0 + 1, j = b - u0;
+  if (tid == 0) {
+    int *cnt = args.locks + w.sk_slot;
+    bool ok = false;
+    for (int i = 0; i < args.max_spin; ++i) {
+      if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n) {
+        ok = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (!ok) __hip_atomic_store(args.error_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  lds_barrier();
+  constexpr int NQ = CFG::BM * CFG::BN / 4;
+  const int q_begin = (int)((int64_t)NQ * j / n), q_end = (int)((int64_t)NQ * (j + 1) / n);
+  const __amdgpu_buffer_rsrc_t pr = partial_rsrc(args.partials);
+  const uint32_t base = slot_byte<CFG>((int64_t)u0 + w.sk_slot);
+  constexpr uint32_t SLOT = CFG::BM * CFG::BN * 4;
+  for (int qq = q_begin + tid; qq < q_end; qq += CFG::THREADS) {
+    // sum over u = 0..n-1 of slot u0 + t + u, left to right; four loads in flight per step
+    const uint32_t off = base + qq * 16;
+    f32x4 sum = load_coherent(pr, off);
+    int u = 1;
+    for (; u + 4 <= n; u += 4) {
+      const f32x4 p0 = load_coherent(pr, off + (u + 0) * SLOT);
+      const f32x4 p1 = load_coherent(pr, off + (u + 1) * SLOT);
+      const f32x4 p2 = load_coherent(pr, off + (u + 2) * SLOT);
+      const f32x4 p3 = load_coherent(pr, off + (u + 3) * SLOT);
+      sum = sum + p0;
+      sum = sum + p1;
+      sum = sum + p2;
+      sum = sum + p3;
+    }
+    for (; u < n; ++u) sum = sum + load_coherent(pr, off + u * SLOT);
+    // storage index qq = ((f * FN + g) * 4 + q) * THREADS + tid_src  ->  (m, n) of the quad
+    const int tid_src = qq % CFG::THREADS, rest = qq / CFG::THREADS;
+    const int q = rest % 4, fg = rest / 4, g = fg % CFG::FN, f = fg / CFG::FN;
+    const int wave_src = tid_src >> 6, lane = tid_src & 63;
+    const int wm = wave_src / CFG::WGN, wn = wave_src % CFG::WGN;
+    const int64_t m = (int64_t)w.m * CFG::BM + wm * CFG::WM + f * 32 + (lane & 31);
+    const int64_t nn = (int64_t)w.n * CFG::BN + wn * CFG::WN + g * 32 + q * 8 + (lane >> 5) * 4;
+    store_quad<CFG>(args, m, nn, sum, alpha);
+  }
+}
+
 template <class CFG, bool RAGGED_K>
 __global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::THREADS),
                                amdgpu_waves_per_eu(CFG::WAVES_PER_SIMD, CFG::WAVES_PER_SIMD)))
 gemm_kernel(KernelArgs args) {
+  // An even number of MFMA sub-steps per k-tile keeps the two fragment buffers in fixed roles,
+  // so a fragment load never targets registers an in-flight MFMA is still reading.
+  static_assert(CFG::KSUB % 2 == 0, "k-tile must hold an even number of MFMA sub-steps");
   __shared__ __attribute__((aligned(1024))) char smem_raw[CFG::LDS_BYTES];
   lds_t *smem = (lds_t *)(size_t)(uint32_t)(size_t)(lds_t *)smem_raw;
 
@@ -513,29 +676,156 @@ gemm_kernel(KernelArgs args) {
       }(std::make_integer_sequence<int, CFG::KSUB>());
     }
 
-    // ---- Stream-K fixup handshake around the epilogue ----
-    if (cw.role == ROLE_MIDDLE || cw.role == ROLE_LAST) {
-      // wait until the k-tiles before K_idx have been reduced into the slot
-      if (tid == 0 && !wait_lock(args.locks + cw.sk_slot, cw.kb, args.max_spin))
-        __hip_atomic_store(args.error_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      lds_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
-    epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid);
-    if (cw.role == ROLE_FIRST || cw.role == ROLE_MIDDLE) {
-      // publish: the slot now holds k-tiles [0, K_idx + count)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      lds_barrier();
-      const bool skip =
-          (args.flags & KF_TEST_SKIP_PUBLISH) && cw.sk_slot == 0 && cw.role == ROLE_FIRST;
-      if (tid == 0 && !skip)
-        __hip_atomic_store(args.locks + cw.sk_slot, cw.ke, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (cw.role == ROLE_WHOLE)
+      epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid);
+    else if (args.sk_mode == SK_CHAIN)
+      fixup_chain<CFG>(args, cw, acc, alpha, wm, wn, tid);
+    else
+      fixup_separate_store<CFG>(args, cw, acc, b, tid);
 
     ++seq;
     cvalid = cursor_next(args.sp, ccur, cw);
   }
+  if (args.sk_mode == SK_SEPARATE && args.sp.sk_tiles > 0) {
+    // second pass over this unit's splits: reduce its share of each tile it touched
+    Cursor rc;
+    cursor_init(args.sp, b, rc);
+    WorkItem rw;
+    while (cursor_next(args.sp, rc, rw))
+      if (rw.role != ROLE_WHOLE) fixup_separate_reduce<CFG>(args, rw, alpha, b, tid);
+  }
+  wait_vmcnt<0>();
+}
+
+// ---- ping-pong kernel (data-parallel tiles) --------------------------------------------------
+//
+// The pages' ping-pong consumer schedule ("H100 Kernel Design" lesson, sections 7.3-7.5) mapped
+// onto two waves per SIMD.  The 8 waves form two groups of 4 (one wave per SIMD each); group g
+// owns rows [g*BM/2, (g+1)*BM/2) of the tile.  Each group alternates a memory phase M(s) -- read
+// all MFMA fragments of k-step s from LDS, issue its share of the loads of step s+S-1 -- and a
+// compute phase C(s) -- MFMAs only (plus the epilogue after an item's last step).  Group 1 runs one
+// barrier-phase behind group 0, so in every phase one wave per SIMD issues MFMAs while the other
+// does memory work, and one group's epilogue overlaps the other group's MFMAs.
+//
+// Phases are separated by workgroup barriers.  Group 0 runs M(0) C(0) M(1) C(1) ...; group 1 waits
+// one phase, then runs the same sequence.  Ring hand-offs (S stages):
+//  * EMPTY: step s-1 was read by group 0 in phase 2s-2 and by group 1 in phase 2s-1 (each wave
+//    waits for its own reads with lgkmcnt(0) before the barrier), so from phase 2s on, stage
+//    (s-1) mod S may take step s+S-1; group 0 issues its loads in phase 2s, group 1 in 2s+1.
+//  * FULL: before the barrier that opens phase 2s+2 (group 0 reads step s+1 there), every wave
+//    waits for its own loads of step s+1 (s_waitcnt vmcnt).
+template <class CFG, bool RAGGED_K>
+__global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::THREADS),
+                               amdgpu_waves_per_eu(2, 2)))
+gemm_kernel_pp(KernelArgs args) {
+  static_assert(CFG::WAVES == 8 && CFG::WGM == 2, "ping-pong: two groups of four waves");
+  static_assert(CFG::STAGES >= 3, "ping-pong needs a stage of slack for the lagging group");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[CFG::LDS_BYTES];
+  lds_t *smem = (lds_t *)(size_t)(uint32_t)(size_t)(lds_t *)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / CFG::WGN, wn = wave % CFG::WGN;
+  const int group = wm;
+  const int32_t b = blockIdx.x;
+
+  float alpha = 1.0f;
+  if constexpr (CFG::DT == DT_FP8) alpha = (*args.scale_a) * (*args.scale_b);
+
+  uint32_t aoff[CFG::KSUB][CFG::CPL], boff[CFG::KSUB][CFG::CPL];
+  {
+    const int r = lane & 31;
+    const int swz = (r >> CFG::SWZ) & (CFG::CH - 1);
+#pragma unroll
+    for (int s = 0; s < CFG::KSUB; ++s)
+#pragma unroll
+      for (int h = 0; h < CFG::CPL; ++h) {
+        const int chunk = (s * 2 + (lane >> 5)) * CFG::CPL + h;
+        const uint32_t in_row = (uint32_t)((chunk ^ swz) * 16);
+        aoff[s][h] = (uint32_t)((wm * CFG::WM + r) * CFG::ROWB) + in_row;
+        boff[s][h] = (uint32_t)(CFG::A_BYTES + (wn * CFG::WN + r) * CFG::ROWB) + in_row;
+      }
+  }
+
+  constexpr int L = CFG::LA + CFG::LB;
+  constexpr int NF = CFG::FM + CFG::FN;
+  Producer<CFG, RAGGED_K> prod;
+  prod.init(args, b, wave, lane);
+  auto issue_all = [&](int stage) {
+    prod.begin(args, smem, stage);
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      (prod.template load<J>(wave, lane), ...);
+    }(std::make_integer_sequence<int, L>());
+    prod.end(args, wave, lane);
+  };
+
+  Cursor ccur;
+  cursor_init(args.sp, b, ccur);
+  WorkItem cw;
+  bool cvalid = cursor_next(args.sp, ccur, cw);
+
+  int issued = 0;
+#pragma unroll
+  for (int s = 0; s < CFG::STAGES - 1; ++s)
+    if (prod.valid) {
+      issue_all(s);
+      ++issued;
+    }
+  if (issued > 0) wait_loads_after<L>(issued - 1);
+  lds_barrier();            // phase 0 begins: step 0 is in LDS
+  if (group == 1) lds_barrier();  // group 1 sits out phase 0
+
+  Frags<CFG> fr[CFG::KSUB];
+  int c = 0;
+  int seq = 0;
+  while (cvalid) {
+    if ((args.flags & KF_TRACE) && tid == 0 && seq < args.trace_cap) {
+      int *t = args.trace + ((int64_t)b * args.trace_cap + seq) * 8;
+      t[0] = b; t[1] = seq; t[2] = cw.tile; t[3] = cw.m;
+      t[4] = cw.n; t[5] = cw.kb; t[6] = cw.ke; t[7] = cw.role;
+    }
+    ++seq;
+    f32x16 acc[CFG::FM][CFG::FN];
+#pragma unroll
+    for (int f = 0; f < CFG::FM; ++f)
+#pragma unroll
+      for (int g = 0; g < CFG::FN; ++g)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.0f;
+
+    for (int k = cw.kb; k < cw.ke; ++k, ++c) {
+      // ---- M(c): fragments of step c, loads of step c+S-1 ----
+      const int stage = c % CFG::STAGES;
+#pragma unroll
+      for (int t = 0; t < CFG::KSUB; ++t)
+        [&]<int... E>(std::integer_sequence<int, E...>) {
+          (load_frag<CFG, E>(smem, stage, t, aoff, boff, fr[t]), ...);
+        }(std::make_integer_sequence<int, NF>());
+      if (prod.valid) {
+        issue_all((c + CFG::STAGES - 1) % CFG::STAGES);
+        ++issued;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (group == 1) wait_loads_after<L>(issued - (c + 1) - 1);
+      lds_barrier();
+      // ---- C(c): MFMAs ----
+#pragma unroll
+      for (int t = 0; t < CFG::KSUB; ++t)
+#pragma unroll
+        for (int f = 0; f < CFG::FM; ++f)
+#pragma unroll
+          for (int g = 0; g < CFG::FN; ++g)
+            acc[f][g] = mfma<CFG::DT>(fr[t].b[g], fr[t].a[f], acc[f][g]);
+      if (group == 0) wait_loads_after<L>(issued - (c + 1) - 1);
+      lds_barrier();
+    }
+    // the stores run at the start of this group's next memory phase, under the other group's
+    // MFMAs
+    epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid);
+    cvalid = cursor_next(args.sp, ccur, cw);
+  }
+  if (group == 0) lds_barrier();  // balance the barrier group 1 skipped at the start
   wait_vmcnt<0>();
 }
 

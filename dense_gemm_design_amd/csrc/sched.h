@@ -183,6 +183,19 @@ DG_HD bool cursor_next(const SchedParams &sp, Cursor &c, WorkItem &w) {
   return true;
 }
 
+// Stream-K units that share band-local tile t: unit u covers iterations
+// [floor(u T / P), floor((u+1) T / P)), so the unit holding iteration x is the largest u with
+// floor(u T / P) <= x, i.e. floor(((x + 1) P - 1) / T).  Tile t spans iterations
+// [t Kt, (t+1) Kt); its units are u0 .. u1, consecutive, in increasing K order.
+DG_HD int32_t sk_unit_of(const SchedParams &sp, int64_t x) {
+  const int64_t T = (int64_t)sp.sk_tiles * sp.Kt;
+  return (int32_t)(((x + 1) * sp.P - 1) / T);
+}
+DG_HD void sk_tile_units(const SchedParams &sp, int32_t t, int32_t &u0, int32_t &u1) {
+  u0 = sk_unit_of(sp, (int64_t)t * sp.Kt);
+  u1 = sk_unit_of(sp, (int64_t)(t + 1) * sp.Kt - 1);
+}
+
 // Hybrid rule: with P workers and `tiles` tasks, the full waves stay data parallel; the tail
 // wave goes to Stream-K only when it is at most half full, otherwise everything is data parallel.
 DG_HD void streamk_plan(int64_t tiles, int32_t P, int32_t &dp_tiles, int32_t &sk_tiles) {

@@ -64,9 +64,12 @@ typedef enum {
 /* flags */
 #define GEMM_FLAG_TRACE 0x1u         /* kernel records every work item it runs in the workspace  */
 #define GEMM_FLAG_NO_XCD_REMAP 0x2u  /* keep worker id = workgroup id (no XCD-contiguous remap)  */
-#define GEMM_FLAG_TEST_SKIP_PUBLISH 0x100u /* test only: the first Stream-K split of slot 0 does
-                                              not publish its lock, so its successor's bounded
-                                              wait expires and reports GEMM_DEVICE_ERR_SPIN      */
+#define GEMM_FLAG_STREAMK_CHAIN 0x4u /* Stream-K fixup as the lock chain of "H100 Stream-K"
+                                        section 6 (each split waits for its predecessor); default
+                                        is the separate reduction, same sums in the same order   */
+#define GEMM_FLAG_TEST_SKIP_PUBLISH 0x100u /* test only: the first Stream-K split of band tile 0
+                                              does not publish its lock / arrival, so the bounded
+                                              waits on it expire and report GEMM_DEVICE_ERR_SPIN */
 
 /* Problem description.  0 in an "auto" field lets the planner choose. */
 typedef struct gemm_desc {
@@ -107,6 +110,8 @@ typedef struct gemm_plan_info {
   int64_t trace_offset;      /* byte offset of the trace records in the workspace (-1: none)    */
   int32_t trace_capacity;    /* records per workgroup                                            */
   int32_t error_offset;      /* byte offset of the device error word in the workspace (-1: none)*/
+  int32_t streamk_mode;      /* 0 lock chain, 1 separate reduction (meaningful when sk_tiles>0)  */
+  int32_t reserved;
 } gemm_plan_info;
 
 /* device error word values (read back from the workspace after a run) */

@@ -40,9 +40,10 @@ def operands(name):
 def test_fullsize_sampled(dev, run):
     wl, mapping, group, sched, tile, out, workers = bench.RUNS[run][:7]
     bk = bench.RUNS[run][7] if len(bench.RUNS[run]) > 7 else 0
+    chain = len(bench.RUNS[run]) > 8 and bench.RUNS[run][8] == "chain"
     op = operands(wl)
     C, plan, _ = run_gpu(op, torch, dev, out, dg.MAPPINGS[mapping], group, dg.SCHEDS[sched],
-                         workers, tile, bk=bk)
+                         workers, tile, bk=bk, flags=L.GEMM_FLAG_STREAMK_CHAIN if chain else 0)
     if bk:
         assert plan.info.bk == bk
     assert np.isfinite(C).all()

@@ -63,12 +63,19 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_small_parity(dev, case):
+SK_MODES = {"separate": 0, "chain": L.GEMM_FLAG_STREAMK_CHAIN}
+CASES = [(c, m) for c in SMALL for m in (SK_MODES if c[9] == L.GEMM_SCHED_STREAMK else ["separate"])]
+
+
+@pytest.mark.parametrize("case,mode", CASES, ids=[f"{c[0]}-{m}" for c, m in CASES])
+def test_small_parity(dev, case, mode):
     name, M, N, K, dt, out, tile, mapping, G, sched, workers = case
     dist = ("normal", 1.0) if dt == "e4m3" else ("uniform",)
     op = gi.make_operands(M, N, K, dt, dist, dist, seed=zlib.crc32(name.encode()) % 10000)
-    C, plan, _ = run_gpu(op, torch, dev, out, mapping, G, sched, workers, tile)
+    C, plan, _ = run_gpu(op, torch, dev, out, mapping, G, sched, workers, tile,
+                         flags=SK_MODES[mode])
+    if plan.info.sk_tiles:
+        assert plan.info.streamk_mode == (0 if mode == "chain" else 1)
     if sched == L.GEMM_SCHED_STREAMK and name != "bf16_streamk_hybrid":
         assert plan.info.sk_tiles > 0
     if name == "bf16_streamk_hybrid":
@@ -88,23 +95,30 @@ def test_closed_form_row_sums_exact(dev, dt, tile, sched, workers):
     assert np.all(C == 7 * K / 16)
 
 
-def test_streamk_small_integers_bit_exact(dev):
+@pytest.mark.parametrize("mode", list(SK_MODES))
+def test_streamk_small_integers_bit_exact(dev, mode):
     """|a|, |b| <= 2 integers: every partial sum is exact in FP32, so the Stream-K fixup must
     reproduce the oracle bit for bit (a lost or doubled k-tile would show)."""
     M, N, K = 256, 128, 16384
     op = gi.make_operands(M, N, K, "bf16", ("smallint", -2, 2), ("smallint", -2, 2), seed=77)
     C, plan, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK,
-                         24, 128)
+                         24, 128, flags=SK_MODES[mode])
     assert plan.info.sk_tiles == 2
     assert np.array_equal(C, reference(op))
 
 
-def test_streamk_deterministic(dev):
+def test_streamk_modes_deterministic_and_identical(dev):
+    """Both fixups sum the splits of a tile left to right in K, so they agree bit for bit with
+    each other and with themselves across runs."""
     op = gi.make_operands(256, 256, 8192, "bf16", seed=5)
     C1, plan, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK,
                           16, 128)
     C2, _, _ = run_gpu(op, torch, dev, "f32", plan=plan)
+    C3, plan3, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK,
+                           16, 128, flags=L.GEMM_FLAG_STREAMK_CHAIN)
+    assert plan.info.streamk_mode == 1 and plan3.info.streamk_mode == 0
     assert np.array_equal(C1, C2)
+    assert np.array_equal(C1, C3)
 
 
 @pytest.mark.parametrize("sched,workers,tile,mapping,G", [
@@ -136,12 +150,13 @@ def test_device_trace_matches_enumeration(dev, sched, workers, tile, mapping, G)
     assert_within_tolerance(C, reference(op), op, "trace run")
 
 
-def test_spin_watchdog_reports_instead_of_hanging(dev):
-    """The first split of slot 0 withholds its lock (test flag); its successor's bounded wait
-    expires, the kernel still finishes, and the device error word says so."""
+@pytest.mark.parametrize("mode", list(SK_MODES))
+def test_spin_watchdog_reports_instead_of_hanging(dev, mode):
+    """The first split of band tile 0 withholds its lock / arrival (test flag); the bounded waits
+    on it expire, the kernel still finishes, and the device error word says so."""
     op = gi.make_operands(256, 256, 4096, "bf16", seed=9)
     C, plan, ws = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK, 8,
-                          128, flags=L.GEMM_FLAG_TEST_SKIP_PUBLISH)
+                          128, flags=L.GEMM_FLAG_TEST_SKIP_PUBLISH | SK_MODES[mode])
     err = int(ws.cpu().numpy()[plan.info.error_offset:plan.info.error_offset + 4].view(np.int32)[0])
     assert err == L.GEMM_DEVICE_ERR_SPIN
     # and a normal run of the same plan shape reports no error
