@@ -1,12 +1,21 @@
 """Benchmark of the MI355X dense GEMM: one step = one C = alpha * A x B through the C ABI.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only NAME]
+                [--copy-calib-mib N]
+python bench.py --ingest-pmc FETCH_CSV WRITE_CSV --only NAME --command "..."   (CPU only)
 
 Headline: BF16 M = N = K = 4096, uniform[-1, 1] operands resident in HBM, FP32 accumulate, bf16
 output, grouped-M (G = 8) tile mapping, persistent scheduler.  The JSON line's "secondary" block
 carries the other workloads (FP8 e4m3 8192^3 with per-tensor scales, the 4096 x 14336 x 4096 MLP
 shape, the 512 x 512 x 65536 Stream-K case, 256^3) timed the same way.  Progress goes to stderr;
 stdout holds exactly one JSON line.
+
+HBM traffic: two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over
+`bench.py --only NAME --copy-calib-mib N`, which after the GEMM launches copies N MiB device to
+device with the runtime's plain copy kernel.  --ingest-pmc scales each GEMM counter by
+known copy bytes / the same counter on that copy, and writes the per-launch figure, keyed by a
+hash of the kernel sources, to profiles/hbm_traffic.json.txt; the JSON line's roofline.traffic
+uses it only while the sources still match.
 """
 import argparse
 import hashlib
@@ -35,10 +44,75 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "hbm_traffic.json.txt")
+
+
+def _read_counter_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _gemm_and_copy(rows, counter):
+    """Per-dispatch counter values (KiB) of the GEMM kernel and of the calibration copies (the
+    copy-kernel dispatches after the last GEMM dispatch)."""
+    rows = [r for r in rows if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    gemm = [r for r in rows if "gemm_kernel" in r["Kernel_Name"]]
+    if not gemm:
+        raise SystemExit(f"no gemm_kernel dispatch with {counter}")
+    last = max(int(r["Dispatch_Id"]) for r in gemm)
+    copy = [r for r in rows if int(r["Dispatch_Id"]) > last and "copyBuffer" in r["Kernel_Name"]]
+    if not copy:
+        raise SystemExit(f"no calibration copy dispatch with {counter} after the GEMMs")
+    return [float(r["Counter_Value"]) for r in gemm], [float(r["Counter_Value"]) for r in copy]
+
+
+def ingest_pmc(fetch_csv, write_csv, name, command, copy_mib):
+    import statistics
+    wl = RUNS[name][0]
+    fg, fc = _gemm_and_copy(_read_counter_csv(fetch_csv), "FETCH_SIZE")
+    wg, wc = _gemm_and_copy(_read_counter_csv(write_csv), "WRITE_SIZE")
+    known = copy_mib * 1024.0  # KiB read and KiB written by one copy
+    f_factor = known / statistics.median(fc)
+    w_factor = known / statistics.median(wc)
+    fetch = statistics.median(fg) * 1024.0 * f_factor
+    write = statistics.median(wg) * 1024.0 * w_factor
+    data = {}
+    if os.path.exists(TRAFFIC_PATH):
+        with open(TRAFFIC_PATH) as f:
+            data = json.loads(f.read().strip().splitlines()[-1])
+    data[wl] = {"run": name, "source_hash": source_hash(), "bytes_per_launch": round(fetch + write),
+                "fetch_bytes": round(fetch), "write_bytes": round(write),
+                "fetch_kib_raw_median": statistics.median(fg),
+                "write_kib_raw_median": statistics.median(wg),
+                "copy_mib": copy_mib, "copy_fetch_factor": round(f_factor, 5),
+                "copy_write_factor": round(w_factor, 5), "gemm_dispatches": len(fg),
+                "command": command}
+    with open(TRAFFIC_PATH, "w") as f:
+        f.write("# HBM bytes per GEMM launch from rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a "
+                "plain device copy of known size; written by bench.py --ingest-pmc\n")
+        f.write(json.dumps(data, sort_keys=True) + "\n")
+    print(json.dumps(data[wl]))
+
+
+def copy_calibration(torch, mib, reps=3):
+    """Plain device-to-device copies of `mib` MiB (the runtime's copy kernel), for counter
+    calibration."""
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    log(f"copy calibration: {reps} x {mib} MiB device copies")
+
+
 def measured_traffic(workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
     current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json.txt")
+    path = TRAFFIC_PATH
     if not os.path.exists(path):
         return None
     try:
@@ -166,7 +240,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", default=None, help="time just this run (see RUNS)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after the runs, copy this many MiB device to device (counter calibration)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--command", default="", help="with --ingest-pmc: the profiling command")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.only or "bf16_4096",
+                   args.command, args.copy_calib_mib or 1024)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the multi-GPU "
               "sharding is a design note, not an implemented path.", file=sys.stderr)
@@ -183,6 +265,8 @@ def main():
     cache = {}
     if args.only:
         res = time_run(args.only, args.steps, args.warmup, torch, dg, gi, cache)
+        if args.copy_calib_mib:
+            copy_calibration(torch, args.copy_calib_mib)
         print(json.dumps(res), flush=True)
         return
 

@@ -310,6 +310,27 @@ __device__ __forceinline__ void load_frag(const lds_t *smem, int stage, int s,
   }
 }
 
+// Load order of a sub-step's fragments: by first use in its MFMA sequence i = f * FN + g, so
+// the first MFMA of a sub-step waits only for the two fragments it reads (a[0], b[0]) and each
+// later fragment has until its own first MFMA to arrive.  Returns the fragment index of load e
+// in load_frag's numbering (A fragments 0..FM-1, then B fragments).
+template <class CFG>
+__host__ __device__ constexpr int frag_order(int e) {
+  int seen_a = 0, seen_b = 0, n = 0;
+  for (int i = 0; i < CFG::FM * CFG::FN; ++i) {
+    const int f = i / CFG::FN, g = i % CFG::FN;
+    if (!((seen_a >> f) & 1)) {
+      seen_a |= 1 << f;
+      if (n++ == e) return f;
+    }
+    if (!((seen_b >> g) & 1)) {
+      seen_b |= 1 << g;
+      if (n++ == e) return CFG::FM + g;
+    }
+  }
+  return -1;
+}
+
 // Slot plan: n memory operations spread over MFMA slots [a, b); operation j follows MFMA
 // a + floor(j (b - a) / n).  ops_before(i, ...) counts the operations placed after MFMAs 0..i-1,
 // so the operations that follow MFMA i are [ops_before(i), ops_before(i + 1)).
@@ -368,6 +389,62 @@ __device__ __forceinline__ void epilogue(const KernelArgs &args, const WorkItem 
                          acc[f][g][4 * q + 3]};
         store_quad<CFG>(args, mbase + f * 32, nbase + g * 32 + q * 8, v, alpha);
       }
+}
+
+// Whole tile with bf16 output, staged through LDS so that every global store writes whole row
+// segments: the wave converts its sub-tile to bf16 in rounds of 32 rows into its own 1/WAVES
+// share of `stage` (a ring stage no wave reads any more), then reads the rows back 16 bytes per
+// lane -- CPR lanes per row, CPR * 16 = WN * 2 contiguous bytes -- and stores them.  Only this
+// wave touches its share, so the rounds need no workgroup barrier (LDS operations of one wave
+// execute in order); the caller's barrier afterwards hands the stage back to the producer.
+// Rows are padded by 16 bytes, which spreads the 32 rows one write touches over the banks while
+// every address stays a per-lane base plus a constant.
+template <class CFG>
+__device__ __forceinline__ void epilogue_staged(const KernelArgs &args, const WorkItem &w,
+                                                const f32x16 (&acc)[CFG::FM][CFG::FN], float alpha,
+                                                int wm, int wn, int wave, int lane, lds_t *smem,
+                                                int stage) {
+  typedef u32x2 __attribute__((address_space(3))) *p64;
+  typedef u32x4 __attribute__((address_space(3))) *p128;
+  constexpr int ROW_BYTES = CFG::WN * 2, CPR = ROW_BYTES / 16, PITCH = ROW_BYTES + 16;
+  constexpr int SHARE = CFG::STAGE_BYTES / CFG::WAVES;
+  static_assert(32 * PITCH <= SHARE, "one 32-row round must fit the wave's share");
+  static_assert(64 % CPR == 0, "a wave-wide read covers whole rows");
+  constexpr int RSTEP = 64 / CPR;        // rows per wave-wide read
+  constexpr int READS = 32 / RSTEP;      // reads per lane per round
+  lds_t *share = smem + stage * CFG::STAGE_BYTES + wave * SHARE;
+  const int64_t m0 = (int64_t)w.m * CFG::BM + wm * CFG::WM;
+  const int64_t n0 = (int64_t)w.n * CFG::BN + wn * CFG::WN;
+  // Stores go through a buffer resource based at the sub-tile origin and ending at the end of C:
+  // rows at or past M fall outside it and are dropped by the hardware range check; a lane's
+  // 8 columns are all inside or all outside N (N is a multiple of 8).
+  const int64_t origin = m0 * args.ldc + n0;
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc(args.C + origin * 2, (args.M * args.ldc - origin) * 2);
+  const int chunk_l = lane % CPR;
+  const bool col_ok = n0 + chunk_l * 8 < args.N;
+  const uint32_t ldc_b = (uint32_t)args.ldc * 2;
+  lds_t *wr = share + (lane & 31) * PITCH + (lane >> 5) * 8;
+  lds_t *rd_p = share + (lane / CPR) * PITCH + chunk_l * 16;
+  const uint32_t st_off = (uint32_t)(lane / CPR) * ldc_b + chunk_l * 16;
+#pragma unroll
+  for (int f = 0; f < CFG::FM; ++f) {
+#pragma unroll
+    for (int g = 0; g < CFG::FN; ++g)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = f32x4{acc[f][g][4 * q + 0], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2],
+                              acc[f][g][4 * q + 3]} * alpha;
+        *(p64)(wr + (g * 4 + q) * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+#pragma unroll
+    for (int j = 0; j < READS; ++j) {
+      const u32x4 v = *(p128)(rd_p + j * RSTEP * PITCH);
+      if (col_ok)
+        __builtin_amdgcn_raw_buffer_store_b128(v, cr, st_off,
+                                               (uint32_t)(f * 32 + j * RSTEP) * ldc_b, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Partial-tile slot layout: quad qi = (f * FN + g) * 4 + q of thread tid sits at
@@ -593,7 +670,7 @@ gemm_kernel(KernelArgs args) {
   if (issued > 0) {
     handshake(0);
     [&]<int... E>(std::integer_sequence<int, E...>) {
-      (load_frag<CFG, E>(smem, 0, 0, aoff, boff, fr[0]), ...);
+      (load_frag<CFG, frag_order<CFG>(E)>(smem, 0, 0, aoff, boff, fr[0]), ...);
     }(std::make_integer_sequence<int, NF>());
   }
 
@@ -634,7 +711,7 @@ gemm_kernel(KernelArgs args) {
               constexpr int lo = ops_before(i, NF, 0, NM);
               constexpr int hi = ops_before(i + 1, NF, 0, NM);
               [&]<int... E>(std::integer_sequence<int, E...>) {
-                (load_frag<CFG, lo + E>(smem, stage, S + 1, aoff, boff, fr[NXT]), ...);
+                (load_frag<CFG, frag_order<CFG>(lo + E)>(smem, stage, S + 1, aoff, boff, fr[NXT]), ...);
               }(std::make_integer_sequence<int, hi - lo>());
             } else {
               if constexpr (i + 1 == HS) {
@@ -644,7 +721,7 @@ gemm_kernel(KernelArgs args) {
               constexpr int hi = ops_before(i + 1, NF, HS, NM);
               if (have_next) {
                 [&]<int... E>(std::integer_sequence<int, E...>) {
-                  (load_frag<CFG, lo + E>(smem, (c + 1) % CFG::STAGES, 0, aoff, boff, fr[NXT]),
+                  (load_frag<CFG, frag_order<CFG>(lo + E)>(smem, (c + 1) % CFG::STAGES, 0, aoff, boff, fr[NXT]),
                    ...);
                 }(std::make_integer_sequence<int, hi - lo>());
               }
@@ -676,9 +753,17 @@ gemm_kernel(KernelArgs args) {
       }(std::make_integer_sequence<int, CFG::KSUB>());
     }
 
-    if (cw.role == ROLE_WHOLE)
-      epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid);
-    else if (args.sk_mode == SK_CHAIN)
+    if (cw.role == ROLE_WHOLE) {
+      if (args.out_bf16) {
+        // the stage read last (c - 1) is drained: its next fill is the pending producer step,
+        // which is issued only after the barrier below
+        epilogue_staged<CFG>(args, cw, acc, alpha, wm, wn, wave, lane, smem,
+                             (c + CFG::STAGES - 1) % CFG::STAGES);
+        lds_barrier();
+      } else {
+        epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid);
+      }
+    } else if (args.sk_mode == SK_CHAIN)
       fixup_chain<CFG>(args, cw, acc, alpha, wm, wn, tid);
     else
       fixup_separate_store<CFG>(args, cw, acc, b, tid);
@@ -800,7 +885,7 @@ gemm_kernel_pp(KernelArgs args) {
 #pragma unroll
       for (int t = 0; t < CFG::KSUB; ++t)
         [&]<int... E>(std::integer_sequence<int, E...>) {
-          (load_frag<CFG, E>(smem, stage, t, aoff, boff, fr[t]), ...);
+          (load_frag<CFG, frag_order<CFG>(E)>(smem, stage, t, aoff, boff, fr[t]), ...);
         }(std::make_integer_sequence<int, NF>());
       if (prod.valid) {
         issue_all((c + CFG::STAGES - 1) % CFG::STAGES);
