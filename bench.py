@@ -142,7 +142,7 @@ RUNS = {
 }
 
 
-def time_run(name, steps, warmup, torch, dg, gi, cache):
+def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
     wl_name, mapping, group, sched, tile, out, workers = RUNS[name][:7]
     bk = RUNS[name][7] if len(RUNS[name]) > 7 else 0
     flags = dg.GEMM_FLAG_STREAMK_CHAIN if len(RUNS[name]) > 8 and RUNS[name][8] == "chain" else 0
@@ -174,9 +174,16 @@ def time_run(name, steps, warmup, torch, dg, gi, cache):
     if plan.workspace_bytes:
         ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=A.device)
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        plan.run(A, B, C, sa, sb, ws, stream)
-    torch.cuda.synchronize()
+    # Warmup: at least `warmup` launches and at least `settle_ms` of back-to-back launches, so the
+    # GPU's clock has left its ramp (it climbs for a few hundred ms under a sustained MFMA load).
+    n_warm, t_w = 0, time.perf_counter()
+    while True:
+        for _ in range(max(1, warmup) if n_warm == 0 else 50):
+            plan.run(A, B, C, sa, sb, ws, stream)
+            n_warm += 1
+        torch.cuda.synchronize()
+        if n_warm >= warmup and (time.perf_counter() - t_w) * 1e3 >= settle_ms:
+            break
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -193,7 +200,7 @@ def time_run(name, steps, warmup, torch, dg, gi, cache):
         "workload": wl_name, "M": op.M, "N": op.N, "K": op.K, "dtype": op.dtype, "out": out,
         "tile": [info.bm, info.bn, info.bk], "stages": info.stages, "mapping": mapping,
         "group": group, "sched": sched, "grid": info.grid,
-        "dp_tiles": info.dp_tiles, "sk_tiles": info.sk_tiles,
+        "dp_tiles": info.dp_tiles, "sk_tiles": info.sk_tiles, "warmup_launches": n_warm,
         "ms_per_step": wall * 1e3 / steps, "kernel_us": dev_ms * 1e3,
         "tflops": flops / (wall / steps) / 1e12, "kernel_tflops": flops / (dev_ms * 1e-3) / 1e12,
     }
@@ -237,6 +244,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="minimum duration of the untimed warmup per run (GPU clock settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", default=None, help="time just this run (see RUNS)")
@@ -264,19 +273,20 @@ def main():
 
     cache = {}
     if args.only:
-        res = time_run(args.only, args.steps, args.warmup, torch, dg, gi, cache)
+        res = time_run(args.only, args.steps, args.warmup, torch, dg, gi, cache, args.settle_ms)
         if args.copy_calib_mib:
             copy_calibration(torch, args.copy_calib_mib)
         print(json.dumps(res), flush=True)
         return
 
-    head = time_run("bf16_4096", args.steps, args.warmup, torch, dg, gi, cache)
+    head = time_run("bf16_4096", args.steps, args.warmup, torch, dg, gi, cache, args.settle_ms)
     secondary = {}
     if not args.no_secondary:
         for name in ("bf16_4096_linear", "bf16_4096_t128", "fp8_8192", "bf16_mlp_up",
                      "bf16_streamk", "bf16_256"):
             steps = max(10, args.steps // (4 if name == "fp8_8192" else 1))
-            r = time_run(name, steps, max(2, args.warmup // 2), torch, dg, gi, cache)
+            r = time_run(name, steps, max(2, args.warmup // 2), torch, dg, gi, cache,
+                         args.settle_ms / 2)
             secondary[name] = {k: r[k] for k in ("kernel_us", "kernel_tflops", "frac_of_peak",
                                                  "hbm_gbs_alg", "tile", "grid", "mapping",
                                                  "sched")}
@@ -303,7 +313,8 @@ def main():
         "config": {"workload": "bf16 gemm M=N=K=4096, uniform[-1,1], fp32 accumulate, bf16 out",
                    "M": 4096, "N": 4096, "K": 4096, "tile": head["tile"],
                    "mapping": "grouped_m", "group": 8, "sched": "persistent",
-                   "grid": head["grid"]},
+                   "grid": head["grid"], "warmup_launches": head["warmup_launches"],
+                   "settle_ms": args.settle_ms},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
                      "traffic": measured_traffic("bf16_4096")},

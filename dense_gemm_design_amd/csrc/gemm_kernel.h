@@ -674,15 +674,18 @@ gemm_kernel(KernelArgs args) {
     }(std::make_integer_sequence<int, NF>());
   }
 
-  // One sub-step: NM MFMAs on fr[CUR]; between them, per the slot plan, the producer's loads (first
-  // sub-step only), the fragments of the next sub-step of this k-step, or -- in the last
-  // sub-step -- the handshake of the next k-step followed by its first fragments.
+  // One sub-step: NM MFMAs on fr[CUR]; between them, per the slot plan, the fragments of the next
+  // sub-step of this k-step, or -- in the last sub-step -- the handshake of the next k-step
+  // followed by its first fragments and the producer's loads of the step after it, which may
+  // fill the stage this k-step has just drained.  At the last k-step of a work item that stage
+  // is kept for the epilogue, and the producer's loads move to the first sub-step of the next
+  // k-step (as after the prologue).
+  bool early = false;  // may the pending loads go out in this k-step's last sub-step?
   auto substep = [&](auto s_c, auto acc_ref) {
     constexpr int S = decltype(s_c)::value;
     constexpr int CUR = S & 1, NXT = (S + 1) & 1;
-    constexpr bool FIRST = S == 0, LAST = S == CFG::KSUB - 1;
+    constexpr bool LAST = S == CFG::KSUB - 1;
     constexpr int HS = LAST ? (CFG::KSUB == 1 ? NM / 2 : NM / 4) : NM;  // handshake slot
-    constexpr int LOAD_END = LAST ? HS : NM;
     auto &acc = *acc_ref;
     const int stage = c % CFG::STAGES;
     const bool have_next = c + 1 < issued;
@@ -692,21 +695,6 @@ gemm_kernel(KernelArgs args) {
             constexpr int i = I;
             constexpr int f = i / CFG::FN, g = i % CFG::FN;
             acc[f][g] = mfma<CFG::DT>(fr[CUR].b[g], fr[CUR].a[f], acc[f][g]);
-            // producer loads of the pending step
-            if constexpr (FIRST) {
-              constexpr int lo = ops_before(i, L, 0, LOAD_END);
-              constexpr int hi = ops_before(i + 1, L, 0, LOAD_END);
-              if (pending) {
-                [&]<int... J>(std::integer_sequence<int, J...>) {
-                  (prod.template load<lo + J>(wave, lane), ...);
-                }(std::make_integer_sequence<int, hi - lo>());
-                if constexpr (hi == L) {
-                  prod.end(args, wave, lane);
-                  ++issued;
-                  pending = false;
-                }
-              }
-            }
             if constexpr (!LAST) {
               constexpr int lo = ops_before(i, NF, 0, NM);
               constexpr int hi = ops_before(i + 1, NF, 0, NM);
@@ -724,6 +712,18 @@ gemm_kernel(KernelArgs args) {
                   (load_frag<CFG, frag_order<CFG>(lo + E)>(smem, (c + 1) % CFG::STAGES, 0, aoff, boff, fr[NXT]),
                    ...);
                 }(std::make_integer_sequence<int, hi - lo>());
+              }
+              constexpr int plo = ops_before(i, L, HS, NM);
+              constexpr int phi = ops_before(i + 1, L, HS, NM);
+              if (pending && early) {
+                [&]<int... J>(std::integer_sequence<int, J...>) {
+                  (prod.template load<plo + J>(wave, lane), ...);
+                }(std::make_integer_sequence<int, phi - plo>());
+                if constexpr (phi == L) {
+                  prod.end(args, wave, lane);
+                  ++issued;
+                  pending = false;
+                }
               }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -748,6 +748,16 @@ gemm_kernel(KernelArgs args) {
         for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.0f;
 
     for (int k = cw.kb; k < cw.ke; ++k, ++c) {
+      // loads still pending from the prologue or an item boundary go out in the first sub-step
+      if (pending) {
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+          (prod.template load<J>(wave, lane), ...);
+        }(std::make_integer_sequence<int, L>());
+        prod.end(args, wave, lane);
+        ++issued;
+        pending = false;
+      }
+      early = k + 1 < cw.ke;
       [&]<int... S>(std::integer_sequence<int, S...>) {
         (substep(std::integral_constant<int, S>(), &acc), ...);
       }(std::make_integer_sequence<int, CFG::KSUB>());
