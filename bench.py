@@ -126,14 +126,15 @@ def measured_traffic(workload):
     return entry.get("bytes_per_launch")
 
 
-# name, workload key, mapping, group, sched, tile, out, workers[, bk]
+# name, workload key, mapping, group, sched, tile, out, workers[, bk[, variant]]
+# variant: "chain" = Stream-K lock-chain fixup, "pp" = ping-pong kernel
 RUNS = {
     "bf16_4096": ("bf16_4096", "grouped_m", 8, "persistent", 0, "bf16", 0),
-    "bf16_4096_pp": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 32),
+    "bf16_4096_pp": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "pp"),
     "bf16_4096_linear": ("bf16_4096", "linear_n", 1, "persistent", 0, "bf16", 0),
     "bf16_4096_t128": ("bf16_4096", "grouped_m", 8, "persistent", 128, "bf16", 0),
     "fp8_8192": ("fp8_8192", "grouped_m", 16, "persistent", 0, "bf16", 0),
-    "fp8_8192_pp": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 64),
+    "fp8_8192_pp": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "pp"),
     "bf16_mlp_up": ("bf16_mlp_up", "grouped_m", 8, "persistent", 0, "bf16", 0),
     "bf16_streamk": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256),
     "bf16_streamk_chain": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256, 0,
@@ -142,10 +143,16 @@ RUNS = {
 }
 
 
+def run_flags(name, dg):
+    """GEMM_FLAG_* bits of a RUNS entry's variant."""
+    variant = RUNS[name][8] if len(RUNS[name]) > 8 else ""
+    return {"": 0, "chain": dg.GEMM_FLAG_STREAMK_CHAIN, "pp": dg.GEMM_FLAG_PINGPONG}[variant]
+
+
 def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
     wl_name, mapping, group, sched, tile, out, workers = RUNS[name][:7]
     bk = RUNS[name][7] if len(RUNS[name]) > 7 else 0
-    flags = dg.GEMM_FLAG_STREAMK_CHAIN if len(RUNS[name]) > 8 and RUNS[name][8] == "chain" else 0
+    flags = run_flags(name, dg)
     wl = gi.WORKLOADS[wl_name]
     if wl_name not in cache:
         t0 = time.time()

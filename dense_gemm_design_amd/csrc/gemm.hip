@@ -23,11 +23,11 @@ using namespace dg;
 // SWZ spreads the 16 rows one 16-lane LDS read phase touches over 16 distinct 16-byte bank groups
 // (1 for 128-byte rows, 2 for 64-byte rows).  Defaults (first match per tile shape): 8 waves of
 // 128 x 64 sub-tiles with 2 stages of 64 KiB -- two waves per SIMD hide each other's LDS waits.
-// The ping-pong variants (bk 32 for bf16, 64 for e4m3) stay selectable through bk.
-using CfgBf16_256pp = TileCfg<DT_BF16, 256, 256, 32, 2, 4, 4, 2>;
+// The ping-pong kernel (GEMM_FLAG_PINGPONG) runs the same 256 x 256 tiles with two wave groups.
+using CfgBf16_256pp = TileCfg<DT_BF16, 256, 256, 64, 2, 4, 2, 1>;
 using CfgBf16_256 = TileCfg<DT_BF16, 256, 256, 64, 2, 4, 2, 1>;
 using CfgBf16_128 = TileCfg<DT_BF16, 128, 128, 64, 2, 2, 2, 1>;
-using CfgFp8_256pp = TileCfg<DT_FP8, 256, 256, 64, 2, 4, 4, 2>;
+using CfgFp8_256pp = TileCfg<DT_FP8, 256, 256, 128, 2, 4, 2, 1>;
 using CfgFp8_256 = TileCfg<DT_FP8, 256, 256, 128, 2, 4, 2, 1>;
 using CfgFp8_128 = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 2, 1>;
 
@@ -74,7 +74,7 @@ constexpr KernelEntry entry() {
 template <class CFG>
 constexpr KernelEntry entry_pp() {
   return KernelEntry{CFG::DT, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::STAGES,
-                     CFG::LDS_BYTES, 1, &launch_pp<CFG>, &kernel_of_pp<CFG>};
+                     pp_lds_bytes<CFG>(), 1, &launch_pp<CFG>, &kernel_of_pp<CFG>};
 }
 
 // The first entry that matches (dtype, bm, bn[, bk]) is the default for that tile shape.
@@ -136,7 +136,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (d.sched < GEMM_SCHED_STATIC || d.sched > GEMM_SCHED_AUTO) return GEMM_ERR_INVALID_ARG;
   if (d.num_workers < 0 || d.bm < 0 || d.bn < 0 || d.bk < 0) return GEMM_ERR_INVALID_ARG;
   if (d.flags & ~(GEMM_FLAG_TRACE | GEMM_FLAG_NO_XCD_REMAP | GEMM_FLAG_STREAMK_CHAIN |
-                  GEMM_FLAG_TEST_SKIP_PUBLISH))
+                  GEMM_FLAG_PINGPONG | GEMM_FLAG_TEST_SKIP_PUBLISH))
     return GEMM_ERR_INVALID_ARG;
 
   // Well-formed; now what the kernels implement.
@@ -146,22 +146,25 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (d.N % 8 != 0) return GEMM_ERR_UNSUPPORTED;           // 16-byte output rows
   if (d.K * eb > (int64_t)1 << 30) return GEMM_ERR_UNSUPPORTED;
 
+  // the ping-pong kernels run data-parallel work only, on 256 x 256 tiles
+  const bool want_pp = (d.flags & GEMM_FLAG_PINGPONG) != 0;
+  if (want_pp && (d.K == 0 || d.sched == GEMM_SCHED_STREAMK || d.sched == GEMM_SCHED_AUTO))
+    return GEMM_ERR_UNSUPPORTED;
+
   // Tile shape: 256 x 256 unless asked otherwise or the problem has too few big tiles.
   int bm = d.bm, bn = d.bn;
   if (bm == 0 && bn == 0) {
     const int64_t big = cdiv(d.M, 256) * cdiv(d.N, 256);  // 0 for an empty output
     const bool streamk = d.sched == GEMM_SCHED_STREAMK;
-    bm = bn = (big >= 128 && !streamk) ? 256 : 128;
+    bm = bn = ((big >= 128 && !streamk) || want_pp) ? 256 : 128;
   } else if (bm == 0 || bn == 0) {
     bm = bn = (bm ? bm : bn);
   }
   const int want_dt = d.dtype_ab == GEMM_BF16 ? DT_BF16 : DT_FP8;
-  // the ping-pong kernels run data-parallel work only
-  const bool may_pp = d.K > 0 && d.sched != GEMM_SCHED_STREAMK && d.sched != GEMM_SCHED_AUTO;
   const KernelEntry *k = nullptr;
   for (const KernelEntry &e : kKernels)
     if (!k && e.dt == want_dt && e.bm == bm && e.bn == bn && (d.bk == 0 || d.bk == e.bk) &&
-        (may_pp || !e.pingpong))
+        (e.pingpong != 0) == want_pp)
       k = &e;
   if (!k) return GEMM_ERR_UNSUPPORTED;
   // rows of one tile must stay addressable by 32-bit buffer offsets

@@ -201,39 +201,38 @@ __device__ __forceinline__ f32x16 mfma(const typename FragT<DT>::type &b,
 // ---- the kernel ------------------------------------------------------------------------------
 
 // Producer side of the ring: the cursor of the next k-tile to load (uniform) and the lane's byte
-// offsets inside a tile (one register per 1 KiB load, fixed for the whole kernel).
-template <class CFG, bool RAGGED_K>
+// offsets inside a tile.  NW waves share the loads of a k-tile: load j of wave w fills tile rows
+// (j * NW + w) * RPL + lane / CH with chunk (lane % CH) ^ swz(row) along K.  The swizzle does not
+// change with j (NW * RPL rows is a whole number of swizzle periods), so load j is load 0 moved
+// by the uniform stride j * NW * RPL rows: one lane offset per operand plus a scalar offset.
+// Rows past M (N) of an edge tile and, for a ragged K, chunks past K get the offset kOOB in the
+// lane's own (vector) offset, which the buffer range check turns into zeros.
+template <class CFG, bool RAGGED_K, int NW = CFG::WAVES>
 struct Producer {
+  static constexpr int LA = CFG::A_BYTES / 1024 / NW, LB = CFG::B_BYTES / 1024 / NW;
+  static_assert(CFG::A_BYTES % (1024 * NW) == 0 && CFG::B_BYTES % (1024 * NW) == 0, "load split");
+  static_assert((NW * CFG::RPL) % (CFG::CH << CFG::SWZ) == 0, "swizzle must repeat per load");
+  static_assert(LA + LB <= 63, "vmcnt range");
   Cursor cur;
-  int32_t valid, k, ke, rows_a, rows_b;
+  int32_t valid, k, ke, rows_a, rows_b, edge;
   __amdgpu_buffer_rsrc_t ra, rb;
-  uint32_t va0[CFG::LA], vb0[CFG::LB];  // lane offsets within a full tile (fixed)
-  uint32_t va[CFG::LA], vb[CFG::LB];    // the same with rows past M (N) of this tile -> kOOB
-
-  // row of tile and 16-byte chunk along K that `lane` fills in load j of `wave`
-  static __device__ __forceinline__ int load_row(int j, int wave, int lane) {
-    return (j * CFG::WAVES + wave) * CFG::RPL + lane / CFG::CH;
-  }
-  static __device__ __forceinline__ int load_chunk(int row, int lane) {
-    return (lane % CFG::CH) ^ ((row >> CFG::SWZ) & (CFG::CH - 1));
-  }
+  int32_t sta, stb;    // byte stride between loads j and j + 1 (uniform)
+  uint32_t voa, vob;   // lane offsets of load 0
+  uint32_t row0;       // tile row of the lane in load 0
+  uint32_t chunk16;    // byte offset of the lane's chunk within a k-tile row
 
   __device__ __forceinline__ void init(const KernelArgs &args, int32_t b, int wave, int lane) {
-#pragma unroll
-    for (int j = 0; j < CFG::LA; ++j) {
-      const int row = load_row(j, wave, lane);
-      va0[j] = (uint32_t)(row * (uint32_t)args.lda_bytes + load_chunk(row, lane) * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < CFG::LB; ++j) {
-      const int row = load_row(j, wave, lane);
-      vb0[j] = (uint32_t)(row * (uint32_t)args.ldb_bytes + load_chunk(row, lane) * 16);
-    }
+    row0 = (uint32_t)(wave * CFG::RPL + lane / CFG::CH);
+    chunk16 = (uint32_t)(((lane % CFG::CH) ^ ((row0 >> CFG::SWZ) & (CFG::CH - 1))) * 16);
+    voa = row0 * (uint32_t)args.lda_bytes + chunk16;
+    vob = row0 * (uint32_t)args.ldb_bytes + chunk16;
+    sta = (int32_t)(NW * CFG::RPL * args.lda_bytes);
+    stb = (int32_t)(NW * CFG::RPL * args.ldb_bytes);
     cursor_init(args.sp, b, cur);
-    next_item(args, wave, lane);
+    next_item(args);
   }
 
-  __device__ __forceinline__ void next_item(const KernelArgs &args, int wave, int lane) {
+  __device__ __forceinline__ void next_item(const KernelArgs &args) {
     WorkItem w;
     // items without k-tiles (K == 0) load nothing
     while ((valid = cursor_next(args.sp, cur, w)) && w.kb == w.ke) {
@@ -244,45 +243,40 @@ struct Producer {
       const int64_t m0 = (int64_t)w.m * CFG::BM, n0 = (int64_t)w.n * CFG::BN;
       rows_a = (int32_t)(args.M - m0 < CFG::BM ? args.M - m0 : CFG::BM);
       rows_b = (int32_t)(args.N - n0 < CFG::BN ? args.N - n0 : CFG::BN);
+      edge = rows_a < CFG::BM || rows_b < CFG::BN;
       ra = make_rsrc(args.A + m0 * args.lda_bytes, (int64_t)rows_a * args.lda_bytes);
       rb = make_rsrc(args.B + n0 * args.ldb_bytes, (int64_t)rows_b * args.ldb_bytes);
-#pragma unroll
-      for (int j = 0; j < CFG::LA; ++j)
-        va[j] = rows_a == CFG::BM || load_row(j, wave, lane) < rows_a ? va0[j] : kOOB;
-#pragma unroll
-      for (int j = 0; j < CFG::LB; ++j)
-        vb[j] = rows_b == CFG::BN || load_row(j, wave, lane) < rows_b ? vb0[j] : kOOB;
     }
   }
 
   // Loads of one k-step are issued one instruction at a time: begin(stage) fixes the stage and
   // the k offset, load(j) issues 1 KiB load j (A loads first, then B), end() advances the cursor.
-  uint32_t kbytes, klimit;
-  int32_t kedge;
+  uint32_t kbytes, koa, kob;
   lds_t *sa;
 
   __device__ __forceinline__ void begin(const KernelArgs &args, lds_t *smem, int stage) {
     kbytes = (uint32_t)k * CFG::ROWB;
     sa = smem + stage * CFG::STAGE_BYTES;
-    kedge = (int64_t)(k + 1) * CFG::ROWB > args.K * CFG::EB;  // the k-tile runs past K
-    klimit = (uint32_t)(args.K * CFG::EB) - kbytes;
+    koa = voa + kbytes;
+    kob = vob + kbytes;
+    if (RAGGED_K && (int64_t)(k + 1) * CFG::ROWB > args.K * CFG::EB) {  // chunks past K read 0
+      if (chunk16 >= (uint32_t)(args.K * CFG::EB) - kbytes) koa = kob = kOOB;
+    }
   }
 
   template <int J>
-  __device__ __forceinline__ void load(int wave, int lane) {
-    constexpr bool IS_A = J < CFG::LA;
-    constexpr int j = IS_A ? J : J - CFG::LA;
-    lds_t *dst = sa + (IS_A ? 0 : CFG::A_BYTES) + (j * CFG::WAVES + wave) * 1024;
-    uint32_t off = (IS_A ? va[j] : vb[j]) + kbytes;  // rows past M (N) stay past the end
-    if (RAGGED_K && kedge) {  // chunks past K read as zero
-      const int row = load_row(j, wave, lane);
-      if ((uint32_t)(load_chunk(row, lane) * 16) >= klimit) off = kOOB;
-    }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(IS_A ? ra : rb, dst, 16, off, 0, 0, 0);
+  __device__ __forceinline__ void load(int wave) {
+    constexpr bool IS_A = J < LA;
+    constexpr int j = IS_A ? J : J - LA;
+    lds_t *dst = sa + (IS_A ? 0 : CFG::A_BYTES) + (j * NW + wave) * 1024;
+    uint32_t off = IS_A ? koa : kob;
+    if (edge && row0 + j * NW * CFG::RPL >= (uint32_t)(IS_A ? rows_a : rows_b)) off = kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(IS_A ? ra : rb, dst, 16, off, j * (IS_A ? sta : stb),
+                                             0, 0);
   }
 
-  __device__ __forceinline__ void end(const KernelArgs &args, int wave, int lane) {
-    if (++k == ke) next_item(args, wave, lane);
+  __device__ __forceinline__ void end(const KernelArgs &args) {
+    if (++k == ke) next_item(args);
   }
 };
 
@@ -627,7 +621,8 @@ gemm_kernel(KernelArgs args) {
       }
   }
 
-  Producer<CFG, RAGGED_K> prod;
+  using Prod = Producer<CFG, RAGGED_K>;
+  Prod prod;
   prod.init(args, b, wave, lane);
 
   Cursor ccur;
@@ -640,7 +635,7 @@ gemm_kernel(KernelArgs args) {
   // loads of step c have landed -- and EMPTY(c-1) -- every wave has finished its LDS reads of
   // step c-1 -- after which step c+S-1 may be loaded into stage (c-1) mod S.  Those loads are
   // issued during the first sub-step of step c (`pending`).
-  constexpr int L = CFG::LA + CFG::LB;
+  constexpr int L = Prod::LA + Prod::LB;       // loads per wave per k-step
   constexpr int NM = CFG::FM * CFG::FN;       // MFMAs per sub-step
   constexpr int NF = CFG::FM + CFG::FN;       // fragments per sub-step
   int issued = 0;
@@ -649,9 +644,9 @@ gemm_kernel(KernelArgs args) {
     if (prod.valid) {
       prod.begin(args, smem, s);
       [&]<int... J>(std::integer_sequence<int, J...>) {
-        (prod.template load<J>(wave, lane), ...);
+        (prod.template load<J>(wave), ...);
       }(std::make_integer_sequence<int, L>());
-      prod.end(args, wave, lane);
+      prod.end(args);
       ++issued;
     }
 
@@ -717,10 +712,10 @@ gemm_kernel(KernelArgs args) {
               constexpr int phi = ops_before(i + 1, L, HS, NM);
               if (pending && early) {
                 [&]<int... J>(std::integer_sequence<int, J...>) {
-                  (prod.template load<plo + J>(wave, lane), ...);
+                  (prod.template load<plo + J>(wave), ...);
                 }(std::make_integer_sequence<int, phi - plo>());
                 if constexpr (phi == L) {
-                  prod.end(args, wave, lane);
+                  prod.end(args);
                   ++issued;
                   pending = false;
                 }
@@ -751,9 +746,9 @@ gemm_kernel(KernelArgs args) {
       // loads still pending from the prologue or an item boundary go out in the first sub-step
       if (pending) {
         [&]<int... J>(std::integer_sequence<int, J...>) {
-          (prod.template load<J>(wave, lane), ...);
+          (prod.template load<J>(wave), ...);
         }(std::make_integer_sequence<int, L>());
-        prod.end(args, wave, lane);
+        prod.end(args);
         ++issued;
         pending = false;
       }
@@ -765,8 +760,14 @@ gemm_kernel(KernelArgs args) {
 
     if (cw.role == ROLE_WHOLE) {
       if (args.out_bf16) {
-        // the stage read last (c - 1) is drained: its next fill is the pending producer step,
-        // which is issued only after the barrier below
+        // The stage read last (c - 1) becomes the staging area; its next fill is the pending
+        // producer step, which is issued only after the barrier below.  Every wave has finished
+        // reading it once the handshake of step c has run; without a next step (this worker's
+        // last item) there was none, so wait for everyone's reads here.
+        if (c >= issued) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          lds_barrier();
+        }
         epilogue_staged<CFG>(args, cw, acc, alpha, wm, wn, wave, lane, smem,
                              (c + CFG::STAGES - 1) % CFG::STAGES);
         lds_barrier();
@@ -795,27 +796,82 @@ gemm_kernel(KernelArgs args) {
 // ---- ping-pong kernel (data-parallel tiles) --------------------------------------------------
 //
 // The pages' ping-pong consumer schedule ("H100 Kernel Design" lesson, sections 7.3-7.5) mapped
-// onto two waves per SIMD.  The 8 waves form two groups of 4 (one wave per SIMD each); group g
-// owns rows [g*BM/2, (g+1)*BM/2) of the tile.  Each group alternates a memory phase M(s) -- read
-// all MFMA fragments of k-step s from LDS, issue its share of the loads of step s+S-1 -- and a
-// compute phase C(s) -- MFMAs only (plus the epilogue after an item's last step).  Group 1 runs one
-// barrier-phase behind group 0, so in every phase one wave per SIMD issues MFMAs while the other
-// does memory work, and one group's epilogue overlaps the other group's MFMAs.
+// onto the two waves of each SIMD.  The 8 waves form two groups of four (one wave per SIMD each);
+// group g owns rows [g*BM/2, (g+1)*BM/2) of the tile, each wave a WM x WN sub-tile.  A wave
+// alternates a memory phase M(c) -- read every MFMA fragment of k-step c from LDS into registers
+// (and, in group 0, issue the loads of k-step c+1) -- and a compute phase C(c): the k-step's MFMAs
+// back to back, with no memory operation in between.  Group 1 runs one phase behind group 0, so in
+// every phase one wave of each SIMD feeds the matrix core while the other does the memory work.
 //
-// Phases are separated by workgroup barriers.  Group 0 runs M(0) C(0) M(1) C(1) ...; group 1 waits
-// one phase, then runs the same sequence.  Ring hand-offs (S stages):
-//  * EMPTY: step s-1 was read by group 0 in phase 2s-2 and by group 1 in phase 2s-1 (each wave
-//    waits for its own reads with lgkmcnt(0) before the barrier), so from phase 2s on, stage
-//    (s-1) mod S may take step s+S-1; group 0 issues its loads in phase 2s, group 1 in 2s+1.
-//  * FULL: before the barrier that opens phase 2s+2 (group 0 reads step s+1 there), every wave
-//    waits for its own loads of step s+1 (s_waitcnt vmcnt).
+// Phases are separated by workgroup barriers (barrier n closes phase n for every wave).  With two
+// stages the ring hand-offs are:
+//  * EMPTY: stage c mod 2 is read in phase 2c (group 0) and 2c+1 (group 1); every wave retires its
+//    reads (lgkmcnt(0)) before the barrier closing its memory phase, so from phase 2c+2 on the
+//    stage may take k-step c+2.  Group 0 issues those loads in its memory phase M(c+1), which is
+//    phase 2c+2 -- a whole k-step (two phases) before they are read.
+//  * FULL: at the end of C(c+1) (phase 2c+3) group 0 waits for its loads of step c+2
+//    (s_waitcnt vmcnt(0)) before the barrier that opens phase 2c+4, where M(c+2) reads them.
+// Group 1 therefore never issues global loads; the prologue loads steps 0 and 1.  Group 1 sits out
+// phase 0 with one extra barrier and group 0 balances it with one after its last phase.
+// After an item's last C, the wave writes its sub-tile through its own 4 KiB slice of an LDS area
+// outside the ring, during its next memory phase (under the other group's MFMAs).
+template <class CFG>
+__device__ __forceinline__ void epilogue_pp(const KernelArgs &args, const WorkItem &w,
+                                            const f32x16 (&acc)[CFG::FM][CFG::FN], float alpha,
+                                            int wm, int wn, int lane, lds_t *slice) {
+  typedef u32x2 __attribute__((address_space(3))) *p64;
+  typedef u32x4 __attribute__((address_space(3))) *p128;
+  static_assert(CFG::WN * 2 == 128, "rows of the staged sub-tile are 128 bytes");
+  // chunk c (16 bytes) of staged row r sits at chunk position c ^ (r mod 8): the 8 lanes reading a
+  // row back touch 8 distinct bank groups
+  const int64_t m0 = (int64_t)w.m * CFG::BM + wm * CFG::WM;
+  const int64_t n0 = (int64_t)w.n * CFG::BN + wn * CFG::WN;
+  const int64_t origin = m0 * args.ldc + n0;
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc(args.C + origin * 2, (args.M * args.ldc - origin) * 2);
+  const int chunk_l = lane & 7, rrow = lane >> 3;  // read-back: 8 rows per wave-wide read
+  const bool col_ok = n0 + chunk_l * 8 < args.N;
+  const uint32_t ldc_b = (uint32_t)args.ldc * 2;
+  const uint32_t st_off = (uint32_t)rrow * ldc_b + chunk_l * 16;
+  lds_t *rd_p = slice + rrow * 128 + ((chunk_l ^ rrow) * 16);
+  lds_t *wr_row = slice + (lane & 31) * 128 + (lane >> 5) * 8;
+  const int x = lane & 7;  // (row mod 8) of the lane's staged row
+#pragma unroll
+  for (int f = 0; f < CFG::FM; ++f) {
+#pragma unroll
+    for (int g = 0; g < CFG::FN; ++g)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = f32x4{acc[f][g][4 * q + 0], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2],
+                              acc[f][g][4 * q + 3]} * alpha;
+        *(p64)(wr_row + (((g * 4 + q) ^ x) * 16)) =
+            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 v = *(p128)(rd_p + j * 1024);
+      if (col_ok)
+        __builtin_amdgcn_raw_buffer_store_b128(v, cr, st_off, (uint32_t)(f * 32 + j * 8) * ldc_b,
+                                               0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+constexpr int kPPSlice = 4096;  // per-wave epilogue staging area of the ping-pong kernel
+template <class CFG>
+constexpr int pp_lds_bytes() {
+  return CFG::LDS_BYTES + CFG::WAVES * kPPSlice;
+}
+
 template <class CFG, bool RAGGED_K>
 __global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::THREADS),
                                amdgpu_waves_per_eu(2, 2)))
 gemm_kernel_pp(KernelArgs args) {
-  static_assert(CFG::WAVES == 8 && CFG::WGM == 2, "ping-pong: two groups of four waves");
-  static_assert(CFG::STAGES >= 3, "ping-pong needs a stage of slack for the lagging group");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[CFG::LDS_BYTES];
+  static_assert(CFG::WAVES == 8 && CFG::WGM == 2 && CFG::WGN == 4, "two groups of four waves");
+  static_assert(CFG::STAGES == 2, "ping-pong ring of two stages");
+  constexpr int EPI_SLICE = kPPSlice;
+  static_assert(pp_lds_bytes<CFG>() <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[pp_lds_bytes<CFG>()];
   lds_t *smem = (lds_t *)(size_t)(uint32_t)(size_t)(lds_t *)smem_raw;
 
   const int tid = threadIdx.x;
@@ -824,6 +880,7 @@ gemm_kernel_pp(KernelArgs args) {
   const int wm = wave / CFG::WGN, wn = wave % CFG::WGN;
   const int group = wm;
   const int32_t b = blockIdx.x;
+  lds_t *slice = smem + CFG::LDS_BYTES + wave * EPI_SLICE;
 
   float alpha = 1.0f;
   if constexpr (CFG::DT == DT_FP8) alpha = (*args.scale_a) * (*args.scale_b);
@@ -843,16 +900,18 @@ gemm_kernel_pp(KernelArgs args) {
       }
   }
 
-  constexpr int L = CFG::LA + CFG::LB;
+  // group 0's four waves load everything
+  using Prod = Producer<CFG, RAGGED_K, 4>;
+  constexpr int L = Prod::LA + Prod::LB;
   constexpr int NF = CFG::FM + CFG::FN;
-  Producer<CFG, RAGGED_K> prod;
-  prod.init(args, b, wave, lane);
-  auto issue_all = [&](int stage) {
+  Prod prod;
+  prod.init(args, b, wn, lane);
+  auto issue = [&](int stage) {
     prod.begin(args, smem, stage);
     [&]<int... J>(std::integer_sequence<int, J...>) {
-      (prod.template load<J>(wave, lane), ...);
+      (prod.template load<J>(wn), ...);
     }(std::make_integer_sequence<int, L>());
-    prod.end(args, wave, lane);
+    prod.end(args);
   };
 
   Cursor ccur;
@@ -860,15 +919,18 @@ gemm_kernel_pp(KernelArgs args) {
   WorkItem cw;
   bool cvalid = cursor_next(args.sp, ccur, cw);
 
-  int issued = 0;
+  int issued = 0;  // k-steps whose loads group 0 has issued
+  if (group == 0) {
 #pragma unroll
-  for (int s = 0; s < CFG::STAGES - 1; ++s)
-    if (prod.valid) {
-      issue_all(s);
-      ++issued;
-    }
-  if (issued > 0) wait_loads_after<L>(issued - 1);
-  lds_barrier();            // phase 0 begins: step 0 is in LDS
+    for (int s = 0; s < 2; ++s)
+      if (prod.valid) {
+        issue(s);
+        ++issued;
+      }
+    if (issued == 2) wait_vmcnt<L>();
+    else wait_vmcnt<0>();
+  }
+  lds_barrier();                  // phase 0 opens: step 0 is in LDS
   if (group == 1) lds_barrier();  // group 1 sits out phase 0
 
   Frags<CFG> fr[CFG::KSUB];
@@ -890,21 +952,20 @@ gemm_kernel_pp(KernelArgs args) {
         for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.0f;
 
     for (int k = cw.kb; k < cw.ke; ++k, ++c) {
-      // ---- M(c): fragments of step c, loads of step c+S-1 ----
-      const int stage = c % CFG::STAGES;
+      // ---- M(c): every fragment of step c; group 0 also loads step c+1 when its stage is free
+      const int stage = c & 1;
 #pragma unroll
       for (int t = 0; t < CFG::KSUB; ++t)
         [&]<int... E>(std::integer_sequence<int, E...>) {
           (load_frag<CFG, frag_order<CFG>(E)>(smem, stage, t, aoff, boff, fr[t]), ...);
         }(std::make_integer_sequence<int, NF>());
-      if (prod.valid) {
-        issue_all((c + CFG::STAGES - 1) % CFG::STAGES);
+      if (group == 0 && prod.valid && issued == c + 1) {
+        issue((c + 1) & 1);
         ++issued;
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (group == 1) wait_loads_after<L>(issued - (c + 1) - 1);
       lds_barrier();
-      // ---- C(c): MFMAs ----
+      // ---- C(c): the k-step's MFMAs, nothing else
 #pragma unroll
       for (int t = 0; t < CFG::KSUB; ++t)
 #pragma unroll
@@ -912,19 +973,19 @@ gemm_kernel_pp(KernelArgs args) {
 #pragma unroll
           for (int g = 0; g < CFG::FN; ++g)
             acc[f][g] = mfma<CFG::DT>(fr[t].b[g], fr[t].a[f], acc[f][g]);
-      if (group == 0) wait_loads_after<L>(issued - (c + 1) - 1);
+      if (group == 0) wait_vmcnt<0>();  // step c+1 has landed before M(c+1) reads it
       lds_barrier();
     }
-    // the stores run at the start of this group's next memory phase, under the other group's
-    // MFMAs
-    epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid);
+    if (args.out_bf16)
+      epilogue_pp<CFG>(args, cw, acc, alpha, wm, wn, lane, slice);
+    else
+      epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid);
     cvalid = cursor_next(args.sp, ccur, cw);
   }
   if (group == 0) lds_barrier();  // balance the barrier group 1 skipped at the start
   wait_vmcnt<0>();
 }
 
-// Clears the Stream-K locks and the error word before a run.
 __global__ void clear_ints_kernel(int *p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;

@@ -67,6 +67,12 @@ typedef enum {
 #define GEMM_FLAG_STREAMK_CHAIN 0x4u /* Stream-K fixup as the lock chain of "H100 Stream-K"
                                         section 6 (each split waits for its predecessor); default
                                         is the separate reduction, same sums in the same order   */
+#define GEMM_FLAG_PINGPONG 0x8u      /* run the tiles on the ping-pong kernel: two wave groups, one
+                                        wave of each per SIMD, alternate a memory phase (fragments
+                                        and loads) and an MFMA-only phase ("H100 Kernel Design"
+                                        sections 7.3-7.5).  256 x 256 tiles, data-parallel
+                                        schedules only (static or persistent, K > 0); other plans
+                                        with this flag return GEMM_ERR_UNSUPPORTED               */
 #define GEMM_FLAG_TEST_SKIP_PUBLISH 0x100u /* test only: the first Stream-K split of band tile 0
                                               does not publish its lock / arrival, so the bounded
                                               waits on it expire and report GEMM_DEVICE_ERR_SPIN */

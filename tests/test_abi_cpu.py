@@ -95,6 +95,12 @@ def create(**kw):
     (dict(K=104), L.GEMM_OK),                         # ragged K (multiple of 8 bf16 elements)
     (dict(M=300, N=264), L.GEMM_OK),                  # ragged M and N
     (dict(dtype_ab=L.GEMM_FP8_E4M3, K=272, bm=128, bn=128), L.GEMM_OK),
+    (dict(flags=L.GEMM_FLAG_PINGPONG), L.GEMM_OK),   # ping-pong picks 256 x 256 tiles
+    (dict(flags=L.GEMM_FLAG_PINGPONG, dtype_ab=L.GEMM_FP8_E4M3), L.GEMM_OK),
+    (dict(flags=L.GEMM_FLAG_PINGPONG, sched=L.GEMM_SCHED_STATIC, M=300, K=104), L.GEMM_OK),
+    (dict(flags=L.GEMM_FLAG_PINGPONG, K=0), L.GEMM_ERR_UNSUPPORTED),
+    (dict(flags=L.GEMM_FLAG_PINGPONG, bm=128, bn=128), L.GEMM_ERR_UNSUPPORTED),
+    (dict(flags=L.GEMM_FLAG_PINGPONG, sched=L.GEMM_SCHED_STREAMK), L.GEMM_ERR_UNSUPPORTED),
 ])
 def test_create_validation(kw, want):
     assert create(**kw) == want

@@ -83,6 +83,47 @@ def test_small_parity(dev, case, mode):
     assert_within_tolerance(C, reference(op), op, name)
 
 
+PINGPONG = [
+    # id, M, N, K, dtype, out, mapping, G, sched, workers
+    ("pp_bf16_persist", 512, 768, 1024, "bf16", "bf16", L.GEMM_MAP_GROUPED_M, 2,
+     L.GEMM_SCHED_PERSISTENT, 3),
+    ("pp_bf16_ragged", 300, 264, 104, "bf16", "bf16", L.GEMM_MAP_LINEAR_N, 1,
+     L.GEMM_SCHED_PERSISTENT, 1),
+    ("pp_bf16_one_kstep_many_items", 768, 512, 64, "bf16", "bf16", L.GEMM_MAP_GROUPED_M, 2,
+     L.GEMM_SCHED_PERSISTENT, 2),
+    ("pp_bf16_f32_static", 512, 512, 200, "bf16", "f32", L.GEMM_MAP_LINEAR_M, 1,
+     L.GEMM_SCHED_STATIC, 0),
+    ("pp_bf16_short_k", 264, 520, 8, "bf16", "bf16", L.GEMM_MAP_LINEAR_N, 1,
+     L.GEMM_SCHED_PERSISTENT, 2),
+    ("pp_fp8_persist", 512, 512, 1024, "e4m3", "bf16", L.GEMM_MAP_GROUPED_M, 16,
+     L.GEMM_SCHED_PERSISTENT, 2),
+    ("pp_fp8_ragged", 520, 264, 400, "e4m3", "bf16", L.GEMM_MAP_GROUPED_N, 2,
+     L.GEMM_SCHED_PERSISTENT, 3),
+]
+
+
+@pytest.mark.parametrize("case", PINGPONG, ids=[c[0] for c in PINGPONG])
+def test_pingpong_parity(dev, case):
+    """The ping-pong kernel (GEMM_FLAG_PINGPONG): several items per worker, ragged M/N/K, one
+    k-step per item, fp32 and bf16 outputs."""
+    name, M, N, K, dt, out, mapping, G, sched, workers = case
+    dist = ("normal", 1.0) if dt == "e4m3" else ("uniform",)
+    op = gi.make_operands(M, N, K, dt, dist, dist, seed=zlib.crc32(name.encode()) % 10000)
+    C, plan, _ = run_gpu(op, torch, dev, out, mapping, G, sched, workers, 256,
+                         flags=L.GEMM_FLAG_PINGPONG)
+    assert plan.info.bm == 256 and plan.info.threads == 512
+    assert_within_tolerance(C, reference(op), op, name)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "e4m3"])
+def test_pingpong_closed_form_exact(dev, dt):
+    M, N, K = 640, 520, 2048
+    op = gi.rowsum_pattern(M, N, K, dt)
+    C, plan, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_GROUPED_M, 2, L.GEMM_SCHED_PERSISTENT,
+                         2, 256, flags=L.GEMM_FLAG_PINGPONG)
+    assert np.all(C == 7 * K / 16)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "e4m3"])
 @pytest.mark.parametrize("tile,sched,workers", [(128, L.GEMM_SCHED_STATIC, 0),
                                                  (256, L.GEMM_SCHED_PERSISTENT, 3),
