@@ -127,14 +127,15 @@ def measured_traffic(workload):
 
 
 # name, workload key, mapping, group, sched, tile, out, workers[, bk[, variant]]
-# variant: "chain" = Stream-K lock-chain fixup, "pp" = ping-pong kernel
+# variant: "chain" = Stream-K lock-chain fixup, "coop" = the cooperative kernel instead of the
+# default ping-pong one for data-parallel 256 x 256 tiles
 RUNS = {
     "bf16_4096": ("bf16_4096", "grouped_m", 8, "persistent", 0, "bf16", 0),
-    "bf16_4096_pp": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "pp"),
+    "bf16_4096_coop": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "coop"),
     "bf16_4096_linear": ("bf16_4096", "linear_n", 1, "persistent", 0, "bf16", 0),
     "bf16_4096_t128": ("bf16_4096", "grouped_m", 8, "persistent", 128, "bf16", 0),
     "fp8_8192": ("fp8_8192", "grouped_m", 16, "persistent", 0, "bf16", 0),
-    "fp8_8192_pp": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "pp"),
+    "fp8_8192_coop": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "coop"),
     "bf16_mlp_up": ("bf16_mlp_up", "grouped_m", 8, "persistent", 0, "bf16", 0),
     "bf16_streamk": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256),
     "bf16_streamk_chain": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256, 0,
@@ -146,7 +147,8 @@ RUNS = {
 def run_flags(name, dg):
     """GEMM_FLAG_* bits of a RUNS entry's variant."""
     variant = RUNS[name][8] if len(RUNS[name]) > 8 else ""
-    return {"": 0, "chain": dg.GEMM_FLAG_STREAMK_CHAIN, "pp": dg.GEMM_FLAG_PINGPONG}[variant]
+    return {"": 0, "chain": dg.GEMM_FLAG_STREAMK_CHAIN, "pp": dg.GEMM_FLAG_PINGPONG,
+            "coop": dg.GEMM_FLAG_COOPERATIVE}[variant]
 
 
 def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
@@ -206,6 +208,7 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
     res = {
         "workload": wl_name, "M": op.M, "N": op.N, "K": op.K, "dtype": op.dtype, "out": out,
         "tile": [info.bm, info.bn, info.bk], "stages": info.stages, "mapping": mapping,
+        "kernel": "ping-pong" if info.kernel else "cooperative",
         "group": group, "sched": sched, "grid": info.grid,
         "dp_tiles": info.dp_tiles, "sk_tiles": info.sk_tiles, "warmup_launches": n_warm,
         "ms_per_step": wall * 1e3 / steps, "kernel_us": dev_ms * 1e3,
@@ -217,7 +220,7 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
     res["hbm_gbs_alg"] = alg_bytes / (dev_ms * 1e-3) / 1e9
     log(f"{name}: {res['kernel_us']:.1f} us/launch, {res['kernel_tflops']:.1f} TFLOP/s "
         f"({100 * res['frac_of_peak']:.1f}% of {PEAK_TFLOPS[op.dtype]:.0f}), grid {info.grid}, "
-        f"tile {info.bm}x{info.bn}x{info.bk}")
+        f"tile {info.bm}x{info.bn}x{info.bk}, {res['kernel']}")
     return res
 
 
@@ -289,14 +292,14 @@ def main():
     head = time_run("bf16_4096", args.steps, args.warmup, torch, dg, gi, cache, args.settle_ms)
     secondary = {}
     if not args.no_secondary:
-        for name in ("bf16_4096_linear", "bf16_4096_t128", "fp8_8192", "bf16_mlp_up",
-                     "bf16_streamk", "bf16_256"):
-            steps = max(10, args.steps // (4 if name == "fp8_8192" else 1))
+        for name in ("bf16_4096_coop", "bf16_4096_linear", "bf16_4096_t128", "fp8_8192",
+                     "fp8_8192_coop", "bf16_mlp_up", "bf16_streamk", "bf16_256"):
+            steps = max(10, args.steps // (4 if name.startswith("fp8_8192") else 1))
             r = time_run(name, steps, max(2, args.warmup // 2), torch, dg, gi, cache,
                          args.settle_ms / 2)
             secondary[name] = {k: r[k] for k in ("kernel_us", "kernel_tflops", "frac_of_peak",
                                                  "hbm_gbs_alg", "tile", "grid", "mapping",
-                                                 "sched")}
+                                                 "sched", "kernel")}
             if name in cache:
                 del cache[name]
     cache.clear()
@@ -320,7 +323,8 @@ def main():
         "config": {"workload": "bf16 gemm M=N=K=4096, uniform[-1,1], fp32 accumulate, bf16 out",
                    "M": 4096, "N": 4096, "K": 4096, "tile": head["tile"],
                    "mapping": "grouped_m", "group": 8, "sched": "persistent",
-                   "grid": head["grid"], "warmup_launches": head["warmup_launches"],
+                   "grid": head["grid"], "kernel": head["kernel"],
+                   "warmup_launches": head["warmup_launches"],
                    "settle_ms": args.settle_ms},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),

@@ -22,6 +22,7 @@ GEMM_FLAG_TRACE = 0x1
 GEMM_FLAG_NO_XCD_REMAP = 0x2
 GEMM_FLAG_STREAMK_CHAIN = 0x4
 GEMM_FLAG_PINGPONG = 0x8
+GEMM_FLAG_COOPERATIVE = 0x10
 GEMM_FLAG_TEST_SKIP_PUBLISH = 0x100
 GEMM_DEVICE_OK, GEMM_DEVICE_ERR_SPIN = 0, 1
 
@@ -52,7 +53,7 @@ class GemmPlanInfo(ctypes.Structure):
                 ("dp_tiles", ctypes.c_int64), ("sk_tiles", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("trace_offset", ctypes.c_int64),
                 ("trace_capacity", ctypes.c_int32), ("error_offset", ctypes.c_int32),
-                ("streamk_mode", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("streamk_mode", ctypes.c_int32), ("kernel", ctypes.c_int32)]
 
 
 _lib = None

@@ -136,7 +136,9 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (d.sched < GEMM_SCHED_STATIC || d.sched > GEMM_SCHED_AUTO) return GEMM_ERR_INVALID_ARG;
   if (d.num_workers < 0 || d.bm < 0 || d.bn < 0 || d.bk < 0) return GEMM_ERR_INVALID_ARG;
   if (d.flags & ~(GEMM_FLAG_TRACE | GEMM_FLAG_NO_XCD_REMAP | GEMM_FLAG_STREAMK_CHAIN |
-                  GEMM_FLAG_PINGPONG | GEMM_FLAG_TEST_SKIP_PUBLISH))
+                  GEMM_FLAG_PINGPONG | GEMM_FLAG_COOPERATIVE | GEMM_FLAG_TEST_SKIP_PUBLISH))
+    return GEMM_ERR_INVALID_ARG;
+  if ((d.flags & GEMM_FLAG_PINGPONG) && (d.flags & GEMM_FLAG_COOPERATIVE))
     return GEMM_ERR_INVALID_ARG;
 
   // Well-formed; now what the kernels implement.
@@ -147,8 +149,8 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (d.K * eb > (int64_t)1 << 30) return GEMM_ERR_UNSUPPORTED;
 
   // the ping-pong kernels run data-parallel work only, on 256 x 256 tiles
-  const bool want_pp = (d.flags & GEMM_FLAG_PINGPONG) != 0;
-  if (want_pp && (d.K == 0 || d.sched == GEMM_SCHED_STREAMK || d.sched == GEMM_SCHED_AUTO))
+  const bool force_pp = (d.flags & GEMM_FLAG_PINGPONG) != 0;
+  if (force_pp && (d.K == 0 || d.sched == GEMM_SCHED_STREAMK || d.sched == GEMM_SCHED_AUTO))
     return GEMM_ERR_UNSUPPORTED;
 
   // Tile shape: 256 x 256 unless asked otherwise or the problem has too few big tiles.
@@ -156,17 +158,19 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (bm == 0 && bn == 0) {
     const int64_t big = cdiv(d.M, 256) * cdiv(d.N, 256);  // 0 for an empty output
     const bool streamk = d.sched == GEMM_SCHED_STREAMK;
-    bm = bn = ((big >= 128 && !streamk) || want_pp) ? 256 : 128;
+    bm = bn = ((big >= 128 && !streamk) || force_pp) ? 256 : 128;
   } else if (bm == 0 || bn == 0) {
     bm = bn = (bm ? bm : bn);
   }
   const int want_dt = d.dtype_ab == GEMM_BF16 ? DT_BF16 : DT_FP8;
-  const KernelEntry *k = nullptr;
+  const KernelEntry *k_coop = nullptr, *k_pp = nullptr;
   for (const KernelEntry &e : kKernels)
-    if (!k && e.dt == want_dt && e.bm == bm && e.bn == bn && (d.bk == 0 || d.bk == e.bk) &&
-        (e.pingpong != 0) == want_pp)
-      k = &e;
-  if (!k) return GEMM_ERR_UNSUPPORTED;
+    if (e.dt == want_dt && e.bm == bm && e.bn == bn && (d.bk == 0 || d.bk == e.bk)) {
+      if (e.pingpong && !k_pp) k_pp = &e;
+      if (!e.pingpong && !k_coop) k_coop = &e;
+    }
+  if (force_pp ? !k_pp : !k_coop) return GEMM_ERR_UNSUPPORTED;
+  const KernelEntry *k = force_pp ? k_pp : k_coop;  // the schedule is planned with this one
   // rows of one tile must stay addressable by 32-bit buffer offsets
   if ((int64_t)bm * d.K * eb >= 0x7FFFFFF0ll || (int64_t)bn * d.K * eb >= 0x7FFFFFF0ll)
     return GEMM_ERR_UNSUPPORTED;
@@ -194,6 +198,11 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     streamk_plan(tiles, workers, dp, sk);
     sched = sk > 0 ? GEMM_SCHED_STREAMK : GEMM_SCHED_PERSISTENT;
   }
+  // Data-parallel work on 256 x 256 tiles runs on the ping-pong kernel unless the cooperative one
+  // is asked for (both hold one workgroup per CU, so the worker count stays).
+  if (!force_pp && !(d.flags & GEMM_FLAG_COOPERATIVE) && k_pp && d.K > 0 &&
+      (sched == GEMM_SCHED_STATIC || sched == GEMM_SCHED_PERSISTENT))
+    k = k_pp;
 
   SchedParams sp;
   memset(&sp, 0, sizeof sp);
@@ -294,6 +303,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   in.trace_capacity = (d.flags & GEMM_FLAG_TRACE) ? kTraceCap : 0;
   in.error_offset = (int32_t)p->error_off;
   in.streamk_mode = sk_mode;
+  in.kernel = k->pingpong ? 1 : 0;
   *out = p;
   return GEMM_OK;
 }

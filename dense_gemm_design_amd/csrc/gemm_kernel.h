@@ -799,20 +799,22 @@ gemm_kernel(KernelArgs args) {
 // onto the two waves of each SIMD.  The 8 waves form two groups of four (one wave per SIMD each);
 // group g owns rows [g*BM/2, (g+1)*BM/2) of the tile, each wave a WM x WN sub-tile.  A wave
 // alternates a memory phase M(c) -- read every MFMA fragment of k-step c from LDS into registers
-// (and, in group 0, issue the loads of k-step c+1) -- and a compute phase C(c): the k-step's MFMAs
-// back to back, with no memory operation in between.  Group 1 runs one phase behind group 0, so in
-// every phase one wave of each SIMD feeds the matrix core while the other does the memory work.
+// -- and a compute phase C(c): the k-step's MFMAs back to back.  Group 1 runs one phase behind
+// group 0, so in every phase one wave of each SIMD feeds the matrix core while the other reads LDS.
+// Group 0 issues all global->LDS loads: those of k-step c+2 after its fragment reads of M(c+1)
+// (phase 2c+2, the first phase their stage is free in).  Loads placed between the MFMAs of a
+// compute phase stretch that phase, and loads issued in phase 2c+3 would have only one phase to
+// land, so the whole share stays in group 0's memory phase.
 //
 // Phases are separated by workgroup barriers (barrier n closes phase n for every wave).  With two
 // stages the ring hand-offs are:
 //  * EMPTY: stage c mod 2 is read in phase 2c (group 0) and 2c+1 (group 1); every wave retires its
 //    reads (lgkmcnt(0)) before the barrier closing its memory phase, so from phase 2c+2 on the
-//    stage may take k-step c+2.  Group 0 issues those loads in its memory phase M(c+1), which is
-//    phase 2c+2 -- a whole k-step (two phases) before they are read.
-//  * FULL: at the end of C(c+1) (phase 2c+3) group 0 waits for its loads of step c+2
-//    (s_waitcnt vmcnt(0)) before the barrier that opens phase 2c+4, where M(c+2) reads them.
-// Group 1 therefore never issues global loads; the prologue loads steps 0 and 1.  Group 1 sits out
-// phase 0 with one extra barrier and group 0 balances it with one after its last phase.
+//    stage may take k-step c+2.
+//  * FULL: group 0 waits for its loads of step c+2 (s_waitcnt vmcnt(0)) at the end of its C(c+1),
+//    before the barrier that closes phase 2c+3; its M(c+2) reads the step in phase 2c+4.
+// The prologue loads steps 0 and 1.  Group 1 sits out phase 0 with one extra barrier and group 0
+// balances it with one after its last phase.
 // After an item's last C, the wave writes its sub-tile through its own 4 KiB slice of an LDS area
 // outside the ring, during its next memory phase (under the other group's MFMAs).
 template <class CFG>
@@ -857,7 +859,8 @@ __device__ __forceinline__ void epilogue_pp(const KernelArgs &args, const WorkIt
   }
 }
 
-constexpr int kPPSlice = 4096;  // per-wave epilogue staging area of the ping-pong kernel
+constexpr int kPPSlice = 4096;
+  // per-wave epilogue staging area of the ping-pong kernel
 template <class CFG>
 constexpr int pp_lds_bytes() {
   return CFG::LDS_BYTES + CFG::WAVES * kPPSlice;
@@ -900,12 +903,18 @@ gemm_kernel_pp(KernelArgs args) {
       }
   }
 
-  // group 0's four waves load everything
+  // group 0's four waves issue every load
   using Prod = Producer<CFG, RAGGED_K, 4>;
   constexpr int L = Prod::LA + Prod::LB;
   constexpr int NF = CFG::FM + CFG::FN;
   Prod prod;
   prod.init(args, b, wn, lane);
+  Cursor ccur;
+  cursor_init(args.sp, b, ccur);
+  WorkItem cw;
+  bool cvalid = cursor_next(args.sp, ccur, cw);
+
+  int issued = 0;  // k-steps whose loads group 0 has issued
   auto issue = [&](int stage) {
     prod.begin(args, smem, stage);
     [&]<int... J>(std::integer_sequence<int, J...>) {
@@ -913,13 +922,6 @@ gemm_kernel_pp(KernelArgs args) {
     }(std::make_integer_sequence<int, L>());
     prod.end(args);
   };
-
-  Cursor ccur;
-  cursor_init(args.sp, b, ccur);
-  WorkItem cw;
-  bool cvalid = cursor_next(args.sp, ccur, cw);
-
-  int issued = 0;  // k-steps whose loads group 0 has issued
   if (group == 0) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -927,8 +929,7 @@ gemm_kernel_pp(KernelArgs args) {
         issue(s);
         ++issued;
       }
-    if (issued == 2) wait_vmcnt<L>();
-    else wait_vmcnt<0>();
+    wait_vmcnt<0>();
   }
   lds_barrier();                  // phase 0 opens: step 0 is in LDS
   if (group == 1) lds_barrier();  // group 1 sits out phase 0
@@ -959,6 +960,7 @@ gemm_kernel_pp(KernelArgs args) {
         [&]<int... E>(std::integer_sequence<int, E...>) {
           (load_frag<CFG, frag_order<CFG>(E)>(smem, stage, t, aoff, boff, fr[t]), ...);
         }(std::make_integer_sequence<int, NF>());
+      // group 0: the loads of step c+1, whose stage became free with the phase that just began
       if (group == 0 && prod.valid && issued == c + 1) {
         issue((c + 1) & 1);
         ++issued;
@@ -973,7 +975,7 @@ gemm_kernel_pp(KernelArgs args) {
 #pragma unroll
           for (int g = 0; g < CFG::FN; ++g)
             acc[f][g] = mfma<CFG::DT>(fr[t].b[g], fr[t].a[f], acc[f][g]);
-      if (group == 0) wait_vmcnt<0>();  // step c+1 has landed before M(c+1) reads it
+      if (group == 0) wait_vmcnt<0>();  // step c+1 is in LDS before M(c+1) reads it
       lds_barrier();
     }
     if (args.out_bf16)

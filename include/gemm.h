@@ -67,12 +67,16 @@ typedef enum {
 #define GEMM_FLAG_STREAMK_CHAIN 0x4u /* Stream-K fixup as the lock chain of "H100 Stream-K"
                                         section 6 (each split waits for its predecessor); default
                                         is the separate reduction, same sums in the same order   */
-#define GEMM_FLAG_PINGPONG 0x8u      /* run the tiles on the ping-pong kernel: two wave groups, one
-                                        wave of each per SIMD, alternate a memory phase (fragments
-                                        and loads) and an MFMA-only phase ("H100 Kernel Design"
+#define GEMM_FLAG_PINGPONG 0x8u      /* require the ping-pong kernel: two wave groups, one wave of
+                                        each per SIMD, alternate a memory phase (fragments and
+                                        loads) and an MFMA-only phase ("H100 Kernel Design"
                                         sections 7.3-7.5).  256 x 256 tiles, data-parallel
                                         schedules only (static or persistent, K > 0); other plans
-                                        with this flag return GEMM_ERR_UNSUPPORTED               */
+                                        with this flag return GEMM_ERR_UNSUPPORTED.  Without
+                                        either kernel flag, such plans use it by default        */
+#define GEMM_FLAG_COOPERATIVE 0x10u  /* require the cooperative kernel (every wave loads and
+                                        computes; also runs Stream-K and 128 x 128 tiles).  Not
+                                        together with GEMM_FLAG_PINGPONG (GEMM_ERR_INVALID_ARG) */
 #define GEMM_FLAG_TEST_SKIP_PUBLISH 0x100u /* test only: the first Stream-K split of band tile 0
                                               does not publish its lock / arrival, so the bounded
                                               waits on it expire and report GEMM_DEVICE_ERR_SPIN */
@@ -117,7 +121,7 @@ typedef struct gemm_plan_info {
   int32_t trace_capacity;    /* records per workgroup                                            */
   int32_t error_offset;      /* byte offset of the device error word in the workspace (-1: none)*/
   int32_t streamk_mode;      /* 0 lock chain, 1 separate reduction (meaningful when sk_tiles>0)  */
-  int32_t reserved;
+  int32_t kernel;            /* 0 cooperative kernel, 1 ping-pong kernel                         */
 } gemm_plan_info;
 
 /* device error word values (read back from the workspace after a run) */

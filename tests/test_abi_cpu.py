@@ -101,6 +101,8 @@ def create(**kw):
     (dict(flags=L.GEMM_FLAG_PINGPONG, K=0), L.GEMM_ERR_UNSUPPORTED),
     (dict(flags=L.GEMM_FLAG_PINGPONG, bm=128, bn=128), L.GEMM_ERR_UNSUPPORTED),
     (dict(flags=L.GEMM_FLAG_PINGPONG, sched=L.GEMM_SCHED_STREAMK), L.GEMM_ERR_UNSUPPORTED),
+    (dict(flags=L.GEMM_FLAG_COOPERATIVE), L.GEMM_OK),
+    (dict(flags=L.GEMM_FLAG_COOPERATIVE | L.GEMM_FLAG_PINGPONG), L.GEMM_ERR_INVALID_ARG),
 ])
 def test_create_validation(kw, want):
     assert create(**kw) == want
@@ -130,6 +132,11 @@ def test_plan_info_and_workspace():
     q = L.Plan(L.make_desc(4096, 4096, 4096, sched=L.GEMM_SCHED_PERSISTENT, num_workers=256,
                            mapping=L.GEMM_MAP_GROUPED_M, group=8))
     assert q.workspace_bytes == 0 and q.info.bm == 256 and q.info.grid == 256
+    assert i.kernel == 0 and q.info.kernel == 1     # Stream-K: cooperative; 256^2 DP: ping-pong
+    assert q.info.lds_bytes == 160 * 1024
+    r = L.Plan(L.make_desc(4096, 4096, 4096, sched=L.GEMM_SCHED_PERSISTENT, num_workers=256,
+                           flags=L.GEMM_FLAG_COOPERATIVE))
+    assert r.info.kernel == 0 and r.info.lds_bytes == 128 * 1024
     s = L.Plan(L.make_desc(256, 256, 256, sched=L.GEMM_SCHED_STATIC, bm=128, bn=128))
     assert s.info.grid == 4 and s.info.sched == L.GEMM_SCHED_STATIC
 

@@ -64,7 +64,17 @@ SMALL = [
 
 
 SK_MODES = {"separate": 0, "chain": L.GEMM_FLAG_STREAMK_CHAIN}
-CASES = [(c, m) for c in SMALL for m in (SK_MODES if c[9] == L.GEMM_SCHED_STREAMK else ["separate"])]
+# data-parallel 256 x 256 plans default to the ping-pong kernel; "coop" forces the cooperative one
+MODES = dict(SK_MODES, coop=L.GEMM_FLAG_COOPERATIVE)
+
+
+def modes_of(case):
+    if case[9] == L.GEMM_SCHED_STREAMK:
+        return list(SK_MODES)
+    return ["separate", "coop"] if case[6] == 256 else ["separate"]
+
+
+CASES = [(c, m) for c in SMALL for m in modes_of(c)]
 
 
 @pytest.mark.parametrize("case,mode", CASES, ids=[f"{c[0]}-{m}" for c, m in CASES])
@@ -73,7 +83,9 @@ def test_small_parity(dev, case, mode):
     dist = ("normal", 1.0) if dt == "e4m3" else ("uniform",)
     op = gi.make_operands(M, N, K, dt, dist, dist, seed=zlib.crc32(name.encode()) % 10000)
     C, plan, _ = run_gpu(op, torch, dev, out, mapping, G, sched, workers, tile,
-                         flags=SK_MODES[mode])
+                         flags=MODES[mode])
+    if tile == 256 and sched != L.GEMM_SCHED_STREAMK:
+        assert plan.info.kernel == (0 if mode == "coop" else 1)
     if plan.info.sk_tiles:
         assert plan.info.streamk_mode == (0 if mode == "chain" else 1)
     if sched == L.GEMM_SCHED_STREAMK and name != "bf16_streamk_hybrid":
@@ -129,11 +141,14 @@ def test_pingpong_closed_form_exact(dev, dt):
                                                  (256, L.GEMM_SCHED_PERSISTENT, 3),
                                                  (128, L.GEMM_SCHED_STREAMK, 9)])
 def test_closed_form_row_sums_exact(dev, dt, tile, sched, workers):
-    """A[m,k] = ((m+k) mod 8)/8, B = 1: every output is exactly 7K/16 in FP32."""
+    """A[m,k] = ((m+k) mod 8)/8, B = 1: every output is exactly 7K/16 in FP32 (256 x 256
+    data-parallel plans: both kernels)."""
     M, N, K = 384, 264, 2048
     op = gi.rowsum_pattern(M, N, K, dt)
-    C, plan, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_GROUPED_M, 2, sched, workers, tile)
-    assert np.all(C == 7 * K / 16)
+    for flags in ([0, L.GEMM_FLAG_COOPERATIVE] if tile == 256 else [0]):
+        C, plan, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_GROUPED_M, 2, sched, workers, tile,
+                             flags=flags)
+        assert np.all(C == 7 * K / 16)
 
 
 @pytest.mark.parametrize("mode", list(SK_MODES))
