@@ -149,6 +149,10 @@ constexpr uint32_t kOOB = 0x80000000u;  // any offset >= num_records reads as ze
 // partial-tile area, which the planner keeps below 2 GiB.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCachePolicySC1 = 16;
+#ifndef C_STORE_POLICY
+#define C_STORE_POLICY 0
+#endif
+constexpr int kCStorePolicy = C_STORE_POLICY;  // cache-policy bits of the output stores
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const float *partials) {
   return __builtin_amdgcn_make_buffer_rsrc((void *)partials, (short)0, 0x7FFFFFF0, 0x00020000);
 }
@@ -853,7 +857,7 @@ __device__ __forceinline__ void epilogue_pp(const KernelArgs &args, const WorkIt
       const u32x4 v = *(p128)(rd_p + j * 1024);
       if (col_ok)
         __builtin_amdgcn_raw_buffer_store_b128(v, cr, st_off, (uint32_t)(f * 32 + j * 8) * ldc_b,
-                                               0);
+                                               kCStorePolicy);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
