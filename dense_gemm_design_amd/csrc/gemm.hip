@@ -28,6 +28,8 @@ using CfgBf16_256pp = TileCfg<DT_BF16, 256, 256, 64, 2, 4, 2, 1>;
 using CfgBf16_256 = TileCfg<DT_BF16, 256, 256, 64, 2, 4, 2, 1>;
 using CfgBf16_128 = TileCfg<DT_BF16, 128, 128, 64, 2, 2, 2, 1>;
 using CfgFp8_256pp = TileCfg<DT_FP8, 256, 256, 128, 2, 4, 2, 1>;
+using CfgBf16_256vs = TileCfg<DT_BF16, 256, 256, 64, 2, 2, 2, 1>;
+using CfgFp8_256vs = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1>;
 using CfgFp8_256 = TileCfg<DT_FP8, 256, 256, 128, 2, 4, 2, 1>;
 using CfgFp8_128 = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 2, 1>;
 
@@ -58,10 +60,24 @@ template <class CFG>
 const void *kernel_of_pp() {
   return (const void *)&gemm_kernel_pp<CFG, false>;
 }
+template <class CFG>
+hipError_t launch_vs(const KernelArgs &a, int grid, bool ragged_k, hipStream_t s) {
+  if (ragged_k)
+    hipLaunchKernelGGL((gemm_kernel_vs<CFG, true>), dim3(grid), dim3(CFG::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel_vs<CFG, false>), dim3(grid), dim3(CFG::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+template <class CFG>
+const void *kernel_of_vs() {
+  return (const void *)&gemm_kernel_vs<CFG, false>;
+}
 
-// pingpong: runs data-parallel work only (no Stream-K splits, K > 0)
+// kind: KIND_COOP runs every plan; KIND_PP and KIND_VS run data-parallel work only (no Stream-K
+// splits, K > 0)
+enum { KIND_COOP = 0, KIND_PP = 1, KIND_VS = 2 };
 struct KernelEntry {
-  int dt, bm, bn, bk, threads, stages, lds, pingpong;
+  int dt, bm, bn, bk, threads, stages, lds, kind;
   launch_fn launch;
   kernel_fn kernel;
 };
@@ -69,12 +85,17 @@ struct KernelEntry {
 template <class CFG>
 constexpr KernelEntry entry() {
   return KernelEntry{CFG::DT, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::STAGES,
-                     CFG::LDS_BYTES, 0, &launch_cfg<CFG>, &kernel_of<CFG>};
+                     CFG::LDS_BYTES, KIND_COOP, &launch_cfg<CFG>, &kernel_of<CFG>};
 }
 template <class CFG>
 constexpr KernelEntry entry_pp() {
   return KernelEntry{CFG::DT, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::STAGES,
-                     pp_lds_bytes<CFG>(), 1, &launch_pp<CFG>, &kernel_of_pp<CFG>};
+                     pp_lds_bytes<CFG>(), KIND_PP, &launch_pp<CFG>, &kernel_of_pp<CFG>};
+}
+template <class CFG>
+constexpr KernelEntry entry_vs() {
+  return KernelEntry{CFG::DT, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::STAGES,
+                     CFG::LDS_BYTES, KIND_VS, &launch_vs<CFG>, &kernel_of_vs<CFG>};
 }
 
 // The first entry that matches (dtype, bm, bn[, bk]) is the default for that tile shape.
@@ -84,6 +105,8 @@ const KernelEntry kKernels[] = {
     entry<CfgBf16_128>(),
     entry<CfgFp8_256>(),
     entry_pp<CfgFp8_256pp>(),
+    entry_vs<CfgBf16_256vs>(),
+    entry_vs<CfgFp8_256vs>(),
     entry<CfgFp8_128>(),
 };
 
@@ -135,11 +158,11 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (grouped && d.group < 1) return GEMM_ERR_INVALID_ARG;
   if (d.sched < GEMM_SCHED_STATIC || d.sched > GEMM_SCHED_AUTO) return GEMM_ERR_INVALID_ARG;
   if (d.num_workers < 0 || d.bm < 0 || d.bn < 0 || d.bk < 0) return GEMM_ERR_INVALID_ARG;
-  if (d.flags & ~(GEMM_FLAG_TRACE | GEMM_FLAG_NO_XCD_REMAP | GEMM_FLAG_STREAMK_CHAIN |
-                  GEMM_FLAG_PINGPONG | GEMM_FLAG_COOPERATIVE | GEMM_FLAG_TEST_SKIP_PUBLISH))
+  const uint32_t kind_flags = GEMM_FLAG_PINGPONG | GEMM_FLAG_COOPERATIVE | GEMM_FLAG_REGSTAGED;
+  if (d.flags & ~(GEMM_FLAG_TRACE | GEMM_FLAG_NO_XCD_REMAP | GEMM_FLAG_STREAMK_CHAIN | kind_flags |
+                  GEMM_FLAG_TEST_SKIP_PUBLISH))
     return GEMM_ERR_INVALID_ARG;
-  if ((d.flags & GEMM_FLAG_PINGPONG) && (d.flags & GEMM_FLAG_COOPERATIVE))
-    return GEMM_ERR_INVALID_ARG;
+  if (__builtin_popcount(d.flags & kind_flags) > 1) return GEMM_ERR_INVALID_ARG;
 
   // Well-formed; now what the kernels implement.
   if (d.layout_a != GEMM_ROW_MAJOR || d.layout_b != GEMM_COL_MAJOR) return GEMM_ERR_UNSUPPORTED;
@@ -148,9 +171,13 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (d.N % 8 != 0) return GEMM_ERR_UNSUPPORTED;           // 16-byte output rows
   if (d.K * eb > (int64_t)1 << 30) return GEMM_ERR_UNSUPPORTED;
 
-  // the ping-pong kernels run data-parallel work only, on 256 x 256 tiles
-  const bool force_pp = (d.flags & GEMM_FLAG_PINGPONG) != 0;
-  if (force_pp && (d.K == 0 || d.sched == GEMM_SCHED_STREAMK || d.sched == GEMM_SCHED_AUTO))
+  // the ping-pong and register-staged kernels run data-parallel work only, on 256 x 256 tiles
+  const int force_kind = (d.flags & GEMM_FLAG_PINGPONG)      ? KIND_PP
+                         : (d.flags & GEMM_FLAG_REGSTAGED)   ? KIND_VS
+                         : (d.flags & GEMM_FLAG_COOPERATIVE) ? KIND_COOP
+                                                             : -1;
+  const bool force_dp = force_kind == KIND_PP || force_kind == KIND_VS;
+  if (force_dp && (d.K == 0 || d.sched == GEMM_SCHED_STREAMK || d.sched == GEMM_SCHED_AUTO))
     return GEMM_ERR_UNSUPPORTED;
 
   // Tile shape: 256 x 256 unless asked otherwise or the problem has too few big tiles.
@@ -158,19 +185,18 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (bm == 0 && bn == 0) {
     const int64_t big = cdiv(d.M, 256) * cdiv(d.N, 256);  // 0 for an empty output
     const bool streamk = d.sched == GEMM_SCHED_STREAMK;
-    bm = bn = ((big >= 128 && !streamk) || force_pp) ? 256 : 128;
+    bm = bn = ((big >= 128 && !streamk) || force_dp) ? 256 : 128;
   } else if (bm == 0 || bn == 0) {
     bm = bn = (bm ? bm : bn);
   }
   const int want_dt = d.dtype_ab == GEMM_BF16 ? DT_BF16 : DT_FP8;
-  const KernelEntry *k_coop = nullptr, *k_pp = nullptr;
+  const KernelEntry *by_kind[3] = {nullptr, nullptr, nullptr};
   for (const KernelEntry &e : kKernels)
-    if (e.dt == want_dt && e.bm == bm && e.bn == bn && (d.bk == 0 || d.bk == e.bk)) {
-      if (e.pingpong && !k_pp) k_pp = &e;
-      if (!e.pingpong && !k_coop) k_coop = &e;
-    }
-  if (force_pp ? !k_pp : !k_coop) return GEMM_ERR_UNSUPPORTED;
-  const KernelEntry *k = force_pp ? k_pp : k_coop;  // the schedule is planned with this one
+    if (e.dt == want_dt && e.bm == bm && e.bn == bn && (d.bk == 0 || d.bk == e.bk) &&
+        !by_kind[e.kind])
+      by_kind[e.kind] = &e;
+  const KernelEntry *k = by_kind[force_kind >= 0 ? force_kind : KIND_COOP];
+  if (!k) return GEMM_ERR_UNSUPPORTED;  // the schedule is planned with this one
   // rows of one tile must stay addressable by 32-bit buffer offsets
   if ((int64_t)bm * d.K * eb >= 0x7FFFFFF0ll || (int64_t)bn * d.K * eb >= 0x7FFFFFF0ll)
     return GEMM_ERR_UNSUPPORTED;
@@ -198,11 +224,11 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     streamk_plan(tiles, workers, dp, sk);
     sched = sk > 0 ? GEMM_SCHED_STREAMK : GEMM_SCHED_PERSISTENT;
   }
-  // Data-parallel work on 256 x 256 tiles runs on the ping-pong kernel unless the cooperative one
-  // is asked for (both hold one workgroup per CU, so the worker count stays).
-  if (!force_pp && !(d.flags & GEMM_FLAG_COOPERATIVE) && k_pp && d.K > 0 &&
+  // Data-parallel work on 256 x 256 tiles runs on the ping-pong kernel unless a kernel is asked
+  // for (all of them hold one workgroup per CU, so the worker count stays).
+  if (force_kind < 0 && by_kind[KIND_PP] && d.K > 0 &&
       (sched == GEMM_SCHED_STATIC || sched == GEMM_SCHED_PERSISTENT))
-    k = k_pp;
+    k = by_kind[KIND_PP];
 
   SchedParams sp;
   memset(&sp, 0, sizeof sp);
@@ -303,7 +329,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   in.trace_capacity = (d.flags & GEMM_FLAG_TRACE) ? kTraceCap : 0;
   in.error_offset = (int32_t)p->error_off;
   in.streamk_mode = sk_mode;
-  in.kernel = k->pingpong ? 1 : 0;
+  in.kernel = k->kind;
   *out = p;
   return GEMM_OK;
 }

@@ -389,6 +389,24 @@ __device__ __forceinline__ void epilogue(const KernelArgs &args, const WorkItem 
       }
 }
 
+// Reads an accumulator that lives in an accumulation register (AGPR) into a VGPR.  The "a"
+// constraint keeps the value in its AGPR until this point; without it the compiler moves a whole
+// tile of accumulators out of the AGPRs at once when the k-loop ends.
+__device__ __forceinline__ float agpr_read(float x) {
+  float y;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(y) : "a"(x));
+  return y;
+}
+
+template <bool AGPR>
+__device__ __forceinline__ f32x4 quad_of(const f32x16 &blk, int q) {
+  if constexpr (AGPR)
+    return f32x4{agpr_read(blk[4 * q + 0]), agpr_read(blk[4 * q + 1]), agpr_read(blk[4 * q + 2]),
+                 agpr_read(blk[4 * q + 3])};
+  else
+    return f32x4{blk[4 * q + 0], blk[4 * q + 1], blk[4 * q + 2], blk[4 * q + 3]};
+}
+
 // Whole tile with bf16 output, staged through LDS so that every global store writes whole row
 // segments: the wave converts its sub-tile to bf16 in rounds of 32 rows into its own 1/WAVES
 // share of `stage` (a ring stage no wave reads any more), then reads the rows back 16 bytes per
@@ -397,7 +415,7 @@ __device__ __forceinline__ void epilogue(const KernelArgs &args, const WorkItem 
 // execute in order); the caller's barrier afterwards hands the stage back to the producer.
 // Rows are padded by 16 bytes, which spreads the 32 rows one write touches over the banks while
 // every address stays a per-lane base plus a constant.
-template <class CFG>
+template <class CFG, bool AGPR = false>
 __device__ __forceinline__ void epilogue_staged(const KernelArgs &args, const WorkItem &w,
                                                 const f32x16 (&acc)[CFG::FM][CFG::FN], float alpha,
                                                 int wm, int wn, int wave, int lane, lds_t *smem,
@@ -430,9 +448,10 @@ __device__ __forceinline__ void epilogue_staged(const KernelArgs &args, const Wo
     for (int g = 0; g < CFG::FN; ++g)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const f32x4 v = f32x4{acc[f][g][4 * q + 0], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2],
-                              acc[f][g][4 * q + 3]} * alpha;
+        const f32x4 v = quad_of<AGPR>(acc[f][g], q) * alpha;
         *(p64)(wr + (g * 4 + q) * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        // one quad at a time: the accumulators leave their registers in small groups
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
     for (int j = 0; j < READS; ++j) {
@@ -805,18 +824,19 @@ gemm_kernel(KernelArgs args) {
 // alternates a memory phase M(c) -- read every MFMA fragment of k-step c from LDS into registers
 // -- and a compute phase C(c): the k-step's MFMAs back to back.  Group 1 runs one phase behind
 // group 0, so in every phase one wave of each SIMD feeds the matrix core while the other reads LDS.
-// Group 0 issues all global->LDS loads: those of k-step c+2 after its fragment reads of M(c+1)
-// (phase 2c+2, the first phase their stage is free in).  Loads placed between the MFMAs of a
-// compute phase stretch that phase, and loads issued in phase 2c+3 would have only one phase to
-// land, so the whole share stays in group 0's memory phase.
+// The global->LDS loads of k-step c+1 go out in the memory phases M(c): group 0 issues the A
+// loads after its fragment reads (phase 2c, the first phase the stage is free in), group 1 the B
+// loads before its fragment reads (phase 2c+1), so each memory phase carries half of them.
+// Loads placed between the MFMAs of a compute phase stretch that phase instead.
 //
 // Phases are separated by workgroup barriers (barrier n closes phase n for every wave).  With two
 // stages the ring hand-offs are:
 //  * EMPTY: stage c mod 2 is read in phase 2c (group 0) and 2c+1 (group 1); every wave retires its
 //    reads (lgkmcnt(0)) before the barrier closing its memory phase, so from phase 2c+2 on the
 //    stage may take k-step c+2.
-//  * FULL: group 0 waits for its loads of step c+2 (s_waitcnt vmcnt(0)) at the end of its C(c+1),
-//    before the barrier that closes phase 2c+3; its M(c+2) reads the step in phase 2c+4.
+//  * FULL: step c+1 is read from phase 2c+2 on.  Group 0 waits for its loads of it
+//    (s_waitcnt vmcnt(0)) at the end of its C(c) and group 1 at the end of its M(c), both before
+//    the barrier that closes phase 2c+1.
 // The prologue loads steps 0 and 1.  Group 1 sits out phase 0 with one extra barrier and group 0
 // balances it with one after its last phase.
 // After an item's last C, the wave writes its sub-tile through its own 4 KiB slice of an LDS area
@@ -864,6 +884,9 @@ __device__ __forceinline__ void epilogue_pp(const KernelArgs &args, const WorkIt
 }
 
 constexpr int kPPSlice = 4096;
+#ifndef PP_SPLIT
+#define PP_SPLIT 1  // 1: A loads by group 0, B loads by group 1; 0: group 0 issues all
+#endif
   // per-wave epilogue staging area of the ping-pong kernel
 template <class CFG>
 constexpr int pp_lds_bytes() {
@@ -907,7 +930,7 @@ gemm_kernel_pp(KernelArgs args) {
       }
   }
 
-  // group 0's four waves issue every load
+  // the four waves of each group share a k-step's loads (see PP_SPLIT)
   using Prod = Producer<CFG, RAGGED_K, 4>;
   constexpr int L = Prod::LA + Prod::LB;
   constexpr int NF = CFG::FM + CFG::FN;
@@ -918,15 +941,23 @@ gemm_kernel_pp(KernelArgs args) {
   WorkItem cw;
   bool cvalid = cursor_next(args.sp, ccur, cw);
 
-  int issued = 0;  // k-steps whose loads group 0 has issued
+  // PP_SPLIT 0: group 0 issues every load; 1: group 0 the A loads, group 1 the B loads
+  constexpr int G0_HI = PP_SPLIT ? Prod::LA : L;  // group 0's loads [0, G0_HI), group 1's the rest
+  int issued = 0;  // k-steps whose loads this wave has issued
   auto issue = [&](int stage) {
     prod.begin(args, smem, stage);
-    [&]<int... J>(std::integer_sequence<int, J...>) {
-      (prod.template load<J>(wn), ...);
-    }(std::make_integer_sequence<int, L>());
+    if (group == 0) {
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        (prod.template load<J>(wn), ...);
+      }(std::make_integer_sequence<int, G0_HI>());
+    } else {
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        (prod.template load<G0_HI + J>(wn), ...);
+      }(std::make_integer_sequence<int, L - G0_HI>());
+    }
     prod.end(args);
   };
-  if (group == 0) {
+  if (group == 0 || PP_SPLIT) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       if (prod.valid) {
@@ -959,6 +990,11 @@ gemm_kernel_pp(KernelArgs args) {
     for (int k = cw.kb; k < cw.ke; ++k, ++c) {
       // ---- M(c): every fragment of step c; group 0 also loads step c+1 when its stage is free
       const int stage = c & 1;
+      // group 1 (split loads): its loads of step c+1 first, to give them the whole phase
+      if (PP_SPLIT && group == 1 && prod.valid && issued == c + 1) {
+        issue((c + 1) & 1);
+        ++issued;
+      }
 #pragma unroll
       for (int t = 0; t < CFG::KSUB; ++t)
         [&]<int... E>(std::integer_sequence<int, E...>) {
@@ -970,6 +1006,7 @@ gemm_kernel_pp(KernelArgs args) {
         ++issued;
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (PP_SPLIT && group == 1) wait_vmcnt<0>();  // its loads of step c+1 have landed
       lds_barrier();
       // ---- C(c): the k-step's MFMAs, nothing else
 #pragma unroll
@@ -989,6 +1026,314 @@ gemm_kernel_pp(KernelArgs args) {
     cvalid = cursor_next(args.sp, ccur, cw);
   }
   if (group == 0) lds_barrier();  // balance the barrier group 1 skipped at the start
+  wait_vmcnt<0>();
+}
+
+// ---- register-staged kernel (data-parallel tiles) ---------------------------------------------
+//
+// Four waves, one per SIMD, each owning a 128 x 128 sub-tile (4 x 4 MFMA blocks, accumulators in
+// the accumulation registers): a third fewer LDS fragment reads per MFMA than 128 x 64 sub-tiles.
+// The operands go global -> registers -> LDS ("cuTensorMap" lesson's staging into shared memory,
+// done by the waves themselves): load j of k-step c+2 is issued in k-step c right after the LDS
+// write j of k-step c+1 has taken its registers, so one set of L staging registers suffices, the
+// address unit is busy all through the k-step instead of in bursts, and every load has a whole
+// k-step to arrive.  Because a wave's loads complete in issue order, the write j waits for
+// vmcnt(L-1): the L-1 loads issued after load j may still be in flight.
+//
+// Ring (2 stages) per k-step c, handshake at slot HS of the last sub-step as in gemm_kernel:
+//  * EMPTY(c-1): stage (c+1) mod 2 held step c-1, whose last fragment reads came before the
+//    handshake of step c (lgkmcnt(0) then s_barrier), so during step c the waves write step c+1
+//    into it;
+//  * FULL(c+1): the handshake of step c+1 (in step c's last sub-step) waits for the wave's own LDS
+//    writes (lgkmcnt(0)) and then the barrier, after which everyone reads step c+1.
+// The writes of step c+1 sit in the slots before that handshake.
+#ifndef VS_NBUF
+#define VS_NBUF 1  // staging register sets of the register-staged kernel (1 or 2)
+#endif
+template <class CFG, bool RAGGED_K>
+struct Stager {
+  static constexpr int NW = CFG::WAVES;
+  static constexpr int LA = CFG::A_BYTES / 1024 / NW, LB = CFG::B_BYTES / 1024 / NW;
+  static constexpr int L = LA + LB;
+  static_assert(CFG::A_BYTES % (1024 * NW) == 0 && CFG::B_BYTES % (1024 * NW) == 0, "load split");
+  static_assert((NW * CFG::RPL) % (CFG::CH << CFG::SWZ) == 0, "swizzle must repeat per load");
+  static_assert(L <= 63, "vmcnt range");
+  Cursor cur;
+  int32_t valid, k, ke, rows_a, rows_b, edge;
+  __amdgpu_buffer_rsrc_t ra, rb;
+  int32_t sta, stb;   // global byte stride between loads j and j + 1 (uniform)
+  uint32_t voa, vob;  // lane global offsets of load 0: row row0, chunk lane % CH (coalesced)
+  uint32_t row0;      // tile row of the lane in load 0
+  uint32_t lds0;      // lane LDS offset of load 0 within an operand: the row's swizzled chunk
+  uint32_t chunk16;
+  u32x4 buf[VS_NBUF][L];  // staging registers; k-step c uses set c mod VS_NBUF
+
+  __device__ __forceinline__ void init(const KernelArgs &args, int32_t b, int wave, int lane) {
+    row0 = (uint32_t)(wave * CFG::RPL + lane / CFG::CH);
+    const uint32_t chunk = (uint32_t)(lane % CFG::CH);
+    chunk16 = chunk * 16;
+    voa = row0 * (uint32_t)args.lda_bytes + chunk16;
+    vob = row0 * (uint32_t)args.ldb_bytes + chunk16;
+    lds0 = row0 * CFG::ROWB + ((chunk ^ ((row0 >> CFG::SWZ) & (CFG::CH - 1))) * 16);
+    sta = (int32_t)(NW * CFG::RPL * args.lda_bytes);
+    stb = (int32_t)(NW * CFG::RPL * args.ldb_bytes);
+    cursor_init(args.sp, b, cur);
+    next_item(args);
+  }
+
+  __device__ __forceinline__ void next_item(const KernelArgs &args) {
+    WorkItem w;
+    while ((valid = cursor_next(args.sp, cur, w)) && w.kb == w.ke) {
+    }
+    if (valid) {
+      k = w.kb;
+      ke = w.ke;
+      const int64_t m0 = (int64_t)w.m * CFG::BM, n0 = (int64_t)w.n * CFG::BN;
+      rows_a = (int32_t)(args.M - m0 < CFG::BM ? args.M - m0 : CFG::BM);
+      rows_b = (int32_t)(args.N - n0 < CFG::BN ? args.N - n0 : CFG::BN);
+      edge = rows_a < CFG::BM || rows_b < CFG::BN;
+      ra = make_rsrc(args.A + m0 * args.lda_bytes, (int64_t)rows_a * args.lda_bytes);
+      rb = make_rsrc(args.B + n0 * args.ldb_bytes, (int64_t)rows_b * args.ldb_bytes);
+    }
+  }
+
+  uint32_t koa, kob;
+  // loads of the cursor's k-step: begin() fixes the k offset, load<J>() fetches 1 KiB per wave
+  // into buf[J], end() advances the cursor.  With no k-step left (valid == 0) the loads still go
+  // out, at an offset past every range: they read zeros and touch no memory, which keeps the
+  // count of a wave's outstanding loads the same in every k-step.
+  __device__ __forceinline__ void begin(const KernelArgs &args) {
+    const uint32_t kbytes = (uint32_t)k * CFG::ROWB;
+    koa = voa + kbytes;
+    kob = vob + kbytes;
+    if (RAGGED_K && (int64_t)(k + 1) * CFG::ROWB > args.K * CFG::EB) {  // chunks past K read 0
+      if (chunk16 >= (uint32_t)(args.K * CFG::EB) - kbytes) koa = kob = kOOB;
+    }
+    if (!valid) koa = kob = kOOB;
+  }
+  template <int J, int SET>
+  __device__ __forceinline__ void load() {
+    constexpr bool IS_A = J < LA;
+    constexpr int j = IS_A ? J : J - LA;
+    uint32_t off = IS_A ? koa : kob;
+    if (edge && row0 + j * NW * CFG::RPL >= (uint32_t)(IS_A ? rows_a : rows_b)) off = kOOB;
+    buf[SET][J] =
+        __builtin_amdgcn_raw_buffer_load_b128(IS_A ? ra : rb, off, j * (IS_A ? sta : stb), 0);
+  }
+  __device__ __forceinline__ void end(const KernelArgs &args) {
+    if (++k == ke) next_item(args);
+  }
+  // LDS write of buf[SET][J] into `stage`
+  template <int J, int SET>
+  __device__ __forceinline__ void store(lds_t *smem, int stage) const {
+    typedef u32x4 __attribute__((address_space(3))) *p128;
+    constexpr bool IS_A = J < LA;
+    constexpr int j = IS_A ? J : J - LA;
+    *(p128)(smem + stage * CFG::STAGE_BYTES + (IS_A ? 0 : CFG::A_BYTES) + lds0 +
+            j * NW * CFG::RPL * CFG::ROWB) = buf[SET][J];
+  }
+};
+
+template <class CFG, bool RAGGED_K>
+__global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::THREADS),
+                               amdgpu_waves_per_eu(1, 1)))
+gemm_kernel_vs(KernelArgs args) {
+  static_assert(CFG::WAVES == 4 && CFG::STAGES == 2, "four waves, two stages");
+  static_assert(CFG::KSUB % 2 == 0, "k-tile must hold an even number of MFMA sub-steps");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[CFG::LDS_BYTES];
+  lds_t *smem = (lds_t *)(size_t)(uint32_t)(size_t)(lds_t *)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / CFG::WGN, wn = wave % CFG::WGN;
+  const int32_t b = blockIdx.x;
+
+  float alpha = 1.0f;
+  if constexpr (CFG::DT == DT_FP8) alpha = (*args.scale_a) * (*args.scale_b);
+
+  uint32_t aoff[CFG::KSUB][CFG::CPL], boff[CFG::KSUB][CFG::CPL];
+  {
+    const int r = lane & 31;
+    const int swz = (r >> CFG::SWZ) & (CFG::CH - 1);
+#pragma unroll
+    for (int s = 0; s < CFG::KSUB; ++s)
+#pragma unroll
+      for (int h = 0; h < CFG::CPL; ++h) {
+        const int chunk = (s * 2 + (lane >> 5)) * CFG::CPL + h;
+        const uint32_t in_row = (uint32_t)((chunk ^ swz) * 16);
+        aoff[s][h] = (uint32_t)((wm * CFG::WM + r) * CFG::ROWB) + in_row;
+        boff[s][h] = (uint32_t)(CFG::A_BYTES + (wn * CFG::WN + r) * CFG::ROWB) + in_row;
+      }
+  }
+
+  using St = Stager<CFG, RAGGED_K>;
+  constexpr int L = St::L;
+  constexpr int NM = CFG::FM * CFG::FN;  // MFMAs per sub-step
+  constexpr int NF = CFG::FM + CFG::FN;
+  constexpr int HS = NM / 4;             // handshake slot in the last sub-step
+  constexpr int WSLOTS = (CFG::KSUB - 1) * NM + HS;  // slots of a k-step before its handshake
+  St st;
+  st.init(args, b, wave, lane);
+
+  Cursor ccur;
+  cursor_init(args.sp, b, ccur);
+  WorkItem cw;
+  bool cvalid = cursor_next(args.sp, ccur, cw);
+
+  // k-steps whose loads are issued / written to LDS so far
+  int loaded = 0, written = 0;
+  auto load_step = [&](auto set_c) {
+    constexpr int SET = decltype(set_c)::value;
+    st.begin(args);
+    [&]<int... J>(std::integer_sequence<int, J...>) { (st.template load<J, SET>(), ...); }(
+        std::make_integer_sequence<int, L>());
+    if (st.valid) {
+      st.end(args);
+      ++loaded;
+    }
+  };
+  // Prologue: step 0 into stage 0, loads of step 1 in flight (zeros past the last k-step).
+  const bool any = st.valid;
+  load_step(std::integral_constant<int, 0>());
+  [&]<int... J>(std::integer_sequence<int, J...>) { (st.template store<J, 0>(smem, 0), ...); }(
+      std::make_integer_sequence<int, L>());
+  if (any) ++written;
+  load_step(std::integral_constant<int, 1 % VS_NBUF>());
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  lds_barrier();
+
+  Frags<CFG> fr[2];
+  if (written > 0) {
+    [&]<int... E>(std::integer_sequence<int, E...>) {
+      (load_frag<CFG, frag_order<CFG>(E)>(smem, 0, 0, aoff, boff, fr[0]), ...);
+    }(std::make_integer_sequence<int, NF>());
+  }
+
+  int c = 0;
+  bool pairs = false;  // does this k-step write step c+1 (and load step c+2)?
+  // PAR = c mod VS_NBUF: step c+1 sits in staging set (PAR+1) mod VS_NBUF, step c+2 goes to
+  // set PAR (with one set both are the same registers, taken one load at a time)
+  auto substep = [&](auto s_c, auto par_c, auto acc_ref) {
+    constexpr int S = decltype(s_c)::value;
+    constexpr int PAR = decltype(par_c)::value;
+    constexpr int WSET = (PAR + 1) % VS_NBUF, LSET = PAR;
+    constexpr int CUR = S & 1, NXT = (S + 1) & 1;
+    constexpr bool LAST = S == CFG::KSUB - 1;
+    auto &acc = *acc_ref;
+    const int stage = c & 1;
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (
+          [&] {
+            constexpr int i = I;
+            constexpr int f = i / CFG::FN, g = i % CFG::FN;
+            acc[f][g] = mfma<CFG::DT>(fr[CUR].b[g], fr[CUR].a[f], acc[f][g]);
+            // (LDS write j of step c+1, load j of step c+2) pairs in the slots before the
+            // handshake.  They run in every k-step: past the last k-step the writes land in the
+            // drained stage nobody reads and the loads read zeros (see Stager::begin), so the
+            // number of outstanding loads at each write is always L-1.
+            constexpr int slot = S * NM + i;
+            if constexpr (slot < WSLOTS) {
+              constexpr int lo = ops_before(slot, L, 0, WSLOTS);
+              constexpr int hi = ops_before(slot + 1, L, 0, WSLOTS);
+              [&]<int... J>(std::integer_sequence<int, J...>) {
+                (
+                    [&] {
+                      constexpr int j = lo + J;
+                      st.template store<j, WSET>(smem, (c + 1) & 1);
+                      if constexpr (j == 0) st.begin(args);
+                      st.template load<j, LSET>();
+                      if constexpr (j == L - 1) {
+                        if (pairs) ++written;
+                        if (st.valid) {
+                          st.end(args);
+                          ++loaded;
+                        }
+                      }
+                    }(),
+                    ...);
+              }(std::make_integer_sequence<int, hi - lo>());
+            }
+            if constexpr (!LAST) {
+              constexpr int lo = ops_before(i, NF, 0, NM);
+              constexpr int hi = ops_before(i + 1, NF, 0, NM);
+              [&]<int... E>(std::integer_sequence<int, E...>) {
+                (load_frag<CFG, frag_order<CFG>(lo + E)>(smem, stage, S + 1, aoff, boff,
+                                                         fr[NXT]),
+                 ...);
+              }(std::make_integer_sequence<int, hi - lo>());
+            } else {
+              if constexpr (i + 1 == HS) {
+                if (c + 1 < written) {
+                  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                  lds_barrier();
+                }
+              }
+              if constexpr (i + 1 >= HS) {
+                constexpr int lo = ops_before(i, NF, HS, NM);
+                constexpr int hi = ops_before(i + 1, NF, HS, NM);
+                if (c + 1 < written) {
+                  [&]<int... E>(std::integer_sequence<int, E...>) {
+                    (load_frag<CFG, frag_order<CFG>(lo + E)>(smem, (c + 1) & 1, 0, aoff, boff,
+                                                             fr[NXT]),
+                     ...);
+                  }(std::make_integer_sequence<int, hi - lo>());
+                }
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }(),
+          ...);
+    }(std::make_integer_sequence<int, NM>());
+  };
+
+  int seq = 0;
+  while (cvalid) {
+    if ((args.flags & KF_TRACE) && tid == 0 && seq < args.trace_cap) {
+      int *t = args.trace + ((int64_t)b * args.trace_cap + seq) * 8;
+      t[0] = b; t[1] = seq; t[2] = cw.tile; t[3] = cw.m;
+      t[4] = cw.n; t[5] = cw.kb; t[6] = cw.ke; t[7] = cw.role;
+    }
+    f32x16 acc[CFG::FM][CFG::FN];
+#pragma unroll
+    for (int f = 0; f < CFG::FM; ++f)
+#pragma unroll
+      for (int g = 0; g < CFG::FN; ++g)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.0f;
+
+    for (int k = cw.kb; k < cw.ke; ++k, ++c) {
+      // this k-step writes step c+1 if its loads were issued and, at the item's last k-step,
+      // if no epilogue needs that stage: the staged epilogue uses stage c mod 2, step c+1 goes
+      // to the other one, so writing is always allowed
+      pairs = loaded > c + 1;
+      auto kstep = [&](auto par_c) {
+        [&]<int... S>(std::integer_sequence<int, S...>) {
+          (substep(std::integral_constant<int, S>(), par_c, &acc), ...);
+        }(std::make_integer_sequence<int, CFG::KSUB>());
+      };
+      if (VS_NBUF == 2 && (c & 1))
+        kstep(std::integral_constant<int, 1 % VS_NBUF>());
+      else
+        kstep(std::integral_constant<int, 0>());
+    }
+
+    if (args.out_bf16) {
+      // stage c-1 is drained once the handshake of step c ran (all waves past their reads of it);
+      // without a next step there was none
+      if (c >= written) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+      }
+      epilogue_staged<CFG, true>(args, cw, acc, alpha, wm, wn, wave, lane, smem,
+                                 (c + CFG::STAGES - 1) % CFG::STAGES);
+      lds_barrier();  // the stage takes step c+1's writes in the next k-step
+    } else {
+      epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid);
+    }
+    ++seq;
+    cvalid = cursor_next(args.sp, ccur, cw);
+  }
   wait_vmcnt<0>();
 }
 

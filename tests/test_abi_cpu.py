@@ -103,6 +103,11 @@ def create(**kw):
     (dict(flags=L.GEMM_FLAG_PINGPONG, sched=L.GEMM_SCHED_STREAMK), L.GEMM_ERR_UNSUPPORTED),
     (dict(flags=L.GEMM_FLAG_COOPERATIVE), L.GEMM_OK),
     (dict(flags=L.GEMM_FLAG_COOPERATIVE | L.GEMM_FLAG_PINGPONG), L.GEMM_ERR_INVALID_ARG),
+    (dict(flags=L.GEMM_FLAG_REGSTAGED | L.GEMM_FLAG_PINGPONG), L.GEMM_ERR_INVALID_ARG),
+    (dict(flags=L.GEMM_FLAG_REGSTAGED), L.GEMM_OK),
+    (dict(flags=L.GEMM_FLAG_REGSTAGED, dtype_ab=L.GEMM_FP8_E4M3, K=400, M=300), L.GEMM_OK),
+    (dict(flags=L.GEMM_FLAG_REGSTAGED, sched=L.GEMM_SCHED_STREAMK), L.GEMM_ERR_UNSUPPORTED),
+    (dict(flags=L.GEMM_FLAG_REGSTAGED, K=0), L.GEMM_ERR_UNSUPPORTED),
 ])
 def test_create_validation(kw, want):
     assert create(**kw) == want

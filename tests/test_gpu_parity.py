@@ -114,25 +114,32 @@ PINGPONG = [
 ]
 
 
+# data-parallel kernels for 256 x 256 tiles: flag, plan_info.kernel, threads
+DP_KERNELS = {"pingpong": (L.GEMM_FLAG_PINGPONG, 1, 512),
+              "regstaged": (L.GEMM_FLAG_REGSTAGED, 2, 256)}
+
+
+@pytest.mark.parametrize("kern", list(DP_KERNELS))
 @pytest.mark.parametrize("case", PINGPONG, ids=[c[0] for c in PINGPONG])
-def test_pingpong_parity(dev, case):
-    """The ping-pong kernel (GEMM_FLAG_PINGPONG): several items per worker, ragged M/N/K, one
-    k-step per item, fp32 and bf16 outputs."""
+def test_pingpong_parity(dev, case, kern):
+    """The data-parallel kernels (ping-pong, register-staged): several items per worker, ragged
+    M/N/K, one k-step per item, fp32 and bf16 outputs."""
     name, M, N, K, dt, out, mapping, G, sched, workers = case
+    flag, kind, threads = DP_KERNELS[kern]
     dist = ("normal", 1.0) if dt == "e4m3" else ("uniform",)
     op = gi.make_operands(M, N, K, dt, dist, dist, seed=zlib.crc32(name.encode()) % 10000)
-    C, plan, _ = run_gpu(op, torch, dev, out, mapping, G, sched, workers, 256,
-                         flags=L.GEMM_FLAG_PINGPONG)
-    assert plan.info.bm == 256 and plan.info.threads == 512
+    C, plan, _ = run_gpu(op, torch, dev, out, mapping, G, sched, workers, 256, flags=flag)
+    assert plan.info.bm == 256 and plan.info.threads == threads and plan.info.kernel == kind
     assert_within_tolerance(C, reference(op), op, name)
 
 
+@pytest.mark.parametrize("kern", list(DP_KERNELS))
 @pytest.mark.parametrize("dt", ["bf16", "e4m3"])
-def test_pingpong_closed_form_exact(dev, dt):
+def test_pingpong_closed_form_exact(dev, dt, kern):
     M, N, K = 640, 520, 2048
     op = gi.rowsum_pattern(M, N, K, dt)
     C, plan, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_GROUPED_M, 2, L.GEMM_SCHED_PERSISTENT,
-                         2, 256, flags=L.GEMM_FLAG_PINGPONG)
+                         2, 256, flags=DP_KERNELS[kern][0])
     assert np.all(C == 7 * K / 16)
 
 
