@@ -133,8 +133,10 @@ __device__ __forceinline__ void wait_loads_after(int steps_after) {
   else wait_vmcnt<(4 * L > 63 ? 63 : 4 * L)>();
 }
 
+// A buffer resource over [base, base + bytes): every access at or past the end reads zero or is
+// dropped.  bytes <= 0 (a region that starts past the end of its matrix) gives an empty range.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *base, int64_t bytes) {
-  const int32_t n = bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0 : (int32_t)bytes;
+  const int32_t n = bytes <= 0 ? 0 : bytes > 0x7FFFFFF0ll ? 0x7FFFFFF0 : (int32_t)bytes;
   return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, n, 0x00020000);
 }
 
@@ -149,10 +151,7 @@ constexpr uint32_t kOOB = 0x80000000u;  // any offset >= num_records reads as ze
 // partial-tile area, which the planner keeps below 2 GiB.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCachePolicySC1 = 16;
-#ifndef C_STORE_POLICY
-#define C_STORE_POLICY 0
-#endif
-constexpr int kCStorePolicy = C_STORE_POLICY;  // cache-policy bits of the output stores
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const float *partials) {
   return __builtin_amdgcn_make_buffer_rsrc((void *)partials, (short)0, 0x7FFFFFF0, 0x00020000);
 }
@@ -232,6 +231,7 @@ struct Producer {
     vob = row0 * (uint32_t)args.ldb_bytes + chunk16;
     sta = (int32_t)(NW * CFG::RPL * args.lda_bytes);
     stb = (int32_t)(NW * CFG::RPL * args.ldb_bytes);
+    ra = rb = make_rsrc(args.A, 0);  // empty until an item sets them
     cursor_init(args.sp, b, cur);
     next_item(args);
   }
@@ -431,6 +431,7 @@ __device__ __forceinline__ void epilogue_staged(const KernelArgs &args, const Wo
   lds_t *share = smem + stage * CFG::STAGE_BYTES + wave * SHARE;
   const int64_t m0 = (int64_t)w.m * CFG::BM + wm * CFG::WM;
   const int64_t n0 = (int64_t)w.n * CFG::BN + wn * CFG::WN;
+  if (m0 >= args.M || n0 >= args.N) return;  // the wave's sub-tile lies past the edge of C
   // Stores go through a buffer resource based at the sub-tile origin and ending at the end of C:
   // rows at or past M fall outside it and are dropped by the hardware range check; a lane's
   // 8 columns are all inside or all outside N (N is a multiple of 8).
@@ -852,6 +853,7 @@ __device__ __forceinline__ void epilogue_pp(const KernelArgs &args, const WorkIt
   // row back touch 8 distinct bank groups
   const int64_t m0 = (int64_t)w.m * CFG::BM + wm * CFG::WM;
   const int64_t n0 = (int64_t)w.n * CFG::BN + wn * CFG::WN;
+  if (m0 >= args.M || n0 >= args.N) return;  // the wave's sub-tile lies past the edge of C
   const int64_t origin = m0 * args.ldc + n0;
   const __amdgpu_buffer_rsrc_t cr = make_rsrc(args.C + origin * 2, (args.M * args.ldc - origin) * 2);
   const int chunk_l = lane & 7, rrow = lane >> 3;  // read-back: 8 rows per wave-wide read
@@ -877,16 +879,14 @@ __device__ __forceinline__ void epilogue_pp(const KernelArgs &args, const WorkIt
       const u32x4 v = *(p128)(rd_p + j * 1024);
       if (col_ok)
         __builtin_amdgcn_raw_buffer_store_b128(v, cr, st_off, (uint32_t)(f * 32 + j * 8) * ldc_b,
-                                               kCStorePolicy);
+                                               0);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 constexpr int kPPSlice = 4096;
-#ifndef PP_SPLIT
-#define PP_SPLIT 1  // 1: A loads by group 0, B loads by group 1; 0: group 0 issues all
-#endif
+
   // per-wave epilogue staging area of the ping-pong kernel
 template <class CFG>
 constexpr int pp_lds_bytes() {
@@ -930,7 +930,7 @@ gemm_kernel_pp(KernelArgs args) {
       }
   }
 
-  // the four waves of each group share a k-step's loads (see PP_SPLIT)
+  // the four waves of each group share a k-step's loads
   using Prod = Producer<CFG, RAGGED_K, 4>;
   constexpr int L = Prod::LA + Prod::LB;
   constexpr int NF = CFG::FM + CFG::FN;
@@ -941,8 +941,7 @@ gemm_kernel_pp(KernelArgs args) {
   WorkItem cw;
   bool cvalid = cursor_next(args.sp, ccur, cw);
 
-  // PP_SPLIT 0: group 0 issues every load; 1: group 0 the A loads, group 1 the B loads
-  constexpr int G0_HI = PP_SPLIT ? Prod::LA : L;  // group 0's loads [0, G0_HI), group 1's the rest
+  constexpr int G0_HI = Prod::LA;  // group 0 issues the A loads [0, LA), group 1 the B loads
   int issued = 0;  // k-steps whose loads this wave has issued
   auto issue = [&](int stage) {
     prod.begin(args, smem, stage);
@@ -957,7 +956,7 @@ gemm_kernel_pp(KernelArgs args) {
     }
     prod.end(args);
   };
-  if (group == 0 || PP_SPLIT) {
+  {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       if (prod.valid) {
@@ -990,8 +989,8 @@ gemm_kernel_pp(KernelArgs args) {
     for (int k = cw.kb; k < cw.ke; ++k, ++c) {
       // ---- M(c): every fragment of step c; group 0 also loads step c+1 when its stage is free
       const int stage = c & 1;
-      // group 1 (split loads): its loads of step c+1 first, to give them the whole phase
-      if (PP_SPLIT && group == 1 && prod.valid && issued == c + 1) {
+      // group 1: its loads of step c+1 first, to give them the whole phase
+      if (group == 1 && prod.valid && issued == c + 1) {
         issue((c + 1) & 1);
         ++issued;
       }
@@ -1006,7 +1005,7 @@ gemm_kernel_pp(KernelArgs args) {
         ++issued;
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      if (PP_SPLIT && group == 1) wait_vmcnt<0>();  // its loads of step c+1 have landed
+      if (group == 1) wait_vmcnt<0>();  // its loads of step c+1 have landed
       lds_barrier();
       // ---- C(c): the k-step's MFMAs, nothing else
 #pragma unroll
@@ -1047,9 +1046,6 @@ gemm_kernel_pp(KernelArgs args) {
 //  * FULL(c+1): the handshake of step c+1 (in step c's last sub-step) waits for the wave's own LDS
 //    writes (lgkmcnt(0)) and then the barrier, after which everyone reads step c+1.
 // The writes of step c+1 sit in the slots before that handshake.
-#ifndef VS_NBUF
-#define VS_NBUF 1  // staging register sets of the register-staged kernel (1 or 2)
-#endif
 template <class CFG, bool RAGGED_K>
 struct Stager {
   static constexpr int NW = CFG::WAVES;
@@ -1066,7 +1062,7 @@ struct Stager {
   uint32_t row0;      // tile row of the lane in load 0
   uint32_t lds0;      // lane LDS offset of load 0 within an operand: the row's swizzled chunk
   uint32_t chunk16;
-  u32x4 buf[VS_NBUF][L];  // staging registers; k-step c uses set c mod VS_NBUF
+  u32x4 buf[L];  // staging registers
 
   __device__ __forceinline__ void init(const KernelArgs &args, int32_t b, int wave, int lane) {
     row0 = (uint32_t)(wave * CFG::RPL + lane / CFG::CH);
@@ -1077,6 +1073,7 @@ struct Stager {
     lds0 = row0 * CFG::ROWB + ((chunk ^ ((row0 >> CFG::SWZ) & (CFG::CH - 1))) * 16);
     sta = (int32_t)(NW * CFG::RPL * args.lda_bytes);
     stb = (int32_t)(NW * CFG::RPL * args.ldb_bytes);
+    ra = rb = make_rsrc(args.A, 0);  // empty until an item sets them
     cursor_init(args.sp, b, cur);
     next_item(args);
   }
@@ -1111,26 +1108,25 @@ struct Stager {
     }
     if (!valid) koa = kob = kOOB;
   }
-  template <int J, int SET>
+  template <int J>
   __device__ __forceinline__ void load() {
     constexpr bool IS_A = J < LA;
     constexpr int j = IS_A ? J : J - LA;
     uint32_t off = IS_A ? koa : kob;
     if (edge && row0 + j * NW * CFG::RPL >= (uint32_t)(IS_A ? rows_a : rows_b)) off = kOOB;
-    buf[SET][J] =
-        __builtin_amdgcn_raw_buffer_load_b128(IS_A ? ra : rb, off, j * (IS_A ? sta : stb), 0);
+    buf[J] = __builtin_amdgcn_raw_buffer_load_b128(IS_A ? ra : rb, off, j * (IS_A ? sta : stb), 0);
   }
   __device__ __forceinline__ void end(const KernelArgs &args) {
     if (++k == ke) next_item(args);
   }
-  // LDS write of buf[SET][J] into `stage`
-  template <int J, int SET>
+  // LDS write of buf[J] into `stage`
+  template <int J>
   __device__ __forceinline__ void store(lds_t *smem, int stage) const {
     typedef u32x4 __attribute__((address_space(3))) *p128;
     constexpr bool IS_A = J < LA;
     constexpr int j = IS_A ? J : J - LA;
     *(p128)(smem + stage * CFG::STAGE_BYTES + (IS_A ? 0 : CFG::A_BYTES) + lds0 +
-            j * NW * CFG::RPL * CFG::ROWB) = buf[SET][J];
+            j * NW * CFG::RPL * CFG::ROWB) = buf[J];
   }
 };
 
@@ -1183,10 +1179,9 @@ gemm_kernel_vs(KernelArgs args) {
 
   // k-steps whose loads are issued / written to LDS so far
   int loaded = 0, written = 0;
-  auto load_step = [&](auto set_c) {
-    constexpr int SET = decltype(set_c)::value;
+  auto load_step = [&]() {
     st.begin(args);
-    [&]<int... J>(std::integer_sequence<int, J...>) { (st.template load<J, SET>(), ...); }(
+    [&]<int... J>(std::integer_sequence<int, J...>) { (st.template load<J>(), ...); }(
         std::make_integer_sequence<int, L>());
     if (st.valid) {
       st.end(args);
@@ -1195,11 +1190,11 @@ gemm_kernel_vs(KernelArgs args) {
   };
   // Prologue: step 0 into stage 0, loads of step 1 in flight (zeros past the last k-step).
   const bool any = st.valid;
-  load_step(std::integral_constant<int, 0>());
-  [&]<int... J>(std::integer_sequence<int, J...>) { (st.template store<J, 0>(smem, 0), ...); }(
+  load_step();
+  [&]<int... J>(std::integer_sequence<int, J...>) { (st.template store<J>(smem, 0), ...); }(
       std::make_integer_sequence<int, L>());
   if (any) ++written;
-  load_step(std::integral_constant<int, 1 % VS_NBUF>());
+  load_step();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   lds_barrier();
 
@@ -1212,12 +1207,8 @@ gemm_kernel_vs(KernelArgs args) {
 
   int c = 0;
   bool pairs = false;  // does this k-step write step c+1 (and load step c+2)?
-  // PAR = c mod VS_NBUF: step c+1 sits in staging set (PAR+1) mod VS_NBUF, step c+2 goes to
-  // set PAR (with one set both are the same registers, taken one load at a time)
-  auto substep = [&](auto s_c, auto par_c, auto acc_ref) {
+  auto substep = [&](auto s_c, auto acc_ref) {
     constexpr int S = decltype(s_c)::value;
-    constexpr int PAR = decltype(par_c)::value;
-    constexpr int WSET = (PAR + 1) % VS_NBUF, LSET = PAR;
     constexpr int CUR = S & 1, NXT = (S + 1) & 1;
     constexpr bool LAST = S == CFG::KSUB - 1;
     auto &acc = *acc_ref;
@@ -1240,9 +1231,9 @@ gemm_kernel_vs(KernelArgs args) {
                 (
                     [&] {
                       constexpr int j = lo + J;
-                      st.template store<j, WSET>(smem, (c + 1) & 1);
+                      st.template store<j>(smem, (c + 1) & 1);
                       if constexpr (j == 0) st.begin(args);
-                      st.template load<j, LSET>();
+                      st.template load<j>();
                       if constexpr (j == L - 1) {
                         if (pairs) ++written;
                         if (st.valid) {
@@ -1307,15 +1298,9 @@ gemm_kernel_vs(KernelArgs args) {
       // if no epilogue needs that stage: the staged epilogue uses stage c mod 2, step c+1 goes
       // to the other one, so writing is always allowed
       pairs = loaded > c + 1;
-      auto kstep = [&](auto par_c) {
-        [&]<int... S>(std::integer_sequence<int, S...>) {
-          (substep(std::integral_constant<int, S>(), par_c, &acc), ...);
-        }(std::make_integer_sequence<int, CFG::KSUB>());
-      };
-      if (VS_NBUF == 2 && (c & 1))
-        kstep(std::integral_constant<int, 1 % VS_NBUF>());
-      else
-        kstep(std::integral_constant<int, 0>());
+      [&]<int... S>(std::integer_sequence<int, S...>) {
+        (substep(std::integral_constant<int, S>(), &acc), ...);
+      }(std::make_integer_sequence<int, CFG::KSUB>());
     }
 
     if (args.out_bf16) {

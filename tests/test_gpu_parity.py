@@ -255,3 +255,55 @@ def test_empty_and_zero_depth(dev, M, N, K):
                            (L.GEMM_SCHED_STATIC, 0)):
         C, plan, _ = run_gpu(op, torch, dev, "f32", sched=sched, workers=workers, tile=128)
         assert np.array_equal(C, np.zeros((M, N)))
+
+
+@pytest.mark.parametrize("dt,out", [("bf16", "f32"), ("bf16", "bf16"), ("e4m3", "bf16"),
+                                    ("e4m3", "f32")])
+def test_data_parallel_kernels_bit_identical(dev, dt, out):
+    """Every data-parallel kernel sums each output over the k-tiles in the same order with the
+    same MFMA instruction, so the cooperative (128 and 256 tiles), ping-pong and register-staged
+    kernels must agree bit for bit -- across tile shapes, ragged M/N/K and several items per
+    worker -- and with the oracle within tolerance."""
+    M, N, K = 776, 520, 1000 if dt == "bf16" else 1040
+    dist = ("normal", 1.0) if dt == "e4m3" else ("uniform",)
+    op = gi.make_operands(M, N, K, dt, dist, dist, seed=4242)
+    runs = {}
+    for name, tile, flags in (("coop128", 128, L.GEMM_FLAG_COOPERATIVE),
+                              ("coop256", 256, L.GEMM_FLAG_COOPERATIVE),
+                              ("pingpong", 256, L.GEMM_FLAG_PINGPONG),
+                              ("regstaged", 256, L.GEMM_FLAG_REGSTAGED)):
+        C, plan, _ = run_gpu(op, torch, dev, out, L.GEMM_MAP_GROUPED_M, 2,
+                             L.GEMM_SCHED_PERSISTENT, 3, tile, flags=flags)
+        runs[name] = C
+    assert_within_tolerance(runs["pingpong"], reference(op), op, "dp kernels")
+    for name, C in runs.items():
+        assert np.array_equal(C, runs["pingpong"]), f"{name} differs from the ping-pong kernel"
+
+
+@pytest.mark.parametrize("M,N,K", [(776, 520, 1000), (300, 264, 104), (1, 8, 64), (520, 776, 200)])
+def test_no_writes_past_c(dev, M, N, K):
+    """C is the front of a larger buffer whose tail holds a canary pattern: after every kernel
+    and output type (edge tiles whose waves lie wholly past M or N included) the canary is
+    untouched, and C matches the oracle."""
+    op = gi.make_operands(M, N, K, "bf16", ("uniform",), ("uniform",), seed=M + N + K)
+    ref = reference(op)
+    A, B, sa, sb = to_device(op, torch, dev)
+    for out in ("bf16", "f32"):
+        eb = 2 if out == "bf16" else 4
+        canary_bytes = 4 << 20
+        buf = torch.empty(M * N * eb + canary_bytes, dtype=torch.uint8, device=dev)
+        for tile, flags in ((128, L.GEMM_FLAG_COOPERATIVE), (256, L.GEMM_FLAG_COOPERATIVE),
+                            (256, L.GEMM_FLAG_PINGPONG), (256, L.GEMM_FLAG_REGSTAGED)):
+            buf.fill_(0xA5)
+            plan = L.Plan(L.make_desc(M, N, K, L.GEMM_BF16,
+                                      L.GEMM_BF16 if out == "bf16" else L.GEMM_F32,
+                                      L.GEMM_MAP_GROUPED_M, 2, L.GEMM_SCHED_PERSISTENT, 2,
+                                      tile, tile, 0, flags))
+            st = plan.run_raw(A.data_ptr(), B.data_ptr(), buf.data_ptr())
+            assert st == L.GEMM_OK
+            torch.cuda.synchronize()
+            tail = buf[M * N * eb:]
+            assert bool((tail == 0xA5).all()), f"tile {tile} flags {flags:#x} {out}: wrote past C"
+            C = buf[:M * N * eb].view(torch.bfloat16 if out == "bf16" else torch.float32)
+            got = C.float().cpu().numpy().astype(np.float64).reshape(M, N)
+            assert_within_tolerance(got, ref, op, f"canary {M}x{N}x{K} {out} {flags:#x}")
