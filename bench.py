@@ -127,8 +127,8 @@ def measured_traffic(workload):
 
 
 # name, workload key, mapping, group, sched, tile, out, workers[, bk[, variant]]
-# variant: "chain" = Stream-K lock-chain fixup; "coop" / "vs" = the cooperative / register-staged
-# kernel instead of the default for data-parallel 256 x 256 tiles
+# variant: "chain" = Stream-K lock-chain fixup; "coop" / "vs" / "wide" = the cooperative /
+# register-staged / wide-wave kernel instead of the default for data-parallel 256 x 256 tiles
 RUNS = {
     "bf16_4096": ("bf16_4096", "grouped_m", 8, "persistent", 0, "bf16", 0),
     "bf16_4096_coop": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "coop"),
@@ -138,6 +138,9 @@ RUNS = {
     "fp8_8192_coop": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "coop"),
     "bf16_4096_vs": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "vs"),
     "fp8_8192_vs": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "vs"),
+    "bf16_4096_wide": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "wide"),
+    "fp8_8192_wide": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "wide"),
+    "bf16_mlp_up_wide": ("bf16_mlp_up", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "wide"),
     "bf16_mlp_up": ("bf16_mlp_up", "grouped_m", 8, "persistent", 0, "bf16", 0),
     "bf16_streamk": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256),
     "bf16_streamk_chain": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256, 0,
@@ -150,7 +153,8 @@ def run_flags(name, dg):
     """GEMM_FLAG_* bits of a RUNS entry's variant."""
     variant = RUNS[name][8] if len(RUNS[name]) > 8 else ""
     return {"": 0, "chain": dg.GEMM_FLAG_STREAMK_CHAIN, "pp": dg.GEMM_FLAG_PINGPONG,
-            "coop": dg.GEMM_FLAG_COOPERATIVE, "vs": dg.GEMM_FLAG_REGSTAGED}[variant]
+            "coop": dg.GEMM_FLAG_COOPERATIVE, "vs": dg.GEMM_FLAG_REGSTAGED,
+            "wide": dg.GEMM_FLAG_WIDE}[variant]
 
 
 def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
@@ -210,7 +214,7 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
     res = {
         "workload": wl_name, "M": op.M, "N": op.N, "K": op.K, "dtype": op.dtype, "out": out,
         "tile": [info.bm, info.bn, info.bk], "stages": info.stages, "mapping": mapping,
-        "kernel": ["cooperative", "ping-pong", "register-staged"][info.kernel],
+        "kernel": ["cooperative", "ping-pong", "register-staged", "wide-wave"][info.kernel],
         "group": group, "sched": sched, "grid": info.grid,
         "dp_tiles": info.dp_tiles, "sk_tiles": info.sk_tiles, "warmup_launches": n_warm,
         "ms_per_step": wall * 1e3 / steps, "kernel_us": dev_ms * 1e3,

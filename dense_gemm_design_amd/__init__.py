@@ -9,7 +9,7 @@ from ._lib import (GemmDesc, GemmError, Plan, make_desc, load,  # noqa: F401
                    GEMM_MAP_GROUPED_M, GEMM_MAP_GROUPED_N, GEMM_SCHED_STATIC,
                    GEMM_SCHED_PERSISTENT, GEMM_SCHED_STREAMK, GEMM_SCHED_AUTO, GEMM_FLAG_TRACE,
                    GEMM_FLAG_NO_XCD_REMAP, GEMM_FLAG_STREAMK_CHAIN, GEMM_FLAG_PINGPONG,
-                   GEMM_FLAG_COOPERATIVE, GEMM_FLAG_REGSTAGED)
+                   GEMM_FLAG_COOPERATIVE, GEMM_FLAG_REGSTAGED, GEMM_FLAG_WIDE)
 
 MAPPINGS = {"linear_n": GEMM_MAP_LINEAR_N, "linear_m": GEMM_MAP_LINEAR_M,
             "grouped_m": GEMM_MAP_GROUPED_M, "grouped_n": GEMM_MAP_GROUPED_N}

@@ -24,6 +24,7 @@ GEMM_FLAG_STREAMK_CHAIN = 0x4
 GEMM_FLAG_PINGPONG = 0x8
 GEMM_FLAG_COOPERATIVE = 0x10
 GEMM_FLAG_REGSTAGED = 0x20
+GEMM_FLAG_WIDE = 0x40
 GEMM_FLAG_TEST_SKIP_PUBLISH = 0x100
 GEMM_DEVICE_OK, GEMM_DEVICE_ERR_SPIN = 0, 1
 

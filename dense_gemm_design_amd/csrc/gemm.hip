@@ -32,6 +32,9 @@ using CfgBf16_256vs = TileCfg<DT_BF16, 256, 256, 64, 2, 2, 2, 1>;
 using CfgFp8_256vs = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1>;
 using CfgFp8_256 = TileCfg<DT_FP8, 256, 256, 128, 2, 4, 2, 1>;
 using CfgFp8_128 = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 2, 1>;
+// The wide-wave kernel (GEMM_FLAG_WIDE): four waves of 128 x 128, half-depth k-tiles, four stages.
+using CfgBf16_256w = TileCfg<DT_BF16, 256, 256, 32, 2, 2, 4, 2, 16>;  // 16 x 16 x 32 MFMAs
+using CfgFp8_256w = TileCfg<DT_FP8, 256, 256, 64, 2, 2, 4, 2>;
 
 typedef hipError_t (*launch_fn)(const KernelArgs &, int grid, bool ragged_k, hipStream_t);
 typedef const void *(*kernel_fn)();
@@ -73,9 +76,22 @@ const void *kernel_of_vs() {
   return (const void *)&gemm_kernel_vs<CFG, false>;
 }
 
-// kind: KIND_COOP runs every plan; KIND_PP and KIND_VS run data-parallel work only (no Stream-K
-// splits, K > 0)
-enum { KIND_COOP = 0, KIND_PP = 1, KIND_VS = 2 };
+template <class CFG>
+hipError_t launch_wide(const KernelArgs &a, int grid, bool ragged_k, hipStream_t s) {
+  if (ragged_k)
+    hipLaunchKernelGGL((gemm_kernel_wide<CFG, true>), dim3(grid), dim3(CFG::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel_wide<CFG, false>), dim3(grid), dim3(CFG::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+template <class CFG>
+const void *kernel_of_wide() {
+  return (const void *)&gemm_kernel_wide<CFG, false>;
+}
+
+// kind: KIND_COOP runs every plan; the others run data-parallel work only (no Stream-K splits,
+// K > 0)
+enum { KIND_COOP = 0, KIND_PP = 1, KIND_VS = 2, KIND_WIDE = 3, KIND_COUNT = 4 };
 struct KernelEntry {
   int dt, bm, bn, bk, threads, stages, lds, kind;
   launch_fn launch;
@@ -97,6 +113,11 @@ constexpr KernelEntry entry_vs() {
   return KernelEntry{CFG::DT, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::STAGES,
                      CFG::LDS_BYTES, KIND_VS, &launch_vs<CFG>, &kernel_of_vs<CFG>};
 }
+template <class CFG>
+constexpr KernelEntry entry_wide() {
+  return KernelEntry{CFG::DT, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::STAGES,
+                     wide_lds_bytes<CFG>(), KIND_WIDE, &launch_wide<CFG>, &kernel_of_wide<CFG>};
+}
 
 // The first entry that matches (dtype, bm, bn[, bk]) is the default for that tile shape.
 const KernelEntry kKernels[] = {
@@ -107,6 +128,8 @@ const KernelEntry kKernels[] = {
     entry_pp<CfgFp8_256pp>(),
     entry_vs<CfgBf16_256vs>(),
     entry_vs<CfgFp8_256vs>(),
+    entry_wide<CfgBf16_256w>(),
+    entry_wide<CfgFp8_256w>(),
     entry<CfgFp8_128>(),
 };
 
@@ -158,7 +181,8 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (grouped && d.group < 1) return GEMM_ERR_INVALID_ARG;
   if (d.sched < GEMM_SCHED_STATIC || d.sched > GEMM_SCHED_AUTO) return GEMM_ERR_INVALID_ARG;
   if (d.num_workers < 0 || d.bm < 0 || d.bn < 0 || d.bk < 0) return GEMM_ERR_INVALID_ARG;
-  const uint32_t kind_flags = GEMM_FLAG_PINGPONG | GEMM_FLAG_COOPERATIVE | GEMM_FLAG_REGSTAGED;
+  const uint32_t kind_flags =
+      GEMM_FLAG_PINGPONG | GEMM_FLAG_COOPERATIVE | GEMM_FLAG_REGSTAGED | GEMM_FLAG_WIDE;
   if (d.flags & ~(GEMM_FLAG_TRACE | GEMM_FLAG_NO_XCD_REMAP | GEMM_FLAG_STREAMK_CHAIN | kind_flags |
                   GEMM_FLAG_TEST_SKIP_PUBLISH))
     return GEMM_ERR_INVALID_ARG;
@@ -171,12 +195,14 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (d.N % 8 != 0) return GEMM_ERR_UNSUPPORTED;           // 16-byte output rows
   if (d.K * eb > (int64_t)1 << 30) return GEMM_ERR_UNSUPPORTED;
 
-  // the ping-pong and register-staged kernels run data-parallel work only, on 256 x 256 tiles
+  // the ping-pong, register-staged and wide-wave kernels run data-parallel work only, on
+  // 256 x 256 tiles
   const int force_kind = (d.flags & GEMM_FLAG_PINGPONG)      ? KIND_PP
                          : (d.flags & GEMM_FLAG_REGSTAGED)   ? KIND_VS
+                         : (d.flags & GEMM_FLAG_WIDE)        ? KIND_WIDE
                          : (d.flags & GEMM_FLAG_COOPERATIVE) ? KIND_COOP
                                                              : -1;
-  const bool force_dp = force_kind == KIND_PP || force_kind == KIND_VS;
+  const bool force_dp = force_kind == KIND_PP || force_kind == KIND_VS || force_kind == KIND_WIDE;
   if (force_dp && (d.K == 0 || d.sched == GEMM_SCHED_STREAMK || d.sched == GEMM_SCHED_AUTO))
     return GEMM_ERR_UNSUPPORTED;
 
@@ -190,7 +216,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     bm = bn = (bm ? bm : bn);
   }
   const int want_dt = d.dtype_ab == GEMM_BF16 ? DT_BF16 : DT_FP8;
-  const KernelEntry *by_kind[3] = {nullptr, nullptr, nullptr};
+  const KernelEntry *by_kind[KIND_COUNT] = {};
   for (const KernelEntry &e : kKernels)
     if (e.dt == want_dt && e.bm == bm && e.bn == bn && (d.bk == 0 || d.bk == e.bk) &&
         !by_kind[e.kind])
@@ -201,10 +227,9 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if ((int64_t)bm * d.K * eb >= 0x7FFFFFF0ll || (int64_t)bn * d.K * eb >= 0x7FFFFFF0ll)
     return GEMM_ERR_UNSUPPORTED;
 
-  const int64_t Mt = cdiv(d.M, bm), Nt = cdiv(d.N, bn), Kt = cdiv(d.K, k->bk);
+  const int64_t Mt = cdiv(d.M, bm), Nt = cdiv(d.N, bn);
   const int64_t tiles = Mt * Nt;
-  if (Mt > INT32_MAX || Nt > INT32_MAX || Kt > INT32_MAX || tiles > INT32_MAX)
-    return GEMM_ERR_UNSUPPORTED;
+  if (Mt > INT32_MAX || Nt > INT32_MAX || tiles > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
 
   int sched = d.sched;
   int workers = d.num_workers;
@@ -229,6 +254,8 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (force_kind < 0 && by_kind[KIND_PP] && d.K > 0 &&
       (sched == GEMM_SCHED_STATIC || sched == GEMM_SCHED_PERSISTENT))
     k = by_kind[KIND_PP];
+  const int64_t Kt = cdiv(d.K, k->bk);  // the kernel's own k-tile depth
+  if (Kt > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
 
   SchedParams sp;
   memset(&sp, 0, sizeof sp);

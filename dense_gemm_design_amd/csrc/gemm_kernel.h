@@ -81,16 +81,19 @@ struct KernelArgs {
   int32_t pad_;
 };
 
-template <int DT_, int BM_, int BN_, int BK_, int WGM_, int WGN_, int STAGES_, int SWZ_>
+template <int DT_, int BM_, int BN_, int BK_, int WGM_, int WGN_, int STAGES_, int SWZ_,
+          int MI_ = 32>
 struct TileCfg {
   static constexpr int DT = DT_, BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
   static constexpr int STAGES = STAGES_, SWZ = SWZ_;
+  // MFMA block edge: 32 (32 x 32 blocks, two k-groups of lanes) or 16 (16 x 16, four k-groups)
+  static constexpr int MI = MI_, KG = 64 / MI_;
   static constexpr int WAVES = WGM * WGN, THREADS = WAVES * 64;
   // waves of this workgroup per SIMD (4 SIMDs per CU); with two, each wave gets half the
   // register file and the other wave of the SIMD issues MFMAs while this one waits on LDS
   static constexpr int WAVES_PER_SIMD = (WAVES + 3) / 4;
   static constexpr int WM = BM / WGM, WN = BN / WGN;     // wave sub-tile
-  static constexpr int FM = WM / 32, FN = WN / 32;       // 32 x 32 MFMA blocks per wave
+  static constexpr int FM = WM / MI, FN = WN / MI;       // MI x MI MFMA blocks per wave
   static constexpr int EB = DT == DT_BF16 ? 2 : 1;       // bytes per element
   static constexpr int ROWB = BK * EB;                   // bytes of one tile row in LDS
   static constexpr int CH = ROWB / 16;                   // 16-byte chunks per row
@@ -100,15 +103,18 @@ struct TileCfg {
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int LA = A_BYTES / 1024 / WAVES;      // loads per wave per stage (A)
   static constexpr int LB = B_BYTES / 1024 / WAVES;
-  static constexpr int KMFMA = DT == DT_BF16 ? 16 : 64;  // reduction depth of one MFMA
+  // reduction depth of one MFMA: 32x32x16 / 16x16x32 bf16, 32x32x64 / 16x16x128 e4m3
+  static constexpr int KMFMA = (DT == DT_BF16 ? 16 : 64) * (MI == 16 ? 2 : 1);
   static constexpr int KSUB = BK / KMFMA;                // MFMAs along K per k-tile
-  static constexpr int CPL = KMFMA * EB / 32;            // 16-byte chunks per lane per operand
+  static constexpr int CPL = KMFMA * EB / (KG * 16);     // 16-byte chunks per lane per operand
   static_assert(ROWB == 64 || ROWB == 128, "tile rows must be 64 or 128 bytes");
   static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0, "load split");
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert(MI == 32 || MI == 16, "MFMA block edge");
+  static_assert(WM % MI == 0 && WN % MI == 0, "wave tile must be whole MFMA blocks");
+  static_assert(BK % KMFMA == 0, "k-tile must hold whole MFMAs");
   static_assert(LA + LB <= 63, "vmcnt range");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS per workgroup");
-  static_assert((32 >> SWZ) % CH == 0, "swizzle must not depend on the 32-row block");
+  static_assert((MI >> SWZ) % CH == 0, "swizzle must not depend on the MFMA row block");
 };
 
 // ---- small device helpers ------------------------------------------------------------------
@@ -199,6 +205,55 @@ __device__ __forceinline__ f32x16 mfma(const typename FragT<DT>::type &b,
     // operand formats 0 = e4m3 for both; zero scale operands select the unscaled instruction
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 0, 0, 0);
   }
+}
+
+// 16 x 16 blocks: lane l supplies row l % 16 of each operand, k-group l / 16 (8 bf16 or 32 e4m3),
+// and holds C[m = l % 16][n = 4 (l / 16) + r], r = 0..3, of the block (B passed first).  Per
+// MAC these move half the accumulator bytes of the 32 x 32 forms, which lowers the energy per
+// FLOP and so raises the clock the chip holds under its power limit.
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(const typename FragT<DT>::type &b,
+                                        const typename FragT<DT>::type &a, const f32x4 &c) {
+  if constexpr (DT == DT_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a, c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, 0, 0, 0, 0);
+  }
+}
+
+// The same 16 x 16 MFMAs accumulating in place in an accumulation register.  With 64 blocks of
+// accumulators per wave the compiler's register allocator, given the builtins above, keeps part
+// of them in VGPRs and copies them in and out of AGPRs around every MFMA; written out, the
+// instruction names its accumulator as both source and destination.  The compiler still sees
+// the operands (and waits for the LDS reads that produce A and B), but not the MFMA's latency:
+// callers leave wait states before reading an accumulator written here, and after writing one
+// with a VALU instruction before its first MFMA.
+template <int DT>
+__device__ __forceinline__ void mfma16_inplace(f32x4 &c, const typename FragT<DT>::type &b,
+                                               const typename FragT<DT>::type &a) {
+  if constexpr (DT == DT_BF16)
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+  else
+    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+}
+
+// Accumulator block of a configuration and the MFMA that updates it.
+template <class CFG>
+using acc_t = std::conditional_t<CFG::MI == 32, f32x16, f32x4>;
+
+template <class CFG>
+__device__ __forceinline__ void mfma_blk(acc_t<CFG> &c, const typename FragT<CFG::DT>::type &b,
+                                         const typename FragT<CFG::DT>::type &a) {
+  if constexpr (CFG::MI == 32)
+    c = mfma<CFG::DT>(b, a, c);
+  else
+    mfma16_inplace<CFG::DT>(c, b, a);
+}
+
+// Wait states between VALU writes of accumulators and an MFMA reading them, or between an MFMA
+// writing them and other instructions reading them, where the compiler cannot see the MFMA.
+__device__ __forceinline__ void mfma_wait_states() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
 // ---- the kernel ------------------------------------------------------------------------------
@@ -299,12 +354,12 @@ __device__ __forceinline__ void load_frag(const lds_t *smem, int stage, int s,
   const lds_t *base = smem + stage * CFG::STAGE_BYTES;
   constexpr int H = CFG::CPL - 1;
   if constexpr (E < CFG::FM) {
-    fr.a[E] = lds_frag<CFG::DT>(base + aoff[s][0] + E * 32 * CFG::ROWB,
-                                base + aoff[s][H] + E * 32 * CFG::ROWB);
+    fr.a[E] = lds_frag<CFG::DT>(base + aoff[s][0] + E * CFG::MI * CFG::ROWB,
+                                base + aoff[s][H] + E * CFG::MI * CFG::ROWB);
   } else {
     constexpr int G = E - CFG::FM;
-    fr.b[G] = lds_frag<CFG::DT>(base + boff[s][0] + G * 32 * CFG::ROWB,
-                                base + boff[s][H] + G * 32 * CFG::ROWB);
+    fr.b[G] = lds_frag<CFG::DT>(base + boff[s][0] + G * CFG::MI * CFG::ROWB,
+                                base + boff[s][H] + G * CFG::MI * CFG::ROWB);
   }
 }
 
@@ -398,8 +453,8 @@ __device__ __forceinline__ float agpr_read(float x) {
   return y;
 }
 
-template <bool AGPR>
-__device__ __forceinline__ f32x4 quad_of(const f32x16 &blk, int q) {
+template <bool AGPR, class BLK>
+__device__ __forceinline__ f32x4 quad_of(const BLK &blk, int q) {
   if constexpr (AGPR)
     return f32x4{agpr_read(blk[4 * q + 0]), agpr_read(blk[4 * q + 1]), agpr_read(blk[4 * q + 2]),
                  agpr_read(blk[4 * q + 3])};
@@ -617,6 +672,7 @@ gemm_kernel(KernelArgs args) {
   // An even number of MFMA sub-steps per k-tile keeps the two fragment buffers in fixed roles,
   // so a fragment load never targets registers an in-flight MFMA is still reading.
   static_assert(CFG::KSUB % 2 == 0, "k-tile must hold an even number of MFMA sub-steps");
+  static_assert(CFG::MI == 32, "32 x 32 MFMA blocks");
   __shared__ __attribute__((aligned(1024))) char smem_raw[CFG::LDS_BYTES];
   lds_t *smem = (lds_t *)(size_t)(uint32_t)(size_t)(lds_t *)smem_raw;
 
@@ -899,6 +955,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::TH
 gemm_kernel_pp(KernelArgs args) {
   static_assert(CFG::WAVES == 8 && CFG::WGM == 2 && CFG::WGN == 4, "two groups of four waves");
   static_assert(CFG::STAGES == 2, "ping-pong ring of two stages");
+  static_assert(CFG::MI == 32, "32 x 32 MFMA blocks");
   constexpr int EPI_SLICE = kPPSlice;
   static_assert(pp_lds_bytes<CFG>() <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) char smem_raw[pp_lds_bytes<CFG>()];
@@ -1135,6 +1192,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::TH
                                amdgpu_waves_per_eu(1, 1)))
 gemm_kernel_vs(KernelArgs args) {
   static_assert(CFG::WAVES == 4 && CFG::STAGES == 2, "four waves, two stages");
+  static_assert(CFG::MI == 32, "32 x 32 MFMA blocks");
   static_assert(CFG::KSUB % 2 == 0, "k-tile must hold an even number of MFMA sub-steps");
   __shared__ __attribute__((aligned(1024))) char smem_raw[CFG::LDS_BYTES];
   lds_t *smem = (lds_t *)(size_t)(uint32_t)(size_t)(lds_t *)smem_raw;
@@ -1317,6 +1375,381 @@ gemm_kernel_vs(KernelArgs args) {
       epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid);
     }
     ++seq;
+    cvalid = cursor_next(args.sp, ccur, cw);
+  }
+  wait_vmcnt<0>();
+}
+
+// ---- wide-wave kernel (data-parallel tiles) ---------------------------------------------------
+//
+// Four waves, one per SIMD, each owning a 128 x 128 sub-tile (4 x 4 MFMA blocks, accumulators in
+// the accumulation registers), fed by the direct global->LDS loads of gemm_kernel.  Per MFMA a
+// 128 x 128 sub-tile reads a third fewer fragment bytes from LDS than a 128 x 64 one, and with one
+// wave per SIMD the wave interleaves its own memory instructions between its MFMAs: about one
+// fragment read per two MFMAs and one load per four keep the matrix core fed.
+//
+// The k-tile is half as deep (32 bf16 / 64 e4m3: 64-byte LDS rows, 32 KiB per stage), which buys a
+// four-stage ring in 128 KiB: the loads of step c+3 are issued during step c and have two whole
+// k-steps to land before the handshake that needs them ("H100 Kernel Design" lesson, section 6:
+// the deeper the ring, the more load latency it hides).  Per k-step c:
+//  * handshake H(c+1) at slot HS of the last sub-step, as in gemm_kernel: FULL(c+1) by
+//    vmcnt(n) -- n counts the loads issued after step c+1's -- and EMPTY(c) by lgkmcnt(0), then
+//    s_barrier;  after it stage c mod S may take step c+S;
+//  * the producer loads of the step begun at the previous handshake are spread over the load
+//    window: every MFMA slot from the first sub-step up to HS of the last one, so all of them are
+//    out before the next handshake begins the following step;
+//  * fragment reads of the next sub-step between the MFMAs (of step c+1 after the handshake).
+// The epilogue stages each wave's sub-tile through its own 8 KiB LDS slice outside the ring, so
+// the ring keeps running across work items: the next tile's loads and first fragment reads are in
+// flight while the wave stores the current tile.  With one sub-step per k-tile (e4m3) the two
+// fragment buffers swap roles every k-step, so the k-loop is unrolled by two.
+constexpr int kWideSlice = 8192;  // 32 rows x 256 bytes of bf16
+
+template <class CFG>
+constexpr int wide_lds_bytes() {
+  return CFG::LDS_BYTES + CFG::WAVES * kWideSlice;
+}
+
+// bf16 output of a 128 x 128 sub-tile through the wave's LDS slice, 32 rows at a time.  Chunk c
+// (16 bytes) of staged row r sits at chunk position c ^ (r mod 16): the rows one write touches
+// and the 4 rows one read-back touches each spread over every bank.  16 lanes store one whole
+// 256-byte row segment.
+template <class CFG>
+__device__ __forceinline__ void epilogue_wide(const KernelArgs &args, const WorkItem &w,
+                                              const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
+                                              float alpha, int wm, int wn, int lane, lds_t *slice) {
+  typedef u32x2 __attribute__((address_space(3))) *p64;
+  typedef u32x4 __attribute__((address_space(3))) *p128;
+  static_assert(CFG::WN * 2 == 256 && CFG::WM == 128, "rows of the staged sub-tile are 256 bytes");
+  const int64_t m0 = (int64_t)w.m * CFG::BM + wm * CFG::WM;
+  const int64_t n0 = (int64_t)w.n * CFG::BN + wn * CFG::WN;
+  if (m0 >= args.M || n0 >= args.N) return;  // the wave's sub-tile lies past the edge of C
+  const int64_t origin = m0 * args.ldc + n0;
+  const __amdgpu_buffer_rsrc_t cr = make_rsrc(args.C + origin * 2, (args.M * args.ldc - origin) * 2);
+  const int chunk_l = lane & 15, rrow = lane >> 4;  // read-back: 4 rows per wave-wide read
+  const bool col_ok = n0 + chunk_l * 8 < args.N;
+  const uint32_t ldc_b = (uint32_t)args.ldc * 2;
+  const uint32_t st_off = (uint32_t)rrow * ldc_b + chunk_l * 16;
+  // read j covers rows rrow + 4j, whose swizzle is (rrow ^ 4 (j mod 4)): four lane bases
+  lds_t *rd_p[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) rd_p[jj] = slice + rrow * 256 + ((chunk_l ^ rrow ^ (4 * jj)) * 16);
+  auto read_back = [&](int round) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x4 v = *(p128)(rd_p[j & 3] + j * 1024);
+      if (col_ok)
+        __builtin_amdgcn_raw_buffer_store_b128(v, cr, st_off, (uint32_t)(round * 32 + j * 4) * ldc_b,
+                                               0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (CFG::MI == 32) {
+    // block (f, g): the lane holds row f*32 + lane%32, columns g*32 + 8q + 4(lane/32) + 0..3
+    const int wrow = lane & 31, x = wrow & 15;
+    lds_t *wr_row = slice + wrow * 256 + (lane >> 5) * 8;
+#pragma unroll
+    for (int f = 0; f < CFG::FM; ++f) {
+#pragma unroll
+      for (int g = 0; g < CFG::FN; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = quad_of<true>(acc[f][g], q) * alpha;
+          *(p64)(wr_row + (((g * 4 + q) ^ x) * 16)) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      read_back(f);
+    }
+  } else {
+    // block (f, g): the lane holds row f*16 + lane%16, columns g*16 + 4(lane/16) + 0..3, i.e.
+    // 16-byte chunk 2g + (lane/16)/2 of its row, half (lane/16) mod 2; two blocks per round
+    const int wrow = lane & 15, kq = lane >> 4;
+    lds_t *wr_row = slice + wrow * 256 + (kq & 1) * 8;
+#pragma unroll
+    for (int p = 0; p < CFG::FM / 2; ++p) {
+#pragma unroll
+      for (int fp = 0; fp < 2; ++fp)
+#pragma unroll
+        for (int g = 0; g < CFG::FN; ++g) {
+          const f32x4 v = quad_of<true>(acc[2 * p + fp][g], 0) * alpha;
+          *(p64)(wr_row + fp * 16 * 256 + (((2 * g + (kq >> 1)) ^ wrow) * 16)) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      read_back(p);
+    }
+  }
+}
+
+// fp32 output straight from the accumulation registers, one quad (16 bytes) per lane and store.
+template <class CFG>
+__device__ __forceinline__ void epilogue_direct(const KernelArgs &args, const WorkItem &w,
+                                                const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
+                                                float alpha, int wm, int wn, int lane) {
+  constexpr int MI = CFG::MI, NQ = MI == 32 ? 4 : 1;
+  const int64_t mbase = (int64_t)w.m * CFG::BM + wm * CFG::WM + (lane % MI);
+  const int64_t nbase = (int64_t)w.n * CFG::BN + wn * CFG::WN + (lane / MI) * 4;
+#pragma unroll
+  for (int f = 0; f < CFG::FM; ++f)
+#pragma unroll
+    for (int g = 0; g < CFG::FN; ++g)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        store_quad<CFG>(args, mbase + f * MI, nbase + g * MI + q * 8, quad_of<true>(acc[f][g], q),
+                        alpha);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+}
+
+template <class CFG, bool RAGGED_K>
+struct WideProducer {
+  static constexpr int NW = CFG::WAVES;
+  static constexpr int LA = CFG::A_BYTES / 1024 / NW, LB = CFG::B_BYTES / 1024 / NW;
+  static constexpr int L = LA + LB;
+  static_assert(CFG::A_BYTES % (1024 * NW) == 0 && CFG::B_BYTES % (1024 * NW) == 0, "load split");
+  static_assert((NW * CFG::RPL) % (CFG::CH << CFG::SWZ) == 0, "swizzle must repeat per load");
+  static_assert(L <= 63, "vmcnt range");
+  Cursor cur;
+  int32_t valid, k, ke;
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t vo[L];      // lane offsets of the item's loads
+  uint32_t row0;       // tile row of the lane in load 0
+  uint32_t chunk16;    // byte offset of the lane's swizzled chunk within a k-tile row
+  uint32_t kbytes;     // byte offset of the k-step within a row (soffset of every load)
+  uint32_t lds_wave;   // LDS address of the wave's first 1 KiB in the current stage
+  bool k_oob;          // ragged K: the lane's chunk lies past K in this k-step
+
+  __device__ __forceinline__ void init(const KernelArgs &args, int32_t b, int wave, int lane) {
+    row0 = (uint32_t)(wave * CFG::RPL + lane / CFG::CH);
+    chunk16 = (uint32_t)(((lane % CFG::CH) ^ ((row0 >> CFG::SWZ) & (CFG::CH - 1))) * 16);
+    ra = rb = make_rsrc(args.A, 0);  // empty until an item sets them
+    cursor_init(args.sp, b, cur);
+    next_item(args);
+  }
+
+  __device__ __forceinline__ void next_item(const KernelArgs &args) {
+    WorkItem w;
+    while ((valid = cursor_next(args.sp, cur, w)) && w.kb == w.ke) {
+    }
+    if (valid) {
+      k = w.kb;
+      ke = w.ke;
+      const int64_t m0 = (int64_t)w.m * CFG::BM, n0 = (int64_t)w.n * CFG::BN;
+      const int32_t rows_a = (int32_t)(args.M - m0 < CFG::BM ? args.M - m0 : CFG::BM);
+      const int32_t rows_b = (int32_t)(args.N - n0 < CFG::BN ? args.N - n0 : CFG::BN);
+      ra = make_rsrc(args.A + m0 * args.lda_bytes, (int64_t)rows_a * args.lda_bytes);
+      rb = make_rsrc(args.B + n0 * args.ldb_bytes, (int64_t)rows_b * args.ldb_bytes);
+#pragma unroll
+      for (int J = 0; J < L; ++J) {
+        const bool is_a = J < LA;
+        const uint32_t row = row0 + (uint32_t)((is_a ? J : J - LA) * NW * CFG::RPL);
+        const uint32_t ld = (uint32_t)(is_a ? args.lda_bytes : args.ldb_bytes);
+        vo[J] = row < (uint32_t)(is_a ? rows_a : rows_b) ? row * ld + chunk16 : kOOB;
+      }
+    } else {
+#pragma unroll
+      for (int J = 0; J < L; ++J) vo[J] = kOOB;
+    }
+  }
+
+  __device__ __forceinline__ void begin(const KernelArgs &args, uint32_t smem_base, int stage) {
+    kbytes = (uint32_t)k * CFG::ROWB;
+    lds_wave = smem_base + (uint32_t)stage * CFG::STAGE_BYTES;
+    if constexpr (RAGGED_K) k_oob = (int64_t)chunk16 + kbytes >= args.K * CFG::EB;
+  }
+
+  // load J (A loads first): 1 KiB of the k-step into LDS; kOOB + kbytes stays below 2^32
+  template <int J>
+  __device__ __forceinline__ void load() {
+    constexpr bool IS_A = J < LA;
+    constexpr int j = IS_A ? J : J - LA;
+    constexpr uint32_t dst_off = (IS_A ? 0 : CFG::A_BYTES) + j * NW * 1024;
+    uint32_t off = vo[J];
+    if constexpr (RAGGED_K) off = k_oob ? kOOB : off;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(IS_A ? ra : rb, (lds_t *)(size_t)(lds_wave + dst_off), 16,
+                                             off, kbytes, 0, 0);
+  }
+
+  __device__ __forceinline__ void end(const KernelArgs &args) {
+    if (valid && ++k == ke) next_item(args);
+  }
+};
+
+template <class CFG, bool RAGGED_K>
+__global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::THREADS),
+                               amdgpu_waves_per_eu(1, 1)))
+gemm_kernel_wide(KernelArgs args) {
+  static_assert(CFG::WAVES == 4 && CFG::WGM == 2 && CFG::WGN == 2, "four waves, one per SIMD");
+  static_assert(CFG::STAGES >= 3 && (CFG::STAGES & (CFG::STAGES - 1)) == 0,
+                "a step's loads have at least one whole k-step to land; stage = c mod S by mask");
+  static_assert(wide_lds_bytes<CFG>() <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[wide_lds_bytes<CFG>()];
+  lds_t *smem = (lds_t *)(size_t)(uint32_t)(size_t)(lds_t *)smem_raw;
+  const uint32_t smem_base = (uint32_t)(size_t)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / CFG::WGN, wn = wave % CFG::WGN;
+  const int32_t b = blockIdx.x;
+  lds_t *slice = smem + CFG::LDS_BYTES + wave * kWideSlice;
+
+  float alpha = 1.0f;
+  if constexpr (CFG::DT == DT_FP8) alpha = (*args.scale_a) * (*args.scale_b);
+
+  uint32_t aoff[CFG::KSUB][CFG::CPL], boff[CFG::KSUB][CFG::CPL];
+  {
+    const int r = lane % CFG::MI;  // fragment row; lane / MI is the lane's k-group
+    const int swz = (r >> CFG::SWZ) & (CFG::CH - 1);
+#pragma unroll
+    for (int s = 0; s < CFG::KSUB; ++s)
+#pragma unroll
+      for (int h = 0; h < CFG::CPL; ++h) {
+        const int chunk = (s * CFG::KG + lane / CFG::MI) * CFG::CPL + h;
+        const uint32_t in_row = (uint32_t)((chunk ^ swz) * 16);
+        aoff[s][h] = (uint32_t)((wm * CFG::WM + r) * CFG::ROWB) + in_row;
+        boff[s][h] = (uint32_t)(CFG::A_BYTES + (wn * CFG::WN + r) * CFG::ROWB) + in_row;
+      }
+  }
+
+  using Prod = WideProducer<CFG, RAGGED_K>;
+  Prod prod;
+  prod.init(args, b, wave, lane);
+  const uint32_t lds_wave0 = smem_base + (uint32_t)wave * 1024;
+  Cursor ccur;
+  cursor_init(args.sp, b, ccur);
+  WorkItem cw;
+  bool cvalid = cursor_next(args.sp, ccur, cw);
+
+  constexpr int L = Prod::L;              // loads per wave per k-step
+  constexpr int NM = CFG::FM * CFG::FN;   // MFMAs per sub-step
+  constexpr int NF = CFG::FM + CFG::FN;   // fragments per sub-step
+  constexpr int HS = CFG::KSUB == 1 ? NM / 2 : NM / 4;  // handshake slot in the last sub-step
+  constexpr int W = (CFG::KSUB - 1) * NM + HS;          // load window of a k-step, in MFMA slots
+  static_assert(W >= L / 2, "load window");
+
+  if (!cvalid) return;  // no work (the whole workgroup alike)
+
+  // Ring position: the loads of step c+S-1 go out in k-step c, those of steps 0..S-2 in the
+  // prologue; handshake H(c) then waits for the loads of step c, followed by those of (S-2) later
+  // steps, so vmcnt((S-2) L) -- loads of the exhausted producer included, they count alike.
+#pragma unroll
+  for (int s = 0; s < CFG::STAGES - 1; ++s) {
+    prod.begin(args, lds_wave0, s);
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      (prod.template load<J>(), ...);
+    }(std::make_integer_sequence<int, L>());
+    prod.end(args);
+  }
+
+  Frags<CFG> fr[2];
+  int c = 0;
+  auto handshake = [&](int step) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // own reads of step-1 are complete
+    wait_vmcnt<((CFG::STAGES - 2) * L > 63 ? 63 : (CFG::STAGES - 2) * L)>();
+    lds_barrier();
+    prod.begin(args, lds_wave0, (step + CFG::STAGES - 1) & (CFG::STAGES - 1));
+  };
+  handshake(0);
+  [&]<int... E>(std::integer_sequence<int, E...>) {
+    (load_frag<CFG, frag_order<CFG>(E)>(smem, 0, 0, aoff, boff, fr[0]), ...);
+  }(std::make_integer_sequence<int, NF>());
+
+  // Sub-step S of k-step c on fragment buffer CUR: NM MFMAs; after MFMA i, in this order, the
+  // window's loads for slot S*NM + i, the handshake (last sub-step, slot HS) and the fragment
+  // reads of the next sub-step or of step c+1.  None of it is conditional: after the worker's
+  // last k-step the handshake and the reads still run (every wave alike, so the barriers match),
+  // reading a stage nobody uses any more.
+  auto substep = [&](auto s_c, auto cur_c, auto acc_ref) {
+    constexpr int S = decltype(s_c)::value;
+    constexpr int CUR = decltype(cur_c)::value, NXT = CUR ^ 1;
+    constexpr bool LAST = S == CFG::KSUB - 1;
+    auto &acc = *acc_ref;
+    const int stage = c & (CFG::STAGES - 1);
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (
+          [&] {
+            constexpr int i = I;
+            constexpr int f = i / CFG::FN, g = i % CFG::FN;
+            mfma_blk<CFG>(acc[f][g], fr[CUR].b[g], fr[CUR].a[f]);
+            constexpr int wslot = S * NM + i;
+            if constexpr (wslot < W) {
+              constexpr int plo = ops_before(wslot, L, 0, W);
+              constexpr int phi = ops_before(wslot + 1, L, 0, W);
+              [&]<int... J>(std::integer_sequence<int, J...>) {
+                (prod.template load<plo + J>(), ...);
+              }(std::make_integer_sequence<int, phi - plo>());
+              if constexpr (phi == L && plo < L) prod.end(args);
+            }
+            if constexpr (!LAST) {
+              constexpr int lo = ops_before(i, NF, 0, NM);
+              constexpr int hi = ops_before(i + 1, NF, 0, NM);
+              [&]<int... E>(std::integer_sequence<int, E...>) {
+                (load_frag<CFG, frag_order<CFG>(lo + E)>(smem, stage, S + 1, aoff, boff, fr[NXT]), ...);
+              }(std::make_integer_sequence<int, hi - lo>());
+            } else {
+              if constexpr (i + 1 == HS) handshake(c + 1);
+              constexpr int lo = ops_before(i, NF, HS, NM);
+              constexpr int hi = ops_before(i + 1, NF, HS, NM);
+              [&]<int... E>(std::integer_sequence<int, E...>) {
+                (load_frag<CFG, frag_order<CFG>(lo + E)>(smem, (c + 1) & (CFG::STAGES - 1), 0, aoff,
+                                                         boff, fr[NXT]),
+                 ...);
+              }(std::make_integer_sequence<int, hi - lo>());
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }(),
+          ...);
+    }(std::make_integer_sequence<int, NM>());
+  };
+  // one k-step whose first sub-step reads fragment buffer P
+  auto kstep = [&](auto p_c, auto acc_ref) {
+    constexpr int P = decltype(p_c)::value;
+    [&]<int... S>(std::integer_sequence<int, S...>) {
+      (substep(std::integral_constant<int, S>(), std::integral_constant<int, (P + S) & 1>(),
+               acc_ref),
+       ...);
+    }(std::make_integer_sequence<int, CFG::KSUB>());
+    ++c;
+  };
+
+  int seq = 0;
+  while (cvalid) {
+    if ((args.flags & KF_TRACE) && tid == 0 && seq < args.trace_cap) {
+      int *t = args.trace + ((int64_t)b * args.trace_cap + seq) * 8;
+      t[0] = b; t[1] = seq; t[2] = cw.tile; t[3] = cw.m;
+      t[4] = cw.n; t[5] = cw.kb; t[6] = cw.ke; t[7] = cw.role;
+    }
+    ++seq;
+    acc_t<CFG> acc[CFG::FM][CFG::FN];
+#pragma unroll
+    for (int f = 0; f < CFG::FM; ++f)
+#pragma unroll
+      for (int g = 0; g < CFG::FN; ++g) acc[f][g] = acc_t<CFG>{};
+    if constexpr (CFG::MI == 16) mfma_wait_states();  // zeroed accumulators reach the MFMAs
+
+    if constexpr (CFG::KSUB % 2 == 0) {
+      for (int k = cw.kb; k < cw.ke; ++k) kstep(std::integral_constant<int, 0>(), &acc);
+    } else {
+      // k-steps in pairs, so each item starts on buffer 0; after an odd last step the next
+      // item's first fragments sit in buffer 1 and move over (once per item)
+      int k = cw.kb;
+      for (; k + 2 <= cw.ke; k += 2) {
+        kstep(std::integral_constant<int, 0>(), &acc);
+        kstep(std::integral_constant<int, 1>(), &acc);
+      }
+      if (k < cw.ke) {
+        kstep(std::integral_constant<int, 0>(), &acc);
+        fr[0] = fr[1];
+      }
+    }
+
+    if constexpr (CFG::MI == 16) mfma_wait_states();  // the last MFMAs' results are written
+    if (args.out_bf16)
+      epilogue_wide<CFG>(args, cw, acc, alpha, wm, wn, lane, slice);
+    else
+      epilogue_direct<CFG>(args, cw, acc, alpha, wm, wn, lane);
     cvalid = cursor_next(args.sp, ccur, cw);
   }
   wait_vmcnt<0>();

@@ -79,7 +79,11 @@ typedef enum {
 #define GEMM_FLAG_REGSTAGED 0x20u    /* require the register-staged kernel: four waves with 128 x
                                         128 sub-tiles, operands staged global -> registers ->
                                         LDS.  Same limits as GEMM_FLAG_PINGPONG.  At most one of
-                                        the three kernel flags (else GEMM_ERR_INVALID_ARG)      */
+                                        the kernel flags (else GEMM_ERR_INVALID_ARG)            */
+#define GEMM_FLAG_WIDE 0x40u         /* require the wide-wave kernel: four waves with 128 x 128
+                                        sub-tiles fed by direct global -> LDS loads through a
+                                        four-stage ring of half-depth k-tiles (bk 32 bf16 / 64
+                                        e4m3).  Same limits as GEMM_FLAG_PINGPONG              */
 #define GEMM_FLAG_TEST_SKIP_PUBLISH 0x100u /* test only: the first Stream-K split of band tile 0
                                               does not publish its lock / arrival, so the bounded
                                               waits on it expire and report GEMM_DEVICE_ERR_SPIN */
@@ -124,7 +128,7 @@ typedef struct gemm_plan_info {
   int32_t trace_capacity;    /* records per workgroup                                            */
   int32_t error_offset;      /* byte offset of the device error word in the workspace (-1: none)*/
   int32_t streamk_mode;      /* 0 lock chain, 1 separate reduction (meaningful when sk_tiles>0)  */
-  int32_t kernel;            /* 0 cooperative, 1 ping-pong, 2 register-staged kernel             */
+  int32_t kernel;            /* 0 cooperative, 1 ping-pong, 2 register-staged, 3 wide-wave       */
 } gemm_plan_info;
 
 /* device error word values (read back from the workspace after a run) */

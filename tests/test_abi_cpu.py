@@ -82,7 +82,7 @@ def create(**kw):
     (dict(mapping=L.GEMM_MAP_GROUPED_M, group=0), L.GEMM_ERR_INVALID_ARG),
     (dict(sched=9), L.GEMM_ERR_INVALID_ARG),
     (dict(num_workers=-1), L.GEMM_ERR_INVALID_ARG),
-    (dict(flags=0x40), L.GEMM_ERR_INVALID_ARG),
+    (dict(flags=0x80), L.GEMM_ERR_INVALID_ARG),
     (dict(layout_a=3), L.GEMM_ERR_INVALID_ARG),
     (dict(layout_a=L.GEMM_COL_MAJOR), L.GEMM_ERR_UNSUPPORTED),
     (dict(layout_b=L.GEMM_ROW_MAJOR), L.GEMM_ERR_UNSUPPORTED),
@@ -108,6 +108,12 @@ def create(**kw):
     (dict(flags=L.GEMM_FLAG_REGSTAGED, dtype_ab=L.GEMM_FP8_E4M3, K=400, M=300), L.GEMM_OK),
     (dict(flags=L.GEMM_FLAG_REGSTAGED, sched=L.GEMM_SCHED_STREAMK), L.GEMM_ERR_UNSUPPORTED),
     (dict(flags=L.GEMM_FLAG_REGSTAGED, K=0), L.GEMM_ERR_UNSUPPORTED),
+    (dict(flags=L.GEMM_FLAG_WIDE), L.GEMM_OK),
+    (dict(flags=L.GEMM_FLAG_WIDE, dtype_ab=L.GEMM_FP8_E4M3, K=400, M=300), L.GEMM_OK),
+    (dict(flags=L.GEMM_FLAG_WIDE, bk=64), L.GEMM_ERR_UNSUPPORTED),  # its bf16 k-tile is 32 deep
+    (dict(flags=L.GEMM_FLAG_WIDE, sched=L.GEMM_SCHED_STREAMK), L.GEMM_ERR_UNSUPPORTED),
+    (dict(flags=L.GEMM_FLAG_WIDE, K=0), L.GEMM_ERR_UNSUPPORTED),
+    (dict(flags=L.GEMM_FLAG_WIDE | L.GEMM_FLAG_COOPERATIVE), L.GEMM_ERR_INVALID_ARG),
 ])
 def test_create_validation(kw, want):
     assert create(**kw) == want
@@ -142,6 +148,13 @@ def test_plan_info_and_workspace():
     r = L.Plan(L.make_desc(4096, 4096, 4096, sched=L.GEMM_SCHED_PERSISTENT, num_workers=256,
                            flags=L.GEMM_FLAG_COOPERATIVE))
     assert r.info.kernel == 0 and r.info.lds_bytes == 128 * 1024
+    w = L.Plan(L.make_desc(4096, 4096, 4096, sched=L.GEMM_SCHED_PERSISTENT, num_workers=256,
+                           flags=L.GEMM_FLAG_WIDE))
+    assert (w.info.kernel, w.info.threads, w.info.bk, w.info.kt) == (3, 256, 32, 128)
+    assert w.info.lds_bytes == 160 * 1024 and w.info.stages == 4
+    w8 = L.Plan(L.make_desc(8192, 8192, 8192, dtype_ab=L.GEMM_FP8_E4M3, num_workers=256,
+                            sched=L.GEMM_SCHED_PERSISTENT, flags=L.GEMM_FLAG_WIDE))
+    assert (w8.info.kernel, w8.info.bk, w8.info.kt) == (3, 64, 128)
     s = L.Plan(L.make_desc(256, 256, 256, sched=L.GEMM_SCHED_STATIC, bm=128, bn=128))
     assert s.info.grid == 4 and s.info.sched == L.GEMM_SCHED_STATIC
 

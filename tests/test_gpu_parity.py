@@ -116,14 +116,15 @@ PINGPONG = [
 
 # data-parallel kernels for 256 x 256 tiles: flag, plan_info.kernel, threads
 DP_KERNELS = {"pingpong": (L.GEMM_FLAG_PINGPONG, 1, 512),
-              "regstaged": (L.GEMM_FLAG_REGSTAGED, 2, 256)}
+              "regstaged": (L.GEMM_FLAG_REGSTAGED, 2, 256),
+              "wide": (L.GEMM_FLAG_WIDE, 3, 256)}
 
 
 @pytest.mark.parametrize("kern", list(DP_KERNELS))
 @pytest.mark.parametrize("case", PINGPONG, ids=[c[0] for c in PINGPONG])
 def test_pingpong_parity(dev, case, kern):
-    """The data-parallel kernels (ping-pong, register-staged): several items per worker, ragged
-    M/N/K, one k-step per item, fp32 and bf16 outputs."""
+    """The data-parallel kernels (ping-pong, register-staged, wide-wave): several items per
+    worker, ragged M/N/K, one k-step per item, fp32 and bf16 outputs."""
     name, M, N, K, dt, out, mapping, G, sched, workers = case
     flag, kind, threads = DP_KERNELS[kern]
     dist = ("normal", 1.0) if dt == "e4m3" else ("uniform",)
@@ -257,27 +258,40 @@ def test_empty_and_zero_depth(dev, M, N, K):
         assert np.array_equal(C, np.zeros((M, N)))
 
 
+# kernels whose MFMA is the 16 x 16 form (a different summation order inside each MFMA than the
+# 32 x 32 form the other kernels use), per operand type
+MFMA16 = {("wide", "bf16")}
+
+
 @pytest.mark.parametrize("dt,out", [("bf16", "f32"), ("bf16", "bf16"), ("e4m3", "bf16"),
                                     ("e4m3", "f32")])
 def test_data_parallel_kernels_bit_identical(dev, dt, out):
-    """Every data-parallel kernel sums each output over the k-tiles in the same order with the
-    same MFMA instruction, so the cooperative (128 and 256 tiles), ping-pong and register-staged
-    kernels must agree bit for bit -- across tile shapes, ragged M/N/K and several items per
-    worker -- and with the oracle within tolerance."""
+    """Every data-parallel kernel with the same MFMA shape sums each output over K in the same
+    order with the same instruction (k-tile depth only groups the MFMAs), so kernels of one
+    shape -- cooperative (128 and 256 tiles), ping-pong, register-staged, wide-wave -- must agree
+    bit for bit, across tile shapes, ragged M/N/K and several items per worker; every kernel is
+    within tolerance of the oracle."""
     M, N, K = 776, 520, 1000 if dt == "bf16" else 1040
     dist = ("normal", 1.0) if dt == "e4m3" else ("uniform",)
     op = gi.make_operands(M, N, K, dt, dist, dist, seed=4242)
+    ref = reference(op)
     runs = {}
     for name, tile, flags in (("coop128", 128, L.GEMM_FLAG_COOPERATIVE),
                               ("coop256", 256, L.GEMM_FLAG_COOPERATIVE),
                               ("pingpong", 256, L.GEMM_FLAG_PINGPONG),
-                              ("regstaged", 256, L.GEMM_FLAG_REGSTAGED)):
+                              ("regstaged", 256, L.GEMM_FLAG_REGSTAGED),
+                              ("wide", 256, L.GEMM_FLAG_WIDE)):
         C, plan, _ = run_gpu(op, torch, dev, out, L.GEMM_MAP_GROUPED_M, 2,
                              L.GEMM_SCHED_PERSISTENT, 3, tile, flags=flags)
+        assert_within_tolerance(C, ref, op, f"dp kernel {name}")
         runs[name] = C
-    assert_within_tolerance(runs["pingpong"], reference(op), op, "dp kernels")
+    families = {}
     for name, C in runs.items():
-        assert np.array_equal(C, runs["pingpong"]), f"{name} differs from the ping-pong kernel"
+        families.setdefault((name, dt) in MFMA16, []).append((name, C))
+    for members in families.values():
+        first, C0 = members[0]
+        for name, C in members[1:]:
+            assert np.array_equal(C, C0), f"{name} differs from {first} (same MFMA shape)"
 
 
 @pytest.mark.parametrize("M,N,K", [(776, 520, 1000), (300, 264, 104), (1, 8, 64), (520, 776, 200)])
@@ -293,7 +307,8 @@ def test_no_writes_past_c(dev, M, N, K):
         canary_bytes = 4 << 20
         buf = torch.empty(M * N * eb + canary_bytes, dtype=torch.uint8, device=dev)
         for tile, flags in ((128, L.GEMM_FLAG_COOPERATIVE), (256, L.GEMM_FLAG_COOPERATIVE),
-                            (256, L.GEMM_FLAG_PINGPONG), (256, L.GEMM_FLAG_REGSTAGED)):
+                            (256, L.GEMM_FLAG_PINGPONG), (256, L.GEMM_FLAG_REGSTAGED),
+                            (256, L.GEMM_FLAG_WIDE)):
             buf.fill_(0xA5)
             plan = L.Plan(L.make_desc(M, N, K, L.GEMM_BF16,
                                       L.GEMM_BF16 if out == "bf16" else L.GEMM_F32,
