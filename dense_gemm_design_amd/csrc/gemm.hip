@@ -32,9 +32,9 @@ using CfgBf16_256vs = TileCfg<DT_BF16, 256, 256, 64, 2, 2, 2, 1>;
 using CfgFp8_256vs = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1>;
 using CfgFp8_256 = TileCfg<DT_FP8, 256, 256, 128, 2, 4, 2, 1>;
 using CfgFp8_128 = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 2, 1>;
-// The wide-wave kernel (GEMM_FLAG_WIDE): four waves of 128 x 128, half-depth k-tiles, four stages.
-using CfgBf16_256w = TileCfg<DT_BF16, 256, 256, 32, 2, 2, 4, 2, 16>;  // 16 x 16 x 32 MFMAs
-using CfgFp8_256w = TileCfg<DT_FP8, 256, 256, 64, 2, 2, 4, 2>;
+// The wide-wave kernel (GEMM_FLAG_WIDE): four waves of 128 x 128, two stages.
+using CfgBf16_256w = TileCfg<DT_BF16, 256, 256, 64, 2, 2, 2, 1, 16>;  // 16 x 16 x 32 MFMAs
+using CfgFp8_256w = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1>;
 
 typedef hipError_t (*launch_fn)(const KernelArgs &, int grid, bool ragged_k, hipStream_t);
 typedef const void *(*kernel_fn)();

@@ -1388,17 +1388,16 @@ gemm_kernel_vs(KernelArgs args) {
 // wave per SIMD the wave interleaves its own memory instructions between its MFMAs: about one
 // fragment read per two MFMAs and one load per four keep the matrix core fed.
 //
-// The k-tile is half as deep (32 bf16 / 64 e4m3: 64-byte LDS rows, 32 KiB per stage), which buys a
-// four-stage ring in 128 KiB: the loads of step c+3 are issued during step c and have two whole
-// k-steps to land before the handshake that needs them ("H100 Kernel Design" lesson, section 6:
-// the deeper the ring, the more load latency it hides).  Per k-step c:
+// The k-tile keeps 128-byte rows in LDS (64 bf16 / 128 e4m3 deep), so each 1 KiB load covers 8
+// whole 128-byte lines; half-depth tiles with 64-byte rows measured twice the L2 requests for
+// the same bytes.  Two 64 KiB stages fill 128 KiB.  Per k-step c:
 //  * handshake H(c+1) at slot HS of the last sub-step, as in gemm_kernel: FULL(c+1) by
-//    vmcnt(n) -- n counts the loads issued after step c+1's -- and EMPTY(c) by lgkmcnt(0), then
-//    s_barrier;  after it stage c mod S may take step c+S;
-//  * the producer loads of the step begun at the previous handshake are spread over the load
-//    window: every MFMA slot from the first sub-step up to HS of the last one, so all of them are
-//    out before the next handshake begins the following step;
-//  * fragment reads of the next sub-step between the MFMAs (of step c+1 after the handshake).
+//    vmcnt(n) -- n counts the loads issued after step c+1's -- and EMPTY(c) by lgkmcnt(0) (step
+//    c's fragments are all in registers by then), then s_barrier;  after it stage c mod S may
+//    take step c+S;
+//  * right after the handshake, spread over the rest of that sub-step, the fragment reads of
+//    step c+1 and the loads of step c+S: those loads get a whole k-step, until H(c+2), to land;
+//  * in the other sub-steps, the fragment reads of the next sub-step between the MFMAs.
 // The epilogue stages each wave's sub-tile through its own 8 KiB LDS slice outside the ring, so
 // the ring keeps running across work items: the next tile's loads and first fragment reads are in
 // flight while the wave stores the current tile.  With one sub-step per k-tile (e4m3) the two
@@ -1581,8 +1580,8 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::TH
                                amdgpu_waves_per_eu(1, 1)))
 gemm_kernel_wide(KernelArgs args) {
   static_assert(CFG::WAVES == 4 && CFG::WGM == 2 && CFG::WGN == 2, "four waves, one per SIMD");
-  static_assert(CFG::STAGES >= 3 && (CFG::STAGES & (CFG::STAGES - 1)) == 0,
-                "a step's loads have at least one whole k-step to land; stage = c mod S by mask");
+  static_assert(CFG::STAGES >= 2 && (CFG::STAGES & (CFG::STAGES - 1)) == 0,
+                "stage = c mod S by mask");
   static_assert(wide_lds_bytes<CFG>() <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) char smem_raw[wide_lds_bytes<CFG>()];
   lds_t *smem = (lds_t *)(size_t)(uint32_t)(size_t)(lds_t *)smem_raw;
@@ -1626,21 +1625,22 @@ gemm_kernel_wide(KernelArgs args) {
   constexpr int NM = CFG::FM * CFG::FN;   // MFMAs per sub-step
   constexpr int NF = CFG::FM + CFG::FN;   // fragments per sub-step
   constexpr int HS = CFG::KSUB == 1 ? NM / 2 : NM / 4;  // handshake slot in the last sub-step
-  constexpr int W = (CFG::KSUB - 1) * NM + HS;          // load window of a k-step, in MFMA slots
-  static_assert(W >= L / 2, "load window");
 
   if (!cvalid) return;  // no work (the whole workgroup alike)
 
   // Ring position: the loads of step c+S-1 go out in k-step c, those of steps 0..S-2 in the
   // prologue; handshake H(c) then waits for the loads of step c, followed by those of (S-2) later
   // steps, so vmcnt((S-2) L) -- loads of the exhausted producer included, they count alike.
-#pragma unroll
-  for (int s = 0; s < CFG::STAGES - 1; ++s) {
-    prod.begin(args, lds_wave0, s);
+  auto load_all = [&] {
     [&]<int... J>(std::integer_sequence<int, J...>) {
       (prod.template load<J>(), ...);
     }(std::make_integer_sequence<int, L>());
     prod.end(args);
+  };
+#pragma unroll
+  for (int s = 0; s < CFG::STAGES - 1; ++s) {
+    prod.begin(args, lds_wave0, s);
+    load_all();
   }
 
   Frags<CFG> fr[2];
@@ -1652,15 +1652,18 @@ gemm_kernel_wide(KernelArgs args) {
     prod.begin(args, lds_wave0, (step + CFG::STAGES - 1) & (CFG::STAGES - 1));
   };
   handshake(0);
+  load_all();  // step S-1, begun by the handshake
   [&]<int... E>(std::integer_sequence<int, E...>) {
     (load_frag<CFG, frag_order<CFG>(E)>(smem, 0, 0, aoff, boff, fr[0]), ...);
   }(std::make_integer_sequence<int, NF>());
 
   // Sub-step S of k-step c on fragment buffer CUR: NM MFMAs; after MFMA i, in this order, the
-  // window's loads for slot S*NM + i, the handshake (last sub-step, slot HS) and the fragment
-  // reads of the next sub-step or of step c+1.  None of it is conditional: after the worker's
-  // last k-step the handshake and the reads still run (every wave alike, so the barriers match),
-  // reading a stage nobody uses any more.
+  // fragment reads of the next sub-step, or in the last sub-step the handshake H(c+1) (slot HS)
+  // followed by the fragment reads of step c+1 and the loads of step c+S, which H(c+1) began,
+  // both spread over the slots after it: the loads have a whole k-step to land before H(c+2)
+  // waits for them.  None of it is conditional: after the worker's last k-step the handshake,
+  // reads and loads still run (every wave alike, so the barriers match), on a stage nobody uses
+  // any more.
   auto substep = [&](auto s_c, auto cur_c, auto acc_ref) {
     constexpr int S = decltype(s_c)::value;
     constexpr int CUR = decltype(cur_c)::value, NXT = CUR ^ 1;
@@ -1673,15 +1676,6 @@ gemm_kernel_wide(KernelArgs args) {
             constexpr int i = I;
             constexpr int f = i / CFG::FN, g = i % CFG::FN;
             mfma_blk<CFG>(acc[f][g], fr[CUR].b[g], fr[CUR].a[f]);
-            constexpr int wslot = S * NM + i;
-            if constexpr (wslot < W) {
-              constexpr int plo = ops_before(wslot, L, 0, W);
-              constexpr int phi = ops_before(wslot + 1, L, 0, W);
-              [&]<int... J>(std::integer_sequence<int, J...>) {
-                (prod.template load<plo + J>(), ...);
-              }(std::make_integer_sequence<int, phi - plo>());
-              if constexpr (phi == L && plo < L) prod.end(args);
-            }
             if constexpr (!LAST) {
               constexpr int lo = ops_before(i, NF, 0, NM);
               constexpr int hi = ops_before(i + 1, NF, 0, NM);
@@ -1697,6 +1691,12 @@ gemm_kernel_wide(KernelArgs args) {
                                                          boff, fr[NXT]),
                  ...);
               }(std::make_integer_sequence<int, hi - lo>());
+              constexpr int plo = ops_before(i, L, HS, NM);
+              constexpr int phi = ops_before(i + 1, L, HS, NM);
+              [&]<int... J>(std::integer_sequence<int, J...>) {
+                (prod.template load<plo + J>(), ...);
+              }(std::make_integer_sequence<int, phi - plo>());
+              if constexpr (phi == L && plo < L) prod.end(args);
             }
             __builtin_amdgcn_sched_barrier(0);
           }(),

@@ -81,9 +81,8 @@ typedef enum {
                                         LDS.  Same limits as GEMM_FLAG_PINGPONG.  At most one of
                                         the kernel flags (else GEMM_ERR_INVALID_ARG)            */
 #define GEMM_FLAG_WIDE 0x40u         /* require the wide-wave kernel: four waves with 128 x 128
-                                        sub-tiles fed by direct global -> LDS loads through a
-                                        four-stage ring of half-depth k-tiles (bk 32 bf16 / 64
-                                        e4m3).  Same limits as GEMM_FLAG_PINGPONG              */
+                                        sub-tiles fed by direct global -> LDS loads, 16 x 16
+                                        MFMAs for bf16.  Same limits as GEMM_FLAG_PINGPONG      */
 #define GEMM_FLAG_TEST_SKIP_PUBLISH 0x100u /* test only: the first Stream-K split of band tile 0
                                               does not publish its lock / arrival, so the bounded
                                               waits on it expire and report GEMM_DEVICE_ERR_SPIN */

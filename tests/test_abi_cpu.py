@@ -110,7 +110,7 @@ def create(**kw):
     (dict(flags=L.GEMM_FLAG_REGSTAGED, K=0), L.GEMM_ERR_UNSUPPORTED),
     (dict(flags=L.GEMM_FLAG_WIDE), L.GEMM_OK),
     (dict(flags=L.GEMM_FLAG_WIDE, dtype_ab=L.GEMM_FP8_E4M3, K=400, M=300), L.GEMM_OK),
-    (dict(flags=L.GEMM_FLAG_WIDE, bk=64), L.GEMM_ERR_UNSUPPORTED),  # its bf16 k-tile is 32 deep
+    (dict(flags=L.GEMM_FLAG_WIDE, bk=32), L.GEMM_ERR_UNSUPPORTED),  # its bf16 k-tile is 64 deep
     (dict(flags=L.GEMM_FLAG_WIDE, sched=L.GEMM_SCHED_STREAMK), L.GEMM_ERR_UNSUPPORTED),
     (dict(flags=L.GEMM_FLAG_WIDE, K=0), L.GEMM_ERR_UNSUPPORTED),
     (dict(flags=L.GEMM_FLAG_WIDE | L.GEMM_FLAG_COOPERATIVE), L.GEMM_ERR_INVALID_ARG),
@@ -150,11 +150,11 @@ def test_plan_info_and_workspace():
     assert r.info.kernel == 0 and r.info.lds_bytes == 128 * 1024
     w = L.Plan(L.make_desc(4096, 4096, 4096, sched=L.GEMM_SCHED_PERSISTENT, num_workers=256,
                            flags=L.GEMM_FLAG_WIDE))
-    assert (w.info.kernel, w.info.threads, w.info.bk, w.info.kt) == (3, 256, 32, 128)
-    assert w.info.lds_bytes == 160 * 1024 and w.info.stages == 4
+    assert (w.info.kernel, w.info.threads, w.info.bk, w.info.kt) == (3, 256, 64, 64)
+    assert w.info.lds_bytes == 160 * 1024 and w.info.stages == 2
     w8 = L.Plan(L.make_desc(8192, 8192, 8192, dtype_ab=L.GEMM_FP8_E4M3, num_workers=256,
                             sched=L.GEMM_SCHED_PERSISTENT, flags=L.GEMM_FLAG_WIDE))
-    assert (w8.info.kernel, w8.info.bk, w8.info.kt) == (3, 64, 128)
+    assert (w8.info.kernel, w8.info.bk, w8.info.kt) == (3, 128, 64)
     s = L.Plan(L.make_desc(256, 256, 256, sched=L.GEMM_SCHED_STATIC, bm=128, bn=128))
     assert s.info.grid == 4 and s.info.sched == L.GEMM_SCHED_STATIC
 
