@@ -127,8 +127,9 @@ def measured_traffic(workload):
 
 
 # name, workload key, mapping, group, sched, tile, out, workers[, bk[, variant]]
-# variant: "chain" = Stream-K lock-chain fixup; "coop" / "vs" / "wide" = the cooperative /
-# register-staged / wide-wave kernel instead of the default for data-parallel 256 x 256 tiles
+# variant: "chain" = Stream-K lock-chain fixup; "coop" / "pp" / "vs" / "wide" = the cooperative /
+# ping-pong / register-staged / wide-wave kernel instead of the default for data-parallel
+# 256 x 256 tiles (the wide-wave kernel)
 RUNS = {
     "bf16_4096": ("bf16_4096", "grouped_m", 8, "persistent", 0, "bf16", 0),
     "bf16_4096_coop": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "coop"),
@@ -138,9 +139,9 @@ RUNS = {
     "fp8_8192_coop": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "coop"),
     "bf16_4096_vs": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "vs"),
     "fp8_8192_vs": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "vs"),
-    "bf16_4096_wide": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "wide"),
-    "fp8_8192_wide": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "wide"),
-    "bf16_mlp_up_wide": ("bf16_mlp_up", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "wide"),
+    "bf16_4096_pp": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "pp"),
+    "fp8_8192_pp": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "pp"),
+    "bf16_mlp_up_pp": ("bf16_mlp_up", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "pp"),
     "bf16_mlp_up": ("bf16_mlp_up", "grouped_m", 8, "persistent", 0, "bf16", 0),
     "bf16_streamk": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256),
     "bf16_streamk_chain": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256, 0,
@@ -298,8 +299,8 @@ def main():
     head = time_run("bf16_4096", args.steps, args.warmup, torch, dg, gi, cache, args.settle_ms)
     secondary = {}
     if not args.no_secondary:
-        for name in ("bf16_4096_coop", "bf16_4096_linear", "bf16_4096_t128", "fp8_8192",
-                     "fp8_8192_coop", "bf16_mlp_up", "bf16_streamk", "bf16_256"):
+        for name in ("bf16_4096_pp", "bf16_4096_coop", "bf16_4096_linear", "bf16_4096_t128",
+                     "fp8_8192", "fp8_8192_pp", "bf16_mlp_up", "bf16_streamk", "bf16_256"):
             steps = max(10, args.steps // (4 if name.startswith("fp8_8192") else 1))
             r = time_run(name, steps, max(2, args.warmup // 2), torch, dg, gi, cache,
                          args.settle_ms / 2)

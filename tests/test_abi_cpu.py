@@ -143,7 +143,7 @@ def test_plan_info_and_workspace():
     q = L.Plan(L.make_desc(4096, 4096, 4096, sched=L.GEMM_SCHED_PERSISTENT, num_workers=256,
                            mapping=L.GEMM_MAP_GROUPED_M, group=8))
     assert q.workspace_bytes == 0 and q.info.bm == 256 and q.info.grid == 256
-    assert i.kernel == 0 and q.info.kernel == 1     # Stream-K: cooperative; 256^2 DP: ping-pong
+    assert i.kernel == 0 and q.info.kernel == 3     # Stream-K: cooperative; 256^2 DP: wide-wave
     assert q.info.lds_bytes == 160 * 1024
     r = L.Plan(L.make_desc(4096, 4096, 4096, sched=L.GEMM_SCHED_PERSISTENT, num_workers=256,
                            flags=L.GEMM_FLAG_COOPERATIVE))

@@ -64,7 +64,7 @@ SMALL = [
 
 
 SK_MODES = {"separate": 0, "chain": L.GEMM_FLAG_STREAMK_CHAIN}
-# data-parallel 256 x 256 plans default to the ping-pong kernel; "coop" forces the cooperative one
+# data-parallel 256 x 256 plans default to the wide-wave kernel; "coop" forces the cooperative one
 MODES = dict(SK_MODES, coop=L.GEMM_FLAG_COOPERATIVE)
 
 
@@ -85,7 +85,7 @@ def test_small_parity(dev, case, mode):
     C, plan, _ = run_gpu(op, torch, dev, out, mapping, G, sched, workers, tile,
                          flags=MODES[mode])
     if tile == 256 and sched != L.GEMM_SCHED_STREAMK:
-        assert plan.info.kernel == (0 if mode == "coop" else 1)
+        assert plan.info.kernel == (0 if mode == "coop" else 3)
     if plan.info.sk_tiles:
         assert plan.info.streamk_mode == (0 if mode == "chain" else 1)
     if sched == L.GEMM_SCHED_STREAMK and name != "bf16_streamk_hybrid":
