@@ -34,7 +34,7 @@ using CfgFp8_256 = TileCfg<DT_FP8, 256, 256, 128, 2, 4, 2, 1>;
 using CfgFp8_128 = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 2, 1>;
 // The wide-wave kernel (GEMM_FLAG_WIDE): four waves of 128 x 128, two stages.
 using CfgBf16_256w = TileCfg<DT_BF16, 256, 256, 64, 2, 2, 2, 1, 16>;  // 16 x 16 x 32 MFMAs
-using CfgFp8_256w = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1>;
+using CfgFp8_256w = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1, 16>;  // 16 x 16 x 128 MFMAs
 
 typedef hipError_t (*launch_fn)(const KernelArgs &, int grid, bool ragged_k, hipStream_t);
 typedef const void *(*kernel_fn)();
@@ -76,17 +76,25 @@ const void *kernel_of_vs() {
   return (const void *)&gemm_kernel_vs<CFG, false>;
 }
 
+// k-tiles one MFMA deep (e4m3 16 x 16 x 128) take the single-A-buffer form of the schedule
+template <class CFG, bool RAGGED_K>
+constexpr auto wide_kernel() {
+  if constexpr (CFG::KSUB == 1)
+    return &gemm_kernel_wide1<CFG, RAGGED_K>;
+  else
+    return &gemm_kernel_wide<CFG, RAGGED_K>;
+}
 template <class CFG>
 hipError_t launch_wide(const KernelArgs &a, int grid, bool ragged_k, hipStream_t s) {
   if (ragged_k)
-    hipLaunchKernelGGL((gemm_kernel_wide<CFG, true>), dim3(grid), dim3(CFG::THREADS), 0, s, a);
+    hipLaunchKernelGGL((wide_kernel<CFG, true>()), dim3(grid), dim3(CFG::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_kernel_wide<CFG, false>), dim3(grid), dim3(CFG::THREADS), 0, s, a);
+    hipLaunchKernelGGL((wide_kernel<CFG, false>()), dim3(grid), dim3(CFG::THREADS), 0, s, a);
   return hipGetLastError();
 }
 template <class CFG>
 const void *kernel_of_wide() {
-  return (const void *)&gemm_kernel_wide<CFG, false>;
+  return (const void *)wide_kernel<CFG, false>();
 }
 
 // kind: KIND_COOP runs every plan; the others run data-parallel work only (no Stream-K splits,

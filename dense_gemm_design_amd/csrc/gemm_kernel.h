@@ -1757,6 +1757,172 @@ gemm_kernel_wide(KernelArgs args) {
   wait_vmcnt<0>();
 }
 
+// ---- wide-wave kernel, one MFMA depth per k-tile (e4m3 16 x 16 x 128) ------------------------
+//
+// The wide-wave schedule for k-tiles exactly one MFMA deep.  A k-step's fragments then fill 128
+// VGPRs, so they cannot all be double buffered next to 256 accumulators: B (read by every row of
+// MFMAs) has two buffers, A one.  The MFMAs go row by row (f-major), and A[f] of step c+1 is read
+// into A[f]'s registers right after the last MFMA of row f of step c, once handshake H(c+1) has
+// passed -- so H(c+1) sits after row 0.  B of step c+1 goes into the other buffer, and the loads
+// of step c+S (begun by H(c+1)) go out over the first half of the slots after the handshake,
+// which leaves them more than half a k-step before H(c+2) waits for them.
+template <class CFG, bool RAGGED_K>
+__global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::THREADS),
+                               amdgpu_waves_per_eu(1, 1)))
+gemm_kernel_wide1(KernelArgs args) {
+  static_assert(CFG::WAVES == 4 && CFG::WGM == 2 && CFG::WGN == 2, "four waves, one per SIMD");
+  static_assert(CFG::KSUB == 1 && CFG::MI == 16, "one 16 x 16 MFMA depth per k-tile");
+  static_assert(CFG::STAGES >= 2 && (CFG::STAGES & (CFG::STAGES - 1)) == 0, "stage = c mod S");
+  static_assert(wide_lds_bytes<CFG>() <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[wide_lds_bytes<CFG>()];
+  lds_t *smem = (lds_t *)(size_t)(uint32_t)(size_t)(lds_t *)smem_raw;
+  const uint32_t smem_base = (uint32_t)(size_t)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / CFG::WGN, wn = wave % CFG::WGN;
+  const int32_t b = blockIdx.x;
+  lds_t *slice = smem + CFG::LDS_BYTES + wave * kWideSlice;
+
+  float alpha = 1.0f;
+  if constexpr (CFG::DT == DT_FP8) alpha = (*args.scale_a) * (*args.scale_b);
+
+  uint32_t aoff[1][CFG::CPL], boff[1][CFG::CPL];
+  {
+    const int r = lane % CFG::MI;
+    const int swz = (r >> CFG::SWZ) & (CFG::CH - 1);
+#pragma unroll
+    for (int h = 0; h < CFG::CPL; ++h) {
+      const int chunk = (lane / CFG::MI) * CFG::CPL + h;
+      const uint32_t in_row = (uint32_t)((chunk ^ swz) * 16);
+      aoff[0][h] = (uint32_t)((wm * CFG::WM + r) * CFG::ROWB) + in_row;
+      boff[0][h] = (uint32_t)(CFG::A_BYTES + (wn * CFG::WN + r) * CFG::ROWB) + in_row;
+    }
+  }
+  typedef typename FragT<CFG::DT>::type Frag;
+  constexpr int H = CFG::CPL - 1;
+  auto read_a = [&](Frag &dst, int stage, int f) {
+    const lds_t *base = smem + stage * CFG::STAGE_BYTES + f * CFG::MI * CFG::ROWB;
+    dst = lds_frag<CFG::DT>(base + aoff[0][0], base + aoff[0][H]);
+  };
+  auto read_b = [&](Frag &dst, int stage, int g) {
+    const lds_t *base = smem + stage * CFG::STAGE_BYTES + g * CFG::MI * CFG::ROWB;
+    dst = lds_frag<CFG::DT>(base + boff[0][0], base + boff[0][H]);
+  };
+
+  using Prod = WideProducer<CFG, RAGGED_K>;
+  Prod prod;
+  prod.init(args, b, wave, lane);
+  const uint32_t lds_wave0 = smem_base + (uint32_t)wave * 1024;
+  Cursor ccur;
+  cursor_init(args.sp, b, ccur);
+  WorkItem cw;
+  bool cvalid = cursor_next(args.sp, ccur, cw);
+  if (!cvalid) return;  // no work (the whole workgroup alike)
+
+  constexpr int L = Prod::L;
+  constexpr int FM = CFG::FM, FN = CFG::FN, NM = FM * FN;
+  constexpr int HS = FN;  // the handshake follows row 0
+  // the loads go out in the first half of the slots after it: the next handshake, in the next
+  // k-step at slot HS, waits for them (vmcnt), and the ones issued last need the time to land
+  constexpr int LW = HS + (NM - HS) / 2;
+  auto load_all = [&] {
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+      (prod.template load<J>(), ...);
+    }(std::make_integer_sequence<int, L>());
+    prod.end(args);
+  };
+#pragma unroll
+  for (int s = 0; s < CFG::STAGES - 1; ++s) {
+    prod.begin(args, lds_wave0, s);
+    load_all();
+  }
+
+  Frag fa[FM], fb[2][FN];
+  int c = 0;
+  auto handshake = [&](int step) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wait_vmcnt<((CFG::STAGES - 2) * L > 63 ? 63 : (CFG::STAGES - 2) * L)>();
+    lds_barrier();
+    prod.begin(args, lds_wave0, (step + CFG::STAGES - 1) & (CFG::STAGES - 1));
+  };
+  handshake(0);
+  load_all();
+#pragma unroll
+  for (int g = 0; g < FN; ++g) read_b(fb[0][g], 0, g);
+#pragma unroll
+  for (int f = 0; f < FM; ++f) read_a(fa[f], 0, f);
+
+  // k-step c on B buffer P: MFMA i = (f, g) = (i / FN, i % FN); after MFMA i: the handshake
+  // (i = HS - 1), A[f] of step c+1 (i = last of row f, from the handshake on), B reads of step
+  // c+1 into buffer P^1 and the loads of step c+S, both spread over the slots after the handshake
+  auto kstep = [&](auto p_c, auto acc_ref) {
+    constexpr int P = decltype(p_c)::value;
+    auto &acc = *acc_ref;
+    const int nstage = (c + 1) & (CFG::STAGES - 1);
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (
+          [&] {
+            constexpr int i = I;
+            constexpr int f = i / FN, g = i % FN;
+            mfma_blk<CFG>(acc[f][g], fb[P][g], fa[f]);
+            if constexpr (i + 1 == HS) handshake(c + 1);
+            if constexpr (i + 1 >= HS) {
+              if constexpr (g == FN - 1) read_a(fa[f], nstage, f);
+              constexpr int blo = ops_before(i, FN, HS, NM), bhi = ops_before(i + 1, FN, HS, NM);
+              [&]<int... E>(std::integer_sequence<int, E...>) {
+                (read_b(fb[P ^ 1][blo + E], nstage, blo + E), ...);
+              }(std::make_integer_sequence<int, bhi - blo>());
+              constexpr int plo = ops_before(i, L, HS, LW), phi = ops_before(i + 1, L, HS, LW);
+              [&]<int... J>(std::integer_sequence<int, J...>) {
+                (prod.template load<plo + J>(), ...);
+              }(std::make_integer_sequence<int, phi - plo>());
+              if constexpr (phi == L && plo < L) prod.end(args);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }(),
+          ...);
+    }(std::make_integer_sequence<int, NM>());
+    ++c;
+  };
+
+  int seq = 0;
+  while (cvalid) {
+    if ((args.flags & KF_TRACE) && tid == 0 && seq < args.trace_cap) {
+      int *t = args.trace + ((int64_t)b * args.trace_cap + seq) * 8;
+      t[0] = b; t[1] = seq; t[2] = cw.tile; t[3] = cw.m;
+      t[4] = cw.n; t[5] = cw.kb; t[6] = cw.ke; t[7] = cw.role;
+    }
+    ++seq;
+    acc_t<CFG> acc[FM][FN];
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int g = 0; g < FN; ++g) acc[f][g] = acc_t<CFG>{};
+    mfma_wait_states();  // zeroed accumulators reach the MFMAs
+    // k-steps in pairs, so each item starts on B buffer 0; after an odd last step the next item's
+    // B sits in buffer 1 and moves over (once per item)
+    int k = cw.kb;
+    for (; k + 2 <= cw.ke; k += 2) {
+      kstep(std::integral_constant<int, 0>(), &acc);
+      kstep(std::integral_constant<int, 1>(), &acc);
+    }
+    if (k < cw.ke) {
+      kstep(std::integral_constant<int, 0>(), &acc);
+#pragma unroll
+      for (int g = 0; g < FN; ++g) fb[0][g] = fb[1][g];
+    }
+    mfma_wait_states();  // the last MFMAs' results are written
+    if (args.out_bf16)
+      epilogue_wide<CFG>(args, cw, acc, alpha, wm, wn, lane, slice);
+    else
+      epilogue_direct<CFG>(args, cw, acc, alpha, wm, wn, lane);
+    cvalid = cursor_next(args.sp, ccur, cw);
+  }
+  wait_vmcnt<0>();
+}
+
 __global__ void clear_ints_kernel(int *p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;

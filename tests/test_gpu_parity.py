@@ -260,7 +260,7 @@ def test_empty_and_zero_depth(dev, M, N, K):
 
 # kernels whose MFMA is the 16 x 16 form (a different summation order inside each MFMA than the
 # 32 x 32 form the other kernels use), per operand type
-MFMA16 = {("wide", "bf16")}
+MFMA16 = {("wide", "bf16"), ("wide", "e4m3")}
 
 
 @pytest.mark.parametrize("dt,out", [("bf16", "f32"), ("bf16", "bf16"), ("e4m3", "bf16"),
