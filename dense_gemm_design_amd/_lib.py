@@ -29,7 +29,7 @@ GEMM_FLAG_TEST_SKIP_PUBLISH = 0x100
 GEMM_DEVICE_OK, GEMM_DEVICE_ERR_SPIN = 0, 1
 
 EXPORTS = ("gemm_create", "gemm_workspace_bytes", "gemm_plan_get", "gemm_run", "gemm_destroy",
-           "gemm_schedule_enumerate", "gemm_status_string")
+           "gemm_schedule_enumerate", "gemm_rank_configs", "gemm_status_string")
 
 
 class GemmDesc(ctypes.Structure):
@@ -55,7 +55,17 @@ class GemmPlanInfo(ctypes.Structure):
                 ("dp_tiles", ctypes.c_int64), ("sk_tiles", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64), ("trace_offset", ctypes.c_int64),
                 ("trace_capacity", ctypes.c_int32), ("error_offset", ctypes.c_int32),
-                ("streamk_mode", ctypes.c_int32), ("kernel", ctypes.c_int32)]
+                ("streamk_mode", ctypes.c_int32), ("kernel", ctypes.c_int32),
+                ("group", ctypes.c_int32)]
+
+
+class GemmConfigScore(ctypes.Structure):
+    _fields_ = [("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
+                ("kernel", ctypes.c_int32), ("sched", ctypes.c_int32),
+                ("workers", ctypes.c_int32), ("group", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("cycles_mfma", ctypes.c_double), ("cycles_l2", ctypes.c_double),
+                ("cycles_local", ctypes.c_double), ("wave_efficiency", ctypes.c_double),
+                ("cycles_fixed", ctypes.c_double), ("score", ctypes.c_double)]
 
 
 _lib = None
@@ -78,6 +88,8 @@ def load():
     lib.gemm_destroy.argtypes = [vp]
     lib.gemm_schedule_enumerate.argtypes = [vp, ctypes.POINTER(GemmWorkItem), sz,
                                             ctypes.POINTER(sz)]
+    lib.gemm_rank_configs.argtypes = [ctypes.POINTER(GemmDesc), ctypes.POINTER(GemmConfigScore),
+                                      sz, ctypes.POINTER(sz)]
     lib.gemm_status_string.argtypes = [ctypes.c_int]
     lib.gemm_status_string.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -104,6 +116,19 @@ def make_desc(M, N, K, dtype_ab=GEMM_BF16, dtype_c=GEMM_F32, mapping=GEMM_MAP_LI
               layout_a=GEMM_ROW_MAJOR, layout_b=GEMM_COL_MAJOR):
     return GemmDesc(M, N, K, dtype_ab, dtype_c, layout_a, layout_b, mapping, group, sched,
                     num_workers, bm, bn, bk, flags)
+
+
+def rank_configs(desc):
+    """The planner's cost-model ranking for `desc` (a GemmDesc), best first."""
+    lib = load()
+    n = ctypes.c_size_t()
+    st = lib.gemm_rank_configs(ctypes.byref(desc), None, 0, ctypes.byref(n))
+    if st not in (GEMM_OK, GEMM_ERR_CAPACITY):
+        _check(st, "gemm_rank_configs")
+    arr = (GemmConfigScore * max(n.value, 1))()
+    _check(lib.gemm_rank_configs(ctypes.byref(desc), arr, n.value, ctypes.byref(n)),
+           "gemm_rank_configs")
+    return list(arr[:n.value])
 
 
 class Plan:

@@ -11,6 +11,10 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
 #include "../../include/gemm.h"
 #include "gemm_kernel.h"
 #include "sched.h"
@@ -149,6 +153,148 @@ constexpr int kTraceCap = 64;
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t align_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
+// ---- kernel-configuration heuristic -----------------------------------------------------------
+// The cost model of "DeepGEMM on SM90" (section "Kernel Configuration Heuristic"), re-fitted to
+// gfx950.  Per candidate, whole-GEMM clocks on three sides:
+//   cycles_l2    = bytes from L2 to the CUs (A/B k-tiles, C, Stream-K partials) / L2->CU bandwidth
+//   cycles_local = bytes through LDS (A/B fills, MFMA fragment reads, C staging) / LDS bandwidth
+//   cycles_mfma  = FLOPs / (matrix-core FLOP per clock x the kernel's measured efficiency)
+// and score = max of the three / wave_efficiency + cycles_fixed, the minimum winning.  The page's
+// SM-side term counts the Tensor Core operand bytes; on gfx950 the fragment reads are those
+// bytes and the matrix cores get their own term, because a kernel's schedule -- not only its
+// bytes -- sets how close it comes to peak.  cycles_fixed adds what does not overlap the MAC
+// loop: a worker's first stage of loads, each item's epilogue, and for Stream-K the partial sums,
+// which go to device memory (coherent accesses past the XCD's L2) after the MAC work.  The
+// constants are measurements on MI355X (all CUs busy):
+constexpr double kL2BytesPerClk = 57.0;      // global->LDS loads per CU
+constexpr double kLdsBytesPerClk = 256.0;    // ds_read_b128 per CU
+constexpr double kDeviceBytesPerClk = 2600;  // Stream-K partials, whole device (128 MiB in 25 us)
+constexpr double kLatencyClk = 2000;         // first load or store round trip of a phase
+// MFMA efficiency of whole launches at the held clock (bench workloads, profiles/)
+double kernel_efficiency(int kind, int bm, int dt) {
+  if (kind == KIND_WIDE) return dt == DT_BF16 ? 0.76 : 0.79;
+  if (kind == KIND_PP) return 0.66;
+  if (bm == 256) return dt == DT_BF16 ? 0.60 : 0.70;
+  return dt == DT_BF16 ? 0.35 : 0.25;
+}
+double flop_per_clk_per_cu(int dt) { return dt == DT_BF16 ? 4096.0 : 8192.0; }
+
+// G for a grouped mapping: each XCD runs `chunk` consecutive tiles of F(i) at a time (the XCD
+// remap gives it a contiguous run of workers); under grouped-M(G) they form a G x (chunk / G)
+// block, which reads G + chunk / G operand strips per k-step.  The fewest strips win, the larger
+// G on a tie.
+int choose_group(int mapping, int64_t Mt, int64_t Nt, int64_t chunk) {
+  const int64_t span = mapping == GEMM_MAP_GROUPED_M ? Mt : Nt;
+  const int64_t other = mapping == GEMM_MAP_GROUPED_M ? Nt : Mt;
+  int best = 1;
+  int64_t best_strips = INT64_MAX;
+  for (int G = 1; G <= 32; G *= 2) {
+    const int64_t g = G < span ? G : (span > 0 ? span : 1);
+    int64_t cols = cdiv(chunk, g);
+    if (cols > other) cols = other;
+    const int64_t strips = g + cols;
+    if (strips <= best_strips) {
+      best_strips = strips;
+      best = G;
+    }
+    if (G >= span) break;
+  }
+  return best;
+}
+
+struct ModelCand {
+  int kind, bm, bn, sched;
+};
+
+// Scores every feasible candidate for `d` (already validated), best first.  cus / occupancy come
+// from the device when num_workers == 0.
+int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
+  const int dt = d.dtype_ab == GEMM_BF16 ? DT_BF16 : DT_FP8;
+  const double eb = dt == DT_BF16 ? 2.0 : 1.0, ec = d.dtype_c == GEMM_BF16 ? 2.0 : 4.0;
+  const ModelCand cands[] = {{KIND_WIDE, 256, 256, GEMM_SCHED_PERSISTENT},
+                             {KIND_COOP, 128, 128, GEMM_SCHED_PERSISTENT},
+                             {KIND_COOP, 128, 128, GEMM_SCHED_STREAMK},
+                             {KIND_COOP, 256, 256, GEMM_SCHED_STREAMK}};
+  int cus = 0, dev = 0;
+  if (d.num_workers == 0) {
+    if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return GEMM_ERR_HIP;
+  }
+  const bool grouped = d.mapping == GEMM_MAP_GROUPED_M || d.mapping == GEMM_MAP_GROUPED_N;
+  out.clear();
+  for (const ModelCand &c : cands) {
+    if (c.kind != KIND_COOP && d.K == 0) continue;  // the data-parallel kernels need K > 0
+    const KernelEntry *e = nullptr;
+    for (const KernelEntry &k : kKernels)
+      if (k.dt == dt && k.bm == c.bm && k.bn == c.bn && k.kind == c.kind) {
+        e = &k;
+        break;
+      }
+    if (!e) continue;
+    int occ = 1;
+    int P = d.num_workers;
+    if (P == 0) {
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, e->kernel(), e->threads, 0) !=
+          hipSuccess)
+        return GEMM_ERR_HIP;
+      if (occ < 1) occ = 1;
+      P = cus * occ;
+    }
+    // without a device: one worker per CU
+    const double ncu = d.num_workers == 0 ? (double)cus : (double)P;
+    const int64_t Mt = cdiv(d.M, c.bm), Nt = cdiv(d.N, c.bn), tiles = Mt * Nt;
+    const int64_t Kt = cdiv(d.K, e->bk), Keff = Kt * e->bk;
+    int32_t dp = (int32_t)tiles, sk = 0;
+    if (c.sched == GEMM_SCHED_STREAMK) {
+      if (tiles > INT32_MAX) continue;
+      streamk_plan(tiles, P, dp, sk);
+      if (sk == 0 || Kt == 0) continue;  // no tail to balance: the data-parallel candidate covers it
+    }
+    const int wgm = 2, wgn = e->threads / 64 / 2;  // waves along M and N
+    const double t = (double)tiles, bm = c.bm, bn = c.bn, kk = (double)Keff;
+    gemm_config_score r;
+    memset(&r, 0, sizeof r);
+    r.bm = c.bm;
+    r.bn = c.bn;
+    r.bk = e->bk;
+    r.kernel = c.kind;
+    r.sched = c.sched;
+    r.workers = P;
+    const int X = P % 8 == 0 ? 8 : 1;
+    r.group = grouped ? (d.group > 0 ? d.group : choose_group(d.mapping, Mt, Nt, P / X)) : 1;
+    const double bytes_l2 = t * (kk * (bm + bn) * eb + bm * bn * ec);
+    const double bytes_local = t * (kk * (bm + bn) * eb + kk * (bm * wgn + bn * wgm) * eb + bm * bn * ec);
+    r.cycles_l2 = bytes_l2 / (ncu * kL2BytesPerClk);
+    r.cycles_local = bytes_local / (ncu * kLdsBytesPerClk);
+    r.cycles_mfma = 2.0 * bm * bn * kk * t /
+                    (ncu * flop_per_clk_per_cu(dt) * kernel_efficiency(c.kind, c.bm, dt));
+    // wave efficiency over the CUs (a CU that runs fewer resident workgroups runs each faster)
+    double items;  // items per worker, for the epilogues
+    if (c.sched == GEMM_SCHED_STREAMK) {
+      const double iters = t * (double)Kt;
+      r.wave_efficiency = iters / (std::ceil(iters / P) * P);
+      items = std::ceil((double)dp / P) + 2.0;  // data-parallel tiles and about two splits
+    } else {
+      r.wave_efficiency = tiles > 0 ? t / (std::ceil(t / ncu) * ncu) : 1.0;
+      items = std::ceil(t / ncu);
+    }
+    const double stage_bytes = (bm + bn) * e->bk * eb;
+    r.cycles_fixed = stage_bytes * (e->stages - 1) / kL2BytesPerClk + kLatencyClk +
+                     items * (bm * bn * ec / kL2BytesPerClk + kLatencyClk / 2);
+    if (sk > 0) {  // separate reduction: every split writes its partial, the reduction reads it
+      const double units_per_tile = std::ceil((double)P / sk);
+      r.cycles_fixed += 2.0 * sk * units_per_tile * bm * bn * 4.0 / kDeviceBytesPerClk + kLatencyClk;
+    }
+    const double worst = std::max(r.cycles_mfma, std::max(r.cycles_l2, r.cycles_local));
+    r.score = worst / r.wave_efficiency + r.cycles_fixed;
+    out.push_back(r);
+  }
+  std::stable_sort(out.begin(), out.end(), [](const gemm_config_score &a,
+                                              const gemm_config_score &b) { return a.score < b.score; });
+  return out.empty() ? GEMM_ERR_UNSUPPORTED : GEMM_OK;
+}
+
 }  // namespace
 
 struct gemm_plan {
@@ -186,7 +332,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     return GEMM_ERR_INVALID_ARG;
   if (d.mapping < GEMM_MAP_LINEAR_N || d.mapping > GEMM_MAP_GROUPED_N) return GEMM_ERR_INVALID_ARG;
   const bool grouped = d.mapping == GEMM_MAP_GROUPED_M || d.mapping == GEMM_MAP_GROUPED_N;
-  if (grouped && d.group < 1) return GEMM_ERR_INVALID_ARG;
+  if (grouped && d.group < 0) return GEMM_ERR_INVALID_ARG;  // 0: the planner picks G
   if (d.sched < GEMM_SCHED_STATIC || d.sched > GEMM_SCHED_AUTO) return GEMM_ERR_INVALID_ARG;
   if (d.num_workers < 0 || d.bm < 0 || d.bn < 0 || d.bk < 0) return GEMM_ERR_INVALID_ARG;
   const uint32_t kind_flags =
@@ -214,9 +360,18 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (force_dp && (d.K == 0 || d.sched == GEMM_SCHED_STREAMK || d.sched == GEMM_SCHED_AUTO))
     return GEMM_ERR_UNSUPPORTED;
 
-  // Tile shape: 256 x 256 unless asked otherwise or the problem has too few big tiles.
+  // Tile shape and scheduler: the cost model when everything is left to the planner, else
+  // 256 x 256 unless asked otherwise or the problem has too few big tiles.
   int bm = d.bm, bn = d.bn;
-  if (bm == 0 && bn == 0) {
+  int model_sched = -1;
+  if (bm == 0 && bn == 0 && d.bk == 0 && d.sched == GEMM_SCHED_AUTO && force_kind < 0) {
+    std::vector<gemm_config_score> ranked;
+    const int st = rank_configs(d, ranked);
+    if (st != GEMM_OK) return st;
+    bm = ranked[0].bm;
+    bn = ranked[0].bn;
+    model_sched = ranked[0].sched;
+  } else if (bm == 0 && bn == 0) {
     const int64_t big = cdiv(d.M, 256) * cdiv(d.N, 256);  // 0 for an empty output
     const bool streamk = d.sched == GEMM_SCHED_STREAMK;
     bm = bn = ((big >= 128 && !streamk) || force_dp) ? 256 : 128;
@@ -239,7 +394,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   const int64_t tiles = Mt * Nt;
   if (Mt > INT32_MAX || Nt > INT32_MAX || tiles > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
 
-  int sched = d.sched;
+  int sched = model_sched >= 0 ? model_sched : d.sched;
   int workers = d.num_workers;
   if (sched != GEMM_SCHED_STATIC && workers == 0) {
     int dev = 0, cus = 0, per_cu = 0;
@@ -294,6 +449,8 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     if ((int64_t)sp.sk_tiles * Kt > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
   }
   sp.X = (d.flags & GEMM_FLAG_NO_XCD_REMAP) ? 1 : kXcds;
+  if (grouped && d.group == 0)  // the planner's G: fewest operand strips per XCD's run of tiles
+    sp.G = choose_group(d.mapping, Mt, Nt, sp.P % sp.X == 0 ? sp.P / sp.X : sp.P);
   sched_prepare(sp);
 
   gemm_plan *p = new (std::nothrow) gemm_plan;
@@ -368,7 +525,26 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   in.error_offset = (int32_t)p->error_off;
   in.streamk_mode = sk_mode;
   in.kernel = k->kind;
+  in.group = sp.G;
   *out = p;
+  return GEMM_OK;
+}
+
+int gemm_rank_configs(const gemm_desc *desc, gemm_config_score *items, size_t cap,
+                      size_t *n_out) {
+  if (!desc || !n_out || (cap && !items)) return GEMM_ERR_INVALID_ARG;
+  *n_out = 0;
+  const gemm_desc d = *desc;
+  if (d.M < 0 || d.N < 0 || d.K < 0 || d.num_workers < 0 || d.group < 0) return GEMM_ERR_INVALID_ARG;
+  if (d.dtype_ab != GEMM_BF16 && d.dtype_ab != GEMM_FP8_E4M3) return GEMM_ERR_INVALID_ARG;
+  if (d.dtype_c != GEMM_F32 && d.dtype_c != GEMM_BF16) return GEMM_ERR_INVALID_ARG;
+  if (d.mapping < GEMM_MAP_LINEAR_N || d.mapping > GEMM_MAP_GROUPED_N) return GEMM_ERR_INVALID_ARG;
+  std::vector<gemm_config_score> ranked;
+  const int st = rank_configs(d, ranked);
+  if (st != GEMM_OK) return st;
+  *n_out = ranked.size();
+  if (cap < ranked.size()) return GEMM_ERR_CAPACITY;
+  for (size_t i = 0; i < ranked.size(); ++i) items[i] = ranked[i];
   return GEMM_OK;
 }
 

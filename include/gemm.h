@@ -96,7 +96,8 @@ typedef struct gemm_desc {
   int32_t layout_a;          /* must be GEMM_ROW_MAJOR: a(m,k) at A[m*K + k]                    */
   int32_t layout_b;          /* must be GEMM_COL_MAJOR: b(k,n) at B[n*K + k]                    */
   int32_t mapping;           /* gemm_mapping                                                     */
-  int32_t group;             /* G for the grouped mappings (>= 1); ignored by the linear ones   */
+  int32_t group;             /* G for the grouped mappings (>= 1, or 0 = chosen by the planner);
+                                ignored by the linear ones                                      */
   int32_t sched;             /* gemm_sched                                                       */
   int32_t num_workers;       /* P for persistent / Stream-K; 0 = CUs x resident workgroups/CU    */
   int32_t bm, bn, bk;        /* tile shape; 0 = auto.  Supported: see gemm_create              */
@@ -128,6 +129,7 @@ typedef struct gemm_plan_info {
   int32_t error_offset;      /* byte offset of the device error word in the workspace (-1: none)*/
   int32_t streamk_mode;      /* 0 lock chain, 1 separate reduction (meaningful when sk_tiles>0)  */
   int32_t kernel;            /* 0 cooperative, 1 ping-pong, 2 register-staged, 3 wide-wave       */
+  int32_t group;             /* G of a grouped mapping as planned (1 for the linear ones)       */
 } gemm_plan_info;
 
 /* device error word values (read back from the workspace after a run) */
@@ -163,6 +165,36 @@ int gemm_destroy(gemm_handle h);
  * items in processing order) and the total count to *n_out.  Returns GEMM_ERR_CAPACITY (with
  * *n_out set) when cap is too small. */
 int gemm_schedule_enumerate(gemm_handle h, gemm_work_item *items, size_t cap, size_t *n_out);
+
+/* One candidate configuration as the planner's cost model scores it (gemm_rank_configs). */
+typedef struct gemm_config_score {
+  int32_t bm, bn, bk;        /* tile                                                             */
+  int32_t kernel;            /* as gemm_plan_info.kernel                                        */
+  int32_t sched;             /* GEMM_SCHED_PERSISTENT or GEMM_SCHED_STREAMK                     */
+  int32_t workers;           /* P the plan would launch                                         */
+  int32_t group;             /* G for a grouped mapping (1 for the linear ones)                 */
+  int32_t pad_;
+  double cycles_mfma;        /* modelled clocks, whole GEMM, matrix-core side                   */
+  double cycles_l2;          /* L2 -> CU side: A/B tile loads and C                             */
+  double cycles_local;       /* LDS side: tile fills, fragment reads, C staging                 */
+  double wave_efficiency;    /* busy CU slots / (waves x CUs); Stream-K: over its units         */
+  double cycles_fixed;       /* not overlapped with the MAC loop: first loads, epilogues, and
+                                Stream-K partial sums through device memory                    */
+  double score;              /* max(mfma, l2, local) / wave_efficiency + fixed; lower is better */
+} gemm_config_score;
+
+/* Kernel-configuration heuristic: the cost model of "DeepGEMM on SM90" (section "Kernel
+ * Configuration Heuristic") -- candidates from a small discrete set, a resource filter, then
+ * score = max(cycles_local, cycles_L2) / wave_efficiency with the minimum winning -- re-fitted to
+ * gfx950: the candidates are this library's kernels and tiles (256 x 256 wide-wave data-parallel,
+ * 128 x 128 cooperative data-parallel, both tiles on the cooperative kernel with a Stream-K tail),
+ * the bandwidths and per-kernel MFMA efficiencies are measured on MI355X, a matrix-core term
+ * joins the two data-movement terms, and the costs that do not overlap the MAC loop are added.  Fills up to `cap` candidates, best first, and the total to
+ * *n_out (GEMM_ERR_CAPACITY when cap is too small; items may be NULL with cap 0).  gemm_create
+ * takes the best one when bm = bn = bk = 0, sched = GEMM_SCHED_AUTO and no kernel flag is set;
+ * with a grouped mapping and group = 0 it takes the G reported here.  Needs a visible GPU only
+ * when num_workers == 0. */
+int gemm_rank_configs(const gemm_desc *desc, gemm_config_score *items, size_t cap, size_t *n_out);
 
 /* Static string for a gemm_status value. */
 const char *gemm_status_string(int status);

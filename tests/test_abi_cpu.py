@@ -79,7 +79,8 @@ def create(**kw):
     (dict(dtype_ab=L.GEMM_F32), L.GEMM_ERR_INVALID_ARG),
     (dict(dtype_c=9), L.GEMM_ERR_INVALID_ARG),
     (dict(mapping=4), L.GEMM_ERR_INVALID_ARG),
-    (dict(mapping=L.GEMM_MAP_GROUPED_M, group=0), L.GEMM_ERR_INVALID_ARG),
+    (dict(mapping=L.GEMM_MAP_GROUPED_M, group=-1), L.GEMM_ERR_INVALID_ARG),
+    (dict(mapping=L.GEMM_MAP_GROUPED_M, group=0), L.GEMM_OK),       # the planner picks G
     (dict(sched=9), L.GEMM_ERR_INVALID_ARG),
     (dict(num_workers=-1), L.GEMM_ERR_INVALID_ARG),
     (dict(flags=0x80), L.GEMM_ERR_INVALID_ARG),

@@ -1,0 +1,156 @@
+"""The planner's kernel-configuration heuristic (gemm_rank_configs): the cost model of "DeepGEMM
+on SM90" (section "Kernel Configuration Heuristic") re-fitted to gfx950.  CPU tests check the
+model's arithmetic and its choices on the workloads whose best configuration was measured; the
+GPU test times every candidate the model ranks and checks that its pick is close to the fastest."""
+import math
+import os
+import sys
+import time
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+from dense_gemm_design_amd import _lib as L  # noqa: E402
+
+P = 256
+
+
+def desc(M, N, K, dt=L.GEMM_BF16, out=L.GEMM_BF16, mapping=L.GEMM_MAP_GROUPED_M, group=0, P=P):
+    return L.make_desc(M, N, K, dt, out, mapping, group, L.GEMM_SCHED_AUTO, P)
+
+
+def test_scores_are_the_models_formula():
+    for d in (desc(4096, 4096, 4096), desc(4096, 14336, 4096), desc(512, 512, 65536, out=L.GEMM_F32),
+              desc(8192, 8192, 8192, dt=L.GEMM_FP8_E4M3)):
+        ranked = L.rank_configs(d)
+        assert ranked, "at least one feasible candidate"
+        assert [c.score for c in ranked] == sorted(c.score for c in ranked)
+        for c in ranked:
+            worst = max(c.cycles_mfma, c.cycles_l2, c.cycles_local)
+            assert c.score == pytest.approx(worst / c.wave_efficiency + c.cycles_fixed, rel=1e-12)
+            assert c.cycles_fixed > 0
+            assert 0 < c.wave_efficiency <= 1
+
+
+def test_wave_efficiency_of_a_partial_last_wave():
+    # 4096 x 14336 on 256 x 256 tiles: 16 x 56 = 896 tiles, 3.5 waves of 256
+    ranked = L.rank_configs(desc(4096, 14336, 4096))
+    dp = [c for c in ranked if c.bm == 256 and c.sched == L.GEMM_SCHED_PERSISTENT][0]
+    assert dp.wave_efficiency == pytest.approx(896 / (4 * 256))
+    # the cooperative 128 x 128 candidate has 3584 tiles = 14 whole waves
+    c128 = [c for c in ranked if c.bm == 128 and c.sched == L.GEMM_SCHED_PERSISTENT][0]
+    assert c128.wave_efficiency == pytest.approx(1.0)
+
+
+def test_data_movement_terms():
+    # bf16 4096^3, 256 x 256 wide-wave: per tile K (BM + BN) 2 bytes of A/B plus BM BN 2 of C
+    # through L2, at 57 B/clk/CU on 256 CUs
+    c = [c for c in L.rank_configs(desc(4096, 4096, 4096)) if c.kernel == 3][0]
+    tiles = 16 * 16
+    l2_bytes = tiles * (4096 * 512 * 2 + 256 * 256 * 2)
+    assert c.cycles_l2 == pytest.approx(l2_bytes / (P * 57.0))
+    # LDS: fills plus fragment reads (each A row read by 2 waves, each B row by 2) plus C staging
+    lds_bytes = tiles * (4096 * 512 * 2 + 4096 * (256 * 2 + 256 * 2) * 2 + 256 * 256 * 2)
+    assert c.cycles_local == pytest.approx(lds_bytes / (P * 256.0))
+    # MFMA: 2 M N K / (4096 FLOP per clock per CU x 256 CUs x the kernel's measured efficiency)
+    eff = 2 * 4096 ** 3 / (P * 4096.0) / c.cycles_mfma
+    assert 0.5 < eff < 1.0
+
+
+@pytest.mark.parametrize("shape,dt,out,want", [
+    ((4096, 4096, 4096), L.GEMM_BF16, L.GEMM_BF16, (256, 3, L.GEMM_SCHED_PERSISTENT)),
+    ((8192, 8192, 8192), L.GEMM_FP8_E4M3, L.GEMM_BF16, (256, 3, L.GEMM_SCHED_PERSISTENT)),
+    ((4096, 14336, 4096), L.GEMM_BF16, L.GEMM_BF16, (256, 3, L.GEMM_SCHED_PERSISTENT)),
+    ((512, 512, 65536), L.GEMM_BF16, L.GEMM_F32, (None, 0, L.GEMM_SCHED_STREAMK)),
+    ((256, 256, 256), L.GEMM_BF16, L.GEMM_F32, (128, 0, L.GEMM_SCHED_PERSISTENT)),
+])
+def test_choices_on_measured_workloads(shape, dt, out, want):
+    d = desc(*shape, dt=dt, out=out)
+    best = L.rank_configs(d)[0]
+    bm, kernel, sched = want
+    assert (best.kernel, best.sched) == (kernel, sched)
+    if bm is not None:
+        assert best.bm == bm
+    # gemm_create with everything left to the planner takes the best candidate
+    info = L.Plan(d).info
+    assert (info.bm, info.kernel, info.sched) == (best.bm, best.kernel, best.sched)
+
+
+def test_zero_depth_keeps_to_the_kernel_that_runs_it():
+    ranked = L.rank_configs(desc(512, 512, 0, out=L.GEMM_F32))
+    assert ranked and all(c.kernel == 0 for c in ranked)
+
+
+def test_group_choice_minimises_operand_strips():
+    # each XCD runs 32 consecutive tiles: G x 32/G block -> G + 32/G strips, least at G = 4 or 8;
+    # the larger wins the tie
+    info = L.Plan(desc(4096, 4096, 4096)).info
+    assert info.group == 8
+    assert L.rank_configs(desc(4096, 4096, 4096))[0].group == 8
+    # few tile rows: G never exceeds them
+    few = L.Plan(desc(512, 8192, 4096)).info
+    assert few.group <= few.mt
+    # an explicit G is kept
+    assert L.Plan(desc(4096, 4096, 4096, group=16)).info.group == 16
+    for G in (1, 2, 4, 8, 16, 32):
+        strips = min(G, 16) + math.ceil(32 / min(G, 16))
+        assert strips >= 12
+
+
+def test_rank_validation():
+    lib = L.load()
+    import ctypes
+    n = ctypes.c_size_t()
+    assert lib.gemm_rank_configs(None, None, 0, ctypes.byref(n)) == L.GEMM_ERR_INVALID_ARG
+    d = desc(4096, 4096, 4096)
+    assert lib.gemm_rank_configs(ctypes.byref(d), None, 0, ctypes.byref(n)) == L.GEMM_ERR_CAPACITY
+    assert n.value >= 2
+    bad = desc(-1, 4, 4)
+    assert lib.gemm_rank_configs(ctypes.byref(bad), None, 0, ctypes.byref(n)) == \
+        L.GEMM_ERR_INVALID_ARG
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("shape,dt,out", [
+    ((4096, 4096, 4096), L.GEMM_BF16, L.GEMM_BF16),
+    ((4096, 14336, 4096), L.GEMM_BF16, L.GEMM_BF16),
+    ((512, 512, 65536), L.GEMM_BF16, L.GEMM_F32),
+    ((2048, 2048, 2048), L.GEMM_BF16, L.GEMM_BF16),
+    ((1024, 1024, 16384), L.GEMM_FP8_E4M3, L.GEMM_BF16),
+])
+def test_pick_is_close_to_the_fastest_candidate(shape, dt, out):
+    """Each candidate the model ranks runs as a forced plan; the model's pick must be within 15 %
+    of the fastest measured (the model ignores launch and fixup latencies)."""
+    import torch
+    dev = torch.device("cuda:0")
+    M, N, K = shape
+    eb = 2 if dt == L.GEMM_BF16 else 1
+    A = torch.randint(0, 256, (M * K * eb,), dtype=torch.uint8, device=dev) & 0x3f
+    B = torch.randint(0, 256, (N * K * eb,), dtype=torch.uint8, device=dev) & 0x3f
+    C = torch.empty(M * N * (2 if out == L.GEMM_BF16 else 4), dtype=torch.uint8, device=dev)
+    sa = torch.ones(1, dtype=torch.float32, device=dev)
+    d = L.make_desc(M, N, K, dt, out, L.GEMM_MAP_GROUPED_M, 0, L.GEMM_SCHED_AUTO, 0)
+    ranked = L.rank_configs(d)
+    times = []
+    for c in ranked:
+        flags = L.GEMM_FLAG_COOPERATIVE if c.kernel == 0 else 0
+        plan = L.Plan(L.make_desc(M, N, K, dt, out, L.GEMM_MAP_GROUPED_M, c.group, c.sched, 0,
+                                  c.bm, c.bn, c.bk, flags))
+        ws = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device=dev)
+        run = lambda: plan.run(A, B, C, sa, sa, ws if plan.workspace_bytes else None)
+        t0 = time.time()
+        while time.time() - t0 < 0.2:
+            run()
+            torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 20)
+    print(f"{shape}: " + ", ".join(f"{c.bm}/{c.kernel}/{c.sched}: {t * 1e3:.1f} us"
+                                   for c, t in zip(ranked, times)), flush=True)
+    assert times[0] <= 1.15 * min(times), "the model's pick is much slower than the fastest"
