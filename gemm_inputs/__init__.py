@@ -114,6 +114,13 @@ def make_operands(M, N, K, dtype="bf16", dist_a=("uniform",), dist_b=("uniform",
     raise ValueError(f"unknown dtype {dtype}")
 
 
+def make_vector(n, seed, dist=("normal", 1.0)):
+    """A seeded fp32 vector of length n (a bias), as a numpy float32 array."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed))
+    return _draw(gen, (int(n),), dist).numpy().copy()
+
+
 def make_workload(name_or_wl):
     wl = WORKLOADS[name_or_wl] if isinstance(name_or_wl, str) else name_or_wl
     return make_operands(wl.M, wl.N, wl.K, wl.dtype, wl.dist_a, wl.dist_b, wl.seed)

@@ -7,7 +7,10 @@ only the seeded input generators in gemm_inputs/, which hold none of the GEMM's 
 Contents
   gemm_ref / gemm_ref_sampled   fp64 C = A x B over the raw operand bytes (gemm_oracle.c)
   decode_bf16 / decode_e4m3     exact operand decoders (gemm_oracle.c)
-  encode_e4m3                   nearest-even, saturating e4m3 encoder (checks the generator)
+  encode_e4m3 / _f64 / _array   nearest-even, saturating e4m3 encoder (checks the generator,
+                                expected codes of an e4m3 output)
+  epilogue                      the fused epilogue: bias, activation, amax, output quantisation
+                                (oracle/epilogue.py)
   tolerance                     the per-element acceptance bound
   schedule                      CPU enumeration of the tile mapping, worker assignment and
                                 Stream-K splits (oracle/schedule.py)
@@ -46,6 +49,10 @@ def _load():
     lib.oracle_decode_e4m3.restype = dbl
     lib.oracle_encode_e4m3.argtypes = [ctypes.c_float]
     lib.oracle_encode_e4m3.restype = ctypes.c_uint8
+    lib.oracle_encode_e4m3_f64.argtypes = [dbl]
+    lib.oracle_encode_e4m3_f64.restype = ctypes.c_uint8
+    lib.oracle_encode_e4m3_array.argtypes = [vp, vp, i64]
+    lib.oracle_encode_e4m3_array.restype = None
     lib.oracle_gemm.argtypes = [i64, i64, i64, i32, vp, i32, vp, i32, dbl, dbl, vp, i32]
     lib.oracle_gemm.restype = i32
     lib.oracle_gemm_sampled.argtypes = [i64, i64, i64, i32, vp, i32, vp, i32, dbl, dbl,
@@ -73,7 +80,21 @@ def decode_e4m3(code: int) -> float:
 
 
 def encode_e4m3(x: float) -> int:
+    """e4m3 code of x rounded to binary32 first (the generator's fp32 quantisation)."""
     return int(_load().oracle_encode_e4m3(float(x)))
+
+
+def encode_e4m3_f64(x: float) -> int:
+    """e4m3 code of x at full double precision."""
+    return int(_load().oracle_encode_e4m3_f64(float(x)))
+
+
+def encode_e4m3_array(x) -> np.ndarray:
+    """e4m3 codes (uint8, same shape) of an array of doubles, each at full double precision."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _load().oracle_encode_e4m3_array(x.ctypes.data, out.ctypes.data, x.size)
+    return out
 
 
 def _raw(arr, dtype):
@@ -140,3 +161,6 @@ def max_abs_decoded(raw, dtype, scale=1.0):
     bits = raw.reshape(-1).astype(np.uint32) << np.uint32(16)
     vals = np.abs(bits.view(np.float32).astype(np.float64))
     return float(vals.max(initial=0.0)) * float(scale)
+
+
+from . import epilogue  # noqa: E402,F401  (re-exported; uses the encoders above)

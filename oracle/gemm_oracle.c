@@ -18,9 +18,10 @@
  *     finite magnitude is 448 ("WGMMA part 2" lesson, sections 9-10).
  *   - per-tensor FP32 scales multiply the exact integer-grid sum: C = s_a * s_b * sum q_a q_b
  *     ("WGMMA part 2" lesson, section 11, tensor-wise scaling).
- *   - oracle_encode_e4m3: round-to-nearest-even onto the e4m3 grid with saturation to +-448
- *     ("WGMMA part 2" lesson, sections 10 and 13: satfinite clamps out-of-range values to the
- *     signed maximum normal).  Used only to check the input generator's quantised bytes.
+ *   - oracle_encode_e4m3 (binary32 input) / _f64 / _array: round-to-nearest-even onto the e4m3
+ *     grid with saturation to +-448 ("WGMMA part 2" lesson, sections 10 and 13: satfinite clamps
+ *     out-of-range values to the signed maximum normal).  Checks the input generator's quantised
+ *     bytes and gives the expected codes of an e4m3 output (fused-epilogue quantisation).
  *
  * Layout: A row-major means a(m,k) = A[m*K + k]; A column-major means a(m,k) = A[k*M + m].
  * B row-major (K x N) means b(k,n) = B[k*N + n]; B column-major means b(k,n) = B[n*K + k].
@@ -54,9 +55,10 @@ double oracle_decode_e4m3(uint8_t code) {
   return sign ? -mag : mag;
 }
 
-/* Nearest e4m3 code to x, ties to the code with an even mantissa, magnitudes above 448 saturate. */
-uint8_t oracle_encode_e4m3(float xf) {
-  double x = (double)xf;
+/* Nearest e4m3 code to x, ties to the code with an even mantissa, magnitudes above 448 saturate.
+ * x is taken at full double precision, so a value just past a rounding midpoint rounds away from
+ * it even when the nearest binary32 value would sit on the midpoint. */
+uint8_t oracle_encode_e4m3_f64(double x) {
   uint8_t sign = 0;
   if (isnan(x)) return 0x7F;
   if (signbit(x)) {
@@ -76,6 +78,13 @@ uint8_t oracle_encode_e4m3(float xf) {
     }
   }
   return sign | (uint8_t)best;
+}
+
+uint8_t oracle_encode_e4m3(float xf) { return oracle_encode_e4m3_f64((double)xf); }
+
+/* out[i] = oracle_encode_e4m3_f64(x[i]) for i < n. */
+void oracle_encode_e4m3_array(const double *x, uint8_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_encode_e4m3_f64(x[i]);
 }
 
 static double decode_one(int dtype, const void *p, int64_t idx) {
