@@ -9,31 +9,45 @@ from ._lib import (GemmDesc, GemmError, Plan, make_desc, load,  # noqa: F401
                    GEMM_MAP_GROUPED_M, GEMM_MAP_GROUPED_N, GEMM_SCHED_STATIC,
                    GEMM_SCHED_PERSISTENT, GEMM_SCHED_STREAMK, GEMM_SCHED_AUTO, GEMM_FLAG_TRACE,
                    GEMM_FLAG_NO_XCD_REMAP, GEMM_FLAG_STREAMK_CHAIN, GEMM_FLAG_PINGPONG,
-                   GEMM_FLAG_COOPERATIVE, GEMM_FLAG_REGSTAGED, GEMM_FLAG_WIDE)
+                   GEMM_FLAG_COOPERATIVE, GEMM_FLAG_REGSTAGED, GEMM_FLAG_WIDE,
+                   GEMM_EPI_BIAS_ROW, GEMM_EPI_BIAS_COL, GEMM_EPI_RELU, GEMM_EPI_GELU,
+                   GEMM_EPI_SILU, GEMM_EPI_AMAX, GemmEpilogueArgs)
 
 MAPPINGS = {"linear_n": GEMM_MAP_LINEAR_N, "linear_m": GEMM_MAP_LINEAR_M,
             "grouped_m": GEMM_MAP_GROUPED_M, "grouped_n": GEMM_MAP_GROUPED_N}
 SCHEDS = {"static": GEMM_SCHED_STATIC, "persistent": GEMM_SCHED_PERSISTENT,
           "streamk": GEMM_SCHED_STREAMK, "auto": GEMM_SCHED_AUTO}
+ACTIVATIONS = {None: 0, "relu": GEMM_EPI_RELU, "gelu": GEMM_EPI_GELU, "silu": GEMM_EPI_SILU}
+OUT_DTYPES = {"f32": GEMM_F32, "bf16": GEMM_BF16, "e4m3": GEMM_FP8_E4M3}
 
 
 def gemm(A, B, out_dtype="f32", scale_a=None, scale_b=None, mapping="grouped_m", group=8,
-         sched="auto", tile=0, flags=0):
-    """C = alpha * A x B for torch device tensors: A (M, K) row-major; B given as (N, K), i.e. the
-    K x N operand in column-major storage; bf16 or uint8-coded e4m3 (then scale_a / scale_b are
-    one-element float32 device tensors).  Returns C (M, N) in float32 or bfloat16."""
+         sched="auto", tile=0, flags=0, bias_row=None, bias_col=None, activation=None,
+         scale_d=None, amax=None):
+    """D = epilogue(alpha * A x B) for torch device tensors: A (M, K) row-major; B given as (N, K),
+    i.e. the K x N operand in column-major storage; bf16 or uint8-coded e4m3 (then scale_a /
+    scale_b are one-element float32 device tensors).  Optional fused epilogue: a float32 bias per
+    row (M) or per column (N), an activation ("relu", "gelu", "silu"), amax (a one-element float32
+    device tensor the kernel max-combines max |Y| into), and out_dtype "e4m3" (uint8 codes of
+    Y / scale_d, scale_d a one-element float32 device tensor).  Returns C (M, N): float32,
+    bfloat16, or uint8 e4m3 codes."""
     import torch
     M, K = A.shape
     N = B.shape[0]
     fp8 = A.dtype in (torch.uint8, torch.float8_e4m3fn)
-    desc = make_desc(M, N, K, GEMM_FP8_E4M3 if fp8 else GEMM_BF16,
-                     GEMM_BF16 if out_dtype == "bf16" else GEMM_F32, MAPPINGS[mapping], group,
-                     SCHEDS[sched], 0, tile, tile, 0, flags)
+    epi = ACTIVATIONS[activation]
+    epi |= GEMM_EPI_BIAS_ROW if bias_row is not None else 0
+    epi |= GEMM_EPI_BIAS_COL if bias_col is not None else 0
+    epi |= GEMM_EPI_AMAX if amax is not None else 0
+    desc = make_desc(M, N, K, GEMM_FP8_E4M3 if fp8 else GEMM_BF16, OUT_DTYPES[out_dtype],
+                     MAPPINGS[mapping], group, SCHEDS[sched], 0, tile, tile, 0, flags,
+                     epilogue=epi)
     plan = Plan(desc)
-    C = torch.empty((M, N), device=A.device,
-                    dtype=torch.bfloat16 if out_dtype == "bf16" else torch.float32)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8}[out_dtype]
+    C = torch.empty((M, N), device=A.device, dtype=dt)
     ws = None
     if plan.workspace_bytes:
         ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=A.device)
-    plan.run(A, B, C, scale_a, scale_b, ws)
+    plan.run(A, B, C, scale_a, scale_b, ws, bias=bias_row if bias_row is not None else bias_col,
+             scale_d=scale_d, amax=amax)
     return C

@@ -27,9 +27,15 @@ GEMM_FLAG_REGSTAGED = 0x20
 GEMM_FLAG_WIDE = 0x40
 GEMM_FLAG_TEST_SKIP_PUBLISH = 0x100
 GEMM_DEVICE_OK, GEMM_DEVICE_ERR_SPIN = 0, 1
+GEMM_EPI_BIAS_ROW = 0x1
+GEMM_EPI_BIAS_COL = 0x2
+GEMM_EPI_RELU = 0x4
+GEMM_EPI_GELU = 0x8
+GEMM_EPI_SILU = 0x10
+GEMM_EPI_AMAX = 0x20
 
-EXPORTS = ("gemm_create", "gemm_workspace_bytes", "gemm_plan_get", "gemm_run", "gemm_destroy",
-           "gemm_schedule_enumerate", "gemm_rank_configs", "gemm_status_string")
+EXPORTS = ("gemm_create", "gemm_workspace_bytes", "gemm_plan_get", "gemm_run", "gemm_run_ex",
+           "gemm_destroy", "gemm_schedule_enumerate", "gemm_rank_configs", "gemm_status_string")
 
 
 class GemmDesc(ctypes.Structure):
@@ -39,7 +45,12 @@ class GemmDesc(ctypes.Structure):
                 ("mapping", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("sched", ctypes.c_int32), ("num_workers", ctypes.c_int32),
                 ("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("epilogue", ctypes.c_uint32)]
+
+
+class GemmEpilogueArgs(ctypes.Structure):
+    _fields_ = [("bias", ctypes.c_void_p), ("scale_d", ctypes.c_void_p),
+                ("amax", ctypes.c_void_p)]
 
 
 class GemmWorkItem(ctypes.Structure):
@@ -85,6 +96,8 @@ def load():
     lib.gemm_workspace_bytes.argtypes = [vp, ctypes.POINTER(sz)]
     lib.gemm_plan_get.argtypes = [vp, ctypes.POINTER(GemmPlanInfo)]
     lib.gemm_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gemm_run_ex.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(GemmEpilogueArgs), vp, sz,
+                                vp]
     lib.gemm_destroy.argtypes = [vp]
     lib.gemm_schedule_enumerate.argtypes = [vp, ctypes.POINTER(GemmWorkItem), sz,
                                             ctypes.POINTER(sz)]
@@ -113,9 +126,9 @@ def _check(status, where):
 
 def make_desc(M, N, K, dtype_ab=GEMM_BF16, dtype_c=GEMM_F32, mapping=GEMM_MAP_LINEAR_N, group=1,
               sched=GEMM_SCHED_PERSISTENT, num_workers=0, bm=0, bn=0, bk=0, flags=0,
-              layout_a=GEMM_ROW_MAJOR, layout_b=GEMM_COL_MAJOR):
+              layout_a=GEMM_ROW_MAJOR, layout_b=GEMM_COL_MAJOR, epilogue=0):
     return GemmDesc(M, N, K, dtype_ab, dtype_c, layout_a, layout_b, mapping, group, sched,
-                    num_workers, bm, bn, bk, flags)
+                    num_workers, bm, bn, bk, flags, epilogue)
 
 
 def rank_configs(desc):
@@ -179,15 +192,24 @@ class Plan:
         return load().gemm_run(self.handle, A, B, C, scale_a or None, scale_b or None,
                                workspace or None, workspace_bytes, stream or None)
 
-    def run(self, A, B, C, scale_a=None, scale_b=None, workspace=None, stream=None):
-        """A, B, C, scales, workspace: torch tensors on the GPU; stream: torch.cuda.Stream."""
+    def run_ex_raw(self, A, B, C, scale_a=0, scale_b=0, bias=0, scale_d=0, amax=0, workspace=0,
+                   workspace_bytes=0, stream=0, epi_null=False):
+        """gemm_run_ex with raw integer device pointers (epi_null passes a NULL epilogue-args
+        pointer); returns the gemm_status."""
+        epi = None if epi_null else ctypes.byref(
+            GemmEpilogueArgs(bias or None, scale_d or None, amax or None))
+        return load().gemm_run_ex(self.handle, A, B, C, scale_a or None, scale_b or None, epi,
+                                  workspace or None, workspace_bytes, stream or None)
+
+    def run(self, A, B, C, scale_a=None, scale_b=None, workspace=None, stream=None, bias=None,
+            scale_d=None, amax=None):
+        """A, B, C, scales, workspace, bias, amax: torch tensors on the GPU; stream:
+        torch.cuda.Stream.  bias / scale_d / amax feed the fused epilogue (gemm_run_ex)."""
         import torch
         if stream is None:
             stream = torch.cuda.current_stream()
-        ws_ptr = workspace.data_ptr() if workspace is not None else 0
+        ptr = lambda t: t.data_ptr() if t is not None else 0
         ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        st = self.run_raw(A.data_ptr(), B.data_ptr(), C.data_ptr(),
-                          scale_a.data_ptr() if scale_a is not None else 0,
-                          scale_b.data_ptr() if scale_b is not None else 0,
-                          ws_ptr, ws_len, stream.cuda_stream)
-        _check(st, "gemm_run")
+        st = self.run_ex_raw(ptr(A), ptr(B), ptr(C), ptr(scale_a), ptr(scale_b), ptr(bias),
+                             ptr(scale_d), ptr(amax), ptr(workspace), ws_len, stream.cuda_stream)
+        _check(st, "gemm_run_ex")

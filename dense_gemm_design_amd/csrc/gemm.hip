@@ -43,12 +43,23 @@ using CfgFp8_256w = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1, 16>;  // 16 x 16 
 typedef hipError_t (*launch_fn)(const KernelArgs &, int grid, bool ragged_k, hipStream_t);
 typedef const void *(*kernel_fn)();
 
+// A plan with a fused epilogue (EPI_* bits or an e4m3 output) launches the kernels' FUSED
+// instantiation; all others the plain one.
+bool fused_args(const KernelArgs &a) { return a.epi != 0 || a.out_fp8; }
+
 template <class CFG>
 hipError_t launch_cfg(const KernelArgs &a, int grid, bool ragged_k, hipStream_t s) {
-  if (ragged_k)
-    hipLaunchKernelGGL((gemm_kernel<CFG, true>), dim3(grid), dim3(CFG::THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL((gemm_kernel<CFG, false>), dim3(grid), dim3(CFG::THREADS), 0, s, a);
+  const dim3 g(grid), t(CFG::THREADS);
+  if (fused_args(a)) {
+    if (ragged_k)
+      hipLaunchKernelGGL((gemm_kernel<CFG, true, true>), g, t, 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_kernel<CFG, false, true>), g, t, 0, s, a);
+  } else if (ragged_k) {
+    hipLaunchKernelGGL((gemm_kernel<CFG, true>), g, t, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<CFG, false>), g, t, 0, s, a);
+  }
   return hipGetLastError();
 }
 template <class CFG>
@@ -81,19 +92,26 @@ const void *kernel_of_vs() {
 }
 
 // k-tiles one MFMA deep (e4m3 16 x 16 x 128) take the single-A-buffer form of the schedule
-template <class CFG, bool RAGGED_K>
+template <class CFG, bool RAGGED_K, bool FUSED = false>
 constexpr auto wide_kernel() {
   if constexpr (CFG::KSUB == 1)
-    return &gemm_kernel_wide1<CFG, RAGGED_K>;
+    return &gemm_kernel_wide1<CFG, RAGGED_K, FUSED>;
   else
-    return &gemm_kernel_wide<CFG, RAGGED_K>;
+    return &gemm_kernel_wide<CFG, RAGGED_K, FUSED>;
 }
 template <class CFG>
 hipError_t launch_wide(const KernelArgs &a, int grid, bool ragged_k, hipStream_t s) {
-  if (ragged_k)
-    hipLaunchKernelGGL((wide_kernel<CFG, true>()), dim3(grid), dim3(CFG::THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL((wide_kernel<CFG, false>()), dim3(grid), dim3(CFG::THREADS), 0, s, a);
+  const dim3 g(grid), t(CFG::THREADS);
+  if (fused_args(a)) {
+    if (ragged_k)
+      hipLaunchKernelGGL((wide_kernel<CFG, true, true>()), g, t, 0, s, a);
+    else
+      hipLaunchKernelGGL((wide_kernel<CFG, false, true>()), g, t, 0, s, a);
+  } else if (ragged_k) {
+    hipLaunchKernelGGL((wide_kernel<CFG, true>()), g, t, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((wide_kernel<CFG, false>()), g, t, 0, s, a);
+  }
   return hipGetLastError();
 }
 template <class CFG>
@@ -153,6 +171,19 @@ constexpr int kTraceCap = 64;
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t align_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
+// Known GEMM_EPI_* bits, at most one bias vector and at most one activation.
+bool epilogue_valid(uint32_t e) {
+  const uint32_t all = GEMM_EPI_BIAS_ROW | GEMM_EPI_BIAS_COL | GEMM_EPI_RELU | GEMM_EPI_GELU |
+                       GEMM_EPI_SILU | GEMM_EPI_AMAX;
+  if (e & ~all) return false;
+  if (__builtin_popcount(e & (GEMM_EPI_BIAS_ROW | GEMM_EPI_BIAS_COL)) > 1) return false;
+  return __builtin_popcount(e & (GEMM_EPI_RELU | GEMM_EPI_GELU | GEMM_EPI_SILU)) <= 1;
+}
+static_assert(GEMM_EPI_BIAS_ROW == EPI_BIAS_ROW && GEMM_EPI_BIAS_COL == EPI_BIAS_COL &&
+                  GEMM_EPI_RELU == EPI_RELU && GEMM_EPI_GELU == EPI_GELU &&
+                  GEMM_EPI_SILU == EPI_SILU && GEMM_EPI_AMAX == EPI_AMAX,
+              "epilogue bits shared with the kernels");
+
 // ---- kernel-configuration heuristic -----------------------------------------------------------
 // The cost model of "DeepGEMM on SM90" (section "Kernel Configuration Heuristic"), re-fitted to
 // gfx950.  Per candidate, whole-GEMM clocks on three sides:
@@ -210,7 +241,9 @@ struct ModelCand {
 // from the device when num_workers == 0.
 int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
   const int dt = d.dtype_ab == GEMM_BF16 ? DT_BF16 : DT_FP8;
-  const double eb = dt == DT_BF16 ? 2.0 : 1.0, ec = d.dtype_c == GEMM_BF16 ? 2.0 : 4.0;
+  const double eb = dt == DT_BF16 ? 2.0 : 1.0, ec = d.dtype_c == GEMM_BF16       ? 2.0
+                                                    : d.dtype_c == GEMM_FP8_E4M3 ? 1.0
+                                                                                 : 4.0;
   const ModelCand cands[] = {{KIND_WIDE, 256, 256, GEMM_SCHED_PERSISTENT},
                              {KIND_COOP, 128, 128, GEMM_SCHED_PERSISTENT},
                              {KIND_COOP, 128, 128, GEMM_SCHED_STREAMK},
@@ -312,7 +345,7 @@ const char *gemm_status_string(int status) {
     case GEMM_OK: return "ok";
     case GEMM_ERR_INVALID_ARG: return "invalid argument";
     case GEMM_ERR_UNSUPPORTED: return "unsupported problem or configuration";
-    case GEMM_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
+    case GEMM_ERR_ALIGNMENT: return "device pointer misaligned";
     case GEMM_ERR_WORKSPACE: return "workspace missing or too small";
     case GEMM_ERR_HIP: return "HIP runtime error";
     case GEMM_ERR_CAPACITY: return "output buffer too small";
@@ -326,7 +359,9 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   const gemm_desc d = *desc;
   if (d.M < 0 || d.N < 0 || d.K < 0) return GEMM_ERR_INVALID_ARG;
   if (d.dtype_ab != GEMM_BF16 && d.dtype_ab != GEMM_FP8_E4M3) return GEMM_ERR_INVALID_ARG;
-  if (d.dtype_c != GEMM_F32 && d.dtype_c != GEMM_BF16) return GEMM_ERR_INVALID_ARG;
+  if (d.dtype_c != GEMM_F32 && d.dtype_c != GEMM_BF16 && d.dtype_c != GEMM_FP8_E4M3)
+    return GEMM_ERR_INVALID_ARG;
+  if (!epilogue_valid(d.epilogue)) return GEMM_ERR_INVALID_ARG;
   if ((d.layout_a != GEMM_ROW_MAJOR && d.layout_a != GEMM_COL_MAJOR) ||
       (d.layout_b != GEMM_ROW_MAJOR && d.layout_b != GEMM_COL_MAJOR))
     return GEMM_ERR_INVALID_ARG;
@@ -359,6 +394,9 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   const bool force_dp = force_kind == KIND_PP || force_kind == KIND_VS || force_kind == KIND_WIDE;
   if (force_dp && (d.K == 0 || d.sched == GEMM_SCHED_STREAMK || d.sched == GEMM_SCHED_AUTO))
     return GEMM_ERR_UNSUPPORTED;
+  // the fused epilogue runs on the wide-wave and cooperative kernels
+  const bool fused = d.epilogue != 0 || d.dtype_c == GEMM_FP8_E4M3;
+  if (fused && (force_kind == KIND_PP || force_kind == KIND_VS)) return GEMM_ERR_UNSUPPORTED;
 
   // Tile shape and scheduler: the cost model when everything is left to the planner, else
   // 256 x 256 unless asked otherwise or the problem has too few big tiles.
@@ -417,7 +455,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (force_kind < 0 && d.K > 0 && (sched == GEMM_SCHED_STATIC || sched == GEMM_SCHED_PERSISTENT)) {
     if (by_kind[KIND_WIDE])
       k = by_kind[KIND_WIDE];
-    else if (by_kind[KIND_PP])
+    else if (by_kind[KIND_PP] && !fused)
       k = by_kind[KIND_PP];
   }
   const int64_t Kt = cdiv(d.K, k->bk);  // the kernel's own k-tile depth
@@ -499,6 +537,8 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   a.ldc = d.N;
   a.sp = sp;
   a.out_bf16 = d.dtype_c == GEMM_BF16;
+  a.out_fp8 = d.dtype_c == GEMM_FP8_E4M3;
+  a.epi = d.epilogue;
   a.flags = d.flags;
   a.trace_cap = kTraceCap;
   a.max_spin = (d.flags & GEMM_FLAG_TEST_SKIP_PUBLISH) ? kTestSpin : kDefaultSpin;
@@ -537,7 +577,9 @@ int gemm_rank_configs(const gemm_desc *desc, gemm_config_score *items, size_t ca
   const gemm_desc d = *desc;
   if (d.M < 0 || d.N < 0 || d.K < 0 || d.num_workers < 0 || d.group < 0) return GEMM_ERR_INVALID_ARG;
   if (d.dtype_ab != GEMM_BF16 && d.dtype_ab != GEMM_FP8_E4M3) return GEMM_ERR_INVALID_ARG;
-  if (d.dtype_c != GEMM_F32 && d.dtype_c != GEMM_BF16) return GEMM_ERR_INVALID_ARG;
+  if (d.dtype_c != GEMM_F32 && d.dtype_c != GEMM_BF16 && d.dtype_c != GEMM_FP8_E4M3)
+    return GEMM_ERR_INVALID_ARG;
+  if (!epilogue_valid(d.epilogue)) return GEMM_ERR_INVALID_ARG;
   if (d.mapping < GEMM_MAP_LINEAR_N || d.mapping > GEMM_MAP_GROUPED_N) return GEMM_ERR_INVALID_ARG;
   std::vector<gemm_config_score> ranked;
   const int st = rank_configs(d, ranked);
@@ -562,7 +604,24 @@ int gemm_plan_get(gemm_handle h, gemm_plan_info *info) {
 
 int gemm_run(gemm_handle h, const void *A, const void *B, void *C, const float *scale_a,
              const float *scale_b, void *workspace, size_t workspace_bytes, void *stream) {
+  return gemm_run_ex(h, A, B, C, scale_a, scale_b, nullptr, workspace, workspace_bytes, stream);
+}
+
+int gemm_run_ex(gemm_handle h, const void *A, const void *B, void *C, const float *scale_a,
+                const float *scale_b, const gemm_epilogue_args *epi, void *workspace,
+                size_t workspace_bytes, void *stream) {
   if (!h) return GEMM_ERR_INVALID_ARG;
+  // epilogue operands: checked before the empty-output return, so a bad call fails alike
+  const uint32_t ebits = h->d.epilogue;
+  const bool need_bias = ebits & (GEMM_EPI_BIAS_ROW | GEMM_EPI_BIAS_COL);
+  const bool need_amax = ebits & GEMM_EPI_AMAX;
+  const bool out_fp8 = h->d.dtype_c == GEMM_FP8_E4M3;
+  if ((need_bias || need_amax || out_fp8) && !epi) return GEMM_ERR_INVALID_ARG;
+  if ((need_bias && !epi->bias) || (need_amax && !epi->amax) || (out_fp8 && !epi->scale_d))
+    return GEMM_ERR_INVALID_ARG;
+  if ((need_bias && ((uintptr_t)epi->bias & 15)) || (need_amax && ((uintptr_t)epi->amax & 3)) ||
+      (out_fp8 && ((uintptr_t)epi->scale_d & 3)))
+    return GEMM_ERR_ALIGNMENT;
   if (h->info.grid == 0) return GEMM_OK;  // empty output: nothing to compute
   if (!C || (h->d.K > 0 && (!A || !B))) return GEMM_ERR_INVALID_ARG;  // K == 0 reads no operand
   const bool fp8 = h->d.dtype_ab == GEMM_FP8_E4M3;
@@ -581,6 +640,9 @@ int gemm_run(gemm_handle h, const void *A, const void *B, void *C, const float *
   a.C = (char *)C;
   a.scale_a = scale_a;
   a.scale_b = scale_b;
+  if (need_bias) a.bias = epi->bias;
+  if (need_amax) a.amax = epi->amax;
+  if (out_fp8) a.scale_d = epi->scale_d;
   if (h->ws_bytes > 0) {
     char *ws = (char *)workspace;
     a.partials = (float *)(ws + h->partial_off);

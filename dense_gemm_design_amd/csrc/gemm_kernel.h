@@ -78,6 +78,11 @@ struct KernelArgs {
   int32_t trace_cap;
   int32_t max_spin;
   int32_t sk_mode;         // SK_CHAIN or SK_SEPARATE
+  uint32_t epi;            // fused epilogue: EPI_* bits (0 = alpha and the cast only)
+  const float *bias;       // EPI_BIAS_ROW: M floats, EPI_BIAS_COL: N floats
+  const float *scale_d;    // e4m3 output: its dequantisation scale (a code q stands for s_d * q)
+  float *amax;             // EPI_AMAX: max |Y| is folded in (atomic max on the float's bits)
+  int32_t out_fp8;         // C holds e4m3 codes
   int32_t pad_;
 };
 
@@ -417,6 +422,137 @@ __device__ __forceinline__ void store_quad(const KernelArgs &args, int64_t m, in
   }
 }
 
+// ---- fused epilogue ("H100 Kernel Design" lesson, section 12) ------------------------------
+// Z = alpha * Acc + bias, Y = act(Z), amax over Y, then the cast -- for an e4m3 output the code
+// of Y / scale_d -- and the store, in the order of section 12.2 (steps 2 to 7).  Kernels take
+// this path in their FUSED instantiation, chosen at launch when EPI_* bits or an e4m3 output
+// are asked for; every other launch runs the plain epilogues above and below.
+enum : uint32_t {
+  EPI_BIAS_ROW = 0x1u,
+  EPI_BIAS_COL = 0x2u,
+  EPI_RELU = 0x4u,
+  EPI_GELU = 0x8u,
+  EPI_SILU = 0x10u,
+  EPI_AMAX = 0x20u
+};
+
+// State of the fused epilogue in one lane: the output's inverse scale and the running max |Y|.
+struct EpiCtx {
+  float inv_d;  // 1 / scale_d for an e4m3 output, else 1
+  float am;     // max |Y| over the elements this lane has written
+};
+
+__device__ __forceinline__ EpiCtx epi_init(const KernelArgs &args) {
+  return EpiCtx{args.out_fp8 ? 1.0f / *args.scale_d : 1.0f, 0.0f};
+}
+
+// erf(x) by the rational approximation of Abramowitz and Stegun, formula 7.1.26 (after Hastings):
+// erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2), t = 1 / (1 + p x) for x >= 0,
+// odd in x, absolute error below 1.5e-7 -- inline, where a library call would make the caller
+// save the whole accumulator tile around it.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+  float poly = 1.061405429f;
+  poly = poly * t - 1.453152027f;
+  poly = poly * t + 1.421413741f;
+  poly = poly * t - 0.284496736f;
+  poly = poly * t + 0.254829592f;
+  poly = poly * t;
+  // exp(-x^2) = 2^(-x^2 log2 e); underflows to 0 for |x| > ~9.4, where erf is 1 in fp32
+  const float r = 1.0f - poly * __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
+  return __builtin_copysignf(r, x);
+}
+
+// GELU in its exact form z Phi(z) = z (1 + erf(z / sqrt 2)) / 2
+__device__ __forceinline__ float act_gelu(float z) {
+  return 0.5f * z * (1.0f + erf_as(z * 0.70710678118654752f));
+}
+// SiLU z sigmoid(z) = z / (1 + exp(-z)); exp and reciprocal at hardware precision (a few ulp).
+// exp(-z) = inf for very negative z gives -0, and 0 for very large z gives z.
+__device__ __forceinline__ float act_silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
+
+// Y = act(Z) for one quad (the uniform EPI_* bits choose the branch) and |Y| into the amax
+__device__ __forceinline__ f32x4 epi_act(uint32_t epi, f32x4 z, float &am) {
+  if (epi & EPI_RELU) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = z[e] < 0.0f ? 0.0f : z[e];  // NaN stays NaN
+  } else if (epi & EPI_GELU) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = act_gelu(z[e]);
+  } else if (epi & EPI_SILU) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = act_silu(z[e]);
+  }
+  am = fmaxf(am, fmaxf(fmaxf(fabsf(z[0]), fabsf(z[1])), fmaxf(fabsf(z[2]), fabsf(z[3]))));
+  // fold each quad in as it goes: left free, the compiler regroups the max over the whole
+  // tile and keeps the |Y| values live across the epilogue (spilling the kernel)
+  asm volatile("" : "+v"(am));
+  return z;
+}
+
+// e4m3 codes of four values already divided by the output scale, byte e = value e: clamped to
+// +-448, the format's largest finite magnitude (NaN passes the comparisons unchanged), then
+// rounded to nearest-even by the hardware conversion.
+__device__ __forceinline__ uint32_t pack_e4m3x4(f32x4 v) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = v[e] > 448.0f ? 448.0f : (v[e] < -448.0f ? -448.0f : v[e]);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+  return (uint32_t)w;
+}
+
+// Fused store of one accumulator quad: 4 consecutive n of row m (n a multiple of 4, so a column
+// bias quad is one aligned 16-byte load).
+__device__ __forceinline__ void store_quad_fused(const KernelArgs &args, int64_t m, int64_t n,
+                                                 f32x4 v, float alpha, EpiCtx &ec) {
+  if (m >= args.M || n >= args.N) return;
+  v = v * alpha;
+  if (args.epi & EPI_BIAS_ROW) v = v + args.bias[m];
+  if (args.epi & EPI_BIAS_COL) v = v + *(const f32x4 *)(args.bias + n);
+  v = epi_act(args.epi, v, ec.am);
+  if (args.out_fp8) {
+    *(uint32_t *)(args.C + m * args.ldc + n) = pack_e4m3x4(v * ec.inv_d);
+  } else if (args.out_bf16) {
+    u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *(u32x2 *)(args.C + (m * args.ldc + n) * 2) = pk;
+  } else {
+    *(f32x4 *)(args.C + (m * args.ldc + n) * 4) = v;
+  }
+}
+
+template <bool FUSED, class CFG>
+__device__ __forceinline__ void store_quad_sel(const KernelArgs &args, int64_t m, int64_t n,
+                                               f32x4 v, float alpha, EpiCtx &ec) {
+  if constexpr (FUSED)
+    store_quad_fused(args, m, n, v, alpha, ec);
+  else
+    store_quad<CFG>(args, m, n, v, alpha);
+}
+
+// The workgroup's largest amax, folded into *amax by one atomic max on its bit pattern (non-negative
+// floats order like their bits).  red: WAVES floats of LDS that no wave uses any more once every
+// wave has reached this point.
+template <int WAVES>
+__device__ __forceinline__ void publish_amax(float *amax, float am, lds_t *red, int wave,
+                                             int lane) {
+  typedef float __attribute__((address_space(3))) *pf;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+  __syncthreads();  // every wave is past its last use of `red`
+  if (lane == 0) *(pf)(red + wave * 4) = am;
+  __syncthreads();
+  if (wave == 0 && lane == 0) {
+    float m = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) m = fmaxf(m, *(pf)(red + w * 4));
+    __hip_atomic_fetch_max((unsigned int *)amax, __float_as_uint(m), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 template <class CFG, int F, int G, int Q>
 __device__ __forceinline__ f32x4 acc_quad(const f32x16 (&acc)[CFG::FM][CFG::FN]) {
   return f32x4{acc[F][G][4 * Q + 0], acc[F][G][4 * Q + 1], acc[F][G][4 * Q + 2],
@@ -425,10 +561,10 @@ __device__ __forceinline__ f32x4 acc_quad(const f32x16 (&acc)[CFG::FM][CFG::FN])
 
 // Whole tile: C = cast(alpha * acc), one accumulator quad at a time.  The lane holds, for its
 // MFMA block (f, g), rows m = f*32 + lane%32 and columns n = g*32 + 8q + 4*(lane/32) + 0..3.
-template <class CFG>
+template <class CFG, bool FUSED = false>
 __device__ __forceinline__ void epilogue(const KernelArgs &args, const WorkItem &w,
                                          const f32x16 (&acc)[CFG::FM][CFG::FN], float alpha,
-                                         int wm, int wn, int tid) {
+                                         int wm, int wn, int tid, EpiCtx &ec) {
   const int lane = tid & 63;
   const int64_t mbase = (int64_t)w.m * CFG::BM + wm * CFG::WM + (lane & 31);
   const int64_t nbase = (int64_t)w.n * CFG::BN + wn * CFG::WN + (lane >> 5) * 4;
@@ -440,7 +576,7 @@ __device__ __forceinline__ void epilogue(const KernelArgs &args, const WorkItem 
       for (int q = 0; q < 4; ++q) {
         const f32x4 v = {acc[f][g][4 * q + 0], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2],
                          acc[f][g][4 * q + 3]};
-        store_quad<CFG>(args, mbase + f * 32, nbase + g * 32 + q * 8, v, alpha);
+        store_quad_sel<FUSED, CFG>(args, mbase + f * 32, nbase + g * 32 + q * 8, v, alpha, ec);
       }
 }
 
@@ -531,10 +667,10 @@ __device__ __forceinline__ uint32_t slot_byte(int64_t slot) {
 // partial; every later split waits until the lock equals its K_idx, adds the slot to its own sum
 // and either stores it back (middle) or finishes the tile (final).  The lock then becomes
 // K_idx + k_tile_count.  Sums are formed left to right in K.
-template <class CFG>
+template <class CFG, bool FUSED = false>
 __device__ __forceinline__ void fixup_chain(const KernelArgs &args, const WorkItem &w,
                                             const f32x16 (&acc)[CFG::FM][CFG::FN], float alpha,
-                                            int wm, int wn, int tid) {
+                                            int wm, int wn, int tid, EpiCtx &ec) {
   const int lane = tid & 63;
   const bool add_slot = w.role == ROLE_MIDDLE || w.role == ROLE_LAST;
   const bool to_slot = w.role == ROLE_FIRST || w.role == ROLE_MIDDLE;
@@ -569,7 +705,8 @@ __device__ __forceinline__ void fixup_chain(const KernelArgs &args, const WorkIt
             if (to_slot)
               store_coherent(pr, slot + qi * CFG::THREADS * 16, v);
             else
-              store_quad<CFG>(args, mbase + f * 32, nbase + g * 32 + q * 8, v, alpha);
+              store_quad_sel<FUSED, CFG>(args, mbase + f * 32, nbase + g * 32 + q * 8, v, alpha,
+                                         ec);
           }
           // one batch of four loads in flight at a time: the accumulators fill most registers
           __builtin_amdgcn_sched_barrier(0);
@@ -614,9 +751,10 @@ __device__ __forceinline__ void fixup_separate_store(const KernelArgs &args, con
 // waits on another unit's reduction): unit b, the j-th of the n units u0..u1 of tile t, waits for
 // all n arrivals, then sums the n partials of its 1/n share of the tile in K order (u0 first --
 // the same association as the chain) and writes that share of C.
-template <class CFG>
+template <class CFG, bool FUSED = false>
 __device__ __forceinline__ void fixup_separate_reduce(const KernelArgs &args, const WorkItem &w,
-                                                      float alpha, int32_t b, int tid) {
+                                                      float alpha, int32_t b, int tid,
+                                                      EpiCtx &ec) {
   int32_t u0, u1;
   sk_tile_units(args.sp, w.sk_slot, u0, u1);
   const int n = u1 - u0 + 1, j = b - u0;
@@ -661,11 +799,11 @@ __device__ __forceinline__ void fixup_separate_reduce(const KernelArgs &args, co
     const int wm = wave_src / CFG::WGN, wn = wave_src % CFG::WGN;
     const int64_t m = (int64_t)w.m * CFG::BM + wm * CFG::WM + f * 32 + (lane & 31);
     const int64_t nn = (int64_t)w.n * CFG::BN + wn * CFG::WN + g * 32 + q * 8 + (lane >> 5) * 4;
-    store_quad<CFG>(args, m, nn, sum, alpha);
+    store_quad_sel<FUSED, CFG>(args, m, nn, sum, alpha, ec);
   }
 }
 
-template <class CFG, bool RAGGED_K>
+template <class CFG, bool RAGGED_K, bool FUSED = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::THREADS),
                                amdgpu_waves_per_eu(CFG::WAVES_PER_SIMD, CFG::WAVES_PER_SIMD)))
 gemm_kernel(KernelArgs args) {
@@ -684,6 +822,8 @@ gemm_kernel(KernelArgs args) {
 
   float alpha = 1.0f;
   if constexpr (CFG::DT == DT_FP8) alpha = (*args.scale_a) * (*args.scale_b);
+  EpiCtx ec = {1.0f, 0.0f};
+  if constexpr (FUSED) ec = epi_init(args);
 
   // Per-lane LDS read offsets of the MFMA operands (bytes within a stage).
   uint32_t aoff[CFG::KSUB][CFG::CPL], boff[CFG::KSUB][CFG::CPL];
@@ -839,7 +979,9 @@ gemm_kernel(KernelArgs args) {
     }
 
     if (cw.role == ROLE_WHOLE) {
-      if (args.out_bf16) {
+      if (FUSED) {
+        epilogue<CFG, FUSED>(args, cw, acc, alpha, wm, wn, tid, ec);  // direct stores
+      } else if (args.out_bf16) {
         // The stage read last (c - 1) becomes the staging area; its next fill is the pending
         // producer step, which is issued only after the barrier below.  Every wave has finished
         // reading it once the handshake of step c has run; without a next step (this worker's
@@ -852,10 +994,10 @@ gemm_kernel(KernelArgs args) {
                              (c + CFG::STAGES - 1) % CFG::STAGES);
         lds_barrier();
       } else {
-        epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid);
+        epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid, ec);
       }
     } else if (args.sk_mode == SK_CHAIN)
-      fixup_chain<CFG>(args, cw, acc, alpha, wm, wn, tid);
+      fixup_chain<CFG, FUSED>(args, cw, acc, alpha, wm, wn, tid, ec);
     else
       fixup_separate_store<CFG>(args, cw, acc, b, tid);
 
@@ -868,9 +1010,11 @@ gemm_kernel(KernelArgs args) {
     cursor_init(args.sp, b, rc);
     WorkItem rw;
     while (cursor_next(args.sp, rc, rw))
-      if (rw.role != ROLE_WHOLE) fixup_separate_reduce<CFG>(args, rw, alpha, b, tid);
+      if (rw.role != ROLE_WHOLE) fixup_separate_reduce<CFG, FUSED>(args, rw, alpha, b, tid, ec);
   }
   wait_vmcnt<0>();
+  if constexpr (FUSED)
+    if (args.epi & EPI_AMAX) publish_amax<CFG::WAVES>(args.amax, ec.am, smem, wave, lane);
 }
 
 // ---- ping-pong kernel (data-parallel tiles) --------------------------------------------------
@@ -1075,10 +1219,12 @@ gemm_kernel_pp(KernelArgs args) {
       if (group == 0) wait_vmcnt<0>();  // step c+1 is in LDS before M(c+1) reads it
       lds_barrier();
     }
-    if (args.out_bf16)
+    if (args.out_bf16) {
       epilogue_pp<CFG>(args, cw, acc, alpha, wm, wn, lane, slice);
-    else
-      epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid);
+    } else {
+      EpiCtx ec_unused = {1.0f, 0.0f};
+      epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid, ec_unused);
+    }
     cvalid = cursor_next(args.sp, ccur, cw);
   }
   if (group == 0) lds_barrier();  // balance the barrier group 1 skipped at the start
@@ -1372,7 +1518,8 @@ gemm_kernel_vs(KernelArgs args) {
                                  (c + CFG::STAGES - 1) % CFG::STAGES);
       lds_barrier();  // the stage takes step c+1's writes in the next k-step
     } else {
-      epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid);
+      EpiCtx ec_unused = {1.0f, 0.0f};
+      epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid, ec_unused);
     }
     ++seq;
     cvalid = cursor_next(args.sp, ccur, cw);
@@ -1412,11 +1559,14 @@ constexpr int wide_lds_bytes() {
 // bf16 output of a 128 x 128 sub-tile through the wave's LDS slice, 32 rows at a time.  Chunk c
 // (16 bytes) of staged row r sits at chunk position c ^ (r mod 16): the rows one write touches
 // and the 4 rows one read-back touches each spread over every bank.  16 lanes store one whole
-// 256-byte row segment.
-template <class CFG>
+// 256-byte row segment.  FUSED adds the bias, the activation and the amax (16 x 16 blocks): rows
+// and columns past the edge of C hold zero accumulators and read zero bias, so they give Y = 0.
+template <class CFG, bool FUSED = false>
 __device__ __forceinline__ void epilogue_wide(const KernelArgs &args, const WorkItem &w,
                                               const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
-                                              float alpha, int wm, int wn, int lane, lds_t *slice) {
+                                              float alpha, int wm, int wn, int lane, lds_t *slice,
+                                              EpiCtx &ec) {
+  static_assert(!FUSED || CFG::MI == 16, "fused epilogue on 16 x 16 blocks");
   typedef u32x2 __attribute__((address_space(3))) *p64;
   typedef u32x4 __attribute__((address_space(3))) *p128;
   static_assert(CFG::WN * 2 == 256 && CFG::WM == 128, "rows of the staged sub-tile are 256 bytes");
@@ -1465,27 +1615,52 @@ __device__ __forceinline__ void epilogue_wide(const KernelArgs &args, const Work
     // 16-byte chunk 2g + (lane/16)/2 of its row, half (lane/16) mod 2; two blocks per round
     const int wrow = lane & 15, kq = lane >> 4;
     lds_t *wr_row = slice + wrow * 256 + (kq & 1) * 8;
+    // fused: bias through range-checked buffer loads (zero past M or N)
+    f32x4 bcol[CFG::FN];
+    const __amdgpu_buffer_rsrc_t brs =
+        make_rsrc((const char *)args.bias, ((args.epi & EPI_BIAS_COL) ? args.N : args.M) * 4);
+    if constexpr (FUSED) {
+#pragma unroll
+      for (int g = 0; g < CFG::FN; ++g) bcol[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (args.epi & EPI_BIAS_COL) {
+#pragma unroll
+        for (int g = 0; g < CFG::FN; ++g)
+          bcol[g] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                         brs, (uint32_t)((n0 + g * 16 + kq * 4) * 4), 0, 0));
+      }
+    }
 #pragma unroll
     for (int p = 0; p < CFG::FM / 2; ++p) {
 #pragma unroll
-      for (int fp = 0; fp < 2; ++fp)
+      for (int fp = 0; fp < 2; ++fp) {
+        float brow = 0.0f;
+        if constexpr (FUSED)
+          if (args.epi & EPI_BIAS_ROW)
+            brow = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(
+                           brs, (uint32_t)((m0 + (2 * p + fp) * 16 + wrow) * 4), 0, 0));
 #pragma unroll
         for (int g = 0; g < CFG::FN; ++g) {
-          const f32x4 v = quad_of<true>(acc[2 * p + fp][g], 0) * alpha;
+          f32x4 v = quad_of<true>(acc[2 * p + fp][g], 0) * alpha;
+          if constexpr (FUSED) v = epi_act(args.epi, v + brow + bcol[g], ec.am);
           *(p64)(wr_row + fp * 16 * 256 + (((2 * g + (kq >> 1)) ^ wrow) * 16)) =
               u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
       read_back(p);
     }
   }
 }
 
-// fp32 output straight from the accumulation registers, one quad (16 bytes) per lane and store.
-template <class CFG>
+// fp32 output straight from the accumulation registers, one quad (16 bytes) per lane and store;
+// FUSED: any output type, one quad per store (4 bytes of e4m3 codes, 8 of bf16, 16 of fp32).
+template <class CFG, bool FUSED = false>
 __device__ __forceinline__ void epilogue_direct(const KernelArgs &args, const WorkItem &w,
                                                 const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
-                                                float alpha, int wm, int wn, int lane) {
+                                                float alpha, int wm, int wn, int lane,
+                                                EpiCtx &ec) {
   constexpr int MI = CFG::MI, NQ = MI == 32 ? 4 : 1;
   const int64_t mbase = (int64_t)w.m * CFG::BM + wm * CFG::WM + (lane % MI);
   const int64_t nbase = (int64_t)w.n * CFG::BN + wn * CFG::WN + (lane / MI) * 4;
@@ -1495,8 +1670,8 @@ __device__ __forceinline__ void epilogue_direct(const KernelArgs &args, const Wo
     for (int g = 0; g < CFG::FN; ++g)
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        store_quad<CFG>(args, mbase + f * MI, nbase + g * MI + q * 8, quad_of<true>(acc[f][g], q),
-                        alpha);
+        store_quad_sel<FUSED, CFG>(args, mbase + f * MI, nbase + g * MI + q * 8,
+                                   quad_of<true>(acc[f][g], q), alpha, ec);
         __builtin_amdgcn_sched_barrier(0);
       }
 }
@@ -1575,7 +1750,7 @@ struct WideProducer {
   }
 };
 
-template <class CFG, bool RAGGED_K>
+template <class CFG, bool RAGGED_K, bool FUSED = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::THREADS),
                                amdgpu_waves_per_eu(1, 1)))
 gemm_kernel_wide(KernelArgs args) {
@@ -1596,6 +1771,8 @@ gemm_kernel_wide(KernelArgs args) {
 
   float alpha = 1.0f;
   if constexpr (CFG::DT == DT_FP8) alpha = (*args.scale_a) * (*args.scale_b);
+  EpiCtx ec = {1.0f, 0.0f};
+  if constexpr (FUSED) ec = epi_init(args);
 
   uint32_t aoff[CFG::KSUB][CFG::CPL], boff[CFG::KSUB][CFG::CPL];
   {
@@ -1749,12 +1926,15 @@ gemm_kernel_wide(KernelArgs args) {
 
     if constexpr (CFG::MI == 16) mfma_wait_states();  // the last MFMAs' results are written
     if (args.out_bf16)
-      epilogue_wide<CFG>(args, cw, acc, alpha, wm, wn, lane, slice);
+      epilogue_wide<CFG, FUSED>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
     else
-      epilogue_direct<CFG>(args, cw, acc, alpha, wm, wn, lane);
+      epilogue_direct<CFG, FUSED>(args, cw, acc, alpha, wm, wn, lane, ec);
     cvalid = cursor_next(args.sp, ccur, cw);
   }
   wait_vmcnt<0>();
+  if constexpr (FUSED)
+    if (args.epi & EPI_AMAX)
+      publish_amax<CFG::WAVES>(args.amax, ec.am, smem + CFG::LDS_BYTES, wave, lane);
 }
 
 // ---- wide-wave kernel, one MFMA depth per k-tile (e4m3 16 x 16 x 128) ------------------------
@@ -1766,7 +1946,7 @@ gemm_kernel_wide(KernelArgs args) {
 // passed -- so H(c+1) sits after row 0.  B of step c+1 goes into the other buffer, and the loads
 // of step c+S (begun by H(c+1)) go out over the first half of the slots after the handshake,
 // which leaves them more than half a k-step before H(c+2) waits for them.
-template <class CFG, bool RAGGED_K>
+template <class CFG, bool RAGGED_K, bool FUSED = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::THREADS),
                                amdgpu_waves_per_eu(1, 1)))
 gemm_kernel_wide1(KernelArgs args) {
@@ -1787,6 +1967,8 @@ gemm_kernel_wide1(KernelArgs args) {
 
   float alpha = 1.0f;
   if constexpr (CFG::DT == DT_FP8) alpha = (*args.scale_a) * (*args.scale_b);
+  EpiCtx ec = {1.0f, 0.0f};
+  if constexpr (FUSED) ec = epi_init(args);
 
   uint32_t aoff[1][CFG::CPL], boff[1][CFG::CPL];
   {
@@ -1915,12 +2097,15 @@ gemm_kernel_wide1(KernelArgs args) {
     }
     mfma_wait_states();  // the last MFMAs' results are written
     if (args.out_bf16)
-      epilogue_wide<CFG>(args, cw, acc, alpha, wm, wn, lane, slice);
+      epilogue_wide<CFG, FUSED>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
     else
-      epilogue_direct<CFG>(args, cw, acc, alpha, wm, wn, lane);
+      epilogue_direct<CFG, FUSED>(args, cw, acc, alpha, wm, wn, lane, ec);
     cvalid = cursor_next(args.sp, ccur, cw);
   }
   wait_vmcnt<0>();
+  if constexpr (FUSED)
+    if (args.epi & EPI_AMAX)
+      publish_amax<CFG::WAVES>(args.amax, ec.am, smem + CFG::LDS_BYTES, wave, lane);
 }
 
 __global__ void clear_ints_kernel(int *p, int n) {

@@ -7,7 +7,9 @@
  * section: C[m, n] is the sum over k of A[m, k] B[k, n]) in BF16, or in FP8 e4m3 with one FP32
  * scale per tensor ("WGMMA part 2" lesson, section 11, tensor-wise scaling), accumulated in FP32
  * ("WGMMA part 2" lesson, section 14).  The fused epilogue applies alpha and casts to the output
- * type ("H100 Kernel Design" lesson, section 12: Z = alpha * Acc, then cast and store).  The work
+ * type ("H100 Kernel Design" lesson, section 12: Z = alpha * Acc, then cast and store); on request
+ * it also adds a bias, applies an activation, tracks amax and quantises to e4m3 (GEMM_EPI_*,
+ * gemm_run_ex), all before the one store of C.  The work
  * is cut into BM x BN output tiles and BK-deep k-tiles, ordered by a tile mapping F(i) -> (m, n)
  * and handed to workgroups by a static, persistent or Stream-K scheduler ("DeepGEMM on SM90" page,
  * mapping table; "H100 Kernel Design" lesson, sections 9-10; "H100 Stream-K" lesson).
@@ -36,7 +38,7 @@ typedef enum {
   GEMM_OK = 0,
   GEMM_ERR_INVALID_ARG = -1,  /* bad enum, non-positive size, NULL handle/pointer ...        */
   GEMM_ERR_UNSUPPORTED = -2,  /* well-formed but outside what the kernels implement          */
-  GEMM_ERR_ALIGNMENT = -3,    /* a device pointer is not 16-byte aligned                      */
+  GEMM_ERR_ALIGNMENT = -3,    /* a device pointer is misaligned (16 bytes; 4 for one float)   */
   GEMM_ERR_WORKSPACE = -4,    /* workspace missing or smaller than gemm_workspace_bytes()     */
   GEMM_ERR_HIP = -5,          /* a HIP runtime call failed (no device, launch failure ...)    */
   GEMM_ERR_CAPACITY = -6      /* a buffer passed to the library is too small for the result   */
@@ -87,12 +89,31 @@ typedef enum {
                                               does not publish its lock / arrival, so the bounded
                                               waits on it expire and report GEMM_DEVICE_ERR_SPIN */
 
+/* Fused epilogue operations (gemm_desc.epilogue), "H100 Kernel Design" lesson, section 12: items
+ * 2, 3 and 8 of its operation list, in the order of its section 12.2 --
+ *   Z = alpha * Acc;  Z += bias;  Y = act(Z);  amax = max |Y|;  D = cast(Y) (e4m3: of Y / scale_d)
+ * -- all applied to the finished accumulators before C is stored once (a Stream-K tile: by the
+ * split that writes it, after the full sum).  At most one bias bit and one activation bit.
+ * A plan with epilogue bits or an e4m3 output runs on the wide-wave or the cooperative kernel
+ * (GEMM_FLAG_PINGPONG / GEMM_FLAG_REGSTAGED with them: GEMM_ERR_UNSUPPORTED). */
+#define GEMM_EPI_BIAS_ROW 0x1u  /* Z[m][n] += bias[m]; bias holds M floats                     */
+#define GEMM_EPI_BIAS_COL 0x2u  /* Z[m][n] += bias[n]; bias holds N floats                     */
+#define GEMM_EPI_RELU 0x4u      /* Y = max(Z, 0)                                                  */
+#define GEMM_EPI_GELU 0x8u      /* Y = Z * Phi(Z) = Z * (1 + erf(Z / sqrt 2)) / 2 (exact form)    */
+#define GEMM_EPI_SILU 0x10u     /* Y = Z / (1 + exp(-Z))                                          */
+#define GEMM_EPI_AMAX 0x20u     /* *amax = max(*amax, max over C of |Y|): Y in fp32, before the
+                                   output scale and cast.  The kernel folds its result into the
+                                   float already there (an atomic max on the bit pattern), so the
+                                   caller sets *amax (to 0, or a running value) before the run;
+                                   NaN elements of Y are not propagated                          */
+
 /* Problem description.  0 in an "auto" field lets the planner choose. */
 typedef struct gemm_desc {
   int64_t M, N, K;           /* C is M x N, the reduction is over K (all >= 0; M or N == 0 is an
                                 empty product and gemm_run does nothing; K == 0 writes C = 0)   */
   int32_t dtype_ab;          /* GEMM_BF16 or GEMM_FP8_E4M3                                      */
-  int32_t dtype_c;           /* GEMM_F32 or GEMM_BF16                                           */
+  int32_t dtype_c;           /* GEMM_F32, GEMM_BF16, or GEMM_FP8_E4M3 (e4m3 codes of Y / scale_d,
+                                see gemm_epilogue_args; fused-epilogue plans only)            */
   int32_t layout_a;          /* must be GEMM_ROW_MAJOR: a(m,k) at A[m*K + k]                    */
   int32_t layout_b;          /* must be GEMM_COL_MAJOR: b(k,n) at B[n*K + k]                    */
   int32_t mapping;           /* gemm_mapping                                                     */
@@ -102,6 +123,7 @@ typedef struct gemm_desc {
   int32_t num_workers;       /* P for persistent / Stream-K; 0 = CUs x resident workgroups/CU    */
   int32_t bm, bn, bk;        /* tile shape; 0 = auto.  Supported: see gemm_create              */
   uint32_t flags;            /* GEMM_FLAG_*                                                      */
+  uint32_t epilogue;         /* GEMM_EPI_* bits: fused bias / activation / amax (0 = none)      */
 } gemm_desc;
 
 /* One unit of work as the scheduler hands it out (gemm_schedule_enumerate, device trace). */
@@ -158,6 +180,25 @@ int gemm_plan_get(gemm_handle h, gemm_plan_info *info);
  * 16-byte aligned; the library clears the parts it needs at the start of every run. */
 int gemm_run(gemm_handle h, const void *A, const void *B, void *C, const float *scale_a,
              const float *scale_b, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Device operands of the fused epilogue; all DEVICE pointers owned by the caller. */
+typedef struct gemm_epilogue_args {
+  const float *bias;     /* with a GEMM_EPI_BIAS_* bit: M (row) or N (column) floats, 16-byte
+                            aligned; else ignored                                                */
+  const float *scale_d;  /* with dtype_c = GEMM_FP8_E4M3: one float, the output's dequantisation
+                            scale (a code q stands for scale_d * q, so q = e4m3(Y / scale_d),
+                            nearest-even, saturated to +-448); else ignored                    */
+  float *amax;           /* with GEMM_EPI_AMAX: one float, 4-byte aligned, read and updated by
+                            the kernel (see GEMM_EPI_AMAX); else ignored                        */
+} gemm_epilogue_args;
+
+/* gemm_run with the fused epilogue's operands.  `epi` may be NULL when the plan needs none of
+ * them (gemm_run is this call with epi = NULL).  A missing required pointer is
+ * GEMM_ERR_INVALID_ARG, a misaligned one GEMM_ERR_ALIGNMENT, both checked before anything is
+ * enqueued.  Calls that overlap in time and share one amax combine their maxima. */
+int gemm_run_ex(gemm_handle h, const void *A, const void *B, void *C, const float *scale_a,
+                const float *scale_b, const gemm_epilogue_args *epi, void *workspace,
+                size_t workspace_bytes, void *stream);
 
 int gemm_destroy(gemm_handle h);
 

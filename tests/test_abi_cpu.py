@@ -30,7 +30,8 @@ def test_struct_layouts_match_c_compiler(tmp_path):
     """sizeof and every field offset of the ctypes mirrors equal what a C compiler sees."""
     import subprocess
     structs = {"gemm_desc": L.GemmDesc, "gemm_work_item": L.GemmWorkItem,
-               "gemm_plan_info": L.GemmPlanInfo}
+               "gemm_plan_info": L.GemmPlanInfo, "gemm_config_score": L.GemmConfigScore,
+               "gemm_epilogue_args": L.GemmEpilogueArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "gemm.h"', 'int main(void){']
     for cname, py in structs.items():
         lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
@@ -115,6 +116,22 @@ def create(**kw):
     (dict(flags=L.GEMM_FLAG_WIDE, sched=L.GEMM_SCHED_STREAMK), L.GEMM_ERR_UNSUPPORTED),
     (dict(flags=L.GEMM_FLAG_WIDE, K=0), L.GEMM_ERR_UNSUPPORTED),
     (dict(flags=L.GEMM_FLAG_WIDE | L.GEMM_FLAG_COOPERATIVE), L.GEMM_ERR_INVALID_ARG),
+    # fused epilogue
+    (dict(epilogue=0x40), L.GEMM_ERR_INVALID_ARG),                       # unknown bit
+    (dict(epilogue=L.GEMM_EPI_BIAS_ROW | L.GEMM_EPI_BIAS_COL), L.GEMM_ERR_INVALID_ARG),
+    (dict(epilogue=L.GEMM_EPI_RELU | L.GEMM_EPI_GELU), L.GEMM_ERR_INVALID_ARG),
+    (dict(epilogue=L.GEMM_EPI_SILU | L.GEMM_EPI_GELU), L.GEMM_ERR_INVALID_ARG),
+    (dict(epilogue=0x3F & ~(L.GEMM_EPI_BIAS_ROW | L.GEMM_EPI_RELU | L.GEMM_EPI_SILU)), L.GEMM_OK),
+    (dict(epilogue=L.GEMM_EPI_BIAS_ROW | L.GEMM_EPI_SILU | L.GEMM_EPI_AMAX), L.GEMM_OK),
+    (dict(dtype_c=L.GEMM_FP8_E4M3), L.GEMM_OK),
+    (dict(dtype_c=L.GEMM_FP8_E4M3, dtype_ab=L.GEMM_FP8_E4M3), L.GEMM_OK),
+    (dict(epilogue=L.GEMM_EPI_RELU, K=0), L.GEMM_OK),                    # Z = bias: cooperative
+    (dict(epilogue=L.GEMM_EPI_RELU, sched=L.GEMM_SCHED_STREAMK, bm=128, bn=128), L.GEMM_OK),
+    (dict(epilogue=L.GEMM_EPI_RELU, flags=L.GEMM_FLAG_WIDE), L.GEMM_OK),
+    (dict(epilogue=L.GEMM_EPI_RELU, flags=L.GEMM_FLAG_COOPERATIVE), L.GEMM_OK),
+    (dict(epilogue=L.GEMM_EPI_RELU, flags=L.GEMM_FLAG_PINGPONG), L.GEMM_ERR_UNSUPPORTED),
+    (dict(epilogue=L.GEMM_EPI_RELU, flags=L.GEMM_FLAG_REGSTAGED), L.GEMM_ERR_UNSUPPORTED),
+    (dict(dtype_c=L.GEMM_FP8_E4M3, flags=L.GEMM_FLAG_PINGPONG), L.GEMM_ERR_UNSUPPORTED),
 ])
 def test_create_validation(kw, want):
     assert create(**kw) == want
@@ -181,6 +198,55 @@ def test_run_validation_before_enqueue():
     # an empty output is a no-op that needs no pointers at all
     e = L.Plan(L.make_desc(0, 256, 256, num_workers=4))
     assert e.info.grid == 0 and e.run_raw(0, 0, 0) == L.GEMM_OK
+
+
+def test_fused_epilogue_plans():
+    """Epilogue plans run on the wide-wave kernel for data-parallel 256 x 256 work and on the
+    cooperative kernel otherwise; without epilogue bits nothing changes."""
+    kw = dict(sched=L.GEMM_SCHED_PERSISTENT, num_workers=256)
+    dp = L.Plan(L.make_desc(4096, 4096, 4096, epilogue=L.GEMM_EPI_GELU | L.GEMM_EPI_BIAS_COL,
+                            **kw))
+    assert (dp.info.kernel, dp.info.bm) == (3, 256)
+    q = L.Plan(L.make_desc(4096, 4096, 4096, dtype_ab=L.GEMM_FP8_E4M3, dtype_c=L.GEMM_FP8_E4M3,
+                           **kw))
+    assert (q.info.kernel, q.info.bk) == (3, 128)
+    sk = L.Plan(L.make_desc(512, 512, 65536, sched=L.GEMM_SCHED_STREAMK, num_workers=256, bm=128,
+                            bn=128, epilogue=L.GEMM_EPI_AMAX))
+    assert sk.info.kernel == 0 and sk.info.sk_tiles > 0
+    z = L.Plan(L.make_desc(256, 256, 0, epilogue=L.GEMM_EPI_BIAS_ROW, num_workers=4))
+    assert z.info.kernel == 0
+    # the planner's own choice (everything auto) takes a kernel that has the fused epilogue
+    for M, N, K in ((4096, 4096, 4096), (512, 512, 65536), (2048, 2048, 2048), (256, 512, 4096)):
+        a = L.Plan(L.make_desc(M, N, K, sched=L.GEMM_SCHED_AUTO, num_workers=256,
+                               epilogue=L.GEMM_EPI_SILU))
+        assert a.info.kernel in (0, 3), (M, N, K)
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                    reason="validation-only test; on a GPU machine the parity suite covers runs")
+def test_run_ex_validation_before_enqueue():
+    ok = 1 << 20
+    epi = L.GEMM_EPI_BIAS_COL | L.GEMM_EPI_RELU | L.GEMM_EPI_AMAX
+    p = L.Plan(L.make_desc(256, 256, 256, num_workers=4, epilogue=epi,
+                           dtype_c=L.GEMM_FP8_E4M3))
+    full = dict(bias=ok, scale_d=ok, amax=ok)
+    assert p.run_ex_raw(ok, ok, ok, epi_null=True) == L.GEMM_ERR_INVALID_ARG
+    for missing in full:
+        assert p.run_ex_raw(ok, ok, ok, **{**full, missing: 0}) == L.GEMM_ERR_INVALID_ARG, missing
+    assert p.run_ex_raw(ok, ok, ok, **{**full, "bias": ok + 4}) == L.GEMM_ERR_ALIGNMENT
+    assert p.run_ex_raw(ok, ok, ok, **{**full, "amax": ok + 2}) == L.GEMM_ERR_ALIGNMENT
+    assert p.run_ex_raw(ok, ok, ok, **{**full, "scale_d": ok + 1}) == L.GEMM_ERR_ALIGNMENT
+    assert p.run_ex_raw(ok, ok, ok, **{**full, "amax": ok + 4}) == L.GEMM_ERR_HIP  # 4 B is enough
+    # gemm_run is gemm_run_ex without epilogue operands
+    assert p.run_raw(ok, ok, ok) == L.GEMM_ERR_INVALID_ARG
+    # a plan that needs no epilogue operand accepts a NULL epi and ignores the pointers
+    b = L.Plan(L.make_desc(256, 256, 256, num_workers=4, epilogue=L.GEMM_EPI_GELU))
+    assert b.run_ex_raw(ok, ok, ok, epi_null=True) == L.GEMM_ERR_HIP
+    assert b.run_ex_raw(ok, ok, ok, bias=3, amax=5) == L.GEMM_ERR_HIP
+    # an empty output checks the epilogue operands, then does nothing
+    e = L.Plan(L.make_desc(0, 256, 256, num_workers=4, epilogue=L.GEMM_EPI_AMAX))
+    assert e.run_ex_raw(0, 0, 0, epi_null=True) == L.GEMM_ERR_INVALID_ARG
+    assert e.run_ex_raw(0, 0, 0, amax=ok) == L.GEMM_OK
 
 
 def test_package_has_no_cpu_fallback():
