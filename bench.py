@@ -126,10 +126,11 @@ def measured_traffic(workload):
     return entry.get("bytes_per_launch")
 
 
-# name, workload key, mapping, group, sched, tile, out, workers[, bk[, variant]]
+# name, workload key, mapping, group, sched, tile, out, workers[, bk[, variant[, epilogue]]]
 # variant: "chain" = Stream-K lock-chain fixup; "coop" / "pp" / "vs" / "wide" = the cooperative /
 # ping-pong / register-staged / wide-wave kernel instead of the default for data-parallel
-# 256 x 256 tiles (the wide-wave kernel)
+# 256 x 256 tiles (the wide-wave kernel).  epilogue: the fused operations, {"bias": "row" |
+# "col", "act": "relu" | "gelu" | "silu", "amax": True}; out "e4m3" quantises the output.
 RUNS = {
     "bf16_4096": ("bf16_4096", "grouped_m", 8, "persistent", 0, "bf16", 0),
     "bf16_4096_coop": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "coop"),
@@ -147,6 +148,12 @@ RUNS = {
     "bf16_streamk_chain": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256, 0,
                            "chain"),
     "bf16_256": ("bf16_256", "linear_n", 1, "static", 128, "f32", 0),
+    # fused epilogues: the MLP up-projection with its bias and GELU; an FP8 layer whose output
+    # is quantised back to e4m3 with amax tracking
+    "bf16_mlp_up_bias_gelu": ("bf16_mlp_up", "grouped_m", 8, "persistent", 0, "bf16", 0, 0, "",
+                              {"bias": "col", "act": "gelu"}),
+    "fp8_8192_e4m3_amax": ("fp8_8192", "grouped_m", 16, "persistent", 0, "e4m3", 0, 0, "",
+                           {"amax": True}),
 }
 
 
@@ -161,6 +168,7 @@ def run_flags(name, dg):
 def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
     wl_name, mapping, group, sched, tile, out, workers = RUNS[name][:7]
     bk = RUNS[name][7] if len(RUNS[name]) > 7 else 0
+    epi_spec = RUNS[name][9] if len(RUNS[name]) > 9 else {}
     flags = run_flags(name, dg)
     wl = gi.WORKLOADS[wl_name]
     if wl_name not in cache:
@@ -179,23 +187,42 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
         cache[wl_name] = (op, A, B, sa, sb)
         log(f"{wl_name}: inputs generated and resident in HBM ({time.time() - t0:.1f} s)")
     op, A, B, sa, sb = cache[wl_name]
+    epi = dg.ACTIVATIONS[epi_spec.get("act")]
+    epi |= {None: 0, "row": dg.GEMM_EPI_BIAS_ROW, "col": dg.GEMM_EPI_BIAS_COL}[
+        epi_spec.get("bias")]
+    epi |= dg.GEMM_EPI_AMAX if epi_spec.get("amax") else 0
     desc = dg.make_desc(op.M, op.N, op.K,
                         dg.GEMM_BF16 if op.dtype == "bf16" else dg.GEMM_FP8_E4M3,
-                        dg.GEMM_BF16 if out == "bf16" else dg.GEMM_F32, dg.MAPPINGS[mapping],
-                        group, dg.SCHEDS[sched], workers, tile, tile, bk, flags)
+                        dg.OUT_DTYPES[out], dg.MAPPINGS[mapping],
+                        group, dg.SCHEDS[sched], workers, tile, tile, bk, flags, epilogue=epi)
     plan = dg.Plan(desc)
     C = torch.empty((op.M, op.N), device=A.device,
-                    dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+                    dtype={"bf16": torch.bfloat16, "f32": torch.float32, "e4m3": torch.uint8}[out])
     ws = None
     if plan.workspace_bytes:
         ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=A.device)
+    bias = amax = scale_d = None
+    bias_bytes = 0
+    if epi_spec.get("bias"):
+        n = op.M if epi_spec["bias"] == "row" else op.N
+        bias = torch.from_numpy(gi.make_vector(n, seed=wl.seed + 7)).to(A.device)
+        bias_bytes = 4 * n
+    if epi_spec.get("amax"):
+        amax = torch.zeros(1, dtype=torch.float32, device=A.device)
+    if out == "e4m3":  # the output's dequantisation scale: N(0, 1) operands give |C| up to
+        # about 4 sqrt(K), mapped onto the format's 448
+        scale_d = torch.tensor([4.0 * op.K ** 0.5 / 448.0], dtype=torch.float32,
+                               device=A.device)
     stream = torch.cuda.current_stream()
+
+    def launch():
+        plan.run(A, B, C, sa, sb, ws, stream, bias=bias, scale_d=scale_d, amax=amax)
     # Warmup: at least `warmup` launches and at least `settle_ms` of back-to-back launches, so the
     # GPU's clock has left its ramp (it climbs for a few hundred ms under a sustained MFMA load).
     n_warm, t_w = 0, time.perf_counter()
     while True:
         for _ in range(max(1, warmup) if n_warm == 0 else 50):
-            plan.run(A, B, C, sa, sb, ws, stream)
+            launch()
             n_warm += 1
         torch.cuda.synchronize()
         if n_warm >= warmup and (time.perf_counter() - t_w) * 1e3 >= settle_ms:
@@ -205,7 +232,7 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(steps):
-        plan.run(A, B, C, sa, sb, ws, stream)
+        launch()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -216,13 +243,14 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
         "workload": wl_name, "M": op.M, "N": op.N, "K": op.K, "dtype": op.dtype, "out": out,
         "tile": [info.bm, info.bn, info.bk], "stages": info.stages, "mapping": mapping,
         "kernel": ["cooperative", "ping-pong", "register-staged", "wide-wave"][info.kernel],
-        "group": group, "sched": sched, "grid": info.grid,
+        "group": group, "sched": sched, "grid": info.grid, "epilogue": epi_spec,
         "dp_tiles": info.dp_tiles, "sk_tiles": info.sk_tiles, "warmup_launches": n_warm,
         "ms_per_step": wall * 1e3 / steps, "kernel_us": dev_ms * 1e3,
         "tflops": flops / (wall / steps) / 1e12, "kernel_tflops": flops / (dev_ms * 1e-3) / 1e12,
     }
     res["frac_of_peak"] = res["kernel_tflops"] / PEAK_TFLOPS[op.dtype]
-    alg_bytes = op.A.nbytes + op.B.nbytes + op.M * op.N * (2 if out == "bf16" else 4)
+    alg_bytes = (op.A.nbytes + op.B.nbytes + bias_bytes +
+                 op.M * op.N * {"bf16": 2, "f32": 4, "e4m3": 1}[out])
     res["alg_bytes"] = alg_bytes
     res["hbm_gbs_alg"] = alg_bytes / (dev_ms * 1e-3) / 1e9
     log(f"{name}: {res['kernel_us']:.1f} us/launch, {res['kernel_tflops']:.1f} TFLOP/s "
@@ -300,13 +328,14 @@ def main():
     secondary = {}
     if not args.no_secondary:
         for name in ("bf16_4096_pp", "bf16_4096_coop", "bf16_4096_linear", "bf16_4096_t128",
-                     "fp8_8192", "fp8_8192_pp", "bf16_mlp_up", "bf16_streamk", "bf16_256"):
+                     "fp8_8192_pp", "fp8_8192_e4m3_amax", "fp8_8192", "bf16_mlp_up_bias_gelu",
+                     "bf16_mlp_up", "bf16_streamk", "bf16_256"):
             steps = max(10, args.steps // (4 if name.startswith("fp8_8192") else 1))
             r = time_run(name, steps, max(2, args.warmup // 2), torch, dg, gi, cache,
                          args.settle_ms / 2)
             secondary[name] = {k: r[k] for k in ("kernel_us", "kernel_tflops", "frac_of_peak",
                                                  "hbm_gbs_alg", "tile", "grid", "mapping",
-                                                 "sched", "kernel")}
+                                                 "sched", "kernel", "out", "epilogue")}
             if name in cache:
                 del cache[name]
     cache.clear()

@@ -92,25 +92,36 @@ const void *kernel_of_vs() {
 }
 
 // k-tiles one MFMA deep (e4m3 16 x 16 x 128) take the single-A-buffer form of the schedule
-template <class CFG, bool RAGGED_K, bool FUSED = false>
+template <class CFG, bool RAGGED_K, int FUSE = FUSE_OFF>
 constexpr auto wide_kernel() {
   if constexpr (CFG::KSUB == 1)
-    return &gemm_kernel_wide1<CFG, RAGGED_K, FUSED>;
+    return &gemm_kernel_wide1<CFG, RAGGED_K, FUSE>;
   else
-    return &gemm_kernel_wide<CFG, RAGGED_K, FUSED>;
+    return &gemm_kernel_wide<CFG, RAGGED_K, FUSE>;
+}
+// activation of a fused plan, the wide-wave kernels' FUSE argument
+int act_of(uint32_t epi) {
+  return (epi & EPI_RELU) ? ACT_RELU : (epi & EPI_GELU) ? ACT_GELU : (epi & EPI_SILU) ? ACT_SILU
+                                                                                   : ACT_NONE;
+}
+template <class CFG, int FUSE>
+void launch_wide_as(const KernelArgs &a, int grid, bool ragged_k, hipStream_t s) {
+  if (ragged_k)
+    hipLaunchKernelGGL((wide_kernel<CFG, true, FUSE>()), dim3(grid), dim3(CFG::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((wide_kernel<CFG, false, FUSE>()), dim3(grid), dim3(CFG::THREADS), 0, s, a);
 }
 template <class CFG>
 hipError_t launch_wide(const KernelArgs &a, int grid, bool ragged_k, hipStream_t s) {
-  const dim3 g(grid), t(CFG::THREADS);
-  if (fused_args(a)) {
-    if (ragged_k)
-      hipLaunchKernelGGL((wide_kernel<CFG, true, true>()), g, t, 0, s, a);
-    else
-      hipLaunchKernelGGL((wide_kernel<CFG, false, true>()), g, t, 0, s, a);
-  } else if (ragged_k) {
-    hipLaunchKernelGGL((wide_kernel<CFG, true>()), g, t, 0, s, a);
+  if (!fused_args(a)) {
+    launch_wide_as<CFG, FUSE_OFF>(a, grid, ragged_k, s);
   } else {
-    hipLaunchKernelGGL((wide_kernel<CFG, false>()), g, t, 0, s, a);
+    switch (act_of(a.epi)) {
+      case ACT_RELU: launch_wide_as<CFG, ACT_RELU>(a, grid, ragged_k, s); break;
+      case ACT_GELU: launch_wide_as<CFG, ACT_GELU>(a, grid, ragged_k, s); break;
+      case ACT_SILU: launch_wide_as<CFG, ACT_SILU>(a, grid, ragged_k, s); break;
+      default: launch_wide_as<CFG, ACT_NONE>(a, grid, ragged_k, s); break;
+    }
   }
   return hipGetLastError();
 }

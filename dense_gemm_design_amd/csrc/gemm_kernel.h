@@ -425,8 +425,10 @@ __device__ __forceinline__ void store_quad(const KernelArgs &args, int64_t m, in
 // ---- fused epilogue ("H100 Kernel Design" lesson, section 12) ------------------------------
 // Z = alpha * Acc + bias, Y = act(Z), amax over Y, then the cast -- for an e4m3 output the code
 // of Y / scale_d -- and the store, in the order of section 12.2 (steps 2 to 7).  Kernels take
-// this path in their FUSED instantiation, chosen at launch when EPI_* bits or an e4m3 output
-// are asked for; every other launch runs the plain epilogues above and below.
+// this path in a fused instantiation, chosen at launch when EPI_* bits or an e4m3 output are
+// asked for; every other launch runs the plain epilogues above and below.  The wide-wave kernels
+// have one fused instantiation per activation (no per-element branch on it); the cooperative
+// kernel has one that reads the activation from the EPI_* bits.
 enum : uint32_t {
   EPI_BIAS_ROW = 0x1u,
   EPI_BIAS_COL = 0x2u,
@@ -435,6 +437,10 @@ enum : uint32_t {
   EPI_SILU = 0x10u,
   EPI_AMAX = 0x20u
 };
+
+// FUSE template argument: FUSE_OFF = the plain epilogue; ACT_* = fused, with that activation;
+// ACT_RT = fused, activation chosen by the EPI_* bits at run time.
+enum { FUSE_OFF = -1, ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_SILU = 3, ACT_RT = 4 };
 
 // State of the fused epilogue in one lane: the output's inverse scale and the running max |Y|.
 struct EpiCtx {
@@ -446,27 +452,26 @@ __device__ __forceinline__ EpiCtx epi_init(const KernelArgs &args) {
   return EpiCtx{args.out_fp8 ? 1.0f / *args.scale_d : 1.0f, 0.0f};
 }
 
-// erf(x) by the rational approximation of Abramowitz and Stegun, formula 7.1.26 (after Hastings):
-// erf(x) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2), t = 1 / (1 + p x) for x >= 0,
-// odd in x, absolute error below 1.5e-7 -- inline, where a library call would make the caller
-// save the whole accumulator tile around it.
-__device__ __forceinline__ float erf_as(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
-  float poly = 1.061405429f;
-  poly = poly * t - 1.453152027f;
-  poly = poly * t + 1.421413741f;
-  poly = poly * t - 0.284496736f;
-  poly = poly * t + 0.254829592f;
-  poly = poly * t;
-  // exp(-x^2) = 2^(-x^2 log2 e); underflows to 0 for |x| > ~9.4, where erf is 1 in fp32
-  const float r = 1.0f - poly * __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
-  return __builtin_copysignf(r, x);
-}
-
-// GELU in its exact form z Phi(z) = z (1 + erf(z / sqrt 2)) / 2
+// GELU in its exact form z Phi(z) = z (1 + erf(z / sqrt 2)) / 2, with erf from the rational
+// approximation of Abramowitz and Stegun, formula 7.1.26 (after Hastings): for x >= 0,
+//   erf(x) = 1 - P(t) exp(-x^2),  P(t) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))),  t = 1/(1 + p x),
+// absolute error below 1.5e-7, odd in x.  With x = |z| / sqrt 2 both signs of z collapse to
+//   GELU(z) = max(z, 0) - |z| P(t) exp(-z^2 / 2) / 2
+// (z >= 0: z (2 - P e) / 2;  z < 0: z P e / 2), the 1/2 folded into P's coefficients: ten
+// VALU operations, a reciprocal and an exp2 per element, inline -- a library call would make
+// the caller save the whole accumulator tile around it.
 __device__ __forceinline__ float act_gelu(float z) {
-  return 0.5f * z * (1.0f + erf_as(z * 0.70710678118654752f));
+  const float az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(az, 0.3275911f * 0.70710678118654752f, 1.0f));
+  float q = 0.5f * 1.061405429f;
+  q = fmaf(q, t, 0.5f * -1.453152027f);
+  q = fmaf(q, t, 0.5f * 1.421413741f);
+  q = fmaf(q, t, 0.5f * -0.284496736f);
+  q = fmaf(q, t, 0.5f * 0.254829592f);
+  q = q * t;
+  // exp(-z^2 / 2) = 2^(-z^2 log2(e) / 2): 0 once z^2 / 2 passes ~104, where the term vanishes
+  const float e = __builtin_amdgcn_exp2f(z * z * -0.72134752044448170f);
+  return fmaf(-az, q * e, fmaxf(z, 0.0f));
 }
 // SiLU z sigmoid(z) = z / (1 + exp(-z)); exp and reciprocal at hardware precision (a few ulp).
 // exp(-z) = inf for very negative z gives -0, and 0 for very large z gives z.
@@ -474,19 +479,32 @@ __device__ __forceinline__ float act_silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
 }
 
-// Y = act(Z) for one quad (the uniform EPI_* bits choose the branch) and |Y| into the amax
-__device__ __forceinline__ f32x4 epi_act(uint32_t epi, f32x4 z, float &am) {
-  if (epi & EPI_RELU) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) z[e] = z[e] < 0.0f ? 0.0f : z[e];  // NaN stays NaN
-  } else if (epi & EPI_GELU) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) z[e] = act_gelu(z[e]);
-  } else if (epi & EPI_SILU) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) z[e] = act_silu(z[e]);
+template <int ACT>
+__device__ __forceinline__ float act_apply(float z) {
+  if constexpr (ACT == ACT_RELU)
+    return z < 0.0f ? 0.0f : z;  // NaN stays NaN
+  else if constexpr (ACT == ACT_GELU)
+    return act_gelu(z);
+  else if constexpr (ACT == ACT_SILU)
+    return act_silu(z);
+  else
+    return z;
+}
+
+// Y = act(Z) for one quad and, if the quad lies inside C (ok), |Y| into the amax.  ACT_RT: the
+// uniform EPI_* bits choose.
+template <int ACT>
+__device__ __forceinline__ f32x4 epi_act(uint32_t epi, f32x4 z, float &am, bool ok = true) {
+  if constexpr (ACT == ACT_RT) {
+    if (epi & EPI_RELU) return epi_act<ACT_RELU>(epi, z, am, ok);
+    if (epi & EPI_GELU) return epi_act<ACT_GELU>(epi, z, am, ok);
+    if (epi & EPI_SILU) return epi_act<ACT_SILU>(epi, z, am, ok);
+    return epi_act<ACT_NONE>(epi, z, am, ok);
   }
-  am = fmaxf(am, fmaxf(fmaxf(fabsf(z[0]), fabsf(z[1])), fmaxf(fabsf(z[2]), fabsf(z[3]))));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) z[e] = act_apply<ACT>(z[e]);
+  const float q = fmaxf(fmaxf(fabsf(z[0]), fabsf(z[1])), fmaxf(fabsf(z[2]), fabsf(z[3])));
+  am = fmaxf(am, ok ? q : 0.0f);
   // fold each quad in as it goes: left free, the compiler regroups the max over the whole
   // tile and keeps the |Y| values live across the epilogue (spilling the kernel)
   asm volatile("" : "+v"(am));
@@ -506,13 +524,14 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(f32x4 v) {
 
 // Fused store of one accumulator quad: 4 consecutive n of row m (n a multiple of 4, so a column
 // bias quad is one aligned 16-byte load).
+template <int ACT>
 __device__ __forceinline__ void store_quad_fused(const KernelArgs &args, int64_t m, int64_t n,
                                                  f32x4 v, float alpha, EpiCtx &ec) {
   if (m >= args.M || n >= args.N) return;
   v = v * alpha;
   if (args.epi & EPI_BIAS_ROW) v = v + args.bias[m];
   if (args.epi & EPI_BIAS_COL) v = v + *(const f32x4 *)(args.bias + n);
-  v = epi_act(args.epi, v, ec.am);
+  v = epi_act<ACT>(args.epi, v, ec.am);
   if (args.out_fp8) {
     *(uint32_t *)(args.C + m * args.ldc + n) = pack_e4m3x4(v * ec.inv_d);
   } else if (args.out_bf16) {
@@ -523,11 +542,11 @@ __device__ __forceinline__ void store_quad_fused(const KernelArgs &args, int64_t
   }
 }
 
-template <bool FUSED, class CFG>
+template <int FUSE, class CFG>
 __device__ __forceinline__ void store_quad_sel(const KernelArgs &args, int64_t m, int64_t n,
                                                f32x4 v, float alpha, EpiCtx &ec) {
-  if constexpr (FUSED)
-    store_quad_fused(args, m, n, v, alpha, ec);
+  if constexpr (FUSE != FUSE_OFF)
+    store_quad_fused<FUSE>(args, m, n, v, alpha, ec);
   else
     store_quad<CFG>(args, m, n, v, alpha);
 }
@@ -561,7 +580,7 @@ __device__ __forceinline__ f32x4 acc_quad(const f32x16 (&acc)[CFG::FM][CFG::FN])
 
 // Whole tile: C = cast(alpha * acc), one accumulator quad at a time.  The lane holds, for its
 // MFMA block (f, g), rows m = f*32 + lane%32 and columns n = g*32 + 8q + 4*(lane/32) + 0..3.
-template <class CFG, bool FUSED = false>
+template <class CFG, int FUSE = FUSE_OFF>
 __device__ __forceinline__ void epilogue(const KernelArgs &args, const WorkItem &w,
                                          const f32x16 (&acc)[CFG::FM][CFG::FN], float alpha,
                                          int wm, int wn, int tid, EpiCtx &ec) {
@@ -576,7 +595,7 @@ __device__ __forceinline__ void epilogue(const KernelArgs &args, const WorkItem 
       for (int q = 0; q < 4; ++q) {
         const f32x4 v = {acc[f][g][4 * q + 0], acc[f][g][4 * q + 1], acc[f][g][4 * q + 2],
                          acc[f][g][4 * q + 3]};
-        store_quad_sel<FUSED, CFG>(args, mbase + f * 32, nbase + g * 32 + q * 8, v, alpha, ec);
+        store_quad_sel<FUSE, CFG>(args, mbase + f * 32, nbase + g * 32 + q * 8, v, alpha, ec);
       }
 }
 
@@ -667,7 +686,7 @@ __device__ __forceinline__ uint32_t slot_byte(int64_t slot) {
 // partial; every later split waits until the lock equals its K_idx, adds the slot to its own sum
 // and either stores it back (middle) or finishes the tile (final).  The lock then becomes
 // K_idx + k_tile_count.  Sums are formed left to right in K.
-template <class CFG, bool FUSED = false>
+template <class CFG, int FUSE = FUSE_OFF>
 __device__ __forceinline__ void fixup_chain(const KernelArgs &args, const WorkItem &w,
                                             const f32x16 (&acc)[CFG::FM][CFG::FN], float alpha,
                                             int wm, int wn, int tid, EpiCtx &ec) {
@@ -705,8 +724,8 @@ __device__ __forceinline__ void fixup_chain(const KernelArgs &args, const WorkIt
             if (to_slot)
               store_coherent(pr, slot + qi * CFG::THREADS * 16, v);
             else
-              store_quad_sel<FUSED, CFG>(args, mbase + f * 32, nbase + g * 32 + q * 8, v, alpha,
-                                         ec);
+              store_quad_sel<FUSE, CFG>(args, mbase + f * 32, nbase + g * 32 + q * 8, v, alpha,
+                                        ec);
           }
           // one batch of four loads in flight at a time: the accumulators fill most registers
           __builtin_amdgcn_sched_barrier(0);
@@ -751,7 +770,7 @@ __device__ __forceinline__ void fixup_separate_store(const KernelArgs &args, con
 // waits on another unit's reduction): unit b, the j-th of the n units u0..u1 of tile t, waits for
 // all n arrivals, then sums the n partials of its 1/n share of the tile in K order (u0 first --
 // the same association as the chain) and writes that share of C.
-template <class CFG, bool FUSED = false>
+template <class CFG, int FUSE = FUSE_OFF>
 __device__ __forceinline__ void fixup_separate_reduce(const KernelArgs &args, const WorkItem &w,
                                                       float alpha, int32_t b, int tid,
                                                       EpiCtx &ec) {
@@ -799,7 +818,7 @@ __device__ __forceinline__ void fixup_separate_reduce(const KernelArgs &args, co
     const int wm = wave_src / CFG::WGN, wn = wave_src % CFG::WGN;
     const int64_t m = (int64_t)w.m * CFG::BM + wm * CFG::WM + f * 32 + (lane & 31);
     const int64_t nn = (int64_t)w.n * CFG::BN + wn * CFG::WN + g * 32 + q * 8 + (lane >> 5) * 4;
-    store_quad_sel<FUSED, CFG>(args, m, nn, sum, alpha, ec);
+    store_quad_sel<FUSE, CFG>(args, m, nn, sum, alpha, ec);
   }
 }
 
@@ -822,6 +841,7 @@ gemm_kernel(KernelArgs args) {
 
   float alpha = 1.0f;
   if constexpr (CFG::DT == DT_FP8) alpha = (*args.scale_a) * (*args.scale_b);
+  constexpr int FUSE = FUSED ? ACT_RT : FUSE_OFF;
   EpiCtx ec = {1.0f, 0.0f};
   if constexpr (FUSED) ec = epi_init(args);
 
@@ -980,7 +1000,7 @@ gemm_kernel(KernelArgs args) {
 
     if (cw.role == ROLE_WHOLE) {
       if (FUSED) {
-        epilogue<CFG, FUSED>(args, cw, acc, alpha, wm, wn, tid, ec);  // direct stores
+        epilogue<CFG, FUSE>(args, cw, acc, alpha, wm, wn, tid, ec);  // direct stores
       } else if (args.out_bf16) {
         // The stage read last (c - 1) becomes the staging area; its next fill is the pending
         // producer step, which is issued only after the barrier below.  Every wave has finished
@@ -997,7 +1017,7 @@ gemm_kernel(KernelArgs args) {
         epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid, ec);
       }
     } else if (args.sk_mode == SK_CHAIN)
-      fixup_chain<CFG, FUSED>(args, cw, acc, alpha, wm, wn, tid, ec);
+      fixup_chain<CFG, FUSE>(args, cw, acc, alpha, wm, wn, tid, ec);
     else
       fixup_separate_store<CFG>(args, cw, acc, b, tid);
 
@@ -1010,7 +1030,7 @@ gemm_kernel(KernelArgs args) {
     cursor_init(args.sp, b, rc);
     WorkItem rw;
     while (cursor_next(args.sp, rc, rw))
-      if (rw.role != ROLE_WHOLE) fixup_separate_reduce<CFG, FUSED>(args, rw, alpha, b, tid, ec);
+      if (rw.role != ROLE_WHOLE) fixup_separate_reduce<CFG, FUSE>(args, rw, alpha, b, tid, ec);
   }
   wait_vmcnt<0>();
   if constexpr (FUSED)
@@ -1556,17 +1576,75 @@ constexpr int wide_lds_bytes() {
   return CFG::LDS_BYTES + CFG::WAVES * kWideSlice;
 }
 
+// Bias of a 16 x 16-block sub-tile as the lane meets it: rows m0 + 16f + lane%16 (one value per
+// row block f, all loaded here) and columns n0 + 16g + 4(lane/16) + 0..3 (one quad per column
+// block g, loaded by col() one block ahead of its use); zero where the bias is absent or past M
+// or N (range-checked loads).  Without a bias no load is issued at all: a wait on one would also
+// wait for the next item's operand loads, which are still in flight when the epilogue starts.
+template <class CFG>
+struct WideBias {
+  __amdgpu_buffer_rsrc_t cols;
+  int64_t nb;
+  float row[CFG::FM];
+  uint32_t ok;  // bit f: row block f inside C; bit 16 + g: column block g inside C
+  bool by_col;
+
+  __device__ __forceinline__ void init(const KernelArgs &args, int64_t m0, int64_t n0, int lane) {
+    static_assert(CFG::FM <= 16 && CFG::FN <= 16, "one bit per block");
+    const int64_t mb = m0 + (lane & 15);
+    nb = n0 + (lane >> 4) * 4;
+    by_col = (args.epi & EPI_BIAS_COL) != 0;
+    cols = make_rsrc((const char *)args.bias, by_col ? args.N * 4 : 0);
+    ok = 0;
+#pragma unroll
+    for (int f = 0; f < CFG::FM; ++f) {
+      row[f] = 0.0f;
+      ok |= (mb + f * 16 < args.M ? 1u : 0u) << f;
+    }
+    if (args.epi & EPI_BIAS_ROW) {
+      const __amdgpu_buffer_rsrc_t rows = make_rsrc((const char *)args.bias, args.M * 4);
+#pragma unroll
+      for (int f = 0; f < CFG::FM; ++f)
+        row[f] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rows, (uint32_t)((mb + f * 16) * 4), 0, 0));
+    }
+#pragma unroll
+    for (int g = 0; g < CFG::FN; ++g) ok |= (nb + g * 16 < args.N ? 1u : 0u) << (16 + g);
+  }
+  __device__ __forceinline__ f32x4 col(int g) const {
+    if (!by_col) return f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    return __builtin_bit_cast(
+        f32x4, __builtin_amdgcn_raw_buffer_load_b128(cols, (uint32_t)((nb + g * 16) * 4), 0, 0));
+  }
+  __device__ __forceinline__ bool inside(int f, int g) const {
+    return ((ok >> f) & (ok >> (16 + g)) & 1u) != 0;
+  }
+};
+
+// Y of accumulator quad (f, g) of a 16 x 16-block sub-tile: alpha * Acc + bias, then the
+// activation and, inside C, the amax.
+template <class CFG, int ACT>
+__device__ __forceinline__ f32x4 wide_fused_quad(const KernelArgs &args, const acc_t<CFG> &blk,
+                                                 float alpha, f32x4 bcol, const WideBias<CFG> &bias,
+                                                 EpiCtx &ec, int f, int g) {
+  const f32x4 a = quad_of<true>(blk, 0);
+  f32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = fmaf(a[e], alpha, bcol[e] + bias.row[f]);
+  return epi_act<ACT>(args.epi, v, ec.am, bias.inside(f, g));
+}
+
 // bf16 output of a 128 x 128 sub-tile through the wave's LDS slice, 32 rows at a time.  Chunk c
 // (16 bytes) of staged row r sits at chunk position c ^ (r mod 16): the rows one write touches
 // and the 4 rows one read-back touches each spread over every bank.  16 lanes store one whole
-// 256-byte row segment.  FUSED adds the bias, the activation and the amax (16 x 16 blocks): rows
-// and columns past the edge of C hold zero accumulators and read zero bias, so they give Y = 0.
-template <class CFG, bool FUSED = false>
+// 256-byte row segment.  A fused FUSE adds the bias, the activation and the amax (16 x 16
+// blocks).
+template <class CFG, int FUSE = FUSE_OFF>
 __device__ __forceinline__ void epilogue_wide(const KernelArgs &args, const WorkItem &w,
                                               const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
                                               float alpha, int wm, int wn, int lane, lds_t *slice,
                                               EpiCtx &ec) {
-  static_assert(!FUSED || CFG::MI == 16, "fused epilogue on 16 x 16 blocks");
+  static_assert(FUSE == FUSE_OFF || CFG::MI == 16, "fused epilogue on 16 x 16 blocks");
   typedef u32x2 __attribute__((address_space(3))) *p64;
   typedef u32x4 __attribute__((address_space(3))) *p128;
   static_assert(CFG::WN * 2 == 256 && CFG::WM == 128, "rows of the staged sub-tile are 256 bytes");
@@ -1615,48 +1693,41 @@ __device__ __forceinline__ void epilogue_wide(const KernelArgs &args, const Work
     // 16-byte chunk 2g + (lane/16)/2 of its row, half (lane/16) mod 2; two blocks per round
     const int wrow = lane & 15, kq = lane >> 4;
     lds_t *wr_row = slice + wrow * 256 + (kq & 1) * 8;
-    // fused: bias through range-checked buffer loads (zero past M or N)
-    f32x4 bcol[CFG::FN];
-    const __amdgpu_buffer_rsrc_t brs =
-        make_rsrc((const char *)args.bias, ((args.epi & EPI_BIAS_COL) ? args.N : args.M) * 4);
-    if constexpr (FUSED) {
-#pragma unroll
-      for (int g = 0; g < CFG::FN; ++g) bcol[g] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      if (args.epi & EPI_BIAS_COL) {
-#pragma unroll
-        for (int g = 0; g < CFG::FN; ++g)
-          bcol[g] = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                         brs, (uint32_t)((n0 + g * 16 + kq * 4) * 4), 0, 0));
-      }
+    // fused: column-block major inside each round of two row blocks, so one column bias quad
+    // serves both (loaded one column block ahead)
+    WideBias<CFG> bias;
+    f32x4 bq;
+    if constexpr (FUSE != FUSE_OFF) {
+      bias.init(args, m0, n0, lane);
+      bq = bias.col(0);
     }
 #pragma unroll
     for (int p = 0; p < CFG::FM / 2; ++p) {
 #pragma unroll
-      for (int fp = 0; fp < 2; ++fp) {
-        float brow = 0.0f;
-        if constexpr (FUSED)
-          if (args.epi & EPI_BIAS_ROW)
-            brow = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(
-                           brs, (uint32_t)((m0 + (2 * p + fp) * 16 + wrow) * 4), 0, 0));
+      for (int g = 0; g < CFG::FN; ++g) {
+        f32x4 bnext;
+        if constexpr (FUSE != FUSE_OFF) bnext = bias.col((g + 1) % CFG::FN);
 #pragma unroll
-        for (int g = 0; g < CFG::FN; ++g) {
-          f32x4 v = quad_of<true>(acc[2 * p + fp][g], 0) * alpha;
-          if constexpr (FUSED) v = epi_act(args.epi, v + brow + bcol[g], ec.am);
+        for (int fp = 0; fp < 2; ++fp) {
+          f32x4 v;
+          if constexpr (FUSE != FUSE_OFF)
+            v = wide_fused_quad<CFG, FUSE>(args, acc[2 * p + fp][g], alpha, bq, bias, ec,
+                                           2 * p + fp, g);
+          else
+            v = quad_of<true>(acc[2 * p + fp][g], 0) * alpha;
           *(p64)(wr_row + fp * 16 * 256 + (((2 * g + (kq >> 1)) ^ wrow) * 16)) =
               u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (FUSE != FUSE_OFF) bq = bnext;
       }
       read_back(p);
     }
   }
 }
 
-// fp32 output straight from the accumulation registers, one quad (16 bytes) per lane and store;
-// FUSED: any output type, one quad per store (4 bytes of e4m3 codes, 8 of bf16, 16 of fp32).
-template <class CFG, bool FUSED = false>
+// fp32 output straight from the accumulation registers, one quad (16 bytes) per lane and store.
+template <class CFG, int FUSE = FUSE_OFF>
 __device__ __forceinline__ void epilogue_direct(const KernelArgs &args, const WorkItem &w,
                                                 const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
                                                 float alpha, int wm, int wn, int lane,
@@ -1670,10 +1741,50 @@ __device__ __forceinline__ void epilogue_direct(const KernelArgs &args, const Wo
     for (int g = 0; g < CFG::FN; ++g)
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        store_quad_sel<FUSED, CFG>(args, mbase + f * MI, nbase + g * MI + q * 8,
+        store_quad_sel<FUSE, CFG>(args, mbase + f * MI, nbase + g * MI + q * 8,
                                    quad_of<true>(acc[f][g], q), alpha, ec);
         __builtin_amdgcn_sched_barrier(0);
       }
+}
+
+// Fused fp32 or e4m3 output of a 16 x 16-block sub-tile straight from the accumulation registers,
+// one quad per store (16 bytes of fp32, 4 of e4m3 codes; for e4m3 this measured faster than
+// staging the codes through LDS, which needs registers the e4m3 kernel does not have to spare).
+// Column-block major: the lane's row biases (one per row block) are loaded first, a column
+// block's bias quad one block ahead of its use.  Without a bias of that orientation the loads go
+// to an empty buffer range and read zero, so no branch sits in the loop.
+template <class CFG, int ACT>
+__device__ __forceinline__ void epilogue_direct_fused(const KernelArgs &args, const WorkItem &w,
+                                                      const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
+                                                      float alpha, int wm, int wn, int lane,
+                                                      EpiCtx &ec) {
+  static_assert(CFG::MI == 16, "16 x 16 blocks");
+  const int64_t m0 = (int64_t)w.m * CFG::BM + wm * CFG::WM;
+  const int64_t n0 = (int64_t)w.n * CFG::BN + wn * CFG::WN;
+  if (m0 >= args.M || n0 >= args.N) return;  // the wave's sub-tile lies past the edge of C
+  const int64_t mb = m0 + (lane & 15), nb = n0 + (lane >> 4) * 4;
+  WideBias<CFG> bias;
+  bias.init(args, m0, n0, lane);
+  f32x4 bq = bias.col(0);
+#pragma unroll
+  for (int g = 0; g < CFG::FN; ++g) {
+    const f32x4 bnext = bias.col((g + 1) % CFG::FN);
+    const int64_t n = nb + g * 16;
+#pragma unroll
+    for (int f = 0; f < CFG::FM; ++f) {
+      const int64_t m = mb + f * 16;
+      const bool ok = bias.inside(f, g);
+      const f32x4 v = wide_fused_quad<CFG, ACT>(args, acc[f][g], alpha, bq, bias, ec, f, g);
+      if (ok) {
+        if (args.out_fp8)
+          *(uint32_t *)(args.C + m * args.ldc + n) = pack_e4m3x4(v * ec.inv_d);
+        else
+          *(f32x4 *)(args.C + (m * args.ldc + n) * 4) = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bq = bnext;
+  }
 }
 
 template <class CFG, bool RAGGED_K>
@@ -1750,7 +1861,7 @@ struct WideProducer {
   }
 };
 
-template <class CFG, bool RAGGED_K, bool FUSED = false>
+template <class CFG, bool RAGGED_K, int FUSE = FUSE_OFF>
 __global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::THREADS),
                                amdgpu_waves_per_eu(1, 1)))
 gemm_kernel_wide(KernelArgs args) {
@@ -1772,7 +1883,7 @@ gemm_kernel_wide(KernelArgs args) {
   float alpha = 1.0f;
   if constexpr (CFG::DT == DT_FP8) alpha = (*args.scale_a) * (*args.scale_b);
   EpiCtx ec = {1.0f, 0.0f};
-  if constexpr (FUSED) ec = epi_init(args);
+  if constexpr (FUSE != FUSE_OFF) ec = epi_init(args);
 
   uint32_t aoff[CFG::KSUB][CFG::CPL], boff[CFG::KSUB][CFG::CPL];
   {
@@ -1926,13 +2037,15 @@ gemm_kernel_wide(KernelArgs args) {
 
     if constexpr (CFG::MI == 16) mfma_wait_states();  // the last MFMAs' results are written
     if (args.out_bf16)
-      epilogue_wide<CFG, FUSED>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
+      epilogue_wide<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
+    else if constexpr (FUSE != FUSE_OFF)
+      epilogue_direct_fused<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, ec);
     else
-      epilogue_direct<CFG, FUSED>(args, cw, acc, alpha, wm, wn, lane, ec);
+      epilogue_direct<CFG>(args, cw, acc, alpha, wm, wn, lane, ec);
     cvalid = cursor_next(args.sp, ccur, cw);
   }
   wait_vmcnt<0>();
-  if constexpr (FUSED)
+  if constexpr (FUSE != FUSE_OFF)
     if (args.epi & EPI_AMAX)
       publish_amax<CFG::WAVES>(args.amax, ec.am, smem + CFG::LDS_BYTES, wave, lane);
 }
@@ -1946,7 +2059,7 @@ gemm_kernel_wide(KernelArgs args) {
 // passed -- so H(c+1) sits after row 0.  B of step c+1 goes into the other buffer, and the loads
 // of step c+S (begun by H(c+1)) go out over the first half of the slots after the handshake,
 // which leaves them more than half a k-step before H(c+2) waits for them.
-template <class CFG, bool RAGGED_K, bool FUSED = false>
+template <class CFG, bool RAGGED_K, int FUSE = FUSE_OFF>
 __global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::THREADS),
                                amdgpu_waves_per_eu(1, 1)))
 gemm_kernel_wide1(KernelArgs args) {
@@ -1968,7 +2081,7 @@ gemm_kernel_wide1(KernelArgs args) {
   float alpha = 1.0f;
   if constexpr (CFG::DT == DT_FP8) alpha = (*args.scale_a) * (*args.scale_b);
   EpiCtx ec = {1.0f, 0.0f};
-  if constexpr (FUSED) ec = epi_init(args);
+  if constexpr (FUSE != FUSE_OFF) ec = epi_init(args);
 
   uint32_t aoff[1][CFG::CPL], boff[1][CFG::CPL];
   {
@@ -2097,13 +2210,15 @@ gemm_kernel_wide1(KernelArgs args) {
     }
     mfma_wait_states();  // the last MFMAs' results are written
     if (args.out_bf16)
-      epilogue_wide<CFG, FUSED>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
+      epilogue_wide<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
+    else if constexpr (FUSE != FUSE_OFF)
+      epilogue_direct_fused<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, ec);
     else
-      epilogue_direct<CFG, FUSED>(args, cw, acc, alpha, wm, wn, lane, ec);
+      epilogue_direct<CFG>(args, cw, acc, alpha, wm, wn, lane, ec);
     cvalid = cursor_next(args.sp, ccur, cw);
   }
   wait_vmcnt<0>();
-  if constexpr (FUSED)
+  if constexpr (FUSE != FUSE_OFF)
     if (args.epi & EPI_AMAX)
       publish_amax<CFG::WAVES>(args.amax, ec.am, smem + CFG::LDS_BYTES, wave, lane);
 }

@@ -222,3 +222,30 @@ def test_fused_path_keeps_the_products(dev, flags, tile, out):
     plain = decode_output(C, torch)
     assert np.array_equal(fused, plain)
     assert am == float(np.float32(np.abs(plain).max())) or out == "bf16"
+
+
+@pytest.mark.parametrize("kern", [("wide", L.GEMM_FLAG_WIDE, 256), ("coop", 0, 128),
+                                  ("streamk", 0, 128)])
+@pytest.mark.parametrize("out", ["bf16", "e4m3", "f32"])
+@pytest.mark.parametrize("bias_kind", ["row", "col"])
+def test_amax_ignores_positions_past_the_edge(dev, kern, out, bias_kind):
+    """Ragged M and N: the tile positions past the edge of C have zero accumulators but still
+    meet a bias (a row bias reaches columns past N, a column bias rows past M).  With every bias
+    below -C, |Y| there would exceed every |Y| inside C, so amax must come from inside C only:
+    exactly max |C + bias| for integer-exact products."""
+    name, flags, tile = kern
+    M, N, K = 300, 264, (64 if name != "streamk" else 4096)
+    op = gi.rowsum_pattern(M, N, K, "bf16")                     # C = 7K/16 everywhere
+    c = 7 * K / 16
+    n_bias = M if bias_kind == "row" else N
+    bias = (-c - 8.0 - (np.arange(n_bias) % 64) / 4.0).astype(np.float32)  # Z in [-23.75, -8]
+    sched = L.GEMM_SCHED_STREAMK if name == "streamk" else L.GEMM_SCHED_PERSISTENT
+    workers = 7 if name == "streamk" else 3
+    got, am, plan = run_epi(op, dev, out, bias_kind, bias, None, True, 0.125, flags, sched,
+                            workers, tile)
+    _, y = expected(op, bias_kind, bias, None)
+    assert am == E.amax(y) == 23.75, (name, out, bias_kind, am)
+    if out == "e4m3":
+        assert np.array_equal(E4M3_TABLE[got], E4M3_TABLE[E.quantize_e4m3(y, 0.125)])
+    else:
+        assert np.array_equal(got, y)
