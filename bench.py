@@ -148,6 +148,13 @@ RUNS = {
     "bf16_streamk_chain": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256, 0,
                            "chain"),
     "bf16_256": ("bf16_256", "linear_n", 1, "static", 128, "f32", 0),
+    # the other mapping families: 2D blocking (the planner's box: the 32 tiles an XCD runs at a
+    # time as a 4 x 8 box) and Morton
+    "bf16_4096_blocked": ("bf16_4096", "blocked", 0, "persistent", 0, "bf16", 0),
+    "fp8_8192_blocked": ("fp8_8192", "blocked", 0, "persistent", 0, "bf16", 0),
+    "bf16_mlp_up_blocked": ("bf16_mlp_up", "blocked", 0, "persistent", 0, "bf16", 0),
+    "fp8_8192_morton": ("fp8_8192", "morton", 1, "persistent", 0, "bf16", 0),
+    "bf16_mlp_up_morton": ("bf16_mlp_up", "morton", 1, "persistent", 0, "bf16", 0),
     # fused epilogues: the MLP up-projection with its bias and GELU; an FP8 layer whose output
     # is quantised back to e4m3 with amax tracking
     "bf16_mlp_up_bias_gelu": ("bf16_mlp_up", "grouped_m", 8, "persistent", 0, "bf16", 0, 0, "",
@@ -243,7 +250,8 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
         "workload": wl_name, "M": op.M, "N": op.N, "K": op.K, "dtype": op.dtype, "out": out,
         "tile": [info.bm, info.bn, info.bk], "stages": info.stages, "mapping": mapping,
         "kernel": ["cooperative", "ping-pong", "register-staged", "wide-wave"][info.kernel],
-        "group": group, "sched": sched, "grid": info.grid, "epilogue": epi_spec,
+        "group": info.group, "group_n": info.group_n, "sched": sched, "grid": info.grid,
+        "epilogue": epi_spec,
         "dp_tiles": info.dp_tiles, "sk_tiles": info.sk_tiles, "warmup_launches": n_warm,
         "ms_per_step": wall * 1e3 / steps, "kernel_us": dev_ms * 1e3,
         "tflops": flops / (wall / steps) / 1e12, "kernel_tflops": flops / (dev_ms * 1e-3) / 1e12,
@@ -328,14 +336,16 @@ def main():
     secondary = {}
     if not args.no_secondary:
         for name in ("bf16_4096_pp", "bf16_4096_coop", "bf16_4096_linear", "bf16_4096_t128",
-                     "fp8_8192_pp", "fp8_8192_e4m3_amax", "fp8_8192", "bf16_mlp_up_bias_gelu",
-                     "bf16_mlp_up", "bf16_streamk", "bf16_256"):
+                     "bf16_4096_blocked", "fp8_8192_pp", "fp8_8192_e4m3_amax", "fp8_8192_blocked",
+                     "fp8_8192_morton", "fp8_8192", "bf16_mlp_up_bias_gelu", "bf16_mlp_up",
+                     "bf16_streamk", "bf16_256"):
             steps = max(10, args.steps // (4 if name.startswith("fp8_8192") else 1))
             r = time_run(name, steps, max(2, args.warmup // 2), torch, dg, gi, cache,
                          args.settle_ms / 2)
             secondary[name] = {k: r[k] for k in ("kernel_us", "kernel_tflops", "frac_of_peak",
                                                  "hbm_gbs_alg", "tile", "grid", "mapping",
-                                                 "sched", "kernel", "out", "epilogue")}
+                                                 "sched", "kernel", "out", "epilogue",
+                                                 "group", "group_n")}
             if name in cache:
                 del cache[name]
     cache.clear()

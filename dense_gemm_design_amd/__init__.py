@@ -6,7 +6,8 @@ is its Python binding.  See gemm() for a one-call helper on torch tensors.
 from . import _lib
 from ._lib import (GemmDesc, GemmError, Plan, make_desc, load,  # noqa: F401
                    GEMM_BF16, GEMM_FP8_E4M3, GEMM_F32, GEMM_MAP_LINEAR_N, GEMM_MAP_LINEAR_M,
-                   GEMM_MAP_GROUPED_M, GEMM_MAP_GROUPED_N, GEMM_SCHED_STATIC,
+                   GEMM_MAP_GROUPED_M, GEMM_MAP_GROUPED_N, GEMM_MAP_BLOCKED, GEMM_MAP_MORTON,
+                   GEMM_SCHED_STATIC,
                    GEMM_SCHED_PERSISTENT, GEMM_SCHED_STREAMK, GEMM_SCHED_AUTO, GEMM_FLAG_TRACE,
                    GEMM_FLAG_NO_XCD_REMAP, GEMM_FLAG_STREAMK_CHAIN, GEMM_FLAG_PINGPONG,
                    GEMM_FLAG_COOPERATIVE, GEMM_FLAG_REGSTAGED, GEMM_FLAG_WIDE,
@@ -14,7 +15,8 @@ from ._lib import (GemmDesc, GemmError, Plan, make_desc, load,  # noqa: F401
                    GEMM_EPI_SILU, GEMM_EPI_AMAX, GemmEpilogueArgs)
 
 MAPPINGS = {"linear_n": GEMM_MAP_LINEAR_N, "linear_m": GEMM_MAP_LINEAR_M,
-            "grouped_m": GEMM_MAP_GROUPED_M, "grouped_n": GEMM_MAP_GROUPED_N}
+            "grouped_m": GEMM_MAP_GROUPED_M, "grouped_n": GEMM_MAP_GROUPED_N,
+            "blocked": GEMM_MAP_BLOCKED, "morton": GEMM_MAP_MORTON}
 SCHEDS = {"static": GEMM_SCHED_STATIC, "persistent": GEMM_SCHED_PERSISTENT,
           "streamk": GEMM_SCHED_STREAMK, "auto": GEMM_SCHED_AUTO}
 ACTIVATIONS = {None: 0, "relu": GEMM_EPI_RELU, "gelu": GEMM_EPI_GELU, "silu": GEMM_EPI_SILU}
@@ -23,7 +25,7 @@ OUT_DTYPES = {"f32": GEMM_F32, "bf16": GEMM_BF16, "e4m3": GEMM_FP8_E4M3}
 
 def gemm(A, B, out_dtype="f32", scale_a=None, scale_b=None, mapping="grouped_m", group=8,
          sched="auto", tile=0, flags=0, bias_row=None, bias_col=None, activation=None,
-         scale_d=None, amax=None):
+         scale_d=None, amax=None, group_n=0):
     """D = epilogue(alpha * A x B) for torch device tensors: A (M, K) row-major; B given as (N, K),
     i.e. the K x N operand in column-major storage; bf16 or uint8-coded e4m3 (then scale_a /
     scale_b are one-element float32 device tensors).  Optional fused epilogue: a float32 bias per
@@ -41,7 +43,7 @@ def gemm(A, B, out_dtype="f32", scale_a=None, scale_b=None, mapping="grouped_m",
     epi |= GEMM_EPI_AMAX if amax is not None else 0
     desc = make_desc(M, N, K, GEMM_FP8_E4M3 if fp8 else GEMM_BF16, OUT_DTYPES[out_dtype],
                      MAPPINGS[mapping], group, SCHEDS[sched], 0, tile, tile, 0, flags,
-                     epilogue=epi)
+                     epilogue=epi, group_n=group_n)
     plan = Plan(desc)
     dt = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8}[out_dtype]
     C = torch.empty((M, N), device=A.device, dtype=dt)

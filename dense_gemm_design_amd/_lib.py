@@ -17,6 +17,7 @@ GEMM_ERR_ALIGNMENT, GEMM_ERR_WORKSPACE, GEMM_ERR_HIP, GEMM_ERR_CAPACITY = -3, -4
 GEMM_BF16, GEMM_FP8_E4M3, GEMM_F32 = 0, 1, 2
 GEMM_ROW_MAJOR, GEMM_COL_MAJOR = 0, 1
 GEMM_MAP_LINEAR_N, GEMM_MAP_LINEAR_M, GEMM_MAP_GROUPED_M, GEMM_MAP_GROUPED_N = 0, 1, 2, 3
+GEMM_MAP_BLOCKED, GEMM_MAP_MORTON = 4, 5
 GEMM_SCHED_STATIC, GEMM_SCHED_PERSISTENT, GEMM_SCHED_STREAMK, GEMM_SCHED_AUTO = 0, 1, 2, 3
 GEMM_FLAG_TRACE = 0x1
 GEMM_FLAG_NO_XCD_REMAP = 0x2
@@ -45,7 +46,8 @@ class GemmDesc(ctypes.Structure):
                 ("mapping", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("sched", ctypes.c_int32), ("num_workers", ctypes.c_int32),
                 ("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
-                ("flags", ctypes.c_uint32), ("epilogue", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("epilogue", ctypes.c_uint32),
+                ("group_n", ctypes.c_int32)]
 
 
 class GemmEpilogueArgs(ctypes.Structure):
@@ -67,13 +69,13 @@ class GemmPlanInfo(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_int64), ("trace_offset", ctypes.c_int64),
                 ("trace_capacity", ctypes.c_int32), ("error_offset", ctypes.c_int32),
                 ("streamk_mode", ctypes.c_int32), ("kernel", ctypes.c_int32),
-                ("group", ctypes.c_int32)]
+                ("group", ctypes.c_int32), ("group_n", ctypes.c_int32), ("pad_", ctypes.c_int32)]
 
 
 class GemmConfigScore(ctypes.Structure):
     _fields_ = [("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
                 ("kernel", ctypes.c_int32), ("sched", ctypes.c_int32),
-                ("workers", ctypes.c_int32), ("group", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("workers", ctypes.c_int32), ("group", ctypes.c_int32), ("group_n", ctypes.c_int32),
                 ("cycles_mfma", ctypes.c_double), ("cycles_l2", ctypes.c_double),
                 ("cycles_local", ctypes.c_double), ("wave_efficiency", ctypes.c_double),
                 ("cycles_fixed", ctypes.c_double), ("score", ctypes.c_double)]
@@ -126,9 +128,9 @@ def _check(status, where):
 
 def make_desc(M, N, K, dtype_ab=GEMM_BF16, dtype_c=GEMM_F32, mapping=GEMM_MAP_LINEAR_N, group=1,
               sched=GEMM_SCHED_PERSISTENT, num_workers=0, bm=0, bn=0, bk=0, flags=0,
-              layout_a=GEMM_ROW_MAJOR, layout_b=GEMM_COL_MAJOR, epilogue=0):
+              layout_a=GEMM_ROW_MAJOR, layout_b=GEMM_COL_MAJOR, epilogue=0, group_n=0):
     return GemmDesc(M, N, K, dtype_ab, dtype_c, layout_a, layout_b, mapping, group, sched,
-                    num_workers, bm, bn, bk, flags, epilogue)
+                    num_workers, bm, bn, bk, flags, epilogue, group_n)
 
 
 def rank_configs(desc):

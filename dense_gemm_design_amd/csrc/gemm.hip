@@ -244,6 +244,33 @@ int choose_group(int mapping, int64_t Mt, int64_t Nt, int64_t chunk) {
   return best;
 }
 
+// Box of the blocked mapping for the same `chunk` tiles: H x W = chunk tile rows x columns (a
+// given H or W kept, the other one derived), reading H + W operand strips per k-step.  The
+// fewest strips win, the wider box on a tie.
+void choose_box(int64_t Mt, int64_t Nt, int64_t chunk, int32_t &H, int32_t &W) {
+  if (H > 0 && W > 0) return;
+  if (H > 0) {
+    W = (int32_t)std::min<int64_t>(std::max<int64_t>(cdiv(chunk, H), 1), std::max<int64_t>(Nt, 1));
+    return;
+  }
+  if (W > 0) {
+    H = (int32_t)std::min<int64_t>(std::max<int64_t>(cdiv(chunk, W), 1), std::max<int64_t>(Mt, 1));
+    return;
+  }
+  int64_t best = INT64_MAX;
+  for (int64_t h = 1; h <= 64; h *= 2) {
+    const int64_t hh = std::min<int64_t>(h, std::max<int64_t>(Mt, 1));
+    const int64_t ww = std::min<int64_t>(std::max<int64_t>(cdiv(chunk, hh), 1), std::max<int64_t>(Nt, 1));
+    const int64_t strips = hh + ww;
+    if (strips < best || (strips == best && ww > W)) {
+      best = strips;
+      H = (int32_t)hh;
+      W = (int32_t)ww;
+    }
+    if (h >= Mt) break;
+  }
+}
+
 struct ModelCand {
   int kind, bm, bn, sched;
 };
@@ -266,6 +293,7 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
       return GEMM_ERR_HIP;
   }
   const bool grouped = d.mapping == GEMM_MAP_GROUPED_M || d.mapping == GEMM_MAP_GROUPED_N;
+  const bool blocked = d.mapping == GEMM_MAP_BLOCKED;
   out.clear();
   for (const ModelCand &c : cands) {
     if (c.kind != KIND_COOP && d.K == 0) continue;  // the data-parallel kernels need K > 0
@@ -307,6 +335,12 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
     r.workers = P;
     const int X = P % 8 == 0 ? 8 : 1;
     r.group = grouped ? (d.group > 0 ? d.group : choose_group(d.mapping, Mt, Nt, P / X)) : 1;
+    r.group_n = 1;
+    if (blocked) {
+      r.group = d.group;
+      r.group_n = d.group_n;
+      choose_box(Mt, Nt, P / X, r.group, r.group_n);
+    }
     const double bytes_l2 = t * (kk * (bm + bn) * eb + bm * bn * ec);
     const double bytes_local = t * (kk * (bm + bn) * eb + kk * (bm * wgn + bn * wgm) * eb + bm * bn * ec);
     r.cycles_l2 = bytes_l2 / (ncu * kL2BytesPerClk);
@@ -376,9 +410,11 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if ((d.layout_a != GEMM_ROW_MAJOR && d.layout_a != GEMM_COL_MAJOR) ||
       (d.layout_b != GEMM_ROW_MAJOR && d.layout_b != GEMM_COL_MAJOR))
     return GEMM_ERR_INVALID_ARG;
-  if (d.mapping < GEMM_MAP_LINEAR_N || d.mapping > GEMM_MAP_GROUPED_N) return GEMM_ERR_INVALID_ARG;
-  const bool grouped = d.mapping == GEMM_MAP_GROUPED_M || d.mapping == GEMM_MAP_GROUPED_N;
+  if (d.mapping < GEMM_MAP_LINEAR_N || d.mapping > GEMM_MAP_MORTON) return GEMM_ERR_INVALID_ARG;
+  const bool blocked = d.mapping == GEMM_MAP_BLOCKED;
+  const bool grouped = d.mapping == GEMM_MAP_GROUPED_M || d.mapping == GEMM_MAP_GROUPED_N || blocked;
   if (grouped && d.group < 0) return GEMM_ERR_INVALID_ARG;  // 0: the planner picks G
+  if (blocked && d.group_n < 0) return GEMM_ERR_INVALID_ARG;
   if (d.sched < GEMM_SCHED_STATIC || d.sched > GEMM_SCHED_AUTO) return GEMM_ERR_INVALID_ARG;
   if (d.num_workers < 0 || d.bm < 0 || d.bn < 0 || d.bk < 0) return GEMM_ERR_INVALID_ARG;
   const uint32_t kind_flags =
@@ -479,6 +515,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   sp.Kt = (int32_t)Kt;
   sp.mapping = d.mapping;
   sp.G = grouped ? d.group : 1;
+  sp.G2 = blocked ? d.group_n : 1;
   if (sched == GEMM_SCHED_STATIC) {
     sp.P = (int32_t)tiles;
     sp.dp_tiles = (int32_t)tiles;
@@ -498,7 +535,9 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     if ((int64_t)sp.sk_tiles * Kt > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
   }
   sp.X = (d.flags & GEMM_FLAG_NO_XCD_REMAP) ? 1 : kXcds;
-  if (grouped && d.group == 0)  // the planner's G: fewest operand strips per XCD's run of tiles
+  if (blocked) {  // the planner's box: fewest operand strips per XCD's run of tiles
+    choose_box(Mt, Nt, sp.P % sp.X == 0 ? sp.P / sp.X : sp.P, sp.G, sp.G2);
+  } else if (grouped && d.group == 0)  // likewise for the strip width G
     sp.G = choose_group(d.mapping, Mt, Nt, sp.P % sp.X == 0 ? sp.P / sp.X : sp.P);
   sched_prepare(sp);
 
@@ -577,6 +616,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   in.streamk_mode = sk_mode;
   in.kernel = k->kind;
   in.group = sp.G;
+  in.group_n = sp.G2;
   *out = p;
   return GEMM_OK;
 }
@@ -591,7 +631,8 @@ int gemm_rank_configs(const gemm_desc *desc, gemm_config_score *items, size_t ca
   if (d.dtype_c != GEMM_F32 && d.dtype_c != GEMM_BF16 && d.dtype_c != GEMM_FP8_E4M3)
     return GEMM_ERR_INVALID_ARG;
   if (!epilogue_valid(d.epilogue)) return GEMM_ERR_INVALID_ARG;
-  if (d.mapping < GEMM_MAP_LINEAR_N || d.mapping > GEMM_MAP_GROUPED_N) return GEMM_ERR_INVALID_ARG;
+  if (d.mapping < GEMM_MAP_LINEAR_N || d.mapping > GEMM_MAP_MORTON) return GEMM_ERR_INVALID_ARG;
+  if (d.mapping == GEMM_MAP_BLOCKED && d.group_n < 0) return GEMM_ERR_INVALID_ARG;
   std::vector<gemm_config_score> ranked;
   const int st = rank_configs(d, ranked);
   if (st != GEMM_OK) return st;

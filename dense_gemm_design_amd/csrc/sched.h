@@ -6,7 +6,9 @@
 // Sources:
 //  * "DeepGEMM on SM90" page, CTA <-> output tile section and its mapping-family table: F(i) names
 //    the output tile of the i-th linear task; Linear N-fast, Linear M-fast, Grouped-M strip
-//    (M cut into strips of G tile-rows, M-fast inside), Grouped-N strip (the transpose).
+//    (M cut into strips of G tile-rows, M-fast inside), Grouped-N strip (the transpose), 2D
+//    blocking (the tiles that run together packed into a box, then the box moves) and Morton
+//    (Z-order: the bits of m and n interleaved).
 //    Persistence is not a mapping: a persistent worker p takes i = p, p + P, p + 2P, ...
 //  * "H100 Kernel Design" lesson, sections 9-10 (persistent grid-stride loop, Stream-K hybrid:
 //    data-parallel full waves, Stream-K only for a tail wave at most half full, backward tile
@@ -23,7 +25,14 @@
 
 namespace dg {
 
-enum Mapping { MAP_LINEAR_N = 0, MAP_LINEAR_M = 1, MAP_GROUPED_M = 2, MAP_GROUPED_N = 3 };
+enum Mapping {
+  MAP_LINEAR_N = 0,
+  MAP_LINEAR_M = 1,
+  MAP_GROUPED_M = 2,
+  MAP_GROUPED_N = 3,
+  MAP_BLOCKED = 4,
+  MAP_MORTON = 5
+};
 enum Role { ROLE_WHOLE = 0, ROLE_FIRST = 1, ROLE_MIDDLE = 2, ROLE_LAST = 3 };
 
 // Division of a non-negative 31-bit value by a fixed positive divisor as a multiply-high, add
@@ -52,10 +61,10 @@ DG_HD int32_t fdiv(int32_t n, const FastDiv &f) {
 
 struct SchedParams {
   int32_t Mt, Nt, Kt;      // tiles along M and N, k-tiles along K
-  int32_t mapping, G;      // F(i) family and strip width
+  int32_t mapping, G;      // F(i) family and strip width (blocked: box height in tile rows)
   int32_t P;               // workgroups in the launch (workers)
   int32_t X;               // XCDs the workgroups are dealt to round-robin (1 = no remap)
-  int32_t pad_;
+  int32_t G2;              // blocked: box width in tile columns
   int32_t dp_tiles;        // tasks i < dp_tiles run whole (data parallel)
   int32_t sk_tiles;        // the next sk_tiles tasks are split along K (Stream-K band)
   // divisors of the mapping and of the Stream-K band (filled by sched_prepare)
@@ -63,25 +72,33 @@ struct SchedParams {
   FastDiv div_g;           // G (grouped), unused otherwise
   FastDiv div_g_last;      // width of the short last strip (grouped), else = div_g
   FastDiv div_kt;          // Kt (Stream-K band), 1 when Kt == 0
-  int32_t full_strips;     // strips of exactly G
-  int32_t pad2_;
+  FastDiv div_box;         // blocked: G * G2 tiles of a full-height box
+  FastDiv div_box_last;    // blocked: (height of the short last box row) * G2
+  int32_t full_strips;     // strips (blocked: box rows) of exactly G
+  int32_t morton_size;     // Morton: the smallest power of two >= max(Mt, Nt)
 };
 
-// Fills the divisor fields from Mt, Nt, Kt, mapping and G.
+// Fills the divisor fields from Mt, Nt, Kt, mapping, G and G2.
 inline void sched_prepare(SchedParams &sp) {
   const int32_t G = sp.G < 1 ? 1 : sp.G;
+  const int32_t G2 = sp.G2 < 1 ? 1 : sp.G2;
   switch (sp.mapping) {
     case MAP_LINEAR_N: sp.div_major = make_fastdiv(sp.Nt > 0 ? sp.Nt : 1); break;
     case MAP_LINEAR_M: sp.div_major = make_fastdiv(sp.Mt > 0 ? sp.Mt : 1); break;
-    case MAP_GROUPED_M: sp.div_major = make_fastdiv((uint32_t)(G * (sp.Nt > 0 ? sp.Nt : 1))); break;
-    default: sp.div_major = make_fastdiv((uint32_t)(G * (sp.Mt > 0 ? sp.Mt : 1))); break;
+    case MAP_GROUPED_N: sp.div_major = make_fastdiv((uint32_t)(G * (sp.Mt > 0 ? sp.Mt : 1))); break;
+    default: sp.div_major = make_fastdiv((uint32_t)(G * (sp.Nt > 0 ? sp.Nt : 1))); break;
   }
   const int32_t rows = sp.mapping == MAP_GROUPED_N ? sp.Nt : sp.Mt;
   sp.full_strips = rows / G;
   const int32_t last = rows - sp.full_strips * G;
   sp.div_g = make_fastdiv((uint32_t)G);
   sp.div_g_last = make_fastdiv((uint32_t)(last > 0 ? last : G));
+  sp.div_box = make_fastdiv((uint32_t)(G * G2));
+  sp.div_box_last = make_fastdiv((uint32_t)((last > 0 ? last : G) * G2));
   sp.div_kt = make_fastdiv((uint32_t)(sp.Kt > 0 ? sp.Kt : 1));
+  int32_t size = 1;
+  while (size < sp.Mt || size < sp.Nt) size *= 2;
+  sp.morton_size = size;
 }
 
 struct WorkItem {
@@ -96,11 +113,39 @@ struct TileMN {
   int32_t m, n;
 };
 
+// Morton (Z-order) F(i): the i-th tile of the grid in the order of its interleaved code -- bit b
+// of n at code bit 2b, bit b of m at 2b + 1, so a 2 x 2 square goes (0,0) (0,1) (1,0) (1,1).  On a
+// grid that is not a power-of-two square the codes outside the grid are skipped: descend the
+// quadtree of the enclosing 2^k square, skipping whole quadrants by their count of grid tiles.
+DG_HD TileMN morton_tile(const SchedParams &sp, int32_t i) {
+  int32_t m0 = 0, n0 = 0;
+  for (int32_t half = sp.morton_size / 2; half >= 1; half /= 2) {
+#pragma unroll
+    for (int32_t q = 0; q < 4; ++q) {
+      const int32_t qm = m0 + (q >> 1) * half, qn = n0 + (q & 1) * half;
+      const int32_t rows = sp.Mt - qm < 0 ? 0 : (sp.Mt - qm < half ? sp.Mt - qm : half);
+      const int32_t cols = sp.Nt - qn < 0 ? 0 : (sp.Nt - qn < half ? sp.Nt - qn : half);
+      const int32_t cnt = rows * cols;
+      if (i < cnt || q == 3) {
+        m0 = qm;
+        n0 = qn;
+        break;
+      }
+      i -= cnt;
+    }
+  }
+  return TileMN{m0, n0};
+}
+
 // F(i) -> (m, n).  Grouped-M: a strip holds G tile-rows (fewer in a short last strip) and is
 // walked column by column, M-fast inside: i = strip * (G * Nt) + n * g + (m - strip * G).
-// Task indices fit in 32 bits (the planner rejects larger grids).
+// Blocked: box rows of G tile-rows (fewer in the last), each cut into boxes of G2 tile-columns
+// (fewer in the last) walked along N; inside a box of g rows, M-fast:
+// i = boxrow * (G * Nt) + box * (g * G2) + (n - box * G2) * g + (m - boxrow * G).  G2 = Nt is
+// Grouped-M(G).  Task indices fit in 32 bits (the planner rejects larger grids).
 DG_HD TileMN map_tile(const SchedParams &sp, int32_t i) {
   TileMN t;
+  if (sp.mapping == MAP_MORTON) return morton_tile(sp, i);
   const int32_t q = fdiv(i, sp.div_major);
   const int32_t r = i - q * (int32_t)sp.div_major.d;
   if (sp.mapping == MAP_LINEAR_N) {
@@ -109,6 +154,16 @@ DG_HD TileMN map_tile(const SchedParams &sp, int32_t i) {
   } else if (sp.mapping == MAP_LINEAR_M) {
     t.n = q;
     t.m = r;
+  } else if (sp.mapping == MAP_BLOCKED) {
+    // box row q (g rows), position r inside it: box b, position u inside the box
+    const bool last = q >= sp.full_strips;
+    const FastDiv &dbox = last ? sp.div_box_last : sp.div_box;
+    const FastDiv &dg = last ? sp.div_g_last : sp.div_g;
+    const int32_t b = fdiv(r, dbox);
+    const int32_t u = r - b * (int32_t)dbox.d;
+    const int32_t col = fdiv(u, dg);
+    t.m = q * sp.G + (u - col * (int32_t)dg.d);
+    t.n = b * sp.G2 + col;
   } else {
     // strip q, position r inside it; the strip is g wide (G, or less for the last one)
     const bool last = q >= sp.full_strips;

@@ -47,12 +47,18 @@ typedef enum {
 typedef enum { GEMM_BF16 = 0, GEMM_FP8_E4M3 = 1, GEMM_F32 = 2 } gemm_dtype;
 typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout;
 
-/* Tile mapping F(i) -> (m, n) ("DeepGEMM on SM90" page, mapping-family table). */
+/* Tile mapping F(i) -> (m, n) ("DeepGEMM on SM90" page, mapping-family table: linear, grouped
+ * strips, 2D blocking / box, Morton / Z-order). */
 typedef enum {
   GEMM_MAP_LINEAR_N = 0,   /* C00, C01, ..., C10, ...  (m = i / Nt, n = i % Nt)               */
   GEMM_MAP_LINEAR_M = 1,   /* C00, C10, ..., C01, ...  (m = i % Mt, n = i / Mt)               */
   GEMM_MAP_GROUPED_M = 2,  /* strips of G tile-rows, M-fast inside a strip                    */
-  GEMM_MAP_GROUPED_N = 3   /* strips of G tile-columns, N-fast inside a strip                 */
+  GEMM_MAP_GROUPED_N = 3,  /* strips of G tile-columns, N-fast inside a strip                 */
+  GEMM_MAP_BLOCKED = 4,    /* 2D blocking: boxes of group x group_n tiles (rows x columns) hold
+                              the tiles that run together; boxes walk along N, box rows along M;
+                              M-fast inside a box.  group_n = Nt is GROUPED_M(group)          */
+  GEMM_MAP_MORTON = 5      /* Z-order: tiles in the order of their bit-interleaved (m, n) code,
+                              n in the even bits; codes outside the grid are skipped          */
 } gemm_mapping;
 
 /* Assignment of tasks to workgroups ("H100 Kernel Design" lesson, sections 9.2-10.3). */
@@ -117,13 +123,17 @@ typedef struct gemm_desc {
   int32_t layout_a;          /* must be GEMM_ROW_MAJOR: a(m,k) at A[m*K + k]                    */
   int32_t layout_b;          /* must be GEMM_COL_MAJOR: b(k,n) at B[n*K + k]                    */
   int32_t mapping;           /* gemm_mapping                                                     */
-  int32_t group;             /* G for the grouped mappings (>= 1, or 0 = chosen by the planner);
-                                ignored by the linear ones                                      */
+  int32_t group;             /* G for the grouped mappings, the box height in tile rows for
+                                BLOCKED (>= 1, or 0 = chosen by the planner); ignored by the
+                                linear ones and MORTON                                          */
   int32_t sched;             /* gemm_sched                                                       */
   int32_t num_workers;       /* P for persistent / Stream-K; 0 = CUs x resident workgroups/CU    */
   int32_t bm, bn, bk;        /* tile shape; 0 = auto.  Supported: see gemm_create              */
   uint32_t flags;            /* GEMM_FLAG_*                                                      */
   uint32_t epilogue;         /* GEMM_EPI_* bits: fused bias / activation / amax (0 = none)      */
+  int32_t group_n;           /* BLOCKED: box width in tile columns (>= 1, or 0 = chosen by the
+                                planner, which then fills the box with the tiles one XCD runs
+                                at a time); ignored by the other mappings                      */
 } gemm_desc;
 
 /* One unit of work as the scheduler hands it out (gemm_schedule_enumerate, device trace). */
@@ -152,6 +162,8 @@ typedef struct gemm_plan_info {
   int32_t streamk_mode;      /* 0 lock chain, 1 separate reduction (meaningful when sk_tiles>0)  */
   int32_t kernel;            /* 0 cooperative, 1 ping-pong, 2 register-staged, 3 wide-wave       */
   int32_t group;             /* G of a grouped mapping as planned (1 for the linear ones)       */
+  int32_t group_n;           /* box width of BLOCKED as planned (1 for the other mappings)      */
+  int32_t pad_;
 } gemm_plan_info;
 
 /* device error word values (read back from the workspace after a run) */
@@ -213,8 +225,8 @@ typedef struct gemm_config_score {
   int32_t kernel;            /* as gemm_plan_info.kernel                                        */
   int32_t sched;             /* GEMM_SCHED_PERSISTENT or GEMM_SCHED_STREAMK                     */
   int32_t workers;           /* P the plan would launch                                         */
-  int32_t group;             /* G for a grouped mapping (1 for the linear ones)                 */
-  int32_t pad_;
+  int32_t group;             /* G for a grouped mapping, box height for BLOCKED (1 otherwise)  */
+  int32_t group_n;           /* box width for BLOCKED (1 otherwise)                             */
   double cycles_mfma;        /* modelled clocks, whole GEMM, matrix-core side                   */
   double cycles_l2;          /* L2 -> CU side: A/B tile loads and C                             */
   double cycles_local;       /* LDS side: tile fills, fragment reads, C staging                 */

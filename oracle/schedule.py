@@ -9,7 +9,9 @@ Sources
     the mapping F(i) -> (m, n) assigns the i-th linear task an output tile; Linear N-fast visits
     C00, C01, ... then C10; Linear M-fast visits C00, C10, ... then C01; Grouped-M cuts M into
     strips of G tile-rows and runs M-fast inside a strip; Grouped-N cuts N into strips of G
-    tile-columns and runs N-fast inside.  Static assignment gives CTA i the tile F(i);
+    tile-columns and runs N-fast inside; 2D blocking packs the tiles that run together into a
+    box (a local rectangle) and then moves the box; Morton is the Z-order of the bit-interleaved
+    tile coordinates.  Static assignment gives CTA i the tile F(i);
     persistent workers take i = p, p + P, p + 2P, ...
   * Same page, Kernel Configuration Heuristic: CTA count = ceil(M/BM) * ceil(N/BN),
     waves = ceil(CTAs / num_sms), wave efficiency = CTAs / (waves * num_sms).
@@ -22,6 +24,12 @@ Sources
 
 Reading where the pages are open (each is listed in the design doc):
   * a short last strip in the grouped mappings holds the remaining tile rows (columns);
+  * blocking: boxes of H tile-rows x W tile-columns; the boxes of a box row are visited along N,
+    box rows along M; inside a box M runs fastest (as in a Grouped-M strip); boxes at the bottom
+    and right edges hold what is left;
+  * Morton: n supplies the even bits of the code and m the odd ones (a 2 x 2 square is visited
+    (0,0), (0,1), (1,0), (1,1)); tiles are taken in increasing code order, so codes that fall
+    outside a grid which is not a power-of-two square are simply absent;
   * the Stream-K unit u owns iterations [floor(u T / P), floor((u+1) T / P));
   * roles: K_idx == 0 and final -> whole tile; K_idx == 0 only -> first; final only -> last;
     neither -> middle;
@@ -33,7 +41,7 @@ every XCD owns a contiguous run of worker ids.  It is enumerated here from that 
 """
 from dataclasses import dataclass
 
-LINEAR_N, LINEAR_M, GROUPED_M, GROUPED_N = 0, 1, 2, 3
+LINEAR_N, LINEAR_M, GROUPED_M, GROUPED_N, BLOCKED, MORTON = 0, 1, 2, 3, 4, 5
 STATIC, PERSISTENT, STREAMK = 0, 1, 2
 ROLE_WHOLE, ROLE_FIRST, ROLE_MIDDLE, ROLE_LAST = 0, 1, 2, 3
 
@@ -44,8 +52,19 @@ def tile_counts(M, N, K, BM, BN, BK):
     return cdiv(M, BM), cdiv(N, BN), cdiv(K, BK)
 
 
-def tile_order(mode, Mt, Nt, G=1):
-    """The list F(0), F(1), ... of (m, n) tile coordinates, built by walking the grid."""
+def morton_code(m, n):
+    """Interleave the bits of n (even positions) and m (odd positions)."""
+    code, bit = 0, 0
+    while (m >> bit) or (n >> bit):
+        code |= ((n >> bit) & 1) << (2 * bit)
+        code |= ((m >> bit) & 1) << (2 * bit + 1)
+        bit += 1
+    return code
+
+
+def tile_order(mode, Mt, Nt, G=1, W=1):
+    """The list F(0), F(1), ... of (m, n) tile coordinates, built by walking the grid.
+    G: strip width (grouped) or box height (blocked); W: box width (blocked)."""
     order = []
     if mode == LINEAR_N:
         for m in range(Mt):
@@ -71,6 +90,18 @@ def tile_order(mode, Mt, Nt, G=1):
             for m in range(Mt):
                 for n in cols:
                     order.append((m, n))
+    elif mode == BLOCKED:
+        if G < 1 or W < 1:
+            raise ValueError("box sides must be >= 1")
+        for row_start in range(0, Mt, G):             # box rows, along M
+            rows = range(row_start, min(row_start + G, Mt))
+            for col_start in range(0, Nt, W):         # boxes of the row, along N
+                for n in range(col_start, min(col_start + W, Nt)):
+                    for m in rows:                    # M-fast inside the box
+                        order.append((m, n))
+    elif mode == MORTON:
+        order = sorted(((m, n) for m in range(Mt) for n in range(Nt)),
+                       key=lambda t: morton_code(*t))
     else:
         raise ValueError(f"unknown mapping {mode}")
     return order
@@ -145,10 +176,11 @@ def role_of(k_idx, final):
     return ROLE_LAST if final else ROLE_MIDDLE
 
 
-def enumerate_schedule(M, N, K, BM, BN, BK, mapping, G, sched, P=None, X=8, xcd_remap=True):
+def enumerate_schedule(M, N, K, BM, BN, BK, mapping, G, sched, P=None, X=8, xcd_remap=True,
+                       W=1):
     """Every work item of the launch, grouped by workgroup, in each workgroup's order."""
     Mt, Nt, Kt = tile_counts(M, N, K, BM, BN, BK)
-    order = tile_order(mapping, Mt, Nt, G)
+    order = tile_order(mapping, Mt, Nt, G, W)
     tiles = Mt * Nt
     items = []
     if sched == STATIC:

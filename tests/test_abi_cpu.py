@@ -79,7 +79,12 @@ def create(**kw):
     (dict(dtype_ab=7), L.GEMM_ERR_INVALID_ARG),
     (dict(dtype_ab=L.GEMM_F32), L.GEMM_ERR_INVALID_ARG),
     (dict(dtype_c=9), L.GEMM_ERR_INVALID_ARG),
-    (dict(mapping=4), L.GEMM_ERR_INVALID_ARG),
+    (dict(mapping=6), L.GEMM_ERR_INVALID_ARG),
+    (dict(mapping=L.GEMM_MAP_BLOCKED), L.GEMM_OK),                    # the planner picks the box
+    (dict(mapping=L.GEMM_MAP_BLOCKED, group=2, group_n=3), L.GEMM_OK),
+    (dict(mapping=L.GEMM_MAP_BLOCKED, group_n=-1), L.GEMM_ERR_INVALID_ARG),
+    (dict(mapping=L.GEMM_MAP_BLOCKED, group=-1), L.GEMM_ERR_INVALID_ARG),
+    (dict(mapping=L.GEMM_MAP_MORTON), L.GEMM_OK),
     (dict(mapping=L.GEMM_MAP_GROUPED_M, group=-1), L.GEMM_ERR_INVALID_ARG),
     (dict(mapping=L.GEMM_MAP_GROUPED_M, group=0), L.GEMM_OK),       # the planner picks G
     (dict(sched=9), L.GEMM_ERR_INVALID_ARG),

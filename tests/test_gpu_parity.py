@@ -185,17 +185,21 @@ def test_streamk_modes_deterministic_and_identical(dev):
     assert np.array_equal(C1, C3)
 
 
-@pytest.mark.parametrize("sched,workers,tile,mapping,G", [
-    (L.GEMM_SCHED_STREAMK, 20, 128, L.GEMM_MAP_GROUPED_M, 2),
-    (L.GEMM_SCHED_PERSISTENT, 8, 256, L.GEMM_MAP_GROUPED_N, 3),
-    (L.GEMM_SCHED_STATIC, 0, 128, L.GEMM_MAP_LINEAR_M, 1),
+@pytest.mark.parametrize("sched,workers,tile,mapping,G,W", [
+    (L.GEMM_SCHED_STREAMK, 20, 128, L.GEMM_MAP_GROUPED_M, 2, 0),
+    (L.GEMM_SCHED_PERSISTENT, 8, 256, L.GEMM_MAP_GROUPED_N, 3, 0),
+    (L.GEMM_SCHED_STATIC, 0, 128, L.GEMM_MAP_LINEAR_M, 1, 0),
+    (L.GEMM_SCHED_STREAMK, 20, 128, L.GEMM_MAP_BLOCKED, 2, 3),
+    (L.GEMM_SCHED_PERSISTENT, 2, 256, L.GEMM_MAP_BLOCKED, 2, 2),
+    (L.GEMM_SCHED_STATIC, 0, 128, L.GEMM_MAP_MORTON, 1, 0),
+    (L.GEMM_SCHED_PERSISTENT, 3, 256, L.GEMM_MAP_MORTON, 1, 0),
 ])
-def test_device_trace_matches_enumeration(dev, sched, workers, tile, mapping, G):
+def test_device_trace_matches_enumeration(dev, sched, workers, tile, mapping, G, W):
     """Work items recorded by the kernel equal the CPU replay and the oracle's enumeration."""
     M, N, K = 640, 640, 2048
     op = gi.make_operands(M, N, K, "bf16", seed=3)
     C, plan, ws = run_gpu(op, torch, dev, "f32", mapping, G, sched, workers, tile,
-                          flags=L.GEMM_FLAG_TRACE)
+                          flags=L.GEMM_FLAG_TRACE, group_n=W)
     info = plan.info
     raw = ws.cpu().numpy()[info.trace_offset:].view(np.int32)[: info.grid * info.trace_capacity * 8]
     rec = raw.reshape(info.grid, info.trace_capacity, 8)
@@ -206,10 +210,12 @@ def test_device_trace_matches_enumeration(dev, sched, workers, tile, mapping, G)
                 got.append(tuple(int(x) for x in r))
     want = plan.schedule()
     assert got == want
-    MAP = {0: S.LINEAR_N, 1: S.LINEAR_M, 2: S.GROUPED_M, 3: S.GROUPED_N}
+    MAP = {0: S.LINEAR_N, 1: S.LINEAR_M, 2: S.GROUPED_M, 3: S.GROUPED_N, 4: S.BLOCKED,
+           5: S.MORTON}
     SCH = {0: S.STATIC, 1: S.PERSISTENT, 2: S.STREAMK}
     ora = S.enumerate_schedule(M, N, K, tile, tile, info.bk, MAP[mapping], G, SCH[sched],
-                               P=None if sched == L.GEMM_SCHED_STATIC else info.grid)
+                               P=None if sched == L.GEMM_SCHED_STATIC else info.grid,
+                               W=info.group_n)
     assert got == [(w.worker, w.seq, w.tile, w.m, w.n, w.k_begin, w.k_end, w.role) for w in ora]
     assert_within_tolerance(C, reference(op), op, "trace run")
 
@@ -230,14 +236,21 @@ def test_spin_watchdog_reports_instead_of_hanging(dev, mode):
     assert err == L.GEMM_DEVICE_OK
 
 
-def test_linear_and_grouped_give_identical_bits(dev):
-    """The mapping only reorders whole tiles; each tile's arithmetic is unchanged."""
-    op = gi.make_operands(1024, 1024, 512, "bf16", seed=12)
+@pytest.mark.parametrize("tile", [128, 256])
+def test_every_mapping_gives_identical_bits(dev, tile):
+    """The mapping only reorders whole tiles; each tile's arithmetic is unchanged: linear,
+    grouped, blocked and Morton orders give the same bits (ragged grid, several items per
+    worker)."""
+    op = gi.make_operands(1160, 1288, 512, "bf16", seed=12)
     C1, _, _ = run_gpu(op, torch, dev, "bf16", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_PERSISTENT,
-                       7, 128)
-    C2, _, _ = run_gpu(op, torch, dev, "bf16", L.GEMM_MAP_GROUPED_M, 8, L.GEMM_SCHED_PERSISTENT,
-                       7, 128)
-    assert np.array_equal(C1, C2)
+                       7, tile)
+    assert_within_tolerance(C1, reference(op), op, "linear")
+    for mapping, G, W in ((L.GEMM_MAP_GROUPED_M, 8, 0), (L.GEMM_MAP_GROUPED_N, 3, 0),
+                          (L.GEMM_MAP_BLOCKED, 2, 3), (L.GEMM_MAP_BLOCKED, 0, 0),
+                          (L.GEMM_MAP_MORTON, 1, 0)):
+        C2, _, _ = run_gpu(op, torch, dev, "bf16", mapping, G, L.GEMM_SCHED_PERSISTENT, 7, tile,
+                           group_n=W)
+        assert np.array_equal(C1, C2), (mapping, G, W)
 
 
 @pytest.mark.parametrize("M,N,K", [(0, 64, 64), (64, 0, 64), (64, 64, 0), (130, 136, 0)])

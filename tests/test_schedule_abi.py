@@ -6,7 +6,8 @@ from dense_gemm_design_amd import _lib as L
 from oracle import schedule as S
 
 MAP = {L.GEMM_MAP_LINEAR_N: S.LINEAR_N, L.GEMM_MAP_LINEAR_M: S.LINEAR_M,
-       L.GEMM_MAP_GROUPED_M: S.GROUPED_M, L.GEMM_MAP_GROUPED_N: S.GROUPED_N}
+       L.GEMM_MAP_GROUPED_M: S.GROUPED_M, L.GEMM_MAP_GROUPED_N: S.GROUPED_N,
+       L.GEMM_MAP_BLOCKED: S.BLOCKED, L.GEMM_MAP_MORTON: S.MORTON}
 SCHED = {L.GEMM_SCHED_STATIC: S.STATIC, L.GEMM_SCHED_PERSISTENT: S.PERSISTENT,
          L.GEMM_SCHED_STREAMK: S.STREAMK}
 
@@ -26,27 +27,40 @@ CASES = [
     (384, 256, 448, L.GEMM_BF16, 128, L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK, 5, True),
     (300, 264, 104, L.GEMM_BF16, 128, L.GEMM_MAP_GROUPED_M, 2, L.GEMM_SCHED_STREAMK, 3, True),
     (2048, 2048, 2048, L.GEMM_FP8_E4M3, 128, L.GEMM_MAP_GROUPED_N, 8, L.GEMM_SCHED_STREAMK, 300, True),
+    # 2D blocking (G = box height, the box width in the last field) and Morton
+    (8192, 8192, 8192, L.GEMM_FP8_E4M3, 256, L.GEMM_MAP_BLOCKED, 4, L.GEMM_SCHED_PERSISTENT, 256, True, 8),
+    (4096, 14336, 4096, L.GEMM_BF16, 256, L.GEMM_MAP_BLOCKED, 4, L.GEMM_SCHED_PERSISTENT, 256, True, 8),
+    (1000, 3000, 512, L.GEMM_BF16, 128, L.GEMM_MAP_BLOCKED, 3, L.GEMM_SCHED_PERSISTENT, 24, True, 5),
+    (1000, 3000, 512, L.GEMM_BF16, 128, L.GEMM_MAP_BLOCKED, 3, L.GEMM_SCHED_STATIC, 0, True, 5),
+    (1280, 640, 1024, L.GEMM_BF16, 128, L.GEMM_MAP_BLOCKED, 2, L.GEMM_SCHED_STREAMK, 40, True, 3),
+    (4096, 4096, 4096, L.GEMM_BF16, 256, L.GEMM_MAP_MORTON, 1, L.GEMM_SCHED_PERSISTENT, 256, True),
+    (1000, 3000, 512, L.GEMM_BF16, 128, L.GEMM_MAP_MORTON, 1, L.GEMM_SCHED_PERSISTENT, 24, True),
+    (4096, 14336, 4096, L.GEMM_BF16, 256, L.GEMM_MAP_MORTON, 1, L.GEMM_SCHED_STATIC, 0, True),
+    (1280, 640, 1024, L.GEMM_BF16, 128, L.GEMM_MAP_MORTON, 1, L.GEMM_SCHED_STREAMK, 40, True),
 ]
 
 
 @pytest.mark.parametrize("case", CASES)
 def test_enumeration_matches_oracle(case):
-    M, N, K, dt, tile, mapping, G, sched, P, remap = case
+    M, N, K, dt, tile, mapping, G, sched, P, remap = case[:10]
+    W = case[10] if len(case) > 10 else 0
     flags = 0 if remap else L.GEMM_FLAG_NO_XCD_REMAP
     plan = L.Plan(L.make_desc(M, N, K, dtype_ab=dt, mapping=mapping, group=G, sched=sched,
-                              num_workers=P, bm=tile, bn=tile, flags=flags))
+                              num_workers=P, bm=tile, bn=tile, flags=flags, group_n=W))
+    if mapping == L.GEMM_MAP_BLOCKED:
+        assert (plan.info.group, plan.info.group_n) == (G, W)
     got = plan.schedule()
     bk = plan.info.bk
     Pw = plan.info.grid if sched != L.GEMM_SCHED_STATIC else None
     want = S.enumerate_schedule(M, N, K, tile, tile, bk, MAP[mapping], G, SCHED[sched],
                                 P=P if sched != L.GEMM_SCHED_STATIC else None,
-                                xcd_remap=remap)
+                                xcd_remap=remap, W=max(W, 1))
     want = [(w.worker, w.seq, w.tile, w.m, w.n, w.k_begin, w.k_end, w.role) for w in want]
     if sched == L.GEMM_SCHED_PERSISTENT:
         # the planner caps P at the tile count; the oracle is asked with the same P
         want = [(w.worker, w.seq, w.tile, w.m, w.n, w.k_begin, w.k_end, w.role) for w in
                 S.enumerate_schedule(M, N, K, tile, tile, bk, MAP[mapping], G, SCHED[sched],
-                                     P=Pw, xcd_remap=remap)]
+                                     P=Pw, xcd_remap=remap, W=max(W, 1))]
     assert got == want
 
 
@@ -60,3 +74,22 @@ def test_enumerate_capacity_reporting():
     assert lib.gemm_schedule_enumerate(plan.handle, arr, 3, ctypes.byref(n)) == L.GEMM_ERR_CAPACITY
     assert n.value == 64
     assert (arr[0].worker, arr[0].seq) == (0, 0)
+
+
+def test_blocked_planner_box():
+    """group = group_n = 0: the planner fills a box with the tiles one XCD runs at a time
+    (P / 8), choosing the fewest operand strips H + W, the wider box on a tie; one given side
+    fixes the other."""
+    def box(M, N, P, G=0, W=0):
+        p = L.Plan(L.make_desc(M, N, 4096, mapping=L.GEMM_MAP_BLOCKED, group=G, group_n=W,
+                               sched=L.GEMM_SCHED_PERSISTENT, num_workers=P, bm=256, bn=256))
+        return p.info.group, p.info.group_n
+    assert box(8192, 8192, 256) == (4, 8)            # 32 tiles per XCD: 4 + 8 strips
+    assert box(4096, 14336, 256) == (4, 8)
+    assert box(8192, 8192, 256, G=2) == (2, 16)
+    assert box(8192, 8192, 256, W=2) == (16, 2)
+    assert box(512, 8192, 256) == (2, 4)             # 64 tiles: P = 64, 8 per XCD
+    # Morton and the linear mappings report 1 x 1
+    p = L.Plan(L.make_desc(1024, 1024, 1024, mapping=L.GEMM_MAP_MORTON, num_workers=8, bm=128,
+                           bn=128))
+    assert (p.info.group, p.info.group_n) == (1, 1)

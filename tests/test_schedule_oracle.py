@@ -46,10 +46,11 @@ def test_mapping_working_set_example():
     assert len({m for m, _ in lin}) == 1 and len({n for _, n in lin}) == 8
 
 
-@pytest.mark.parametrize("mode", [S.LINEAR_N, S.LINEAR_M, S.GROUPED_M, S.GROUPED_N])
+@pytest.mark.parametrize("mode", [S.LINEAR_N, S.LINEAR_M, S.GROUPED_M, S.GROUPED_N, S.BLOCKED,
+                                  S.MORTON])
 @pytest.mark.parametrize("Mt,Nt,G", [(1, 1, 1), (7, 5, 3), (32, 32, 8), (4, 112, 8), (9, 2, 4)])
 def test_mapping_is_a_bijection(mode, Mt, Nt, G):
-    order = S.tile_order(mode, Mt, Nt, G)
+    order = S.tile_order(mode, Mt, Nt, G, W=3)
     assert len(order) == Mt * Nt
     assert set(order) == {(m, n) for m in range(Mt) for n in range(Nt)}
 
@@ -66,6 +67,68 @@ def test_mapping_equivalences_from_table():
             gn = S.tile_order(S.GROUPED_N, Mt, Nt, G)
             gm_t = [(m, n) for (n, m) in S.tile_order(S.GROUPED_M, Nt, Mt, G)]
             assert gn == gm_t
+
+
+def test_blocking_working_set_example():
+    """The page's working-set example (8 concurrent tiles on a 16 x 16 grid, 6 MiB) with a 4 x 2
+    box: the first 8 tiles are one 4 x 2 rectangle, 4 A bands and 2 B bands."""
+    g = load("mapping_working_set.txt")
+    mt, nt = ints(g["grid"][0])
+    BM, BN, K = int(g["BM"][0]), int(g["BN"][0]), int(g["K"][0])
+    esz, conc = int(g["bytes_per_element"][0]), int(g["concurrent"][0])
+    first = S.tile_order(S.BLOCKED, mt, nt, 4, W=2)[:conc]
+    assert set(first) == {(m, n) for m in range(4) for n in range(2)}
+    a_bytes = len({m for m, _ in first}) * BM * K * esz
+    b_bytes = len({n for _, n in first}) * BN * K * esz
+    assert a_bytes + b_bytes == int(g["working_set_mib"][0]) << 20
+
+
+def test_blocking_equivalences():
+    """A box as wide as the grid is a Grouped-M strip; one-row boxes are Linear N-fast; a box of
+    all rows and one column is Linear M-fast."""
+    for Mt, Nt in [(5, 7), (8, 8), (1, 9), (12, 20)]:
+        for G in (1, 2, 3, 4):
+            assert S.tile_order(S.BLOCKED, Mt, Nt, G, W=Nt) == S.tile_order(S.GROUPED_M, Mt, Nt, G)
+        for W in (1, 2, 5):
+            assert S.tile_order(S.BLOCKED, Mt, Nt, 1, W=W) == S.tile_order(S.LINEAR_N, Mt, Nt)
+        assert S.tile_order(S.BLOCKED, Mt, Nt, Mt, W=1) == S.tile_order(S.LINEAR_M, Mt, Nt)
+
+
+def test_blocking_boxes_are_rectangles():
+    """Every run of H * W consecutive tiles that starts at a box boundary fills one H x W box,
+    and the boxes of a box row follow each other along N; edge boxes hold what is left."""
+    Mt, Nt, H, W = 10, 13, 4, 3
+    order = S.tile_order(S.BLOCKED, Mt, Nt, H, W=W)
+    i = 0
+    for r0 in range(0, Mt, H):
+        for c0 in range(0, Nt, W):
+            h, w = min(H, Mt - r0), min(W, Nt - c0)
+            box = order[i:i + h * w]
+            assert set(box) == {(m, n) for m in range(r0, r0 + h) for n in range(c0, c0 + w)}
+            assert box[:h] == [(m, c0) for m in range(r0, r0 + h)]   # M-fast inside
+            i += h * w
+    assert i == Mt * Nt
+
+
+def test_morton_textbook_order():
+    """The Z-order curve of a 4 x 4 grid (n in the even bits, m in the odd ones)."""
+    z = [(0, 0), (0, 1), (1, 0), (1, 1), (0, 2), (0, 3), (1, 2), (1, 3),
+         (2, 0), (2, 1), (3, 0), (3, 1), (2, 2), (2, 3), (3, 2), (3, 3)]
+    assert S.tile_order(S.MORTON, 4, 4) == z
+    assert [S.morton_code(m, n) for m, n in z] == list(range(16))
+    # bit interleaving by hand: m = 0b101, n = 0b011 -> code bits m2 n2 m1 n1 m0 n0 = 100111
+    assert S.morton_code(5, 3) == 0b100111
+
+
+@pytest.mark.parametrize("Mt,Nt", [(3, 5), (7, 2), (16, 56), (1, 6), (9, 9)])
+def test_morton_on_a_partial_grid_keeps_the_square_order(Mt, Nt):
+    """On a grid that is not a power-of-two square the order is the enclosing square's Z-order
+    with the tiles outside the grid left out."""
+    side = 1
+    while side < max(Mt, Nt):
+        side *= 2
+    full = S.tile_order(S.MORTON, side, side)
+    assert S.tile_order(S.MORTON, Mt, Nt) == [(m, n) for m, n in full if m < Mt and n < Nt]
 
 
 def test_grouped_m_inside_a_strip_is_m_fast():
