@@ -39,6 +39,9 @@ using CfgFp8_128 = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 2, 1>;
 // The wide-wave kernel (GEMM_FLAG_WIDE): four waves of 128 x 128, two stages.
 using CfgBf16_256w = TileCfg<DT_BF16, 256, 256, 64, 2, 2, 2, 1, 16>;  // 16 x 16 x 32 MFMAs
 using CfgFp8_256w = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1, 16>;  // 16 x 16 x 128 MFMAs
+// ... and on 128 x 128 tiles: four waves of 64 x 64
+using CfgBf16_128w = TileCfg<DT_BF16, 128, 128, 64, 2, 2, 2, 1, 16>;
+using CfgFp8_128w = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 2, 1, 16>;
 
 typedef hipError_t (*launch_fn)(const KernelArgs &, int grid, bool ragged_k, hipStream_t);
 typedef const void *(*kernel_fn)();
@@ -171,6 +174,8 @@ const KernelEntry kKernels[] = {
     entry_vs<CfgFp8_256vs>(),
     entry_wide<CfgBf16_256w>(),
     entry_wide<CfgFp8_256w>(),
+    entry_wide<CfgBf16_128w>(),
+    entry_wide<CfgFp8_128w>(),
     entry<CfgFp8_128>(),
 };
 
@@ -214,6 +219,7 @@ constexpr double kDeviceBytesPerClk = 2600;  // Stream-K partials, whole device 
 constexpr double kLatencyClk = 2000;         // first load or store round trip of a phase
 // MFMA efficiency of whole launches at the held clock (bench workloads, profiles/)
 double kernel_efficiency(int kind, int bm, int dt) {
+  if (kind == KIND_WIDE && bm == 128) return dt == DT_BF16 ? 0.43 : 0.40;
   if (kind == KIND_WIDE) return dt == DT_BF16 ? 0.76 : 0.79;
   if (kind == KIND_PP) return 0.66;
   if (bm == 256) return dt == DT_BF16 ? 0.60 : 0.70;
@@ -283,8 +289,11 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
                                                     : d.dtype_c == GEMM_FP8_E4M3 ? 1.0
                                                                                  : 4.0;
   const ModelCand cands[] = {{KIND_WIDE, 256, 256, GEMM_SCHED_PERSISTENT},
+                             {KIND_WIDE, 128, 128, GEMM_SCHED_PERSISTENT},
                              {KIND_COOP, 128, 128, GEMM_SCHED_PERSISTENT},
+                             {KIND_WIDE, 128, 128, GEMM_SCHED_STREAMK},
                              {KIND_COOP, 128, 128, GEMM_SCHED_STREAMK},
+                             {KIND_WIDE, 256, 256, GEMM_SCHED_STREAMK},
                              {KIND_COOP, 256, 256, GEMM_SCHED_STREAMK}};
   int cus = 0, dev = 0;
   if (d.num_workers == 0) {
@@ -310,7 +319,7 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, e->kernel(), e->threads, 0) !=
           hipSuccess)
         return GEMM_ERR_HIP;
-      if (occ < 1) occ = 1;
+      if (occ < 1 || e->kind == KIND_WIDE) occ = 1;  // wide-wave: one wave per SIMD by design
       P = cus * occ;
     }
     // without a device: one worker per CU
@@ -322,6 +331,9 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
       if (tiles > INT32_MAX) continue;
       streamk_plan(tiles, P, dp, sk);
       if (sk == 0 || Kt == 0) continue;  // no tail to balance: the data-parallel candidate covers it
+      // the wide-wave kernel's separate reduction needs a band of at least P iterations
+      if (c.kind == KIND_WIDE && ((int64_t)sk * Kt < P || (d.flags & GEMM_FLAG_STREAMK_CHAIN)))
+        continue;
     }
     const int wgm = 2, wgn = e->threads / 64 / 2;  // waves along M and N
     const double t = (double)tiles, bm = c.bm, bn = c.bn, kk = (double)Keff;
@@ -438,8 +450,11 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
                          : (d.flags & GEMM_FLAG_WIDE)        ? KIND_WIDE
                          : (d.flags & GEMM_FLAG_COOPERATIVE) ? KIND_COOP
                                                              : -1;
+  // (the wide-wave kernel also runs Stream-K plans, with the separate-reduction fixup)
   const bool force_dp = force_kind == KIND_PP || force_kind == KIND_VS || force_kind == KIND_WIDE;
-  if (force_dp && (d.K == 0 || d.sched == GEMM_SCHED_STREAMK || d.sched == GEMM_SCHED_AUTO))
+  const bool dp_only = force_kind == KIND_PP || force_kind == KIND_VS;
+  if (force_dp && (d.K == 0 || (dp_only && (d.sched == GEMM_SCHED_STREAMK ||
+                                            d.sched == GEMM_SCHED_AUTO))))
     return GEMM_ERR_UNSUPPORTED;
   // the fused epilogue runs on the wide-wave and cooperative kernels
   const bool fused = d.epilogue != 0 || d.dtype_c == GEMM_FP8_E4M3;
@@ -448,7 +463,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   // Tile shape and scheduler: the cost model when everything is left to the planner, else
   // 256 x 256 unless asked otherwise or the problem has too few big tiles.
   int bm = d.bm, bn = d.bn;
-  int model_sched = -1;
+  int model_sched = -1, model_kind = -1;
   if (bm == 0 && bn == 0 && d.bk == 0 && d.sched == GEMM_SCHED_AUTO && force_kind < 0) {
     std::vector<gemm_config_score> ranked;
     const int st = rank_configs(d, ranked);
@@ -456,6 +471,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     bm = ranked[0].bm;
     bn = ranked[0].bn;
     model_sched = ranked[0].sched;
+    model_kind = ranked[0].kernel;
   } else if (bm == 0 && bn == 0) {
     const int64_t big = cdiv(d.M, 256) * cdiv(d.N, 256);  // 0 for an empty output
     const bool streamk = d.sched == GEMM_SCHED_STREAMK;
@@ -490,6 +506,13 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
         hipSuccess)
       return GEMM_ERR_HIP;
     if (per_cu < 1) per_cu = 1;
+    // the wide-wave kernels, which take every plan with K > 0 unless another kernel is asked
+    // for, run one workgroup -- one wave per SIMD -- per CU (two measured no faster for
+    // data-parallel 128 x 128 tiles and 30 % slower for Stream-K)
+    const bool wide_next = force_kind == KIND_WIDE ||
+                           (force_kind < 0 && d.K > 0 && by_kind[KIND_WIDE] &&
+                            model_kind != KIND_COOP);
+    if (wide_next) per_cu = 1;
     workers = cus * per_cu;
   }
   if (sched == GEMM_SCHED_AUTO) {
@@ -498,12 +521,16 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     sched = sk > 0 ? GEMM_SCHED_STREAMK : GEMM_SCHED_PERSISTENT;
   }
   // Data-parallel work on 256 x 256 tiles runs on the wide-wave kernel unless a kernel is asked
-  // for (all of them hold one workgroup per CU, so the worker count stays).
+  // for (all of them hold one workgroup per CU, so the worker count stays); so does Stream-K work
+  // on 256 x 256 tiles, unless it needs the lock chain (checked below, once the band is known).
   if (force_kind < 0 && d.K > 0 && (sched == GEMM_SCHED_STATIC || sched == GEMM_SCHED_PERSISTENT)) {
     if (by_kind[KIND_WIDE])
       k = by_kind[KIND_WIDE];
     else if (by_kind[KIND_PP] && !fused)
       k = by_kind[KIND_PP];
+  } else if (force_kind < 0 && d.K > 0 && sched == GEMM_SCHED_STREAMK && by_kind[KIND_WIDE] &&
+             !(d.flags & GEMM_FLAG_STREAMK_CHAIN) && (model_kind < 0 || model_kind == KIND_WIDE)) {
+    k = by_kind[KIND_WIDE];
   }
   const int64_t Kt = cdiv(d.K, k->bk);  // the kernel's own k-tile depth
   if (Kt > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
@@ -551,6 +578,14 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   // (band of T >= P iterations); otherwise, or when asked, the lock chain.
   const bool chain = (d.flags & GEMM_FLAG_STREAMK_CHAIN) || (int64_t)sp.sk_tiles * Kt < sp.P;
   const int sk_mode = chain ? SK_CHAIN : SK_SEPARATE;
+  if (chain && sp.sk_tiles > 0 && k->kind == KIND_WIDE) {  // the wide-wave kernel has no chain
+    if (force_kind == KIND_WIDE) {
+      delete p;
+      return GEMM_ERR_UNSUPPORTED;
+    }
+    k = by_kind[KIND_COOP];
+    p->k = k;
+  }
   // partial tiles: one per split tile (chain), or one per (unit, tile) pair, indexed unit + tile,
   // at most P + sk_tiles of them (separate)
   const int64_t partial_slots = sp.sk_tiles == 0 ? 0 : (chain ? sp.sk_tiles : sp.P + sp.sk_tiles);

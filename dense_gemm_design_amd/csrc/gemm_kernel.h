@@ -233,13 +233,11 @@ __device__ __forceinline__ f32x4 mfma16(const typename FragT<DT>::type &b,
 // the operands (and waits for the LDS reads that produce A and B), but not the MFMA's latency:
 // callers leave wait states before reading an accumulator written here, and after writing one
 // with a VALU instruction before its first MFMA.
-template <int DT>
-__device__ __forceinline__ void mfma16_inplace(f32x4 &c, const typename FragT<DT>::type &b,
-                                               const typename FragT<DT>::type &a) {
-  if constexpr (DT == DT_BF16)
-    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
-  else
-    asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+__device__ __forceinline__ void mfma16_inplace(f32x4 &c, const bf16x8 &b, const bf16x8 &a) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+}
+__device__ __forceinline__ void mfma16_inplace(f32x4 &c, const i32x8 &b, const i32x8 &a) {
+  asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
 }
 
 // Accumulator block of a configuration and the MFMA that updates it.
@@ -252,7 +250,7 @@ __device__ __forceinline__ void mfma_blk(acc_t<CFG> &c, const typename FragT<CFG
   if constexpr (CFG::MI == 32)
     c = mfma<CFG::DT>(b, a, c);
   else
-    mfma16_inplace<CFG::DT>(c, b, a);
+    mfma16_inplace(c, b, a);
 }
 
 // Wait states between VALU writes of accumulators and an MFMA reading them, or between an MFMA
@@ -1726,7 +1724,8 @@ __device__ __forceinline__ void epilogue_wide(const KernelArgs &args, const Work
   }
 }
 
-// fp32 output straight from the accumulation registers, one quad (16 bytes) per lane and store.
+// Output straight from the accumulation registers, one quad per lane and store (fp32; bf16 from
+// kernels whose sub-tiles are too narrow to stage).
 template <class CFG, int FUSE = FUSE_OFF>
 __device__ __forceinline__ void epilogue_direct(const KernelArgs &args, const WorkItem &w,
                                                 const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
@@ -1747,9 +1746,10 @@ __device__ __forceinline__ void epilogue_direct(const KernelArgs &args, const Wo
       }
 }
 
-// Fused fp32 or e4m3 output of a 16 x 16-block sub-tile straight from the accumulation registers,
-// one quad per store (16 bytes of fp32, 4 of e4m3 codes; for e4m3 this measured faster than
-// staging the codes through LDS, which needs registers the e4m3 kernel does not have to spare).
+// Fused output of a 16 x 16-block sub-tile straight from the accumulation registers, one quad per
+// store (16 bytes of fp32, 8 of bf16, 4 of e4m3 codes; for e4m3 this measured faster than
+// staging the codes through LDS, which needs registers the e4m3 kernel does not have to spare;
+// bf16 takes this path only on 64-wide sub-tiles, whose rows are too short to stage).
 // Column-block major: the lane's row biases (one per row block) are loaded first, a column
 // block's bias quad one block ahead of its use.  Without a bias of that orientation the loads go
 // to an empty buffer range and read zero, so no branch sits in the loop.
@@ -1778,12 +1778,92 @@ __device__ __forceinline__ void epilogue_direct_fused(const KernelArgs &args, co
       if (ok) {
         if (args.out_fp8)
           *(uint32_t *)(args.C + m * args.ldc + n) = pack_e4m3x4(v * ec.inv_d);
+        else if (args.out_bf16)
+          *(u32x2 *)(args.C + (m * args.ldc + n) * 2) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         else
           *(f32x4 *)(args.C + (m * args.ldc + n) * 4) = v;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     bq = bnext;
+  }
+}
+
+// Stream-K in the wide-wave kernels (separate reduction, "H100 Stream-K" lesson, section 6, with
+// every split storing its own partial): the partial slot of (unit b, band tile t) is b + t, like
+// the cooperative kernel's, but laid out row-major -- element (r, c) of the BM x BN tile at
+// (r BN + c) 4 bytes -- so the reduction reads whole rows whatever MFMA shape wrote them.
+template <class CFG>
+__device__ __forceinline__ void wide_partial_store(const KernelArgs &args, const WorkItem &w,
+                                                   const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
+                                                   int32_t b, int wm, int wn, int lane, int tid) {
+  static_assert(CFG::MI == 16, "16 x 16 blocks");
+  const __amdgpu_buffer_rsrc_t pr = partial_rsrc(args.partials);
+  const uint32_t slot = slot_byte<CFG>((int64_t)b + w.sk_slot);
+  const uint32_t r0 = (uint32_t)(wm * CFG::WM + (lane & 15));
+  const uint32_t c0 = (uint32_t)(wn * CFG::WN + (lane >> 4) * 4);
+#pragma unroll
+  for (int f = 0; f < CFG::FM; ++f)
+#pragma unroll
+    for (int g = 0; g < CFG::FN; ++g) {
+      const uint32_t off = ((r0 + f * 16) * CFG::BN + c0 + g * 16) * 4;
+      store_coherent(pr, slot + off, quad_of<true>(acc[f][g], 0));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  wait_vmcnt<0>();  // this wave's partial is stored (the ring's loads in flight complete too) ...
+  lds_barrier();    // ... and so is every wave's: arrive
+  const bool skip = (args.flags & KF_TEST_SKIP_PUBLISH) && w.sk_slot == 0 && w.role == ROLE_FIRST;
+  if (tid == 0 && !skip)
+    __hip_atomic_fetch_add(args.locks + w.sk_slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The reduction of the row-major partials: unit b, the j-th of the n units u0..u1 of band tile t,
+// waits for all n arrivals, then sums its 1/n share of the tile's quads over the n partials in K
+// order (u0 first) and stores that share of C through the (fused) output path.
+template <class CFG, int FUSE>
+__device__ __forceinline__ void wide_reduce(const KernelArgs &args, const WorkItem &w, float alpha,
+                                            int32_t b, int tid, EpiCtx &ec) {
+  int32_t u0, u1;
+  sk_tile_units(args.sp, w.sk_slot, u0, u1);
+  const int n = u1 - u0 + 1, j = b - u0;
+  if (tid == 0) {
+    int *cnt = args.locks + w.sk_slot;
+    bool ok = false;
+    for (int i = 0; i < args.max_spin; ++i) {
+      if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n) {
+        ok = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (!ok) __hip_atomic_store(args.error_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  lds_barrier();
+  constexpr int QPR = CFG::BN / 4;  // quads per tile row
+  constexpr int NQ = CFG::BM * QPR;
+  constexpr uint32_t SLOT = CFG::BM * CFG::BN * 4;
+  const int q_begin = (int)((int64_t)NQ * j / n), q_end = (int)((int64_t)NQ * (j + 1) / n);
+  const __amdgpu_buffer_rsrc_t pr = partial_rsrc(args.partials);
+  const uint32_t base = slot_byte<CFG>((int64_t)u0 + w.sk_slot);
+  for (int qq = q_begin + tid; qq < q_end; qq += CFG::THREADS) {
+    const uint32_t off = base + (uint32_t)qq * 16;
+    f32x4 sum = load_coherent(pr, off);
+    int u = 1;
+    for (; u + 4 <= n; u += 4) {
+      const f32x4 p0 = load_coherent(pr, off + (u + 0) * SLOT);
+      const f32x4 p1 = load_coherent(pr, off + (u + 1) * SLOT);
+      const f32x4 p2 = load_coherent(pr, off + (u + 2) * SLOT);
+      const f32x4 p3 = load_coherent(pr, off + (u + 3) * SLOT);
+      sum = sum + p0;
+      sum = sum + p1;
+      sum = sum + p2;
+      sum = sum + p3;
+    }
+    for (; u < n; ++u) sum = sum + load_coherent(pr, off + u * SLOT);
+    const int64_t m = (int64_t)w.m * CFG::BM + qq / QPR;
+    const int64_t nn = (int64_t)w.n * CFG::BN + (qq % QPR) * 4;
+    store_quad_sel<FUSE, CFG>(args, m, nn, sum, alpha, ec);
   }
 }
 
@@ -2036,13 +2116,25 @@ gemm_kernel_wide(KernelArgs args) {
     }
 
     if constexpr (CFG::MI == 16) mfma_wait_states();  // the last MFMAs' results are written
-    if (args.out_bf16)
-      epilogue_wide<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
-    else if constexpr (FUSE != FUSE_OFF)
+    if (cw.role != ROLE_WHOLE) {  // a Stream-K split: its partial, reduced after all MAC work
+      wide_partial_store<CFG>(args, cw, acc, b, wm, wn, lane, tid);
+    } else if (CFG::WN == 128 && args.out_bf16) {  // staged through the wave's LDS slice
+      if constexpr (CFG::WN == 128)
+        epilogue_wide<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
+    } else if constexpr (FUSE != FUSE_OFF) {
       epilogue_direct_fused<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, ec);
-    else
+    } else {
       epilogue_direct<CFG>(args, cw, acc, alpha, wm, wn, lane, ec);
+    }
     cvalid = cursor_next(args.sp, ccur, cw);
+  }
+  if (args.sp.sk_tiles > 0) {
+    // second pass over this unit's splits: reduce its share of each tile it touched
+    Cursor rc;
+    cursor_init(args.sp, b, rc);
+    WorkItem rw;
+    while (cursor_next(args.sp, rc, rw))
+      if (rw.role != ROLE_WHOLE) wide_reduce<CFG, FUSE>(args, rw, alpha, b, tid, ec);
   }
   wait_vmcnt<0>();
   if constexpr (FUSE != FUSE_OFF)
@@ -2209,13 +2301,25 @@ gemm_kernel_wide1(KernelArgs args) {
       for (int g = 0; g < FN; ++g) fb[0][g] = fb[1][g];
     }
     mfma_wait_states();  // the last MFMAs' results are written
-    if (args.out_bf16)
-      epilogue_wide<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
-    else if constexpr (FUSE != FUSE_OFF)
+    if (cw.role != ROLE_WHOLE) {  // a Stream-K split: its partial, reduced after all MAC work
+      wide_partial_store<CFG>(args, cw, acc, b, wm, wn, lane, tid);
+    } else if (CFG::WN == 128 && args.out_bf16) {  // staged through the wave's LDS slice
+      if constexpr (CFG::WN == 128)
+        epilogue_wide<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
+    } else if constexpr (FUSE != FUSE_OFF) {
       epilogue_direct_fused<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, ec);
-    else
+    } else {
       epilogue_direct<CFG>(args, cw, acc, alpha, wm, wn, lane, ec);
+    }
     cvalid = cursor_next(args.sp, ccur, cw);
+  }
+  if (args.sp.sk_tiles > 0) {
+    // second pass over this unit's splits: reduce its share of each tile it touched
+    Cursor rc;
+    cursor_init(args.sp, b, rc);
+    WorkItem rw;
+    while (cursor_next(args.sp, rc, rw))
+      if (rw.role != ROLE_WHOLE) wide_reduce<CFG, FUSE>(args, rw, alpha, b, tid, ec);
   }
   wait_vmcnt<0>();
   if constexpr (FUSE != FUSE_OFF)

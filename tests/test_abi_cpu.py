@@ -118,7 +118,11 @@ def create(**kw):
     (dict(flags=L.GEMM_FLAG_WIDE), L.GEMM_OK),
     (dict(flags=L.GEMM_FLAG_WIDE, dtype_ab=L.GEMM_FP8_E4M3, K=400, M=300), L.GEMM_OK),
     (dict(flags=L.GEMM_FLAG_WIDE, bk=32), L.GEMM_ERR_UNSUPPORTED),  # its bf16 k-tile is 64 deep
-    (dict(flags=L.GEMM_FLAG_WIDE, sched=L.GEMM_SCHED_STREAMK), L.GEMM_ERR_UNSUPPORTED),
+    (dict(flags=L.GEMM_FLAG_WIDE, sched=L.GEMM_SCHED_STREAMK), L.GEMM_OK),  # separate fixup
+    (dict(flags=L.GEMM_FLAG_WIDE | L.GEMM_FLAG_STREAMK_CHAIN, sched=L.GEMM_SCHED_STREAMK),
+     L.GEMM_ERR_UNSUPPORTED),                                       # it has no lock chain
+    (dict(flags=L.GEMM_FLAG_WIDE, sched=L.GEMM_SCHED_STREAMK, K=64, num_workers=256),
+     L.GEMM_ERR_UNSUPPORTED),                                       # band < P: chain needed
     (dict(flags=L.GEMM_FLAG_WIDE, K=0), L.GEMM_ERR_UNSUPPORTED),
     (dict(flags=L.GEMM_FLAG_WIDE | L.GEMM_FLAG_COOPERATIVE), L.GEMM_ERR_INVALID_ARG),
     # fused epilogue
@@ -166,7 +170,7 @@ def test_plan_info_and_workspace():
     q = L.Plan(L.make_desc(4096, 4096, 4096, sched=L.GEMM_SCHED_PERSISTENT, num_workers=256,
                            mapping=L.GEMM_MAP_GROUPED_M, group=8))
     assert q.workspace_bytes == 0 and q.info.bm == 256 and q.info.grid == 256
-    assert i.kernel == 0 and q.info.kernel == 3     # Stream-K: cooperative; 256^2 DP: wide-wave
+    assert i.kernel == 3 and q.info.kernel == 3     # Stream-K and 256^2 DP: wide-wave
     assert q.info.lds_bytes == 160 * 1024
     r = L.Plan(L.make_desc(4096, 4096, 4096, sched=L.GEMM_SCHED_PERSISTENT, num_workers=256,
                            flags=L.GEMM_FLAG_COOPERATIVE))
@@ -217,7 +221,7 @@ def test_fused_epilogue_plans():
     assert (q.info.kernel, q.info.bk) == (3, 128)
     sk = L.Plan(L.make_desc(512, 512, 65536, sched=L.GEMM_SCHED_STREAMK, num_workers=256, bm=128,
                             bn=128, epilogue=L.GEMM_EPI_AMAX))
-    assert sk.info.kernel == 0 and sk.info.sk_tiles > 0
+    assert sk.info.kernel == 3 and sk.info.sk_tiles > 0
     z = L.Plan(L.make_desc(256, 256, 0, epilogue=L.GEMM_EPI_BIAS_ROW, num_workers=4))
     assert z.info.kernel == 0
     # the planner's own choice (everything auto) takes a kernel that has the fused epilogue

@@ -115,8 +115,14 @@ CASES = [
      L.GEMM_SCHED_PERSISTENT, 3, "col", "gelu"),
     ("coop128_bf16_e4m3_ragged_relu", 300, 264, 104, "bf16", "e4m3", L.GEMM_FLAG_COOPERATIVE,
      128, L.GEMM_SCHED_STATIC, 0, "row", "relu"),
-    ("coop128_fp8_f32_silu", 384, 264, 272, "e4m3", "f32", 0, 128, L.GEMM_SCHED_PERSISTENT, 4,
+    ("coop128_fp8_f32_silu", 384, 264, 272, "e4m3", "f32", L.GEMM_FLAG_COOPERATIVE, 128,
+     L.GEMM_SCHED_PERSISTENT, 4, "col", "silu"),
+    ("wide128_fp8_bf16_gelu", 384, 264, 272, "e4m3", "bf16", 0, 128, L.GEMM_SCHED_PERSISTENT, 4,
+     "row", "gelu"),
+    ("wide128_bf16_e4m3_silu", 300, 264, 1000, "bf16", "e4m3", 0, 128, L.GEMM_SCHED_STATIC, 0,
      "col", "silu"),
+    ("coop_streamk_sep_gelu", 256, 256, 8192, "bf16", "bf16", L.GEMM_FLAG_COOPERATIVE, 128,
+     L.GEMM_SCHED_STREAMK, 8, "row", "gelu"),
     ("streamk_sep_bf16_f32_gelu", 256, 256, 8192, "bf16", "f32", 0, 128, L.GEMM_SCHED_STREAMK,
      8, "col", "gelu"),
     ("streamk_chain_bf16_bf16_silu", 256, 256, 8192, "bf16", "bf16", L.GEMM_FLAG_STREAMK_CHAIN,
@@ -125,6 +131,11 @@ CASES = [
      "col", "relu"),
     ("streamk_hybrid_ragged_gelu", 200, 136, 1000, "bf16", "bf16", 0, 128, L.GEMM_SCHED_STREAMK,
      9, "col", "gelu"),
+    # Stream-K on the wide-wave kernel (256 x 256 tiles): the reduction applies the epilogue
+    ("wide_streamk_bf16_gelu", 300, 520, 3000, "bf16", "bf16", L.GEMM_FLAG_WIDE, 256,
+     L.GEMM_SCHED_STREAMK, 5, "col", "gelu"),
+    ("wide_streamk_fp8_e4m3_silu", 512, 768, 8192, "e4m3", "e4m3", L.GEMM_FLAG_WIDE, 256,
+     L.GEMM_SCHED_STREAMK, 4, "row", "silu"),
 ]
 
 
@@ -140,10 +151,9 @@ def test_fused_epilogue_parity(dev, case):
         scale_d = float(np.float32(E.amax(y) / 448.0 * 0.8))
     got, am, plan = run_epi(op, dev, out, bias_kind, bias, act, True, scale_d, flags, sched,
                             workers, tile)
-    if flags & L.GEMM_FLAG_WIDE:
-        assert plan.info.kernel == 3
-    else:
-        assert plan.info.kernel == 0
+    # the cooperative kernel when asked for, or for the Stream-K lock chain; else wide-wave
+    coop = flags & (L.GEMM_FLAG_COOPERATIVE | L.GEMM_FLAG_STREAMK_CHAIN)
+    assert plan.info.kernel == (0 if coop else 3)
     if sched == L.GEMM_SCHED_STREAMK:
         assert plan.info.sk_tiles > 0
     check(op, got, am, out, bias_kind, bias, act, scale_d, name)
@@ -224,8 +234,9 @@ def test_fused_path_keeps_the_products(dev, flags, tile, out):
     assert am == float(np.float32(np.abs(plain).max())) or out == "bf16"
 
 
-@pytest.mark.parametrize("kern", [("wide", L.GEMM_FLAG_WIDE, 256), ("coop", 0, 128),
-                                  ("streamk", 0, 128)])
+@pytest.mark.parametrize("kern", [("wide", L.GEMM_FLAG_WIDE, 256), ("coop", L.GEMM_FLAG_COOPERATIVE, 128),
+                                  ("wide", 0, 128), ("streamk", 0, 128), ("streamk", 0, 256),
+                                  ("streamk", L.GEMM_FLAG_COOPERATIVE, 128)])
 @pytest.mark.parametrize("out", ["bf16", "e4m3", "f32"])
 @pytest.mark.parametrize("bias_kind", ["row", "col"])
 def test_amax_ignores_positions_past_the_edge(dev, kern, out, bias_kind):
@@ -240,9 +251,12 @@ def test_amax_ignores_positions_past_the_edge(dev, kern, out, bias_kind):
     n_bias = M if bias_kind == "row" else N
     bias = (-c - 8.0 - (np.arange(n_bias) % 64) / 4.0).astype(np.float32)  # Z in [-23.75, -8]
     sched = L.GEMM_SCHED_STREAMK if name == "streamk" else L.GEMM_SCHED_PERSISTENT
-    workers = 7 if name == "streamk" else 3
+    workers = (7 if tile == 128 else 16) if name == "streamk" else 3
     got, am, plan = run_epi(op, dev, out, bias_kind, bias, None, True, 0.125, flags, sched,
                             workers, tile)
+    if name == "streamk":
+        assert plan.info.sk_tiles > 0
+    assert plan.info.kernel == (0 if flags & L.GEMM_FLAG_COOPERATIVE else 3)
     _, y = expected(op, bias_kind, bias, None)
     assert am == E.amax(y) == 23.75, (name, out, bias_kind, am)
     if out == "e4m3":

@@ -70,8 +70,8 @@ MODES = dict(SK_MODES, coop=L.GEMM_FLAG_COOPERATIVE)
 
 def modes_of(case):
     if case[9] == L.GEMM_SCHED_STREAMK:
-        return list(SK_MODES)
-    return ["separate", "coop"] if case[6] == 256 else ["separate"]
+        return list(SK_MODES) + ["coop"]
+    return ["separate", "coop"]
 
 
 CASES = [(c, m) for c in SMALL for m in modes_of(c)]
@@ -84,9 +84,10 @@ def test_small_parity(dev, case, mode):
     op = gi.make_operands(M, N, K, dt, dist, dist, seed=zlib.crc32(name.encode()) % 10000)
     C, plan, _ = run_gpu(op, torch, dev, out, mapping, G, sched, workers, tile,
                          flags=MODES[mode])
-    if tile == 256 and sched != L.GEMM_SCHED_STREAMK:
-        assert plan.info.kernel == (0 if mode == "coop" else 3)
-    if plan.info.sk_tiles:
+    # wide-wave unless the cooperative kernel is asked for or the lock chain is needed
+    assert plan.info.kernel == (0 if mode == "coop" or plan.info.streamk_mode == 0 and
+                                plan.info.sk_tiles else 3)
+    if plan.info.sk_tiles and mode != "coop":
         assert plan.info.streamk_mode == (0 if mode == "chain" else 1)
     if sched == L.GEMM_SCHED_STREAMK and name != "bf16_streamk_hybrid":
         assert plan.info.sk_tiles > 0
@@ -172,17 +173,24 @@ def test_streamk_small_integers_bit_exact(dev, mode):
 
 
 def test_streamk_modes_deterministic_and_identical(dev):
-    """Both fixups sum the splits of a tile left to right in K, so they agree bit for bit with
-    each other and with themselves across runs."""
+    """Both fixups sum the splits of a tile left to right in K, so on one kernel (the cooperative
+    one runs both) they agree bit for bit with each other and with themselves across runs; the
+    wide-wave kernel's separate reduction is deterministic too."""
     op = gi.make_operands(256, 256, 8192, "bf16", seed=5)
+    coop = L.GEMM_FLAG_COOPERATIVE
     C1, plan, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK,
-                          16, 128)
+                          16, 128, flags=coop)
     C2, _, _ = run_gpu(op, torch, dev, "f32", plan=plan)
     C3, plan3, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK,
-                           16, 128, flags=L.GEMM_FLAG_STREAMK_CHAIN)
+                           16, 128, flags=coop | L.GEMM_FLAG_STREAMK_CHAIN)
     assert plan.info.streamk_mode == 1 and plan3.info.streamk_mode == 0
     assert np.array_equal(C1, C2)
     assert np.array_equal(C1, C3)
+    W1, wplan, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK,
+                           16, 128)
+    W2, _, _ = run_gpu(op, torch, dev, "f32", plan=wplan)
+    assert wplan.info.kernel == 3 and np.array_equal(W1, W2)
+    assert_within_tolerance(W1, reference(op), op, "wide Stream-K")
 
 
 @pytest.mark.parametrize("sched,workers,tile,mapping,G,W", [
@@ -193,6 +201,7 @@ def test_streamk_modes_deterministic_and_identical(dev):
     (L.GEMM_SCHED_PERSISTENT, 2, 256, L.GEMM_MAP_BLOCKED, 2, 2),
     (L.GEMM_SCHED_STATIC, 0, 128, L.GEMM_MAP_MORTON, 1, 0),
     (L.GEMM_SCHED_PERSISTENT, 3, 256, L.GEMM_MAP_MORTON, 1, 0),
+    (L.GEMM_SCHED_STREAMK, 6, 256, L.GEMM_MAP_GROUPED_M, 2, 0),     # wide-wave Stream-K
 ])
 def test_device_trace_matches_enumeration(dev, sched, workers, tile, mapping, G, W):
     """Work items recorded by the kernel equal the CPU replay and the oracle's enumeration."""
@@ -273,7 +282,7 @@ def test_empty_and_zero_depth(dev, M, N, K):
 
 # kernels whose MFMA is the 16 x 16 form (a different summation order inside each MFMA than the
 # 32 x 32 form the other kernels use), per operand type
-MFMA16 = {("wide", "bf16"), ("wide", "e4m3")}
+MFMA16 = {("wide", "bf16"), ("wide", "e4m3"), ("wide128", "bf16"), ("wide128", "e4m3")}
 
 
 @pytest.mark.parametrize("dt,out", [("bf16", "f32"), ("bf16", "bf16"), ("e4m3", "bf16"),
@@ -293,7 +302,8 @@ def test_data_parallel_kernels_bit_identical(dev, dt, out):
                               ("coop256", 256, L.GEMM_FLAG_COOPERATIVE),
                               ("pingpong", 256, L.GEMM_FLAG_PINGPONG),
                               ("regstaged", 256, L.GEMM_FLAG_REGSTAGED),
-                              ("wide", 256, L.GEMM_FLAG_WIDE)):
+                              ("wide", 256, L.GEMM_FLAG_WIDE),
+                              ("wide128", 128, L.GEMM_FLAG_WIDE)):
         C, plan, _ = run_gpu(op, torch, dev, out, L.GEMM_MAP_GROUPED_M, 2,
                              L.GEMM_SCHED_PERSISTENT, 3, tile, flags=flags)
         assert_within_tolerance(C, ref, op, f"dp kernel {name}")
@@ -321,7 +331,7 @@ def test_no_writes_past_c(dev, M, N, K):
         buf = torch.empty(M * N * eb + canary_bytes, dtype=torch.uint8, device=dev)
         for tile, flags in ((128, L.GEMM_FLAG_COOPERATIVE), (256, L.GEMM_FLAG_COOPERATIVE),
                             (256, L.GEMM_FLAG_PINGPONG), (256, L.GEMM_FLAG_REGSTAGED),
-                            (256, L.GEMM_FLAG_WIDE)):
+                            (256, L.GEMM_FLAG_WIDE), (128, L.GEMM_FLAG_WIDE)):
             buf.fill_(0xA5)
             plan = L.Plan(L.make_desc(M, N, K, L.GEMM_BF16,
                                       L.GEMM_BF16 if out == "bf16" else L.GEMM_F32,
@@ -335,3 +345,59 @@ def test_no_writes_past_c(dev, M, N, K):
             C = buf[:M * N * eb].view(torch.bfloat16 if out == "bf16" else torch.float32)
             got = C.float().cpu().numpy().astype(np.float64).reshape(M, N)
             assert_within_tolerance(got, ref, op, f"canary {M}x{N}x{K} {out} {flags:#x}")
+
+
+WIDE_SK = [
+    # id, M, N, K, dtype, out, workers, mapping, G; 256 x 256 tiles, Stream-K
+    ("bf16_all_split", 512, 512, 16384, "bf16", "f32", 8, L.GEMM_MAP_LINEAR_N, 1),
+    ("bf16_hybrid_ragged", 300, 520, 3000, "bf16", "bf16", 5, L.GEMM_MAP_GROUPED_M, 2),
+    ("fp8_hybrid", 512, 768, 8192, "e4m3", "bf16", 4, L.GEMM_MAP_GROUPED_N, 2),
+    ("fp8_all_split_f32", 256, 520, 16384, "e4m3", "f32", 16, L.GEMM_MAP_BLOCKED, 1),
+]
+
+
+@pytest.mark.parametrize("forced", [True, False])
+@pytest.mark.parametrize("case", WIDE_SK, ids=[c[0] for c in WIDE_SK])
+def test_wide_streamk_parity(dev, case, forced):
+    """Stream-K plans on 256 x 256 tiles run on the wide-wave kernel (by default, or forced):
+    splits store row-major partials, every unit reduces its share after its MAC work."""
+    name, M, N, K, dt, out, workers, mapping, G = case
+    dist = ("normal", 1.0) if dt == "e4m3" else ("uniform",)
+    op = gi.make_operands(M, N, K, dt, dist, dist, seed=zlib.crc32(name.encode()) % 10000)
+    C, plan, ws = run_gpu(op, torch, dev, out, mapping, G, L.GEMM_SCHED_STREAMK, workers, 256,
+                          flags=L.GEMM_FLAG_WIDE if forced else 0)
+    info = plan.info
+    assert info.kernel == 3 and info.sk_tiles > 0 and info.streamk_mode == 1
+    err = int(ws.cpu().numpy()[info.error_offset:info.error_offset + 4].view(np.int32)[0])
+    assert err == L.GEMM_DEVICE_OK
+    assert_within_tolerance(C, reference(op), op, name)
+
+
+def test_wide_streamk_small_integers_bit_exact(dev):
+    """Small-integer operands: every partial and every sum is exact in fp32, so the wide-wave
+    Stream-K result equals the oracle bit for bit (and the cooperative kernel's)."""
+    M, N, K = 512, 512, 32768
+    op = gi.make_operands(M, N, K, "bf16", ("smallint", -2, 2), ("smallint", -2, 2), seed=77)
+    ref = reference(op)
+    C, plan, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK, 24,
+                         256)
+    assert plan.info.kernel == 3 and plan.info.sk_tiles == 4
+    assert np.array_equal(C, ref)
+    C2, plan2, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK,
+                           24, 256, flags=L.GEMM_FLAG_COOPERATIVE)
+    assert plan2.info.kernel == 0 and np.array_equal(C2, ref)
+
+
+def test_wide_streamk_watchdog(dev):
+    """The first split of band tile 0 withholds its arrival (test flag): the bounded wait on it
+    expires, the kernel finishes, and the device error word says so; a normal run reports OK."""
+    op = gi.make_operands(512, 512, 8192, "bf16", seed=9)
+    C, plan, ws = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK, 8,
+                          256, flags=L.GEMM_FLAG_TEST_SKIP_PUBLISH)
+    assert plan.info.kernel == 3
+    err = int(ws.cpu().numpy()[plan.info.error_offset:plan.info.error_offset + 4].view(np.int32)[0])
+    assert err == L.GEMM_DEVICE_ERR_SPIN
+    C, plan, ws = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK, 8,
+                          256)
+    err = int(ws.cpu().numpy()[plan.info.error_offset:plan.info.error_offset + 4].view(np.int32)[0])
+    assert err == L.GEMM_DEVICE_OK

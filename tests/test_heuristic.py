@@ -61,9 +61,10 @@ def test_data_movement_terms():
 @pytest.mark.parametrize("shape,dt,out,want", [
     ((4096, 4096, 4096), L.GEMM_BF16, L.GEMM_BF16, (256, 3, L.GEMM_SCHED_PERSISTENT)),
     ((8192, 8192, 8192), L.GEMM_FP8_E4M3, L.GEMM_BF16, (256, 3, L.GEMM_SCHED_PERSISTENT)),
-    ((4096, 14336, 4096), L.GEMM_BF16, L.GEMM_BF16, (256, 3, L.GEMM_SCHED_PERSISTENT)),
-    ((512, 512, 65536), L.GEMM_BF16, L.GEMM_F32, (None, 0, L.GEMM_SCHED_STREAMK)),
-    ((256, 256, 256), L.GEMM_BF16, L.GEMM_F32, (128, 0, L.GEMM_SCHED_PERSISTENT)),
+    # 896 tiles = 3.5 waves: the wide-wave kernel with a Stream-K tail balances the half wave
+    ((4096, 14336, 4096), L.GEMM_BF16, L.GEMM_BF16, (256, 3, L.GEMM_SCHED_STREAMK)),
+    ((512, 512, 65536), L.GEMM_BF16, L.GEMM_F32, (128, 3, L.GEMM_SCHED_STREAMK)),
+    ((256, 256, 256), L.GEMM_BF16, L.GEMM_F32, (128, 3, L.GEMM_SCHED_PERSISTENT)),
 ])
 def test_choices_on_measured_workloads(shape, dt, out, want):
     d = desc(*shape, dt=dt, out=out)
@@ -125,9 +126,16 @@ def test_pick_is_close_to_the_fastest_candidate(shape, dt, out):
     import torch
     dev = torch.device("cuda:0")
     M, N, K = shape
-    eb = 2 if dt == L.GEMM_BF16 else 1
-    A = torch.randint(0, 256, (M * K * eb,), dtype=torch.uint8, device=dev) & 0x3f
-    B = torch.randint(0, 256, (N * K * eb,), dtype=torch.uint8, device=dev) & 0x3f
+    # operands like the workloads' (uniform[-1, 1] bf16, or N(0, 1) e4m3): the clock the board
+    # holds, and so the time, depends on the data
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+    if dt == L.GEMM_BF16:
+        A = (torch.rand(M * K, device=dev, generator=gen) * 2 - 1).to(torch.bfloat16)
+        B = (torch.rand(N * K, device=dev, generator=gen) * 2 - 1).to(torch.bfloat16)
+    else:
+        A = torch.randn(M * K, device=dev, generator=gen).to(torch.float8_e4m3fn).view(torch.uint8)
+        B = torch.randn(N * K, device=dev, generator=gen).to(torch.float8_e4m3fn).view(torch.uint8)
     C = torch.empty(M * N * (2 if out == L.GEMM_BF16 else 4), dtype=torch.uint8, device=dev)
     sa = torch.ones(1, dtype=torch.float32, device=dev)
     d = L.make_desc(M, N, K, dt, out, L.GEMM_MAP_GROUPED_M, 0, L.GEMM_SCHED_AUTO, 0)
@@ -139,18 +147,23 @@ def test_pick_is_close_to_the_fastest_candidate(shape, dt, out):
                                   c.bm, c.bn, c.bk, flags))
         ws = torch.empty(max(plan.workspace_bytes, 1), dtype=torch.uint8, device=dev)
         run = lambda: plan.run(A, B, C, sa, sa, ws if plan.workspace_bytes else None)
+        # the clock climbs for a few hundred ms under load: settle, then take the better of two
+        # timed batches
         t0 = time.time()
-        while time.time() - t0 < 0.2:
+        while time.time() - t0 < 0.5:
             run()
             torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(20):
-            run()
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) / 20)
+        best = float("inf")
+        for _ in range(2):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / 20)
+        times.append(best)
     print(f"{shape}: " + ", ".join(f"{c.bm}/{c.kernel}/{c.sched}: {t * 1e3:.1f} us"
                                    for c, t in zip(ranked, times)), flush=True)
     assert times[0] <= 1.15 * min(times), "the model's pick is much slower than the fastest"
