@@ -31,6 +31,9 @@ Reading where the pages are open (each is listed in the design doc):
     (0,0), (0,1), (1,0), (1,1)); tiles are taken in increasing code order, so codes that fall
     outside a grid which is not a power-of-two square are simply absent;
   * the Stream-K unit u owns iterations [floor(u T / P), floor((u+1) T / P));
+  * Stream-K groups: group g holds the units g P/G' ... (g+1) P/G' - 1 (G' groups, G' | P) and
+    the band tiles j with j mod G' = g; a group's unit v owns [floor(v T_g / (P/G')),
+    floor((v+1) T_g / (P/G'))) of the group's own T_g iterations;
   * roles: K_idx == 0 and final -> whole tile; K_idx == 0 only -> first; final only -> last;
     neither -> middle;
   * the data-parallel tiles run first, then the Stream-K tail.
@@ -150,21 +153,39 @@ def streamk_split_plan(tiles, P):
     return full * P, tail
 
 
-def streamk_units(sk_tiles, Kt, P, first_tile=0):
-    """For each unit u, its splits [(tile, K_idx, count, final)] in forward k order."""
-    T = sk_tiles * Kt
+def streamk_units(sk_tiles, Kt, P, first_tile=0, groups=1):
+    """For each unit u, its splits [(tile, K_idx, count, final)] in forward k order.
+
+    With `groups` > 1 ("H100 Stream-K" lesson, section 7) the units form that many independent
+    groups and so do the band's tiles: band tile j belongs to group j mod groups as that group's
+    (j div groups)-th tile (tile id = id in group * groups + group index), and each group splits
+    the iterations of its own tiles equally over its own units.  Reading: the units of a group are
+    a contiguous block of P / groups unit ids (group g = u div (P / groups)), so that units with
+    the same index in every group -- which work the same K range of neighbouring tiles -- are
+    P / groups apart.
+    """
+    if groups < 1 or P % groups != 0:
+        raise ValueError("the group count must divide P")
+    if groups > max(sk_tiles, 1):
+        raise ValueError("more Stream-K groups than Stream-K tiles")
+    per_group = P // groups
+    # the tiles of each group, in the group's own order
+    group_tiles = [[j for j in range(sk_tiles) if j % groups == g] for g in range(groups)]
     units = []
     for u in range(P):
-        lo, hi = (u * T) // P, ((u + 1) * T) // P
+        g, v = divmod(u, per_group)
+        mine = group_tiles[g]
+        T = len(mine) * Kt
+        lo, hi = (v * T) // per_group, ((v + 1) * T) // per_group
         splits = []
         it = lo
         while it < hi:
-            t = it // Kt
+            t = it // Kt                      # position of the tile in the group's list
             tile_first_iter = t * Kt
             end = min(hi, tile_first_iter + Kt)
             k_idx = it - tile_first_iter
             count = end - it
-            splits.append((first_tile + t, k_idx, count, k_idx + count == Kt))
+            splits.append((first_tile + mine[t], k_idx, count, k_idx + count == Kt))
             it = end
         units.append(splits)
     return units
@@ -177,7 +198,7 @@ def role_of(k_idx, final):
 
 
 def enumerate_schedule(M, N, K, BM, BN, BK, mapping, G, sched, P=None, X=8, xcd_remap=True,
-                       W=1):
+                       W=1, sk_groups=1):
     """Every work item of the launch, grouped by workgroup, in each workgroup's order."""
     Mt, Nt, Kt = tile_counts(M, N, K, BM, BN, BK)
     order = tile_order(mapping, Mt, Nt, G, W)
@@ -201,7 +222,8 @@ def enumerate_schedule(M, N, K, BM, BN, BK, mapping, G, sched, P=None, X=8, xcd_
     else:
         raise ValueError(f"unknown scheduler {sched}")
     ids = xcd_worker_ids(P, X) if xcd_remap else list(range(P))
-    units = streamk_units(sk_tiles, Kt, P, first_tile=dp_tiles) if sk_tiles else None
+    units = (streamk_units(sk_tiles, Kt, P, first_tile=dp_tiles, groups=sk_groups)
+             if sk_tiles else None)
     for b in range(P):
         seq = 0
         for i in range(ids[b], dp_tiles, P):

@@ -218,3 +218,94 @@ def test_streamk_backward_tile_order_and_roles():
         want = {(True, True): S.ROLE_WHOLE, (True, False): S.ROLE_FIRST,
                 (False, False): S.ROLE_MIDDLE, (False, True): S.ROLE_LAST}[(first, final)]
         assert it.role == want
+
+
+# ---- Stream-K groups ("H100 Stream-K" lesson, section 7) -------------------------------------
+
+def test_streamk_groups_hand_example():
+    """4 band tiles of 4 k-tiles, 8 units, 2 groups: group 0 holds tiles 0 and 2 and units 0-3,
+    group 1 tiles 1 and 3 and units 4-7; each group splits its 8 iterations 2 per unit."""
+    plan = S.streamk_units(4, 4, 8, groups=2)
+    want = [[(0, 0, 2, False)], [(0, 2, 2, True)], [(2, 0, 2, False)], [(2, 2, 2, True)],
+            [(1, 0, 2, False)], [(1, 2, 2, True)], [(3, 0, 2, False)], [(3, 2, 2, True)]]
+    assert plan == want
+
+
+@pytest.mark.parametrize("sk_tiles,Kt,P,G", [(16, 1024, 256, 4), (16, 1024, 256, 8), (5, 7, 6, 2),
+                                            (64, 32, 256, 8), (10, 16, 40, 5), (3, 9, 12, 3),
+                                            (100, 64, 256, 8), (7, 5, 8, 4)])
+def test_streamk_groups_partition_and_interleave(sk_tiles, Kt, P, G):
+    """Every (tile, k-tile) of the band is done exactly once; a tile's splits all come from one
+    group's units, a contiguous block in K order; band tile j is in group j mod G at position
+    j div G (tile id = id in group * G + group index); each group's units share its iterations
+    equally (within one)."""
+    first = 37
+    plan = S.streamk_units(sk_tiles, Kt, P, first_tile=first, groups=G)
+    U = P // G
+    cnt = Counter()
+    owners = {}
+    for u, splits in enumerate(plan):
+        g = u // U
+        for (tile, k_idx, count, final) in splits:
+            j = tile - first
+            assert 0 <= j < sk_tiles and j % G == g
+            assert final == (k_idx + count == Kt)
+            for k in range(k_idx, k_idx + count):
+                cnt[(j, k)] += 1
+            owners.setdefault(j, []).append((k_idx, u))
+    assert set(cnt) == {(j, k) for j in range(sk_tiles) for k in range(Kt)}
+    assert set(cnt.values()) == {1}
+    for j, ks in owners.items():
+        ks.sort()
+        units = [u for _, u in ks]
+        assert units == list(range(units[0], units[0] + len(units)))
+    for g in range(G):
+        tiles_g = len(range(g, sk_tiles, G))
+        work = [sum(c for (_, _, c, _) in plan[u]) for u in range(g * U, (g + 1) * U)]
+        assert sum(work) == tiles_g * Kt and max(work) - min(work) <= 1
+
+
+@pytest.mark.parametrize("sk_tiles,Kt,P,G", [(16, 1024, 256, 4), (64, 32, 256, 8), (6, 7, 9, 3)])
+def test_streamk_groups_same_k_range_across_groups(sk_tiles, Kt, P, G):
+    """With equal groups, the v-th unit of every group works the same K ranges, on the tiles that
+    sit next to each other in the band (the same wave of the data-parallel raster order)."""
+    plan = S.streamk_units(sk_tiles, Kt, P, groups=G)
+    U = P // G
+    for v in range(U):
+        base = plan[v]
+        for g in range(1, G):
+            other = plan[g * U + v]
+            assert [(t - g, k, c, f) for (t, k, c, f) in other] == base
+
+
+def test_streamk_one_group_is_the_single_pool():
+    """G = 1 is the plain Stream-K split (the lesson's worked example holds for it)."""
+    for args in [(16, 1024, 256), (7, 5, 8), (100, 64, 256)]:
+        assert S.streamk_units(*args, groups=1) == S.streamk_units(*args)
+    g = load("streamk_worked_example.txt")
+    tiles, kt, units = int(g["tiles"][0]), int(g["k_tiles_per_tile"][0]), int(g["units"][0])
+    plan = S.streamk_units(tiles, kt, units, groups=1)
+    for s in g["split"]:
+        u, t, k_idx, count, final = ints(s)
+        assert (t, k_idx, count, bool(final)) in plan[u]
+
+
+def test_streamk_groups_rejected_shapes():
+    with pytest.raises(ValueError):
+        S.streamk_units(16, 64, 256, groups=3)      # 3 does not divide 256
+    with pytest.raises(ValueError):
+        S.streamk_units(2, 64, 256, groups=4)       # more groups than band tiles
+
+
+def test_streamk_groups_in_the_launch_enumeration():
+    """enumerate_schedule passes the group count through: 3072^2 on 128 x 128 tiles and 256
+    workers leaves a band of 64 tiles after two data-parallel waves; with 8 groups the band's
+    tile j is split only among workers 32 (j mod 8) ... 32 (j mod 8) + 31."""
+    items = S.enumerate_schedule(3072, 3072, 4096, 128, 128, 64, S.LINEAR_N, 1, S.STREAMK,
+                                 P=256, sk_groups=8)
+    dp = [it for it in items if it.tile < 512]
+    sk = [it for it in items if it.tile >= 512]
+    assert all(it.k_begin == 0 and it.k_end == 64 for it in dp) and len(dp) == 512
+    for it in sk:
+        assert it.worker // 32 == (it.tile - 512) % 8
+    assert Counter(it.tile for it in sk) == {t: 4 for t in range(512, 576)}
