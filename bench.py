@@ -126,11 +126,13 @@ def measured_traffic(workload):
     return entry.get("bytes_per_launch")
 
 
-# name, workload key, mapping, group, sched, tile, out, workers[, bk[, variant[, epilogue]]]
+# name, workload key, mapping, group, sched, tile, out, workers[, bk[, variant[, epilogue[,
+# Stream-K groups]]]]
 # variant: "chain" = Stream-K lock-chain fixup; "coop" / "pp" / "vs" / "wide" = the cooperative /
 # ping-pong / register-staged / wide-wave kernel instead of the default for data-parallel
 # 256 x 256 tiles (the wide-wave kernel).  epilogue: the fused operations, {"bias": "row" |
 # "col", "act": "relu" | "gelu" | "silu", "amax": True}; out "e4m3" quantises the output.
+# Stream-K groups: 0 / 1 = one pool of units over the band, up to 8.
 RUNS = {
     "bf16_4096": ("bf16_4096", "grouped_m", 8, "persistent", 0, "bf16", 0),
     "bf16_4096_coop": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "coop"),
@@ -176,6 +178,7 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
     wl_name, mapping, group, sched, tile, out, workers = RUNS[name][:7]
     bk = RUNS[name][7] if len(RUNS[name]) > 7 else 0
     epi_spec = RUNS[name][9] if len(RUNS[name]) > 9 else {}
+    sk_groups = RUNS[name][10] if len(RUNS[name]) > 10 else 0
     flags = run_flags(name, dg)
     wl = gi.WORKLOADS[wl_name]
     if wl_name not in cache:
@@ -201,7 +204,8 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
     desc = dg.make_desc(op.M, op.N, op.K,
                         dg.GEMM_BF16 if op.dtype == "bf16" else dg.GEMM_FP8_E4M3,
                         dg.OUT_DTYPES[out], dg.MAPPINGS[mapping],
-                        group, dg.SCHEDS[sched], workers, tile, tile, bk, flags, epilogue=epi)
+                        group, dg.SCHEDS[sched], workers, tile, tile, bk, flags, epilogue=epi,
+                        sk_groups=sk_groups)
     plan = dg.Plan(desc)
     C = torch.empty((op.M, op.N), device=A.device,
                     dtype={"bf16": torch.bfloat16, "f32": torch.float32, "e4m3": torch.uint8}[out])
@@ -251,6 +255,7 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
         "tile": [info.bm, info.bn, info.bk], "stages": info.stages, "mapping": mapping,
         "kernel": ["cooperative", "ping-pong", "register-staged", "wide-wave"][info.kernel],
         "group": info.group, "group_n": info.group_n, "sched": sched, "grid": info.grid,
+        "sk_groups": info.sk_groups,
         "epilogue": epi_spec,
         "dp_tiles": info.dp_tiles, "sk_tiles": info.sk_tiles, "warmup_launches": n_warm,
         "ms_per_step": wall * 1e3 / steps, "kernel_us": dev_ms * 1e3,

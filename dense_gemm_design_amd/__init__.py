@@ -25,13 +25,14 @@ OUT_DTYPES = {"f32": GEMM_F32, "bf16": GEMM_BF16, "e4m3": GEMM_FP8_E4M3}
 
 def gemm(A, B, out_dtype="f32", scale_a=None, scale_b=None, mapping="grouped_m", group=8,
          sched="auto", tile=0, flags=0, bias_row=None, bias_col=None, activation=None,
-         scale_d=None, amax=None, group_n=0):
+         scale_d=None, amax=None, group_n=0, sk_groups=0):
     """D = epilogue(alpha * A x B) for torch device tensors: A (M, K) row-major; B given as (N, K),
     i.e. the K x N operand in column-major storage; bf16 or uint8-coded e4m3 (then scale_a /
     scale_b are one-element float32 device tensors).  Optional fused epilogue: a float32 bias per
     row (M) or per column (N), an activation ("relu", "gelu", "silu"), amax (a one-element float32
     device tensor the kernel max-combines max |Y| into), and out_dtype "e4m3" (uint8 codes of
-    Y / scale_d, scale_d a one-element float32 device tensor).  Returns C (M, N): float32,
+    Y / scale_d, scale_d a one-element float32 device tensor).  sk_groups: Stream-K groups (0-8)
+    of a plan with a Stream-K band.  Returns C (M, N): float32,
     bfloat16, or uint8 e4m3 codes."""
     import torch
     M, K = A.shape
@@ -43,7 +44,7 @@ def gemm(A, B, out_dtype="f32", scale_a=None, scale_b=None, mapping="grouped_m",
     epi |= GEMM_EPI_AMAX if amax is not None else 0
     desc = make_desc(M, N, K, GEMM_FP8_E4M3 if fp8 else GEMM_BF16, OUT_DTYPES[out_dtype],
                      MAPPINGS[mapping], group, SCHEDS[sched], 0, tile, tile, 0, flags,
-                     epilogue=epi, group_n=group_n)
+                     epilogue=epi, group_n=group_n, sk_groups=sk_groups)
     plan = Plan(desc)
     dt = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8}[out_dtype]
     C = torch.empty((M, N), device=A.device, dtype=dt)

@@ -47,7 +47,7 @@ class GemmDesc(ctypes.Structure):
                 ("sched", ctypes.c_int32), ("num_workers", ctypes.c_int32),
                 ("bm", ctypes.c_int32), ("bn", ctypes.c_int32), ("bk", ctypes.c_int32),
                 ("flags", ctypes.c_uint32), ("epilogue", ctypes.c_uint32),
-                ("group_n", ctypes.c_int32)]
+                ("group_n", ctypes.c_int32), ("sk_groups", ctypes.c_int32)]
 
 
 class GemmEpilogueArgs(ctypes.Structure):
@@ -69,7 +69,8 @@ class GemmPlanInfo(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_int64), ("trace_offset", ctypes.c_int64),
                 ("trace_capacity", ctypes.c_int32), ("error_offset", ctypes.c_int32),
                 ("streamk_mode", ctypes.c_int32), ("kernel", ctypes.c_int32),
-                ("group", ctypes.c_int32), ("group_n", ctypes.c_int32), ("pad_", ctypes.c_int32)]
+                ("group", ctypes.c_int32), ("group_n", ctypes.c_int32),
+                ("sk_groups", ctypes.c_int32)]
 
 
 class GemmConfigScore(ctypes.Structure):
@@ -128,9 +129,10 @@ def _check(status, where):
 
 def make_desc(M, N, K, dtype_ab=GEMM_BF16, dtype_c=GEMM_F32, mapping=GEMM_MAP_LINEAR_N, group=1,
               sched=GEMM_SCHED_PERSISTENT, num_workers=0, bm=0, bn=0, bk=0, flags=0,
-              layout_a=GEMM_ROW_MAJOR, layout_b=GEMM_COL_MAJOR, epilogue=0, group_n=0):
+              layout_a=GEMM_ROW_MAJOR, layout_b=GEMM_COL_MAJOR, epilogue=0, group_n=0,
+              sk_groups=0):
     return GemmDesc(M, N, K, dtype_ab, dtype_c, layout_a, layout_b, mapping, group, sched,
-                    num_workers, bm, bn, bk, flags, epilogue, group_n)
+                    num_workers, bm, bn, bk, flags, epilogue, group_n, sk_groups)
 
 
 def rank_configs(desc):

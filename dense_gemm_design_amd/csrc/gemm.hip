@@ -182,6 +182,16 @@ const KernelEntry kKernels[] = {
 };
 
 constexpr int kXcds = 8;           // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kMaxSkGroups = 8;    // Stream-K groups: at most 8 ("H100 Stream-K" lesson, sec. 7)
+
+// Stream-K group count of a plan: the request (0 = one pool), lowered to the largest count that
+// divides the P units evenly and leaves every group at least one band tile.
+int32_t streamk_groups(int32_t requested, int32_t P, int32_t sk_tiles) {
+  if (sk_tiles <= 0 || requested <= 1) return 1;
+  for (int32_t g = requested; g > 1; --g)
+    if (P % g == 0 && g <= sk_tiles) return g;
+  return 1;
+}
 constexpr int kDefaultSpin = 1 << 24;
 constexpr int kTestSpin = 4096;
 constexpr int kTraceCap = 64;
@@ -429,6 +439,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   const bool grouped = d.mapping == GEMM_MAP_GROUPED_M || d.mapping == GEMM_MAP_GROUPED_N || blocked;
   if (grouped && d.group < 0) return GEMM_ERR_INVALID_ARG;  // 0: the planner picks G
   if (blocked && d.group_n < 0) return GEMM_ERR_INVALID_ARG;
+  if (d.sk_groups < 0 || d.sk_groups > kMaxSkGroups) return GEMM_ERR_INVALID_ARG;
   if (d.sched < GEMM_SCHED_STATIC || d.sched > GEMM_SCHED_AUTO) return GEMM_ERR_INVALID_ARG;
   if (d.num_workers < 0 || d.bm < 0 || d.bn < 0 || d.bk < 0) return GEMM_ERR_INVALID_ARG;
   const uint32_t kind_flags =
@@ -563,6 +574,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     }
     if ((int64_t)sp.sk_tiles * Kt > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
   }
+  sp.sk_groups = streamk_groups(d.sk_groups, sp.P, sp.sk_tiles);
   sp.X = (d.flags & GEMM_FLAG_NO_XCD_REMAP) ? 1 : kXcds;
   if (blocked) {  // the planner's box: fewest operand strips per XCD's run of tiles
     choose_box(Mt, Nt, sp.P % sp.X == 0 ? sp.P / sp.X : sp.P, sp.G, sp.G2);
@@ -577,8 +589,10 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   p->k = k;
 
   // Stream-K fixup mode: the separate reduction needs every unit to own at least one iteration
-  // (band of T >= P iterations); otherwise, or when asked, the lock chain.
-  const bool chain = (d.flags & GEMM_FLAG_STREAMK_CHAIN) || (int64_t)sp.sk_tiles * Kt < sp.P;
+  // (each group's band of T_g >= P / G iterations; the smallest group holds floor(sk_tiles / G)
+  // tiles); otherwise, or when asked, the lock chain.
+  const bool chain = (d.flags & GEMM_FLAG_STREAMK_CHAIN) ||
+                     (int64_t)(sp.sk_tiles / sp.sk_groups) * Kt < sp.sk_gunits;
   const int sk_mode = chain ? SK_CHAIN : SK_SEPARATE;
   if (chain && sp.sk_tiles > 0 && k->kind == KIND_WIDE) {  // the wide-wave kernel has no chain
     if (force_kind == KIND_WIDE) {
@@ -588,9 +602,9 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     k = by_kind[KIND_COOP];
     p->k = k;
   }
-  // partial tiles: one per split tile (chain), or one per (unit, tile) pair, indexed unit + tile,
-  // at most P + sk_tiles of them (separate)
-  const int64_t partial_slots = sp.sk_tiles == 0 ? 0 : (chain ? sp.sk_tiles : sp.P + sp.sk_tiles);
+  // partial tiles: one per split tile (chain), or one per (unit, tile) pair (separate: per group,
+  // unit + the group's tile, P / G + ceil(sk_tiles / G) of them)
+  const int64_t partial_slots = sp.sk_tiles == 0 ? 0 : (chain ? sp.sk_tiles : sk_partial_slots(sp));
   // the kernels address the partial area with 32-bit buffer offsets
   if (partial_slots * (int64_t)bm * bn * 4 > 0x7FFFFFF0ll) {
     delete p;
@@ -654,6 +668,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   in.kernel = k->kind;
   in.group = sp.G;
   in.group_n = sp.G2;
+  in.sk_groups = sp.sk_groups;
   *out = p;
   return GEMM_OK;
 }
@@ -670,6 +685,7 @@ int gemm_rank_configs(const gemm_desc *desc, gemm_config_score *items, size_t ca
   if (!epilogue_valid(d.epilogue)) return GEMM_ERR_INVALID_ARG;
   if (d.mapping < GEMM_MAP_LINEAR_N || d.mapping > GEMM_MAP_MORTON) return GEMM_ERR_INVALID_ARG;
   if (d.mapping == GEMM_MAP_BLOCKED && d.group_n < 0) return GEMM_ERR_INVALID_ARG;
+  if (d.sk_groups < 0 || d.sk_groups > kMaxSkGroups) return GEMM_ERR_INVALID_ARG;
   std::vector<gemm_config_score> ranked;
   const int st = rank_configs(d, ranked);
   if (st != GEMM_OK) return st;

@@ -740,13 +740,13 @@ __device__ __forceinline__ void fixup_chain(const KernelArgs &args, const WorkIt
 }
 
 // Separate-reduction fixup, part 1: split (unit b on band tile t) stores its partial into its own
-// slot b + t and arrives on the tile's counter.
+// partial slot (sk_partial_slot) and arrives on the tile's counter.
 template <class CFG>
 __device__ __forceinline__ void fixup_separate_store(const KernelArgs &args, const WorkItem &w,
                                                      const f32x16 (&acc)[CFG::FM][CFG::FN],
                                                      int32_t b, int tid) {
   const __amdgpu_buffer_rsrc_t pr = partial_rsrc(args.partials);
-  const uint32_t slot = slot_byte<CFG>((int64_t)b + w.sk_slot) + tid * 16;
+  const uint32_t slot = slot_byte<CFG>(sk_partial_slot(args.sp, b, w.sk_slot)) + tid * 16;
 #pragma unroll
   for (int f = 0; f < CFG::FM; ++f)
 #pragma unroll
@@ -791,10 +791,10 @@ __device__ __forceinline__ void fixup_separate_reduce(const KernelArgs &args, co
   constexpr int NQ = CFG::BM * CFG::BN / 4;
   const int q_begin = (int)((int64_t)NQ * j / n), q_end = (int)((int64_t)NQ * (j + 1) / n);
   const __amdgpu_buffer_rsrc_t pr = partial_rsrc(args.partials);
-  const uint32_t base = slot_byte<CFG>((int64_t)u0 + w.sk_slot);
+  const uint32_t base = slot_byte<CFG>(sk_partial_slot(args.sp, u0, w.sk_slot));
   constexpr uint32_t SLOT = CFG::BM * CFG::BN * 4;
   for (int qq = q_begin + tid; qq < q_end; qq += CFG::THREADS) {
-    // sum over u = 0..n-1 of slot u0 + t + u, left to right; four loads in flight per step
+    // sum over u = 0..n-1 of the tile's consecutive slots, left to right; four loads in flight
     const uint32_t off = base + qq * 16;
     f32x4 sum = load_coherent(pr, off);
     int u = 1;
@@ -1800,7 +1800,7 @@ __device__ __forceinline__ void wide_partial_store(const KernelArgs &args, const
                                                    int32_t b, int wm, int wn, int lane, int tid) {
   static_assert(CFG::MI == 16, "16 x 16 blocks");
   const __amdgpu_buffer_rsrc_t pr = partial_rsrc(args.partials);
-  const uint32_t slot = slot_byte<CFG>((int64_t)b + w.sk_slot);
+  const uint32_t slot = slot_byte<CFG>(sk_partial_slot(args.sp, b, w.sk_slot));
   const uint32_t r0 = (uint32_t)(wm * CFG::WM + (lane & 15));
   const uint32_t c0 = (uint32_t)(wn * CFG::WN + (lane >> 4) * 4);
 #pragma unroll
@@ -1845,7 +1845,7 @@ __device__ __forceinline__ void wide_reduce(const KernelArgs &args, const WorkIt
   constexpr uint32_t SLOT = CFG::BM * CFG::BN * 4;
   const int q_begin = (int)((int64_t)NQ * j / n), q_end = (int)((int64_t)NQ * (j + 1) / n);
   const __amdgpu_buffer_rsrc_t pr = partial_rsrc(args.partials);
-  const uint32_t base = slot_byte<CFG>((int64_t)u0 + w.sk_slot);
+  const uint32_t base = slot_byte<CFG>(sk_partial_slot(args.sp, u0, w.sk_slot));
   for (int qq = q_begin + tid; qq < q_end; qq += CFG::THREADS) {
     const uint32_t off = base + (uint32_t)qq * 16;
     f32x4 sum = load_coherent(pr, off);

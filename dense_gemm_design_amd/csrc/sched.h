@@ -67,11 +67,15 @@ struct SchedParams {
   int32_t G2;              // blocked: box width in tile columns
   int32_t dp_tiles;        // tasks i < dp_tiles run whole (data parallel)
   int32_t sk_tiles;        // the next sk_tiles tasks are split along K (Stream-K band)
+  int32_t sk_groups;       // Stream-K groups (divides P, at most sk_tiles; 1 = one pool)
+  int32_t sk_gunits;       // units per group, P / sk_groups
+  int32_t sk_gtiles;       // band tiles of the largest group, ceil(sk_tiles / sk_groups)
   // divisors of the mapping and of the Stream-K band (filled by sched_prepare)
   FastDiv div_major;       // Nt (linear N), Mt (linear M), G*Nt (grouped M), G*Mt (grouped N)
   FastDiv div_g;           // G (grouped), unused otherwise
   FastDiv div_g_last;      // width of the short last strip (grouped), else = div_g
   FastDiv div_kt;          // Kt (Stream-K band), 1 when Kt == 0
+  FastDiv div_skg;         // sk_groups
   FastDiv div_box;         // blocked: G * G2 tiles of a full-height box
   FastDiv div_box_last;    // blocked: (height of the short last box row) * G2
   int32_t full_strips;     // strips (blocked: box rows) of exactly G
@@ -96,6 +100,10 @@ inline void sched_prepare(SchedParams &sp) {
   sp.div_box = make_fastdiv((uint32_t)(G * G2));
   sp.div_box_last = make_fastdiv((uint32_t)((last > 0 ? last : G) * G2));
   sp.div_kt = make_fastdiv((uint32_t)(sp.Kt > 0 ? sp.Kt : 1));
+  if (sp.sk_groups < 1) sp.sk_groups = 1;
+  sp.sk_gunits = sp.P / sp.sk_groups;
+  sp.sk_gtiles = (sp.sk_tiles + sp.sk_groups - 1) / sp.sk_groups;
+  sp.div_skg = make_fastdiv((uint32_t)sp.sk_groups);
   int32_t size = 1;
   while (size < sp.Mt || size < sp.Nt) size *= 2;
   sp.morton_size = size;
@@ -194,16 +202,28 @@ DG_HD int32_t xcd_worker(int32_t b, int32_t P, int32_t X) {
 // the last tile it touches back to the first.
 struct Cursor {
   int32_t next_dp;         // next data-parallel task
-  int32_t sk_lo, sk_hi;    // remaining Stream-K iterations [sk_lo, sk_hi), consumed from the top
+  int32_t sk_lo, sk_hi;    // remaining Stream-K iterations [sk_lo, sk_hi) of the unit's group,
+                           // consumed from the top
+  int32_t sk_group;        // the unit's Stream-K group
 };
+
+// Stream-K groups: unit u is unit v = u mod (P/G) of group g = u div (P/G); band tile t is tile
+// t div G of group t mod G.  Group g has ceil((sk_tiles - g) / G) tiles and T_g = tiles * Kt
+// iterations, of which its unit v owns [floor(v T_g / (P/G)), floor((v+1) T_g / (P/G))).  With
+// G = 1 this is the single pool: unit b owns [floor(b T / P), floor((b+1) T / P)).
+DG_HD int64_t sk_group_iters(const SchedParams &sp, int32_t g) {
+  return (int64_t)((sp.sk_tiles - g + sp.sk_groups - 1) / sp.sk_groups) * sp.Kt;
+}
 
 DG_HD void cursor_init(const SchedParams &sp, int32_t b, Cursor &c) {
   c.next_dp = xcd_worker(b, sp.P, sp.X);
+  c.sk_group = 0;
   if (sp.sk_tiles > 0) {
-    // unit b owns iterations [floor(b T / P), floor((b+1) T / P)) of the band of T iterations
-    const int64_t T = sp.sk_tiles * (int64_t)sp.Kt;
-    c.sk_lo = (int32_t)((int64_t)b * T / sp.P);
-    c.sk_hi = (int32_t)((int64_t)(b + 1) * T / sp.P);
+    const int32_t g = b / sp.sk_gunits, v = b - g * sp.sk_gunits;
+    const int64_t T = sk_group_iters(sp, g);
+    c.sk_group = g;
+    c.sk_lo = (int32_t)((int64_t)v * T / sp.sk_gunits);
+    c.sk_hi = (int32_t)((int64_t)(v + 1) * T / sp.sk_gunits);
   } else {
     c.sk_lo = c.sk_hi = 0;
   }
@@ -219,9 +239,10 @@ DG_HD bool cursor_next(const SchedParams &sp, Cursor &c, WorkItem &w) {
     w.sk_slot = -1;
   } else if (c.sk_hi > c.sk_lo) {
     const int32_t last = c.sk_hi - 1;
-    const int32_t t = fdiv(last, sp.div_kt);        // band-local tile of the top iteration
-    const int32_t t_first = t * sp.Kt;
+    const int32_t tg = fdiv(last, sp.div_kt);       // the group's tile of the top iteration
+    const int32_t t_first = tg * sp.Kt;
     const int32_t start = c.sk_lo > t_first ? c.sk_lo : t_first;
+    const int32_t t = tg * sp.sk_groups + c.sk_group;  // band-local tile
     w.tile = sp.dp_tiles + t;
     w.kb = start - t_first;
     w.ke = c.sk_hi - t_first;
@@ -238,17 +259,30 @@ DG_HD bool cursor_next(const SchedParams &sp, Cursor &c, WorkItem &w) {
   return true;
 }
 
-// Stream-K units that share band-local tile t: unit u covers iterations
-// [floor(u T / P), floor((u+1) T / P)), so the unit holding iteration x is the largest u with
-// floor(u T / P) <= x, i.e. floor(((x + 1) P - 1) / T).  Tile t spans iterations
-// [t Kt, (t+1) Kt); its units are u0 .. u1, consecutive, in increasing K order.
-DG_HD int32_t sk_unit_of(const SchedParams &sp, int64_t x) {
-  const int64_t T = (int64_t)sp.sk_tiles * sp.Kt;
-  return (int32_t)(((x + 1) * sp.P - 1) / T);
-}
+// Stream-K units that share band-local tile t: in its group g, unit v covers iterations
+// [floor(v T_g / U), floor((v+1) T_g / U)) (U = P/G units per group), so the unit holding
+// iteration x is the largest v with floor(v T_g / U) <= x, i.e. floor(((x + 1) U - 1) / T_g).
+// Tile t is the group's tile t div G and spans its iterations [(t div G) Kt, (t div G + 1) Kt);
+// its units are u0 .. u1 (unit ids g U + v), consecutive, in increasing K order.
 DG_HD void sk_tile_units(const SchedParams &sp, int32_t t, int32_t &u0, int32_t &u1) {
-  u0 = sk_unit_of(sp, (int64_t)t * sp.Kt);
-  u1 = sk_unit_of(sp, (int64_t)(t + 1) * sp.Kt - 1);
+  const int32_t tg = fdiv(t, sp.div_skg), g = t - tg * sp.sk_groups;
+  const int64_t T = sk_group_iters(sp, g), U = sp.sk_gunits;
+  const int64_t x0 = (int64_t)tg * sp.Kt, x1 = x0 + sp.Kt - 1;
+  u0 = g * sp.sk_gunits + (int32_t)(((x0 + 1) * U - 1) / T);
+  u1 = g * sp.sk_gunits + (int32_t)(((x1 + 1) * U - 1) / T);
+}
+
+// Separate-reduction partial slot of unit u's split of band tile t.  Within a group, unit v and
+// the group's tile tg give v + tg, which no other split of the group shares (a later unit only
+// touches the same or later tiles, so v' > v and tg' < tg never meet); groups take disjoint
+// ranges of U + sk_gtiles slots, and the units of one tile have consecutive slots.
+DG_HD int64_t sk_partial_slot(const SchedParams &sp, int32_t u, int32_t t) {
+  const int32_t tg = fdiv(t, sp.div_skg), g = t - tg * sp.sk_groups;
+  const int32_t v = u - g * sp.sk_gunits;
+  return (int64_t)g * (sp.sk_gunits + sp.sk_gtiles) + v + tg;
+}
+DG_HD int64_t sk_partial_slots(const SchedParams &sp) {
+  return (int64_t)sp.sk_groups * (sp.sk_gunits + sp.sk_gtiles);
 }
 
 // Hybrid rule: with P workers and `tiles` tasks, the full waves stay data parallel; the tail

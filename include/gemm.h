@@ -127,13 +127,23 @@ typedef struct gemm_desc {
                                 BLOCKED (>= 1, or 0 = chosen by the planner); ignored by the
                                 linear ones and MORTON                                          */
   int32_t sched;             /* gemm_sched                                                       */
-  int32_t num_workers;       /* P for persistent / Stream-K; 0 = CUs x resident workgroups/CU    */
+  int32_t num_workers;       /* P for persistent / Stream-K; 0 = CUs x resident workgroups/CU.
+                                Stream-K workgroups wait on each other: a P above what the
+                                device holds at once makes the bounded waits expire
+                                (GEMM_DEVICE_ERR_SPIN in the error word)                        */
   int32_t bm, bn, bk;        /* tile shape; 0 = auto.  Supported: see gemm_create              */
   uint32_t flags;            /* GEMM_FLAG_*                                                      */
   uint32_t epilogue;         /* GEMM_EPI_* bits: fused bias / activation / amax (0 = none)      */
   int32_t group_n;           /* BLOCKED: box width in tile columns (>= 1, or 0 = chosen by the
                                 planner, which then fills the box with the tiles one XCD runs
                                 at a time); ignored by the other mappings                      */
+  int32_t sk_groups;         /* Stream-K groups ("H100 Stream-K" lesson, section 7), 0..8; 0 or 1
+                                = one pool of units over the whole band.  With G > 1 band tile
+                                j goes to group j mod G and workgroups g P/G .. (g+1) P/G - 1 form
+                                group g, which splits its own tiles' iterations equally; G is
+                                lowered to the largest count that divides P and is at most the
+                                band's tile count (gemm_plan_info.sk_groups).  Ignored without a
+                                Stream-K band.                                                  */
 } gemm_desc;
 
 /* One unit of work as the scheduler hands it out (gemm_schedule_enumerate, device trace). */
@@ -163,7 +173,7 @@ typedef struct gemm_plan_info {
   int32_t kernel;            /* 0 cooperative, 1 ping-pong, 2 register-staged, 3 wide-wave       */
   int32_t group;             /* G of a grouped mapping as planned (1 for the linear ones)       */
   int32_t group_n;           /* box width of BLOCKED as planned (1 for the other mappings)      */
-  int32_t pad_;
+  int32_t sk_groups;         /* Stream-K groups as planned (1 without a band)                   */
 } gemm_plan_info;
 
 /* device error word values (read back from the workspace after a run) */

@@ -401,3 +401,75 @@ def test_wide_streamk_watchdog(dev):
                           256)
     err = int(ws.cpu().numpy()[plan.info.error_offset:plan.info.error_offset + 4].view(np.int32)[0])
     assert err == L.GEMM_DEVICE_OK
+
+
+# ---- Stream-K groups ---------------------------------------------------------------------------
+
+SKG_KERNELS = {"wide": (0, 3, 1), "coop_separate": (L.GEMM_FLAG_COOPERATIVE, 0, 1),
+               "coop_chain": (L.GEMM_FLAG_COOPERATIVE | L.GEMM_FLAG_STREAMK_CHAIN, 0, 0)}
+SKG_CASES = [
+    # id, M, N, K, dtype, out, workers, tile, mapping, G, requested groups -> planned groups
+    ("all_split_g4", 512, 512, 16384, "bf16", "f32", 64, 128, L.GEMM_MAP_LINEAR_N, 1, 4, 4),
+    ("hybrid_g5", 1280, 640, 2048, "bf16", "bf16", 40, 128, L.GEMM_MAP_GROUPED_M, 4, 5, 5),
+    ("hybrid_g8_ragged", 1256, 632, 1000, "bf16", "f32", 40, 128, L.GEMM_MAP_LINEAR_N, 1, 8, 8),
+    ("fp8_256_g3", 768, 1280, 4096, "e4m3", "bf16", 12, 256, L.GEMM_MAP_GROUPED_N, 2, 3, 3),
+]
+
+
+@pytest.mark.parametrize("kern", list(SKG_KERNELS))
+@pytest.mark.parametrize("case", SKG_CASES, ids=[c[0] for c in SKG_CASES])
+def test_streamk_groups_parity(dev, case, kern):
+    """Stream-K groups on both kernels and both fixups: within tolerance of the oracle, the
+    device error word clear, the plan as asked."""
+    name, M, N, K, dt, out, workers, tile, mapping, G, req, planned = case
+    flags, kind, mode = SKG_KERNELS[kern]
+    dist = ("normal", 1.0) if dt == "e4m3" else ("uniform",)
+    op = gi.make_operands(M, N, K, dt, dist, dist, seed=zlib.crc32(name.encode()) % 10000)
+    C, plan, ws = run_gpu(op, torch, dev, out, mapping, G, L.GEMM_SCHED_STREAMK, workers, tile,
+                          flags=flags, sk_groups=req)
+    info = plan.info
+    assert info.sk_tiles > 0 and info.sk_groups == planned
+    assert info.kernel == kind and info.streamk_mode == mode
+    err = int(ws.cpu().numpy()[info.error_offset:info.error_offset + 4].view(np.int32)[0])
+    assert err == L.GEMM_DEVICE_OK
+    assert_within_tolerance(C, reference(op), op, f"{name} {kern}")
+
+
+@pytest.mark.parametrize("kern", list(SKG_KERNELS))
+def test_streamk_groups_small_integers_bit_exact(dev, kern):
+    """Exact partial sums: every group count gives the oracle's result bit for bit (a k-tile lost
+    or doubled by the group split would show)."""
+    flags = SKG_KERNELS[kern][0]
+    M, N, K = 1280, 640, 4096
+    op = gi.make_operands(M, N, K, "bf16", ("smallint", -2, 2), ("smallint", -2, 2), seed=91)
+    ref = reference(op)
+    for req in (1, 2, 5, 8):
+        C, plan, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_GROUPED_M, 4, L.GEMM_SCHED_STREAMK,
+                             40, 128, flags=flags, sk_groups=req)
+        assert plan.info.sk_groups == req and plan.info.sk_tiles == 10
+        assert np.array_equal(C, ref), f"{kern} groups {req}"
+
+
+@pytest.mark.parametrize("tile,workers,req,flags", [(128, 40, 5, 0), (128, 40, 8, 0),
+                                                    (256, 12, 3, 0),
+                                                    (128, 40, 4, L.GEMM_FLAG_COOPERATIVE),
+                                                    (128, 40, 2, L.GEMM_FLAG_STREAMK_CHAIN)])
+def test_device_trace_streamk_groups(dev, tile, workers, req, flags):
+    """Work items the kernel records under Stream-K groups equal the CPU replay and the oracle."""
+    M, N, K = 1280, 640, 2048
+    if tile == 256:
+        M, N = 768, 1280
+    op = gi.make_operands(M, N, K, "bf16", seed=13)
+    C, plan, ws = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_GROUPED_M, 2, L.GEMM_SCHED_STREAMK,
+                          workers, tile, flags=flags | L.GEMM_FLAG_TRACE, sk_groups=req)
+    info = plan.info
+    assert info.sk_groups == req and info.sk_tiles > 0
+    raw = ws.cpu().numpy()[info.trace_offset:].view(np.int32)[: info.grid * info.trace_capacity * 8]
+    rec = raw.reshape(info.grid, info.trace_capacity, 8)
+    got = [tuple(int(x) for x in r) for w in range(info.grid) for r in rec[w]
+           if r[0] == w and r[6] > 0]
+    assert got == plan.schedule()
+    ora = S.enumerate_schedule(M, N, K, tile, tile, info.bk, S.GROUPED_M, 2, S.STREAMK,
+                               P=info.grid, sk_groups=req)
+    assert got == [(w.worker, w.seq, w.tile, w.m, w.n, w.k_begin, w.k_end, w.role) for w in ora]
+    assert_within_tolerance(C, reference(op), op, "groups trace run")

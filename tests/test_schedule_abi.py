@@ -93,3 +93,71 @@ def test_blocked_planner_box():
     p = L.Plan(L.make_desc(1024, 1024, 1024, mapping=L.GEMM_MAP_MORTON, num_workers=8, bm=128,
                            bn=128))
     assert (p.info.group, p.info.group_n) == (1, 1)
+
+
+SK_GROUP_CASES = [
+    # M, N, K, dtype, tile, mapping, G (mapping), P, requested groups, planned groups
+    (512, 512, 65536, L.GEMM_BF16, 128, L.GEMM_MAP_LINEAR_N, 1, 256, 4, 4),
+    (512, 512, 65536, L.GEMM_BF16, 128, L.GEMM_MAP_LINEAR_N, 1, 256, 8, 8),
+    (3072, 3072, 4096, L.GEMM_BF16, 128, L.GEMM_MAP_GROUPED_M, 8, 256, 8, 8),
+    (3072, 3072, 4096, L.GEMM_BF16, 256, L.GEMM_MAP_LINEAR_N, 1, 64, 8, 8),
+    (1280, 640, 1024, L.GEMM_BF16, 128, L.GEMM_MAP_GROUPED_M, 4, 40, 8, 8),
+    (1280, 640, 1024, L.GEMM_BF16, 128, L.GEMM_MAP_GROUPED_M, 4, 40, 7, 5),   # 7, 6 do not divide 40
+    (1280, 640, 1024, L.GEMM_BF16, 128, L.GEMM_MAP_GROUPED_M, 4, 40, 3, 2),
+    (384, 256, 448, L.GEMM_BF16, 128, L.GEMM_MAP_LINEAR_N, 1, 5, 4, 1),       # a band of 1 tile
+    (2048, 2048, 2048, L.GEMM_FP8_E4M3, 128, L.GEMM_MAP_GROUPED_N, 8, 768, 6, 6),
+    (1280, 640, 1024, L.GEMM_BF16, 128, L.GEMM_MAP_BLOCKED, 2, 40, 4, 4),
+]
+
+
+@pytest.mark.parametrize("case", SK_GROUP_CASES)
+def test_streamk_groups_enumeration_matches_oracle(case):
+    """Stream-K groups: the planned count follows the lowering rule (largest count <= the request
+    that divides P and leaves every group a tile), and the schedule equals the oracle's."""
+    M, N, K, dt, tile, mapping, G, P, req, planned = case
+    W = 3 if mapping == L.GEMM_MAP_BLOCKED else 0
+    plan = L.Plan(L.make_desc(M, N, K, dtype_ab=dt, mapping=mapping, group=G,
+                              sched=L.GEMM_SCHED_STREAMK, num_workers=P, bm=tile, bn=tile,
+                              group_n=W, sk_groups=req))
+    info = plan.info
+    assert info.sk_tiles > 0 and info.sk_groups == planned
+    want = S.enumerate_schedule(M, N, K, tile, tile, info.bk, MAP[mapping], G, S.STREAMK,
+                                P=info.grid, W=max(W, 1), sk_groups=planned)
+    assert plan.schedule() == [(w.worker, w.seq, w.tile, w.m, w.n, w.k_begin, w.k_end, w.role)
+                               for w in want]
+
+
+def test_streamk_groups_validation_and_reporting():
+    lib = L.load()
+    import ctypes
+    h = ctypes.c_void_p()
+    for bad in (-1, 9):
+        d = L.make_desc(512, 512, 65536, sched=L.GEMM_SCHED_STREAMK, num_workers=256, bm=128,
+                        bn=128, sk_groups=bad)
+        assert lib.gemm_create(ctypes.byref(d), ctypes.byref(h)) == L.GEMM_ERR_INVALID_ARG
+    # no band: reported as one group, whatever was asked
+    p = L.Plan(L.make_desc(1024, 1024, 1024, sched=L.GEMM_SCHED_PERSISTENT, num_workers=8,
+                           bm=128, bn=128, sk_groups=4))
+    assert p.info.sk_groups == 1
+    p = L.Plan(L.make_desc(512, 512, 65536, sched=L.GEMM_SCHED_STREAMK, num_workers=256, bm=128,
+                           bn=128))
+    assert p.info.sk_groups == 1
+
+
+def test_streamk_groups_fixup_mode_and_workspace():
+    """The separate reduction needs every unit of every group to own an iteration; the partial
+    area holds G (P/G + ceil(sk_tiles/G)) tiles."""
+    d = dict(sched=L.GEMM_SCHED_STREAMK, num_workers=256, bm=128, bn=128)
+    one = L.Plan(L.make_desc(512, 512, 65536, sk_groups=1, **d)).info
+    eight = L.Plan(L.make_desc(512, 512, 65536, sk_groups=8, **d)).info
+    assert one.streamk_mode == eight.streamk_mode == 1
+    slot = 128 * 128 * 4
+    assert eight.workspace_bytes - one.workspace_bytes == (8 * (32 + 2) - (256 + 16)) * slot
+    # 10 band tiles of 4 k-tiles over 40 units: one pool gives every unit an iteration; in 8
+    # groups of 5 units the smallest group has one tile (4 iterations) -> the lock chain
+    d = dict(sched=L.GEMM_SCHED_STREAMK, num_workers=40, bm=128, bn=128,
+             mapping=L.GEMM_MAP_GROUPED_M, group=4)
+    p1 = L.Plan(L.make_desc(1280, 640, 256, sk_groups=1, **d)).info
+    p8 = L.Plan(L.make_desc(1280, 640, 256, sk_groups=8, **d)).info
+    assert p1.sk_tiles == p8.sk_tiles == 10 and p8.sk_groups == 8
+    assert p1.streamk_mode == 1 and p8.streamk_mode == 0
