@@ -137,13 +137,16 @@ typedef struct gemm_desc {
   int32_t group_n;           /* BLOCKED: box width in tile columns (>= 1, or 0 = chosen by the
                                 planner, which then fills the box with the tiles one XCD runs
                                 at a time); ignored by the other mappings                      */
-  int32_t sk_groups;         /* Stream-K groups ("H100 Stream-K" lesson, section 7), 0..8; 0 or 1
-                                = one pool of units over the whole band.  With G > 1 band tile
-                                j goes to group j mod G and workgroups g P/G .. (g+1) P/G - 1 form
-                                group g, which splits its own tiles' iterations equally; G is
-                                lowered to the largest count that divides P and is at most the
-                                band's tile count (gemm_plan_info.sk_groups).  Ignored without a
-                                Stream-K band.                                                  */
+  int32_t sk_groups;         /* Stream-K groups ("H100 Stream-K" lesson, section 7), 0..8; 1 =
+                                one pool of units over the whole band, 0 = chosen by the
+                                planner.  With G > 1 band tile j goes to group j mod G and
+                                workgroups g P/G .. (g+1) P/G - 1 form group g, which splits its
+                                own tiles' iterations equally; a requested G is lowered to the
+                                largest count that divides P and is at most the band's tile
+                                count.  The planner takes the largest such count up to 8 whose
+                                P / G is a multiple of the XCD count and which keeps the fixup
+                                mode of one pool (gemm_plan_info.sk_groups reports the count).
+                                Ignored without a Stream-K band.                                */
 } gemm_desc;
 
 /* One unit of work as the scheduler hands it out (gemm_schedule_enumerate, device trace). */

@@ -224,7 +224,7 @@ def test_device_trace_matches_enumeration(dev, sched, workers, tile, mapping, G,
     SCH = {0: S.STATIC, 1: S.PERSISTENT, 2: S.STREAMK}
     ora = S.enumerate_schedule(M, N, K, tile, tile, info.bk, MAP[mapping], G, SCH[sched],
                                P=None if sched == L.GEMM_SCHED_STATIC else info.grid,
-                               W=info.group_n)
+                               W=info.group_n, sk_groups=info.sk_groups)
     assert got == [(w.worker, w.seq, w.tile, w.m, w.n, w.k_begin, w.k_end, w.role) for w in ora]
     assert_within_tolerance(C, reference(op), op, "trace run")
 

@@ -54,13 +54,14 @@ def test_enumeration_matches_oracle(case):
     Pw = plan.info.grid if sched != L.GEMM_SCHED_STATIC else None
     want = S.enumerate_schedule(M, N, K, tile, tile, bk, MAP[mapping], G, SCHED[sched],
                                 P=P if sched != L.GEMM_SCHED_STATIC else None,
-                                xcd_remap=remap, W=max(W, 1))
+                                xcd_remap=remap, W=max(W, 1), sk_groups=plan.info.sk_groups)
     want = [(w.worker, w.seq, w.tile, w.m, w.n, w.k_begin, w.k_end, w.role) for w in want]
     if sched == L.GEMM_SCHED_PERSISTENT:
         # the planner caps P at the tile count; the oracle is asked with the same P
         want = [(w.worker, w.seq, w.tile, w.m, w.n, w.k_begin, w.k_end, w.role) for w in
                 S.enumerate_schedule(M, N, K, tile, tile, bk, MAP[mapping], G, SCHED[sched],
-                                     P=Pw, xcd_remap=remap, W=max(W, 1))]
+                                     P=Pw, xcd_remap=remap, W=max(W, 1),
+                                     sk_groups=plan.info.sk_groups)]
     assert got == want
 
 
@@ -140,8 +141,26 @@ def test_streamk_groups_validation_and_reporting():
                            bm=128, bn=128, sk_groups=4))
     assert p.info.sk_groups == 1
     p = L.Plan(L.make_desc(512, 512, 65536, sched=L.GEMM_SCHED_STREAMK, num_workers=256, bm=128,
-                           bn=128))
+                           bn=128, sk_groups=1))
     assert p.info.sk_groups == 1
+
+
+def test_streamk_groups_planner_choice():
+    """sk_groups = 0: the largest count up to 8 that divides P, leaves P / G a multiple of the 8
+    XCDs, gives every group a tile, and keeps the fixup mode one pool would have."""
+    def planned(M, N, K, P, tile=128):
+        i = L.Plan(L.make_desc(M, N, K, sched=L.GEMM_SCHED_STREAMK, num_workers=P, bm=tile,
+                               bn=tile)).info
+        return i.sk_tiles, i.sk_groups, i.streamk_mode
+    assert planned(512, 512, 65536, 256) == (16, 8, 1)
+    assert planned(1280, 1280, 32768, 256) == (100, 8, 1)
+    assert planned(1280, 640, 1024, 40) == (10, 5, 1)           # 40 / 8 = 5 units: not on one XCD
+    assert planned(768, 1280, 4096, 12, 256) == (3, 1, 1)       # 12 / 3 = 4 units
+    # 12 band tiles of 22 k-tiles on 256 units: 8 groups would leave groups of one tile (22
+    # iterations) for 32 units -> the chain; 4 groups (3 tiles, 66 iterations, 64 units) do not
+    assert planned(512, 67 * 128, 22 * 64, 256) == (12, 4, 1)
+    # no XCD-compatible count at all
+    assert planned(1280, 640, 1024, 36)[1] == 1
 
 
 def test_streamk_groups_fixup_mode_and_workspace():
