@@ -1791,8 +1791,8 @@ __device__ __forceinline__ void epilogue_direct_fused(const KernelArgs &args, co
 }
 
 // Stream-K in the wide-wave kernels (separate reduction, "H100 Stream-K" lesson, section 6, with
-// every split storing its own partial): the partial slot of (unit b, band tile t) is b + t, like
-// the cooperative kernel's, but laid out row-major -- element (r, c) of the BM x BN tile at
+// every split storing its own partial): the partial slot of (unit b, band tile t) is
+// sk_partial_slot(b, t), like the cooperative kernel's, but laid out row-major -- element (r, c) of the BM x BN tile at
 // (r BN + c) 4 bytes -- so the reduction reads whole rows whatever MFMA shape wrote them.
 template <class CFG>
 __device__ __forceinline__ void wide_partial_store(const KernelArgs &args, const WorkItem &w,
