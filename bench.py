@@ -145,7 +145,7 @@ RUNS = {
     "bf16_4096_pp": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "pp"),
     "fp8_8192_pp": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "pp"),
     "bf16_mlp_up_pp": ("bf16_mlp_up", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "pp"),
-    "bf16_mlp_up": ("bf16_mlp_up", "grouped_m", 8, "persistent", 0, "bf16", 0),
+    "bf16_mlp_up": ("bf16_mlp_up", "grouped_m", 8, "auto", 0, "bf16", 0),
     "bf16_streamk": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256),
     "bf16_streamk_chain": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256, 0,
                            "chain"),
@@ -159,7 +159,7 @@ RUNS = {
     "bf16_mlp_up_morton": ("bf16_mlp_up", "morton", 1, "persistent", 0, "bf16", 0),
     # fused epilogues: the MLP up-projection with its bias and GELU; an FP8 layer whose output
     # is quantised back to e4m3 with amax tracking
-    "bf16_mlp_up_bias_gelu": ("bf16_mlp_up", "grouped_m", 8, "persistent", 0, "bf16", 0, 0, "",
+    "bf16_mlp_up_bias_gelu": ("bf16_mlp_up", "grouped_m", 8, "auto", 0, "bf16", 0, 0, "",
                               {"bias": "col", "act": "gelu"}),
     "fp8_8192_e4m3_amax": ("fp8_8192", "grouped_m", 16, "persistent", 0, "e4m3", 0, 0, "",
                            {"amax": True}),

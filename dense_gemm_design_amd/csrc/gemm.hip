@@ -44,6 +44,12 @@ using CfgFp8_256w = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1, 16>;  // 16 x 16 
 // at 4096^3 and 34 % on 1024 x 1024 x 16384 e4m3 than two stages)
 using CfgBf16_128w = TileCfg<DT_BF16, 128, 128, 64, 2, 2, 4, 1, 16>;
 using CfgFp8_128w = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 4, 1, 16>;
+// ... and on 256 x 224 tiles (waves of 128 x 112): a block width from the heuristic's aligned set
+// below 256 that fills whole waves where 256 does not -- N = 14336 is 64 such columns, so
+// 4096 x 14336 makes 1024 tiles, four full waves of 256 CUs, where 256 x 256 tiles leave the
+// fourth wave half empty
+using CfgBf16_224w = TileCfg<DT_BF16, 256, 224, 64, 2, 2, 2, 1, 16>;
+using CfgFp8_224w = TileCfg<DT_FP8, 256, 224, 128, 2, 2, 2, 1, 16>;
 
 typedef hipError_t (*launch_fn)(const KernelArgs &, int grid, bool ragged_k, hipStream_t);
 typedef const void *(*kernel_fn)();
@@ -178,6 +184,8 @@ const KernelEntry kKernels[] = {
     entry_wide<CfgFp8_256w>(),
     entry_wide<CfgBf16_128w>(),
     entry_wide<CfgFp8_128w>(),
+    entry_wide<CfgBf16_224w>(),
+    entry_wide<CfgFp8_224w>(),
     entry<CfgFp8_128>(),
 };
 
@@ -248,8 +256,11 @@ constexpr double kLdsBytesPerClk = 256.0;    // ds_read_b128 per CU
 constexpr double kDeviceBytesPerClk = 2600;  // Stream-K partials, whole device (128 MiB in 25 us)
 constexpr double kLatencyClk = 2000;         // first load or store round trip of a phase
 // MFMA efficiency of whole launches at the held clock (bench workloads, profiles/)
-double kernel_efficiency(int kind, int bm, int dt) {
+double kernel_efficiency(int kind, int bm, int bn, int dt) {
   if (kind == KIND_WIDE && bm == 128) return dt == DT_BF16 ? 0.56 : 0.55;
+  // 256 x 224: 6 % below 256 x 256 at whole waves (8192 x 14336 x 4096 bf16: 1,397 against
+  // 1,492 TFLOP/s) -- 12.5 % fewer MACs per operand byte and the output without LDS staging
+  if (kind == KIND_WIDE && bn == 224) return dt == DT_BF16 ? 0.71 : 0.74;
   if (kind == KIND_WIDE) return dt == DT_BF16 ? 0.76 : 0.79;
   if (kind == KIND_PP) return 0.66;
   if (bm == 256) return dt == DT_BF16 ? 0.60 : 0.70;
@@ -319,6 +330,7 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
                                                     : d.dtype_c == GEMM_FP8_E4M3 ? 1.0
                                                                                  : 4.0;
   const ModelCand cands[] = {{KIND_WIDE, 256, 256, GEMM_SCHED_PERSISTENT},
+                             {KIND_WIDE, 256, 224, GEMM_SCHED_PERSISTENT},
                              {KIND_WIDE, 128, 128, GEMM_SCHED_PERSISTENT},
                              {KIND_COOP, 128, 128, GEMM_SCHED_PERSISTENT},
                              {KIND_WIDE, 128, 128, GEMM_SCHED_STREAMK},
@@ -388,7 +400,7 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
     r.cycles_l2 = bytes_l2 / (ncu * kL2BytesPerClk);
     r.cycles_local = bytes_local / (ncu * kLdsBytesPerClk);
     r.cycles_mfma = 2.0 * bm * bn * kk * t /
-                    (ncu * flop_per_clk_per_cu(dt) * kernel_efficiency(c.kind, c.bm, dt));
+                    (ncu * flop_per_clk_per_cu(dt) * kernel_efficiency(c.kind, c.bm, c.bn, dt));
     // wave efficiency over the CUs (a CU that runs fewer resident workgroups runs each faster)
     double items;  // items per worker, for the epilogues
     if (c.sched == GEMM_SCHED_STREAMK) {
@@ -517,6 +529,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
         !by_kind[e.kind])
       by_kind[e.kind] = &e;
   const KernelEntry *k = by_kind[force_kind >= 0 ? force_kind : KIND_COOP];
+  if (!k && force_kind < 0) k = by_kind[KIND_WIDE];  // tile shapes only the wide-wave kernel has
   if (!k) return GEMM_ERR_UNSUPPORTED;  // the schedule is planned with this one
   // rows of one tile must stay addressable by 32-bit buffer offsets
   if ((int64_t)bm * d.K * eb >= 0x7FFFFFF0ll || (int64_t)bn * d.K * eb >= 0x7FFFFFF0ll)
@@ -614,7 +627,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
                      (int64_t)(sp.sk_tiles / sp.sk_groups) * Kt < sp.sk_gunits;
   const int sk_mode = chain ? SK_CHAIN : SK_SEPARATE;
   if (chain && sp.sk_tiles > 0 && k->kind == KIND_WIDE) {  // the wide-wave kernel has no chain
-    if (force_kind == KIND_WIDE) {
+    if (force_kind == KIND_WIDE || !by_kind[KIND_COOP]) {
       delete p;
       return GEMM_ERR_UNSUPPORTED;
     }

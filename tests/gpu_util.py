@@ -26,14 +26,14 @@ def decode_output(C, torch):
 
 def run_gpu(op, torch, device, out="f32", mapping=L.GEMM_MAP_LINEAR_N, group=1,
             sched=L.GEMM_SCHED_PERSISTENT, workers=0, tile=0, flags=0, plan=None, keep=False,
-            bk=0, group_n=0, sk_groups=0):
+            bk=0, group_n=0, sk_groups=0, bn=0):
     """Runs C = alpha * A x B on the GPU; returns (C decoded to float64, plan, workspace)."""
     A, B, sa, sb = to_device(op, torch, device)
     if plan is None:
         desc = L.make_desc(op.M, op.N, op.K,
                            L.GEMM_BF16 if op.dtype == "bf16" else L.GEMM_FP8_E4M3,
                            L.GEMM_BF16 if out == "bf16" else L.GEMM_F32, mapping, group, sched,
-                           workers, tile, tile, bk, flags, group_n=group_n,
+                           workers, tile, bn or tile, bk, flags, group_n=group_n,
                            sk_groups=sk_groups)
         plan = L.Plan(desc)
     C = torch.empty((op.M, op.N), device=device,

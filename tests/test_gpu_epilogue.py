@@ -40,8 +40,9 @@ def run_epi(op, dev, out, bias_kind=None, bias=None, act=None, amax=True, scale_
     A, B, sa, sb = to_device(op, torch, dev)
     epi = ACT_BITS[act] | (L.GEMM_EPI_AMAX if amax else 0)
     epi |= {None: 0, "row": L.GEMM_EPI_BIAS_ROW, "col": L.GEMM_EPI_BIAS_COL}[bias_kind]
+    bm, bn = tile if isinstance(tile, tuple) else (tile, tile)
     desc = L.make_desc(op.M, op.N, op.K, L.GEMM_BF16 if op.dtype == "bf16" else L.GEMM_FP8_E4M3,
-                       OUT[out], mapping, group, sched, workers, tile, tile, 0, flags,
+                       OUT[out], mapping, group, sched, workers, bm, bn, 0, flags,
                        epilogue=epi)
     plan = L.Plan(desc)
     dt = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8}[out]
@@ -136,6 +137,13 @@ CASES = [
      L.GEMM_SCHED_STREAMK, 5, "col", "gelu"),
     ("wide_streamk_fp8_e4m3_silu", 512, 768, 8192, "e4m3", "e4m3", L.GEMM_FLAG_WIDE, 256,
      L.GEMM_SCHED_STREAMK, 4, "row", "silu"),
+    # 256 x 224 tiles (wide-wave only): ragged edges, every output type, Stream-K
+    ("wide224_bf16_bias_col_gelu", 520, 904, 1000, "bf16", "bf16", 0, (256, 224),
+     L.GEMM_SCHED_PERSISTENT, 3, "col", "gelu"),
+    ("wide224_fp8_e4m3_row_silu", 776, 688, 1040, "e4m3", "e4m3", 0, (256, 224),
+     L.GEMM_SCHED_PERSISTENT, 4, "row", "silu"),
+    ("wide224_streamk_bf16_f32_relu", 512, 448, 8192, "bf16", "f32", 0, (256, 224),
+     L.GEMM_SCHED_STREAMK, 8, "col", "relu"),
 ]
 
 

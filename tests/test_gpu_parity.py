@@ -473,3 +473,53 @@ def test_device_trace_streamk_groups(dev, tile, workers, req, flags):
                                P=info.grid, sk_groups=req)
     assert got == [(w.worker, w.seq, w.tile, w.m, w.n, w.k_begin, w.k_end, w.role) for w in ora]
     assert_within_tolerance(C, reference(op), op, "groups trace run")
+
+
+# ---- 256 x 224 tiles ---------------------------------------------------------------------------
+
+T224 = [
+    # id, M, N, K, dtype, out, sched, workers, mapping, G
+    ("bf16_ragged", 520, 904, 1000, "bf16", "bf16", L.GEMM_SCHED_PERSISTENT, 3,
+     L.GEMM_MAP_GROUPED_M, 2),
+    ("bf16_f32_static", 512, 672, 512, "bf16", "f32", L.GEMM_SCHED_STATIC, 0,
+     L.GEMM_MAP_LINEAR_N, 1),
+    ("fp8_ragged", 776, 688, 1040, "e4m3", "bf16", L.GEMM_SCHED_PERSISTENT, 4,
+     L.GEMM_MAP_BLOCKED, 0),
+    ("bf16_streamk", 512, 448, 16384, "bf16", "f32", L.GEMM_SCHED_STREAMK, 8,
+     L.GEMM_MAP_LINEAR_N, 1),
+    ("fp8_streamk_hybrid", 768, 1344, 4096, "e4m3", "bf16", L.GEMM_SCHED_STREAMK, 12,
+     L.GEMM_MAP_GROUPED_N, 2),
+]
+
+
+@pytest.mark.parametrize("case", T224, ids=[c[0] for c in T224])
+def test_tile_256x224_parity(dev, case):
+    """256 x 224 tiles run on the wide-wave kernel only (waves of 128 x 112): within tolerance
+    of the oracle for data-parallel and Stream-K plans, ragged edges included."""
+    name, M, N, K, dt, out, sched, workers, mapping, G = case
+    dist = ("normal", 1.0) if dt == "e4m3" else ("uniform",)
+    op = gi.make_operands(M, N, K, dt, dist, dist, seed=zlib.crc32(name.encode()) % 10000)
+    C, plan, ws = run_gpu(op, torch, dev, out, mapping, G, sched, workers, 256, bn=224)
+    info = plan.info
+    assert info.kernel == 3 and (info.bm, info.bn) == (256, 224)
+    if sched == L.GEMM_SCHED_STREAMK:
+        assert info.sk_tiles > 0
+        err = int(ws.cpu().numpy()[info.error_offset:info.error_offset + 4].view(np.int32)[0])
+        assert err == L.GEMM_DEVICE_OK
+    assert_within_tolerance(C, reference(op), op, name)
+
+
+def test_tile_256x224_small_integers_bit_exact(dev):
+    """Exact partial sums: the 256 x 224 kernel equals the oracle bit for bit, data-parallel and
+    Stream-K, and equals the 256 x 256 kernel (same MFMA, same k order)."""
+    M, N, K = 512, 896, 8192
+    op = gi.make_operands(M, N, K, "bf16", ("smallint", -2, 2), ("smallint", -2, 2), seed=33)
+    ref = reference(op)
+    C1, p1, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_PERSISTENT, 8,
+                        256, bn=224)
+    C2, p2, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK, 24,
+                        256, bn=224)
+    C3, _, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_PERSISTENT, 8,
+                       256)
+    assert p1.info.bn == 224 and p2.info.sk_tiles > 0
+    assert np.array_equal(C1, ref) and np.array_equal(C2, ref) and np.array_equal(C3, ref)
