@@ -1632,11 +1632,11 @@ __device__ __forceinline__ f32x4 wide_fused_quad(const KernelArgs &args, const a
   return epi_act<ACT>(args.epi, v, ec.am, bias.inside(f, g));
 }
 
-// bf16 output of a 128 x 128 sub-tile through the wave's LDS slice, 32 rows at a time.  Chunk c
-// (16 bytes) of staged row r sits at chunk position c ^ (r mod 16): the rows one write touches
-// and the 4 rows one read-back touches each spread over every bank.  16 lanes store one whole
-// 256-byte row segment.  A fused FUSE adds the bias, the activation and the amax (16 x 16
-// blocks).
+// bf16 output of a 128-row sub-tile (128 or 112 columns) through the wave's LDS slice, 32 rows at
+// a time, at a pitch of 256 bytes.  Chunk c (16 bytes) of staged row r sits at chunk position
+// c ^ (r mod 16): the rows one write touches and the 4 rows one read-back touches each spread
+// over every bank.  16 lanes store one row segment (the sub-tile's 14 or 16 chunks).  A fused
+// FUSE adds the bias, the activation and the amax (16 x 16 blocks).
 template <class CFG, int FUSE = FUSE_OFF>
 __device__ __forceinline__ void epilogue_wide(const KernelArgs &args, const WorkItem &w,
                                               const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
@@ -1645,14 +1645,17 @@ __device__ __forceinline__ void epilogue_wide(const KernelArgs &args, const Work
   static_assert(FUSE == FUSE_OFF || CFG::MI == 16, "fused epilogue on 16 x 16 blocks");
   typedef u32x2 __attribute__((address_space(3))) *p64;
   typedef u32x4 __attribute__((address_space(3))) *p128;
-  static_assert(CFG::WN * 2 == 256 && CFG::WM == 128, "rows of the staged sub-tile are 256 bytes");
+  static_assert(CFG::WN * 2 <= 256 && CFG::WN % 16 == 0 && CFG::WM == 128,
+                "staged sub-tile rows fit the slice's 256-byte pitch");
   const int64_t m0 = (int64_t)w.m * CFG::BM + wm * CFG::WM;
   const int64_t n0 = (int64_t)w.n * CFG::BN + wn * CFG::WN;
   if (m0 >= args.M || n0 >= args.N) return;  // the wave's sub-tile lies past the edge of C
   const int64_t origin = m0 * args.ldc + n0;
   const __amdgpu_buffer_rsrc_t cr = make_rsrc(args.C + origin * 2, (args.M * args.ldc - origin) * 2);
   const int chunk_l = lane & 15, rrow = lane >> 4;  // read-back: 4 rows per wave-wide read
-  const bool col_ok = n0 + chunk_l * 8 < args.N;
+  // 16 lanes cover a 256-byte pitch; a narrower sub-tile (112 columns: 14 chunks) leaves the
+  // last chunks of each staged row unused
+  const bool col_ok = chunk_l * 8 < CFG::WN && n0 + chunk_l * 8 < args.N;
   const uint32_t ldc_b = (uint32_t)args.ldc * 2;
   const uint32_t st_off = (uint32_t)rrow * ldc_b + chunk_l * 16;
   // read j covers rows rrow + 4j, whose swizzle is (rrow ^ 4 (j mod 4)): four lane bases
@@ -2118,8 +2121,8 @@ gemm_kernel_wide(KernelArgs args) {
     if constexpr (CFG::MI == 16) mfma_wait_states();  // the last MFMAs' results are written
     if (cw.role != ROLE_WHOLE) {  // a Stream-K split: its partial, reduced after all MAC work
       wide_partial_store<CFG>(args, cw, acc, b, wm, wn, lane, tid);
-    } else if (CFG::WN == 128 && args.out_bf16) {  // staged through the wave's LDS slice
-      if constexpr (CFG::WN == 128)
+    } else if (CFG::WM == 128 && args.out_bf16) {  // staged through the wave's LDS slice
+      if constexpr (CFG::WM == 128)
         epilogue_wide<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
     } else if constexpr (FUSE != FUSE_OFF) {
       epilogue_direct_fused<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, ec);
@@ -2303,8 +2306,8 @@ gemm_kernel_wide1(KernelArgs args) {
     mfma_wait_states();  // the last MFMAs' results are written
     if (cw.role != ROLE_WHOLE) {  // a Stream-K split: its partial, reduced after all MAC work
       wide_partial_store<CFG>(args, cw, acc, b, wm, wn, lane, tid);
-    } else if (CFG::WN == 128 && args.out_bf16) {  // staged through the wave's LDS slice
-      if constexpr (CFG::WN == 128)
+    } else if (CFG::WM == 128 && args.out_bf16) {  // staged through the wave's LDS slice
+      if constexpr (CFG::WM == 128)
         epilogue_wide<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
     } else if constexpr (FUSE != FUSE_OFF) {
       epilogue_direct_fused<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, ec);
