@@ -89,8 +89,9 @@ typedef enum {
                                         LDS.  Same limits as GEMM_FLAG_PINGPONG.  At most one of
                                         the kernel flags (else GEMM_ERR_INVALID_ARG)            */
 #define GEMM_FLAG_WIDE 0x40u         /* require the wide-wave kernel: four waves with 128 x 128
-                                        sub-tiles fed by direct global -> LDS loads, 16 x 16
-                                        MFMAs for bf16.  Same limits as GEMM_FLAG_PINGPONG      */
+                                        (or 128 x 112, 64 x 64) sub-tiles fed by direct global ->
+                                        LDS loads, 16 x 16 MFMAs.  Runs data-parallel plans and
+                                        Stream-K with the separate reduction                    */
 #define GEMM_FLAG_TEST_SKIP_PUBLISH 0x100u /* test only: the first Stream-K split of band tile 0
                                               does not publish its lock / arrival, so the bounded
                                               waits on it expire and report GEMM_DEVICE_ERR_SPIN */
@@ -186,8 +187,10 @@ typedef struct gemm_plan_info {
 typedef struct gemm_plan *gemm_handle;
 
 /* Validates the description and builds a plan.  Supported in this version:
- *   dtype_ab BF16 with tiles (bm, bn, bk) in {(256,256,64), (128,128,64)},
- *   dtype_ab FP8_E4M3 with tiles in {(256,256,128), (128,128,128)};
+ *   dtype_ab BF16 with tiles (bm, bn, bk) in {(256,256,64), (256,224,64), (128,128,64)},
+ *   dtype_ab FP8_E4M3 with tiles in {(256,256,128), (256,224,128), (128,128,128)}; 256 x 224
+ *   tiles run on the wide-wave kernel only (a plan that needs another kernel -- the Stream-K lock
+ *   chain, or a kernel flag other than GEMM_FLAG_WIDE -- returns GEMM_ERR_UNSUPPORTED);
  *   layout_a ROW and layout_b COL (both operands K-contiguous);
  *   K * sizeof(element) a multiple of 16 bytes; N a multiple of 8;
  *   M, N arbitrary otherwise (ragged tiles are masked), K ragged in the last k-tile.
@@ -252,8 +255,9 @@ typedef struct gemm_config_score {
 /* Kernel-configuration heuristic: the cost model of "DeepGEMM on SM90" (section "Kernel
  * Configuration Heuristic") -- candidates from a small discrete set, a resource filter, then
  * score = max(cycles_local, cycles_L2) / wave_efficiency with the minimum winning -- re-fitted to
- * gfx950: the candidates are this library's kernels and tiles (256 x 256 wide-wave data-parallel,
- * 128 x 128 cooperative data-parallel, both tiles on the cooperative kernel with a Stream-K tail),
+ * gfx950: the candidates are this library's kernels and tiles (256 x 256 and 256 x 224 wide-wave
+ * data-parallel -- the block width from the page's aligned set that fills whole waves -- 128 x 128
+ * wide-wave and cooperative data-parallel, and Stream-K tails on the 128 x 128 and 256 x 256 tiles),
  * the bandwidths and per-kernel MFMA efficiencies are measured on MI355X, a matrix-core term
  * joins the two data-movement terms, and the costs that do not overlap the MAC loop are added.  Fills up to `cap` candidates, best first, and the total to
  * *n_out (GEMM_ERR_CAPACITY when cap is too small; items may be NULL with cap 0).  gemm_create
