@@ -255,6 +255,12 @@ constexpr double kL2BytesPerClk = 57.0;      // global->LDS loads per CU
 constexpr double kLdsBytesPerClk = 256.0;    // ds_read_b128 per CU
 constexpr double kDeviceBytesPerClk = 2600;  // Stream-K partials, whole device (128 MiB in 25 us)
 constexpr double kLatencyClk = 2000;         // first load or store round trip of a phase
+// A partial last wave: the board is held at its power limit, so with a fraction f of the CUs busy
+// the busy ones clock higher (144 of 256 CUs finish a 256 x 256 x 4096 bf16 tile in 75 us, all
+// 256 in 95), up to the clock's headroom (2.4 GHz against the 1.9 held under full load).  Such a
+// wave is costed f^0.39 of a full one (fit to that pair), and no less than 1 / 1.3.
+constexpr double kPartialWaveExp = 0.39;
+constexpr double kMinPartialWave = 1.0 / 1.3;
 // MFMA efficiency of whole launches at the held clock (bench workloads, profiles/)
 double kernel_efficiency(int kind, int bm, int bn, int dt) {
   if (kind == KIND_WIDE && bm == 128) return dt == DT_BF16 ? 0.56 : 0.55;
@@ -408,7 +414,9 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
       r.wave_efficiency = iters / (std::ceil(iters / P) * P);
       items = std::ceil((double)dp / P) + 2.0;  // data-parallel tiles and about two splits
     } else {
-      r.wave_efficiency = tiles > 0 ? t / (std::ceil(t / ncu) * ncu) : 1.0;
+      const double waves = t / ncu, full = std::floor(waves), frac = waves - full;
+      const double last = frac > 0 ? std::max(std::pow(frac, kPartialWaveExp), kMinPartialWave) : 0.0;
+      r.wave_efficiency = tiles > 0 ? waves / (full + last) : 1.0;
       items = std::ceil(t / ncu);
     }
     const double stage_bytes = (bm + bn) * e->bk * eb;

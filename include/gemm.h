@@ -246,7 +246,10 @@ typedef struct gemm_config_score {
   double cycles_mfma;        /* modelled clocks, whole GEMM, matrix-core side                   */
   double cycles_l2;          /* L2 -> CU side: A/B tile loads and C                             */
   double cycles_local;       /* LDS side: tile fills, fragment reads, C staging                 */
-  double wave_efficiency;    /* busy CU slots / (waves x CUs); Stream-K: over its units         */
+  double wave_efficiency;    /* tiles / (CUs x effective waves), a partial last wave with a
+                                fraction f of the CUs busy counting f^0.39 of a full one (at
+                                least 1/1.3: the busy CUs clock higher under the board's power
+                                limit); Stream-K: busy unit slots over its units                 */
   double cycles_fixed;       /* not overlapped with the MAC loop: first loads, epilogues, and
                                 Stream-K partial sums through device memory                    */
   double score;              /* max(mfma, l2, local) / wave_efficiency + fixed; lower is better */

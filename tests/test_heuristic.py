@@ -34,10 +34,20 @@ def test_scores_are_the_models_formula():
 
 
 def test_wave_efficiency_of_a_partial_last_wave():
-    # 4096 x 14336 on 256 x 256 tiles: 16 x 56 = 896 tiles, 3.5 waves of 256
+    # 4096 x 14336 on 256 x 256 tiles: 16 x 56 = 896 tiles, 3.5 waves of 256; the half-busy last
+    # wave runs at a higher clock (power limit) and costs max(0.5^0.39, 1/1.3) of a full one
     ranked = L.rank_configs(desc(4096, 14336, 4096))
     dp = [c for c in ranked if (c.bm, c.bn) == (256, 256) and c.sched == L.GEMM_SCHED_PERSISTENT][0]
-    assert dp.wave_efficiency == pytest.approx(896 / (4 * 256))
+    assert dp.wave_efficiency == pytest.approx(3.5 / (3 + max(0.5 ** 0.39, 1 / 1.3)))
+    # 3072 x 3072 on 256 x 256 tiles: 144 tiles, one wave with 56 % of the CUs busy
+    d256 = [c for c in L.rank_configs(desc(3072, 3072, 4096))
+            if (c.bm, c.bn) == (256, 256) and c.sched == L.GEMM_SCHED_PERSISTENT][0]
+    assert d256.wave_efficiency == pytest.approx((144 / 256) / (144 / 256) ** 0.39)
+    # a nearly empty wave costs no less than the clock headroom allows (1 / 1.3 of a full one):
+    # 512 x 512 on 128 x 128 tiles is 16 tiles on 256 CUs
+    small = [c for c in L.rank_configs(desc(512, 512, 65536, out=L.GEMM_F32))
+             if c.bm == 128 and c.sched == L.GEMM_SCHED_PERSISTENT][0]
+    assert small.wave_efficiency == pytest.approx((16 / 256) * 1.3)
     # 256 x 224 tiles: 16 x 64 = 1024 tiles, four whole waves
     d224 = [c for c in ranked if (c.bm, c.bn) == (256, 224)][0]
     assert d224.wave_efficiency == pytest.approx(1.0)
@@ -70,6 +80,9 @@ def test_data_movement_terms():
     ((4096, 14336, 4096), L.GEMM_FP8_E4M3, L.GEMM_BF16, ((256, 224), 3, L.GEMM_SCHED_PERSISTENT)),
     # 1792 tiles of 256 x 256 = 7 whole waves: the wider tile stays
     ((8192, 14336, 4096), L.GEMM_BF16, L.GEMM_BF16, ((256, 256), 3, L.GEMM_SCHED_PERSISTENT)),
+    # one partial wave of big tiles (168 of 256 CUs, at a higher clock) beats 128 x 128 tiles
+    # with a Stream-K tail (measured 69 against 83 us)
+    ((3072, 3072, 4096), L.GEMM_BF16, L.GEMM_BF16, ((256, 224), 3, L.GEMM_SCHED_PERSISTENT)),
     ((512, 512, 65536), L.GEMM_BF16, L.GEMM_F32, (128, 3, L.GEMM_SCHED_STREAMK)),
     ((256, 256, 256), L.GEMM_BF16, L.GEMM_F32, (128, 3, L.GEMM_SCHED_PERSISTENT)),
 ])
@@ -129,6 +142,10 @@ def test_rank_validation():
     ((512, 512, 65536), L.GEMM_BF16, L.GEMM_F32),
     ((2048, 2048, 2048), L.GEMM_BF16, L.GEMM_BF16),
     ((1024, 1024, 16384), L.GEMM_FP8_E4M3, L.GEMM_BF16),
+    ((8192, 14336, 4096), L.GEMM_BF16, L.GEMM_BF16),
+    ((3072, 3072, 4096), L.GEMM_BF16, L.GEMM_BF16),
+    ((1280, 1280, 32768), L.GEMM_BF16, L.GEMM_BF16),
+    ((6144, 6144, 6144), L.GEMM_FP8_E4M3, L.GEMM_BF16),
 ])
 def test_pick_is_close_to_the_fastest_candidate(shape, dt, out):
     """Each candidate the model ranks runs as a forced plan; the model's pick must be within 15 %
