@@ -537,7 +537,8 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
         !by_kind[e.kind])
       by_kind[e.kind] = &e;
   const KernelEntry *k = by_kind[force_kind >= 0 ? force_kind : KIND_COOP];
-  if (!k && force_kind < 0) k = by_kind[KIND_WIDE];  // tile shapes only the wide-wave kernel has
+  // tile shapes only the wide-wave kernel has (which needs K > 0, like every data-parallel kernel)
+  if (!k && force_kind < 0 && d.K > 0) k = by_kind[KIND_WIDE];
   if (!k) return GEMM_ERR_UNSUPPORTED;  // the schedule is planned with this one
   // rows of one tile must stay addressable by 32-bit buffer offsets
   if ((int64_t)bm * d.K * eb >= 0x7FFFFFF0ll || (int64_t)bn * d.K * eb >= 0x7FFFFFF0ll)

@@ -189,8 +189,9 @@ typedef struct gemm_plan *gemm_handle;
 /* Validates the description and builds a plan.  Supported in this version:
  *   dtype_ab BF16 with tiles (bm, bn, bk) in {(256,256,64), (256,224,64), (128,128,64)},
  *   dtype_ab FP8_E4M3 with tiles in {(256,256,128), (256,224,128), (128,128,128)}; 256 x 224
- *   tiles run on the wide-wave kernel only (a plan that needs another kernel -- the Stream-K lock
- *   chain, or a kernel flag other than GEMM_FLAG_WIDE -- returns GEMM_ERR_UNSUPPORTED);
+ *   tiles run on the wide-wave kernel only (a plan that needs another kernel -- K = 0, the
+ *   Stream-K lock chain, or a kernel flag other than GEMM_FLAG_WIDE -- returns
+ *   GEMM_ERR_UNSUPPORTED);
  *   layout_a ROW and layout_b COL (both operands K-contiguous);
  *   K * sizeof(element) a multiple of 16 bytes; N a multiple of 8;
  *   M, N arbitrary otherwise (ragged tiles are masked), K ragged in the last k-tile.

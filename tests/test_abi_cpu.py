@@ -268,3 +268,31 @@ def test_package_has_no_cpu_fallback():
         assert not re.search(r"^\s*(import|from)\s+oracle", src, re.M), name
         for pat in ("matmul", "torch.mm(", "einsum", "bmm(", "np.dot", " @ "):
             assert pat not in src, (name, pat)
+
+
+def test_tile_256x224_plans():
+    """256 x 224 tiles exist only on the wide-wave kernel: data-parallel and separate-reduction
+    Stream-K plans are built; K = 0, the lock chain and the other kernels are refused."""
+    import ctypes
+    lib = L.load()
+    h = ctypes.c_void_p()
+
+    def status(K, sched=L.GEMM_SCHED_PERSISTENT, flags=0, P=8):
+        d = L.make_desc(512, 448, K, L.GEMM_BF16, L.GEMM_F32, L.GEMM_MAP_LINEAR_N, 1, sched, P,
+                        256, 224, 0, flags)
+        st = lib.gemm_create(ctypes.byref(d), ctypes.byref(h))
+        if st == L.GEMM_OK:
+            info = L.GemmPlanInfo()
+            lib.gemm_plan_get(h, ctypes.byref(info))
+            lib.gemm_destroy(h)
+            return st, info.kernel
+        return st, None
+    assert status(1024) == (L.GEMM_OK, 3)
+    assert status(1024, flags=L.GEMM_FLAG_WIDE) == (L.GEMM_OK, 3)
+    assert status(16384, sched=L.GEMM_SCHED_STREAMK) == (L.GEMM_OK, 3)
+    assert status(0)[0] == L.GEMM_ERR_UNSUPPORTED
+    assert status(0, flags=L.GEMM_FLAG_WIDE)[0] == L.GEMM_ERR_UNSUPPORTED
+    assert status(1024, flags=L.GEMM_FLAG_COOPERATIVE)[0] == L.GEMM_ERR_UNSUPPORTED
+    assert status(1024, flags=L.GEMM_FLAG_PINGPONG)[0] == L.GEMM_ERR_UNSUPPORTED
+    assert status(16384, sched=L.GEMM_SCHED_STREAMK,
+                  flags=L.GEMM_FLAG_STREAMK_CHAIN)[0] == L.GEMM_ERR_UNSUPPORTED
