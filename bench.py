@@ -146,6 +146,7 @@ RUNS = {
     "fp8_8192_pp": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "pp"),
     "bf16_mlp_up_pp": ("bf16_mlp_up", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "pp"),
     "bf16_mlp_up": ("bf16_mlp_up", "grouped_m", 8, "auto", 0, "bf16", 0),
+    "bf16_mlp_up_t256": ("bf16_mlp_up", "grouped_m", 8, "persistent", 256, "bf16", 0),
     "bf16_streamk": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256),
     "bf16_streamk_chain": ("bf16_streamk", "linear_n", 1, "streamk", 128, "f32", 256, 0,
                            "chain"),
@@ -343,6 +344,7 @@ def main():
         for name in ("bf16_4096_pp", "bf16_4096_coop", "bf16_4096_linear", "bf16_4096_t128",
                      "bf16_4096_blocked", "fp8_8192_pp", "fp8_8192_e4m3_amax", "fp8_8192_blocked",
                      "fp8_8192_morton", "fp8_8192", "bf16_mlp_up_bias_gelu", "bf16_mlp_up",
+                     "bf16_mlp_up_t256",
                      "bf16_streamk", "bf16_256"):
             steps = max(10, args.steps // (4 if name.startswith("fp8_8192") else 1))
             r = time_run(name, steps, max(2, args.warmup // 2), torch, dg, gi, cache,
