@@ -31,8 +31,9 @@ def gemm(A, B, out_dtype="f32", scale_a=None, scale_b=None, mapping="grouped_m",
     scale_b are one-element float32 device tensors).  Optional fused epilogue: a float32 bias per
     row (M) or per column (N), an activation ("relu", "gelu", "silu"), amax (a one-element float32
     device tensor the kernel max-combines max |Y| into), and out_dtype "e4m3" (uint8 codes of
-    Y / scale_d, scale_d a one-element float32 device tensor).  sk_groups: Stream-K groups (0-8)
-    of a plan with a Stream-K band.  Returns C (M, N): float32,
+    Y / scale_d, scale_d a one-element float32 device tensor).  tile: 0 (the planner's), an int
+    for square tiles, or (bm, bn), e.g. (256, 224).  sk_groups: Stream-K groups (0 = the
+    planner's count, 1-8) of a plan with a Stream-K band.  Returns C (M, N): float32,
     bfloat16, or uint8 e4m3 codes."""
     import torch
     M, K = A.shape
@@ -42,8 +43,9 @@ def gemm(A, B, out_dtype="f32", scale_a=None, scale_b=None, mapping="grouped_m",
     epi |= GEMM_EPI_BIAS_ROW if bias_row is not None else 0
     epi |= GEMM_EPI_BIAS_COL if bias_col is not None else 0
     epi |= GEMM_EPI_AMAX if amax is not None else 0
+    bm, bn = tile if isinstance(tile, tuple) else (tile, tile)
     desc = make_desc(M, N, K, GEMM_FP8_E4M3 if fp8 else GEMM_BF16, OUT_DTYPES[out_dtype],
-                     MAPPINGS[mapping], group, SCHEDS[sched], 0, tile, tile, 0, flags,
+                     MAPPINGS[mapping], group, SCHEDS[sched], 0, bm, bn, 0, flags,
                      epilogue=epi, group_n=group_n, sk_groups=sk_groups)
     plan = Plan(desc)
     dt = {"f32": torch.float32, "bf16": torch.bfloat16, "e4m3": torch.uint8}[out_dtype]

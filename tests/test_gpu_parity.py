@@ -523,3 +523,19 @@ def test_tile_256x224_small_integers_bit_exact(dev):
                        256)
     assert p1.info.bn == 224 and p2.info.sk_tiles > 0
     assert np.array_equal(C1, ref) and np.array_equal(C2, ref) and np.array_equal(C3, ref)
+
+
+def test_python_gemm_wrapper_tiles_and_groups(dev):
+    """dg.gemm(): (bm, bn) tiles and Stream-K groups reach the plan; results within tolerance."""
+    import dense_gemm_design_amd as dg
+    op = gi.make_operands(512, 896, 8192, "bf16", seed=41)
+    A, B, _, _ = to_device(op, torch, dev)
+    ref = reference(op)
+    C = dg.gemm(A, B, out_dtype="f32", mapping="linear_n", group=1, sched="persistent",
+                tile=(256, 224))
+    torch.cuda.synchronize()
+    assert_within_tolerance(C.cpu().numpy().astype(np.float64), ref, op, "gemm() 256 x 224")
+    C = dg.gemm(A, B, out_dtype="f32", mapping="linear_n", group=1, sched="streamk", tile=128,
+                sk_groups=4)
+    torch.cuda.synchronize()
+    assert_within_tolerance(C.cpu().numpy().astype(np.float64), ref, op, "gemm() Stream-K groups")
