@@ -146,6 +146,10 @@ def test_rank_validation():
     ((3072, 3072, 4096), L.GEMM_BF16, L.GEMM_BF16),
     ((1280, 1280, 32768), L.GEMM_BF16, L.GEMM_BF16),
     ((6144, 6144, 6144), L.GEMM_FP8_E4M3, L.GEMM_BF16),
+    # shapes the model's constants were not fitted to
+    ((5120, 5120, 5120), L.GEMM_BF16, L.GEMM_BF16),
+    ((4096, 11008, 4096), L.GEMM_BF16, L.GEMM_BF16),
+    ((4096, 28672, 8192), L.GEMM_FP8_E4M3, L.GEMM_BF16),
 ])
 def test_pick_is_close_to_the_fastest_candidate(shape, dt, out):
     """Each candidate the model ranks runs as a forced plan; the model's pick must be within 15 %
