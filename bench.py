@@ -35,16 +35,85 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+# The device code: the kernels and the scheduler they run.  A counter record stays valid while
+# these are unchanged; the planner (gemm.hip) only picks among them.
+DEVICE_SOURCES = ("gemm_kernel.h", "sched.h")
+
+
 def source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_gemm_design_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in DEVICE_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "hbm_traffic.json.txt")
+PEAK_CLOCK_MHZ = 2400.0  # the engine clock the published MFMA peaks assume
+
+
+class BoardSampler:
+    """Samples the GPU's shader clock (mean over its XCDs) and socket power through the amdsmi
+    library in a background thread while the timed launches run.  Without amdsmi, or if the GPU
+    cannot be matched to torch's device 0 by PCI address, it records nothing (fields None)."""
+
+    def __init__(self, torch):
+        self.handle = None
+        self.samples = []
+        self._stop = None
+        try:
+            import amdsmi
+            self.amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            props = torch.cuda.get_device_properties(0)
+            want = (int(props.pci_domain_id), int(props.pci_bus_id), int(props.pci_device_id))
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self.handle = h
+            if self.handle is None:
+                log(f"board sampler: no amdsmi GPU at PCI {want}; clock and power not recorded")
+        except Exception as e:  # amdsmi missing or not permitted: measure without it
+            log(f"board sampler unavailable ({type(e).__name__}: {e})")
+
+    def read(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and
+                0 < c < 10000]
+        pw = m.get("current_socket_power")
+        return (sum(clks) / len(clks) if clks else None,
+                float(pw) if isinstance(pw, (int, float)) and pw < 100000 else None)
+
+    def start(self):
+        import threading
+        self.samples = []
+        if self.handle is None:
+            return
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self.read())
+                except Exception:
+                    return
+                self._stop.wait(0.002)
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        """Stops sampling; returns {"clock_mhz", "power_w", "samples"} (means; None if none)."""
+        if self._stop is not None:
+            self._stop.set()
+            self._thread.join()
+            self._stop = None
+        clk = [c for c, _ in self.samples if c is not None]
+        pw = [p for _, p in self.samples if p is not None]
+        return {"clock_mhz": round(sum(clk) / len(clk), 1) if clk else None,
+                "power_w": round(sum(pw) / len(pw), 1) if pw else None,
+                "samples": len(self.samples)}
 
 
 def _read_counter_csv(path):
@@ -175,19 +244,14 @@ def run_flags(name, dg):
             "wide": dg.GEMM_FLAG_WIDE}[variant]
 
 
-def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
-    wl_name, mapping, group, sched, tile, out, workers = RUNS[name][:7]
-    bk = RUNS[name][7] if len(RUNS[name]) > 7 else 0
-    epi_spec = RUNS[name][9] if len(RUNS[name]) > 9 else {}
-    sk_groups = RUNS[name][10] if len(RUNS[name]) > 10 else 0
-    flags = run_flags(name, dg)
-    wl = gi.WORKLOADS[wl_name]
+def workload_operands(wl_name, torch, gi, cache):
+    """The workload's operands on the host (gemm_inputs) and resident in HBM, cached by name."""
     if wl_name not in cache:
+        import numpy as np
         t0 = time.time()
         op = gi.make_workload(wl_name)
         dev = torch.device("cuda:0")
         if op.dtype == "bf16":
-            import numpy as np
             A = torch.from_numpy(op.A.view(np.int16)).to(dev)
             B = torch.from_numpy(op.B.view(np.int16)).to(dev)
         else:
@@ -197,7 +261,21 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
         sb = torch.tensor([op.scale_b], dtype=torch.float32, device=dev)
         cache[wl_name] = (op, A, B, sa, sb)
         log(f"{wl_name}: inputs generated and resident in HBM ({time.time() - t0:.1f} s)")
-    op, A, B, sa, sb = cache[wl_name]
+    return cache[wl_name]
+
+
+def setup_run(name, torch, dg, gi, cache):
+    """The launch configuration of a RUNS entry, as the benchmark times it and the full-size
+    tests check it: the plan, the output and workspace buffers, and the fused epilogue's device
+    operands.  Returns a dict; run["launch"](stream) enqueues one GEMM (into run["C"], or into
+    the buffer given as out_buf)."""
+    wl_name, mapping, group, sched, tile, out, workers = RUNS[name][:7]
+    bk = RUNS[name][7] if len(RUNS[name]) > 7 else 0
+    epi_spec = RUNS[name][9] if len(RUNS[name]) > 9 else {}
+    sk_groups = RUNS[name][10] if len(RUNS[name]) > 10 else 0
+    flags = run_flags(name, dg)
+    wl = gi.WORKLOADS[wl_name]
+    op, A, B, sa, sb = workload_operands(wl_name, torch, gi, cache)
     epi = dg.ACTIVATIONS[epi_spec.get("act")]
     epi |= {None: 0, "row": dg.GEMM_EPI_BIAS_ROW, "col": dg.GEMM_EPI_BIAS_COL}[
         epi_spec.get("bias")]
@@ -213,11 +291,12 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
     ws = None
     if plan.workspace_bytes:
         ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=A.device)
-    bias = amax = scale_d = None
+    bias = amax = scale_d = bias_host = None
     bias_bytes = 0
     if epi_spec.get("bias"):
         n = op.M if epi_spec["bias"] == "row" else op.N
-        bias = torch.from_numpy(gi.make_vector(n, seed=wl.seed + 7)).to(A.device)
+        bias_host = gi.make_vector(n, seed=wl.seed + 7)
+        bias = torch.from_numpy(bias_host).to(A.device)
         bias_bytes = 4 * n
     if epi_spec.get("amax"):
         amax = torch.zeros(1, dtype=torch.float32, device=A.device)
@@ -225,10 +304,32 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
         # about 4 sqrt(K), mapped onto the format's 448
         scale_d = torch.tensor([4.0 * op.K ** 0.5 / 448.0], dtype=torch.float32,
                                device=A.device)
+
+    def launch(stream=None, out_buf=None):
+        plan.run(A, B, C if out_buf is None else out_buf, sa, sb, ws, stream, bias=bias,
+                 scale_d=scale_d, amax=amax)
+    return {"name": name, "workload": wl_name, "op": op, "plan": plan, "C": C, "ws": ws,
+            "out": out, "epi": epi_spec, "bias": bias, "bias_host": bias_host, "amax": amax,
+            "scale_d": scale_d, "bias_bytes": bias_bytes, "mapping": mapping, "sched": sched,
+            "launch": launch}
+
+
+def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0, batches=10, batch=50,
+             sampler=None):
+    """Times one RUNS entry.  Returns a dict with the contract's wall-clock figures over exactly
+    `steps` launches (ms_per_step, tflops) and the kernel time as the median of `batches`
+    event-timed batches of `batch` launches (kernel_us, kernel_tflops), with the shader clock
+    and socket power sampled during the batches."""
+    import statistics
+    run = setup_run(name, torch, dg, gi, cache)
+    op, plan, out, epi_spec = run["op"], run["plan"], run["out"], run["epi"]
+    wl_name, mapping, sched, bias_bytes = run["workload"], run["mapping"], run["sched"], \
+        run["bias_bytes"]
+    A = cache[wl_name][1]
     stream = torch.cuda.current_stream()
 
     def launch():
-        plan.run(A, B, C, sa, sb, ws, stream, bias=bias, scale_d=scale_d, amax=amax)
+        run["launch"](stream)
     # Warmup: at least `warmup` launches and at least `settle_ms` of back-to-back launches, so the
     # GPU's clock has left its ramp (it climbs for a few hundred ms under a sustained MFMA load).
     n_warm, t_w = 0, time.perf_counter()
@@ -239,16 +340,30 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
         torch.cuda.synchronize()
         if n_warm >= warmup and (time.perf_counter() - t_w) * 1e3 >= settle_ms:
             break
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    # The contract's timed region: exactly `steps` launches, synchronised on both sides.
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record(stream)
     for _ in range(steps):
         launch()
-    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dev_ms = e0.elapsed_time(e1) / steps
+    # The kernel time: `batches` batches of `batch` back-to-back launches, each bracketed by HIP
+    # events recorded on the launch stream; the median batch over its launch count.  Clock and
+    # power are sampled meanwhile.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(batches)]
+    if sampler is not None:
+        sampler.start()
+    for e0, e1 in ev:
+        e0.record(stream)
+        for _ in range(batch):
+            launch()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    board = sampler.stop() if sampler is not None else {"clock_mhz": None, "power_w": None,
+                                                         "samples": 0}
+    batch_us = sorted(e0.elapsed_time(e1) * 1e3 / batch for e0, e1 in ev)
+    dev_ms = statistics.median(batch_us) * 1e-3
     flops = 2.0 * op.M * op.N * op.K
     info = plan.info
     res = {
@@ -261,15 +376,25 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0):
         "dp_tiles": info.dp_tiles, "sk_tiles": info.sk_tiles, "warmup_launches": n_warm,
         "ms_per_step": wall * 1e3 / steps, "kernel_us": dev_ms * 1e3,
         "tflops": flops / (wall / steps) / 1e12, "kernel_tflops": flops / (dev_ms * 1e-3) / 1e12,
+        "batches": batches, "batch": batch,
+        "batch_us_min_median_max": [round(batch_us[0], 2), round(dev_ms * 1e3, 2),
+                                    round(batch_us[-1], 2)],
+        "clock_mhz": board["clock_mhz"], "power_w": board["power_w"],
+        "board_samples": board["samples"],
     }
     res["frac_of_peak"] = res["kernel_tflops"] / PEAK_TFLOPS[op.dtype]
+    # against the peak at the clock the chip held: CUs x FLOP/clk/CU x f_measured
+    res["frac_clock_adjusted"] = (res["frac_of_peak"] * PEAK_CLOCK_MHZ / board["clock_mhz"]
+                                  if board["clock_mhz"] else None)
     alg_bytes = (op.A.nbytes + op.B.nbytes + bias_bytes +
                  op.M * op.N * {"bf16": 2, "f32": 4, "e4m3": 1}[out])
     res["alg_bytes"] = alg_bytes
     res["hbm_gbs_alg"] = alg_bytes / (dev_ms * 1e-3) / 1e9
+    clk = (f", {board['clock_mhz']:.0f} MHz, {board['power_w']:.0f} W"
+           if board["clock_mhz"] and board["power_w"] else "")
     log(f"{name}: {res['kernel_us']:.1f} us/launch, {res['kernel_tflops']:.1f} TFLOP/s "
         f"({100 * res['frac_of_peak']:.1f}% of {PEAK_TFLOPS[op.dtype]:.0f}), grid {info.grid}, "
-        f"tile {info.bm}x{info.bn}x{info.bk}, {res['kernel']}")
+        f"tile {info.bm}x{info.bn}x{info.bk}, {res['kernel']}{clk}")
     return res
 
 
@@ -293,7 +418,14 @@ def cpu_baseline(gi, budget_s=12.0):
     tflops = 2.0 * rows * op.N * op.K / dt / 1e12
     log(f"cpu baseline: oracle on {rows} x {op.N} x {op.K} rows in {dt:.1f} s with {threads} "
         f"threads -> {tflops * 1e3:.2f} GFLOP/s")
-    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    host = os.cpu_count() or 0
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = host
+    log(f"cpu baseline: host has {host} cores ({usable} usable by this process; nproc)")
+    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "host_cores": host,
+            "host_cores_usable": usable, "kind": "oracle",
             "sample": f"rows 0..{rows - 1} of the bf16 4096^3 product (all 4096 columns, full K), "
                       f"fp64 sequential dot products, {dt:.1f} s"}
 
@@ -305,6 +437,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--settle-ms", type=float, default=500.0,
                     help="minimum duration of the untimed warmup per run (GPU clock settle)")
+    ap.add_argument("--batches", type=int, default=10,
+                    help="event-timed batches per run for the kernel time (median batch)")
+    ap.add_argument("--batch", type=int, default=50, help="launches per timed batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--only", default=None, help="time just this run (see RUNS)")
@@ -331,14 +466,18 @@ def main():
     dg.load()  # fails loudly if the HIP library is not built
 
     cache = {}
+    sampler = BoardSampler(torch)
+    timing = dict(batches=args.batches, batch=args.batch, sampler=sampler)
     if args.only:
-        res = time_run(args.only, args.steps, args.warmup, torch, dg, gi, cache, args.settle_ms)
+        res = time_run(args.only, args.steps, args.warmup, torch, dg, gi, cache, args.settle_ms,
+                       **timing)
         if args.copy_calib_mib:
             copy_calibration(torch, args.copy_calib_mib)
         print(json.dumps(res), flush=True)
         return
 
-    head = time_run("bf16_4096", args.steps, args.warmup, torch, dg, gi, cache, args.settle_ms)
+    head = time_run("bf16_4096", args.steps, args.warmup, torch, dg, gi, cache, args.settle_ms,
+                    **timing)
     secondary = {}
     if not args.no_secondary:
         for name in ("bf16_4096_pp", "bf16_4096_coop", "bf16_4096_linear", "bf16_4096_t128",
@@ -348,8 +487,10 @@ def main():
                      "bf16_streamk", "bf16_256"):
             steps = max(10, args.steps // (4 if name.startswith("fp8_8192") else 1))
             r = time_run(name, steps, max(2, args.warmup // 2), torch, dg, gi, cache,
-                         args.settle_ms / 2)
+                         args.settle_ms / 2, **timing)
             secondary[name] = {k: r[k] for k in ("kernel_us", "kernel_tflops", "frac_of_peak",
+                                                 "frac_clock_adjusted", "clock_mhz", "power_w",
+                                                 "batch_us_min_median_max",
                                                  "hbm_gbs_alg", "tile", "grid", "mapping",
                                                  "sched", "kernel", "out", "epilogue",
                                                  "group", "group_n")}
@@ -381,7 +522,15 @@ def main():
                    "settle_ms": args.settle_ms},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
-                     "traffic": measured_traffic("bf16_4096")},
+                     "traffic": measured_traffic("bf16_4096"),
+                     "kernel_us": round(head["kernel_us"], 2),
+                     "timing": f"median of {args.batches} batches of {args.batch} launches, HIP "
+                               "events on the launch stream",
+                     "clock_mhz": head["clock_mhz"], "power_w": head["power_w"],
+                     "peak_at_clock": (round(PEAK_TFLOPS["bf16"] * head["clock_mhz"] /
+                                             PEAK_CLOCK_MHZ, 1) if head["clock_mhz"] else None),
+                     "frac_clock_adjusted": (round(head["frac_clock_adjusted"], 4)
+                                             if head["frac_clock_adjusted"] else None)},
         "secondary": secondary,
     }
     if not args.no_cpu_baseline:

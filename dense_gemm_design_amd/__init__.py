@@ -34,11 +34,25 @@ def gemm(A, B, out_dtype="f32", scale_a=None, scale_b=None, mapping="grouped_m",
     Y / scale_d, scale_d a one-element float32 device tensor).  tile: 0 (the planner's), an int
     for square tiles, or (bm, bn), e.g. (256, 224).  sk_groups: Stream-K groups (0 = the
     planner's count, 1-8) of a plan with a Stream-K band.  Returns C (M, N): float32,
-    bfloat16, or uint8 e4m3 codes."""
+    bfloat16, or uint8 e4m3 codes.  Shapes, element types, contiguity and devices are checked
+    before anything is launched (ValueError)."""
     import torch
+    if not isinstance(A, torch.Tensor) or not isinstance(B, torch.Tensor):
+        raise ValueError("A and B must be torch tensors")
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError(f"A and B must be 2-D; got {tuple(A.shape)} and {tuple(B.shape)}")
     M, K = A.shape
     N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError(f"B must be (N, K) = (N, {K}), the K x N operand stored column-major; "
+                         f"got {tuple(B.shape)}")
     fp8 = A.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if fp8 != (B.dtype in (torch.uint8, torch.float8_e4m3fn)):
+        raise ValueError(f"A and B must both be bf16 or both e4m3; got {A.dtype} and {B.dtype}")
+    if out_dtype not in OUT_DTYPES:
+        raise ValueError(f"out_dtype must be one of {sorted(OUT_DTYPES)}")
+    if bias_row is not None and bias_col is not None:
+        raise ValueError("one bias at most (bias_row or bias_col)")
     epi = ACTIVATIONS[activation]
     epi |= GEMM_EPI_BIAS_ROW if bias_row is not None else 0
     epi |= GEMM_EPI_BIAS_COL if bias_col is not None else 0

@@ -205,11 +205,22 @@ class Plan:
         return load().gemm_run_ex(self.handle, A, B, C, scale_a or None, scale_b or None, epi,
                                   workspace or None, workspace_bytes, stream or None)
 
+    def validate(self, A, B, C, scale_a=None, scale_b=None, workspace=None, bias=None,
+                 scale_d=None, amax=None):
+        """Checks torch tensors against the plan before any pointer reaches the library: the
+        kernels size their buffer ranges from M, N, K, not from the tensors, so a tensor that is
+        too small, strided or of the wrong element type would be read or written past its end.
+        Raises ValueError naming the first problem; returns None."""
+        validate_operands(self.desc, A, B, C, scale_a, scale_b, workspace, bias, scale_d, amax,
+                          self.workspace_bytes)
+
     def run(self, A, B, C, scale_a=None, scale_b=None, workspace=None, stream=None, bias=None,
             scale_d=None, amax=None):
         """A, B, C, scales, workspace, bias, amax: torch tensors on the GPU; stream:
-        torch.cuda.Stream.  bias / scale_d / amax feed the fused epilogue (gemm_run_ex)."""
+        torch.cuda.Stream.  bias / scale_d / amax feed the fused epilogue (gemm_run_ex).  The
+        tensors are checked first (validate); a mismatch raises ValueError."""
         import torch
+        self.validate(A, B, C, scale_a, scale_b, workspace, bias, scale_d, amax)
         if stream is None:
             stream = torch.cuda.current_stream()
         ptr = lambda t: t.data_ptr() if t is not None else 0
@@ -217,3 +228,68 @@ class Plan:
         st = self.run_ex_raw(ptr(A), ptr(B), ptr(C), ptr(scale_a), ptr(scale_b), ptr(bias),
                              ptr(scale_d), ptr(amax), ptr(workspace), ws_len, stream.cuda_stream)
         _check(st, "gemm_run_ex")
+
+
+def _dtype_names(torch):
+    return {GEMM_BF16: (torch.bfloat16, torch.int16),
+            GEMM_FP8_E4M3: (torch.uint8, torch.float8_e4m3fn),
+            GEMM_F32: (torch.float32,)}
+
+
+def validate_operands(desc, A, B, C, scale_a=None, scale_b=None, workspace=None, bias=None,
+                      scale_d=None, amax=None, workspace_bytes=0):
+    """The checks of Plan.validate for a GemmDesc: shapes, element types and contiguity first
+    (so they can be exercised on CPU tensors), then that every tensor is on one GPU."""
+    import torch
+    M, N, K = desc.M, desc.N, desc.K
+    kinds = _dtype_names(torch)
+    used = []
+
+    def need(t, what, dtypes, numel=None, shape=None, at_least=False):
+        if t is None:
+            raise ValueError(f"{what} is required for this plan")
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{what} must be a torch tensor")
+        if t.dtype not in dtypes:
+            raise ValueError(f"{what} has dtype {t.dtype}; expected one of "
+                             f"{[str(d) for d in dtypes]}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{what} has shape {tuple(t.shape)}; expected {tuple(shape)}")
+        if numel is not None and (t.numel() < numel if at_least else t.numel() != numel):
+            raise ValueError(f"{what} has {t.numel()} elements; expected "
+                             f"{'at least ' if at_least else ''}{numel}")
+        if not t.is_contiguous():
+            raise ValueError(f"{what} must be contiguous (the library takes packed rows)")
+        used.append((what, t))
+
+    if M > 0 and N > 0:
+        if K > 0:
+            need(A, "A", kinds[desc.dtype_ab], shape=(M, K))
+            need(B, "B (the K x N operand stored as N rows of K)", kinds[desc.dtype_ab],
+                 shape=(N, K))
+        need(C, "C", kinds[desc.dtype_c], numel=M * N, at_least=True)
+        if desc.dtype_ab == GEMM_FP8_E4M3:
+            need(scale_a, "scale_a", (torch.float32,), numel=1)
+            need(scale_b, "scale_b", (torch.float32,), numel=1)
+        if desc.epilogue & (GEMM_EPI_BIAS_ROW | GEMM_EPI_BIAS_COL):
+            n = M if desc.epilogue & GEMM_EPI_BIAS_ROW else N
+            need(bias, "bias", (torch.float32,), numel=n)
+        if desc.dtype_c == GEMM_FP8_E4M3:
+            need(scale_d, "scale_d", (torch.float32,), numel=1)
+        if desc.epilogue & GEMM_EPI_AMAX:
+            need(amax, "amax", (torch.float32,), numel=1)
+        if workspace_bytes:
+            if workspace is None:
+                raise ValueError(f"this plan needs a workspace of {workspace_bytes} bytes")
+            if not workspace.is_contiguous():
+                raise ValueError("workspace must be contiguous")
+            have = workspace.numel() * workspace.element_size()
+            if have < workspace_bytes:
+                raise ValueError(f"workspace has {have} bytes; the plan needs {workspace_bytes}")
+            used.append(("workspace", workspace))
+    devices = {(t.device.type, t.device.index) for _, t in used}
+    for what, t in used:
+        if t.device.type != "cuda":
+            raise ValueError(f"{what} is on {t.device}; every operand must be on the GPU")
+    if len(devices) > 1:
+        raise ValueError(f"operands are on different devices: {sorted(devices)}")

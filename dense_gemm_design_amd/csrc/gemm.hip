@@ -573,10 +573,11 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     streamk_plan(tiles, workers, dp, sk);
     sched = sk > 0 ? GEMM_SCHED_STREAMK : GEMM_SCHED_PERSISTENT;
   }
-  // Data-parallel work on 256 x 256 tiles runs on the wide-wave kernel unless a kernel is asked
-  // for (all of them hold one workgroup per CU, so the worker count stays); so does Stream-K work
-  // on 256 x 256 tiles, unless it needs the lock chain (checked below, once the band is known).
-  if (force_kind < 0 && d.K > 0 && (sched == GEMM_SCHED_STATIC || sched == GEMM_SCHED_PERSISTENT)) {
+  // Data-parallel work runs on the wide-wave kernel unless a kernel is asked for, or the cost
+  // model picked another one (its grid was sized for that kernel above); so does Stream-K work,
+  // unless it needs the lock chain (checked below, once the band is known).
+  if (force_kind < 0 && d.K > 0 && (sched == GEMM_SCHED_STATIC || sched == GEMM_SCHED_PERSISTENT) &&
+      (model_kind < 0 || model_kind == KIND_WIDE)) {
     if (by_kind[KIND_WIDE])
       k = by_kind[KIND_WIDE];
     else if (by_kind[KIND_PP] && !fused)

@@ -2184,7 +2184,13 @@ gemm_kernel_wide1(KernelArgs args) {
     const int swz = (r >> CFG::SWZ) & (CFG::CH - 1);
 #pragma unroll
     for (int h = 0; h < CFG::CPL; ++h) {
-      const int chunk = (lane / CFG::MI) * CFG::CPL + h;
+      // The lane's two 16-byte chunks of a 128-byte row are kq and kq + 4 (kq = lane / 16), not
+      // 2 kq and 2 kq + 1: then each ds_read_b128 (one h) reads the same set of rows and chunks
+      // as the bf16 kernel's read of one sub-step, which counts no LDS bank conflicts, where the
+      // adjacent-pair order counted one extra 4-cycle pass per read (SQ_LDS_BANK_CONFLICT about
+      // half of SQ_LDS_IDX_ACTIVE).  A and B use the same lane-to-k map, so the MFMA still sums
+      // over all 128 k of the k-tile.
+      const int chunk = h * CFG::KG + lane / CFG::MI;
       const uint32_t in_row = (uint32_t)((chunk ^ swz) * 16);
       aoff[0][h] = (uint32_t)((wm * CFG::WM + r) * CFG::ROWB) + in_row;
       boff[0][h] = (uint32_t)(CFG::A_BYTES + (wn * CFG::WN + r) * CFG::ROWB) + in_row;

@@ -186,7 +186,13 @@ typedef struct gemm_plan_info {
 
 typedef struct gemm_plan *gemm_handle;
 
-/* Validates the description and builds a plan.  Supported in this version:
+/* Validates the description and builds a plan.  The description carries the per-problem inputs
+ * and knobs of the "DeepGEMM on SM90" page, section "Kernel Configuration Heuristic" (M, N, K,
+ * the operand type, layout / GEMM type, and the chosen BM, BN, BK, G, stages and scheduler);
+ * the plan records the tile grid of that section (Mt = ceil(M/BM), Nt = ceil(N/BN), one task per
+ * output tile) and, for Stream-K, the workspace layout of the "H100 Stream-K" lesson, section 6
+ * (The Lock).  The handle owns host memory only; it is freed by gemm_destroy.  On error *out is
+ * left unchanged and nothing is allocated.  Supported in this version:
  *   dtype_ab BF16 with tiles (bm, bn, bk) in {(256,256,64), (256,224,64), (128,128,64)},
  *   dtype_ab FP8_E4M3 with tiles in {(256,256,128), (256,224,128), (128,128,128)}; 256 x 224
  *   tiles run on the wide-wave kernel only (a plan that needs another kernel -- K = 0, the
@@ -198,12 +204,24 @@ typedef struct gemm_plan *gemm_handle;
  * Needs a visible GPU only when num_workers == 0 (it then queries the CU count). */
 int gemm_create(const gemm_desc *desc, gemm_handle *out);
 
-/* Device bytes the caller must pass to gemm_run as workspace (0 when none is needed). */
+/* Device bytes the caller must pass to gemm_run as workspace (0 when none is needed).  The
+ * workspace follows the "H100 Stream-K" lesson, section 6 (The Lock): the FP32 partial-tile
+ * buffer first, the per-tile int lock (or arrival counter) array right after it in the same
+ * allocation, then the device error word (and the trace, with GEMM_FLAG_TRACE); every lock is
+ * zero when the kernel starts, because gemm_run clears them on the stream before the launch.
+ * The caller owns and allocates it.  GEMM_ERR_INVALID_ARG for a NULL handle or pointer. */
 int gemm_workspace_bytes(gemm_handle h, size_t *bytes);
 
+/* Copies the plan as chosen (tile, grid, schedule counts, kernel, workspace layout) into *info,
+ * a caller-owned struct.  GEMM_ERR_INVALID_ARG for a NULL handle or pointer. */
 int gemm_plan_get(gemm_handle h, gemm_plan_info *info);
 
-/* Enqueues C = alpha * A x B on `stream`.  A: M x K row-major, B: K x N column-major, C: M x N
+/* Enqueues C = alpha * A x B on `stream`.  The call follows the stream-ordered, asynchronous
+ * model of the "DeepGEMM on SM90" page, CUDA programming-model section 1 (Host-Device
+ * Execution): returning means the work is submitted, not complete; work on one stream runs in
+ * order; the caller synchronises explicitly.  Its argument list has the shape of the library
+ * call of the "Multi GPU Part 2" lesson (Lesson 10), section 6.1: buffers, sizes and datatype
+ * (here fixed at gemm_create), the operation's operands, and the stream last.  A: M x K row-major, B: K x N column-major, C: M x N
  * row-major of dtype_c (A and B may be NULL when K == 0; nothing is needed when M or N is 0).  scale_a / scale_b: device pointers to one float each for FP8 (required),
  * ignored for BF16 (may be NULL).  workspace: device memory of at least gemm_workspace_bytes(),
  * 16-byte aligned; the library clears the parts it needs at the start of every run. */
@@ -229,10 +247,17 @@ int gemm_run_ex(gemm_handle h, const void *A, const void *B, void *C, const floa
                 const float *scale_b, const gemm_epilogue_args *epi, void *workspace,
                 size_t workspace_bytes, void *stream);
 
+/* Frees the handle's host memory.  Work already enqueued with it is unaffected (a launch holds
+ * its own copy of the arguments).  NULL is GEMM_ERR_INVALID_ARG. */
 int gemm_destroy(gemm_handle h);
 
-/* CPU replay of the plan's schedule: writes up to `cap` items (grouped by worker, each worker's
- * items in processing order) and the total count to *n_out.  Returns GEMM_ERR_CAPACITY (with
+/* CPU replay of the plan's schedule: the tasks of the tile mapping F(i) -> (m, n) ("DeepGEMM on
+ * SM90" page, mapping-family table), as the static / persistent assignment ("H100 Kernel Design"
+ * lesson, sections 9.2-10.2: worker p takes tasks p, p + P, ...) or the Stream-K split ("H100
+ * Stream-K" lesson, sections 2-5: equal iteration ranges per unit, cut at tile boundaries into
+ * first / middle / final splits) hands them out.  Runs on the host with the same code the
+ * kernels use; items is a caller-owned host array.  Writes up to `cap` items (grouped by worker,
+ * each worker's items in processing order) and the total count to *n_out.  Returns GEMM_ERR_CAPACITY (with
  * *n_out set) when cap is too small. */
 int gemm_schedule_enumerate(gemm_handle h, gemm_work_item *items, size_t cap, size_t *n_out);
 
@@ -270,7 +295,9 @@ typedef struct gemm_config_score {
  * when num_workers == 0. */
 int gemm_rank_configs(const gemm_desc *desc, gemm_config_score *items, size_t cap, size_t *n_out);
 
-/* Static string for a gemm_status value. */
+/* Static string for a gemm_status value (never NULL; unknown values give "unknown status").
+ * The status codes are this library's own: the pages define no error interface; every call
+ * reports through them instead of printing or aborting. */
 const char *gemm_status_string(int status);
 
 #ifdef __cplusplus

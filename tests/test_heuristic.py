@@ -162,12 +162,13 @@ def test_pick_is_close_to_the_fastest_candidate(shape, dt, out):
     gen = torch.Generator(device=dev)
     gen.manual_seed(1)
     if dt == L.GEMM_BF16:
-        A = (torch.rand(M * K, device=dev, generator=gen) * 2 - 1).to(torch.bfloat16)
-        B = (torch.rand(N * K, device=dev, generator=gen) * 2 - 1).to(torch.bfloat16)
+        A = (torch.rand((M, K), device=dev, generator=gen) * 2 - 1).to(torch.bfloat16)
+        B = (torch.rand((N, K), device=dev, generator=gen) * 2 - 1).to(torch.bfloat16)
     else:
-        A = torch.randn(M * K, device=dev, generator=gen).to(torch.float8_e4m3fn).view(torch.uint8)
-        B = torch.randn(N * K, device=dev, generator=gen).to(torch.float8_e4m3fn).view(torch.uint8)
-    C = torch.empty(M * N * (2 if out == L.GEMM_BF16 else 4), dtype=torch.uint8, device=dev)
+        A = torch.randn((M, K), device=dev, generator=gen).to(torch.float8_e4m3fn).view(torch.uint8)
+        B = torch.randn((N, K), device=dev, generator=gen).to(torch.float8_e4m3fn).view(torch.uint8)
+    C = torch.empty((M, N), dtype=torch.bfloat16 if out == L.GEMM_BF16 else torch.float32,
+                    device=dev)
     sa = torch.ones(1, dtype=torch.float32, device=dev)
     d = L.make_desc(M, N, K, dt, out, L.GEMM_MAP_GROUPED_M, 0, L.GEMM_SCHED_AUTO, 0)
     ranked = L.rank_configs(d)
