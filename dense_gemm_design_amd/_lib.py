@@ -14,6 +14,8 @@ LIB_PATH = os.path.join(_HERE, "libdgemm.so")
 # enums (gemm.h)
 GEMM_OK, GEMM_ERR_INVALID_ARG, GEMM_ERR_UNSUPPORTED = 0, -1, -2
 GEMM_ERR_ALIGNMENT, GEMM_ERR_WORKSPACE, GEMM_ERR_HIP, GEMM_ERR_CAPACITY = -3, -4, -5, -6
+GEMM_ERR_SCRATCH_LIMIT = -7
+GEMM_NOALLOC_SCRATCH_BYTES = 32 << 20
 GEMM_BF16, GEMM_FP8_E4M3, GEMM_F32 = 0, 1, 2
 GEMM_ROW_MAJOR, GEMM_COL_MAJOR = 0, 1
 GEMM_MAP_LINEAR_N, GEMM_MAP_LINEAR_M, GEMM_MAP_GROUPED_M, GEMM_MAP_GROUPED_N = 0, 1, 2, 3
@@ -36,7 +38,7 @@ GEMM_EPI_SILU = 0x10
 GEMM_EPI_AMAX = 0x20
 
 EXPORTS = ("gemm_create", "gemm_workspace_bytes", "gemm_plan_get", "gemm_run", "gemm_run_ex",
-           "gemm_destroy", "gemm_schedule_enumerate", "gemm_rank_configs", "gemm_status_string")
+           "gemm_run_noalloc", "gemm_destroy", "gemm_schedule_enumerate", "gemm_rank_configs", "gemm_status_string")
 
 
 class GemmDesc(ctypes.Structure):
@@ -101,6 +103,8 @@ def load():
     lib.gemm_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gemm_run_ex.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(GemmEpilogueArgs), vp, sz,
                                 vp]
+    lib.gemm_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(GemmEpilogueArgs),
+                                     vp]
     lib.gemm_destroy.argtypes = [vp]
     lib.gemm_schedule_enumerate.argtypes = [vp, ctypes.POINTER(GemmWorkItem), sz,
                                             ctypes.POINTER(sz)]
@@ -213,6 +217,27 @@ class Plan:
         Raises ValueError naming the first problem; returns None."""
         validate_operands(self.desc, A, B, C, scale_a, scale_b, workspace, bias, scale_d, amax,
                           self.workspace_bytes)
+
+    def run_noalloc_raw(self, A, B, C, scale_a=0, scale_b=0, bias=0, scale_d=0, amax=0,
+                        stream=0, epi_null=False):
+        """gemm_run_noalloc with raw integer device pointers; returns the gemm_status."""
+        epi = None if epi_null else ctypes.byref(
+            GemmEpilogueArgs(bias or None, scale_d or None, amax or None))
+        return load().gemm_run_noalloc(self.handle, A, B, C, scale_a or None, scale_b or None,
+                                       epi, stream or None)
+
+    def run_noalloc(self, A, B, C, scale_a=None, scale_b=None, stream=None, bias=None,
+                    scale_d=None, amax=None):
+        """gemm_run_noalloc on torch tensors: as run(), with the library's own scratch as the
+        workspace (nothing is allocated).  The tensors are checked first (ValueError)."""
+        import torch
+        validate_operands(self.desc, A, B, C, scale_a, scale_b, None, bias, scale_d, amax, 0)
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        ptr = lambda t: t.data_ptr() if t is not None else 0
+        st = self.run_noalloc_raw(ptr(A), ptr(B), ptr(C), ptr(scale_a), ptr(scale_b), ptr(bias),
+                                  ptr(scale_d), ptr(amax), stream.cuda_stream)
+        _check(st, "gemm_run_noalloc")
 
     def run(self, A, B, C, scale_a=None, scale_b=None, workspace=None, stream=None, bias=None,
             scale_d=None, amax=None):

@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "../../include/gemm.h"
@@ -445,6 +446,32 @@ struct gemm_plan {
   int64_t partial_off, lock_off, error_off, trace_off, ws_bytes;
 };
 
+// Workspace of gemm_run_noalloc: one array per GPU, allocated when the code object is loaded on
+// that GPU and held until the process ends.  In host code `scratch` names a host-side stand-in
+// for the symbol, not a device address: the kernels get the address hipGetSymbolAddress reports
+// for the current device, looked up once per device and kept in scratch_addr.
+static __device__ __align__(256) char scratch[GEMM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_addr[kMaxDevices];
+
+int scratch_of_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GEMM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GEMM_ERR_HIP;
+    scratch_addr[dev] = p;
+  }
+  *out = scratch_addr[dev];
+  return GEMM_OK;
+}
+}  // namespace
+
 extern "C" {
 
 const char *gemm_status_string(int status) {
@@ -456,6 +483,8 @@ const char *gemm_status_string(int status) {
     case GEMM_ERR_WORKSPACE: return "workspace missing or too small";
     case GEMM_ERR_HIP: return "HIP runtime error";
     case GEMM_ERR_CAPACITY: return "output buffer too small";
+    case GEMM_ERR_SCRATCH_LIMIT:
+      return "plan needs more workspace than the no-allocation entry point's scratch holds";
     default: return "unknown status";
   }
 }
@@ -808,6 +837,18 @@ int gemm_run_ex(gemm_handle h, const void *A, const void *B, void *C, const floa
   const bool ragged_k = h->d.K % h->k->bk != 0;
   if (h->k->launch(a, h->info.grid, ragged_k, s) != hipSuccess) return GEMM_ERR_HIP;
   return GEMM_OK;
+}
+
+int gemm_run_noalloc(gemm_handle h, const void *A, const void *B, void *C, const float *scale_a,
+                     const float *scale_b, const gemm_epilogue_args *epi, void *stream) {
+  if (!h) return GEMM_ERR_INVALID_ARG;
+  if (h->ws_bytes > (int64_t)GEMM_NOALLOC_SCRATCH_BYTES) return GEMM_ERR_SCRATCH_LIMIT;
+  void *ws = nullptr;
+  if (h->ws_bytes > 0 && h->info.grid > 0) {
+    const int st = scratch_of_current_device(&ws);
+    if (st != GEMM_OK) return st;
+  }
+  return gemm_run_ex(h, A, B, C, scale_a, scale_b, epi, ws, ws ? (size_t)h->ws_bytes : 0, stream);
 }
 
 int gemm_destroy(gemm_handle h) {

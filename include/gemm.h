@@ -41,7 +41,8 @@ typedef enum {
   GEMM_ERR_ALIGNMENT = -3,    /* a device pointer is misaligned (16 bytes; 4 for one float)   */
   GEMM_ERR_WORKSPACE = -4,    /* workspace missing or smaller than gemm_workspace_bytes()     */
   GEMM_ERR_HIP = -5,          /* a HIP runtime call failed (no device, launch failure ...)    */
-  GEMM_ERR_CAPACITY = -6      /* a buffer passed to the library is too small for the result   */
+  GEMM_ERR_CAPACITY = -6,     /* a buffer passed to the library is too small for the result   */
+  GEMM_ERR_SCRATCH_LIMIT = -7 /* gemm_run_noalloc: the plan's workspace exceeds the scratch   */
 } gemm_status;
 
 typedef enum { GEMM_BF16 = 0, GEMM_FP8_E4M3 = 1, GEMM_F32 = 2 } gemm_dtype;
@@ -249,6 +250,26 @@ int gemm_run_ex(gemm_handle h, const void *A, const void *B, void *C, const floa
 
 /* Frees the handle's host memory.  Work already enqueued with it is unaffected (a launch holds
  * its own copy of the arguments).  NULL is GEMM_ERR_INVALID_ARG. */
+/* Size of the scratch array gemm_run_noalloc uses as workspace, in bytes (per GPU). */
+#define GEMM_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* gemm_run_ex for callers that cannot allocate device memory -- code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation: the workspace is a file-scope device
+ * array of GEMM_NOALLOC_SCRATCH_BYTES inside the library (one per GPU, allocated when the library's
+ * code is loaded on that GPU and held until the process ends), so the call allocates nothing and
+ * takes no workspace argument.  The caller still passes A, B, C, the scales and the epilogue
+ * operands, as for gemm_run_ex, with the same checks and errors; the work is enqueued on `stream`,
+ * which must belong to the current device (the scratch used is the current device's).  A plan
+ * whose gemm_workspace_bytes() exceeds GEMM_NOALLOC_SCRATCH_BYTES returns GEMM_ERR_SCRATCH_LIMIT
+ * before anything else happens (the largest Stream-K plans; 512 x 512 x 65536 on 256 workgroups
+ * needs 17 MiB).  The parts of the scratch that must start at zero (the Stream-K locks and
+ * counters, the error word) are cleared on the stream at the start of every call, with a fill
+ * kernel.  Within a process, every call on one GPU shares that GPU's array and finds the previous
+ * call's contents: calls that overlap in time on one GPU (from different streams or threads) race
+ * on it, so the caller orders them. */
+int gemm_run_noalloc(gemm_handle h, const void *A, const void *B, void *C, const float *scale_a,
+                     const float *scale_b, const gemm_epilogue_args *epi, void *stream);
+
 int gemm_destroy(gemm_handle h);
 
 /* CPU replay of the plan's schedule: the tasks of the tile mapping F(i) -> (m, n) ("DeepGEMM on

@@ -53,7 +53,7 @@ def test_struct_layouts_match_c_compiler(tmp_path):
 
 def test_status_strings():
     lib = L.load()
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert lib.gemm_status_string(st).decode() not in ("", "unknown status")
     assert lib.gemm_status_string(12345).decode() == "unknown status"
 
@@ -296,3 +296,17 @@ def test_tile_256x224_plans():
     assert status(1024, flags=L.GEMM_FLAG_PINGPONG)[0] == L.GEMM_ERR_UNSUPPORTED
     assert status(16384, sched=L.GEMM_SCHED_STREAMK,
                   flags=L.GEMM_FLAG_STREAMK_CHAIN)[0] == L.GEMM_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects_plans_beyond_the_scratch_before_any_device_call():
+    """A Stream-K plan whose workspace exceeds the no-allocation entry point's scratch returns
+    GEMM_ERR_SCRATCH_LIMIT at once (no GPU is needed to reach that answer)."""
+    plan = L.Plan(L.make_desc(1024, 1024, 65536, L.GEMM_BF16, L.GEMM_F32, L.GEMM_MAP_LINEAR_N,
+                              1, L.GEMM_SCHED_STREAMK, 1024, 128, 128))
+    assert plan.workspace_bytes > L.GEMM_NOALLOC_SCRATCH_BYTES
+    st = plan.run_noalloc_raw(16, 16, 16)
+    assert st == L.GEMM_ERR_SCRATCH_LIMIT
+    assert "scratch" in L.load().gemm_status_string(st).decode()
+    assert plan.run_noalloc_raw(16, 16, 16, epi_null=True) == L.GEMM_ERR_SCRATCH_LIMIT
+    assert L.load().gemm_run_noalloc(None, None, None, None, None, None, None, None) == \
+        L.GEMM_ERR_INVALID_ARG
