@@ -54,9 +54,15 @@ PEAK_CLOCK_MHZ = 2400.0  # the engine clock the published MFMA peaks assume
 
 
 class BoardSampler:
-    """Samples the GPU's shader clock (mean over its XCDs) and socket power through the amdsmi
-    library in a background thread while the timed launches run.  Without amdsmi, or if the GPU
-    cannot be matched to torch's device 0 by PCI address, it records nothing (fields None)."""
+    """Reads the GPU's shader clock (mean over its XCDs), socket power and energy counter through
+    the amdsmi library in a background thread.  The board's metrics table behind these values is
+    refreshed about once a second (its timestamp and the energy counter step together), so only
+    refreshes that happen while the kernel under test runs back to back tell anything: a run
+    keeps its kernel busy for over a second after the clock ramp, and stop() uses the tables
+    first seen from then on -- the clock as their mean, the power as the energy counter's
+    increase between the first and last of them over their timestamps (or the table's own power
+    reading when only one refresh fell in the window).  Without amdsmi, or if the GPU cannot be
+    matched to torch's device 0 by PCI address, it records nothing (fields None)."""
 
     def __init__(self, torch):
         self.handle = None
@@ -79,12 +85,17 @@ class BoardSampler:
             log(f"board sampler unavailable ({type(e).__name__}: {e})")
 
     def read(self):
+        """(host time s, table timestamp ns, mean shader clock MHz over the XCDs, socket power
+        W, energy J)."""
         m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        e = self.amdsmi.amdsmi_get_energy_count(self.handle)
         clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and
                 0 < c < 10000]
         pw = m.get("current_socket_power")
-        return (sum(clks) / len(clks) if clks else None,
-                float(pw) if isinstance(pw, (int, float)) and pw < 100000 else None)
+        return (time.perf_counter(), int(e["timestamp"]),
+                sum(clks) / len(clks) if clks else None,
+                float(pw) if isinstance(pw, (int, float)) and pw < 100000 else None,
+                e["energy_accumulator"] * e["counter_resolution"] * 1e-6)
 
     def start(self):
         import threading
@@ -99,21 +110,34 @@ class BoardSampler:
                     self.samples.append(self.read())
                 except Exception:
                     return
-                self._stop.wait(0.002)
+                self._stop.wait(0.01)
         self._thread = threading.Thread(target=loop, daemon=True)
         self._thread.start()
 
-    def stop(self):
-        """Stops sampling; returns {"clock_mhz", "power_w", "samples"} (means; None if none)."""
+    def stop(self, since=0.0):
+        """Stops sampling; returns {"clock_mhz", "clock_mhz_min_max", "power_w", "refreshes"}
+        from the metrics tables first seen at or after host time `since`."""
         if self._stop is not None:
             self._stop.set()
             self._thread.join()
             self._stop = None
-        clk = [c for c, _ in self.samples if c is not None]
-        pw = [p for _, p in self.samples if p is not None]
+        seen, tables = set(), []
+        for t, ts, clk, pw, en in self.samples:
+            if ts in seen:
+                continue
+            seen.add(ts)
+            if t >= since:
+                tables.append((ts, clk, pw, en))
+        clk = [c for _, c, _, _ in tables if c is not None]
+        power = None
+        if len(tables) >= 2 and tables[-1][0] > tables[0][0]:
+            power = (tables[-1][3] - tables[0][3]) / ((tables[-1][0] - tables[0][0]) * 1e-9)
+        elif tables and tables[0][2] is not None:
+            power = tables[0][2]
         return {"clock_mhz": round(sum(clk) / len(clk), 1) if clk else None,
-                "power_w": round(sum(pw) / len(pw), 1) if pw else None,
-                "samples": len(self.samples)}
+                "clock_mhz_min_max": [min(clk), max(clk)] if clk else None,
+                "power_w": round(power, 1) if power else None,
+                "refreshes": len(tables)}
 
 
 def _read_counter_csv(path):
@@ -332,7 +356,10 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0, batches=1
         run["launch"](stream)
     # Warmup: at least `warmup` launches and at least `settle_ms` of back-to-back launches, so the
     # GPU's clock has left its ramp (it climbs for a few hundred ms under a sustained MFMA load).
+    if sampler is not None:
+        sampler.start()
     n_warm, t_w = 0, time.perf_counter()
+    since = t_w + min(0.4 * settle_ms * 1e-3, 0.4)  # past the clock's ramp
     while True:
         for _ in range(max(1, warmup) if n_warm == 0 else 50):
             launch()
@@ -352,16 +379,14 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0, batches=1
     # power are sampled meanwhile.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(batches)]
-    if sampler is not None:
-        sampler.start()
     for e0, e1 in ev:
         e0.record(stream)
         for _ in range(batch):
             launch()
         e1.record(stream)
     torch.cuda.synchronize()
-    board = sampler.stop() if sampler is not None else {"clock_mhz": None, "power_w": None,
-                                                         "samples": 0}
+    board = sampler.stop(since) if sampler is not None else {
+        "clock_mhz": None, "clock_mhz_min_max": None, "power_w": None, "refreshes": 0}
     batch_us = sorted(e0.elapsed_time(e1) * 1e3 / batch for e0, e1 in ev)
     dev_ms = statistics.median(batch_us) * 1e-3
     flops = 2.0 * op.M * op.N * op.K
@@ -379,8 +404,8 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0, batches=1
         "batches": batches, "batch": batch,
         "batch_us_min_median_max": [round(batch_us[0], 2), round(dev_ms * 1e3, 2),
                                     round(batch_us[-1], 2)],
-        "clock_mhz": board["clock_mhz"], "power_w": board["power_w"],
-        "board_samples": board["samples"],
+        "clock_mhz": board["clock_mhz"], "clock_mhz_min_max": board["clock_mhz_min_max"],
+        "power_w": board["power_w"], "board_refreshes": board["refreshes"],
     }
     res["frac_of_peak"] = res["kernel_tflops"] / PEAK_TFLOPS[op.dtype]
     # against the peak at the clock the chip held: CUs x FLOP/clk/CU x f_measured
@@ -399,7 +424,9 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0, batches=1
 
 
 def cpu_baseline(gi, budget_s=12.0):
-    """The oracle as it stands, timed on the host's cores on a row block of the 4096^3 workload."""
+    """The oracle as it stands, timed on the host's cores over the bf16 4096^3 workload: the
+    whole product (all rows) when it takes less than the budget, repeated until about
+    `budget_s` seconds of CPU work have run (a row block of it on a slower host)."""
     import numpy as np
     import oracle
     op = gi.make_workload("bf16_4096")
@@ -412,12 +439,15 @@ def cpu_baseline(gi, budget_s=12.0):
     rows = int(min(op.M, max(64, rows * budget_s / max(t_probe, 1e-3))))
     rows -= rows % 64 or 0
     rows = max(rows, 64)
-    t0 = time.perf_counter()
-    oracle.gemm_ref(rows, op.N, op.K, oracle.BF16, A[: rows * op.K], op.B, threads=threads)
-    dt = time.perf_counter() - t0
-    tflops = 2.0 * rows * op.N * op.K / dt / 1e12
-    log(f"cpu baseline: oracle on {rows} x {op.N} x {op.K} rows in {dt:.1f} s with {threads} "
-        f"threads -> {tflops * 1e3:.2f} GFLOP/s")
+    reps, dt = 0, 0.0
+    while dt < 0.8 * budget_s or reps == 0:
+        t0 = time.perf_counter()
+        oracle.gemm_ref(rows, op.N, op.K, oracle.BF16, A[: rows * op.K], op.B, threads=threads)
+        dt += time.perf_counter() - t0
+        reps += 1
+    tflops = 2.0 * rows * op.N * op.K * reps / dt / 1e12
+    log(f"cpu baseline: oracle on {rows} x {op.N} x {op.K}, {reps} times, in {dt:.1f} s with "
+        f"{threads} threads -> {tflops * 1e3:.2f} GFLOP/s")
     host = os.cpu_count() or 0
     try:
         usable = len(os.sched_getaffinity(0))
@@ -427,7 +457,7 @@ def cpu_baseline(gi, budget_s=12.0):
     return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "host_cores": host,
             "host_cores_usable": usable, "kind": "oracle",
             "sample": f"rows 0..{rows - 1} of the bf16 4096^3 product (all 4096 columns, full K), "
-                      f"fp64 sequential dot products, {dt:.1f} s"}
+                      f"{reps} times, fp64 sequential dot products, {dt:.1f} s"}
 
 
 def main():
@@ -435,8 +465,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--settle-ms", type=float, default=500.0,
-                    help="minimum duration of the untimed warmup per run (GPU clock settle)")
+    ap.add_argument("--settle-ms", type=float, default=1500.0,
+                    help="minimum duration of the untimed warmup per run: the GPU clock settles "
+                         "and the board's metrics table (refreshed about once a second) is read "
+                         "under load")
     ap.add_argument("--batches", type=int, default=10,
                     help="event-timed batches per run for the kernel time (median batch)")
     ap.add_argument("--batch", type=int, default=50, help="launches per timed batch")
@@ -487,7 +519,7 @@ def main():
                      "bf16_streamk", "bf16_256"):
             steps = max(10, args.steps // (4 if name.startswith("fp8_8192") else 1))
             r = time_run(name, steps, max(2, args.warmup // 2), torch, dg, gi, cache,
-                         args.settle_ms / 2, **timing)
+                         args.settle_ms, **timing)
             secondary[name] = {k: r[k] for k in ("kernel_us", "kernel_tflops", "frac_of_peak",
                                                  "frac_clock_adjusted", "clock_mhz", "power_w",
                                                  "batch_us_min_median_max",

@@ -95,6 +95,10 @@ def load():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run dense_gemm_design_amd/build.py "
                            "(or __graft_entry__.build())")
+    # PyTorch-ROCm carries its own HIP runtime; importing torch first makes the library bind to
+    # that same runtime, so torch's device pointers and streams are valid in it (loading the
+    # library first would bring in a second runtime, in which torch's allocations do not exist).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     lib.gemm_create.argtypes = [ctypes.POINTER(GemmDesc), ctypes.POINTER(vp)]
