@@ -221,8 +221,8 @@ def measured_traffic(workload):
 
 # name, workload key, mapping, group, sched, tile, out, workers[, bk[, variant[, epilogue[,
 # Stream-K groups]]]]
-# variant: "chain" = Stream-K lock-chain fixup; "coop" / "pp" / "vs" / "wide" = the cooperative /
-# ping-pong / register-staged / wide-wave kernel instead of the default for data-parallel
+# variant: "chain" = Stream-K lock-chain fixup; "coop" / "pp" / "wide" = the cooperative /
+# ping-pong / wide-wave kernel instead of the default for data-parallel
 # 256 x 256 tiles (the wide-wave kernel).  epilogue: the fused operations, {"bias": "row" |
 # "col", "act": "relu" | "gelu" | "silu", "amax": True}; out "e4m3" quantises the output.
 # Stream-K groups: 0 / 1 = one pool of units over the band, up to 8.
@@ -233,8 +233,6 @@ RUNS = {
     "bf16_4096_t128": ("bf16_4096", "grouped_m", 8, "persistent", 128, "bf16", 0),
     "fp8_8192": ("fp8_8192", "grouped_m", 16, "persistent", 0, "bf16", 0),
     "fp8_8192_coop": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "coop"),
-    "bf16_4096_vs": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "vs"),
-    "fp8_8192_vs": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "vs"),
     "bf16_4096_pp": ("bf16_4096", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "pp"),
     "fp8_8192_pp": ("fp8_8192", "grouped_m", 16, "persistent", 256, "bf16", 0, 0, "pp"),
     "bf16_mlp_up_pp": ("bf16_mlp_up", "grouped_m", 8, "persistent", 256, "bf16", 0, 0, "pp"),
@@ -264,7 +262,7 @@ def run_flags(name, dg):
     """GEMM_FLAG_* bits of a RUNS entry's variant."""
     variant = RUNS[name][8] if len(RUNS[name]) > 8 else ""
     return {"": 0, "chain": dg.GEMM_FLAG_STREAMK_CHAIN, "pp": dg.GEMM_FLAG_PINGPONG,
-            "coop": dg.GEMM_FLAG_COOPERATIVE, "vs": dg.GEMM_FLAG_REGSTAGED,
+            "coop": dg.GEMM_FLAG_COOPERATIVE,
             "wide": dg.GEMM_FLAG_WIDE}[variant]
 
 
@@ -394,7 +392,7 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0, batches=1
     res = {
         "workload": wl_name, "M": op.M, "N": op.N, "K": op.K, "dtype": op.dtype, "out": out,
         "tile": [info.bm, info.bn, info.bk], "stages": info.stages, "mapping": mapping,
-        "kernel": ["cooperative", "ping-pong", "register-staged", "wide-wave"][info.kernel],
+        "kernel": dg.KERNEL_NAMES[info.kernel],
         "group": info.group, "group_n": info.group_n, "sched": sched, "grid": info.grid,
         "sk_groups": info.sk_groups,
         "epilogue": epi_spec,

@@ -10,10 +10,11 @@ from ._lib import (GemmDesc, GemmError, Plan, make_desc, load,  # noqa: F401
                    GEMM_SCHED_STATIC,
                    GEMM_SCHED_PERSISTENT, GEMM_SCHED_STREAMK, GEMM_SCHED_AUTO, GEMM_FLAG_TRACE,
                    GEMM_FLAG_NO_XCD_REMAP, GEMM_FLAG_STREAMK_CHAIN, GEMM_FLAG_PINGPONG,
-                   GEMM_FLAG_COOPERATIVE, GEMM_FLAG_REGSTAGED, GEMM_FLAG_WIDE,
+                   GEMM_FLAG_COOPERATIVE, GEMM_FLAG_WIDE,
                    GEMM_EPI_BIAS_ROW, GEMM_EPI_BIAS_COL, GEMM_EPI_RELU, GEMM_EPI_GELU,
                    GEMM_EPI_SILU, GEMM_EPI_AMAX, GemmEpilogueArgs)
 
+KERNEL_NAMES = {0: "cooperative", 1: "ping-pong", 3: "wide-wave"}  # gemm_plan_info.kernel
 MAPPINGS = {"linear_n": GEMM_MAP_LINEAR_N, "linear_m": GEMM_MAP_LINEAR_M,
             "grouped_m": GEMM_MAP_GROUPED_M, "grouped_n": GEMM_MAP_GROUPED_N,
             "blocked": GEMM_MAP_BLOCKED, "morton": GEMM_MAP_MORTON}

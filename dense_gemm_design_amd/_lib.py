@@ -26,7 +26,6 @@ GEMM_FLAG_NO_XCD_REMAP = 0x2
 GEMM_FLAG_STREAMK_CHAIN = 0x4
 GEMM_FLAG_PINGPONG = 0x8
 GEMM_FLAG_COOPERATIVE = 0x10
-GEMM_FLAG_REGSTAGED = 0x20
 GEMM_FLAG_WIDE = 0x40
 GEMM_FLAG_TEST_SKIP_PUBLISH = 0x100
 GEMM_DEVICE_OK, GEMM_DEVICE_ERR_SPIN = 0, 1
@@ -72,7 +71,8 @@ class GemmPlanInfo(ctypes.Structure):
                 ("trace_capacity", ctypes.c_int32), ("error_offset", ctypes.c_int32),
                 ("streamk_mode", ctypes.c_int32), ("kernel", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("group_n", ctypes.c_int32),
-                ("sk_groups", ctypes.c_int32)]
+                ("sk_groups", ctypes.c_int32), ("xcd_box_r", ctypes.c_int32),
+                ("xcd_box_c", ctypes.c_int32)]
 
 
 class GemmConfigScore(ctypes.Structure):

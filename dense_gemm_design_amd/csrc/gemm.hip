@@ -33,8 +33,6 @@ using CfgBf16_256pp = TileCfg<DT_BF16, 256, 256, 64, 2, 4, 2, 1>;
 using CfgBf16_256 = TileCfg<DT_BF16, 256, 256, 64, 2, 4, 2, 1>;
 using CfgBf16_128 = TileCfg<DT_BF16, 128, 128, 64, 2, 2, 2, 1>;
 using CfgFp8_256pp = TileCfg<DT_FP8, 256, 256, 128, 2, 4, 2, 1>;
-using CfgBf16_256vs = TileCfg<DT_BF16, 256, 256, 64, 2, 2, 2, 1>;
-using CfgFp8_256vs = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1>;
 using CfgFp8_256 = TileCfg<DT_FP8, 256, 256, 128, 2, 4, 2, 1>;
 using CfgFp8_128 = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 2, 1>;
 // The wide-wave kernel (GEMM_FLAG_WIDE): four waves of 128 x 128, two stages of 64 KiB.
@@ -90,19 +88,6 @@ template <class CFG>
 const void *kernel_of_pp() {
   return (const void *)&gemm_kernel_pp<CFG, false>;
 }
-template <class CFG>
-hipError_t launch_vs(const KernelArgs &a, int grid, bool ragged_k, hipStream_t s) {
-  if (ragged_k)
-    hipLaunchKernelGGL((gemm_kernel_vs<CFG, true>), dim3(grid), dim3(CFG::THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL((gemm_kernel_vs<CFG, false>), dim3(grid), dim3(CFG::THREADS), 0, s, a);
-  return hipGetLastError();
-}
-template <class CFG>
-const void *kernel_of_vs() {
-  return (const void *)&gemm_kernel_vs<CFG, false>;
-}
-
 // k-tiles one MFMA deep (e4m3 16 x 16 x 128) take the single-A-buffer form of the schedule
 template <class CFG, bool RAGGED_K, int FUSE = FUSE_OFF>
 constexpr auto wide_kernel() {
@@ -144,7 +129,8 @@ const void *kernel_of_wide() {
 
 // kind: KIND_COOP runs every plan; the others run data-parallel work only (no Stream-K splits,
 // K > 0)
-enum { KIND_COOP = 0, KIND_PP = 1, KIND_VS = 2, KIND_WIDE = 3, KIND_COUNT = 4 };
+// (value 2 belonged to a register-staged kernel that is no longer built)
+enum { KIND_COOP = 0, KIND_PP = 1, KIND_WIDE = 3, KIND_COUNT = 4 };
 struct KernelEntry {
   int dt, bm, bn, bk, threads, stages, lds, kind;
   launch_fn launch;
@@ -162,11 +148,6 @@ constexpr KernelEntry entry_pp() {
                      pp_lds_bytes<CFG>(), KIND_PP, &launch_pp<CFG>, &kernel_of_pp<CFG>};
 }
 template <class CFG>
-constexpr KernelEntry entry_vs() {
-  return KernelEntry{CFG::DT, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::STAGES,
-                     CFG::LDS_BYTES, KIND_VS, &launch_vs<CFG>, &kernel_of_vs<CFG>};
-}
-template <class CFG>
 constexpr KernelEntry entry_wide() {
   return KernelEntry{CFG::DT, CFG::BM, CFG::BN, CFG::BK, CFG::THREADS, CFG::STAGES,
                      wide_lds_bytes<CFG>(), KIND_WIDE, &launch_wide<CFG>, &kernel_of_wide<CFG>};
@@ -179,8 +160,6 @@ const KernelEntry kKernels[] = {
     entry<CfgBf16_128>(),
     entry<CfgFp8_256>(),
     entry_pp<CfgFp8_256pp>(),
-    entry_vs<CfgBf16_256vs>(),
-    entry_vs<CfgFp8_256vs>(),
     entry_wide<CfgBf16_256w>(),
     entry_wide<CfgFp8_256w>(),
     entry_wide<CfgBf16_128w>(),
@@ -301,6 +280,36 @@ int choose_group(int mapping, int64_t Mt, int64_t Nt, int64_t chunk) {
 // Box of the blocked mapping for the same `chunk` tiles: H x W = chunk tile rows x columns (a
 // given H or W kept, the other one derived), reading H + W operand strips per k-step.  The
 // fewest strips win, the wider box on a tie.
+// XCD box remap of a grouped mapping (sched.h, xcd_box_task): used when every data-parallel wave
+// of P tasks is a whole G x (P/G) block of one strip (all strips full, strip length a multiple
+// of P) and an r x c box per XCD (r | G, c | P/G, r c = P/X, r + c smallest, the taller box on a
+// tie) needs fewer operand strips than the contiguous runs of P/X tasks do.
+void choose_xcd_box(SchedParams &sp) {
+  sp.xbox_r = sp.xbox_c = 0;
+  const int32_t X = sp.X, P = sp.P, G = sp.G;
+  if (sp.mapping != MAP_GROUPED_M && sp.mapping != MAP_GROUPED_N) return;
+  if (X <= 1 || P < X || P % X != 0 || G < 1 || P % G != 0) return;
+  const int32_t across = sp.mapping == MAP_GROUPED_M ? sp.Mt : sp.Nt;
+  const int32_t along = sp.mapping == MAP_GROUPED_M ? sp.Nt : sp.Mt;
+  if (across % G != 0 || ((int64_t)G * along) % P != 0) return;
+  const int32_t per = P / X, len = P / G;
+  int32_t best_r = 0, best_c = 0;
+  for (int32_t r = G; r >= 1; --r) {
+    if (G % r != 0 || per % r != 0 || len % (per / r) != 0) continue;
+    const int32_t c = per / r;
+    if (best_r == 0 || r + c < best_r + best_c) {
+      best_r = r;
+      best_c = c;
+    }
+  }
+  // a contiguous run of `per` tasks is a G x per/G slab (or a per x 1 column when G > per)
+  const int32_t contiguous = per % G == 0 ? G + per / G : (G % per == 0 ? per + 1 : INT32_MAX);
+  if (best_r > 0 && best_r + best_c < contiguous) {
+    sp.xbox_r = best_r;
+    sp.xbox_c = best_c;
+  }
+}
+
 void choose_box(int64_t Mt, int64_t Nt, int64_t chunk, int32_t &H, int32_t &W) {
   if (H > 0 && W > 0) return;
   if (H > 0) {
@@ -510,7 +519,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (d.sched < GEMM_SCHED_STATIC || d.sched > GEMM_SCHED_AUTO) return GEMM_ERR_INVALID_ARG;
   if (d.num_workers < 0 || d.bm < 0 || d.bn < 0 || d.bk < 0) return GEMM_ERR_INVALID_ARG;
   const uint32_t kind_flags =
-      GEMM_FLAG_PINGPONG | GEMM_FLAG_COOPERATIVE | GEMM_FLAG_REGSTAGED | GEMM_FLAG_WIDE;
+      GEMM_FLAG_PINGPONG | GEMM_FLAG_COOPERATIVE | GEMM_FLAG_WIDE;
   if (d.flags & ~(GEMM_FLAG_TRACE | GEMM_FLAG_NO_XCD_REMAP | GEMM_FLAG_STREAMK_CHAIN | kind_flags |
                   GEMM_FLAG_TEST_SKIP_PUBLISH))
     return GEMM_ERR_INVALID_ARG;
@@ -523,22 +532,21 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   if (d.N % 8 != 0) return GEMM_ERR_UNSUPPORTED;           // 16-byte output rows
   if (d.K * eb > (int64_t)1 << 30) return GEMM_ERR_UNSUPPORTED;
 
-  // the ping-pong, register-staged and wide-wave kernels run data-parallel work only, on
+  // the ping-pong and wide-wave kernels run data-parallel work only, on
   // 256 x 256 tiles
   const int force_kind = (d.flags & GEMM_FLAG_PINGPONG)      ? KIND_PP
-                         : (d.flags & GEMM_FLAG_REGSTAGED)   ? KIND_VS
                          : (d.flags & GEMM_FLAG_WIDE)        ? KIND_WIDE
                          : (d.flags & GEMM_FLAG_COOPERATIVE) ? KIND_COOP
                                                              : -1;
   // (the wide-wave kernel also runs Stream-K plans, with the separate-reduction fixup)
-  const bool force_dp = force_kind == KIND_PP || force_kind == KIND_VS || force_kind == KIND_WIDE;
-  const bool dp_only = force_kind == KIND_PP || force_kind == KIND_VS;
+  const bool force_dp = force_kind == KIND_PP || force_kind == KIND_WIDE;
+  const bool dp_only = force_kind == KIND_PP;
   if (force_dp && (d.K == 0 || (dp_only && (d.sched == GEMM_SCHED_STREAMK ||
                                             d.sched == GEMM_SCHED_AUTO))))
     return GEMM_ERR_UNSUPPORTED;
   // the fused epilogue runs on the wide-wave and cooperative kernels
   const bool fused = d.epilogue != 0 || d.dtype_c == GEMM_FP8_E4M3;
-  if (fused && (force_kind == KIND_PP || force_kind == KIND_VS)) return GEMM_ERR_UNSUPPORTED;
+  if (fused && force_kind == KIND_PP) return GEMM_ERR_UNSUPPORTED;
 
   // Tile shape and scheduler: the cost model when everything is left to the planner, else
   // 256 x 256 unless asked otherwise or the problem has too few big tiles.
@@ -651,6 +659,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     choose_box(Mt, Nt, sp.P % sp.X == 0 ? sp.P / sp.X : sp.P, sp.G, sp.G2);
   } else if (grouped && d.group == 0)  // likewise for the strip width G
     sp.G = choose_group(d.mapping, Mt, Nt, sp.P % sp.X == 0 ? sp.P / sp.X : sp.P);
+  if (sched != GEMM_SCHED_STATIC) choose_xcd_box(sp);
   sched_prepare(sp);
 
   gemm_plan *p = new (std::nothrow) gemm_plan;
@@ -740,6 +749,8 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   in.group = sp.G;
   in.group_n = sp.G2;
   in.sk_groups = sp.sk_groups;
+  in.xcd_box_r = sp.xbox_r;
+  in.xcd_box_c = sp.xbox_c;
   *out = p;
   return GEMM_OK;
 }

@@ -253,8 +253,19 @@ __device__ __forceinline__ void mfma_blk(acc_t<CFG> &c, const typename FragT<CFG
     mfma16_inplace(c, b, a);
 }
 
-// Wait states between VALU writes of accumulators and an MFMA reading them, or between an MFMA
-// writing them and other instructions reading them, where the compiler cannot see the MFMA.
+// Wait states where the compiler cannot see an MFMA written as inline asm (mfma16_inplace), so
+// its hazard recognizer inserts none.  Two places need them, both once per work item:
+//  * after the accumulators are zeroed (VALU / accumulator-register writes) and before the first
+//    MFMA reads them as its C operand: the ISA's dependency table asks for a few wait states
+//    there;
+//  * after the last MFMA of the k-loop and before anything else reads its result (the epilogue's
+//    accumulator reads, the Stream-K partial stores): an MFMA of P passes (four cycles each)
+//    needs a little over P wait states before a non-MFMA instruction may read what it wrote.
+//    The forms used here are 4-pass (16 x 16 x 32 bf16) and 8-pass (16 x 16 x 128 e4m3) -- 16
+//    and 32 busy cycles per instruction in the SQ_VALU_MFMA_BUSY_CYCLES counter.
+// Three s_nop 7 give 24 wait states, more than either place needs for these forms; a longer MFMA
+// (more passes) or a new reader of the accumulators between the k-loop and this call would need
+// this count revisited.
 __device__ __forceinline__ void mfma_wait_states() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
@@ -1249,302 +1260,6 @@ gemm_kernel_pp(KernelArgs args) {
   wait_vmcnt<0>();
 }
 
-// ---- register-staged kernel (data-parallel tiles) ---------------------------------------------
-//
-// Four waves, one per SIMD, each owning a 128 x 128 sub-tile (4 x 4 MFMA blocks, accumulators in
-// the accumulation registers): a third fewer LDS fragment reads per MFMA than 128 x 64 sub-tiles.
-// The operands go global -> registers -> LDS ("cuTensorMap" lesson's staging into shared memory,
-// done by the waves themselves): load j of k-step c+2 is issued in k-step c right after the LDS
-// write j of k-step c+1 has taken its registers, so one set of L staging registers suffices, the
-// address unit is busy all through the k-step instead of in bursts, and every load has a whole
-// k-step to arrive.  Because a wave's loads complete in issue order, the write j waits for
-// vmcnt(L-1): the L-1 loads issued after load j may still be in flight.
-//
-// Ring (2 stages) per k-step c, handshake at slot HS of the last sub-step as in gemm_kernel:
-//  * EMPTY(c-1): stage (c+1) mod 2 held step c-1, whose last fragment reads came before the
-//    handshake of step c (lgkmcnt(0) then s_barrier), so during step c the waves write step c+1
-//    into it;
-//  * FULL(c+1): the handshake of step c+1 (in step c's last sub-step) waits for the wave's own LDS
-//    writes (lgkmcnt(0)) and then the barrier, after which everyone reads step c+1.
-// The writes of step c+1 sit in the slots before that handshake.
-template <class CFG, bool RAGGED_K>
-struct Stager {
-  static constexpr int NW = CFG::WAVES;
-  static constexpr int LA = CFG::A_BYTES / 1024 / NW, LB = CFG::B_BYTES / 1024 / NW;
-  static constexpr int L = LA + LB;
-  static_assert(CFG::A_BYTES % (1024 * NW) == 0 && CFG::B_BYTES % (1024 * NW) == 0, "load split");
-  static_assert((NW * CFG::RPL) % (CFG::CH << CFG::SWZ) == 0, "swizzle must repeat per load");
-  static_assert(L <= 63, "vmcnt range");
-  Cursor cur;
-  int32_t valid, k, ke, rows_a, rows_b, edge;
-  __amdgpu_buffer_rsrc_t ra, rb;
-  int32_t sta, stb;   // global byte stride between loads j and j + 1 (uniform)
-  uint32_t voa, vob;  // lane global offsets of load 0: row row0, chunk lane % CH (coalesced)
-  uint32_t row0;      // tile row of the lane in load 0
-  uint32_t lds0;      // lane LDS offset of load 0 within an operand: the row's swizzled chunk
-  uint32_t chunk16;
-  u32x4 buf[L];  // staging registers
-
-  __device__ __forceinline__ void init(const KernelArgs &args, int32_t b, int wave, int lane) {
-    row0 = (uint32_t)(wave * CFG::RPL + lane / CFG::CH);
-    const uint32_t chunk = (uint32_t)(lane % CFG::CH);
-    chunk16 = chunk * 16;
-    voa = row0 * (uint32_t)args.lda_bytes + chunk16;
-    vob = row0 * (uint32_t)args.ldb_bytes + chunk16;
-    lds0 = row0 * CFG::ROWB + ((chunk ^ ((row0 >> CFG::SWZ) & (CFG::CH - 1))) * 16);
-    sta = (int32_t)(NW * CFG::RPL * args.lda_bytes);
-    stb = (int32_t)(NW * CFG::RPL * args.ldb_bytes);
-    ra = rb = make_rsrc(args.A, 0);  // empty until an item sets them
-    cursor_init(args.sp, b, cur);
-    next_item(args);
-  }
-
-  __device__ __forceinline__ void next_item(const KernelArgs &args) {
-    WorkItem w;
-    while ((valid = cursor_next(args.sp, cur, w)) && w.kb == w.ke) {
-    }
-    if (valid) {
-      k = w.kb;
-      ke = w.ke;
-      const int64_t m0 = (int64_t)w.m * CFG::BM, n0 = (int64_t)w.n * CFG::BN;
-      rows_a = (int32_t)(args.M - m0 < CFG::BM ? args.M - m0 : CFG::BM);
-      rows_b = (int32_t)(args.N - n0 < CFG::BN ? args.N - n0 : CFG::BN);
-      edge = rows_a < CFG::BM || rows_b < CFG::BN;
-      ra = make_rsrc(args.A + m0 * args.lda_bytes, (int64_t)rows_a * args.lda_bytes);
-      rb = make_rsrc(args.B + n0 * args.ldb_bytes, (int64_t)rows_b * args.ldb_bytes);
-    }
-  }
-
-  uint32_t koa, kob;
-  // loads of the cursor's k-step: begin() fixes the k offset, load<J>() fetches 1 KiB per wave
-  // into buf[J], end() advances the cursor.  With no k-step left (valid == 0) the loads still go
-  // out, at an offset past every range: they read zeros and touch no memory, which keeps the
-  // count of a wave's outstanding loads the same in every k-step.
-  __device__ __forceinline__ void begin(const KernelArgs &args) {
-    const uint32_t kbytes = (uint32_t)k * CFG::ROWB;
-    koa = voa + kbytes;
-    kob = vob + kbytes;
-    if (RAGGED_K && (int64_t)(k + 1) * CFG::ROWB > args.K * CFG::EB) {  // chunks past K read 0
-      if (chunk16 >= (uint32_t)(args.K * CFG::EB) - kbytes) koa = kob = kOOB;
-    }
-    if (!valid) koa = kob = kOOB;
-  }
-  template <int J>
-  __device__ __forceinline__ void load() {
-    constexpr bool IS_A = J < LA;
-    constexpr int j = IS_A ? J : J - LA;
-    uint32_t off = IS_A ? koa : kob;
-    if (edge && row0 + j * NW * CFG::RPL >= (uint32_t)(IS_A ? rows_a : rows_b)) off = kOOB;
-    buf[J] = __builtin_amdgcn_raw_buffer_load_b128(IS_A ? ra : rb, off, j * (IS_A ? sta : stb), 0);
-  }
-  __device__ __forceinline__ void end(const KernelArgs &args) {
-    if (++k == ke) next_item(args);
-  }
-  // LDS write of buf[J] into `stage`
-  template <int J>
-  __device__ __forceinline__ void store(lds_t *smem, int stage) const {
-    typedef u32x4 __attribute__((address_space(3))) *p128;
-    constexpr bool IS_A = J < LA;
-    constexpr int j = IS_A ? J : J - LA;
-    *(p128)(smem + stage * CFG::STAGE_BYTES + (IS_A ? 0 : CFG::A_BYTES) + lds0 +
-            j * NW * CFG::RPL * CFG::ROWB) = buf[J];
-  }
-};
-
-template <class CFG, bool RAGGED_K>
-__global__ void __attribute__((amdgpu_flat_work_group_size(CFG::THREADS, CFG::THREADS),
-                               amdgpu_waves_per_eu(1, 1)))
-gemm_kernel_vs(KernelArgs args) {
-  static_assert(CFG::WAVES == 4 && CFG::STAGES == 2, "four waves, two stages");
-  static_assert(CFG::MI == 32, "32 x 32 MFMA blocks");
-  static_assert(CFG::KSUB % 2 == 0, "k-tile must hold an even number of MFMA sub-steps");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[CFG::LDS_BYTES];
-  lds_t *smem = (lds_t *)(size_t)(uint32_t)(size_t)(lds_t *)smem_raw;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / CFG::WGN, wn = wave % CFG::WGN;
-  const int32_t b = blockIdx.x;
-
-  float alpha = 1.0f;
-  if constexpr (CFG::DT == DT_FP8) alpha = (*args.scale_a) * (*args.scale_b);
-
-  uint32_t aoff[CFG::KSUB][CFG::CPL], boff[CFG::KSUB][CFG::CPL];
-  {
-    const int r = lane & 31;
-    const int swz = (r >> CFG::SWZ) & (CFG::CH - 1);
-#pragma unroll
-    for (int s = 0; s < CFG::KSUB; ++s)
-#pragma unroll
-      for (int h = 0; h < CFG::CPL; ++h) {
-        const int chunk = (s * 2 + (lane >> 5)) * CFG::CPL + h;
-        const uint32_t in_row = (uint32_t)((chunk ^ swz) * 16);
-        aoff[s][h] = (uint32_t)((wm * CFG::WM + r) * CFG::ROWB) + in_row;
-        boff[s][h] = (uint32_t)(CFG::A_BYTES + (wn * CFG::WN + r) * CFG::ROWB) + in_row;
-      }
-  }
-
-  using St = Stager<CFG, RAGGED_K>;
-  constexpr int L = St::L;
-  constexpr int NM = CFG::FM * CFG::FN;  // MFMAs per sub-step
-  constexpr int NF = CFG::FM + CFG::FN;
-  constexpr int HS = NM / 4;             // handshake slot in the last sub-step
-  constexpr int WSLOTS = (CFG::KSUB - 1) * NM + HS;  // slots of a k-step before its handshake
-  St st;
-  st.init(args, b, wave, lane);
-
-  Cursor ccur;
-  cursor_init(args.sp, b, ccur);
-  WorkItem cw;
-  bool cvalid = cursor_next(args.sp, ccur, cw);
-
-  // k-steps whose loads are issued / written to LDS so far
-  int loaded = 0, written = 0;
-  auto load_step = [&]() {
-    st.begin(args);
-    [&]<int... J>(std::integer_sequence<int, J...>) { (st.template load<J>(), ...); }(
-        std::make_integer_sequence<int, L>());
-    if (st.valid) {
-      st.end(args);
-      ++loaded;
-    }
-  };
-  // Prologue: step 0 into stage 0, loads of step 1 in flight (zeros past the last k-step).
-  const bool any = st.valid;
-  load_step();
-  [&]<int... J>(std::integer_sequence<int, J...>) { (st.template store<J>(smem, 0), ...); }(
-      std::make_integer_sequence<int, L>());
-  if (any) ++written;
-  load_step();
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  lds_barrier();
-
-  Frags<CFG> fr[2];
-  if (written > 0) {
-    [&]<int... E>(std::integer_sequence<int, E...>) {
-      (load_frag<CFG, frag_order<CFG>(E)>(smem, 0, 0, aoff, boff, fr[0]), ...);
-    }(std::make_integer_sequence<int, NF>());
-  }
-
-  int c = 0;
-  bool pairs = false;  // does this k-step write step c+1 (and load step c+2)?
-  auto substep = [&](auto s_c, auto acc_ref) {
-    constexpr int S = decltype(s_c)::value;
-    constexpr int CUR = S & 1, NXT = (S + 1) & 1;
-    constexpr bool LAST = S == CFG::KSUB - 1;
-    auto &acc = *acc_ref;
-    const int stage = c & 1;
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      (
-          [&] {
-            constexpr int i = I;
-            constexpr int f = i / CFG::FN, g = i % CFG::FN;
-            acc[f][g] = mfma<CFG::DT>(fr[CUR].b[g], fr[CUR].a[f], acc[f][g]);
-            // (LDS write j of step c+1, load j of step c+2) pairs in the slots before the
-            // handshake.  They run in every k-step: past the last k-step the writes land in the
-            // drained stage nobody reads and the loads read zeros (see Stager::begin), so the
-            // number of outstanding loads at each write is always L-1.
-            constexpr int slot = S * NM + i;
-            if constexpr (slot < WSLOTS) {
-              constexpr int lo = ops_before(slot, L, 0, WSLOTS);
-              constexpr int hi = ops_before(slot + 1, L, 0, WSLOTS);
-              [&]<int... J>(std::integer_sequence<int, J...>) {
-                (
-                    [&] {
-                      constexpr int j = lo + J;
-                      st.template store<j>(smem, (c + 1) & 1);
-                      if constexpr (j == 0) st.begin(args);
-                      st.template load<j>();
-                      if constexpr (j == L - 1) {
-                        if (pairs) ++written;
-                        if (st.valid) {
-                          st.end(args);
-                          ++loaded;
-                        }
-                      }
-                    }(),
-                    ...);
-              }(std::make_integer_sequence<int, hi - lo>());
-            }
-            if constexpr (!LAST) {
-              constexpr int lo = ops_before(i, NF, 0, NM);
-              constexpr int hi = ops_before(i + 1, NF, 0, NM);
-              [&]<int... E>(std::integer_sequence<int, E...>) {
-                (load_frag<CFG, frag_order<CFG>(lo + E)>(smem, stage, S + 1, aoff, boff,
-                                                         fr[NXT]),
-                 ...);
-              }(std::make_integer_sequence<int, hi - lo>());
-            } else {
-              if constexpr (i + 1 == HS) {
-                if (c + 1 < written) {
-                  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                  lds_barrier();
-                }
-              }
-              if constexpr (i + 1 >= HS) {
-                constexpr int lo = ops_before(i, NF, HS, NM);
-                constexpr int hi = ops_before(i + 1, NF, HS, NM);
-                if (c + 1 < written) {
-                  [&]<int... E>(std::integer_sequence<int, E...>) {
-                    (load_frag<CFG, frag_order<CFG>(lo + E)>(smem, (c + 1) & 1, 0, aoff, boff,
-                                                             fr[NXT]),
-                     ...);
-                  }(std::make_integer_sequence<int, hi - lo>());
-                }
-              }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }(),
-          ...);
-    }(std::make_integer_sequence<int, NM>());
-  };
-
-  int seq = 0;
-  while (cvalid) {
-    if ((args.flags & KF_TRACE) && tid == 0 && seq < args.trace_cap) {
-      int *t = args.trace + ((int64_t)b * args.trace_cap + seq) * 8;
-      t[0] = b; t[1] = seq; t[2] = cw.tile; t[3] = cw.m;
-      t[4] = cw.n; t[5] = cw.kb; t[6] = cw.ke; t[7] = cw.role;
-    }
-    f32x16 acc[CFG::FM][CFG::FN];
-#pragma unroll
-    for (int f = 0; f < CFG::FM; ++f)
-#pragma unroll
-      for (int g = 0; g < CFG::FN; ++g)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[f][g][r] = 0.0f;
-
-    for (int k = cw.kb; k < cw.ke; ++k, ++c) {
-      // this k-step writes step c+1 if its loads were issued and, at the item's last k-step,
-      // if no epilogue needs that stage: the staged epilogue uses stage c mod 2, step c+1 goes
-      // to the other one, so writing is always allowed
-      pairs = loaded > c + 1;
-      [&]<int... S>(std::integer_sequence<int, S...>) {
-        (substep(std::integral_constant<int, S>(), &acc), ...);
-      }(std::make_integer_sequence<int, CFG::KSUB>());
-    }
-
-    if (args.out_bf16) {
-      // stage c-1 is drained once the handshake of step c ran (all waves past their reads of it);
-      // without a next step there was none
-      if (c >= written) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        lds_barrier();
-      }
-      epilogue_staged<CFG, true>(args, cw, acc, alpha, wm, wn, wave, lane, smem,
-                                 (c + CFG::STAGES - 1) % CFG::STAGES);
-      lds_barrier();  // the stage takes step c+1's writes in the next k-step
-    } else {
-      EpiCtx ec_unused = {1.0f, 0.0f};
-      epilogue<CFG>(args, cw, acc, alpha, wm, wn, tid, ec_unused);
-    }
-    ++seq;
-    cvalid = cursor_next(args.sp, ccur, cw);
-  }
-  wait_vmcnt<0>();
-}
-
 // ---- wide-wave kernel (data-parallel tiles) ---------------------------------------------------
 //
 // Four waves, one per SIMD, each owning a 128 x 128 sub-tile (4 x 4 MFMA blocks, accumulators in
@@ -1870,18 +1585,26 @@ __device__ __forceinline__ void wide_reduce(const KernelArgs &args, const WorkIt
   }
 }
 
-template <class CFG, bool RAGGED_K>
+// LEAN keeps only the first load's lane offset per operand and forms load j's as that plus j
+// uniform row strides (one VALU add per load), instead of one register per load: 14 fewer
+// VGPRs, which the e4m3 kernel (fragments of 128 VGPRs next to 256 accumulators) needs to keep
+// its epilogue out of scratch.  Rows past the edge of an item's operand then get an offset past
+// the end of the item's buffer range instead of kOOB: the range check zeroes them alike.  An
+// exhausted producer switches to an empty range, so every offset reads zero.
+template <class CFG, bool RAGGED_K, bool LEAN = false>
 struct WideProducer {
   static constexpr int NW = CFG::WAVES;
   static constexpr int LA = CFG::A_BYTES / 1024 / NW, LB = CFG::B_BYTES / 1024 / NW;
   static constexpr int L = LA + LB;
+  static constexpr int NV = LEAN ? 2 : L;  // lane offsets kept per item
   static_assert(CFG::A_BYTES % (1024 * NW) == 0 && CFG::B_BYTES % (1024 * NW) == 0, "load split");
   static_assert((NW * CFG::RPL) % (CFG::CH << CFG::SWZ) == 0, "swizzle must repeat per load");
   static_assert(L <= 63, "vmcnt range");
   Cursor cur;
   int32_t valid, k, ke;
   __amdgpu_buffer_rsrc_t ra, rb;
-  uint32_t vo[L];      // lane offsets of the item's loads
+  uint32_t vo[NV];     // lane offsets of the item's loads (LEAN: of the first A and B load)
+  uint32_t step_a, step_b;  // LEAN: byte distance between consecutive loads' rows (uniform)
   uint32_t row0;       // tile row of the lane in load 0
   uint32_t chunk16;    // byte offset of the lane's swizzled chunk within a k-tile row
   uint32_t kbytes;     // byte offset of the k-step within a row (soffset of every load)
@@ -1891,6 +1614,8 @@ struct WideProducer {
   __device__ __forceinline__ void init(const KernelArgs &args, int32_t b, int wave, int lane) {
     row0 = (uint32_t)(wave * CFG::RPL + lane / CFG::CH);
     chunk16 = (uint32_t)(((lane % CFG::CH) ^ ((row0 >> CFG::SWZ) & (CFG::CH - 1))) * 16);
+    step_a = (uint32_t)(NW * CFG::RPL) * (uint32_t)args.lda_bytes;
+    step_b = (uint32_t)(NW * CFG::RPL) * (uint32_t)args.ldb_bytes;
     ra = rb = make_rsrc(args.A, 0);  // empty until an item sets them
     cursor_init(args.sp, b, cur);
     next_item(args);
@@ -1908,16 +1633,23 @@ struct WideProducer {
       const int32_t rows_b = (int32_t)(args.N - n0 < CFG::BN ? args.N - n0 : CFG::BN);
       ra = make_rsrc(args.A + m0 * args.lda_bytes, (int64_t)rows_a * args.lda_bytes);
       rb = make_rsrc(args.B + n0 * args.ldb_bytes, (int64_t)rows_b * args.ldb_bytes);
+      if constexpr (LEAN) {
+        // rows past rows_a (rows_b) lie past the range's end: no per-row test needed
+        vo[0] = row0 * (uint32_t)args.lda_bytes + chunk16;
+        vo[1] = row0 * (uint32_t)args.ldb_bytes + chunk16;
+      } else {
 #pragma unroll
-      for (int J = 0; J < L; ++J) {
-        const bool is_a = J < LA;
-        const uint32_t row = row0 + (uint32_t)((is_a ? J : J - LA) * NW * CFG::RPL);
-        const uint32_t ld = (uint32_t)(is_a ? args.lda_bytes : args.ldb_bytes);
-        vo[J] = row < (uint32_t)(is_a ? rows_a : rows_b) ? row * ld + chunk16 : kOOB;
+        for (int J = 0; J < L; ++J) {
+          const bool is_a = J < LA;
+          const uint32_t row = row0 + (uint32_t)((is_a ? J : J - LA) * NW * CFG::RPL);
+          const uint32_t ld = (uint32_t)(is_a ? args.lda_bytes : args.ldb_bytes);
+          vo[J] = row < (uint32_t)(is_a ? rows_a : rows_b) ? row * ld + chunk16 : kOOB;
+        }
       }
     } else {
+      if constexpr (LEAN) ra = rb = make_rsrc(args.A, 0);
 #pragma unroll
-      for (int J = 0; J < L; ++J) vo[J] = kOOB;
+      for (int J = 0; J < NV; ++J) vo[J] = kOOB;
     }
   }
 
@@ -1933,7 +1665,11 @@ struct WideProducer {
     constexpr bool IS_A = J < LA;
     constexpr int j = IS_A ? J : J - LA;
     constexpr uint32_t dst_off = (IS_A ? 0 : CFG::A_BYTES) + j * NW * 1024;
-    uint32_t off = vo[J];
+    uint32_t off;
+    if constexpr (LEAN)
+      off = (IS_A ? vo[0] : vo[1]) + (uint32_t)j * (IS_A ? step_a : step_b);
+    else
+      off = vo[J];
     if constexpr (RAGGED_K) off = k_oob ? kOOB : off;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(IS_A ? ra : rb, (lds_t *)(size_t)(lds_wave + dst_off), 16,
                                              off, kbytes, 0, 0);
@@ -2100,7 +1836,8 @@ gemm_kernel_wide(KernelArgs args) {
     for (int f = 0; f < CFG::FM; ++f)
 #pragma unroll
       for (int g = 0; g < CFG::FN; ++g) acc[f][g] = acc_t<CFG>{};
-    if constexpr (CFG::MI == 16) mfma_wait_states();  // zeroed accumulators reach the MFMAs
+    // 24 wait states: the zeroed accumulators reach the first (inline-asm) MFMA's C operand
+    if constexpr (CFG::MI == 16) mfma_wait_states();
 
     if constexpr (CFG::KSUB % 2 == 0) {
       for (int k = cw.kb; k < cw.ke; ++k) kstep(std::integral_constant<int, 0>(), &acc);
@@ -2118,7 +1855,9 @@ gemm_kernel_wide(KernelArgs args) {
       }
     }
 
-    if constexpr (CFG::MI == 16) mfma_wait_states();  // the last MFMAs' results are written
+    // 24 wait states (> 4 passes + the ISA's margin): the last MFMAs' results are written before
+    // the epilogue or the partial store reads them
+    if constexpr (CFG::MI == 16) mfma_wait_states();
     if (cw.role != ROLE_WHOLE) {  // a Stream-K split: its partial, reduced after all MAC work
       wide_partial_store<CFG>(args, cw, acc, b, wm, wn, lane, tid);
     } else if (CFG::WM == 128 && args.out_bf16) {  // staged through the wave's LDS slice
@@ -2207,7 +1946,7 @@ gemm_kernel_wide1(KernelArgs args) {
     dst = lds_frag<CFG::DT>(base + boff[0][0], base + boff[0][H]);
   };
 
-  using Prod = WideProducer<CFG, RAGGED_K>;
+  using Prod = WideProducer<CFG, RAGGED_K, true>;
   Prod prod;
   prod.init(args, b, wave, lane);
   const uint32_t lds_wave0 = smem_base + (uint32_t)wave * 1024;
@@ -2296,7 +2035,8 @@ gemm_kernel_wide1(KernelArgs args) {
     for (int f = 0; f < FM; ++f)
 #pragma unroll
       for (int g = 0; g < FN; ++g) acc[f][g] = acc_t<CFG>{};
-    mfma_wait_states();  // zeroed accumulators reach the MFMAs
+    // 24 wait states: the zeroed accumulators reach the first (inline-asm) MFMA's C operand
+    mfma_wait_states();
     // k-steps in pairs, so each item starts on B buffer 0; after an odd last step the next item's
     // B sits in buffer 1 and moves over (once per item)
     int k = cw.kb;
@@ -2309,7 +2049,9 @@ gemm_kernel_wide1(KernelArgs args) {
 #pragma unroll
       for (int g = 0; g < FN; ++g) fb[0][g] = fb[1][g];
     }
-    mfma_wait_states();  // the last MFMAs' results are written
+    // 24 wait states (> 8 passes + the ISA's margin): the last MFMAs' results are written before
+    // the epilogue or the partial store reads them
+    mfma_wait_states();
     if (cw.role != ROLE_WHOLE) {  // a Stream-K split: its partial, reduced after all MAC work
       wide_partial_store<CFG>(args, cw, acc, b, wm, wn, lane, tid);
     } else if (CFG::WM == 128 && args.out_bf16) {  // staged through the wave's LDS slice

@@ -80,6 +80,9 @@ struct SchedParams {
   FastDiv div_box_last;    // blocked: (height of the short last box row) * G2
   int32_t full_strips;     // strips (blocked: box rows) of exactly G
   int32_t morton_size;     // Morton: the smallest power of two >= max(Mt, Nt)
+  int32_t xbox_r, xbox_c;  // XCD box remap (grouped mappings): each XCD's P/X tasks of a wave
+                           // form an xbox_r (across the strip) x xbox_c (along it) box; 0 = the
+                           // contiguous remap (xcd_worker)
 };
 
 // Fills the divisor fields from Mt, Nt, Kt, mapping, G and G2.
@@ -198,6 +201,23 @@ DG_HD int32_t xcd_worker(int32_t b, int32_t P, int32_t X) {
   return (b % X) * (P / X) + b / X;
 }
 
+// XCD box remap of a grouped mapping.  When every wave of P consecutive tasks is a whole G x (P/G)
+// block of one strip (G tile-rows across the strip, P/G positions along it, in-strip task
+// t = along * G + across), contiguous runs of P/X tasks give each XCD a G x (P/(X G)) slab, which
+// needs G + P/(X G) operand strips per k-step in that XCD's L2.  Cutting the block into X boxes of
+// r x c tasks (r | G, c | P/G, r c = P/X) with r + c smallest needs only r + c: for G = 16 and
+// 32 tasks per XCD, 8 x 4 boxes need 12 strips where 16 x 2 slabs need 18.  Workgroup b runs on
+// XCD x = b mod X as its k-th workgroup, k = b div X; XCD x takes box (x mod (G/r), x div (G/r))
+// and its k-th workgroup the task at (k mod r, k div r) inside the box, in every wave.  Returns the
+// workgroup's task in the first wave (later waves add P).
+DG_HD int32_t xcd_box_task(const SchedParams &sp, int32_t b) {
+  const int32_t x = b % sp.X, k = b / sp.X;
+  const int32_t across_boxes = sp.G / sp.xbox_r;
+  const int32_t across = (x % across_boxes) * sp.xbox_r + k % sp.xbox_r;
+  const int32_t along = (x / across_boxes) * sp.xbox_c + k / sp.xbox_r;
+  return along * sp.G + across;
+}
+
 // Cursor over one workgroup's work: its data-parallel tiles first, then its Stream-K splits from
 // the last tile it touches back to the first.
 struct Cursor {
@@ -216,7 +236,7 @@ DG_HD int64_t sk_group_iters(const SchedParams &sp, int32_t g) {
 }
 
 DG_HD void cursor_init(const SchedParams &sp, int32_t b, Cursor &c) {
-  c.next_dp = xcd_worker(b, sp.P, sp.X);
+  c.next_dp = sp.xbox_r > 0 ? xcd_box_task(sp, b) : xcd_worker(b, sp.P, sp.X);
   c.sk_group = 0;
   if (sp.sk_tiles > 0) {
     const int32_t g = b / sp.sk_gunits, v = b - g * sp.sk_gunits;

@@ -81,18 +81,16 @@ typedef enum {
                                         loads) and an MFMA-only phase ("H100 Kernel Design"
                                         sections 7.3-7.5).  256 x 256 tiles, data-parallel
                                         schedules only (static or persistent, K > 0); other plans
-                                        with this flag return GEMM_ERR_UNSUPPORTED.  Without
-                                        either kernel flag, such plans use it by default        */
+                                        with this flag return GEMM_ERR_UNSUPPORTED              */
 #define GEMM_FLAG_COOPERATIVE 0x10u  /* require the cooperative kernel (every wave loads and
                                         computes; also runs Stream-K and 128 x 128 tiles)        */
-#define GEMM_FLAG_REGSTAGED 0x20u    /* require the register-staged kernel: four waves with 128 x
-                                        128 sub-tiles, operands staged global -> registers ->
-                                        LDS.  Same limits as GEMM_FLAG_PINGPONG.  At most one of
-                                        the kernel flags (else GEMM_ERR_INVALID_ARG)            */
 #define GEMM_FLAG_WIDE 0x40u         /* require the wide-wave kernel: four waves with 128 x 128
                                         (or 128 x 112, 64 x 64) sub-tiles fed by direct global ->
                                         LDS loads, 16 x 16 MFMAs.  Runs data-parallel plans and
-                                        Stream-K with the separate reduction                    */
+                                        Stream-K with the separate reduction.  At most one
+                                        kernel flag (else GEMM_ERR_INVALID_ARG); without one the
+                                        planner picks, the wide-wave kernel for every plan with
+                                        K > 0 that does not need the Stream-K lock chain        */
 #define GEMM_FLAG_TEST_SKIP_PUBLISH 0x100u /* test only: the first Stream-K split of band tile 0
                                               does not publish its lock / arrival, so the bounded
                                               waits on it expire and report GEMM_DEVICE_ERR_SPIN */
@@ -103,7 +101,7 @@ typedef enum {
  * -- all applied to the finished accumulators before C is stored once (a Stream-K tile: by the
  * split that writes it, after the full sum).  At most one bias bit and one activation bit.
  * A plan with epilogue bits or an e4m3 output runs on the wide-wave or the cooperative kernel
- * (GEMM_FLAG_PINGPONG / GEMM_FLAG_REGSTAGED with them: GEMM_ERR_UNSUPPORTED). */
+ * (GEMM_FLAG_PINGPONG with them: GEMM_ERR_UNSUPPORTED). */
 #define GEMM_EPI_BIAS_ROW 0x1u  /* Z[m][n] += bias[m]; bias holds M floats                     */
 #define GEMM_EPI_BIAS_COL 0x2u  /* Z[m][n] += bias[n]; bias holds N floats                     */
 #define GEMM_EPI_RELU 0x4u      /* Y = max(Z, 0)                                                  */
@@ -175,10 +173,14 @@ typedef struct gemm_plan_info {
   int32_t trace_capacity;    /* records per workgroup                                            */
   int32_t error_offset;      /* byte offset of the device error word in the workspace (-1: none)*/
   int32_t streamk_mode;      /* 0 lock chain, 1 separate reduction (meaningful when sk_tiles>0)  */
-  int32_t kernel;            /* 0 cooperative, 1 ping-pong, 2 register-staged, 3 wide-wave       */
+  int32_t kernel;            /* 0 cooperative, 1 ping-pong, 3 wide-wave (2 is not used)         */
   int32_t group;             /* G of a grouped mapping as planned (1 for the linear ones)       */
   int32_t group_n;           /* box width of BLOCKED as planned (1 for the other mappings)      */
   int32_t sk_groups;         /* Stream-K groups as planned (1 without a band)                   */
+  int32_t xcd_box_r;         /* XCD box remap of a grouped mapping: each XCD runs an r x c box
+                                of every data-parallel wave (r across the strip, c along it);
+                                0 = contiguous runs of P / xcds workers per XCD               */
+  int32_t xcd_box_c;
 } gemm_plan_info;
 
 /* device error word values (read back from the workspace after a run) */

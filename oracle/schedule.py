@@ -40,7 +40,11 @@ Reading where the pages are open (each is listed in the design doc):
 
 The XCD remap is this build's own MI355X design, not the pages': with X L2 domains (XCDs) and
 workgroups dealt to them round-robin, the worker id that workgroup b runs under is chosen so that
-every XCD owns a contiguous run of worker ids.  It is enumerated here from that statement.
+every XCD owns a contiguous run of worker ids.  It is enumerated here from that statement.  For a
+grouped mapping whose data-parallel waves are whole G x (P/G) blocks of one strip, the build
+instead gives each XCD a box of every wave's block (the analogue, inside one launch, of the
+"DeepGEMM on SM90" page's 2D blocking), when a box needs fewer operand strips than a contiguous
+run; xcd_box_assignment enumerates that from its statement, by geometry.
 """
 from dataclasses import dataclass
 
@@ -128,6 +132,53 @@ def xcd_worker_ids(P, X=8):
     return ids
 
 
+def xcd_box_assignment(mode, Mt, Nt, G, P, X=8):
+    """The first-wave task of each workgroup b under the XCD box remap, or None where it does not
+    apply (then xcd_worker_ids holds).
+
+    It applies to the grouped mappings when every strip holds G tile rows (columns), every wave of
+    P consecutive tasks lies inside one strip (so it is a G x P/G block: G across the strip, P/G
+    along it), X divides P, and the P/X tasks an XCD runs per wave divide G or are a multiple of
+    it.  The box is r across x c along with r | G, c | P/G, r c = P/X, r + c smallest (the taller
+    box on a tie); it is used only when r + c is below the number of operand strips (distinct
+    rows plus distinct columns) of a contiguous run of P/X tasks.  XCD x (the workgroups b with
+    b mod X = x, the k-th of them being b = x + k X) takes the box at block position
+    (x mod (G/r), x div (G/r)) -- counted in boxes across, then along -- and its k-th workgroup
+    the task at (k mod r, k div r) inside that box: in every wave, so later waves add P.
+    """
+    if mode not in (GROUPED_M, GROUPED_N) or X <= 1 or G < 1 or P < X or P % X or P % G:
+        return None
+    n_across, n_along = (Mt, Nt) if mode == GROUPED_M else (Nt, Mt)
+    per = P // X
+    if n_across % G or (G * n_along) % P or not (per % G == 0 or G % per == 0):
+        return None
+    wave = tile_order(mode, Mt, Nt, G)[:P]
+
+    def across_along(t):
+        m, n = wave[t]
+        return (m, n) if mode == GROUPED_M else (n, m)
+
+    first = [across_along(t) for t in range(per)]
+    contiguous = len({a for a, _ in first}) + len({b for _, b in first})
+    boxes = [(r + per // r, -r) for r in range(1, G + 1)
+             if G % r == 0 and per % r == 0 and (P // G) % (per // r) == 0]
+    if not boxes:
+        return None
+    strips, neg_r = min(boxes)
+    r = -neg_r
+    c = per // r
+    if strips >= contiguous:
+        return None
+    task_at = {across_along(t): t for t in range(P)}
+    ids = [None] * P
+    for b in range(P):
+        x, k = b % X, b // X
+        a0 = (x % (G // r)) * r
+        l0 = (x // (G // r)) * c
+        ids[b] = task_at[(a0 + k % r, l0 + k // r)]
+    return ids
+
+
 def wave_efficiency(ctas, num_sms):
     waves = -(-ctas // num_sms)
     return ctas / (waves * num_sms)
@@ -198,7 +249,7 @@ def role_of(k_idx, final):
 
 
 def enumerate_schedule(M, N, K, BM, BN, BK, mapping, G, sched, P=None, X=8, xcd_remap=True,
-                       W=1, sk_groups=1):
+                       W=1, sk_groups=1, xcd_box=True):
     """Every work item of the launch, grouped by workgroup, in each workgroup's order."""
     Mt, Nt, Kt = tile_counts(M, N, K, BM, BN, BK)
     order = tile_order(mapping, Mt, Nt, G, W)
@@ -222,6 +273,10 @@ def enumerate_schedule(M, N, K, BM, BN, BK, mapping, G, sched, P=None, X=8, xcd_
     else:
         raise ValueError(f"unknown scheduler {sched}")
     ids = xcd_worker_ids(P, X) if xcd_remap else list(range(P))
+    if xcd_remap and xcd_box:
+        box = xcd_box_assignment(mapping, Mt, Nt, G, P, X)
+        if box is not None:
+            ids = box
     units = (streamk_units(sk_tiles, Kt, P, first_tile=dp_tiles, groups=sk_groups)
              if sk_tiles else None)
     for b in range(P):

@@ -110,11 +110,8 @@ def create(**kw):
     (dict(flags=L.GEMM_FLAG_PINGPONG, sched=L.GEMM_SCHED_STREAMK), L.GEMM_ERR_UNSUPPORTED),
     (dict(flags=L.GEMM_FLAG_COOPERATIVE), L.GEMM_OK),
     (dict(flags=L.GEMM_FLAG_COOPERATIVE | L.GEMM_FLAG_PINGPONG), L.GEMM_ERR_INVALID_ARG),
-    (dict(flags=L.GEMM_FLAG_REGSTAGED | L.GEMM_FLAG_PINGPONG), L.GEMM_ERR_INVALID_ARG),
-    (dict(flags=L.GEMM_FLAG_REGSTAGED), L.GEMM_OK),
-    (dict(flags=L.GEMM_FLAG_REGSTAGED, dtype_ab=L.GEMM_FP8_E4M3, K=400, M=300), L.GEMM_OK),
-    (dict(flags=L.GEMM_FLAG_REGSTAGED, sched=L.GEMM_SCHED_STREAMK), L.GEMM_ERR_UNSUPPORTED),
-    (dict(flags=L.GEMM_FLAG_REGSTAGED, K=0), L.GEMM_ERR_UNSUPPORTED),
+    (dict(flags=L.GEMM_FLAG_WIDE | L.GEMM_FLAG_PINGPONG), L.GEMM_ERR_INVALID_ARG),
+    (dict(flags=0x20), L.GEMM_ERR_INVALID_ARG),  # the retired register-staged kernel's flag
     (dict(flags=L.GEMM_FLAG_WIDE), L.GEMM_OK),
     (dict(flags=L.GEMM_FLAG_WIDE, dtype_ab=L.GEMM_FP8_E4M3, K=400, M=300), L.GEMM_OK),
     (dict(flags=L.GEMM_FLAG_WIDE, bk=32), L.GEMM_ERR_UNSUPPORTED),  # its bf16 k-tile is 64 deep
@@ -139,7 +136,6 @@ def create(**kw):
     (dict(epilogue=L.GEMM_EPI_RELU, flags=L.GEMM_FLAG_WIDE), L.GEMM_OK),
     (dict(epilogue=L.GEMM_EPI_RELU, flags=L.GEMM_FLAG_COOPERATIVE), L.GEMM_OK),
     (dict(epilogue=L.GEMM_EPI_RELU, flags=L.GEMM_FLAG_PINGPONG), L.GEMM_ERR_UNSUPPORTED),
-    (dict(epilogue=L.GEMM_EPI_RELU, flags=L.GEMM_FLAG_REGSTAGED), L.GEMM_ERR_UNSUPPORTED),
     (dict(dtype_c=L.GEMM_FP8_E4M3, flags=L.GEMM_FLAG_PINGPONG), L.GEMM_ERR_UNSUPPORTED),
 ])
 def test_create_validation(kw, want):

@@ -117,14 +117,13 @@ PINGPONG = [
 
 # data-parallel kernels for 256 x 256 tiles: flag, plan_info.kernel, threads
 DP_KERNELS = {"pingpong": (L.GEMM_FLAG_PINGPONG, 1, 512),
-              "regstaged": (L.GEMM_FLAG_REGSTAGED, 2, 256),
               "wide": (L.GEMM_FLAG_WIDE, 3, 256)}
 
 
 @pytest.mark.parametrize("kern", list(DP_KERNELS))
 @pytest.mark.parametrize("case", PINGPONG, ids=[c[0] for c in PINGPONG])
 def test_pingpong_parity(dev, case, kern):
-    """The data-parallel kernels (ping-pong, register-staged, wide-wave): several items per
+    """The data-parallel kernels (ping-pong, wide-wave): several items per
     worker, ragged M/N/K, one k-step per item, fp32 and bf16 outputs."""
     name, M, N, K, dt, out, mapping, G, sched, workers = case
     flag, kind, threads = DP_KERNELS[kern]
@@ -229,6 +228,29 @@ def test_device_trace_matches_enumeration(dev, sched, workers, tile, mapping, G,
     assert_within_tolerance(C, reference(op), op, "trace run")
 
 
+@pytest.mark.parametrize("mapping", [L.GEMM_MAP_GROUPED_M, L.GEMM_MAP_GROUPED_N])
+def test_device_trace_xcd_box(dev, mapping):
+    """A plan on the XCD box remap (Grouped-M/N(8) on 16 x 8 tiles of 128, 64 workers: every
+    wave is an 8 x 8 block, each XCD takes a 4 x 2 box of it): the kernel's recorded work items
+    equal the CPU replay and the oracle's enumeration, and the product is within tolerance."""
+    M, N, K = (2048, 1024, 256) if mapping == L.GEMM_MAP_GROUPED_M else (1024, 2048, 256)
+    op = gi.make_operands(M, N, K, "bf16", seed=31)
+    C, plan, ws = run_gpu(op, torch, dev, "f32", mapping, 8, L.GEMM_SCHED_PERSISTENT, 64, 128,
+                          flags=L.GEMM_FLAG_TRACE)
+    info = plan.info
+    assert (info.xcd_box_r, info.xcd_box_c) == (4, 2)
+    raw = ws.cpu().numpy()[info.trace_offset:].view(np.int32)[: info.grid * info.trace_capacity * 8]
+    rec = raw.reshape(info.grid, info.trace_capacity, 8)
+    got = [tuple(int(x) for x in r) for w in range(info.grid) for r in rec[w]
+           if r[0] == w and r[6] > 0]
+    assert got == plan.schedule()
+    ora = S.enumerate_schedule(M, N, K, 128, 128, info.bk,
+                               S.GROUPED_M if mapping == L.GEMM_MAP_GROUPED_M else S.GROUPED_N,
+                               8, S.PERSISTENT, P=info.grid)
+    assert got == [(w.worker, w.seq, w.tile, w.m, w.n, w.k_begin, w.k_end, w.role) for w in ora]
+    assert_within_tolerance(C, reference(op), op, "box trace run")
+
+
 @pytest.mark.parametrize("mode", list(SK_MODES))
 def test_spin_watchdog_reports_instead_of_hanging(dev, mode):
     """The first split of band tile 0 withholds its lock / arrival (test flag); the bounded waits
@@ -290,7 +312,7 @@ MFMA16 = {("wide", "bf16"), ("wide", "e4m3"), ("wide128", "bf16"), ("wide128", "
 def test_data_parallel_kernels_bit_identical(dev, dt, out):
     """Every data-parallel kernel with the same MFMA shape sums each output over K in the same
     order with the same instruction (k-tile depth only groups the MFMAs), so kernels of one
-    shape -- cooperative (128 and 256 tiles), ping-pong, register-staged, wide-wave -- must agree
+    shape -- cooperative (128 and 256 tiles), ping-pong, wide-wave -- must agree
     bit for bit, across tile shapes, ragged M/N/K and several items per worker; every kernel is
     within tolerance of the oracle."""
     M, N, K = 776, 520, 1000 if dt == "bf16" else 1040
@@ -301,7 +323,6 @@ def test_data_parallel_kernels_bit_identical(dev, dt, out):
     for name, tile, flags in (("coop128", 128, L.GEMM_FLAG_COOPERATIVE),
                               ("coop256", 256, L.GEMM_FLAG_COOPERATIVE),
                               ("pingpong", 256, L.GEMM_FLAG_PINGPONG),
-                              ("regstaged", 256, L.GEMM_FLAG_REGSTAGED),
                               ("wide", 256, L.GEMM_FLAG_WIDE),
                               ("wide128", 128, L.GEMM_FLAG_WIDE)):
         C, plan, _ = run_gpu(op, torch, dev, out, L.GEMM_MAP_GROUPED_M, 2,
@@ -330,7 +351,7 @@ def test_no_writes_past_c(dev, M, N, K):
         canary_bytes = 4 << 20
         buf = torch.empty(M * N * eb + canary_bytes, dtype=torch.uint8, device=dev)
         for tile, flags in ((128, L.GEMM_FLAG_COOPERATIVE), (256, L.GEMM_FLAG_COOPERATIVE),
-                            (256, L.GEMM_FLAG_PINGPONG), (256, L.GEMM_FLAG_REGSTAGED),
+                            (256, L.GEMM_FLAG_PINGPONG),
                             (256, L.GEMM_FLAG_WIDE), (128, L.GEMM_FLAG_WIDE)):
             buf.fill_(0xA5)
             plan = L.Plan(L.make_desc(M, N, K, L.GEMM_BF16,

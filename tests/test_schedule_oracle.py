@@ -309,3 +309,44 @@ def test_streamk_groups_in_the_launch_enumeration():
     for it in sk:
         assert it.worker // 32 == (it.tile - 512) % 8
     assert Counter(it.tile for it in sk) == {t: 4 for t in range(512, 576)}
+
+
+def test_xcd_box_hand_worked():
+    """8 x 8 tiles, Grouped-M(4), 16 workers on 4 XCDs: a wave is the 4 x 4 block of strip 0
+    (in-strip task t = column * 4 + row).  Runs of 4 tasks would be 4 x 1 columns (5 strips);
+    2 x 2 boxes need 4.  XCD x = b mod 4 takes box (x mod 2, x div 2), its k-th workgroup
+    (k = b div 4) the tile at (k mod 2, k div 2) inside it -- worked out by hand."""
+    ids = S.xcd_box_assignment(S.GROUPED_M, 8, 8, 4, 16, X=4)
+    assert ids == [0, 2, 8, 10, 1, 3, 9, 11, 4, 6, 12, 14, 5, 7, 13, 15]
+
+
+def test_xcd_box_geometry_fp8_8192():
+    """fp8 8192^3 on 256 x 256 tiles, Grouped-M(16), 256 workers: in every wave each XCD's 32
+    tiles form an 8 x 4 box (12 operand strips, against 18 for runs of 32 tasks), and every task
+    is taken exactly once."""
+    Mt = Nt = 32
+    items = S.enumerate_schedule(8192, 8192, 8192, 256, 256, 128, S.GROUPED_M, 16, S.PERSISTENT,
+                                 P=256)
+    assert sorted(w.tile for w in items) == list(range(Mt * Nt))
+    for wave in range(4):
+        for x in range(8):
+            mine = [(w.m, w.n) for w in items if w.worker % 8 == x and w.seq == wave]
+            ms, ns = {m for m, _ in mine}, {n for _, n in mine}
+            assert len(mine) == 32 and len(ms) == 8 and len(ns) == 4
+            assert max(ms) - min(ms) == 7 and max(ns) - min(ns) == 3   # a rectangle
+    contiguous = S.enumerate_schedule(8192, 8192, 8192, 256, 256, 128, S.GROUPED_M, 16,
+                                      S.PERSISTENT, P=256, xcd_box=False)
+    for x in range(8):
+        mine = [(w.m, w.n) for w in contiguous if w.worker % 8 == x and w.seq == 0]
+        assert len({m for m, _ in mine}) + len({n for _, n in mine}) == 18
+
+
+def test_xcd_box_not_used_without_gain_or_outside_whole_blocks():
+    # runs of 32 tasks under Grouped-M(8) on 16 x 64 tiles are already 8 x 4 (12 strips)
+    assert S.xcd_box_assignment(S.GROUPED_M, 16, 64, 8, 256) is None
+    # a wave of 256 tasks spans two Grouped-M(8) strips of 16 x 16 tiles
+    assert S.xcd_box_assignment(S.GROUPED_M, 16, 16, 8, 256) is None
+    # a short last strip (Mt not a multiple of G)
+    assert S.xcd_box_assignment(S.GROUPED_M, 20, 32, 16, 256) is None
+    # the linear mappings keep contiguous runs
+    assert S.xcd_box_assignment(S.LINEAR_N, 32, 32, 1, 256) is None
