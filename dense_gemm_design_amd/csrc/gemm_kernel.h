@@ -1377,13 +1377,20 @@ __device__ __forceinline__ void epilogue_wide(const KernelArgs &args, const Work
   lds_t *rd_p[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) rd_p[jj] = slice + rrow * 256 + ((chunk_l ^ rrow ^ (4 * jj)) * 16);
+  // The reads go out four at a time ahead of their stores: the compiler keeps an LDS read behind
+  // an earlier buffer store, so read, store, read, store would wait out one LDS round trip per
+  // 16-byte chunk.
   auto read_back = [&](int round) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const u32x4 v = *(p128)(rd_p[j & 3] + j * 1024);
-      if (col_ok)
-        __builtin_amdgcn_raw_buffer_store_b128(v, cr, st_off, (uint32_t)(round * 32 + j * 4) * ldc_b,
-                                               0);
+    for (int h = 0; h < 2; ++h) {
+      u32x4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = *(p128)(rd_p[j] + (h * 4 + j) * 1024);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (col_ok)
+          __builtin_amdgcn_raw_buffer_store_b128(v[j], cr, st_off,
+                                                 (uint32_t)(round * 32 + (h * 4 + j) * 4) * ldc_b, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
