@@ -189,6 +189,48 @@ def ingest_pmc(fetch_csv, write_csv, name, command, copy_mib):
     print(json.dumps(data[wl]))
 
 
+def summarize_trace(path, last):
+    """Kernel-trace summary (rocprofv3 --kernel-trace CSV): per GEMM kernel, its resources and the
+    duration of its last `last` dispatches (the timed ones), for the profiles/ summaries."""
+    import statistics
+    rows = _read_counter_csv(path)
+    by = {}
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append(r)
+    for name, rs in sorted(by.items(), key=lambda kv: -len(kv[1])):
+        rs.sort(key=lambda r: int(r.get("Dispatch_Id", 0)))
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
+        tail = d[-last:] if last else d
+        r0 = rs[-1]
+        print(f"kernel: {name}")
+        print(f"  grid {r0.get('Grid_Size', r0.get('Grid_Size_X'))} work-items, workgroup "
+              f"{r0.get('Workgroup_Size', r0.get('Workgroup_Size_X'))}, LDS "
+              f"{r0.get('LDS_Block_Size')} B, arch VGPR {r0.get('VGPR_Count')}, AGPR "
+              f"{r0.get('Accum_VGPR_Count')}, SGPR {r0.get('SGPR_Count')}, scratch "
+              f"{r0.get('Scratch_Size')}")
+        print(f"  dispatches {len(d)}; over the last {len(tail)}: mean {statistics.mean(tail):.1f} us, "
+              f"median {statistics.median(tail):.1f}, min {min(tail):.1f}, max {max(tail):.1f}; "
+              f"over all: mean {statistics.mean(d):.1f} us")
+
+
+def summarize_pmc(path):
+    """Counter summary (rocprofv3 --pmc CSV): per counter, the median over the GEMM dispatches
+    (summed over the counter's instances within a dispatch), with the dispatch duration."""
+    import statistics
+    rows = [r for r in _read_counter_csv(path) if "gemm_kernel" in r["Kernel_Name"]]
+    per = {}
+    dur = {}
+    for r in rows:
+        d = int(r["Dispatch_Id"])
+        per.setdefault(d, {}).setdefault(r["Counter_Name"], 0.0)
+        per[d][r["Counter_Name"]] += float(r["Counter_Value"])
+        dur[d] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    names = sorted({n for v in per.values() for n in v})
+    print(f"GEMM dispatches {len(per)}; median duration {statistics.median(dur.values()):.1f} us")
+    for n in names:
+        print(f"  {n:28s} {statistics.median(v[n] for v in per.values()):.4g}")
+
+
 def copy_calibration(torch, mib, reps=3):
     """Plain device-to-device copies of `mib` MiB (the runtime's copy kernel), for counter
     calibration."""
@@ -477,7 +519,18 @@ def main():
                     help="after the runs, copy this many MiB device to device (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--command", default="", help="with --ingest-pmc: the profiling command")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print a kernel-trace summary (CPU only); --last N timed dispatches")
+    ap.add_argument("--summarize-pmc", metavar="COUNTER_CSV",
+                    help="print a counter summary (CPU only)")
+    ap.add_argument("--last", type=int, default=0)
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.last)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.only or "bf16_4096",
                    args.command, args.copy_calib_mib or 1024)
