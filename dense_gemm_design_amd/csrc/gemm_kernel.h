@@ -173,9 +173,13 @@ __device__ __forceinline__ f32x4 load_coherent(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicySC1));
 }
 
+// Two floats to bf16 (round to nearest even), lo in the low half.  Converted as one two-element
+// vector, so that the compiler emits one v_cvt_pk_bf16_f32 for both; element by element it emits
+// one per value plus a shift and an or to combine them.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // One MFMA operand fragment of a lane: 8 bf16 (one 16-byte chunk) or 32 e4m3 (two chunks).
@@ -239,6 +243,15 @@ __device__ __forceinline__ void mfma16_inplace(f32x4 &c, const bf16x8 &b, const 
 __device__ __forceinline__ void mfma16_inplace(f32x4 &c, const i32x8 &b, const i32x8 &a) {
   asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
 }
+// The same MFMAs starting from zero (C operand 0): the first k-step of a work item, which then
+// needs no zeroed accumulators and leaves the previous item's values readable until each block's
+// own first MFMA overwrites it.
+__device__ __forceinline__ void mfma16_zero(f32x4 &c, const bf16x8 &b, const bf16x8 &a) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(b), "v"(a));
+}
+__device__ __forceinline__ void mfma16_zero(f32x4 &c, const i32x8 &b, const i32x8 &a) {
+  asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=a"(c) : "v"(b), "v"(a));
+}
 
 // Accumulator block of a configuration and the MFMA that updates it.
 template <class CFG>
@@ -252,12 +265,18 @@ __device__ __forceinline__ void mfma_blk(acc_t<CFG> &c, const typename FragT<CFG
   else
     mfma16_inplace(c, b, a);
 }
+template <class CFG>
+__device__ __forceinline__ void mfma_blk_zero(acc_t<CFG> &c, const typename FragT<CFG::DT>::type &b,
+                                              const typename FragT<CFG::DT>::type &a) {
+  static_assert(CFG::MI == 16, "16 x 16 blocks");
+  mfma16_zero(c, b, a);
+}
 
 // Wait states where the compiler cannot see an MFMA written as inline asm (mfma16_inplace), so
 // its hazard recognizer inserts none.  Two places need them, both once per work item:
 //  * after the accumulators are zeroed (VALU / accumulator-register writes) and before the first
 //    MFMA reads them as its C operand: the ISA's dependency table asks for a few wait states
-//    there;
+//    there (not in kernels whose first k-step starts from a zero C operand, mfma16_zero);
 //  * after the last MFMA of the k-loop and before anything else reads its result (the epilogue's
 //    accumulator reads, the Stream-K partial stores): an MFMA of P passes (four cycles each)
 //    needs a little over P wait states before a non-MFMA instruction may read what it wrote.
@@ -1891,6 +1910,128 @@ gemm_kernel_wide(KernelArgs args) {
       publish_amax<CFG::WAVES>(args.amax, ec.am, smem + CFG::LDS_BYTES, wave, lane);
 }
 
+// The staged bf16 output of a finished whole tile, written during the wave's next work item's
+// first k-step instead of after its own last one (plain output; 16 x 16 blocks, 128-row
+// sub-tiles).  That k-step's MFMAs start from a zero C operand, so block (f, g) of the finished
+// tile stays in its accumulation registers until the new item's MFMA (f, g) replaces it: just
+// before that MFMA the wave scales the block, converts it to bf16 and writes it into its LDS
+// slice.  The slice holds two rows of blocks (16 sub-tile rows each, row f in half f mod 2,
+// chunks swizzled as in epilogue_wide), so row f - 1 is read back and stored while row f is
+// written into the other half: read j (4 staged rows) before MFMA (f, 2j), its store before MFMA
+// (f, 2j + 2) -- one read (4 VGPRs) in flight at a time, which the e4m3 kernel's registers
+// allow.  The last row goes out after the k-step (finish).  Rows and columns past the edge of C
+// are dropped as in epilogue_wide; a sub-tile wholly past it stores nothing.
+template <class CFG>
+struct DeferredOut {
+  static_assert(CFG::MI == 16 && CFG::WM == 128 && CFG::WN == 128 && CFG::FM == 8,
+                "8 x 8 blocks of 16 x 16");
+  typedef u32x2 __attribute__((address_space(3))) *p64;
+  typedef u32x4 __attribute__((address_space(3))) *p128;
+  __amdgpu_buffer_rsrc_t cr;
+  uint32_t st_off, ldc_b;
+  // LDS byte addresses: the lane's write of block column 0 and read 0 of a half.  Block column
+  // G moves a write's 32-byte pair of chunks to chunk pair (G ^ wrow / 2): bits 5-7 of the
+  // address, set to wrow / 2 here, XOR G; read J moves the read's chunk by 4 J: bits 6-7, XOR J.
+  uint32_t wa, ra;
+  u32x4 v[2];
+
+  __device__ __forceinline__ void init(const KernelArgs &args, lds_t *slice, int lane) {
+    clear(args);
+    const uint32_t base = (uint32_t)(size_t)slice;  // 256-byte aligned
+    const int wrow = lane & 15, kq = lane >> 4;
+    // chunk (2 G + kq / 2) ^ wrow of row wrow, half kq mod 2 of it
+    wa = base + wrow * 256 + ((kq >> 1) ^ (wrow & 1)) * 16 + (wrow >> 1) * 32 + (kq & 1) * 8;
+    // row rrow (+ 4 J), chunk chunk_l ^ rrow (^ 4 J)
+    const int chunk_l = lane & 15, rrow = lane >> 4;
+    ra = base + rrow * 256 + ((chunk_l ^ rrow) * 16);
+    ldc_b = (uint32_t)args.ldc * 2;
+  }
+  // the finished tile this carries: work item w, the wave's sub-tile (wm, wn); lanes whose
+  // columns lie past N (or whose sub-tile lies past the edge of C) store to an offset outside
+  // the buffer range, which drops the store; rows past M lie outside it too
+  __device__ __forceinline__ void set(const KernelArgs &args, const WorkItem &w, int wm, int wn,
+                                      int lane) {
+    const int64_t m0 = (int64_t)w.m * CFG::BM + wm * CFG::WM;
+    const int64_t n0 = (int64_t)w.n * CFG::BN + wn * CFG::WN;
+    const bool inside = m0 < args.M && n0 < args.N;
+    const int64_t origin = inside ? m0 * args.ldc + n0 : 0;
+    cr = make_rsrc(args.C + origin * 2, (args.M * args.ldc - origin) * 2);
+    const int chunk_l = lane & 15, rrow = lane >> 4;
+    const bool ok = inside && n0 + chunk_l * 8 < args.N;
+    st_off = ok ? (uint32_t)rrow * ldc_b + chunk_l * 16 : kOOB;
+  }
+  // nothing to carry: the stores go to an empty buffer range, which drops them
+  __device__ __forceinline__ void clear(const KernelArgs &args) {
+    cr = make_rsrc(args.C, 0);
+    st_off = 0;
+  }
+  // Start of the k-step: the compiler may not form the addresses of all the step's writes and
+  // row offsets ahead of time (it would hold them in registers the step does not have).
+  __device__ __forceinline__ void begin() {
+    asm volatile("" : "+v"(wa), "+v"(ra));
+    asm volatile("" : "+s"(ldc_b));
+  }
+  template <int F, int G>
+  __device__ __forceinline__ void write(const f32x4 &blk, float alpha) {
+    const f32x4 x = quad_of<true>(blk, 0) * alpha;
+    *(p64)(size_t)((wa ^ (G * 32)) + (F % 2) * 4096) =
+        u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+  }
+  template <int F, int J>
+  __device__ __forceinline__ u32x4 read() {
+    return *(p128)(size_t)((ra ^ (J * 64)) + ((F % 2) * 4 + J) * 1024);
+  }
+  template <int F, int J>
+  __device__ __forceinline__ void store(const u32x4 &x) {
+    __builtin_amdgcn_raw_buffer_store_b128(x, cr, st_off, (uint32_t)(F * 16 + J * 4) * ldc_b, 0);
+  }
+  // beside the new item's MFMA (f, g), before it: rows 0-6 go back out during rows 1-7
+  template <int F, int G>
+  __device__ __forceinline__ void slot(const f32x4 &blk, float alpha) {
+    if constexpr (F >= 1 && G % 2 == 0) {
+      if constexpr (G >= 2)
+        store<F - 1, G / 2 - 1>(v[(G / 2 - 1) % 2]);
+      else if constexpr (F >= 2)
+        store<F - 2, 3>(v[1]);  // the last read of row F - 2, issued before MFMA (F - 1, 6)
+      v[(G / 2) % 2] = read<F - 1, G / 2>();
+    }
+    write<F, G>(blk, alpha);
+  }
+  // the whole tile at once (the worker's last): the same steps without the MFMAs
+  template <class ACC>
+  __device__ __forceinline__ void flush(const ACC &acc, float alpha) {
+    begin();
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (
+          [&] {
+            constexpr int f = I / CFG::FN, g = I % CFG::FN;
+            slot<f, g>(acc[f][g], alpha);
+            __builtin_amdgcn_sched_barrier(0);
+          }(),
+          ...);
+    }(std::make_integer_sequence<int, CFG::FM * CFG::FN>());
+    finish();
+  }
+  // after the k-step: the last row
+  __device__ __forceinline__ void finish() {
+    constexpr int F = CFG::FM - 1;
+    store<F - 1, 3>(v[1]);
+    const u32x4 x0 = read<F, 0>(), x1 = read<F, 1>(), x2 = read<F, 2>(), x3 = read<F, 3>();
+    store<F, 0>(x0);
+    store<F, 1>(x1);
+    store<F, 2>(x2);
+    store<F, 3>(x3);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+};
+
+// stands in for DeferredOut where a kernel never defers its output
+struct NoDeferredOut {
+  __device__ __forceinline__ void begin() {}
+  template <int F, int G, class BLK>
+  __device__ __forceinline__ void slot(const BLK &, float) {}
+};
+
 // ---- wide-wave kernel, one MFMA depth per k-tile (e4m3 16 x 16 x 128) ------------------------
 //
 // The wide-wave schedule for k-tiles exactly one MFMA deep.  A k-step's fragments then fill 128
@@ -1996,19 +2137,32 @@ gemm_kernel_wide1(KernelArgs args) {
 #pragma unroll
   for (int f = 0; f < FM; ++f) read_a(fa[f], 0, f);
 
+  // the previous tile's staged output, carried into the next item's first k-step
+  constexpr bool DEFER = FUSE == FUSE_OFF && CFG::WM == 128 && CFG::WN == 128;
+  std::conditional_t<DEFER, DeferredOut<CFG>, NoDeferredOut> dout;
+  if constexpr (DEFER) dout.init(args, slice, lane);
+
   // k-step c on B buffer P: MFMA i = (f, g) = (i / FN, i % FN); after MFMA i: the handshake
   // (i = HS - 1), A[f] of step c+1 (i = last of row f, from the handshake on), B reads of step
-  // c+1 into buffer P^1 and the loads of step c+S, both spread over the slots after the handshake
-  auto kstep = [&](auto p_c, auto acc_ref) {
+  // c+1 into buffer P^1 and the loads of step c+S, both spread over the slots after the handshake.
+  // An item's first k-step (FIRST) starts its MFMAs from zero; with EPI, the previous tile's
+  // block (f, g) goes to the LDS slice just before MFMA (f, g) replaces it.
+  acc_t<CFG> acc[FM][FN];
+  auto kstep = [&](auto p_c, auto first_c, auto epi_c) {
     constexpr int P = decltype(p_c)::value;
-    auto &acc = *acc_ref;
+    constexpr bool FIRST = decltype(first_c)::value, EPI = decltype(epi_c)::value;
     const int nstage = (c + 1) & (CFG::STAGES - 1);
+    if constexpr (EPI) dout.begin();
     [&]<int... I>(std::integer_sequence<int, I...>) {
       (
           [&] {
             constexpr int i = I;
             constexpr int f = i / FN, g = i % FN;
-            mfma_blk<CFG>(acc[f][g], fb[P][g], fa[f]);
+            if constexpr (EPI) dout.template slot<f, g>(acc[f][g], alpha);
+            if constexpr (FIRST)
+              mfma_blk_zero<CFG>(acc[f][g], fb[P][g], fa[f]);
+            else
+              mfma_blk<CFG>(acc[f][g], fb[P][g], fa[f]);
             if constexpr (i + 1 == HS) handshake(c + 1);
             if constexpr (i + 1 >= HS) {
               if constexpr (g == FN - 1) read_a(fa[f], nstage, f);
@@ -2029,7 +2183,18 @@ gemm_kernel_wide1(KernelArgs args) {
     ++c;
   };
 
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using ON = std::true_type;
+  using OFF = std::false_type;
   int seq = 0;
+  if constexpr (DEFER) {
+    // the first item's first k-step writes these (unset) values out to nowhere
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+      for (int g = 0; g < FN; ++g) acc[f][g] = __builtin_nondeterministic_value(acc[f][g]);
+  }
   while (cvalid) {
     if ((args.flags & KF_TRACE) && tid == 0 && seq < args.trace_cap) {
       int *t = args.trace + ((int64_t)b * args.trace_cap + seq) * 8;
@@ -2037,39 +2202,55 @@ gemm_kernel_wide1(KernelArgs args) {
       t[4] = cw.n; t[5] = cw.kb; t[6] = cw.ke; t[7] = cw.role;
     }
     ++seq;
-    acc_t<CFG> acc[FM][FN];
-#pragma unroll
-    for (int f = 0; f < FM; ++f)
-#pragma unroll
-      for (int g = 0; g < FN; ++g) acc[f][g] = acc_t<CFG>{};
-    // 24 wait states: the zeroed accumulators reach the first (inline-asm) MFMA's C operand
-    mfma_wait_states();
-    // k-steps in pairs, so each item starts on B buffer 0; after an odd last step the next item's
-    // B sits in buffer 1 and moves over (once per item)
-    int k = cw.kb;
+    // Every item has at least one k-step (these kernels are not planned for K = 0).  The first
+    // starts on B buffer 0, the rest go in pairs (1, 0); after an odd count the next item's B
+    // sits in buffer 1 and moves over (once per item).
+    // The first k-step always does the staged output's work: a copy of the step without it,
+    // taken when nothing is carried, costs more registers than the step has; with nothing
+    // carried (dout clear) the stores go nowhere.
+    kstep(I0(), ON(), std::bool_constant<DEFER>());
+    if constexpr (DEFER) dout.finish();
+    int k = cw.kb + 1;
     for (; k + 2 <= cw.ke; k += 2) {
-      kstep(std::integral_constant<int, 0>(), &acc);
-      kstep(std::integral_constant<int, 1>(), &acc);
+      kstep(I1(), OFF(), OFF());
+      kstep(I0(), OFF(), OFF());
     }
     if (k < cw.ke) {
-      kstep(std::integral_constant<int, 0>(), &acc);
+      kstep(I1(), OFF(), OFF());
+    } else {
 #pragma unroll
       for (int g = 0; g < FN; ++g) fb[0][g] = fb[1][g];
     }
-    // 24 wait states (> 8 passes + the ISA's margin): the last MFMAs' results are written before
-    // the epilogue or the partial store reads them
-    mfma_wait_states();
-    if (cw.role != ROLE_WHOLE) {  // a Stream-K split: its partial, reduced after all MAC work
-      wide_partial_store<CFG>(args, cw, acc, b, wm, wn, lane, tid);
-    } else if (CFG::WM == 128 && args.out_bf16) {  // staged through the wave's LDS slice
-      if constexpr (CFG::WM == 128)
-        epilogue_wide<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
-    } else if constexpr (FUSE != FUSE_OFF) {
-      epilogue_direct_fused<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, ec);
+    WorkItem nw;
+    const bool nvalid = cursor_next(args.sp, ccur, nw);
+    if (DEFER && args.out_bf16 && cw.role == ROLE_WHOLE) {
+      // staged bf16 output: carried into the next item's first k-step, which writes it out from
+      // the accumulators as they are; the worker's last tile goes out here, the same way
+      if constexpr (DEFER) {
+        dout.set(args, cw, wm, wn, lane);
+        if (!nvalid) {
+          mfma_wait_states();  // the last MFMAs' results are written before they are read
+          dout.flush(acc, alpha);
+        }
+      }
     } else {
-      epilogue_direct<CFG>(args, cw, acc, alpha, wm, wn, lane, ec);
+      if constexpr (DEFER) dout.clear(args);
+      // 24 wait states (> 8 passes + the ISA's margin): the last MFMAs' results are written
+      // before the epilogue or the partial store reads them
+      mfma_wait_states();
+      if (cw.role != ROLE_WHOLE) {  // a Stream-K split: its partial, reduced after all MAC work
+        wide_partial_store<CFG>(args, cw, acc, b, wm, wn, lane, tid);
+      } else if (!DEFER && CFG::WM == 128 && args.out_bf16) {  // staged through the LDS slice
+        if constexpr (!DEFER && CFG::WM == 128)
+          epilogue_wide<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
+      } else if constexpr (FUSE != FUSE_OFF) {
+        epilogue_direct_fused<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, ec);
+      } else {
+        epilogue_direct<CFG>(args, cw, acc, alpha, wm, wn, lane, ec);
+      }
     }
-    cvalid = cursor_next(args.sp, ccur, cw);
+    cw = nw;
+    cvalid = nvalid;
   }
   if (args.sp.sk_tiles > 0) {
     // second pass over this unit's splits: reduce its share of each tile it touched

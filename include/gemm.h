@@ -202,7 +202,8 @@ typedef struct gemm_plan *gemm_handle;
  *   Stream-K lock chain, or a kernel flag other than GEMM_FLAG_WIDE -- returns
  *   GEMM_ERR_UNSUPPORTED);
  *   layout_a ROW and layout_b COL (both operands K-contiguous);
- *   K * sizeof(element) a multiple of 16 bytes; N a multiple of 8;
+ *   K * sizeof(element) a multiple of 16 bytes and at most 2^30; N a multiple of 8 and at most
+ *   2^22 (the kernels address the rows of an output tile with 32-bit byte offsets);
  *   M, N arbitrary otherwise (ragged tiles are masked), K ragged in the last k-tile.
  * Needs a visible GPU only when num_workers == 0 (it then queries the CU count). */
 int gemm_create(const gemm_desc *desc, gemm_handle *out);

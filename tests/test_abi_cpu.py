@@ -95,6 +95,7 @@ def create(**kw):
     (dict(layout_b=L.GEMM_ROW_MAJOR), L.GEMM_ERR_UNSUPPORTED),
     (dict(K=100), L.GEMM_ERR_UNSUPPORTED),            # 200-byte rows: not a multiple of 16
     (dict(N=100), L.GEMM_ERR_UNSUPPORTED),            # output rows must be 8-element multiples
+    (dict(N=(1 << 22) + 8), L.GEMM_ERR_UNSUPPORTED),  # beyond 32-bit offsets inside a tile
     (dict(bm=64, bn=64), L.GEMM_ERR_UNSUPPORTED),     # no such tile kernel
     (dict(bm=256, bn=256, bk=16), L.GEMM_ERR_UNSUPPORTED),
     (dict(dtype_ab=L.GEMM_FP8_E4M3, K=8), L.GEMM_ERR_UNSUPPORTED),

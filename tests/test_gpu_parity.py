@@ -368,6 +368,41 @@ def test_no_writes_past_c(dev, M, N, K):
             assert_within_tolerance(got, ref, op, f"canary {M}x{N}x{K} {out} {flags:#x}")
 
 
+@pytest.mark.parametrize("M,N,K", [(776, 520, 1040), (300, 264, 128), (1, 8, 64), (520, 776, 256)])
+def test_fp8_wide_staged_output(dev, M, N, K):
+    """The e4m3 wide-wave kernel on 256 x 256 tiles writes a tile's bf16 output during the
+    worker's next item's first k-step (the worker's last tile after its own k-loop).  Over ragged
+    edges (waves wholly past M or N), one-k-step items (K <= 128) and several items per worker:
+    nothing is written past C, both outputs are within tolerance of the oracle, and every bf16
+    output is the round-to-nearest-even bf16 of the same launch's f32 output (alpha * Acc in both:
+    the same accumulators, scaled the same way) bit for bit."""
+    op = gi.make_operands(M, N, K, "e4m3", ("normal", 1.0), ("normal", 1.0), seed=7 * M + N + K)
+    ref = reference(op)
+    A, B, sa, sb = to_device(op, torch, dev)
+    canary_bytes = 4 << 20
+    got = {}
+    for out in ("f32", "bf16"):
+        eb = 2 if out == "bf16" else 4
+        buf = torch.empty(M * N * eb + canary_bytes, dtype=torch.uint8, device=dev)
+        buf.fill_(0xA5)
+        plan = L.Plan(L.make_desc(M, N, K, L.GEMM_FP8_E4M3,
+                                  L.GEMM_BF16 if out == "bf16" else L.GEMM_F32,
+                                  L.GEMM_MAP_GROUPED_M, 2, L.GEMM_SCHED_PERSISTENT, 2,
+                                  256, 256, 0, L.GEMM_FLAG_WIDE))
+        assert plan.info.kernel == 3 and plan.info.bm == 256 and plan.info.bk == 128
+        st = plan.run_raw(A.data_ptr(), B.data_ptr(), buf.data_ptr(), sa.data_ptr(), sb.data_ptr())
+        assert st == L.GEMM_OK
+        torch.cuda.synchronize()
+        assert bool((buf[M * N * eb:] == 0xA5).all()), f"{out}: wrote past C"
+        C = buf[:M * N * eb].view(torch.bfloat16 if out == "bf16" else torch.float32)
+        got[out] = C.reshape(M, N).clone()
+        assert_within_tolerance(C.float().cpu().numpy().astype(np.float64).reshape(M, N), ref, op,
+                                f"fp8 wide {M}x{N}x{K} {out}")
+    want = got["f32"].to(torch.bfloat16).view(torch.int16)
+    diff = int((got["bf16"].view(torch.int16) != want).sum())
+    assert diff == 0, f"{diff} bf16 outputs differ from the bf16 rounding of the f32 outputs"
+
+
 WIDE_SK = [
     # id, M, N, K, dtype, out, workers, mapping, G; 256 x 256 tiles, Stream-K
     ("bf16_all_split", 512, 512, 16384, "bf16", "f32", 8, L.GEMM_MAP_LINEAR_N, 1),
