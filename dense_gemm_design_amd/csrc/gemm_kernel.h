@@ -1354,7 +1354,8 @@ struct WideBias {
 };
 
 // Y of accumulator quad (f, g) of a 16 x 16-block sub-tile: alpha * Acc + bias, then the
-// activation and, inside C, the amax.
+// activation and, inside C, the amax (past the edge of C a row bias still reaches the columns past
+// N, and a column bias the rows past M, so Y there need not be zero).
 template <class CFG, int ACT>
 __device__ __forceinline__ f32x4 wide_fused_quad(const KernelArgs &args, const acc_t<CFG> &blk,
                                                  float alpha, f32x4 bcol, const WideBias<CFG> &bias,
@@ -1447,8 +1448,12 @@ __device__ __forceinline__ void epilogue_wide(const KernelArgs &args, const Work
     for (int p = 0; p < CFG::FM / 2; ++p) {
 #pragma unroll
       for (int g = 0; g < CFG::FN; ++g) {
-        f32x4 bnext;
-        if constexpr (FUSE != FUSE_OFF) bnext = bias.col((g + 1) % CFG::FN);
+        // the next column block's bias (the first again for the next round); none after the
+        // last quad: a load whose value nobody reads stays in flight past the epilogue, and the
+        // next k-loop then waits on it before it reuses the registers it targets
+        f32x4 bnext = bq;
+        if constexpr (FUSE != FUSE_OFF)
+          if (p + 1 < CFG::FM / 2 || g + 1 < CFG::FN) bnext = bias.col((g + 1) % CFG::FN);
 #pragma unroll
         for (int fp = 0; fp < 2; ++fp) {
           f32x4 v;
@@ -1496,7 +1501,46 @@ __device__ __forceinline__ void epilogue_direct(const KernelArgs &args, const Wo
 // bf16 takes this path only on 64-wide sub-tiles, whose rows are too short to stage).
 // Column-block major: the lane's row biases (one per row block) are loaded first, a column
 // block's bias quad one block ahead of its use.  Without a bias of that orientation the loads go
-// to an empty buffer range and read zero, so no branch sits in the loop.
+// to an empty buffer range and read zero, so no branch sits in the loop.  One copy of the loop per
+// output type (OUT: element bytes), and the stores go through a buffer range that starts at the
+// sub-tile's origin: rows past M fall outside it, and a column block past N gets an offset past
+// its end, so a store outside C is dropped without a branch around it.
+template <class CFG, int ACT, int OUT>
+__device__ __forceinline__ void direct_fused_stores(const KernelArgs &args,
+                                                    const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
+                                                    float alpha, int64_t m0, int64_t n0, int lane,
+                                                    const WideBias<CFG> &bias, EpiCtx &ec) {
+  const int64_t origin = m0 * args.ldc + n0;
+  const __amdgpu_buffer_rsrc_t cr =
+      make_rsrc(args.C + origin * OUT, (args.M * args.ldc - origin) * OUT);
+  uint32_t row_b = (uint32_t)args.ldc * OUT;
+  // formed here, not ahead of the kernel's item loop: the row offsets below would otherwise be
+  // hoisted there and held in scalar registers through the whole kernel
+  asm volatile("" : "+s"(row_b));
+  const uint32_t lane_off = (uint32_t)(lane & 15) * row_b + (uint32_t)(lane >> 4) * 4 * OUT;
+  f32x4 bq = bias.col(0);
+#pragma unroll
+  for (int g = 0; g < CFG::FN; ++g) {
+    // no load after the last column block (see epilogue_wide)
+    const f32x4 bnext = g + 1 < CFG::FN ? bias.col(g + 1) : bq;
+    const uint32_t off = ((bias.ok >> (16 + g)) & 1u) ? lane_off + g * 16 * OUT : kOOB;
+#pragma unroll
+    for (int f = 0; f < CFG::FM; ++f) {
+      const f32x4 v = wide_fused_quad<CFG, ACT>(args, acc[f][g], alpha, bq, bias, ec, f, g);
+      const uint32_t soff = (uint32_t)(f * 16) * row_b;
+      if constexpr (OUT == 1)
+        __builtin_amdgcn_raw_buffer_store_b32(pack_e4m3x4(v * ec.inv_d), cr, off, soff, 0);
+      else if constexpr (OUT == 2)
+        __builtin_amdgcn_raw_buffer_store_b64(
+            u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, cr, off, soff, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), cr, off, soff, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bq = bnext;
+  }
+}
+
 template <class CFG, int ACT>
 __device__ __forceinline__ void epilogue_direct_fused(const KernelArgs &args, const WorkItem &w,
                                                       const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
@@ -1506,31 +1550,43 @@ __device__ __forceinline__ void epilogue_direct_fused(const KernelArgs &args, co
   const int64_t m0 = (int64_t)w.m * CFG::BM + wm * CFG::WM;
   const int64_t n0 = (int64_t)w.n * CFG::BN + wn * CFG::WN;
   if (m0 >= args.M || n0 >= args.N) return;  // the wave's sub-tile lies past the edge of C
-  const int64_t mb = m0 + (lane & 15), nb = n0 + (lane >> 4) * 4;
   WideBias<CFG> bias;
   bias.init(args, m0, n0, lane);
-  f32x4 bq = bias.col(0);
+  if constexpr (CFG::DT == DT_FP8) {
+    if (args.out_fp8)
+      direct_fused_stores<CFG, ACT, 1>(args, acc, alpha, m0, n0, lane, bias, ec);
+    else if (args.out_bf16)
+      direct_fused_stores<CFG, ACT, 2>(args, acc, alpha, m0, n0, lane, bias, ec);
+    else
+      direct_fused_stores<CFG, ACT, 4>(args, acc, alpha, m0, n0, lane, bias, ec);
+  } else {
+    // The bf16 kernels keep one loop that picks the store per quad (flat addresses, skipped
+    // outside C): with the three copies above, the compiler put vmcnt waits inside the 256 x 224
+    // fused kernel's k-loop (its bias + GELU workload measured 4 % slower), while none of the
+    // benchmarked workloads sends a bf16 kernel down this path.
+    const int64_t mb = m0 + (lane & 15), nb = n0 + (lane >> 4) * 4;
+    f32x4 bq = bias.col(0);
 #pragma unroll
-  for (int g = 0; g < CFG::FN; ++g) {
-    const f32x4 bnext = bias.col((g + 1) % CFG::FN);
-    const int64_t n = nb + g * 16;
+    for (int g = 0; g < CFG::FN; ++g) {
+      const f32x4 bnext = g + 1 < CFG::FN ? bias.col(g + 1) : bq;
+      const int64_t n = nb + g * 16;
 #pragma unroll
-    for (int f = 0; f < CFG::FM; ++f) {
-      const int64_t m = mb + f * 16;
-      const bool ok = bias.inside(f, g);
-      const f32x4 v = wide_fused_quad<CFG, ACT>(args, acc[f][g], alpha, bq, bias, ec, f, g);
-      if (ok) {
-        if (args.out_fp8)
-          *(uint32_t *)(args.C + m * args.ldc + n) = pack_e4m3x4(v * ec.inv_d);
-        else if (args.out_bf16)
-          *(u32x2 *)(args.C + (m * args.ldc + n) * 2) =
-              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        else
-          *(f32x4 *)(args.C + (m * args.ldc + n) * 4) = v;
+      for (int f = 0; f < CFG::FM; ++f) {
+        const int64_t m = mb + f * 16;
+        const f32x4 v = wide_fused_quad<CFG, ACT>(args, acc[f][g], alpha, bq, bias, ec, f, g);
+        if (bias.inside(f, g)) {
+          if (args.out_fp8)
+            *(uint32_t *)(args.C + m * args.ldc + n) = pack_e4m3x4(v * ec.inv_d);
+          else if (args.out_bf16)
+            *(u32x2 *)(args.C + (m * args.ldc + n) * 2) =
+                u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          else
+            *(f32x4 *)(args.C + (m * args.ldc + n) * 4) = v;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      bq = bnext;
     }
-    bq = bnext;
   }
 }
 
