@@ -530,9 +530,10 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   const int eb = d.dtype_ab == GEMM_BF16 ? 2 : 1;
   if ((d.K * eb) % 16 != 0) return GEMM_ERR_UNSUPPORTED;   // 16-byte rows for the LDS loads
   if (d.N % 8 != 0) return GEMM_ERR_UNSUPPORTED;           // 16-byte output rows
-  // the staged bf16 stores address a wave's output sub-tile with 32-bit byte offsets from its
-  // origin: its last row (127 rows down, under 2^30 bytes here) stays inside the buffer range,
-  // and an out-of-range offset (0x80000000 plus a row offset) stays below 2^32
+  // the buffer stores of C address a wave's output sub-tile with 32-bit byte offsets from its
+  // origin: its last element (127 rows of up to 4-byte elements down: under 2^31 - 16 bytes
+  // here) stays inside the buffer range, and an out-of-range offset (0x80000000 plus a row
+  // offset) stays below 2^32
   if (d.N > ((int64_t)1 << 22)) return GEMM_ERR_UNSUPPORTED;
   if (d.K * eb > (int64_t)1 << 30) return GEMM_ERR_UNSUPPORTED;
 
