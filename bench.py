@@ -536,8 +536,8 @@ def main():
                    args.command, args.copy_calib_mib or 1024)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the multi-GPU "
-              "sharding is a design note, not an implemented path.", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU only (asked for {args.gpus}); sharding "
+              "across GPUs is a design note, not an implemented path.", file=sys.stderr)
         sys.exit(2)
 
     import torch

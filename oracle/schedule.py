@@ -38,10 +38,10 @@ Reading where the pages are open (each is listed in the design doc):
     neither -> middle;
   * the data-parallel tiles run first, then the Stream-K tail.
 
-The XCD remap is this build's own MI355X design, not the pages': with X L2 domains (XCDs) and
+The XCD remap is the library's own MI355X design, not the pages': with X L2 domains (XCDs) and
 workgroups dealt to them round-robin, the worker id that workgroup b runs under is chosen so that
 every XCD owns a contiguous run of worker ids.  It is enumerated here from that statement.  For a
-grouped mapping whose data-parallel waves are whole G x (P/G) blocks of one strip, the build
+grouped mapping whose data-parallel waves are whole G x (P/G) blocks of one strip, the planner
 instead gives each XCD a box of every wave's block (the analogue, inside one launch, of the
 "DeepGEMM on SM90" page's 2D blocking), when a box needs fewer operand strips than a contiguous
 run; xcd_box_assignment enumerates that from its statement, by geometry.
