@@ -244,7 +244,7 @@ constexpr double kMinPartialWave = 1.0 / 1.3;
 // MFMA efficiency of whole launches at the held clock (bench workloads, profiles/)
 double kernel_efficiency(int kind, int bm, int bn, int dt) {
   if (kind == KIND_WIDE && bm == 128) return dt == DT_BF16 ? 0.56 : 0.55;
-  // 256 x 224: 2 % below 256 x 256 at whole waves (8192 x 14336 x 4096 bf16, one box: 1,367
+  // 256 x 224: 2 % below 256 x 256 at whole waves (8192 x 14336 x 4096 bf16, one board: 1,367
   // against 1,397 TFLOP/s) -- 12.5 % fewer MACs per operand byte
   if (kind == KIND_WIDE && bn == 224) return dt == DT_BF16 ? 0.74 : 0.77;
   if (kind == KIND_WIDE) return dt == DT_BF16 ? 0.76 : 0.79;
