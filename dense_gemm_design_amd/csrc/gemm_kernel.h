@@ -1439,7 +1439,7 @@ __device__ __forceinline__ void epilogue_wide(const KernelArgs &args, const Work
     // fused: column-block major inside each round of two row blocks, so one column bias quad
     // serves both (loaded one column block ahead)
     WideBias<CFG> bias;
-    f32x4 bq;
+    f32x4 bq = {0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (FUSE != FUSE_OFF) {
       bias.init(args, m0, n0, lane);
       bq = bias.col(0);

@@ -139,8 +139,8 @@ def xcd_box_assignment(mode, Mt, Nt, G, P, X=8):
     It applies to the grouped mappings when every strip holds G tile rows (columns), every wave of
     P consecutive tasks lies inside one strip (so it is a G x P/G block: G across the strip, P/G
     along it), X divides P, and the P/X tasks an XCD runs per wave divide G or are a multiple of
-    it.  The box is r across x c along with r | G, c | P/G, r c = P/X, r + c smallest (the taller
-    box on a tie); it is used only when r + c is below the number of operand strips (distinct
+    it.  The box is r across x c along with r | G, c | P/G, r c = P/X, r + c smallest (the wider
+    box, smaller r, on a tie); it is used only when r + c is below the number of operand strips (distinct
     rows plus distinct columns) of a contiguous run of P/X tasks.  XCD x (the workgroups b with
     b mod X = x, the k-th of them being b = x + k X) takes the box at block position
     (x mod (G/r), x div (G/r)) -- counted in boxes across, then along -- and its k-th workgroup
@@ -160,12 +160,11 @@ def xcd_box_assignment(mode, Mt, Nt, G, P, X=8):
 
     first = [across_along(t) for t in range(per)]
     contiguous = len({a for a, _ in first}) + len({b for _, b in first})
-    boxes = [(r + per // r, -r) for r in range(1, G + 1)
+    boxes = [(r + per // r, r) for r in range(1, G + 1)
              if G % r == 0 and per % r == 0 and (P // G) % (per // r) == 0]
     if not boxes:
         return None
-    strips, neg_r = min(boxes)
-    r = -neg_r
+    strips, r = min(boxes)
     c = per // r
     if strips >= contiguous:
         return None

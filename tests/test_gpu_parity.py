@@ -231,14 +231,14 @@ def test_device_trace_matches_enumeration(dev, sched, workers, tile, mapping, G,
 @pytest.mark.parametrize("mapping", [L.GEMM_MAP_GROUPED_M, L.GEMM_MAP_GROUPED_N])
 def test_device_trace_xcd_box(dev, mapping):
     """A plan on the XCD box remap (Grouped-M/N(8) on 16 x 8 tiles of 128, 64 workers: every
-    wave is an 8 x 8 block, each XCD takes a 4 x 2 box of it): the kernel's recorded work items
+    wave is an 8 x 8 block, each XCD takes a 2 x 4 box of it): the kernel's recorded work items
     equal the CPU replay and the oracle's enumeration, and the product is within tolerance."""
     M, N, K = (2048, 1024, 256) if mapping == L.GEMM_MAP_GROUPED_M else (1024, 2048, 256)
     op = gi.make_operands(M, N, K, "bf16", seed=31)
     C, plan, ws = run_gpu(op, torch, dev, "f32", mapping, 8, L.GEMM_SCHED_PERSISTENT, 64, 128,
                           flags=L.GEMM_FLAG_TRACE)
     info = plan.info
-    assert (info.xcd_box_r, info.xcd_box_c) == (4, 2)
+    assert (info.xcd_box_r, info.xcd_box_c) == (2, 4)
     raw = ws.cpu().numpy()[info.trace_offset:].view(np.int32)[: info.grid * info.trace_capacity * 8]
     rec = raw.reshape(info.grid, info.trace_capacity, 8)
     got = [tuple(int(x) for x in r) for w in range(info.grid) for r in rec[w]

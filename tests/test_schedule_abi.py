@@ -37,8 +37,8 @@ CASES = [
     (1000, 3000, 512, L.GEMM_BF16, 128, L.GEMM_MAP_MORTON, 1, L.GEMM_SCHED_PERSISTENT, 24, True),
     (4096, 14336, 4096, L.GEMM_BF16, 256, L.GEMM_MAP_MORTON, 1, L.GEMM_SCHED_STATIC, 0, True),
     (1280, 640, 1024, L.GEMM_BF16, 128, L.GEMM_MAP_MORTON, 1, L.GEMM_SCHED_STREAMK, 40, True),
-    # XCD box remap: waves that are whole G x P/G blocks of one strip (G = 8, P = 64: 4 x 2
-    # boxes per XCD instead of 8 x 1 columns); the fp8 8192^3 case above takes 8 x 4 boxes
+    # XCD box remap: waves that are whole G x P/G blocks of one strip (G = 8, P = 64: 2 x 4
+    # boxes per XCD instead of 8 x 1 columns); the fp8 8192^3 case above takes 4 x 8 boxes
     (4096, 2048, 256, L.GEMM_BF16, 256, L.GEMM_MAP_GROUPED_M, 8, L.GEMM_SCHED_PERSISTENT, 64, True),
     (2048, 4096, 256, L.GEMM_BF16, 256, L.GEMM_MAP_GROUPED_N, 8, L.GEMM_SCHED_PERSISTENT, 64, True),
     (4096, 2048, 256, L.GEMM_BF16, 256, L.GEMM_MAP_GROUPED_M, 8, L.GEMM_SCHED_PERSISTENT, 64, False),
@@ -188,8 +188,8 @@ def test_streamk_groups_fixup_mode_and_workspace():
 
 
 @pytest.mark.parametrize("M,N,K,dt,G,P,box", [
-    (8192, 8192, 8192, L.GEMM_FP8_E4M3, 16, 256, (8, 4)),    # 16 x 2 runs -> 8 x 4 boxes
-    (4096, 2048, 256, L.GEMM_BF16, 8, 64, (4, 2)),
+    (8192, 8192, 8192, L.GEMM_FP8_E4M3, 16, 256, (4, 8)),    # 16 x 2 runs -> 4 x 8 boxes
+    (4096, 2048, 256, L.GEMM_BF16, 8, 64, (2, 4)),
     (4096, 14336, 4096, L.GEMM_BF16, 8, 256, (0, 0)),        # 256 x 224 tiles: runs are 8 x 4
     (4096, 4096, 4096, L.GEMM_BF16, 8, 256, (0, 0)),         # a wave spans two strips
 ])

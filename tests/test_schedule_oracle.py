@@ -322,8 +322,8 @@ def test_xcd_box_hand_worked():
 
 def test_xcd_box_geometry_fp8_8192():
     """fp8 8192^3 on 256 x 256 tiles, Grouped-M(16), 256 workers: in every wave each XCD's 32
-    tiles form an 8 x 4 box (12 operand strips, against 18 for runs of 32 tasks), and every task
-    is taken exactly once."""
+    tiles form a 4 x 8 box (12 operand strips, against 18 for runs of 32 tasks; 8 x 4 ties and
+    loses to the wider box), and every task is taken exactly once."""
     Mt = Nt = 32
     items = S.enumerate_schedule(8192, 8192, 8192, 256, 256, 128, S.GROUPED_M, 16, S.PERSISTENT,
                                  P=256)
@@ -332,8 +332,8 @@ def test_xcd_box_geometry_fp8_8192():
         for x in range(8):
             mine = [(w.m, w.n) for w in items if w.worker % 8 == x and w.seq == wave]
             ms, ns = {m for m, _ in mine}, {n for _, n in mine}
-            assert len(mine) == 32 and len(ms) == 8 and len(ns) == 4
-            assert max(ms) - min(ms) == 7 and max(ns) - min(ns) == 3   # a rectangle
+            assert len(mine) == 32 and len(ms) == 4 and len(ns) == 8
+            assert max(ms) - min(ms) == 3 and max(ns) - min(ns) == 7   # a rectangle
     contiguous = S.enumerate_schedule(8192, 8192, 8192, 256, 256, 128, S.GROUPED_M, 16,
                                       S.PERSISTENT, P=256, xcd_box=False)
     for x in range(8):
