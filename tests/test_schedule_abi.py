@@ -42,7 +42,36 @@ CASES = [
     (4096, 2048, 256, L.GEMM_BF16, 256, L.GEMM_MAP_GROUPED_M, 8, L.GEMM_SCHED_PERSISTENT, 64, True),
     (2048, 4096, 256, L.GEMM_BF16, 256, L.GEMM_MAP_GROUPED_N, 8, L.GEMM_SCHED_PERSISTENT, 64, True),
     (4096, 2048, 256, L.GEMM_BF16, 256, L.GEMM_MAP_GROUPED_M, 8, L.GEMM_SCHED_PERSISTENT, 64, False),
+    # grouped plans whose waves span several strips (keep the contiguous runs): two strips of
+    # 8 x 4 tiles per wave of 64, and a Stream-K wave of four 2 x 5 strips
+    (2048, 512, 256, L.GEMM_BF16, 128, L.GEMM_MAP_GROUPED_M, 8, L.GEMM_SCHED_PERSISTENT, 64, True),
+    (512, 2048, 256, L.GEMM_BF16, 128, L.GEMM_MAP_GROUPED_N, 8, L.GEMM_SCHED_PERSISTENT, 64, True),
+    (1280, 640, 2048, L.GEMM_BF16, 128, L.GEMM_MAP_GROUPED_M, 2, L.GEMM_SCHED_STREAMK, 40, True),
 ]
+
+
+@pytest.mark.parametrize("mapping", [L.GEMM_MAP_GROUPED_M, L.GEMM_MAP_GROUPED_N])
+def test_grouped_remap_sweep_matches_oracle(mapping):
+    """Every small grouped plan (tile grids up to 16 x 16, G up to 8, waves of 8 to 128 workers,
+    persistent and Stream-K) enumerates exactly the oracle's schedule, whichever remap applies."""
+    n_box = 0
+    for mt in (2, 4, 6, 8, 16):
+        for nt in (2, 4, 5, 8, 16):
+            for G in (1, 2, 3, 4, 8):
+                for P in (8, 16, 24, 40, 64, 128):
+                    for sched in (L.GEMM_SCHED_PERSISTENT, L.GEMM_SCHED_STREAMK):
+                        M, N = mt * 128, nt * 128
+                        plan = L.Plan(L.make_desc(M, N, 512, mapping=mapping, group=G,
+                                                  sched=sched, num_workers=P, bm=128, bn=128))
+                        info = plan.info
+                        n_box += info.xcd_box_r > 0
+                        want = S.enumerate_schedule(M, N, 512, 128, 128, info.bk, MAP[mapping],
+                                                    G, SCHED[sched], P=info.grid,
+                                                    sk_groups=info.sk_groups)
+                        assert plan.schedule() == [
+                            (w.worker, w.seq, w.tile, w.m, w.n, w.k_begin, w.k_end, w.role)
+                            for w in want], (mt, nt, G, P, sched)
+    assert n_box > 0
 
 
 @pytest.mark.parametrize("case", CASES)
@@ -187,16 +216,28 @@ def test_streamk_groups_fixup_mode_and_workspace():
     assert p1.streamk_mode == 1 and p8.streamk_mode == 0
 
 
-@pytest.mark.parametrize("M,N,K,dt,G,P,box", [
-    (8192, 8192, 8192, L.GEMM_FP8_E4M3, 16, 256, (4, 8)),    # 16 x 2 runs -> 4 x 8 boxes
-    (4096, 2048, 256, L.GEMM_BF16, 8, 64, (2, 4)),
-    (4096, 14336, 4096, L.GEMM_BF16, 8, 256, (0, 0)),        # 256 x 224 tiles: runs are 8 x 4
-    (4096, 4096, 4096, L.GEMM_BF16, 8, 256, (0, 0)),         # a wave spans two strips
+@pytest.mark.parametrize("M,N,K,dt,G,P,sched,box", [
+    # 16 x 2 runs -> 4 x 8 boxes
+    (8192, 8192, 8192, L.GEMM_FP8_E4M3, 16, 256, L.GEMM_SCHED_PERSISTENT, (4, 8)),
+    (4096, 2048, 256, L.GEMM_BF16, 8, 64, L.GEMM_SCHED_PERSISTENT, (2, 4)),
+    # 256 x 256 tiles: 16 x 56, strips of 448 tasks are no multiple of the 256-task wave
+    (4096, 14336, 4096, L.GEMM_BF16, 8, 256, L.GEMM_SCHED_PERSISTENT, (0, 0)),
+    # 256 x 224 tiles: 16 x 64; runs of 32 are 8 x 4 slabs, no box needs fewer strips
+    (4096, 14336, 4096, L.GEMM_BF16, 8, 256, L.GEMM_SCHED_AUTO, (0, 0)),
+    # a wave spans two strips
+    (4096, 4096, 4096, L.GEMM_BF16, 8, 256, L.GEMM_SCHED_PERSISTENT, (0, 0)),
+    # 2 x 20 tiles, Grouped-M(2), 40 workers: runs of 5 tasks are neither a slab nor a column
+    (256, 2560, 256, L.GEMM_BF16, 2, 40, L.GEMM_SCHED_PERSISTENT, (0, 0)),
 ])
-def test_planner_xcd_box(M, N, K, dt, G, P, box):
+def test_planner_xcd_box(M, N, K, dt, G, P, sched, box):
     """The plan reports the box the oracle's rule picks, and none where it does not apply."""
+    bm = 128 if P == 40 else 0
     plan = L.Plan(L.make_desc(M, N, K, dtype_ab=dt, mapping=L.GEMM_MAP_GROUPED_M, group=G,
-                              sched=L.GEMM_SCHED_PERSISTENT, num_workers=P))
-    assert (plan.info.xcd_box_r, plan.info.xcd_box_c) == box
-    ids = S.xcd_box_assignment(S.GROUPED_M, plan.info.mt, plan.info.nt, G, plan.info.grid)
+                              sched=sched, num_workers=P, bm=bm, bn=bm))
+    info = plan.info
+    assert (info.xcd_box_r, info.xcd_box_c) == box
+    ids = S.xcd_box_assignment(S.GROUPED_M, info.mt, info.nt, G, info.grid)
     assert (ids is None) == (box == (0, 0))
+    if ids is not None:   # and the planner's first wave is the oracle's
+        first = [(w[0], w[2]) for w in plan.schedule() if w[1] == 0]
+        assert sorted(first) == list(enumerate(ids))
