@@ -6,6 +6,7 @@ oracle.gemm_ref, in the order of the forward template of the "H100 Kernel Design
 section 12 (12.2 steps 2-5 and 12.3 template 1):
 
     Z = alpha * Acc           gemm_ref's result (alpha = s_a * s_b for e4m3 operands, else 1)
+    Z = Z + beta * S          an optional source matrix S (M x N), 12.1 item 1, 12.2 step 2
     Z = Z + bias              one value per row (length M) or one per column (length N)
     Y = act(Z)                ReLU, GELU or SiLU (12.1 item 3)
     amax = max |Y|            collected at the output-scaling step (12.2 step 5, 12.1 item 8)
@@ -51,13 +52,20 @@ def activation(z, act):
     return {"relu": relu, "gelu": gelu, "silu": silu}[act](z)
 
 
-def apply(c, bias_row=None, bias_col=None, act=None):
-    """Y = act(C + bias) for C = alpha * Acc (M x N float64); returns (Z, Y).
+def apply(c, bias_row=None, bias_col=None, act=None, source=None, beta=0.0):
+    """Y = act(C + beta * S + bias) for C = alpha * Acc (M x N float64); returns (Z, Y).
 
+    source: M x N values S (taken exactly, as float64), scaled by beta -- the linear combination
+    alpha * Acc + beta * C of section 12.1 item 1, formed first (section 12.2 step 2);
     bias_row: length-M vector added to every column (Z[m, n] += bias_row[m]);
     bias_col: length-N vector added to every row (Z[m, n] += bias_col[n]).
     """
     z = np.array(c, dtype=np.float64, copy=True)
+    if source is not None:
+        s = np.asarray(source, dtype=np.float64)
+        if s.shape != z.shape:
+            raise ValueError("the source must be M x N")
+        z = z + float(beta) * s
     if bias_row is not None and bias_col is not None:
         raise ValueError("one bias vector at most")
     if bias_row is not None:
@@ -85,17 +93,20 @@ def quantize_e4m3(y, scale_d):
     return encode_e4m3_array(np.asarray(y, dtype=np.float64) / float(scale_d))
 
 
-def tolerance(y_ref, z_ref, k, max_abs_a, max_abs_b, out="bf16"):
+def tolerance(y_ref, z_ref, k, max_abs_a, max_abs_b, out="bf16", s_ref=None):
     """Per-element bound on |Y_gpu - Y_ref| before any output rounding, plus the output cast.
 
     The accumulation error of Z is bounded as in oracle.tolerance (1e-3 sqrt(K) max|a| max|b|)
-    with a 2e-6 |Z| allowance for the rounded additions of alpha and the bias; the activations
+    with a 2e-6 |Z| allowance for the rounded additions of alpha and the bias, and 2e-6 |beta S|
+    more for the source term s_ref = beta * S (its rounded product and sum); the activations
     are Lipschitz with constant below 1.2 (ReLU 1, SiLU 1.1, GELU 1.13) and are evaluated to a
     few fp32 ulps.  A bf16 output adds its own rounding, 4e-3 |Y_ref|; f32 output adds nothing
     more, and an e4m3 output is checked on the code grid instead (quantized_bounds).
     """
     z = np.abs(np.asarray(z_ref, dtype=np.float64))
     base = 1.2 * (1e-3 * math.sqrt(k) * float(max_abs_a) * float(max_abs_b) + 2e-6 * z) + 1e-6 * z
+    if s_ref is not None:
+        base = base + 1.2 * 2e-6 * np.abs(np.asarray(s_ref, dtype=np.float64))
     if out == "bf16":
         return base + 4e-3 * np.abs(np.asarray(y_ref, dtype=np.float64))
     return base

@@ -86,6 +86,25 @@ def test_bias_is_added_before_the_activation():
     assert np.all(z == 1.0) and np.allclose(y, math.e / (1.0 + math.e), rtol=1e-15)
 
 
+def test_source_term_hand_worked():
+    """Z = alpha Acc + beta S, then the bias, then the activation, worked by hand on all-ones
+    operands (Acc = K = 16): with S = [[3, 1], [-40, 0]], beta = 0.5 and a column bias
+    (0.25, -17), Z = [[16 + 1.5 + 0.25, 16 + 0.5 - 17], [16 - 20 + 0.25, 16 + 0 - 17]]
+    = [[17.75, -0.5], [-3.75, -1]]; ReLU keeps 17.75 alone."""
+    C = _ones(2, 2, 16)
+    S = np.array([[3.0, 1.0], [-40.0, 0.0]])
+    z, y = epi.apply(C, bias_col=np.array([0.25, -17.0]), act="relu", source=S, beta=0.5)
+    assert np.array_equal(z, [[17.75, -0.5], [-3.75, -1.0]])
+    assert np.array_equal(y, [[17.75, 0.0], [0.0, 0.0]])
+    # beta = 0 is the product alone; beta = -1 with S = C cancels it: Z is the bias
+    assert np.array_equal(epi.apply(C, source=S, beta=0.0)[0], C)
+    z, y = epi.apply(C, bias_row=np.array([1.0, -1.0]), act="gelu", source=C, beta=-1.0)
+    assert np.array_equal(z, [[1.0, 1.0], [-1.0, -1.0]])
+    assert abs(y[0, 0] - PHI_TABLE[1.0]) < 5e-5 and abs(y[1, 0] + (1 - PHI_TABLE[1.0])) < 5e-5
+    with pytest.raises(ValueError):
+        epi.apply(C, source=np.zeros((2, 3)), beta=1.0)
+
+
 def test_amax_closed_form():
     M, N, K = 2, 8, 16
     C = _ones(M, N, K)
@@ -139,3 +158,7 @@ def test_epilogue_tolerance_values():
     assert np.allclose(t, [1.2 * (1e-3 * 64 * 0.5 + 2e-6) + 1e-6])
     t = epi.tolerance(np.array([2.0]), np.array([1.0]), 4096, 1.0, 0.5, out="bf16")
     assert np.allclose(t, [1.2 * (1e-3 * 64 * 0.5 + 2e-6) + 1e-6 + 8e-3])
+    # a source term beta S adds 1.2 * 2e-6 |beta S|
+    t = epi.tolerance(np.array([2.0]), np.array([1.0]), 4096, 1.0, 0.5, out="f32",
+                      s_ref=np.array([-100.0]))
+    assert np.allclose(t, [1.2 * (1e-3 * 64 * 0.5 + 2e-6) + 1e-6 + 1.2 * 2e-4])
