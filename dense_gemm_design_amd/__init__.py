@@ -12,7 +12,8 @@ from ._lib import (GemmDesc, GemmError, Plan, make_desc, load,  # noqa: F401
                    GEMM_FLAG_NO_XCD_REMAP, GEMM_FLAG_STREAMK_CHAIN, GEMM_FLAG_PINGPONG,
                    GEMM_FLAG_COOPERATIVE, GEMM_FLAG_WIDE,
                    GEMM_EPI_BIAS_ROW, GEMM_EPI_BIAS_COL, GEMM_EPI_RELU, GEMM_EPI_GELU,
-                   GEMM_EPI_SILU, GEMM_EPI_AMAX, GemmEpilogueArgs)
+                   GEMM_EPI_SILU, GEMM_EPI_AMAX, GEMM_EPI_SOURCE_F32, GEMM_EPI_SOURCE_BF16,
+                   GemmEpilogueArgs)
 
 KERNEL_NAMES = {0: "cooperative", 1: "ping-pong", 3: "wide-wave"}  # gemm_plan_info.kernel
 MAPPINGS = {"linear_n": GEMM_MAP_LINEAR_N, "linear_m": GEMM_MAP_LINEAR_M,
@@ -26,15 +27,17 @@ OUT_DTYPES = {"f32": GEMM_F32, "bf16": GEMM_BF16, "e4m3": GEMM_FP8_E4M3}
 
 def gemm(A, B, out_dtype="f32", scale_a=None, scale_b=None, mapping="grouped_m", group=8,
          sched="auto", tile=0, flags=0, bias_row=None, bias_col=None, activation=None,
-         scale_d=None, amax=None, group_n=0, sk_groups=0):
-    """D = epilogue(alpha * A x B) for torch device tensors: A (M, K) row-major; B given as (N, K),
+         scale_d=None, amax=None, group_n=0, sk_groups=0, source=None, beta=1.0):
+    """D = epilogue(alpha * A x B + beta * source) for torch device tensors: A (M, K) row-major; B given as (N, K),
     i.e. the K x N operand in column-major storage; bf16 or uint8-coded e4m3 (then scale_a /
     scale_b are one-element float32 device tensors).  Optional fused epilogue: a float32 bias per
     row (M) or per column (N), an activation ("relu", "gelu", "silu"), amax (a one-element float32
     device tensor the kernel max-combines max |Y| into), and out_dtype "e4m3" (uint8 codes of
     Y / scale_d, scale_d a one-element float32 device tensor).  tile: 0 (the planner's), an int
     for square tiles, or (bm, bn), e.g. (256, 224).  sk_groups: Stream-K groups (0 = the
-    planner's count, 1-8) of a plan with a Stream-K band.  Returns C (M, N): float32,
+    planner's count, 1-8) of a plan with a Stream-K band.  source: an (M, N) float32 or
+    bfloat16 device tensor added as beta * source before the bias (such plans run on the
+    cooperative kernel).  Returns C (M, N): float32,
     bfloat16, or uint8 e4m3 codes.  Shapes, element types, contiguity and devices are checked
     before anything is launched (ValueError)."""
     import torch
@@ -58,6 +61,8 @@ def gemm(A, B, out_dtype="f32", scale_a=None, scale_b=None, mapping="grouped_m",
     epi |= GEMM_EPI_BIAS_ROW if bias_row is not None else 0
     epi |= GEMM_EPI_BIAS_COL if bias_col is not None else 0
     epi |= GEMM_EPI_AMAX if amax is not None else 0
+    if source is not None:
+        epi |= GEMM_EPI_SOURCE_F32 if source.dtype == torch.float32 else GEMM_EPI_SOURCE_BF16
     bm, bn = tile if isinstance(tile, tuple) else (tile, tile)
     desc = make_desc(M, N, K, GEMM_FP8_E4M3 if fp8 else GEMM_BF16, OUT_DTYPES[out_dtype],
                      MAPPINGS[mapping], group, SCHEDS[sched], 0, bm, bn, 0, flags,
@@ -69,5 +74,5 @@ def gemm(A, B, out_dtype="f32", scale_a=None, scale_b=None, mapping="grouped_m",
     if plan.workspace_bytes:
         ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=A.device)
     plan.run(A, B, C, scale_a, scale_b, ws, bias=bias_row if bias_row is not None else bias_col,
-             scale_d=scale_d, amax=amax)
+             scale_d=scale_d, amax=amax, source=source, beta=beta if source is not None else 0.0)
     return C

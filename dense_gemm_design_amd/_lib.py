@@ -35,6 +35,8 @@ GEMM_EPI_RELU = 0x4
 GEMM_EPI_GELU = 0x8
 GEMM_EPI_SILU = 0x10
 GEMM_EPI_AMAX = 0x20
+GEMM_EPI_SOURCE_F32 = 0x40
+GEMM_EPI_SOURCE_BF16 = 0x80
 
 EXPORTS = ("gemm_create", "gemm_workspace_bytes", "gemm_plan_get", "gemm_run", "gemm_run_ex",
            "gemm_run_noalloc", "gemm_destroy", "gemm_schedule_enumerate", "gemm_rank_configs", "gemm_status_string")
@@ -53,7 +55,7 @@ class GemmDesc(ctypes.Structure):
 
 class GemmEpilogueArgs(ctypes.Structure):
     _fields_ = [("bias", ctypes.c_void_p), ("scale_d", ctypes.c_void_p),
-                ("amax", ctypes.c_void_p)]
+                ("amax", ctypes.c_void_p), ("source", ctypes.c_void_p), ("beta", ctypes.c_float)]
 
 
 class GemmWorkItem(ctypes.Structure):
@@ -205,57 +207,63 @@ class Plan:
                                workspace or None, workspace_bytes, stream or None)
 
     def run_ex_raw(self, A, B, C, scale_a=0, scale_b=0, bias=0, scale_d=0, amax=0, workspace=0,
-                   workspace_bytes=0, stream=0, epi_null=False):
+                   workspace_bytes=0, stream=0, epi_null=False, source=0, beta=0.0):
         """gemm_run_ex with raw integer device pointers (epi_null passes a NULL epilogue-args
         pointer); returns the gemm_status."""
         epi = None if epi_null else ctypes.byref(
-            GemmEpilogueArgs(bias or None, scale_d or None, amax or None))
+            GemmEpilogueArgs(bias or None, scale_d or None, amax or None, source or None,
+                             float(beta)))
         return load().gemm_run_ex(self.handle, A, B, C, scale_a or None, scale_b or None, epi,
                                   workspace or None, workspace_bytes, stream or None)
 
     def validate(self, A, B, C, scale_a=None, scale_b=None, workspace=None, bias=None,
-                 scale_d=None, amax=None):
+                 scale_d=None, amax=None, source=None, beta=0.0):
         """Checks torch tensors against the plan before any pointer reaches the library: the
         kernels size their buffer ranges from M, N, K, not from the tensors, so a tensor that is
         too small, strided or of the wrong element type would be read or written past its end.
         Raises ValueError naming the first problem; returns None."""
         validate_operands(self.desc, A, B, C, scale_a, scale_b, workspace, bias, scale_d, amax,
-                          self.workspace_bytes)
+                          self.workspace_bytes, source, beta)
 
     def run_noalloc_raw(self, A, B, C, scale_a=0, scale_b=0, bias=0, scale_d=0, amax=0,
-                        stream=0, epi_null=False):
+                        stream=0, epi_null=False, source=0, beta=0.0):
         """gemm_run_noalloc with raw integer device pointers; returns the gemm_status."""
         epi = None if epi_null else ctypes.byref(
-            GemmEpilogueArgs(bias or None, scale_d or None, amax or None))
+            GemmEpilogueArgs(bias or None, scale_d or None, amax or None, source or None,
+                             float(beta)))
         return load().gemm_run_noalloc(self.handle, A, B, C, scale_a or None, scale_b or None,
                                        epi, stream or None)
 
     def run_noalloc(self, A, B, C, scale_a=None, scale_b=None, stream=None, bias=None,
-                    scale_d=None, amax=None):
+                    scale_d=None, amax=None, source=None, beta=0.0):
         """gemm_run_noalloc on torch tensors: as run(), with the library's own scratch as the
         workspace (nothing is allocated).  The tensors are checked first (ValueError)."""
         import torch
-        validate_operands(self.desc, A, B, C, scale_a, scale_b, None, bias, scale_d, amax, 0)
+        validate_operands(self.desc, A, B, C, scale_a, scale_b, None, bias, scale_d, amax, 0,
+                          source, beta)
         if stream is None:
             stream = torch.cuda.current_stream()
         ptr = lambda t: t.data_ptr() if t is not None else 0
         st = self.run_noalloc_raw(ptr(A), ptr(B), ptr(C), ptr(scale_a), ptr(scale_b), ptr(bias),
-                                  ptr(scale_d), ptr(amax), stream.cuda_stream)
+                                  ptr(scale_d), ptr(amax), stream.cuda_stream,
+                                  source=ptr(source), beta=beta)
         _check(st, "gemm_run_noalloc")
 
     def run(self, A, B, C, scale_a=None, scale_b=None, workspace=None, stream=None, bias=None,
-            scale_d=None, amax=None):
-        """A, B, C, scales, workspace, bias, amax: torch tensors on the GPU; stream:
-        torch.cuda.Stream.  bias / scale_d / amax feed the fused epilogue (gemm_run_ex).  The
-        tensors are checked first (validate); a mismatch raises ValueError."""
+            scale_d=None, amax=None, source=None, beta=0.0):
+        """A, B, C, scales, workspace, bias, amax, source: torch tensors on the GPU; stream:
+        torch.cuda.Stream.  bias / scale_d / amax / source and beta feed the fused epilogue
+        (gemm_run_ex); source may be C itself.  The tensors are checked first (validate); a
+        mismatch raises ValueError."""
         import torch
-        self.validate(A, B, C, scale_a, scale_b, workspace, bias, scale_d, amax)
+        self.validate(A, B, C, scale_a, scale_b, workspace, bias, scale_d, amax, source, beta)
         if stream is None:
             stream = torch.cuda.current_stream()
         ptr = lambda t: t.data_ptr() if t is not None else 0
         ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
         st = self.run_ex_raw(ptr(A), ptr(B), ptr(C), ptr(scale_a), ptr(scale_b), ptr(bias),
-                             ptr(scale_d), ptr(amax), ptr(workspace), ws_len, stream.cuda_stream)
+                             ptr(scale_d), ptr(amax), ptr(workspace), ws_len, stream.cuda_stream,
+                             source=ptr(source), beta=beta)
         _check(st, "gemm_run_ex")
 
 
@@ -266,7 +274,7 @@ def _dtype_names(torch):
 
 
 def validate_operands(desc, A, B, C, scale_a=None, scale_b=None, workspace=None, bias=None,
-                      scale_d=None, amax=None, workspace_bytes=0):
+                      scale_d=None, amax=None, workspace_bytes=0, source=None, beta=0.0):
     """The checks of Plan.validate for a GemmDesc: shapes, element types and contiguity first
     (so they can be exercised on CPU tensors), then that every tensor is on one GPU."""
     import torch
@@ -307,6 +315,10 @@ def validate_operands(desc, A, B, C, scale_a=None, scale_b=None, workspace=None,
             need(scale_d, "scale_d", (torch.float32,), numel=1)
         if desc.epilogue & GEMM_EPI_AMAX:
             need(amax, "amax", (torch.float32,), numel=1)
+        if desc.epilogue & (GEMM_EPI_SOURCE_F32 | GEMM_EPI_SOURCE_BF16) and float(beta) != 0.0:
+            f32 = desc.epilogue & GEMM_EPI_SOURCE_F32
+            need(source, "source", (torch.float32,) if f32 else (torch.bfloat16, torch.int16),
+                 numel=M * N)
         if workspace_bytes:
             if workspace is None:
                 raise ValueError(f"this plan needs a workspace of {workspace_bytes} bytes")

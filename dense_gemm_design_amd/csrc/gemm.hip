@@ -205,17 +205,21 @@ constexpr int kTraceCap = 64;
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t align_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
-// Known GEMM_EPI_* bits, at most one bias vector and at most one activation.
+constexpr uint32_t kEpiSource = GEMM_EPI_SOURCE_F32 | GEMM_EPI_SOURCE_BF16;
+
+// Known GEMM_EPI_* bits, at most one source, one bias vector and one activation.
 bool epilogue_valid(uint32_t e) {
   const uint32_t all = GEMM_EPI_BIAS_ROW | GEMM_EPI_BIAS_COL | GEMM_EPI_RELU | GEMM_EPI_GELU |
-                       GEMM_EPI_SILU | GEMM_EPI_AMAX;
+                       GEMM_EPI_SILU | GEMM_EPI_AMAX | kEpiSource;
   if (e & ~all) return false;
+  if (__builtin_popcount(e & kEpiSource) > 1) return false;
   if (__builtin_popcount(e & (GEMM_EPI_BIAS_ROW | GEMM_EPI_BIAS_COL)) > 1) return false;
   return __builtin_popcount(e & (GEMM_EPI_RELU | GEMM_EPI_GELU | GEMM_EPI_SILU)) <= 1;
 }
 static_assert(GEMM_EPI_BIAS_ROW == EPI_BIAS_ROW && GEMM_EPI_BIAS_COL == EPI_BIAS_COL &&
                   GEMM_EPI_RELU == EPI_RELU && GEMM_EPI_GELU == EPI_GELU &&
-                  GEMM_EPI_SILU == EPI_SILU && GEMM_EPI_AMAX == EPI_AMAX,
+                  GEMM_EPI_SILU == EPI_SILU && GEMM_EPI_AMAX == EPI_AMAX &&
+                  GEMM_EPI_SOURCE_F32 == EPI_SRC_F32 && GEMM_EPI_SOURCE_BF16 == EPI_SRC_BF16,
               "epilogue bits shared with the kernels");
 
 // ---- kernel-configuration heuristic -----------------------------------------------------------
@@ -355,7 +359,12 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
                              {KIND_WIDE, 128, 128, GEMM_SCHED_STREAMK},
                              {KIND_COOP, 128, 128, GEMM_SCHED_STREAMK},
                              {KIND_WIDE, 256, 256, GEMM_SCHED_STREAMK},
-                             {KIND_COOP, 256, 256, GEMM_SCHED_STREAMK}};
+                             {KIND_COOP, 256, 256, GEMM_SCHED_STREAMK},
+                             {KIND_COOP, 256, 256, GEMM_SCHED_PERSISTENT}};
+  // a source matrix (Z = alpha Acc + beta S) is read by the cooperative kernel only: its plans
+  // rank the cooperative candidates, the others every candidate but the last
+  const bool source = (d.epilogue & kEpiSource) != 0;
+  const double es = !source ? 0.0 : (d.epilogue & GEMM_EPI_SOURCE_F32) ? 4.0 : 2.0;
   int cus = 0, dev = 0;
   if (d.num_workers == 0) {
     if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
@@ -366,6 +375,7 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
   const bool blocked = d.mapping == GEMM_MAP_BLOCKED;
   out.clear();
   for (const ModelCand &c : cands) {
+    if (source ? c.kind != KIND_COOP : &c == &cands[std::size(cands) - 1]) continue;
     if (c.kind != KIND_COOP && d.K == 0) continue;  // the data-parallel kernels need K > 0
     const KernelEntry *e = nullptr;
     for (const KernelEntry &k : kKernels)
@@ -414,7 +424,7 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
       r.group_n = d.group_n;
       choose_box(Mt, Nt, P / X, r.group, r.group_n);
     }
-    const double bytes_l2 = t * (kk * (bm + bn) * eb + bm * bn * ec);
+    const double bytes_l2 = t * (kk * (bm + bn) * eb + bm * bn * (ec + es));
     const double bytes_local = t * (kk * (bm + bn) * eb + kk * (bm * wgn + bn * wgm) * eb + bm * bn * ec);
     r.cycles_l2 = bytes_l2 / (ncu * kL2BytesPerClk);
     r.cycles_local = bytes_local / (ncu * kLdsBytesPerClk);
@@ -434,7 +444,7 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
     }
     const double stage_bytes = (bm + bn) * e->bk * eb;
     r.cycles_fixed = stage_bytes * (e->stages - 1) / kL2BytesPerClk + kLatencyClk +
-                     items * (bm * bn * ec / kL2BytesPerClk + kLatencyClk / 2);
+                     items * (bm * bn * (ec + es) / kL2BytesPerClk + kLatencyClk / 2);
     if (sk > 0) {  // separate reduction: every split writes its partial, the reduction reads it
       const double units_per_tile = std::ceil((double)P / sk);
       r.cycles_fixed += 2.0 * sk * units_per_tile * bm * bn * 4.0 / kDeviceBytesPerClk + kLatencyClk;
@@ -555,6 +565,9 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   // the fused epilogue runs on the wide-wave and cooperative kernels
   const bool fused = d.epilogue != 0 || d.dtype_c == GEMM_FP8_E4M3;
   if (fused && force_kind == KIND_PP) return GEMM_ERR_UNSUPPORTED;
+  // a source matrix is read by the cooperative kernel only
+  const bool source = (d.epilogue & kEpiSource) != 0;
+  if (source && force_kind == KIND_WIDE) return GEMM_ERR_UNSUPPORTED;
 
   // Tile shape and scheduler: the cost model when everything is left to the planner, else
   // 256 x 256 unless asked otherwise or the problem has too few big tiles.
@@ -583,7 +596,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
       by_kind[e.kind] = &e;
   const KernelEntry *k = by_kind[force_kind >= 0 ? force_kind : KIND_COOP];
   // tile shapes only the wide-wave kernel has (which needs K > 0, like every data-parallel kernel)
-  if (!k && force_kind < 0 && d.K > 0) k = by_kind[KIND_WIDE];
+  if (!k && force_kind < 0 && d.K > 0 && !source) k = by_kind[KIND_WIDE];
   if (!k) return GEMM_ERR_UNSUPPORTED;  // the schedule is planned with this one
   // rows of one tile must stay addressable by 32-bit buffer offsets
   if ((int64_t)bm * d.K * eb >= 0x7FFFFFF0ll || (int64_t)bn * d.K * eb >= 0x7FFFFFF0ll)
@@ -609,7 +622,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     // data-parallel 128 x 128 tiles and 30 % slower for Stream-K)
     const bool wide_next = force_kind == KIND_WIDE ||
                            (force_kind < 0 && d.K > 0 && by_kind[KIND_WIDE] &&
-                            model_kind != KIND_COOP);
+                            model_kind != KIND_COOP && !source);
     if (wide_next) per_cu = 1;
     workers = cus * per_cu;
   }
@@ -621,13 +634,15 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   // Data-parallel work runs on the wide-wave kernel unless a kernel is asked for, or the cost
   // model picked another one (its grid was sized for that kernel above); so does Stream-K work,
   // unless it needs the lock chain (checked below, once the band is known).
-  if (force_kind < 0 && d.K > 0 && (sched == GEMM_SCHED_STATIC || sched == GEMM_SCHED_PERSISTENT) &&
+  if (force_kind < 0 && !source && d.K > 0 &&
+      (sched == GEMM_SCHED_STATIC || sched == GEMM_SCHED_PERSISTENT) &&
       (model_kind < 0 || model_kind == KIND_WIDE)) {
     if (by_kind[KIND_WIDE])
       k = by_kind[KIND_WIDE];
     else if (by_kind[KIND_PP] && !fused)
       k = by_kind[KIND_PP];
-  } else if (force_kind < 0 && d.K > 0 && sched == GEMM_SCHED_STREAMK && by_kind[KIND_WIDE] &&
+  } else if (force_kind < 0 && !source && d.K > 0 && sched == GEMM_SCHED_STREAMK &&
+             by_kind[KIND_WIDE] &&
              !(d.flags & GEMM_FLAG_STREAMK_CHAIN) && (model_kind < 0 || model_kind == KIND_WIDE)) {
     k = by_kind[KIND_WIDE];
   }
@@ -814,6 +829,13 @@ int gemm_run_ex(gemm_handle h, const void *A, const void *B, void *C, const floa
   if ((need_bias || need_amax || out_fp8) && !epi) return GEMM_ERR_INVALID_ARG;
   if ((need_bias && !epi->bias) || (need_amax && !epi->amax) || (out_fp8 && !epi->scale_d))
     return GEMM_ERR_INVALID_ARG;
+  // a source bit needs beta; with beta == 0 no source is read
+  const uint32_t src_bit = ebits & kEpiSource;
+  if (src_bit && !epi) return GEMM_ERR_INVALID_ARG;
+  const bool need_source = src_bit && epi->beta != 0.0f;
+  if (need_source && !epi->source) return GEMM_ERR_INVALID_ARG;
+  if (need_source && ((uintptr_t)epi->source & (src_bit == GEMM_EPI_SOURCE_F32 ? 15 : 7)))
+    return GEMM_ERR_ALIGNMENT;
   if ((need_bias && ((uintptr_t)epi->bias & 15)) || (need_amax && ((uintptr_t)epi->amax & 3)) ||
       (out_fp8 && ((uintptr_t)epi->scale_d & 3)))
     return GEMM_ERR_ALIGNMENT;
@@ -835,6 +857,12 @@ int gemm_run_ex(gemm_handle h, const void *A, const void *B, void *C, const floa
   a.C = (char *)C;
   a.scale_a = scale_a;
   a.scale_b = scale_b;
+  if (need_source) {
+    a.src = (const char *)epi->source;
+    a.beta = epi->beta;
+  } else {
+    a.epi &= ~kEpiSource;  // beta == 0: Z = alpha Acc, and nothing is read
+  }
   if (need_bias) a.bias = epi->bias;
   if (need_amax) a.amax = epi->amax;
   if (out_fp8) a.scale_d = epi->scale_d;

@@ -83,7 +83,8 @@ struct KernelArgs {
   const float *scale_d;    // e4m3 output: its dequantisation scale (a code q stands for s_d * q)
   float *amax;             // EPI_AMAX: max |Y| is folded in (atomic max on the float's bits)
   int32_t out_fp8;         // C holds e4m3 codes
-  int32_t pad_;
+  float beta;              // EPI_SRC_*: the source's factor
+  const char *src;         // EPI_SRC_*: S, M x N row-major, ldc elements per row (may be C)
 };
 
 template <int DT_, int BM_, int BN_, int BK_, int WGM_, int WGN_, int STAGES_, int SWZ_,
@@ -451,19 +452,22 @@ __device__ __forceinline__ void store_quad(const KernelArgs &args, int64_t m, in
 }
 
 // ---- fused epilogue ("H100 Kernel Design" lesson, section 12) ------------------------------
-// Z = alpha * Acc + bias, Y = act(Z), amax over Y, then the cast -- for an e4m3 output the code
-// of Y / scale_d -- and the store, in the order of section 12.2 (steps 2 to 7).  Kernels take
-// this path in a fused instantiation, chosen at launch when EPI_* bits or an e4m3 output are
-// asked for; every other launch runs the plain epilogues above and below.  The wide-wave kernels
-// have one fused instantiation per activation (no per-element branch on it); the cooperative
-// kernel has one that reads the activation from the EPI_* bits.
+// Z = alpha * Acc (+ beta * S), + bias, Y = act(Z), amax over Y, then the cast -- for an e4m3
+// output the code of Y / scale_d -- and the store, in the order of section 12.2 (steps 2 to 7).
+// Kernels take this path in a fused instantiation, chosen at launch when EPI_* bits or an e4m3
+// output are asked for; every other launch runs the plain epilogues above and below.  The
+// wide-wave kernels have one fused instantiation per activation (no per-element branch on it);
+// the cooperative kernel has one that reads the activation from the EPI_* bits, and only it
+// reads a source matrix S (the planner gives plans with one to it).
 enum : uint32_t {
   EPI_BIAS_ROW = 0x1u,
   EPI_BIAS_COL = 0x2u,
   EPI_RELU = 0x4u,
   EPI_GELU = 0x8u,
   EPI_SILU = 0x10u,
-  EPI_AMAX = 0x20u
+  EPI_AMAX = 0x20u,
+  EPI_SRC_F32 = 0x40u,
+  EPI_SRC_BF16 = 0x80u
 };
 
 // FUSE template argument: FUSE_OFF = the plain epilogue; ACT_* = fused, with that activation;
@@ -557,6 +561,21 @@ __device__ __forceinline__ void store_quad_fused(const KernelArgs &args, int64_t
                                                  f32x4 v, float alpha, EpiCtx &ec) {
   if (m >= args.M || n >= args.N) return;
   v = v * alpha;
+  if constexpr (ACT == ACT_RT) {
+    // Z = alpha * Acc + beta * S: the source quad is read before this thread writes the same
+    // elements of C, so S may be C itself
+    if (args.epi & EPI_SRC_F32) {
+      const f32x4 s = *(const f32x4 *)(args.src + (m * args.ldc + n) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = fmaf(args.beta, s[e], v[e]);
+    } else if (args.epi & EPI_SRC_BF16) {
+      const u32x2 s = *(const u32x2 *)(args.src + (m * args.ldc + n) * 2);
+      const f32x4 sf = {__uint_as_float(s[0] << 16), __uint_as_float(s[0] & 0xFFFF0000u),
+                        __uint_as_float(s[1] << 16), __uint_as_float(s[1] & 0xFFFF0000u)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = fmaf(args.beta, sf[e], v[e]);
+    }
+  }
   if (args.epi & EPI_BIAS_ROW) v = v + args.bias[m];
   if (args.epi & EPI_BIAS_COL) v = v + *(const f32x4 *)(args.bias + n);
   v = epi_act<ACT>(args.epi, v, ec.am);

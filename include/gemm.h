@@ -96,12 +96,15 @@ typedef enum {
                                               waits on it expire and report GEMM_DEVICE_ERR_SPIN */
 
 /* Fused epilogue operations (gemm_desc.epilogue), "H100 Kernel Design" lesson, section 12: items
- * 2, 3 and 8 of its operation list, in the order of its section 12.2 --
- *   Z = alpha * Acc;  Z += bias;  Y = act(Z);  amax = max |Y|;  D = cast(Y) (e4m3: of Y / scale_d)
+ * 1 (the linear combination with a source matrix), 2, 3 and 8 of its operation list, in the
+ * order of its section 12.2 --
+ *   Z = alpha * Acc + beta * S;  Z += bias;  Y = act(Z);  amax = max |Y|;
+ *   D = cast(Y) (e4m3: of Y / scale_d)
  * -- all applied to the finished accumulators before C is stored once (a Stream-K tile: by the
- * split that writes it, after the full sum).  At most one bias bit and one activation bit.
- * A plan with epilogue bits or an e4m3 output runs on the wide-wave or the cooperative kernel
- * (GEMM_FLAG_PINGPONG with them: GEMM_ERR_UNSUPPORTED). */
+ * split that writes it, after the full sum).  At most one source bit, one bias bit and one
+ * activation bit.  A plan with epilogue bits or an e4m3 output runs on the wide-wave or the
+ * cooperative kernel (GEMM_FLAG_PINGPONG with them: GEMM_ERR_UNSUPPORTED); a plan with a source
+ * bit runs on the cooperative kernel (GEMM_FLAG_WIDE with one: GEMM_ERR_UNSUPPORTED). */
 #define GEMM_EPI_BIAS_ROW 0x1u  /* Z[m][n] += bias[m]; bias holds M floats                     */
 #define GEMM_EPI_BIAS_COL 0x2u  /* Z[m][n] += bias[n]; bias holds N floats                     */
 #define GEMM_EPI_RELU 0x4u      /* Y = max(Z, 0)                                                  */
@@ -112,6 +115,10 @@ typedef enum {
                                    float already there (an atomic max on the bit pattern), so the
                                    caller sets *amax (to 0, or a running value) before the run;
                                    NaN elements of Y are not propagated                          */
+#define GEMM_EPI_SOURCE_F32 0x40u  /* Z = alpha * Acc + beta * S[m][n], S an M x N row-major
+                                      fp32 matrix (gemm_epilogue_args.source, beta): C itself
+                                      for C = alpha A B + beta C with an fp32 C, or any other */
+#define GEMM_EPI_SOURCE_BF16 0x80u /* the same with S in bf16 (C itself for a bf16 C)          */
 
 /* Problem description.  0 in an "auto" field lets the planner choose. */
 typedef struct gemm_desc {
@@ -241,6 +248,13 @@ typedef struct gemm_epilogue_args {
                             nearest-even, saturated to +-448); else ignored                    */
   float *amax;           /* with GEMM_EPI_AMAX: one float, 4-byte aligned, read and updated by
                             the kernel (see GEMM_EPI_AMAX); else ignored                        */
+  const void *source;    /* with a GEMM_EPI_SOURCE_* bit and beta != 0: S, M x N row-major (N
+                            elements per row) of the bit's type, 16-byte aligned (fp32) or
+                            8-byte aligned (bf16); it may be C itself (each element of S is read
+                            before the same element of C is written, by the same thread).  With
+                            beta == 0 the kernels read no source (a NaN in S does not reach C)
+                            and the pointer may be NULL.  Else ignored                         */
+  float beta;            /* with a GEMM_EPI_SOURCE_* bit: the source's factor; else ignored     */
 } gemm_epilogue_args;
 
 /* gemm_run with the fused epilogue's operands.  `epi` may be NULL when the plan needs none of

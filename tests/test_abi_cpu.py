@@ -124,7 +124,15 @@ def create(**kw):
     (dict(flags=L.GEMM_FLAG_WIDE, K=0), L.GEMM_ERR_UNSUPPORTED),
     (dict(flags=L.GEMM_FLAG_WIDE | L.GEMM_FLAG_COOPERATIVE), L.GEMM_ERR_INVALID_ARG),
     # fused epilogue
-    (dict(epilogue=0x40), L.GEMM_ERR_INVALID_ARG),                       # unknown bit
+    (dict(epilogue=0x100), L.GEMM_ERR_INVALID_ARG),                      # unknown bit
+    (dict(epilogue=L.GEMM_EPI_SOURCE_F32 | L.GEMM_EPI_SOURCE_BF16), L.GEMM_ERR_INVALID_ARG),
+    (dict(epilogue=L.GEMM_EPI_SOURCE_F32), L.GEMM_OK),                   # cooperative kernel
+    (dict(epilogue=L.GEMM_EPI_SOURCE_BF16 | L.GEMM_EPI_GELU, sched=L.GEMM_SCHED_STREAMK),
+     L.GEMM_OK),
+    (dict(epilogue=L.GEMM_EPI_SOURCE_F32, K=0), L.GEMM_OK),
+    (dict(epilogue=L.GEMM_EPI_SOURCE_F32, flags=L.GEMM_FLAG_WIDE), L.GEMM_ERR_UNSUPPORTED),
+    (dict(epilogue=L.GEMM_EPI_SOURCE_F32, flags=L.GEMM_FLAG_PINGPONG), L.GEMM_ERR_UNSUPPORTED),
+    (dict(epilogue=L.GEMM_EPI_SOURCE_F32, bm=256, bn=224), L.GEMM_ERR_UNSUPPORTED),
     (dict(epilogue=L.GEMM_EPI_BIAS_ROW | L.GEMM_EPI_BIAS_COL), L.GEMM_ERR_INVALID_ARG),
     (dict(epilogue=L.GEMM_EPI_RELU | L.GEMM_EPI_GELU), L.GEMM_ERR_INVALID_ARG),
     (dict(epilogue=L.GEMM_EPI_SILU | L.GEMM_EPI_GELU), L.GEMM_ERR_INVALID_ARG),
@@ -228,6 +236,32 @@ def test_fused_epilogue_plans():
         assert a.info.kernel in (0, 3), (M, N, K)
 
 
+def test_source_plans_run_on_the_cooperative_kernel():
+    """Only the cooperative kernel reads a source matrix: every plan with one runs it, whatever
+    the planner would pick without it, and the cost model ranks cooperative candidates only (a
+    plan without a source keeps its candidate set)."""
+    for M, N, K, sched in ((4096, 4096, 4096, L.GEMM_SCHED_AUTO),
+                           (4096, 4096, 4096, L.GEMM_SCHED_PERSISTENT),
+                           (4096, 14336, 4096, L.GEMM_SCHED_AUTO),
+                           (512, 512, 65536, L.GEMM_SCHED_STREAMK),
+                           (512, 512, 65536, L.GEMM_SCHED_AUTO), (300, 264, 0, L.GEMM_SCHED_STATIC)):
+        for src in (L.GEMM_EPI_SOURCE_F32, L.GEMM_EPI_SOURCE_BF16):
+            p = L.Plan(L.make_desc(M, N, K, sched=sched, num_workers=256,
+                                   epilogue=src | L.GEMM_EPI_GELU))
+            assert p.info.kernel == 0, (M, N, K, sched)
+            plain = L.Plan(L.make_desc(M, N, K, sched=sched, num_workers=256,
+                                       epilogue=L.GEMM_EPI_GELU))
+            assert plain.info.kernel == (0 if K == 0 else 3), (M, N, K, sched)
+    ranked = L.rank_configs(L.make_desc(4096, 4096, 4096, sched=L.GEMM_SCHED_AUTO,
+                                        num_workers=256, epilogue=L.GEMM_EPI_SOURCE_BF16))
+    assert ranked and all(r.kernel == 0 for r in ranked)
+    assert any(r.bm == 256 and r.sched == L.GEMM_SCHED_PERSISTENT for r in ranked)
+    plain = L.rank_configs(L.make_desc(4096, 4096, 4096, sched=L.GEMM_SCHED_AUTO,
+                                       num_workers=256))
+    assert not any(r.kernel == 0 and r.bm == 256 and r.sched == L.GEMM_SCHED_PERSISTENT
+                   for r in plain)
+
+
 @pytest.mark.skipif(__import__("torch").cuda.is_available(),
                     reason="validation-only test; on a GPU machine the parity suite covers runs")
 def test_run_ex_validation_before_enqueue():
@@ -249,6 +283,16 @@ def test_run_ex_validation_before_enqueue():
     b = L.Plan(L.make_desc(256, 256, 256, num_workers=4, epilogue=L.GEMM_EPI_GELU))
     assert b.run_ex_raw(ok, ok, ok, epi_null=True) == L.GEMM_ERR_HIP
     assert b.run_ex_raw(ok, ok, ok, bias=3, amax=5) == L.GEMM_ERR_HIP
+    # a source matrix: beta != 0 needs it, aligned for its element type; beta == 0 reads none
+    s = L.Plan(L.make_desc(256, 256, 256, num_workers=4, epilogue=L.GEMM_EPI_SOURCE_F32))
+    assert s.run_ex_raw(ok, ok, ok, epi_null=True) == L.GEMM_ERR_INVALID_ARG
+    assert s.run_ex_raw(ok, ok, ok, beta=0.5) == L.GEMM_ERR_INVALID_ARG
+    assert s.run_ex_raw(ok, ok, ok, beta=0.5, source=ok + 8) == L.GEMM_ERR_ALIGNMENT
+    assert s.run_ex_raw(ok, ok, ok, beta=0.5, source=ok) == L.GEMM_ERR_HIP
+    assert s.run_ex_raw(ok, ok, ok, beta=0.0) == L.GEMM_ERR_HIP
+    h = L.Plan(L.make_desc(256, 256, 256, num_workers=4, epilogue=L.GEMM_EPI_SOURCE_BF16))
+    assert h.run_ex_raw(ok, ok, ok, beta=-1.0, source=ok + 4) == L.GEMM_ERR_ALIGNMENT
+    assert h.run_ex_raw(ok, ok, ok, beta=-1.0, source=ok + 8) == L.GEMM_ERR_HIP  # 8 B is enough
     # an empty output checks the epilogue operands, then does nothing
     e = L.Plan(L.make_desc(0, 256, 256, num_workers=4, epilogue=L.GEMM_EPI_AMAX))
     assert e.run_ex_raw(0, 0, 0, epi_null=True) == L.GEMM_ERR_INVALID_ARG

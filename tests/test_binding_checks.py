@@ -44,6 +44,22 @@ def test_shapes_and_types_are_checked_first():
     refused(r"is on cpu", p.validate, A.view(torch.int16), B.view(torch.int16), C)
 
 
+def test_source_operand():
+    """A source bit with beta != 0 needs an M x N source of the bit's type; beta == 0 none."""
+    A, B, C = good_bf16()
+    p = plan_of(epilogue=L.GEMM_EPI_SOURCE_F32)
+    refused(r"source is required", p.validate, A, B, C, source=None, beta=0.5)
+    refused(r"source has dtype", p.validate, A, B, C, source=C.to(torch.bfloat16), beta=0.5)
+    refused(r"source has 32640 elements; expected 32768", p.validate, A, B, C,
+            source=C[: M - 1], beta=0.5)
+    refused(r"is on cpu", p.validate, A, B, C, source=C, beta=0.5)      # C itself: accepted
+    refused(r"is on cpu", p.validate, A, B, C, source=None, beta=0.0)   # nothing read
+    q = plan_of(dtype_c=L.GEMM_BF16, epilogue=L.GEMM_EPI_SOURCE_BF16)
+    Cb = C.to(torch.bfloat16)
+    refused(r"source has dtype", q.validate, A, B, Cb, source=C, beta=1.0)
+    refused(r"is on cpu", q.validate, A, B, Cb, source=Cb.view(torch.int16), beta=1.0)
+
+
 def test_fp8_scales_and_epilogue_operands():
     p = plan_of(L.GEMM_FP8_E4M3, L.GEMM_FP8_E4M3, L.GEMM_EPI_BIAS_ROW | L.GEMM_EPI_AMAX)
     A = torch.zeros((M, K), dtype=torch.uint8)

@@ -1,5 +1,5 @@
-"""Parity of the fused epilogue (bias, activation, amax, e4m3 output) with the oracle's
-(oracle/epilogue.py), through gemm_run_ex, on an MI355X.
+"""Parity of the fused epilogue (source term, bias, activation, amax, e4m3 output) with the
+oracle's (oracle/epilogue.py), through gemm_run_ex, on an MI355X.
 
 Float outputs: |Y - Y_ref| within oracle.epilogue.tolerance.  e4m3 outputs: the stored code lies
 between the codes of (Y_ref -+ tol) / scale_d -- and equals the oracle's code byte for byte
@@ -33,13 +33,29 @@ def dev():
     return torch.device("cuda:0")
 
 
+def make_source(M, N, kind, seed):
+    """A seeded M x N source matrix S of element type `kind` ("f32" or "bf16"): the torch tensor
+    (on the CPU) and the values it holds exactly, as float64."""
+    v = gi.make_vector(M * N, seed=seed, dist=("normal", 2.0)).reshape(M, N)
+    if kind == "f32":
+        t = torch.from_numpy(v.copy())
+        return t, v.astype(np.float64)
+    bits = gi.bf16_bits(torch.from_numpy(v))
+    t = torch.from_numpy(bits.view(np.int16).reshape(M, N).copy()).view(torch.bfloat16)
+    return t, t.float().numpy().astype(np.float64)
+
+
 def run_epi(op, dev, out, bias_kind=None, bias=None, act=None, amax=True, scale_d=1.0,
             flags=0, sched=L.GEMM_SCHED_PERSISTENT, workers=3, tile=256, amax_init=0.0,
-            mapping=L.GEMM_MAP_GROUPED_M, group=2):
-    """One fused GEMM through gemm_run_ex; returns (C as float64 or e4m3 codes, amax, plan)."""
+            mapping=L.GEMM_MAP_GROUPED_M, group=2, source=None, beta=0.0, in_place=False):
+    """One fused GEMM through gemm_run_ex; returns (C as float64 or e4m3 codes, amax, plan).
+    source: a CPU tensor from make_source (its type sets the GEMM_EPI_SOURCE_* bit), passed as
+    S with factor beta -- or, in_place, copied into C and C passed as S."""
     A, B, sa, sb = to_device(op, torch, dev)
     epi = ACT_BITS[act] | (L.GEMM_EPI_AMAX if amax else 0)
     epi |= {None: 0, "row": L.GEMM_EPI_BIAS_ROW, "col": L.GEMM_EPI_BIAS_COL}[bias_kind]
+    if source is not None:
+        epi |= L.GEMM_EPI_SOURCE_F32 if source.dtype == torch.float32 else L.GEMM_EPI_SOURCE_BF16
     bm, bn = tile if isinstance(tile, tuple) else (tile, tile)
     desc = L.make_desc(op.M, op.N, op.K, L.GEMM_BF16 if op.dtype == "bf16" else L.GEMM_FP8_E4M3,
                        OUT[out], mapping, group, sched, workers, bm, bn, 0, flags,
@@ -54,32 +70,41 @@ def run_epi(op, dev, out, bias_kind=None, bias=None, act=None, amax=True, scale_
     b = torch.from_numpy(np.asarray(bias, dtype=np.float32)).to(dev) if bias is not None else None
     am = torch.tensor([amax_init], dtype=torch.float32, device=dev)
     sd = torch.tensor([scale_d], dtype=torch.float32, device=dev)
+    S = None
+    if source is not None:
+        if in_place:
+            C.copy_(source.to(dev))
+            S = C
+        else:
+            S = source.to(dev)
     plan.run(A, B, C, sa, sb, ws, bias=b, scale_d=sd if out == "e4m3" else None,
-             amax=am if amax else None)
+             amax=am if amax else None, source=S, beta=beta)
     torch.cuda.synchronize()
     got = C.cpu().numpy().copy() if out == "e4m3" else decode_output(C, torch)
     return got, float(am.cpu()[0]), plan
 
 
-def expected(op, bias_kind, bias, act):
+def expected(op, bias_kind, bias, act, src=None, beta=0.0):
     C = reference(op)
     kw = {"bias_row": bias} if bias_kind == "row" else (
         {"bias_col": bias} if bias_kind == "col" else {})
-    z, y = E.apply(C, act=act, **{k: np.asarray(v, dtype=np.float64) for k, v in kw.items()})
+    z, y = E.apply(C, act=act, source=src, beta=beta,
+                   **{k: np.asarray(v, dtype=np.float64) for k, v in kw.items()})
     return z, y
 
 
-def check(op, got, am, out, bias_kind, bias, act, scale_d, what):
-    z, y = expected(op, bias_kind, bias, act)
+def check(op, got, am, out, bias_kind, bias, act, scale_d, what, src=None, beta=0.0):
+    z, y = expected(op, bias_kind, bias, act, src, beta)
     ma = oracle.max_abs_decoded(op.A, oracle_dtype(op), op.scale_a)
     mb = oracle.max_abs_decoded(op.B, oracle_dtype(op), op.scale_b)
-    tol = E.tolerance(y, z, op.K, ma, mb, out="f32")
+    s_ref = beta * src if src is not None else None
+    tol = E.tolerance(y, z, op.K, ma, mb, out="f32", s_ref=s_ref)
     if out == "e4m3":
         lo, hi = E.quantized_bounds(y, tol, scale_d)
         v = E4M3_TABLE[got]
         bad = ~((v >= lo) & (v <= hi))
     else:
-        full = E.tolerance(y, z, op.K, ma, mb, out=out)
+        full = E.tolerance(y, z, op.K, ma, mb, out=out, s_ref=s_ref)
         assert np.isfinite(got).all(), f"{what}: non-finite outputs"
         bad = np.abs(got - y) > full
     if bad.any():
@@ -165,6 +190,69 @@ def test_fused_epilogue_parity(dev, case):
     if sched == L.GEMM_SCHED_STREAMK:
         assert plan.info.sk_tiles > 0
     check(op, got, am, out, bias_kind, bias, act, scale_d, name)
+
+
+# Z = alpha Acc + beta S: the cooperative kernel, every output type, S in fp32 or bf16, S = C
+# (in place), Stream-K in both fixup modes, e4m3 operands, K = 0
+# id, M, N, K, operand type, output, source type, in place, beta, flags, tile, sched, workers,
+# bias, activation
+SRC_CASES = [
+    ("src_f32_bias_col_gelu", 520, 776, 1000, "bf16", "f32", "f32", False, 0.75, 0, 256,
+     L.GEMM_SCHED_PERSISTENT, 3, "col", "gelu"),
+    ("src_f32_in_place_ragged_relu", 300, 264, 104, "bf16", "f32", "f32", True, -1.5, 0, 128,
+     L.GEMM_SCHED_STATIC, 0, "row", "relu"),
+    ("src_bf16_in_place_silu", 520, 520, 1000, "bf16", "bf16", "bf16", True, 2.0, 0, 256,
+     L.GEMM_SCHED_PERSISTENT, 3, None, "silu"),
+    ("src_bf16_fp8_e4m3_out", 384, 264, 272, "e4m3", "e4m3", "bf16", False, 0.5, 0, 128,
+     L.GEMM_SCHED_PERSISTENT, 4, "row", "relu"),
+    ("src_f32_fp8_256_bf16_out", 520, 776, 1040, "e4m3", "bf16", "f32", False, -0.25, 0, 256,
+     L.GEMM_SCHED_PERSISTENT, 3, "col", None),
+    ("src_f32_streamk_chain_in_place", 256, 256, 8192, "bf16", "f32", "f32", True, 1.0,
+     L.GEMM_FLAG_STREAMK_CHAIN, 128, L.GEMM_SCHED_STREAMK, 8, "col", "gelu"),
+    ("src_bf16_streamk_separate", 256, 256, 8192, "bf16", "bf16", "bf16", False, -1.0, 0, 128,
+     L.GEMM_SCHED_STREAMK, 8, "row", None),
+    ("src_f32_streamk_hybrid_ragged", 200, 136, 1000, "bf16", "f32", "f32", False, 3.0, 0, 128,
+     L.GEMM_SCHED_STREAMK, 9, None, "silu"),
+    ("src_f32_zero_depth", 130, 136, 0, "bf16", "f32", "f32", False, 0.5, 0, 128,
+     L.GEMM_SCHED_PERSISTENT, 4, "col", "gelu"),
+]
+
+
+@pytest.mark.parametrize("case", SRC_CASES, ids=[c[0] for c in SRC_CASES])
+def test_source_term_parity(dev, case):
+    (name, M, N, K, dt, out, src_kind, in_place, beta, flags, tile, sched, workers, bias_kind,
+     act) = case
+    print(f"source case {name}: {M}x{N}x{K} {dt}->{out} S {src_kind}", flush=True)
+    op = operands(name, M, N, K, dt) if K else gi.make_operands(M, N, 0, dt, seed=3)
+    n_bias = M if bias_kind == "row" else N
+    bias = gi.make_vector(n_bias, seed=zlib.crc32(name.encode()) % 977) if bias_kind else None
+    S, s_vals = make_source(M, N, src_kind, seed=zlib.crc32(name.encode()) % 991)
+    scale_d = 1.0
+    if out == "e4m3":
+        _, y = expected(op, bias_kind, bias, act, s_vals, beta)
+        scale_d = float(np.float32(E.amax(y) / 448.0 * 0.8))
+    got, am, plan = run_epi(op, dev, out, bias_kind, bias, act, True, scale_d, flags, sched,
+                            workers, tile, source=S, beta=beta, in_place=in_place)
+    assert plan.info.kernel == 0
+    if sched == L.GEMM_SCHED_STREAMK:
+        assert plan.info.sk_tiles > 0
+        assert plan.info.streamk_mode == (0 if flags & L.GEMM_FLAG_STREAMK_CHAIN else 1)
+    check(op, got, am, out, bias_kind, bias, act, scale_d, name, s_vals, beta)
+
+
+def test_zero_beta_reads_no_source(dev):
+    """beta = 0: the source is not read, so NaNs in it do not reach C, and the bits equal those
+    of the same plan run without a source (cooperative kernel both)."""
+    M, N, K = 264, 520, 256
+    op = operands("beta0", M, N, K, "bf16")
+    bias = gi.make_vector(N, seed=23)
+    S = torch.full((M, N), float("nan"), dtype=torch.float32)
+    got, am, plan = run_epi(op, dev, "f32", "col", bias, "gelu", True, 1.0, 0, tile=128,
+                            source=S, beta=0.0)
+    plain, am2, plan2 = run_epi(op, dev, "f32", "col", bias, "gelu", True, 1.0,
+                                L.GEMM_FLAG_COOPERATIVE, tile=128)
+    assert plan.info.kernel == plan2.info.kernel == 0
+    assert np.isfinite(got).all() and np.array_equal(got, plain) and am == am2
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16", "e4m3"])

@@ -1,6 +1,7 @@
 """Seeded random sweep of the launch space against the oracle: operand type, M, N, K (ragged),
 tile, kernel flag, scheduler, worker count, mapping, group, and for half the cases a fused
-epilogue (bias row/column, activation, amax, fp32 / bf16 / e4m3 output).  Every combination the
+epilogue (source term in fp32 or bf16, in place or not, bias row/column, activation, amax,
+fp32 / bf16 / e4m3 output).  Every combination the
 planner accepts must match the oracle within the same bounds as the fixed-shape tests
 (plain: |C - C_ref| <= 4e-3 |C_ref| + 1e-3 sqrt(K) max|a| max|b|; fused: oracle.epilogue's
 bounds, e4m3 code bounds and the amax interval); combinations it refuses (GEMM_ERR_UNSUPPORTED)
@@ -50,7 +51,10 @@ def draw(rng):
         out_fused=rng.choice(["f32", "bf16", "e4m3"]),
         bias_kind=rng.choice([None, "row", "col"]),
         act=rng.choice([None, "relu", "gelu", "silu"]),
-        scale_d=rng.choice([1.0, 0.25, 3.0]))
+        scale_d=rng.choice([1.0, 0.25, 3.0]),
+        source=rng.choice([None, None, "f32", "bf16"]),
+        beta=rng.choice([1.0, -0.5, 0.0]),
+        in_place=rng.random() < 0.5)
 
 
 @pytest.mark.parametrize("seed", [11, 12, 13])
@@ -75,11 +79,16 @@ def test_random_launches_match_the_oracle(dev, seed):
                 if c["bias_kind"]:
                     bias = (np.random.default_rng(1000 * seed + i).standard_normal(n_b) * 0.5
                             ).astype(np.float32)
+                S = s_vals = None
+                if c["source"]:
+                    S, s_vals = TE.make_source(c["M"], c["N"], c["source"], seed=2000 * seed + i)
+                in_place = S is not None and c["in_place"] and c["source"] == c["out_fused"]
                 got, am, _ = TE.run_epi(op, dev, c["out_fused"], c["bias_kind"], bias, c["act"],
                                         True, c["scale_d"], c["flags"], c["sched"], c["workers"],
-                                        c["tile"], mapping=c["mapping"], group=c["group"])
+                                        c["tile"], mapping=c["mapping"], group=c["group"],
+                                        source=S, beta=c["beta"], in_place=in_place)
                 TE.check(op, got, am, c["out_fused"], c["bias_kind"], bias, c["act"],
-                         c["scale_d"], what)
+                         c["scale_d"], what, s_vals, c["beta"] if S is not None else 0.0)
             ran += 1
         except L.GemmError as e:
             assert e.status == L.GEMM_ERR_UNSUPPORTED, f"{what}: {e}"
