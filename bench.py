@@ -51,6 +51,9 @@ def source_hash():
 
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "hbm_traffic.json.txt")
 PEAK_CLOCK_MHZ = 2400.0  # the engine clock the published MFMA peaks assume
+# below this mean shader clock the sampled metrics tables were taken while the GPU idled (these
+# kernels hold 1.7 - 2.4 GHz; an idle MI355X drops to a few hundred MHz)
+BUSY_CLOCK_FLOOR_MHZ = 1000.0
 
 
 class BoardSampler:
@@ -129,6 +132,13 @@ class BoardSampler:
             if t >= since:
                 tables.append((ts, clk, pw, en))
         clk = [c for _, c, _, _ in tables if c is not None]
+        if clk and sum(clk) / len(clk) < BUSY_CLOCK_FLOOR_MHZ:
+            # tables refreshed while the GPU idled (as when a tracer holds the launches back and
+            # the refreshes miss the busy stretches): they tell nothing about the kernel
+            log(f"board sampler: mean clock {sum(clk) / len(clk):.0f} MHz over {len(tables)} "
+                f"refreshes is an idle reading; clock and power not recorded")
+            return {"clock_mhz": None, "clock_mhz_min_max": None, "power_w": None,
+                    "refreshes": len(tables)}
         power = None
         if len(tables) >= 2 and tables[-1][0] > tables[0][0]:
             power = (tables[-1][3] - tables[0][3]) / ((tables[-1][0] - tables[0][0]) * 1e-9)

@@ -36,8 +36,8 @@ def gemm(A, B, out_dtype="f32", scale_a=None, scale_b=None, mapping="grouped_m",
     Y / scale_d, scale_d a one-element float32 device tensor).  tile: 0 (the planner's), an int
     for square tiles, or (bm, bn), e.g. (256, 224).  sk_groups: Stream-K groups (0 = the
     planner's count, 1-8) of a plan with a Stream-K band.  source: an (M, N) float32 or
-    bfloat16 device tensor added as beta * source before the bias (such plans run on the
-    cooperative kernel).  Returns C (M, N): float32,
+    bfloat16 device tensor added as beta * source before the bias (it may be C's own storage
+    only through Plan.run; here C is a new tensor).  Returns C (M, N): float32,
     bfloat16, or uint8 e4m3 codes.  Shapes, element types, contiguity and devices are checked
     before anything is launched (ValueError)."""
     import torch

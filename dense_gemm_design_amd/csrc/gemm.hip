@@ -18,37 +18,18 @@
 
 #include "../../include/gemm.h"
 #include "gemm_kernel.h"
+#include "launch.h"
 #include "sched.h"
 
 namespace {
 
 using namespace dg;
 
-// Tile configurations: TileCfg<dtype, BM, BN, BK, wave rows, wave columns, stages, swizzle>.
-// SWZ spreads the 16 rows one 16-lane LDS read phase touches over 16 distinct 16-byte bank groups
-// (1 for 128-byte rows, 2 for 64-byte rows).  Defaults (first match per tile shape): 8 waves of
-// 128 x 64 sub-tiles with 2 stages of 64 KiB -- two waves per SIMD hide each other's LDS waits.
-// The ping-pong kernel (GEMM_FLAG_PINGPONG) runs the same 256 x 256 tiles with two wave groups.
-using CfgBf16_256pp = TileCfg<DT_BF16, 256, 256, 64, 2, 4, 2, 1>;
-using CfgBf16_256 = TileCfg<DT_BF16, 256, 256, 64, 2, 4, 2, 1>;
-using CfgBf16_128 = TileCfg<DT_BF16, 128, 128, 64, 2, 2, 2, 1>;
-using CfgFp8_256pp = TileCfg<DT_FP8, 256, 256, 128, 2, 4, 2, 1>;
-using CfgFp8_256 = TileCfg<DT_FP8, 256, 256, 128, 2, 4, 2, 1>;
-using CfgFp8_128 = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 2, 1>;
-// The wide-wave kernel (GEMM_FLAG_WIDE): four waves of 128 x 128, two stages of 64 KiB.
-using CfgBf16_256w = TileCfg<DT_BF16, 256, 256, 64, 2, 2, 2, 1, 16>;  // 16 x 16 x 32 MFMAs
-using CfgFp8_256w = TileCfg<DT_FP8, 256, 256, 128, 2, 2, 2, 1, 16>;  // 16 x 16 x 128 MFMAs
-// ... and on 128 x 128 tiles: four waves of 64 x 64, four stages of 32 KiB (a k-step of this
-// tile is a quarter as long, so its loads need three k-steps of lead to land: measured 17 % faster
-// at 4096^3 and 34 % on 1024 x 1024 x 16384 e4m3 than two stages)
-using CfgBf16_128w = TileCfg<DT_BF16, 128, 128, 64, 2, 2, 4, 1, 16>;
-using CfgFp8_128w = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 4, 1, 16>;
-// ... and on 256 x 224 tiles (waves of 128 x 112): a block width from the heuristic's aligned set
-// below 256 that fills whole waves where 256 does not -- N = 14336 is 64 such columns, so
-// 4096 x 14336 makes 1024 tiles, four full waves of 256 CUs, where 256 x 256 tiles leave the
-// fourth wave half empty
-using CfgBf16_224w = TileCfg<DT_BF16, 256, 224, 64, 2, 2, 2, 1, 16>;
-using CfgFp8_224w = TileCfg<DT_FP8, 256, 224, 128, 2, 2, 2, 1, 16>;
+// Zeroes the Stream-K locks, the error word and the trace area of a workspace before a run.
+__global__ void clear_ints_kernel(int *p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
 
 typedef hipError_t (*launch_fn)(const KernelArgs &, int grid, bool ragged_k, hipStream_t);
 typedef const void *(*kernel_fn)();
@@ -88,38 +69,14 @@ template <class CFG>
 const void *kernel_of_pp() {
   return (const void *)&gemm_kernel_pp<CFG, false>;
 }
-// k-tiles one MFMA deep (e4m3 16 x 16 x 128) take the single-A-buffer form of the schedule
-template <class CFG, bool RAGGED_K, int FUSE = FUSE_OFF>
-constexpr auto wide_kernel() {
-  if constexpr (CFG::KSUB == 1)
-    return &gemm_kernel_wide1<CFG, RAGGED_K, FUSE>;
-  else
-    return &gemm_kernel_wide<CFG, RAGGED_K, FUSE>;
-}
-// activation of a fused plan, the wide-wave kernels' FUSE argument
-int act_of(uint32_t epi) {
-  return (epi & EPI_RELU) ? ACT_RELU : (epi & EPI_GELU) ? ACT_GELU : (epi & EPI_SILU) ? ACT_SILU
-                                                                                   : ACT_NONE;
-}
-template <class CFG, int FUSE>
-void launch_wide_as(const KernelArgs &a, int grid, bool ragged_k, hipStream_t s) {
-  if (ragged_k)
-    hipLaunchKernelGGL((wide_kernel<CFG, true, FUSE>()), dim3(grid), dim3(CFG::THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL((wide_kernel<CFG, false, FUSE>()), dim3(grid), dim3(CFG::THREADS), 0, s, a);
-}
 template <class CFG>
 hipError_t launch_wide(const KernelArgs &a, int grid, bool ragged_k, hipStream_t s) {
-  if (!fused_args(a)) {
+  if (!fused_args(a))
     launch_wide_as<CFG, FUSE_OFF>(a, grid, ragged_k, s);
-  } else {
-    switch (act_of(a.epi)) {
-      case ACT_RELU: launch_wide_as<CFG, ACT_RELU>(a, grid, ragged_k, s); break;
-      case ACT_GELU: launch_wide_as<CFG, ACT_GELU>(a, grid, ragged_k, s); break;
-      case ACT_SILU: launch_wide_as<CFG, ACT_SILU>(a, grid, ragged_k, s); break;
-      default: launch_wide_as<CFG, ACT_NONE>(a, grid, ragged_k, s); break;
-    }
-  }
+  else if (a.epi & (EPI_SRC_F32 | EPI_SRC_BF16))  // reads a source matrix: its own kernels
+    return launch_wide_src<CFG>(a, grid, ragged_k, s);
+  else
+    launch_wide_act<CFG, 0>(a, grid, ragged_k, s);
   return hipGetLastError();
 }
 template <class CFG>
@@ -361,8 +318,8 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
                              {KIND_WIDE, 256, 256, GEMM_SCHED_STREAMK},
                              {KIND_COOP, 256, 256, GEMM_SCHED_STREAMK},
                              {KIND_COOP, 256, 256, GEMM_SCHED_PERSISTENT}};
-  // a source matrix (Z = alpha Acc + beta S) is read by the cooperative kernel only: its plans
-  // rank the cooperative candidates, the others every candidate but the last
+  // a source matrix (Z = alpha Acc + beta S) adds its bytes to every candidate's output traffic;
+  // the last candidate is ranked for plans with a source only (the others keep their set)
   const bool source = (d.epilogue & kEpiSource) != 0;
   const double es = !source ? 0.0 : (d.epilogue & GEMM_EPI_SOURCE_F32) ? 4.0 : 2.0;
   int cus = 0, dev = 0;
@@ -375,7 +332,7 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
   const bool blocked = d.mapping == GEMM_MAP_BLOCKED;
   out.clear();
   for (const ModelCand &c : cands) {
-    if (source ? c.kind != KIND_COOP : &c == &cands[std::size(cands) - 1]) continue;
+    if (!source && &c == &cands[std::size(cands) - 1]) continue;
     if (c.kind != KIND_COOP && d.K == 0) continue;  // the data-parallel kernels need K > 0
     const KernelEntry *e = nullptr;
     for (const KernelEntry &k : kKernels)
@@ -565,9 +522,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   // the fused epilogue runs on the wide-wave and cooperative kernels
   const bool fused = d.epilogue != 0 || d.dtype_c == GEMM_FP8_E4M3;
   if (fused && force_kind == KIND_PP) return GEMM_ERR_UNSUPPORTED;
-  // a source matrix is read by the cooperative kernel only
-  const bool source = (d.epilogue & kEpiSource) != 0;
-  if (source && force_kind == KIND_WIDE) return GEMM_ERR_UNSUPPORTED;
+
 
   // Tile shape and scheduler: the cost model when everything is left to the planner, else
   // 256 x 256 unless asked otherwise or the problem has too few big tiles.
@@ -596,7 +551,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
       by_kind[e.kind] = &e;
   const KernelEntry *k = by_kind[force_kind >= 0 ? force_kind : KIND_COOP];
   // tile shapes only the wide-wave kernel has (which needs K > 0, like every data-parallel kernel)
-  if (!k && force_kind < 0 && d.K > 0 && !source) k = by_kind[KIND_WIDE];
+  if (!k && force_kind < 0 && d.K > 0) k = by_kind[KIND_WIDE];
   if (!k) return GEMM_ERR_UNSUPPORTED;  // the schedule is planned with this one
   // rows of one tile must stay addressable by 32-bit buffer offsets
   if ((int64_t)bm * d.K * eb >= 0x7FFFFFF0ll || (int64_t)bn * d.K * eb >= 0x7FFFFFF0ll)
@@ -622,7 +577,7 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
     // data-parallel 128 x 128 tiles and 30 % slower for Stream-K)
     const bool wide_next = force_kind == KIND_WIDE ||
                            (force_kind < 0 && d.K > 0 && by_kind[KIND_WIDE] &&
-                            model_kind != KIND_COOP && !source);
+                            model_kind != KIND_COOP);
     if (wide_next) per_cu = 1;
     workers = cus * per_cu;
   }
@@ -634,15 +589,13 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   // Data-parallel work runs on the wide-wave kernel unless a kernel is asked for, or the cost
   // model picked another one (its grid was sized for that kernel above); so does Stream-K work,
   // unless it needs the lock chain (checked below, once the band is known).
-  if (force_kind < 0 && !source && d.K > 0 &&
-      (sched == GEMM_SCHED_STATIC || sched == GEMM_SCHED_PERSISTENT) &&
+  if (force_kind < 0 && d.K > 0 && (sched == GEMM_SCHED_STATIC || sched == GEMM_SCHED_PERSISTENT) &&
       (model_kind < 0 || model_kind == KIND_WIDE)) {
     if (by_kind[KIND_WIDE])
       k = by_kind[KIND_WIDE];
     else if (by_kind[KIND_PP] && !fused)
       k = by_kind[KIND_PP];
-  } else if (force_kind < 0 && !source && d.K > 0 && sched == GEMM_SCHED_STREAMK &&
-             by_kind[KIND_WIDE] &&
+  } else if (force_kind < 0 && d.K > 0 && sched == GEMM_SCHED_STREAMK && by_kind[KIND_WIDE] &&
              !(d.flags & GEMM_FLAG_STREAMK_CHAIN) && (model_kind < 0 || model_kind == KIND_WIDE)) {
     k = by_kind[KIND_WIDE];
   }

@@ -456,9 +456,9 @@ __device__ __forceinline__ void store_quad(const KernelArgs &args, int64_t m, in
 // output the code of Y / scale_d -- and the store, in the order of section 12.2 (steps 2 to 7).
 // Kernels take this path in a fused instantiation, chosen at launch when EPI_* bits or an e4m3
 // output are asked for; every other launch runs the plain epilogues above and below.  The
-// wide-wave kernels have one fused instantiation per activation (no per-element branch on it);
-// the cooperative kernel has one that reads the activation from the EPI_* bits, and only it
-// reads a source matrix S (the planner gives plans with one to it).
+// wide-wave kernels have one fused instantiation per activation (no per-element branch on it),
+// and one more per activation that also reads a source matrix S (FUSE_SRC); the cooperative
+// kernel has one that reads the activation and the source from the EPI_* bits.
 enum : uint32_t {
   EPI_BIAS_ROW = 0x1u,
   EPI_BIAS_COL = 0x2u,
@@ -473,6 +473,11 @@ enum : uint32_t {
 // FUSE template argument: FUSE_OFF = the plain epilogue; ACT_* = fused, with that activation;
 // ACT_RT = fused, activation chosen by the EPI_* bits at run time.
 enum { FUSE_OFF = -1, ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_SILU = 3, ACT_RT = 4 };
+// FUSE_SRC added to a wide-wave kernel's ACT_*: that instantiation also reads a source matrix S,
+// in its own copy of the kernel, so the others keep their registers.
+enum { FUSE_SRC = 8 };
+constexpr int fuse_act(int F) { return F < 0 ? F : (F & 7); }
+constexpr bool fuse_src(int F) { return F >= 0 && (F & FUSE_SRC) != 0; }
 
 // State of the fused epilogue in one lane: the output's inverse scale and the running max |Y|.
 struct EpiCtx {
@@ -556,12 +561,13 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(f32x4 v) {
 
 // Fused store of one accumulator quad: 4 consecutive n of row m (n a multiple of 4, so a column
 // bias quad is one aligned 16-byte load).
-template <int ACT>
+template <int F>
 __device__ __forceinline__ void store_quad_fused(const KernelArgs &args, int64_t m, int64_t n,
                                                  f32x4 v, float alpha, EpiCtx &ec) {
+  constexpr int ACT = fuse_act(F);
   if (m >= args.M || n >= args.N) return;
   v = v * alpha;
-  if constexpr (ACT == ACT_RT) {
+  if constexpr (F == ACT_RT || fuse_src(F)) {
     // Z = alpha * Acc + beta * S: the source quad is read before this thread writes the same
     // elements of C, so S may be C itself
     if (args.epi & EPI_SRC_F32) {
@@ -1372,26 +1378,95 @@ struct WideBias {
   }
 };
 
-// Y of accumulator quad (f, g) of a 16 x 16-block sub-tile: alpha * Acc + bias, then the
-// activation and, inside C, the amax (past the edge of C a row bias still reaches the columns past
-// N, and a column bias the rows past M, so Y there need not be zero).
+// Y of accumulator quad (f, g) of a 16 x 16-block sub-tile: alpha * Acc (+ beta * S) + bias, then
+// the activation and, inside C, the amax (past the edge of C a row bias still reaches the columns
+// past N, and a column bias the rows past M, so Y there need not be zero).  s: the source quad
+// (FUSE_SRC instantiations).
 template <class CFG, int ACT>
 __device__ __forceinline__ f32x4 wide_fused_quad(const KernelArgs &args, const acc_t<CFG> &blk,
                                                  float alpha, f32x4 bcol, const WideBias<CFG> &bias,
-                                                 EpiCtx &ec, int f, int g) {
+                                                 EpiCtx &ec, int f, int g,
+                                                 f32x4 s = f32x4{0.0f, 0.0f, 0.0f, 0.0f}) {
   const f32x4 a = quad_of<true>(blk, 0);
   f32x4 v;
 #pragma unroll
   for (int e = 0; e < 4; ++e) v[e] = fmaf(a[e], alpha, bcol[e] + bias.row[f]);
-  return epi_act<ACT>(args.epi, v, ec.am, bias.inside(f, g));
+  if constexpr (fuse_src(ACT)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = fmaf(args.beta, s[e], v[e]);
+  }
+  return epi_act<fuse_act(ACT)>(args.epi, v, ec.am, bias.inside(f, g));
+}
+
+// Source quads of a 16 x 16-block sub-tile for a FUSE_SRC epilogue (ES: element bytes, 4 for fp32,
+// 2 for bf16; 0 = no source).  Quad (f, g) of the lane is S[m0 + 16f + lane%16][n0 + 16g +
+// 4(lane/16) + 0..3], read through a buffer range that starts at the sub-tile's origin, like the
+// direct stores: rows past M read zero, and a column block past N gets an offset past the range.
+// The loads go out RING quads ahead of their use, in the order the epilogue consumes the quads,
+// into a ring of registers: quad i is taken from slot i mod RING, which then takes quad i + RING.
+template <class CFG, int ES>
+struct WideSource {
+  static constexpr int RING = CFG::WM == 128 && CFG::WN == 128 ? 4 : 8;
+  using raw_t = std::conditional_t<ES == 4, u32x4, u32x2>;
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t lane_off, row_b, cols_ok;
+  raw_t ring[RING];
+
+  __device__ __forceinline__ void init(const KernelArgs &args, int64_t m0, int64_t n0, int lane,
+                                       uint32_t ok) {
+    if constexpr (ES != 0) {
+      const int64_t origin = m0 * args.ldc + n0;
+      r = make_rsrc(args.src + origin * ES, (args.M * args.ldc - origin) * ES);
+      row_b = (uint32_t)args.ldc * ES;
+      asm volatile("" : "+s"(row_b));  // kept here, not hoisted ahead of the item loop
+      lane_off = (uint32_t)(lane & 15) * row_b + (uint32_t)(lane >> 4) * 4 * ES;
+      cols_ok = ok >> 16;  // bit g: column block g inside C
+    }
+  }
+  __device__ __forceinline__ void issue(int i, int f, int g) {
+    if constexpr (ES != 0) {
+      const uint32_t off = ((cols_ok >> g) & 1u) ? lane_off + (uint32_t)(g * 16 * ES) : kOOB;
+      const uint32_t soff = (uint32_t)(f * 16) * row_b;
+      if constexpr (ES == 4)
+        ring[i % RING] = __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+      else
+        ring[i % RING] = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+    }
+  }
+  __device__ __forceinline__ f32x4 take(int i) const {
+    if constexpr (ES == 4) {
+      return __builtin_bit_cast(f32x4, ring[i % RING]);
+    } else if constexpr (ES == 2) {
+      const u32x2 x = ring[i % RING];
+      return f32x4{__uint_as_float(x[0] << 16), __uint_as_float(x[0] & 0xFFFF0000u),
+                   __uint_as_float(x[1] << 16), __uint_as_float(x[1] & 0xFFFF0000u)};
+    } else {
+      return f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  }
+};
+
+// Runs body(std::integral_constant<int, ES>) with the source's element bytes of the launch
+// (FUSE_SRC instantiations; ES = 0 for the others), so the epilogue loops hold no branch on it.
+template <int FUSE, class Body>
+__device__ __forceinline__ void with_source(const KernelArgs &args, Body &&body) {
+  if constexpr (fuse_src(FUSE)) {
+    if (args.epi & EPI_SRC_F32)
+      body(std::integral_constant<int, 4>());
+    else
+      body(std::integral_constant<int, 2>());
+  } else {
+    body(std::integral_constant<int, 0>());
+  }
 }
 
 // bf16 output of a 128-row sub-tile (128 or 112 columns) through the wave's LDS slice, 32 rows at
 // a time, at a pitch of 256 bytes.  Chunk c (16 bytes) of staged row r sits at chunk position
 // c ^ (r mod 16): the rows one write touches and the 4 rows one read-back touches each spread
 // over every bank.  16 lanes store one row segment (the sub-tile's 14 or 16 chunks).  A fused
-// FUSE adds the bias, the activation and the amax (16 x 16 blocks).
-template <class CFG, int FUSE = FUSE_OFF>
+// FUSE adds the bias, the activation and the amax (16 x 16 blocks), and with SES (the source's
+// element bytes) the source term.
+template <class CFG, int FUSE = FUSE_OFF, int SES = 0>
 __device__ __forceinline__ void epilogue_wide(const KernelArgs &args, const WorkItem &w,
                                               const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
                                               float alpha, int wm, int wn, int lane, lds_t *slice,
@@ -1463,6 +1538,22 @@ __device__ __forceinline__ void epilogue_wide(const KernelArgs &args, const Work
       bias.init(args, m0, n0, lane);
       bq = bias.col(0);
     }
+    // source quads in consumption order: quad i is (row block 2p + fp, column block g) with
+    // i = 2 FN p + 2 g + fp
+    constexpr int NQ = CFG::FM * CFG::FN;
+    using Src = WideSource<CFG, SES>;
+    Src src;
+    auto src_issue = [&](int j) {
+      if (j < NQ) {
+        const int p = j / (2 * CFG::FN), r = j % (2 * CFG::FN);
+        src.issue(j, 2 * p + r % 2, r / 2);
+      }
+    };
+    if constexpr (SES != 0) {
+      src.init(args, m0, n0, lane, bias.ok);
+#pragma unroll
+      for (int j = 0; j < Src::RING; ++j) src_issue(j);
+    }
 #pragma unroll
     for (int p = 0; p < CFG::FM / 2; ++p) {
 #pragma unroll
@@ -1476,7 +1567,13 @@ __device__ __forceinline__ void epilogue_wide(const KernelArgs &args, const Work
 #pragma unroll
         for (int fp = 0; fp < 2; ++fp) {
           f32x4 v;
-          if constexpr (FUSE != FUSE_OFF)
+          if constexpr (SES != 0) {
+            const int i = 2 * CFG::FN * p + 2 * g + fp;
+            const f32x4 s = src.take(i);
+            src_issue(i + Src::RING);
+            v = wide_fused_quad<CFG, FUSE>(args, acc[2 * p + fp][g], alpha, bq, bias, ec,
+                                           2 * p + fp, g, s);
+          } else if constexpr (FUSE != FUSE_OFF)
             v = wide_fused_quad<CFG, FUSE>(args, acc[2 * p + fp][g], alpha, bq, bias, ec,
                                            2 * p + fp, g);
           else
@@ -1524,7 +1621,7 @@ __device__ __forceinline__ void epilogue_direct(const KernelArgs &args, const Wo
 // output type (OUT: element bytes), and the stores go through a buffer range that starts at the
 // sub-tile's origin: rows past M fall outside it, and a column block past N gets an offset past
 // its end, so a store outside C is dropped without a branch around it.
-template <class CFG, int ACT, int OUT>
+template <class CFG, int ACT, int OUT, int SES = 0>
 __device__ __forceinline__ void direct_fused_stores(const KernelArgs &args,
                                                     const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
                                                     float alpha, int64_t m0, int64_t n0, int lane,
@@ -1537,6 +1634,18 @@ __device__ __forceinline__ void direct_fused_stores(const KernelArgs &args,
   // hoisted there and held in scalar registers through the whole kernel
   asm volatile("" : "+s"(row_b));
   const uint32_t lane_off = (uint32_t)(lane & 15) * row_b + (uint32_t)(lane >> 4) * 4 * OUT;
+  // source quads in consumption order: quad i is (f, g) with i = FM g + f
+  constexpr int NQ = CFG::FM * CFG::FN;
+  using Src = WideSource<CFG, SES>;
+  Src src;
+  auto src_issue = [&](int j) {
+    if (j < NQ) src.issue(j, j % CFG::FM, j / CFG::FM);
+  };
+  if constexpr (SES != 0) {
+    src.init(args, m0, n0, lane, bias.ok);
+#pragma unroll
+    for (int j = 0; j < Src::RING; ++j) src_issue(j);
+  }
   f32x4 bq = bias.col(0);
 #pragma unroll
   for (int g = 0; g < CFG::FN; ++g) {
@@ -1545,7 +1654,12 @@ __device__ __forceinline__ void direct_fused_stores(const KernelArgs &args,
     const uint32_t off = ((bias.ok >> (16 + g)) & 1u) ? lane_off + g * 16 * OUT : kOOB;
 #pragma unroll
     for (int f = 0; f < CFG::FM; ++f) {
-      const f32x4 v = wide_fused_quad<CFG, ACT>(args, acc[f][g], alpha, bq, bias, ec, f, g);
+      f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (SES != 0) {
+        s = src.take(CFG::FM * g + f);
+        src_issue(CFG::FM * g + f + Src::RING);
+      }
+      const f32x4 v = wide_fused_quad<CFG, ACT>(args, acc[f][g], alpha, bq, bias, ec, f, g, s);
       const uint32_t soff = (uint32_t)(f * 16) * row_b;
       if constexpr (OUT == 1)
         __builtin_amdgcn_raw_buffer_store_b32(pack_e4m3x4(v * ec.inv_d), cr, off, soff, 0);
@@ -1560,7 +1674,7 @@ __device__ __forceinline__ void direct_fused_stores(const KernelArgs &args,
   }
 }
 
-template <class CFG, int ACT>
+template <class CFG, int ACT, int SES = 0>
 __device__ __forceinline__ void epilogue_direct_fused(const KernelArgs &args, const WorkItem &w,
                                                       const acc_t<CFG> (&acc)[CFG::FM][CFG::FN],
                                                       float alpha, int wm, int wn, int lane,
@@ -1573,17 +1687,28 @@ __device__ __forceinline__ void epilogue_direct_fused(const KernelArgs &args, co
   bias.init(args, m0, n0, lane);
   if constexpr (CFG::DT == DT_FP8) {
     if (args.out_fp8)
-      direct_fused_stores<CFG, ACT, 1>(args, acc, alpha, m0, n0, lane, bias, ec);
+      direct_fused_stores<CFG, ACT, 1, SES>(args, acc, alpha, m0, n0, lane, bias, ec);
     else if (args.out_bf16)
-      direct_fused_stores<CFG, ACT, 2>(args, acc, alpha, m0, n0, lane, bias, ec);
+      direct_fused_stores<CFG, ACT, 2, SES>(args, acc, alpha, m0, n0, lane, bias, ec);
     else
-      direct_fused_stores<CFG, ACT, 4>(args, acc, alpha, m0, n0, lane, bias, ec);
+      direct_fused_stores<CFG, ACT, 4, SES>(args, acc, alpha, m0, n0, lane, bias, ec);
   } else {
     // The bf16 kernels keep one loop that picks the store per quad (flat addresses, skipped
     // outside C): with the three copies above, the compiler put vmcnt waits inside the 256 x 224
     // fused kernel's k-loop (its bias + GELU workload measured 4 % slower), while none of the
     // benchmarked workloads sends a bf16 kernel down this path.
     const int64_t mb = m0 + (lane & 15), nb = n0 + (lane >> 4) * 4;
+    constexpr int NQ = CFG::FM * CFG::FN;
+    using Src = WideSource<CFG, SES>;
+    Src src;
+    auto src_issue = [&](int j) {
+      if (j < NQ) src.issue(j, j % CFG::FM, j / CFG::FM);
+    };
+    if constexpr (SES != 0) {
+      src.init(args, m0, n0, lane, bias.ok);
+#pragma unroll
+      for (int j = 0; j < Src::RING; ++j) src_issue(j);
+    }
     f32x4 bq = bias.col(0);
 #pragma unroll
     for (int g = 0; g < CFG::FN; ++g) {
@@ -1592,7 +1717,12 @@ __device__ __forceinline__ void epilogue_direct_fused(const KernelArgs &args, co
 #pragma unroll
       for (int f = 0; f < CFG::FM; ++f) {
         const int64_t m = mb + f * 16;
-        const f32x4 v = wide_fused_quad<CFG, ACT>(args, acc[f][g], alpha, bq, bias, ec, f, g);
+        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (SES != 0) {
+          s = src.take(CFG::FM * g + f);
+          src_issue(CFG::FM * g + f + Src::RING);
+        }
+        const f32x4 v = wide_fused_quad<CFG, ACT>(args, acc[f][g], alpha, bq, bias, ec, f, g, s);
         if (bias.inside(f, g)) {
           if (args.out_fp8)
             *(uint32_t *)(args.C + m * args.ldc + n) = pack_e4m3x4(v * ec.inv_d);
@@ -1963,9 +2093,15 @@ gemm_kernel_wide(KernelArgs args) {
       wide_partial_store<CFG>(args, cw, acc, b, wm, wn, lane, tid);
     } else if (CFG::WM == 128 && args.out_bf16) {  // staged through the wave's LDS slice
       if constexpr (CFG::WM == 128)
-        epilogue_wide<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
+        with_source<FUSE>(args, [&](auto es) {
+          epilogue_wide<CFG, FUSE, decltype(es)::value>(args, cw, acc, alpha, wm, wn, lane, slice,
+                                                        ec);
+        });
     } else if constexpr (FUSE != FUSE_OFF) {
-      epilogue_direct_fused<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, ec);
+      with_source<FUSE>(args, [&](auto es) {
+        epilogue_direct_fused<CFG, FUSE, decltype(es)::value>(args, cw, acc, alpha, wm, wn, lane,
+                                                              ec);
+      });
     } else {
       epilogue_direct<CFG>(args, cw, acc, alpha, wm, wn, lane, ec);
     }
@@ -2317,9 +2453,15 @@ gemm_kernel_wide1(KernelArgs args) {
         wide_partial_store<CFG>(args, cw, acc, b, wm, wn, lane, tid);
       } else if (!DEFER && CFG::WM == 128 && args.out_bf16) {  // staged through the LDS slice
         if constexpr (!DEFER && CFG::WM == 128)
-          epilogue_wide<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, slice, ec);
+          with_source<FUSE>(args, [&](auto es) {
+            epilogue_wide<CFG, FUSE, decltype(es)::value>(args, cw, acc, alpha, wm, wn, lane,
+                                                          slice, ec);
+          });
       } else if constexpr (FUSE != FUSE_OFF) {
-        epilogue_direct_fused<CFG, FUSE>(args, cw, acc, alpha, wm, wn, lane, ec);
+        with_source<FUSE>(args, [&](auto es) {
+          epilogue_direct_fused<CFG, FUSE, decltype(es)::value>(args, cw, acc, alpha, wm, wn,
+                                                                lane, ec);
+        });
       } else {
         epilogue_direct<CFG>(args, cw, acc, alpha, wm, wn, lane, ec);
       }
@@ -2339,11 +2481,6 @@ gemm_kernel_wide1(KernelArgs args) {
   if constexpr (FUSE != FUSE_OFF)
     if (args.epi & EPI_AMAX)
       publish_amax<CFG::WAVES>(args.amax, ec.am, smem + CFG::LDS_BYTES, wave, lane);
-}
-
-__global__ void clear_ints_kernel(int *p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
 }
 
 }  // namespace dg

@@ -103,8 +103,7 @@ typedef enum {
  * -- all applied to the finished accumulators before C is stored once (a Stream-K tile: by the
  * split that writes it, after the full sum).  At most one source bit, one bias bit and one
  * activation bit.  A plan with epilogue bits or an e4m3 output runs on the wide-wave or the
- * cooperative kernel (GEMM_FLAG_PINGPONG with them: GEMM_ERR_UNSUPPORTED); a plan with a source
- * bit runs on the cooperative kernel (GEMM_FLAG_WIDE with one: GEMM_ERR_UNSUPPORTED). */
+ * cooperative kernel (GEMM_FLAG_PINGPONG with them: GEMM_ERR_UNSUPPORTED). */
 #define GEMM_EPI_BIAS_ROW 0x1u  /* Z[m][n] += bias[m]; bias holds M floats                     */
 #define GEMM_EPI_BIAS_COL 0x2u  /* Z[m][n] += bias[n]; bias holds N floats                     */
 #define GEMM_EPI_RELU 0x4u      /* Y = max(Z, 0)                                                  */

@@ -126,13 +126,13 @@ def create(**kw):
     # fused epilogue
     (dict(epilogue=0x100), L.GEMM_ERR_INVALID_ARG),                      # unknown bit
     (dict(epilogue=L.GEMM_EPI_SOURCE_F32 | L.GEMM_EPI_SOURCE_BF16), L.GEMM_ERR_INVALID_ARG),
-    (dict(epilogue=L.GEMM_EPI_SOURCE_F32), L.GEMM_OK),                   # cooperative kernel
+    (dict(epilogue=L.GEMM_EPI_SOURCE_F32), L.GEMM_OK),
     (dict(epilogue=L.GEMM_EPI_SOURCE_BF16 | L.GEMM_EPI_GELU, sched=L.GEMM_SCHED_STREAMK),
      L.GEMM_OK),
     (dict(epilogue=L.GEMM_EPI_SOURCE_F32, K=0), L.GEMM_OK),
-    (dict(epilogue=L.GEMM_EPI_SOURCE_F32, flags=L.GEMM_FLAG_WIDE), L.GEMM_ERR_UNSUPPORTED),
+    (dict(epilogue=L.GEMM_EPI_SOURCE_F32, flags=L.GEMM_FLAG_WIDE), L.GEMM_OK),
     (dict(epilogue=L.GEMM_EPI_SOURCE_F32, flags=L.GEMM_FLAG_PINGPONG), L.GEMM_ERR_UNSUPPORTED),
-    (dict(epilogue=L.GEMM_EPI_SOURCE_F32, bm=256, bn=224), L.GEMM_ERR_UNSUPPORTED),
+    (dict(epilogue=L.GEMM_EPI_SOURCE_F32, bm=256, bn=224), L.GEMM_OK),
     (dict(epilogue=L.GEMM_EPI_BIAS_ROW | L.GEMM_EPI_BIAS_COL), L.GEMM_ERR_INVALID_ARG),
     (dict(epilogue=L.GEMM_EPI_RELU | L.GEMM_EPI_GELU), L.GEMM_ERR_INVALID_ARG),
     (dict(epilogue=L.GEMM_EPI_SILU | L.GEMM_EPI_GELU), L.GEMM_ERR_INVALID_ARG),
@@ -236,30 +236,35 @@ def test_fused_epilogue_plans():
         assert a.info.kernel in (0, 3), (M, N, K)
 
 
-def test_source_plans_run_on_the_cooperative_kernel():
-    """Only the cooperative kernel reads a source matrix: every plan with one runs it, whatever
-    the planner would pick without it, and the cost model ranks cooperative candidates only (a
-    plan without a source keeps its candidate set)."""
+def test_source_plans_take_the_plain_plans_kernel():
+    """A source matrix is read by the wide-wave and the cooperative kernels alike: a plan with one
+    runs the kernel the same plan without it runs (and the kernel asked for by a flag).  The cost
+    model adds the source's bytes to every candidate and ranks one more for such plans,
+    cooperative 256 x 256 data-parallel, which plans without a source never see."""
     for M, N, K, sched in ((4096, 4096, 4096, L.GEMM_SCHED_AUTO),
                            (4096, 4096, 4096, L.GEMM_SCHED_PERSISTENT),
                            (4096, 14336, 4096, L.GEMM_SCHED_AUTO),
                            (512, 512, 65536, L.GEMM_SCHED_STREAMK),
-                           (512, 512, 65536, L.GEMM_SCHED_AUTO), (300, 264, 0, L.GEMM_SCHED_STATIC)):
+                           (300, 264, 0, L.GEMM_SCHED_STATIC)):
         for src in (L.GEMM_EPI_SOURCE_F32, L.GEMM_EPI_SOURCE_BF16):
-            p = L.Plan(L.make_desc(M, N, K, sched=sched, num_workers=256,
-                                   epilogue=src | L.GEMM_EPI_GELU))
-            assert p.info.kernel == 0, (M, N, K, sched)
-            plain = L.Plan(L.make_desc(M, N, K, sched=sched, num_workers=256,
-                                       epilogue=L.GEMM_EPI_GELU))
-            assert plain.info.kernel == (0 if K == 0 else 3), (M, N, K, sched)
+            for flags in (0, L.GEMM_FLAG_COOPERATIVE):
+                p = L.Plan(L.make_desc(M, N, K, sched=sched, num_workers=256, flags=flags,
+                                       epilogue=src | L.GEMM_EPI_GELU))
+                plain = L.Plan(L.make_desc(M, N, K, sched=sched, num_workers=256, flags=flags,
+                                           epilogue=L.GEMM_EPI_GELU))
+                want = 0 if (K == 0 or flags) else 3
+                assert p.info.kernel == plain.info.kernel == want, (M, N, K, sched, flags)
     ranked = L.rank_configs(L.make_desc(4096, 4096, 4096, sched=L.GEMM_SCHED_AUTO,
                                         num_workers=256, epilogue=L.GEMM_EPI_SOURCE_BF16))
-    assert ranked and all(r.kernel == 0 for r in ranked)
-    assert any(r.bm == 256 and r.sched == L.GEMM_SCHED_PERSISTENT for r in ranked)
     plain = L.rank_configs(L.make_desc(4096, 4096, 4096, sched=L.GEMM_SCHED_AUTO,
                                        num_workers=256))
-    assert not any(r.kernel == 0 and r.bm == 256 and r.sched == L.GEMM_SCHED_PERSISTENT
-                   for r in plain)
+    extra = lambda rs: [r for r in rs if r.kernel == 0 and r.bm == 256 and
+                        r.sched == L.GEMM_SCHED_PERSISTENT]
+    assert len(ranked) == len(plain) + 1 and len(extra(ranked)) == 1 and not extra(plain)
+    # the source's bytes raise every candidate's L2 clocks
+    key = lambda r: (r.kernel, r.bm, r.bn, r.sched)
+    base = {key(r): r.cycles_l2 for r in plain}
+    assert all(r.cycles_l2 > base[key(r)] for r in ranked if key(r) in base)
 
 
 @pytest.mark.skipif(__import__("torch").cuda.is_available(),

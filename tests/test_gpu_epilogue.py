@@ -192,8 +192,9 @@ def test_fused_epilogue_parity(dev, case):
     check(op, got, am, out, bias_kind, bias, act, scale_d, name)
 
 
-# Z = alpha Acc + beta S: the cooperative kernel, every output type, S in fp32 or bf16, S = C
-# (in place), Stream-K in both fixup modes, e4m3 operands, K = 0
+# Z = alpha Acc + beta S on both kernel families and every epilogue path (wide-wave: staged bf16
+# on 256 x 256 and 256 x 224, direct fp32 / e4m3 / bf16 on 64-wide sub-tiles, the Stream-K
+# reduction; cooperative: whole tiles, lock chain, K = 0), S in fp32 or bf16, S = C (in place)
 # id, M, N, K, operand type, output, source type, in place, beta, flags, tile, sched, workers,
 # bias, activation
 SRC_CASES = [
@@ -215,6 +216,18 @@ SRC_CASES = [
      L.GEMM_SCHED_STREAMK, 9, None, "silu"),
     ("src_f32_zero_depth", 130, 136, 0, "bf16", "f32", "f32", False, 0.5, 0, 128,
      L.GEMM_SCHED_PERSISTENT, 4, "col", "gelu"),
+    ("src_coop256_f32_bias_col_gelu", 520, 776, 1000, "bf16", "f32", "f32", False, 0.75,
+     L.GEMM_FLAG_COOPERATIVE, 256, L.GEMM_SCHED_PERSISTENT, 3, "col", "gelu"),
+    ("src_coop128_bf16_in_place", 300, 264, 104, "bf16", "bf16", "bf16", True, -2.0,
+     L.GEMM_FLAG_COOPERATIVE, 128, L.GEMM_SCHED_PERSISTENT, 4, "row", "silu"),
+    ("src_wide224_bf16_in_place_gelu", 520, 904, 1000, "bf16", "bf16", "bf16", True, 1.5, 0,
+     (256, 224), L.GEMM_SCHED_PERSISTENT, 3, "col", "gelu"),
+    ("src_wide224_fp8_e4m3_f32_src", 776, 688, 1040, "e4m3", "e4m3", "f32", False, -0.75, 0,
+     (256, 224), L.GEMM_SCHED_PERSISTENT, 4, "row", "relu"),
+    ("src_wide256_fp8_streamk_bf16_src", 512, 768, 8192, "e4m3", "bf16", "bf16", False, 0.5,
+     L.GEMM_FLAG_WIDE, 256, L.GEMM_SCHED_STREAMK, 4, "row", "silu"),
+    ("src_wide256_bf16_f32_in_place_ragged", 300, 520, 3000, "bf16", "f32", "f32", True, 1.0,
+     L.GEMM_FLAG_WIDE, 256, L.GEMM_SCHED_PERSISTENT, 2, None, None),
 ]
 
 
@@ -233,26 +246,45 @@ def test_source_term_parity(dev, case):
         scale_d = float(np.float32(E.amax(y) / 448.0 * 0.8))
     got, am, plan = run_epi(op, dev, out, bias_kind, bias, act, True, scale_d, flags, sched,
                             workers, tile, source=S, beta=beta, in_place=in_place)
-    assert plan.info.kernel == 0
+    coop = K == 0 or flags & (L.GEMM_FLAG_COOPERATIVE | L.GEMM_FLAG_STREAMK_CHAIN)
+    assert plan.info.kernel == (0 if coop else 3)
     if sched == L.GEMM_SCHED_STREAMK:
         assert plan.info.sk_tiles > 0
         assert plan.info.streamk_mode == (0 if flags & L.GEMM_FLAG_STREAMK_CHAIN else 1)
     check(op, got, am, out, bias_kind, bias, act, scale_d, name, s_vals, beta)
 
 
-def test_zero_beta_reads_no_source(dev):
+@pytest.mark.parametrize("flags", [0, L.GEMM_FLAG_COOPERATIVE])
+def test_zero_beta_reads_no_source(dev, flags):
     """beta = 0: the source is not read, so NaNs in it do not reach C, and the bits equal those
-    of the same plan run without a source (cooperative kernel both)."""
+    of the same plan run without a source."""
     M, N, K = 264, 520, 256
     op = operands("beta0", M, N, K, "bf16")
     bias = gi.make_vector(N, seed=23)
     S = torch.full((M, N), float("nan"), dtype=torch.float32)
-    got, am, plan = run_epi(op, dev, "f32", "col", bias, "gelu", True, 1.0, 0, tile=128,
+    got, am, plan = run_epi(op, dev, "f32", "col", bias, "gelu", True, 1.0, flags, tile=128,
                             source=S, beta=0.0)
-    plain, am2, plan2 = run_epi(op, dev, "f32", "col", bias, "gelu", True, 1.0,
-                                L.GEMM_FLAG_COOPERATIVE, tile=128)
-    assert plan.info.kernel == plan2.info.kernel == 0
+    plain, am2, plan2 = run_epi(op, dev, "f32", "col", bias, "gelu", True, 1.0, flags,
+                                tile=128)
+    assert plan.info.kernel == plan2.info.kernel == (0 if flags else 3)
     assert np.isfinite(got).all() and np.array_equal(got, plain) and am == am2
+
+
+@pytest.mark.parametrize("tile", [256, (256, 224), 128])
+def test_source_of_zero_keeps_the_bits(dev, tile):
+    """A zero source with beta = 1 adds exact zeros: the wide-wave kernel's source instantiation
+    must store the bits of its plain fused instantiation (same products, same bias and
+    activation), on the staged and the direct paths."""
+    M, N, K = 520, 904, 1000
+    op = operands("zero_src", M, N, K, "bf16")
+    bias = gi.make_vector(N, seed=29)
+    for out in ("bf16", "f32"):
+        S = torch.zeros((M, N), dtype=torch.float32)
+        got, am, plan = run_epi(op, dev, out, "col", bias, "gelu", True, 1.0, 0, tile=tile,
+                                source=S, beta=1.0)
+        plain, am2, _ = run_epi(op, dev, out, "col", bias, "gelu", True, 1.0, 0, tile=tile)
+        assert plan.info.kernel == 3
+        assert np.array_equal(got, plain) and am == am2, (tile, out)
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16", "e4m3"])
