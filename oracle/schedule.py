@@ -22,7 +22,7 @@ Sources
     (K_idx, k_tile_count, is_final = K_idx + k_tile_count == k-tiles per tile); the worker walks
     its tiles backwards; the lock counts the cumulative k-tiles reduced so far.
 
-Reading where the pages are open (each is listed in the design doc):
+Readings where the pages are open:
   * a short last strip in the grouped mappings holds the remaining tile rows (columns);
   * blocking: boxes of H tile-rows x W tile-columns; the boxes of a box row are visited along N,
     box rows along M; inside a box M runs fastest (as in a Grouped-M strip); boxes at the bottom
