@@ -391,3 +391,25 @@ def test_amax_ignores_positions_past_the_edge(dev, kern, out, bias_kind):
         assert np.array_equal(E4M3_TABLE[got], E4M3_TABLE[E.quantize_e4m3(y, 0.125)])
     else:
         assert np.array_equal(got, y)
+
+
+@pytest.mark.parametrize("src_kind", ["f32", "bf16"])
+def test_gemm_helper_with_source(dev, src_kind):
+    """The package's one-call gemm() with a source, a column bias and ReLU, on the planner's own
+    choices, against the oracle."""
+    import dense_gemm_design_amd as dg
+    M, N, K = 520, 776, 1000
+    op = operands("helper_src_" + src_kind, M, N, K, "bf16")
+    A, B, _, _ = to_device(op, torch, dev)
+    bias = gi.make_vector(N, seed=31)
+    S, s_vals = make_source(M, N, src_kind, seed=37)
+    C = dg.gemm(A.view(torch.bfloat16), B.view(torch.bfloat16), out_dtype="f32",
+                bias_col=torch.from_numpy(bias).to(dev), activation="relu",
+                source=S.to(dev), beta=-0.5)
+    torch.cuda.synchronize()
+    z, y = expected(op, "col", bias, "relu", s_vals, -0.5)
+    ma = oracle.max_abs_decoded(op.A, oracle_dtype(op), op.scale_a)
+    mb = oracle.max_abs_decoded(op.B, oracle_dtype(op), op.scale_b)
+    tol = E.tolerance(y, z, op.K, ma, mb, out="f32", s_ref=-0.5 * s_vals)
+    got = decode_output(C, torch)
+    assert np.isfinite(got).all() and (np.abs(got - y) <= tol).all()
