@@ -318,7 +318,7 @@ def validate_operands(desc, A, B, C, scale_a=None, scale_b=None, workspace=None,
         if desc.epilogue & (GEMM_EPI_SOURCE_F32 | GEMM_EPI_SOURCE_BF16) and float(beta) != 0.0:
             f32 = desc.epilogue & GEMM_EPI_SOURCE_F32
             need(source, "source", (torch.float32,) if f32 else (torch.bfloat16, torch.int16),
-                 numel=M * N)
+                 numel=M * N, at_least=True)   # like C, which it may be
         if workspace_bytes:
             if workspace is None:
                 raise ValueError(f"this plan needs a workspace of {workspace_bytes} bytes")

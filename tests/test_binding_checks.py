@@ -50,7 +50,7 @@ def test_source_operand():
     p = plan_of(epilogue=L.GEMM_EPI_SOURCE_F32)
     refused(r"source is required", p.validate, A, B, C, source=None, beta=0.5)
     refused(r"source has dtype", p.validate, A, B, C, source=C.to(torch.bfloat16), beta=0.5)
-    refused(r"source has 32640 elements; expected 32768", p.validate, A, B, C,
+    refused(r"source has 32640 elements; expected at least 32768", p.validate, A, B, C,
             source=C[: M - 1], beta=0.5)
     refused(r"is on cpu", p.validate, A, B, C, source=C, beta=0.5)      # C itself: accepted
     refused(r"is on cpu", p.validate, A, B, C, source=None, beta=0.0)   # nothing read
