@@ -305,6 +305,10 @@ RUNS = {
     # is quantised back to e4m3 with amax tracking
     "bf16_mlp_up_bias_gelu": ("bf16_mlp_up", "grouped_m", 8, "auto", 0, "bf16", 0, 0, "",
                               {"bias": "col", "act": "gelu"}),
+    # ... and with a bf16 source matrix S added first (Z = Acc + S, then the bias and GELU)
+    "bf16_mlp_up_source_bias_gelu": ("bf16_mlp_up", "grouped_m", 8, "auto", 0, "bf16", 0, 0, "",
+                                     {"source": "bf16", "beta": 1.0, "bias": "col",
+                                      "act": "gelu"}),
     "fp8_8192_e4m3_amax": ("fp8_8192", "grouped_m", 16, "persistent", 0, "e4m3", 0, 0, "",
                            {"amax": True}),
 }
@@ -354,6 +358,8 @@ def setup_run(name, torch, dg, gi, cache):
     epi |= {None: 0, "row": dg.GEMM_EPI_BIAS_ROW, "col": dg.GEMM_EPI_BIAS_COL}[
         epi_spec.get("bias")]
     epi |= dg.GEMM_EPI_AMAX if epi_spec.get("amax") else 0
+    src_kind = epi_spec.get("source")
+    epi |= {None: 0, "f32": dg.GEMM_EPI_SOURCE_F32, "bf16": dg.GEMM_EPI_SOURCE_BF16}[src_kind]
     desc = dg.make_desc(op.M, op.N, op.K,
                         dg.GEMM_BF16 if op.dtype == "bf16" else dg.GEMM_FP8_E4M3,
                         dg.OUT_DTYPES[out], dg.MAPPINGS[mapping],
@@ -366,14 +372,24 @@ def setup_run(name, torch, dg, gi, cache):
     if plan.workspace_bytes:
         ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=A.device)
     bias = amax = scale_d = bias_host = None
-    bias_bytes = 0
+    epi_bytes = 0  # bytes the epilogue reads besides A and B (bias, source)
     if epi_spec.get("bias"):
         n = op.M if epi_spec["bias"] == "row" else op.N
         bias_host = gi.make_vector(n, seed=wl.seed + 7)
         bias = torch.from_numpy(bias_host).to(A.device)
-        bias_bytes = 4 * n
+        epi_bytes = 4 * n
     if epi_spec.get("amax"):
         amax = torch.zeros(1, dtype=torch.float32, device=A.device)
+    source = source_host = None
+    beta = float(epi_spec.get("beta", 0.0))
+    if src_kind:  # a seeded N(0, 1) matrix, held in the source's element type
+        v = gi.make_vector(op.M * op.N, seed=wl.seed + 13).reshape(op.M, op.N)
+        t = torch.from_numpy(v)
+        if src_kind == "bf16":
+            t = t.to(torch.bfloat16)
+        source = t.to(A.device)
+        source_host = t.float().numpy()
+        epi_bytes += t.numel() * t.element_size()
     if out == "e4m3":  # the output's dequantisation scale: N(0, 1) operands give |C| up to
         # about 4 sqrt(K), mapped onto the format's 448
         scale_d = torch.tensor([4.0 * op.K ** 0.5 / 448.0], dtype=torch.float32,
@@ -381,10 +397,11 @@ def setup_run(name, torch, dg, gi, cache):
 
     def launch(stream=None, out_buf=None):
         plan.run(A, B, C if out_buf is None else out_buf, sa, sb, ws, stream, bias=bias,
-                 scale_d=scale_d, amax=amax)
+                 scale_d=scale_d, amax=amax, source=source, beta=beta)
     return {"name": name, "workload": wl_name, "op": op, "plan": plan, "C": C, "ws": ws,
             "out": out, "epi": epi_spec, "bias": bias, "bias_host": bias_host, "amax": amax,
-            "scale_d": scale_d, "bias_bytes": bias_bytes, "mapping": mapping, "sched": sched,
+            "source_host": source_host, "beta": beta,
+            "scale_d": scale_d, "epi_bytes": epi_bytes, "mapping": mapping, "sched": sched,
             "launch": launch}
 
 
@@ -397,8 +414,8 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0, batches=1
     import statistics
     run = setup_run(name, torch, dg, gi, cache)
     op, plan, out, epi_spec = run["op"], run["plan"], run["out"], run["epi"]
-    wl_name, mapping, sched, bias_bytes = run["workload"], run["mapping"], run["sched"], \
-        run["bias_bytes"]
+    wl_name, mapping, sched, epi_bytes = run["workload"], run["mapping"], run["sched"], \
+        run["epi_bytes"]
     A = cache[wl_name][1]
     stream = torch.cuda.current_stream()
 
@@ -461,7 +478,7 @@ def time_run(name, steps, warmup, torch, dg, gi, cache, settle_ms=0.0, batches=1
     # against the peak at the clock the chip held: CUs x FLOP/clk/CU x f_measured
     res["frac_clock_adjusted"] = (res["frac_of_peak"] * PEAK_CLOCK_MHZ / board["clock_mhz"]
                                   if board["clock_mhz"] else None)
-    alg_bytes = (op.A.nbytes + op.B.nbytes + bias_bytes +
+    alg_bytes = (op.A.nbytes + op.B.nbytes + epi_bytes +
                  op.M * op.N * {"bf16": 2, "f32": 4, "e4m3": 1}[out])
     res["alg_bytes"] = alg_bytes
     res["hbm_gbs_alg"] = alg_bytes / (dev_ms * 1e-3) / 1e9
@@ -575,7 +592,8 @@ def main():
     if not args.no_secondary:
         for name in ("bf16_4096_pp", "bf16_4096_coop", "bf16_4096_linear", "bf16_4096_t128",
                      "bf16_4096_blocked", "fp8_8192_pp", "fp8_8192_e4m3_amax", "fp8_8192_blocked",
-                     "fp8_8192_morton", "fp8_8192", "bf16_mlp_up_bias_gelu", "bf16_mlp_up",
+                     "fp8_8192_morton", "fp8_8192", "bf16_mlp_up_bias_gelu",
+                     "bf16_mlp_up_source_bias_gelu", "bf16_mlp_up",
                      "bf16_mlp_up_t256",
                      "bf16_streamk", "bf16_256"):
             steps = max(10, args.steps // (4 if name.startswith("fp8_8192") else 1))

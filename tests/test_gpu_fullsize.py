@@ -91,10 +91,13 @@ def check_every_output(run):
     bias_host = run["bias_host"]
     bias = {} if bias_host is None else {
         ("bias_row" if epi["bias"] == "row" else "bias_col"): bias_host.astype(np.float64)}
-    z, y = E.apply(ref, act=epi.get("act"), **bias)
+    src = {} if run.get("source_host") is None else {
+        "source": run["source_host"].astype(np.float64), "beta": run["beta"]}
+    z, y = E.apply(ref, act=epi.get("act"), **bias, **src)
+    s_ref = src["beta"] * src["source"] if src else None
     if out == "e4m3":
         scale_d = float(run["scale_d"].cpu()[0])
-        tol = E.tolerance(y, z, op.K, amax_a, amax_b, out="f32")
+        tol = E.tolerance(y, z, op.K, amax_a, amax_b, out="f32", s_ref=s_ref)
         lo, hi = E.quantized_bounds(y, tol, scale_d)
         got = e4m3_table()[C.cpu().numpy()]
         bad = ~((lo <= got) & (got <= hi))
@@ -103,7 +106,7 @@ def check_every_output(run):
         worst = 0.0
     else:
         got = C.float().cpu().numpy().astype(np.float64)
-        tol = E.tolerance(y, z, op.K, amax_a, amax_b, out=out)
+        tol = E.tolerance(y, z, op.K, amax_a, amax_b, out=out, s_ref=s_ref)
         err = np.abs(got - y)
         bad = ~(err <= tol)
         assert not bad.any(), f"{run['name']}: {int(bad.sum())} of {bad.size} outputs outside " \
