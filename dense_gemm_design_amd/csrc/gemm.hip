@@ -523,7 +523,6 @@ int gemm_create(const gemm_desc *desc, gemm_handle *out) {
   const bool fused = d.epilogue != 0 || d.dtype_c == GEMM_FP8_E4M3;
   if (fused && force_kind == KIND_PP) return GEMM_ERR_UNSUPPORTED;
 
-
   // Tile shape and scheduler: the cost model when everything is left to the planner, else
   // 256 x 256 unless asked otherwise or the problem has too few big tiles.
   int bm = d.bm, bn = d.bn;
