@@ -123,6 +123,8 @@ const KernelEntry kKernels[] = {
     entry_wide<CfgFp8_128w>(),
     entry_wide<CfgBf16_224w>(),
     entry_wide<CfgFp8_224w>(),
+    entry_wide<CfgBf16_192w>(),
+    entry_wide<CfgFp8_192w>(),
     entry<CfgFp8_128>(),
 };
 
@@ -208,6 +210,8 @@ double kernel_efficiency(int kind, int bm, int bn, int dt) {
   // 256 x 224: 2 % below 256 x 256 at whole waves (8192 x 14336 x 4096 bf16, one board: 1,367
   // against 1,397 TFLOP/s) -- 12.5 % fewer MACs per operand byte
   if (kind == KIND_WIDE && bn == 224) return dt == DT_BF16 ? 0.74 : 0.77;
+  // 256 x 192: 25 % fewer MACs per operand byte than 256 x 256
+  if (kind == KIND_WIDE && bn == 192) return dt == DT_BF16 ? 0.72 : 0.75;
   if (kind == KIND_WIDE) return dt == DT_BF16 ? 0.76 : 0.79;
   if (kind == KIND_PP) return 0.66;
   if (bm == 256) return dt == DT_BF16 ? 0.60 : 0.70;
@@ -311,6 +315,7 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
                                                                                  : 4.0;
   const ModelCand cands[] = {{KIND_WIDE, 256, 256, GEMM_SCHED_PERSISTENT},
                              {KIND_WIDE, 256, 224, GEMM_SCHED_PERSISTENT},
+                             {KIND_WIDE, 256, 192, GEMM_SCHED_PERSISTENT},
                              {KIND_WIDE, 128, 128, GEMM_SCHED_PERSISTENT},
                              {KIND_COOP, 128, 128, GEMM_SCHED_PERSISTENT},
                              {KIND_WIDE, 128, 128, GEMM_SCHED_STREAMK},

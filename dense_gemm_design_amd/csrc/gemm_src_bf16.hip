@@ -15,5 +15,6 @@ hipError_t launch_wide_src(const KernelArgs &a, int grid, bool ragged_k, hipStre
 template hipError_t launch_wide_src<CfgBf16_256w>(const KernelArgs &, int, bool, hipStream_t);
 template hipError_t launch_wide_src<CfgBf16_128w>(const KernelArgs &, int, bool, hipStream_t);
 template hipError_t launch_wide_src<CfgBf16_224w>(const KernelArgs &, int, bool, hipStream_t);
+template hipError_t launch_wide_src<CfgBf16_192w>(const KernelArgs &, int, bool, hipStream_t);
 
 }  // namespace dg

@@ -15,5 +15,6 @@ hipError_t launch_wide_src(const KernelArgs &a, int grid, bool ragged_k, hipStre
 template hipError_t launch_wide_src<CfgFp8_256w>(const KernelArgs &, int, bool, hipStream_t);
 template hipError_t launch_wide_src<CfgFp8_128w>(const KernelArgs &, int, bool, hipStream_t);
 template hipError_t launch_wide_src<CfgFp8_224w>(const KernelArgs &, int, bool, hipStream_t);
+template hipError_t launch_wide_src<CfgFp8_192w>(const KernelArgs &, int, bool, hipStream_t);
 
 }  // namespace dg

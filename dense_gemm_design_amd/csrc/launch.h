@@ -36,6 +36,11 @@ using CfgFp8_128w = TileCfg<DT_FP8, 128, 128, 128, 2, 2, 4, 1, 16>;
 // fourth wave half empty
 using CfgBf16_224w = TileCfg<DT_BF16, 256, 224, 64, 2, 2, 2, 1, 16>;
 using CfgFp8_224w = TileCfg<DT_FP8, 256, 224, 128, 2, 2, 2, 1, 16>;
+// ... and on 256 x 192 tiles (waves of 128 x 96), the next width of that set: N a multiple of
+// 6,144 makes whole waves of them (4096 x 6144: 512 tiles, two waves, where 256 x 256 tiles make
+// one and a half)
+using CfgBf16_192w = TileCfg<DT_BF16, 256, 192, 64, 2, 2, 2, 1, 16>;
+using CfgFp8_192w = TileCfg<DT_FP8, 256, 192, 128, 2, 2, 2, 1, 16>;
 
 // k-tiles one MFMA deep (e4m3 16 x 16 x 128) take the single-A-buffer form of the schedule
 template <class CFG, bool RAGGED_K, int FUSE = FUSE_OFF>

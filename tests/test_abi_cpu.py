@@ -316,16 +316,20 @@ def test_package_has_no_cpu_fallback():
             assert pat not in src, (name, pat)
 
 
-def test_tile_256x224_plans():
-    """256 x 224 tiles exist only on the wide-wave kernel: data-parallel and separate-reduction
-    Stream-K plans are built; K = 0, the lock chain and the other kernels are refused."""
+@pytest.mark.parametrize("bn", [224, 192])
+def test_wide_only_tile_plans(bn):
+    """256 x 224 and 256 x 192 tiles exist only on the wide-wave kernel: data-parallel and
+    separate-reduction Stream-K plans are built; K = 0, the lock chain and the other kernels are
+    refused."""
     import ctypes
     lib = L.load()
     h = ctypes.c_void_p()
 
+    N = 2 * bn  # 2 x 2 tiles: a Stream-K band over 8 workers
+
     def status(K, sched=L.GEMM_SCHED_PERSISTENT, flags=0, P=8):
-        d = L.make_desc(512, 448, K, L.GEMM_BF16, L.GEMM_F32, L.GEMM_MAP_LINEAR_N, 1, sched, P,
-                        256, 224, 0, flags)
+        d = L.make_desc(512, N, K, L.GEMM_BF16, L.GEMM_F32, L.GEMM_MAP_LINEAR_N, 1, sched, P,
+                        256, bn, 0, flags)
         st = lib.gemm_create(ctypes.byref(d), ctypes.byref(h))
         if st == L.GEMM_OK:
             info = L.GemmPlanInfo()

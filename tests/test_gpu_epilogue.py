@@ -169,6 +169,13 @@ CASES = [
      L.GEMM_SCHED_PERSISTENT, 4, "row", "silu"),
     ("wide224_streamk_bf16_f32_relu", 512, 448, 8192, "bf16", "f32", 0, (256, 224),
      L.GEMM_SCHED_STREAMK, 8, "col", "relu"),
+    # 256 x 192 tiles (wide-wave only)
+    ("wide192_bf16_bias_col_gelu", 520, 904, 1000, "bf16", "bf16", 0, (256, 192),
+     L.GEMM_SCHED_PERSISTENT, 3, "col", "gelu"),
+    ("wide192_fp8_e4m3_row_silu", 776, 688, 1040, "e4m3", "e4m3", 0, (256, 192),
+     L.GEMM_SCHED_PERSISTENT, 4, "row", "silu"),
+    ("wide192_streamk_fp8_f32_relu", 512, 384, 8192, "e4m3", "f32", 0, (256, 192),
+     L.GEMM_SCHED_STREAMK, 8, "col", "relu"),
 ]
 
 
@@ -224,6 +231,8 @@ SRC_CASES = [
      (256, 224), L.GEMM_SCHED_PERSISTENT, 3, "col", "gelu"),
     ("src_wide224_fp8_e4m3_f32_src", 776, 688, 1040, "e4m3", "e4m3", "f32", False, -0.75, 0,
      (256, 224), L.GEMM_SCHED_PERSISTENT, 4, "row", "relu"),
+    ("src_wide192_bf16_in_place_silu", 520, 904, 1000, "bf16", "bf16", "bf16", True, 0.5, 0,
+     (256, 192), L.GEMM_SCHED_PERSISTENT, 3, "row", "silu"),
     ("src_wide256_fp8_streamk_bf16_src", 512, 768, 8192, "e4m3", "bf16", "bf16", False, 0.5,
      L.GEMM_FLAG_WIDE, 256, L.GEMM_SCHED_STREAMK, 4, "row", "silu"),
     ("src_wide256_bf16_f32_in_place_ragged", 300, 520, 3000, "bf16", "f32", "f32", True, 1.0,

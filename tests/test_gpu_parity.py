@@ -531,7 +531,7 @@ def test_device_trace_streamk_groups(dev, tile, workers, req, flags):
     assert_within_tolerance(C, reference(op), op, "groups trace run")
 
 
-# ---- 256 x 224 tiles ---------------------------------------------------------------------------
+# ---- 256 x 224 and 256 x 192 tiles ---------------------------------------------------------------
 
 T224 = [
     # id, M, N, K, dtype, out, sched, workers, mapping, G
@@ -548,16 +548,20 @@ T224 = [
 ]
 
 
+@pytest.mark.parametrize("bn", [224, 192])
 @pytest.mark.parametrize("case", T224, ids=[c[0] for c in T224])
-def test_tile_256x224_parity(dev, case):
-    """256 x 224 tiles run on the wide-wave kernel only (waves of 128 x 112): within tolerance
-    of the oracle for data-parallel and Stream-K plans, ragged edges included."""
+def test_tile_256_narrow_parity(dev, case, bn):
+    """256 x 224 and 256 x 192 tiles run on the wide-wave kernel only (waves of 128 x 112 and
+    128 x 96): within tolerance of the oracle for data-parallel and Stream-K plans, ragged edges
+    included."""
     name, M, N, K, dt, out, sched, workers, mapping, G = case
+    if sched == L.GEMM_SCHED_STREAMK:
+        N = N * bn // 224  # the same tile count, so the tail still makes a Stream-K band
     dist = ("normal", 1.0) if dt == "e4m3" else ("uniform",)
     op = gi.make_operands(M, N, K, dt, dist, dist, seed=zlib.crc32(name.encode()) % 10000)
-    C, plan, ws = run_gpu(op, torch, dev, out, mapping, G, sched, workers, 256, bn=224)
+    C, plan, ws = run_gpu(op, torch, dev, out, mapping, G, sched, workers, 256, bn=bn)
     info = plan.info
-    assert info.kernel == 3 and (info.bm, info.bn) == (256, 224)
+    assert info.kernel == 3 and (info.bm, info.bn) == (256, bn)
     if sched == L.GEMM_SCHED_STREAMK:
         assert info.sk_tiles > 0
         err = int(ws.cpu().numpy()[info.error_offset:info.error_offset + 4].view(np.int32)[0])
@@ -565,19 +569,20 @@ def test_tile_256x224_parity(dev, case):
     assert_within_tolerance(C, reference(op), op, name)
 
 
-def test_tile_256x224_small_integers_bit_exact(dev):
-    """Exact partial sums: the 256 x 224 kernel equals the oracle bit for bit, data-parallel and
-    Stream-K, and equals the 256 x 256 kernel (same MFMA, same k order)."""
+@pytest.mark.parametrize("bn", [224, 192])
+def test_tile_256_narrow_small_integers_bit_exact(dev, bn):
+    """Exact partial sums: the 256 x 224 and 256 x 192 kernels equal the oracle bit for bit,
+    data-parallel and Stream-K, and equal the 256 x 256 kernel (same MFMA, same k order)."""
     M, N, K = 512, 896, 8192
     op = gi.make_operands(M, N, K, "bf16", ("smallint", -2, 2), ("smallint", -2, 2), seed=33)
     ref = reference(op)
     C1, p1, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_PERSISTENT, 8,
-                        256, bn=224)
+                        256, bn=bn)
     C2, p2, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_STREAMK, 24,
-                        256, bn=224)
+                        256, bn=bn)
     C3, _, _ = run_gpu(op, torch, dev, "f32", L.GEMM_MAP_LINEAR_N, 1, L.GEMM_SCHED_PERSISTENT, 8,
                        256)
-    assert p1.info.bn == 224 and p2.info.sk_tiles > 0
+    assert p1.info.bn == bn and p2.info.sk_tiles > 0
     assert np.array_equal(C1, ref) and np.array_equal(C2, ref) and np.array_equal(C3, ref)
 
 

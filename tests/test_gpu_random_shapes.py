@@ -38,7 +38,7 @@ def draw(rng):
         M=rng.choice([rng.randint(1, 64), rng.randint(1, 1100), rng.randint(200, 1100)]),
         N=8 * rng.randint(1, 137),
         K=(8 if dt == "bf16" else 16) * rng.randint(1, 190),
-        tile=rng.choice([0, 128, 256, (256, 224)]),
+        tile=rng.choice([0, 128, 256, (256, 224), (256, 192)]),
         flags=rng.choice([0, 0, L.GEMM_FLAG_WIDE, L.GEMM_FLAG_COOPERATIVE]),
         sched=rng.choice([L.GEMM_SCHED_PERSISTENT, L.GEMM_SCHED_STREAMK, L.GEMM_SCHED_STATIC,
                           L.GEMM_SCHED_AUTO]),

@@ -80,9 +80,16 @@ def test_data_movement_terms():
     ((4096, 14336, 4096), L.GEMM_FP8_E4M3, L.GEMM_BF16, ((256, 224), 3, L.GEMM_SCHED_PERSISTENT)),
     # 1792 tiles of 256 x 256 = 7 whole waves: the wider tile stays
     ((8192, 14336, 4096), L.GEMM_BF16, L.GEMM_BF16, ((256, 256), 3, L.GEMM_SCHED_PERSISTENT)),
-    # one partial wave of big tiles (168 of 256 CUs, at a higher clock) beats 128 x 128 tiles
-    # with a Stream-K tail (measured 69 against 83 us)
-    ((3072, 3072, 4096), L.GEMM_BF16, L.GEMM_BF16, ((256, 224), 3, L.GEMM_SCHED_PERSISTENT)),
+    # one partial wave of big tiles (192 of 256 CUs, at a higher clock) beats 128 x 128 tiles
+    # with a Stream-K tail (measured 69 against 83 us); of the big tiles 256 x 192 measured
+    # fastest (65.0 us, 256 x 224 70.9, 256 x 256 83.4)
+    ((3072, 3072, 4096), L.GEMM_BF16, L.GEMM_BF16, ((256, 192), 3, L.GEMM_SCHED_PERSISTENT)),
+    # N a multiple of 6,144: 256 x 192 tiles fill whole waves (measured 148.6 against 161.5 us
+    # for 256 x 224 and 181.7 for 256 x 256 in bf16, 79.6 / 85.3 / 98.2 in e4m3; 6144^2 x 4096
+    # bf16 219.0 / 239.5 / 266.6)
+    ((4096, 6144, 4096), L.GEMM_BF16, L.GEMM_BF16, ((256, 192), 3, L.GEMM_SCHED_PERSISTENT)),
+    ((4096, 6144, 4096), L.GEMM_FP8_E4M3, L.GEMM_BF16, ((256, 192), 3, L.GEMM_SCHED_PERSISTENT)),
+    ((6144, 6144, 4096), L.GEMM_BF16, L.GEMM_BF16, ((256, 192), 3, L.GEMM_SCHED_PERSISTENT)),
     ((512, 512, 65536), L.GEMM_BF16, L.GEMM_F32, (128, 3, L.GEMM_SCHED_STREAMK)),
     ((256, 256, 256), L.GEMM_BF16, L.GEMM_F32, (128, 3, L.GEMM_SCHED_PERSISTENT)),
 ])
@@ -146,7 +153,9 @@ def test_rank_validation():
     ((3072, 3072, 4096), L.GEMM_BF16, L.GEMM_BF16),
     ((1280, 1280, 32768), L.GEMM_BF16, L.GEMM_BF16),
     ((6144, 6144, 6144), L.GEMM_FP8_E4M3, L.GEMM_BF16),
+    ((4096, 6144, 4096), L.GEMM_BF16, L.GEMM_BF16),
     # shapes the model's constants were not fitted to
+    ((2048, 12288, 4096), L.GEMM_BF16, L.GEMM_BF16),
     ((5120, 5120, 5120), L.GEMM_BF16, L.GEMM_BF16),
     ((4096, 11008, 4096), L.GEMM_BF16, L.GEMM_BF16),
     ((4096, 28672, 8192), L.GEMM_FP8_E4M3, L.GEMM_BF16),
