@@ -202,11 +202,12 @@ typedef struct gemm_plan *gemm_handle;
  * output tile) and, for Stream-K, the workspace layout of the "H100 Stream-K" lesson, section 6
  * (The Lock).  The handle owns host memory only; it is freed by gemm_destroy.  On error *out is
  * left unchanged and nothing is allocated.  Supported in this version:
- *   dtype_ab BF16 with tiles (bm, bn, bk) in {(256,256,64), (256,224,64), (128,128,64)},
- *   dtype_ab FP8_E4M3 with tiles in {(256,256,128), (256,224,128), (128,128,128)}; 256 x 224
- *   tiles run on the wide-wave kernel only (a plan that needs another kernel -- K = 0, the
- *   Stream-K lock chain, or a kernel flag other than GEMM_FLAG_WIDE -- returns
- *   GEMM_ERR_UNSUPPORTED);
+ *   dtype_ab BF16 with tiles (bm, bn, bk) in {(256,256,64), (256,224,64), (256,192,64),
+ *   (128,128,64)},
+ *   dtype_ab FP8_E4M3 with tiles in {(256,256,128), (256,224,128), (256,192,128),
+ *   (128,128,128)}; 256 x 224 and 256 x 192 tiles run on the wide-wave kernel only (a plan that
+ *   needs another kernel -- K = 0, the Stream-K lock chain, or a kernel flag other than
+ *   GEMM_FLAG_WIDE -- returns GEMM_ERR_UNSUPPORTED);
  *   layout_a ROW and layout_b COL (both operands K-contiguous);
  *   K * sizeof(element) a multiple of 16 bytes and at most 2^30; N a multiple of 8 and at most
  *   2^22 (the kernels address the rows of an output tile with 32-bit byte offsets);
@@ -321,9 +322,11 @@ typedef struct gemm_config_score {
 /* Kernel-configuration heuristic: the cost model of "DeepGEMM on SM90" (section "Kernel
  * Configuration Heuristic") -- candidates from a small discrete set, a resource filter, then
  * score = max(cycles_local, cycles_L2) / wave_efficiency with the minimum winning -- re-fitted to
- * gfx950: the candidates are this library's kernels and tiles (256 x 256 and 256 x 224 wide-wave
- * data-parallel -- the block width from the page's aligned set that fills whole waves -- 128 x 128
- * wide-wave and cooperative data-parallel, and Stream-K tails on the 128 x 128 and 256 x 256 tiles),
+ * gfx950: the candidates are this library's kernels and tiles (256 x 256, 256 x 224 and
+ * 256 x 192 wide-wave data-parallel -- the narrower block widths from the page's aligned set fill
+ * whole waves where 256 does not -- 128 x 128 wide-wave and cooperative data-parallel, Stream-K
+ * tails on the 128 x 128 and 256 x 256 tiles, and for plans that read a source matrix the
+ * cooperative kernel on 256 x 256 tiles),
  * the bandwidths and per-kernel MFMA efficiencies are measured on MI355X, a matrix-core term
  * joins the two data-movement terms, and the costs that do not overlap the MAC loop are added.  Fills up to `cap` candidates, best first, and the total to
  * *n_out (GEMM_ERR_CAPACITY when cap is too small; items may be NULL with cap 0).  gemm_create
