@@ -204,14 +204,19 @@ constexpr double kLatencyClk = 2000;         // first load or store round trip o
 // wave is costed f^0.39 of a full one (fit to that pair), and no less than 1 / 1.3.
 constexpr double kPartialWaveExp = 0.39;
 constexpr double kMinPartialWave = 1.0 / 1.3;
+// Stream-K plans ran about 3 % slower per costed cycle than data-parallel ones over the same 184
+// shapes (the waits and the fixup's latency, beyond its bytes): their score is scaled by this
+constexpr double kStreamKFactor = 1.03;
 // MFMA efficiency of whole launches at the held clock (bench workloads, profiles/)
 double kernel_efficiency(int kind, int bm, int bn, int dt) {
   if (kind == KIND_WIDE && bm == 128) return dt == DT_BF16 ? 0.56 : 0.55;
   // 256 x 224: 2 % below 256 x 256 at whole waves (8192 x 14336 x 4096 bf16, one board: 1,367
   // against 1,397 TFLOP/s) -- 12.5 % fewer MACs per operand byte
   if (kind == KIND_WIDE && bn == 224) return dt == DT_BF16 ? 0.74 : 0.77;
-  // 256 x 192: 25 % fewer MACs per operand byte than 256 x 256
-  if (kind == KIND_WIDE && bn == 192) return dt == DT_BF16 ? 0.72 : 0.75;
+  // 256 x 192: 25 % fewer MACs per operand byte than 256 x 256; refit with the Stream-K factor
+  // below against every candidate timed on 184 shapes (M 1,024-8,192, N 2,560-28,672, K
+  // 2,048-8,192, both operand types): the pick's time over the fastest averages 1.0038 there
+  if (kind == KIND_WIDE && bn == 192) return dt == DT_BF16 ? 0.71 : 0.74;
   if (kind == KIND_WIDE) return dt == DT_BF16 ? 0.76 : 0.79;
   if (kind == KIND_PP) return 0.66;
   if (bm == 256) return dt == DT_BF16 ? 0.60 : 0.70;
@@ -413,6 +418,7 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
     }
     const double worst = std::max(r.cycles_mfma, std::max(r.cycles_l2, r.cycles_local));
     r.score = worst / r.wave_efficiency + r.cycles_fixed;
+    if (c.sched == GEMM_SCHED_STREAMK) r.score *= kStreamKFactor;
     out.push_back(r);
   }
   std::stable_sort(out.begin(), out.end(), [](const gemm_config_score &a,

@@ -316,7 +316,8 @@ typedef struct gemm_config_score {
                                 limit); Stream-K: busy unit slots over its units                 */
   double cycles_fixed;       /* not overlapped with the MAC loop: first loads, epilogues, and
                                 Stream-K partial sums through device memory                    */
-  double score;              /* max(mfma, l2, local) / wave_efficiency + fixed; lower is better */
+  double score;              /* max(mfma, l2, local) / wave_efficiency + fixed, times 1.03 for
+                                Stream-K; lower is better                                       */
 } gemm_config_score;
 
 /* Kernel-configuration heuristic: the cost model of "DeepGEMM on SM90" (section "Kernel
@@ -328,8 +329,10 @@ typedef struct gemm_config_score {
  * tails on the 128 x 128 and 256 x 256 tiles, and for plans that read a source matrix the
  * cooperative kernel on 256 x 256 tiles),
  * the bandwidths and per-kernel MFMA efficiencies are measured on MI355X, a matrix-core term
- * joins the two data-movement terms, and the costs that do not overlap the MAC loop are added.  Fills up to `cap` candidates, best first, and the total to
- * *n_out (GEMM_ERR_CAPACITY when cap is too small; items may be NULL with cap 0).  gemm_create
+ * joins the two data-movement terms, the costs that do not overlap the MAC loop are added, and a
+ * Stream-K plan's score is scaled by 1.03 (measured).  Fills up to `cap` candidates, best first,
+ * and the total to *n_out (GEMM_ERR_CAPACITY when cap is too small; items may be NULL with cap
+ * 0).  gemm_create
  * takes the best one when bm = bn = bk = 0, sched = GEMM_SCHED_AUTO and no kernel flag is set;
  * with a grouped mapping and group = 0 it takes the G reported here.  Needs a visible GPU only
  * when num_workers == 0. */

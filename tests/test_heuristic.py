@@ -28,7 +28,9 @@ def test_scores_are_the_models_formula():
         assert [c.score for c in ranked] == sorted(c.score for c in ranked)
         for c in ranked:
             worst = max(c.cycles_mfma, c.cycles_l2, c.cycles_local)
-            assert c.score == pytest.approx(worst / c.wave_efficiency + c.cycles_fixed, rel=1e-12)
+            factor = 1.03 if c.sched == L.GEMM_SCHED_STREAMK else 1.0
+            assert c.score == pytest.approx((worst / c.wave_efficiency + c.cycles_fixed) * factor,
+                                            rel=1e-12)
             assert c.cycles_fixed > 0
             assert 0 < c.wave_efficiency <= 1
 
@@ -90,6 +92,11 @@ def test_data_movement_terms():
     ((4096, 6144, 4096), L.GEMM_BF16, L.GEMM_BF16, ((256, 192), 3, L.GEMM_SCHED_PERSISTENT)),
     ((4096, 6144, 4096), L.GEMM_FP8_E4M3, L.GEMM_BF16, ((256, 192), 3, L.GEMM_SCHED_PERSISTENT)),
     ((6144, 6144, 4096), L.GEMM_BF16, L.GEMM_BF16, ((256, 192), 3, L.GEMM_SCHED_PERSISTENT)),
+    # 344 tiles of 256 x 256 (1.34 waves): the Stream-K tail measured no faster than the plain
+    # second wave (324 against 328 us); 256 x 192 tiles (1.81 waves) measured 268 us
+    ((2048, 11008, 8192), L.GEMM_BF16, L.GEMM_BF16, ((256, 192), 3, L.GEMM_SCHED_PERSISTENT)),
+    # 1.34 waves of 256 x 256 in e4m3: data-parallel 504 us, with the Stream-K tail 546
+    ((8192, 11008, 8192), L.GEMM_FP8_E4M3, L.GEMM_BF16, ((256, 256), 3, L.GEMM_SCHED_PERSISTENT)),
     ((512, 512, 65536), L.GEMM_BF16, L.GEMM_F32, (128, 3, L.GEMM_SCHED_STREAMK)),
     ((256, 256, 256), L.GEMM_BF16, L.GEMM_F32, (128, 3, L.GEMM_SCHED_PERSISTENT)),
 ])
@@ -154,6 +161,10 @@ def test_rank_validation():
     ((1280, 1280, 32768), L.GEMM_BF16, L.GEMM_BF16),
     ((6144, 6144, 6144), L.GEMM_FP8_E4M3, L.GEMM_BF16),
     ((4096, 6144, 4096), L.GEMM_BF16, L.GEMM_BF16),
+    # from the 184-shape sweep the 256 x 192 efficiency and the Stream-K factor were refit to
+    ((2048, 11008, 8192), L.GEMM_BF16, L.GEMM_BF16),
+    ((8192, 11008, 8192), L.GEMM_FP8_E4M3, L.GEMM_BF16),
+    ((1536, 5120, 6144), L.GEMM_FP8_E4M3, L.GEMM_BF16),
     # shapes the model's constants were not fitted to
     ((2048, 12288, 4096), L.GEMM_BF16, L.GEMM_BF16),
     ((5120, 5120, 5120), L.GEMM_BF16, L.GEMM_BF16),
