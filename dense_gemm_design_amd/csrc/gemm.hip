@@ -204,6 +204,10 @@ constexpr double kLatencyClk = 2000;         // first load or store round trip o
 // wave is costed f^0.39 of a full one (fit to that pair), and no less than 1 / 1.3.
 constexpr double kPartialWaveExp = 0.39;
 constexpr double kMinPartialWave = 1.0 / 1.3;
+// ... except a launch that is one partial wave of 256 x 224 or 256 x 192 tiles: their k-step is
+// shorter for the same load latency, so the clock headroom buys them less (measured time over
+// score 4-6 % above their classes' medians in such launches, 2 % for 256 x 256)
+constexpr double kPartialWaveExpNarrow = 0.2;
 // Stream-K plans ran about 3 % slower per costed cycle than data-parallel ones over the same 184
 // shapes (the waits and the fixup's latency, beyond its bytes): their score is scaled by this
 constexpr double kStreamKFactor = 1.03;
@@ -405,7 +409,9 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
       items = std::ceil((double)dp / P) + 2.0;  // data-parallel tiles and about two splits
     } else {
       const double waves = t / ncu, full = std::floor(waves), frac = waves - full;
-      const double last = frac > 0 ? std::max(std::pow(frac, kPartialWaveExp), kMinPartialWave) : 0.0;
+      const bool narrow_single = full == 0 && c.kind == KIND_WIDE && (c.bn == 224 || c.bn == 192);
+      const double e = narrow_single ? kPartialWaveExpNarrow : kPartialWaveExp;
+      const double last = frac > 0 ? std::max(std::pow(frac, e), kMinPartialWave) : 0.0;
       r.wave_efficiency = tiles > 0 ? waves / (full + last) : 1.0;
       items = std::ceil(t / ncu);
     }

@@ -45,6 +45,16 @@ def test_wave_efficiency_of_a_partial_last_wave():
     d256 = [c for c in L.rank_configs(desc(3072, 3072, 4096))
             if (c.bm, c.bn) == (256, 256) and c.sched == L.GEMM_SCHED_PERSISTENT][0]
     assert d256.wave_efficiency == pytest.approx((144 / 256) / (144 / 256) ** 0.39)
+    # one partial wave of the narrower tiles gains less from the headroom: f^0.2 (256 x 192: 12 x 16
+    # = 192 tiles; 256 x 224: 12 x 14 = 168), while their partial last waves of longer launches
+    # keep f^0.39 (4096 x 14336 on 256 x 192: 16 x 75 = 1200 tiles, 4.6875 waves)
+    one = L.rank_configs(desc(3072, 3072, 4096))
+    d192 = [c for c in one if (c.bm, c.bn) == (256, 192)][0]
+    assert d192.wave_efficiency == pytest.approx(0.75 / 0.75 ** 0.2)
+    d224s = [c for c in one if (c.bm, c.bn) == (256, 224)][0]
+    assert d224s.wave_efficiency == pytest.approx((168 / 256) / (168 / 256) ** 0.2)
+    m192 = [c for c in ranked if (c.bm, c.bn) == (256, 192)][0]
+    assert m192.wave_efficiency == pytest.approx(4.6875 / (4 + max(0.6875 ** 0.39, 1 / 1.3)))
     # a nearly empty wave costs no less than the clock headroom allows (1 / 1.3 of a full one):
     # 512 x 512 on 128 x 128 tiles is 16 tiles on 256 CUs
     small = [c for c in L.rank_configs(desc(512, 512, 65536, out=L.GEMM_F32))
@@ -97,6 +107,9 @@ def test_data_movement_terms():
     ((2048, 11008, 8192), L.GEMM_BF16, L.GEMM_BF16, ((256, 192), 3, L.GEMM_SCHED_PERSISTENT)),
     # 1.34 waves of 256 x 256 in e4m3: data-parallel 504 us, with the Stream-K tail 546
     ((8192, 11008, 8192), L.GEMM_FP8_E4M3, L.GEMM_BF16, ((256, 256), 3, L.GEMM_SCHED_PERSISTENT)),
+    # one partial wave (0.67) of 256 x 192 tiles against two whole waves of 128 x 128 tiles: the
+    # latter measured 63 against 72 us
+    ((1024, 8192, 4096), L.GEMM_BF16, L.GEMM_BF16, (128, 3, L.GEMM_SCHED_PERSISTENT)),
     ((512, 512, 65536), L.GEMM_BF16, L.GEMM_F32, (128, 3, L.GEMM_SCHED_STREAMK)),
     ((256, 256, 256), L.GEMM_BF16, L.GEMM_F32, (128, 3, L.GEMM_SCHED_PERSISTENT)),
 ])
@@ -165,7 +178,10 @@ def test_rank_validation():
     ((2048, 11008, 8192), L.GEMM_BF16, L.GEMM_BF16),
     ((8192, 11008, 8192), L.GEMM_FP8_E4M3, L.GEMM_BF16),
     ((1536, 5120, 6144), L.GEMM_FP8_E4M3, L.GEMM_BF16),
+    ((1024, 8192, 4096), L.GEMM_BF16, L.GEMM_BF16),
     # shapes the model's constants were not fitted to
+    ((768, 18432, 3072), L.GEMM_BF16, L.GEMM_BF16),
+    ((2560, 9216, 5120), L.GEMM_FP8_E4M3, L.GEMM_BF16),
     ((2048, 12288, 4096), L.GEMM_BF16, L.GEMM_BF16),
     ((5120, 5120, 5120), L.GEMM_BF16, L.GEMM_BF16),
     ((4096, 11008, 4096), L.GEMM_BF16, L.GEMM_BF16),
