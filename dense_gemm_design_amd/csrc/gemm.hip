@@ -197,6 +197,11 @@ static_assert(GEMM_EPI_BIAS_ROW == EPI_BIAS_ROW && GEMM_EPI_BIAS_COL == EPI_BIAS
 constexpr double kL2BytesPerClk = 57.0;      // global->LDS loads per CU
 constexpr double kLdsBytesPerClk = 256.0;    // ds_read_b128 per CU
 constexpr double kDeviceBytesPerClk = 2600;  // Stream-K partials, whole device (128 MiB in 25 us)
+// Lock chain: a hop reads and writes a tile's partial from one CU and hands the lock on; fit to
+// 64 chained splits per tile taking 462 us on 128 x 128 tiles and 590 us on 256 x 256 tiles
+// (256 x 256 x 4096 bf16, cooperative kernel, 512 units)
+constexpr double kChainBytesPerClk = 96;
+constexpr double kChainHopClk = 13000;
 constexpr double kLatencyClk = 2000;         // first load or store round trip of a phase
 // A partial last wave: the board is held at its power limit, so with a fraction f of the CUs busy
 // the busy ones clock higher (144 of 256 CUs finish a 256 x 256 x 4096 bf16 tile in 75 us, all
@@ -211,6 +216,10 @@ constexpr double kPartialWaveExpNarrow = 0.2;
 // Stream-K plans ran about 3 % slower per costed cycle than data-parallel ones over the same 184
 // shapes (the waits and the fixup's latency, beyond its bytes): their score is scaled by this
 constexpr double kStreamKFactor = 1.03;
+// ... and a band that gives each unit fewer k-steps than this is not worth its fixup: on 256 to
+// 1,024-square outputs with K = 4,096 such plans measured 20-50 % slower than data-parallel ones
+// (e4m3 512 x 512 x 4096: 2 k-steps per unit, 29 against 19 us)
+constexpr double kMinStreamKSteps = 6;
 // MFMA efficiency of whole launches at the held clock (bench workloads, profiles/)
 double kernel_efficiency(int kind, int bm, int bn, int dt) {
   if (kind == KIND_WIDE && bm == 128) return dt == DT_BF16 ? 0.56 : 0.55;
@@ -376,6 +385,7 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
       // the wide-wave kernel's separate reduction needs a band of at least P iterations
       if (c.kind == KIND_WIDE && ((int64_t)sk * Kt < P || (d.flags & GEMM_FLAG_STREAMK_CHAIN)))
         continue;
+      if ((double)sk * (double)Kt < kMinStreamKSteps * P) continue;
     }
     const int wgm = 2, wgn = e->threads / 64 / 2;  // waves along M and N
     const double t = (double)tiles, bm = c.bm, bn = c.bn, kk = (double)Keff;
@@ -418,9 +428,17 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
     const double stage_bytes = (bm + bn) * e->bk * eb;
     r.cycles_fixed = stage_bytes * (e->stages - 1) / kL2BytesPerClk + kLatencyClk +
                      items * (bm * bn * (ec + es) / kL2BytesPerClk + kLatencyClk / 2);
-    if (sk > 0) {  // separate reduction: every split writes its partial, the reduction reads it
+    if (sk > 0) {
       const double units_per_tile = std::ceil((double)P / sk);
-      r.cycles_fixed += 2.0 * sk * units_per_tile * bm * bn * 4.0 / kDeviceBytesPerClk + kLatencyClk;
+      if ((d.flags & GEMM_FLAG_STREAMK_CHAIN) || (int64_t)sk * Kt < P) {
+        // lock chain (a band with fewer iterations than units): a tile's non-empty splits add
+        // into its workspace one after another
+        const double splits = std::min(units_per_tile, (double)Kt);
+        r.cycles_fixed += splits * (2.0 * bm * bn * 4.0 / kChainBytesPerClk + kChainHopClk);
+      } else {  // separate reduction: every split writes its partial, the reduction reads it
+        r.cycles_fixed +=
+            2.0 * sk * units_per_tile * bm * bn * 4.0 / kDeviceBytesPerClk + kLatencyClk;
+      }
     }
     const double worst = std::max(r.cycles_mfma, std::max(r.cycles_l2, r.cycles_local));
     r.score = worst / r.wave_efficiency + r.cycles_fixed;

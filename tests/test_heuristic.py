@@ -110,6 +110,8 @@ def test_data_movement_terms():
     # one partial wave (0.67) of 256 x 192 tiles against two whole waves of 128 x 128 tiles: the
     # latter measured 63 against 72 us
     ((1024, 8192, 4096), L.GEMM_BF16, L.GEMM_BF16, (128, 3, L.GEMM_SCHED_PERSISTENT)),
+    # a band of 2 k-steps per unit: data-parallel 128 x 128 tiles measured 19 against 29 us
+    ((512, 512, 4096), L.GEMM_FP8_E4M3, L.GEMM_BF16, (128, 3, L.GEMM_SCHED_PERSISTENT)),
     ((512, 512, 65536), L.GEMM_BF16, L.GEMM_F32, (128, 3, L.GEMM_SCHED_STREAMK)),
     ((256, 256, 256), L.GEMM_BF16, L.GEMM_F32, (128, 3, L.GEMM_SCHED_PERSISTENT)),
 ])
@@ -125,6 +127,21 @@ def test_choices_on_measured_workloads(shape, dt, out, want):
     # gemm_create with everything left to the planner takes the best candidate
     info = L.Plan(d).info
     assert (info.bm, info.bn, info.kernel, info.sched) == (best.bm, best.bn, best.kernel, best.sched)
+
+
+def test_stream_k_fixup_costs():
+    # fewer than 6 band k-steps per unit: no Stream-K candidate (16 tiles x 32 k-steps of e4m3
+    # over 256 units is 2 each)
+    assert all(c.sched != L.GEMM_SCHED_STREAMK
+               for c in L.rank_configs(desc(512, 512, 4096, dt=L.GEMM_FP8_E4M3)))
+    # the lock chain: a tile's non-empty splits hand the lock on one after another, each hop
+    # 13,000 clocks plus the tile's partial read and written at 96 B/clk (16 tiles, 256 units:
+    # 16 splits per tile)
+    d = L.make_desc(512, 512, 65536, L.GEMM_BF16, L.GEMM_F32, L.GEMM_MAP_GROUPED_M, 0,
+                    L.GEMM_SCHED_AUTO, P, flags=L.GEMM_FLAG_STREAMK_CHAIN)
+    sk = [c for c in L.rank_configs(d) if c.sched == L.GEMM_SCHED_STREAMK and c.bm == 128]
+    assert sk and all(c.kernel == 0 for c in sk)  # the wide-wave kernel has no chain
+    assert sk[0].cycles_fixed >= 16 * (13000 + 2 * 128 * 128 * 4 / 96)
 
 
 def test_zero_depth_keeps_to_the_kernel_that_runs_it():
@@ -179,6 +196,8 @@ def test_rank_validation():
     ((8192, 11008, 8192), L.GEMM_FP8_E4M3, L.GEMM_BF16),
     ((1536, 5120, 6144), L.GEMM_FP8_E4M3, L.GEMM_BF16),
     ((1024, 8192, 4096), L.GEMM_BF16, L.GEMM_BF16),
+    ((512, 512, 4096), L.GEMM_FP8_E4M3, L.GEMM_BF16),
+    ((256, 256, 4096), L.GEMM_BF16, L.GEMM_BF16),
     # shapes the model's constants were not fitted to
     ((768, 18432, 3072), L.GEMM_BF16, L.GEMM_BF16),
     ((2560, 9216, 5120), L.GEMM_FP8_E4M3, L.GEMM_BF16),
