@@ -216,10 +216,13 @@ constexpr double kPartialWaveExpNarrow = 0.2;
 // Stream-K plans ran about 3 % slower per costed cycle than data-parallel ones over the same 184
 // shapes (the waits and the fixup's latency, beyond its bytes): their score is scaled by this
 constexpr double kStreamKFactor = 1.03;
-// ... and a band that gives each unit fewer k-steps than this is not worth its fixup: on 256 to
-// 1,024-square outputs with K = 4,096 such plans measured 20-50 % slower than data-parallel ones
-// (e4m3 512 x 512 x 4096: 2 k-steps per unit, 29 against 19 us)
-constexpr double kMinStreamKSteps = 6;
+// ... and a band that gives each unit only a few k-steps: all units then store and reduce their
+// partials at once, a burst the reduction waits on.  Costed kSkBurstClk at one k-step per unit,
+// falling linearly to none at kSkBurstSteps (fit to small outputs: e4m3 512 x 512 x 4096, 2
+// k-steps per unit, ran 29 us on Stream-K against 19 data-parallel; bf16 256 x 256 x 4096, 1
+// k-step per unit, 25 against 29)
+constexpr double kSkBurstClk = 20000;
+constexpr double kSkBurstSteps = 16;
 // MFMA efficiency of whole launches at the held clock (bench workloads, profiles/)
 double kernel_efficiency(int kind, int bm, int bn, int dt) {
   if (kind == KIND_WIDE && bm == 128) return dt == DT_BF16 ? 0.56 : 0.55;
@@ -385,7 +388,6 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
       // the wide-wave kernel's separate reduction needs a band of at least P iterations
       if (c.kind == KIND_WIDE && ((int64_t)sk * Kt < P || (d.flags & GEMM_FLAG_STREAMK_CHAIN)))
         continue;
-      if ((double)sk * (double)Kt < kMinStreamKSteps * P) continue;
     }
     const int wgm = 2, wgn = e->threads / 64 / 2;  // waves along M and N
     const double t = (double)tiles, bm = c.bm, bn = c.bn, kk = (double)Keff;
@@ -439,6 +441,8 @@ int rank_configs(const gemm_desc &d, std::vector<gemm_config_score> &out) {
         r.cycles_fixed +=
             2.0 * sk * units_per_tile * bm * bn * 4.0 / kDeviceBytesPerClk + kLatencyClk;
       }
+      const double steps = (double)sk * (double)Kt / P;  // band k-steps per unit
+      r.cycles_fixed += kSkBurstClk * std::max(0.0, 1.0 - steps / kSkBurstSteps);
     }
     const double worst = std::max(r.cycles_mfma, std::max(r.cycles_l2, r.cycles_local));
     r.score = worst / r.wave_efficiency + r.cycles_fixed;
